@@ -1,0 +1,176 @@
+"""Whole-block references: schedule -> retrieval -> RoPE -> attention (-> ConvKV memory).
+
+A *provider* hands the oracle the stream's inputs, exactly as the GPU path got
+them: ``provider.qkv(layer, block, step) -> (q, k, v)`` each [T, H, D];
+``provider.pose(block) -> [P]``; ``provider.conv_weights(layer) -> (wk, wv)``.
+The oracle keeps no cache: a context block's K/V are asked for again when
+needed, which keeps memory flat and the code short.
+
+Readings (beyond those stated in the modules used here):
+  * PR-Sink positions are absolute: token (f, y, x) of block b sits at
+    t = b * frames + f.  Cached keys keep the position they were written at.
+  * The block's retrieval uses its own pose, once, before its first step; all
+    layers and steps share the result.
+  * With several sampling steps per block (LiveAnimate page, section 方法:
+    three steps), a committed block contributes the K/V of its last step.
+  * ConvKV context order is [memory frames, window blocks oldest first,
+    current block]; temporal positions run 0, 1, 2, ... over those frames.
+"""
+from __future__ import annotations
+
+import numpy as np
+
+from .attention import attention
+from .convkv import conv_memory
+from .retrieval import retrieve
+from .rope import apply_rope
+from .schedule import convkv_schedule, prsink_schedule, token_positions
+
+
+def _scale(cfg):
+    s = cfg.get("softmax_scale", 0.0) or 0.0
+    return float(s) if s > 0 else 1.0 / np.sqrt(cfg["head_dim"])
+
+
+class _Base:
+    def __init__(self, cfg: dict, provider):
+        self.cfg = cfg
+        self.p = provider
+        F, gh, gw = cfg["frames"], cfg["grid_h"], cfg["grid_w"]
+        self.F = F
+        self.T = F * gh * gw
+        self.Tf = gh * gw
+        self.f_tok, self.y_tok, self.x_tok = token_positions(F, gh, gw)
+        self.split = tuple(cfg["rope"])
+        self.theta = float(cfg.get("theta", 10000.0))
+
+    def _rot(self, x, t_of_frame, heads, tok=None):
+        """Rotate x [N, H, D] (tokens ``tok`` of a block, default all) with t = t_of_frame(f)."""
+        tok = np.arange(x.shape[0]) if tok is None else tok
+        xs = np.asarray(x)[:, heads, :]
+        t = np.array([t_of_frame(f) for f in self.f_tok[tok]], np.float64)
+        return apply_rope(xs, t, self.y_tok[tok], self.x_tok[tok], self.split, self.theta)
+
+    def _attend(self, q_rot, ks, vs, heads, rows):
+        k = np.concatenate(ks, axis=0)
+        v = np.concatenate([np.asarray(x, np.float64) for x in vs], axis=0)
+        o_sub = attention(q_rot, k, v, _scale(self.cfg), rows=rows)
+        return o_sub
+
+
+class PRSinkReference(_Base):
+    """Static sink + pose-retrieved dynamic sinks + rolling window + current block."""
+
+    def schedule(self, m: int) -> dict:
+        c = self.cfg
+        return prsink_schedule(m, c["window"], c["bank"], c["static"])
+
+    def selection(self, m: int) -> list:
+        c = self.cfg
+        sch = self.schedule(m)
+        if c["dynamic_k"] == 0 or not sch["bank"]:
+            return []
+        pq = self.p.pose(m)
+        return retrieve(pq, [(b, self.p.pose(b)) for b in sch["bank"]], c["dynamic_k"])
+
+    def context(self, m: int, selection=None) -> list:
+        """[(kind, block id, tokens, t0)] in order static, dynamic, window, current."""
+        sch = self.schedule(m)
+        sel = self.selection(m) if selection is None else selection
+        F, T = self.F, self.T
+        segs = [("static", b, T, b * F) for b in sch["static"]]
+        segs += [("dynamic", b, T, b * F) for b in sel]
+        segs += [("window", b, T, b * F) for b in sch["window"]]
+        segs.append(("current", m, T, m * F))
+        return segs
+
+    def context_kv(self, m: int, layer: int, step: int, heads, selection=None):
+        """Rotated K and raw V of every context segment, each [T, len(heads), D] fp64."""
+        last = self.cfg["steps"] - 1
+        out = []
+        for kind, b, _, _ in self.context(m, selection):
+            s = step if kind == "current" else last
+            _, k, v = self.p.qkv(layer, b, s)
+            kr = self._rot(k, lambda f, b=b: b * self.F + f, heads)
+            out.append((kind, b, kr, np.asarray(v, np.float64)[:, heads, :]))
+        return out
+
+    def attend(self, m: int, layer: int, step: int, heads=None, rows=None, selection=None):
+        """Output [T, len(heads), D] fp64 of block m at (layer, step)."""
+        H = self.cfg["heads"]
+        heads = list(range(H)) if heads is None else list(heads)
+        q, _, _ = self.p.qkv(layer, m, step)
+        q_rot = self._rot(q, lambda f: m * self.F + f, heads)
+        kv = self.context_kv(m, layer, step, heads, selection)
+        return self._attend(q_rot, [x[2] for x in kv], [x[3] for x in kv], heads, rows)
+
+
+class ConvKVReference(_Base):
+    """Conv-compressed memory + rolling window + current block, context-relative RoPE."""
+
+    def schedule(self, m: int) -> dict:
+        c = self.cfg
+        if c["conv_stride"] != c["conv_kernel"]:
+            raise ValueError("the oracle follows the stride == kernel reading")
+        return convkv_schedule(m, self.F, c["window"], c["conv_kernel"], c["memory_frames"])
+
+    def context(self, m: int) -> list:
+        sch = self.schedule(m)
+        segs = [("memory", j, self.Tf, j) for j in range(len(sch["memory"]))]
+        segs += [("window", b, self.T, t0) for b, t0 in zip(sch["window"], sch["t0"]["window"])]
+        segs.append(("current", m, self.T, sch["t0"]["current"]))
+        return segs
+
+    def _frame(self, layer: int, e: int, heads):
+        """Raw K and V [Tf, len(heads), D] of evicted frame number e (last step's)."""
+        b, f = divmod(e, self.F)
+        _, k, v = self.p.qkv(layer, b, self.cfg["steps"] - 1)
+        sl = slice(f * self.Tf, (f + 1) * self.Tf)
+        return (np.asarray(k, np.float64)[sl][:, heads, :], np.asarray(v, np.float64)[sl][:, heads, :])
+
+    def memory(self, m: int, layer: int, heads):
+        """Raw memory K and V, each [n_mem, Tf, len(heads), D] fp64."""
+        sch = self.schedule(m)
+        if not sch["memory"]:
+            return None, None
+        wk, wv = self.p.conv_weights(layer)
+        wk = np.asarray(wk, np.float64)[heads]
+        wv = np.asarray(wv, np.float64)[heads]
+        mk, mv = [], []
+        for group in sch["memory"]:
+            fk, fv = zip(*[self._frame(layer, e, heads) for e in group])
+            # [kernel, Tf, H, D] -> [kernel, H, Tf, D] for conv_memory
+            fk = np.stack(fk).transpose(0, 2, 1, 3)
+            fv = np.stack(fv).transpose(0, 2, 1, 3)
+            mk.append(conv_memory(fk, wk)[0].transpose(1, 0, 2))
+            mv.append(conv_memory(fv, wv)[0].transpose(1, 0, 2))
+        return np.stack(mk), np.stack(mv)
+
+    def context_kv(self, m: int, layer: int, step: int, heads):
+        """Rotated K and raw V of every context segment (memory frames: Tf tokens)."""
+        sch = self.schedule(m)
+        last = self.cfg["steps"] - 1
+        out = []
+        mk, mv = self.memory(m, layer, heads)
+        tok_frame0 = np.arange(self.Tf)                          # a memory frame has frame-0 layout
+        for j in range(len(sch["memory"])):
+            kr = self._rot(mk[j], lambda f, j=j: j, list(range(len(heads))), tok=tok_frame0)
+            out.append(("memory", j, kr, mv[j]))
+        for b, t0 in zip(sch["window"], sch["t0"]["window"]):
+            _, k, v = self.p.qkv(layer, b, last)
+            kr = self._rot(k, lambda f, t0=t0: t0 + f, heads)
+            out.append(("window", b, kr, np.asarray(v, np.float64)[:, heads, :]))
+        t0 = sch["t0"]["current"]
+        _, k, v = self.p.qkv(layer, m, step)
+        kr = self._rot(k, lambda f: t0 + f, heads)
+        out.append(("current", m, kr, np.asarray(v, np.float64)[:, heads, :]))
+        return out
+
+    def attend(self, m: int, layer: int, step: int, heads=None, rows=None):
+        H = self.cfg["heads"]
+        heads = list(range(H)) if heads is None else list(heads)
+        t0 = self.schedule(m)["t0"]["current"]
+        q, _, _ = self.p.qkv(layer, m, step)
+        q_rot = self._rot(q, lambda f: t0 + f, heads)
+        kv = self.context_kv(m, layer, step, heads)
+        return self._attend(q_rot, [x[2] for x in kv], [x[3] for x in kv], heads, rows)

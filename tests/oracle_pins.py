@@ -1,0 +1,228 @@
+"""Checks that pin the oracle to facts outside itself.
+
+Each check takes the oracle function(s) it pins as arguments, so the same
+check runs against the real oracle (tests/test_oracle.py) and against copies
+with a planted mistake (tests/test_oracle_mutations.py), which must fail it.
+Every check raises AssertionError on a mismatch.
+"""
+from __future__ import annotations
+
+import numpy as np
+
+from conftest import ids, read_table
+
+
+# ---------------------------------------------------------------- schedules
+def check_prsink_golden(prsink_schedule):
+    """Hand-derived table (tests/golden) for window 3, bank 8, one static block."""
+    for row in read_table("prsink_schedule_w3_b8_s1.txt"):
+        m = int(row[0])
+        s = prsink_schedule(m, 3, 8, 1)
+        assert s["static"] == ids(row[1]), (m, s)
+        assert s["bank"] == ids(row[2]), (m, s)
+        assert s["window"] == ids(row[3]), (m, s)
+        ev = None if row[4] == "-" else int(row[4])
+        assert s["evicted"] == ev, (m, s)
+
+
+def check_prsink_closed_vs_sim(prsink_schedule, simulate_prsink):
+    for W in (1, 2, 3, 4):
+        for B in (0, 1, 2, 5, 8):
+            for S in (0, 1, 2):
+                sim = simulate_prsink(30, W, B, S)
+                for m in range(30):
+                    assert prsink_schedule(m, W, B, S) == sim[m], (W, B, S, m)
+
+
+def check_convkv_golden(convkv_schedule):
+    for row in read_table("convkv_schedule_f3_w3_k5_m1.txt"):
+        m = int(row[0])
+        s = convkv_schedule(m, 3, 3, 5, 1)
+        assert s["window"] == ids(row[1]), (m, s)
+        assert s["evicted_frames"] == int(row[2]), (m, s)
+        assert s["memory"] == ([] if row[3] == "-" else [ids(row[3])]), (m, s)
+        assert s["t0"]["window"] == ids(row[4]), (m, s)
+        assert s["t0"]["current"] == int(row[5]), (m, s)
+        assert s["evicted"] == (None if row[6] == "-" else int(row[6])), (m, s)
+
+
+def check_convkv_closed_vs_sim(convkv_schedule, simulate_convkv):
+    for F in (1, 2, 3, 4):
+        for W in (1, 2, 3):
+            for K in (2, 3, 5):
+                for M in (1, 2, 3):
+                    sim = simulate_convkv(25, F, W, K, M)
+                    for m in range(25):
+                        assert convkv_schedule(m, F, W, K, M) == sim[m], (F, W, K, M, m)
+
+
+# ---------------------------------------------------------------- retrieval
+def check_retrieval_hand(retrieve):
+    """2-D poses whose cosines are known by hand: 1, 1/sqrt2, 0, -1."""
+    q = np.array([1, 0], np.float32)
+    bank = [(10, np.array([1, 1], np.float32)), (11, np.array([3, 0], np.float32)),
+            (12, np.array([0, 2], np.float32)), (13, np.array([-1, 0], np.float32))]
+    assert retrieve(q, bank, 4) == [11, 10, 12, 13]
+    assert retrieve(q, bank, 2) == [11, 10]
+    assert retrieve(q, bank, 9) == [11, 10, 12, 13]          # fewer candidates than k
+    assert retrieve(q, [], 3) == []
+
+
+def check_retrieval_ties(retrieve, rng):
+    """Exact ties (bitwise duplicate; a copy scaled by 2) go to the lower stream id."""
+    P = 32
+    for trial in range(20):
+        base = rng.standard_normal(P).astype(np.float32)
+        q = (base + 0.3 * rng.standard_normal(P)).astype(np.float32)
+        others = [rng.standard_normal(P).astype(np.float32) for _ in range(5)]
+        dup = base.copy()
+        twice = (base * np.float32(2)).astype(np.float32)
+        for a, b in ((base, dup), (base, twice), (twice, base)):
+            lo, hi = 3 + trial, 40 + trial
+            bank = [(hi, b), (7, others[0]), (lo, a), (90, others[1])]
+            got = retrieve(q, bank, 2)
+            # base is by construction the closest: it and its tie take the top 2, low id first
+            assert got == [lo, hi], (trial, got)
+    # zero-norm poses score 0: ranked above negative cosines, below positive ones
+    q = np.array([1, 0, 0], np.float32)
+    bank = [(5, np.zeros(3, np.float32)), (2, np.array([-1, 0, 0], np.float32)),
+            (9, np.array([1, 1, 0], np.float32)), (3, np.zeros(3, np.float32))]
+    assert retrieve(q, bank, 4) == [9, 3, 5, 2]
+    assert retrieve(np.zeros(3, np.float32), bank, 4) == [2, 3, 5, 9]   # zero query: all tie
+
+
+def check_retrieval_vs_fp64(retrieve, rng):
+    """On tie-free random data the exact ranking equals an fp64 numpy argsort."""
+    from oracle.retrieval import fp64_cosines
+    for trial in range(30):
+        P = int(rng.integers(2, 130))
+        n = int(rng.integers(1, 70))
+        q = rng.standard_normal(P).astype(np.float32)
+        poses = rng.standard_normal((n, P)).astype(np.float32)
+        id_list = list(rng.permutation(1000)[:n])
+        bank = list(zip(id_list, poses))
+        k = int(rng.integers(1, 6))
+        c = fp64_cosines(q, poses)
+        order = np.argsort(-c, kind="stable")
+        assert retrieve(q, bank, k) == [id_list[i] for i in order[:k]], trial
+
+
+def check_repeat_pose(retrieve_stream):
+    """Tiny fp32 stream: blocks 7 and 11 copy an earlier pose (+0.01 noise) and must
+    retrieve exactly that block (LiveAnimate page, 方法: the dynamic sink restores
+    the context of a recurring pose)."""
+    from bounded_kv_block_amd import synth
+    cfg = synth.workload("tiny_fp32")
+    src = synth.repeat_sources(cfg)
+    assert set(src) == {3, 7, 11} and src[3] == 0
+    for m in (7, 11):
+        assert retrieve_stream(cfg, m) == [src[m]], (m, src)
+
+
+# ---------------------------------------------------------------- rope
+def check_rope_frequencies(rope_frequencies):
+    w = rope_frequencies(4, 10000.0)
+    assert np.allclose(w, [1.0, 0.01], rtol=0, atol=1e-15)
+    w = rope_frequencies(44, 10000.0)
+    assert len(w) == 22 and w[0] == 1.0
+    assert np.isclose(w[21], 10000.0 ** (-42.0 / 44.0), rtol=1e-14)
+
+
+def check_rope_properties(apply_rope, rng):
+    N, H, D = 7, 3, 24
+    split = (8, 8, 8)
+    x = rng.standard_normal((N, H, D))
+    zero = np.zeros(N)
+    assert np.array_equal(apply_rope(x, zero, zero, zero, split), x)          # identity at 0
+    pt, ph, pw = rng.integers(0, 50, (3, N)).astype(np.float64)
+    y = apply_rope(x, pt, ph, pw, split)
+    assert np.allclose(np.linalg.norm(y, axis=-1), np.linalg.norm(x, axis=-1), rtol=1e-13)
+    # hand value: one pair, position 1 -> rotation by 1 radian
+    e = np.zeros((1, 1, 2))
+    e[0, 0, 0] = 1.0
+    r = apply_rope(e, np.ones(1), np.zeros(1), np.zeros(1), (2, 0, 0))
+    assert np.allclose(r[0, 0], [np.cos(1.0), np.sin(1.0)], atol=1e-15)
+    # complex-multiplication formulation, per axis
+    out = np.empty_like(x)
+    off = 0
+    for size, pos in zip(split, (pt, ph, pw)):
+        i = np.arange(size // 2)
+        z = x[:, :, off:off + size:2] + 1j * x[:, :, off + 1:off + size:2]
+        z = z * np.exp(1j * pos[:, None, None] * (10000.0 ** (-2.0 * i / size))[None, None, :])
+        out[:, :, off:off + size:2] = z.real
+        out[:, :, off + 1:off + size:2] = z.imag
+        off += size
+    assert np.allclose(y, out, atol=1e-12)
+    # relative positions: shifting every t (or y, x) by a constant keeps q.k
+    q = rng.standard_normal((N, H, D))
+    k = rng.standard_normal((N, H, D))
+    qt, kt = rng.integers(0, 40, (2, N)).astype(np.float64)
+    a = np.einsum("nhd,mhd->hnm", apply_rope(q, qt, ph, pw, split), apply_rope(k, kt, ph, pw, split))
+    b = np.einsum("nhd,mhd->hnm", apply_rope(q, qt + 17, ph + 3, pw, split),
+                  apply_rope(k, kt + 17, ph + 3, pw, split))
+    assert np.allclose(a, b, atol=1e-10)
+    # an axis only touches its own channels
+    y2 = apply_rope(x, pt, zero, zero, split)
+    assert np.array_equal(y2[:, :, 8:], x[:, :, 8:])
+
+
+# ---------------------------------------------------------------- attention
+def check_attention_vs_torch(attention, rng):
+    import torch
+    for (Nq, Nk, H, D) in ((5, 9, 2, 8), (33, 70, 3, 16), (64, 1, 1, 4)):
+        q = rng.standard_normal((Nq, H, D))
+        k = rng.standard_normal((Nk, H, D))
+        v = rng.standard_normal((Nk, H, D))
+        got = attention(q, k, v)
+        t = lambda a: torch.from_numpy(np.ascontiguousarray(a.transpose(1, 0, 2)))[None]
+        ref = torch.nn.functional.scaled_dot_product_attention(t(q), t(k), t(v))[0]
+        assert np.allclose(got, ref.numpy().transpose(1, 0, 2), atol=1e-12), (Nq, Nk)
+
+
+def check_attention_closed_forms(attention, softmax_weights, rng):
+    H, D = 2, 8
+    k = rng.standard_normal((11, H, D))
+    v = rng.standard_normal((11, H, D))
+    o = attention(np.zeros((4, H, D)), k, v)                      # Q = 0 -> mean of V
+    assert np.allclose(o, np.broadcast_to(v.mean(axis=0), o.shape), atol=1e-14)
+    o1 = attention(rng.standard_normal((3, H, D)), k[:1], v[:1])  # one key -> that value
+    assert np.allclose(o1, np.broadcast_to(v[0], o1.shape), atol=1e-14)
+    p = softmax_weights(rng.standard_normal((6, D)), k[:, 0], 0.5)
+    assert np.all(p >= 0) and np.allclose(p.sum(axis=1), 1.0, atol=1e-12)
+    # two keys, closed form: p0 = 1 / (1 + exp(s*(q.k1 - q.k0)))
+    q1 = rng.standard_normal((1, 1, D))
+    kk = rng.standard_normal((2, 1, D))
+    vv = np.zeros((2, 1, D))
+    vv[1, 0, 0] = 1.0
+    s = 1 / np.sqrt(D)
+    z = s * (kk[:, 0] @ q1[0, 0])
+    want = 1 / (1 + np.exp(z[0] - z[1]))
+    assert np.isclose(attention(q1, kk, vv)[0, 0, 0], want, rtol=1e-13)
+    # key/value order does not matter
+    q = rng.standard_normal((5, H, D))
+    perm = rng.permutation(11)
+    assert np.allclose(attention(q, k, v), attention(q, k[perm], v[perm]), atol=1e-13)
+
+
+# ---------------------------------------------------------------- convkv
+def check_conv_memory(conv_memory, rng):
+    n, H, S, D, K = 5, 2, 6, 4, 5
+    fr = rng.standard_normal((n, H, S, D))
+    onehot = np.zeros((H, D, K))
+    onehot[:, :, K - 1] = 1.0
+    assert np.array_equal(conv_memory(fr, onehot)[0], fr[-1])          # tap 4 -> newest frame
+    mean = np.full((H, D, K), 1.0 / K)
+    assert np.allclose(conv_memory(fr, mean)[0], fr.mean(axis=0), atol=1e-14)
+    w = rng.standard_normal((H, D, K))
+    got = conv_memory(fr, w)[0]
+    for h in range(H):
+        for c in range(D):
+            for s in range(S):
+                ref = np.correlate(fr[:, h, s, c], w[h, c, :], mode="valid")
+                assert np.isclose(got[h, s, c], ref[0], rtol=1e-13, atol=1e-14)
+    fr2 = rng.standard_normal((n, H, S, D))
+    assert np.allclose(conv_memory(2 * fr - 3 * fr2, w), 2 * conv_memory(fr, w) - 3 * conv_memory(fr2, w),
+                       atol=1e-12)
+    two = rng.standard_normal((2 * K, H, S, D))                       # two output frames, stride K
+    out = conv_memory(two, w)
+    assert out.shape[0] == 2 and np.allclose(out[1], conv_memory(two[K:], w)[0], atol=1e-14)

@@ -1,0 +1,219 @@
+"""CPU tests: the oracle against its pins (closed forms, library routines,
+hand-derived fixtures, brute force) and stream-level identities."""
+import numpy as np
+import pytest
+
+import oracle
+import oracle_pins as pins
+from conftest import SynthProvider, ids, read_table
+from bounded_kv_block_amd import synth
+
+
+def test_prsink_schedule_golden():
+    pins.check_prsink_golden(oracle.prsink_schedule)
+
+
+def test_prsink_schedule_closed_form_matches_simulation():
+    pins.check_prsink_closed_vs_sim(oracle.prsink_schedule, oracle.simulate_prsink)
+
+
+def test_convkv_schedule_golden():
+    pins.check_convkv_golden(oracle.convkv_schedule)
+
+
+def test_convkv_schedule_closed_form_matches_simulation():
+    pins.check_convkv_closed_vs_sim(oracle.convkv_schedule, oracle.simulate_convkv)
+
+
+def test_constant_context_size():
+    """The key count is constant once warm-up ends (LiveAnimate page, 关键发现: a fixed
+    number of blocks is kept): from block 4 + k for PR-Sink, block 5 for ConvKV."""
+    for name, start in (("tiny_fp32", 5), ("prsink_512", 6), ("prsink_long", 6)):
+        cfg = synth.workload(name)
+        T = synth.tokens_per_block(cfg)
+        n = []
+        for m in range(40):
+            s = oracle.prsink_schedule(m, cfg["window"], cfg["bank"], cfg["static"])
+            n.append(T * (len(s["static"]) + min(cfg["dynamic_k"], len(s["bank"]))
+                          + len(s["window"]) + 1))
+        assert all(x == n[start] for x in n[start:]) and n[start - 1] < n[start]
+        assert n[start] == {"tiny_fp32": 768}.get(name, 21504)
+    cfg = synth.workload("convkv_512")
+    n = []
+    for m in range(40):
+        s = oracle.convkv_schedule(m, 3, 3, 5, 1)
+        n.append(1024 * len(s["memory"]) + 3072 * (len(s["window"]) + 1))
+    assert all(x == 13312 for x in n[5:]) and n[4] != 13312
+
+
+def test_retrieval_hand_values():
+    pins.check_retrieval_hand(oracle.retrieve)
+
+
+def test_retrieval_ties(rng):
+    pins.check_retrieval_ties(oracle.retrieve, rng)
+
+
+def test_retrieval_matches_fp64_argsort(rng):
+    pins.check_retrieval_vs_fp64(oracle.retrieve, rng)
+
+
+def _stream_retrieve(cfg, m):
+    return oracle.PRSinkReference(cfg, SynthProvider(cfg)).selection(m)
+
+
+def test_repeat_pose_retrieves_source():
+    pins.check_repeat_pose(_stream_retrieve)
+
+
+@pytest.mark.parametrize("name", ["tiny_fp32", "prsink_512", "prsink_long"])
+def test_pose_streams_have_no_near_ties(name):
+    """Rankings never hinge on a gap below fp64 resolution (exact ties are built
+    on purpose elsewhere)."""
+    cfg = synth.workload(name)
+    n = min(cfg["blocks"], 200)
+    P = synth.poses(cfg, n)
+    for m in range(n):
+        s = oracle.prsink_schedule(m, cfg["window"], cfg["bank"], cfg["static"])
+        bank = [(b, P[b]) for b in s["bank"]]
+        g = oracle.boundary_gap(P[m], bank, cfg["dynamic_k"])
+        assert g is None or g == 0 or g > 2.0 ** -40, (m, float(g))
+
+
+def test_rope_frequencies():
+    pins.check_rope_frequencies(oracle.rope_frequencies)
+
+
+def test_rope_properties(rng):
+    pins.check_rope_properties(oracle.apply_rope, rng)
+
+
+def test_attention_matches_torch_sdpa(rng):
+    pins.check_attention_vs_torch(oracle.attention, rng)
+
+
+def test_attention_closed_forms(rng):
+    pins.check_attention_closed_forms(oracle.attention, oracle.softmax_weights, rng)
+
+
+def test_conv_memory(rng):
+    pins.check_conv_memory(oracle.conv_memory, rng)
+
+
+# ------------------------------------------------------------ stream identities
+def _all_blocks_kv(cfg, prov, m, layer=0):
+    """K (rotated at absolute positions) and V of blocks 0..m concatenated, with block ids."""
+    F = cfg["frames"]
+    f, y, x = oracle.token_positions(F, cfg["grid_h"], cfg["grid_w"])
+    ks, vs, owner = [], [], []
+    last = cfg["steps"] - 1
+    for b in range(m + 1):
+        _, k, v = prov.qkv(layer, b, last if b < m else 0)
+        ks.append(oracle.apply_rope(k, b * F + f, y, x, cfg["rope"]))
+        vs.append(v)
+        owner += [b] * k.shape[0]
+    return np.concatenate(ks), np.concatenate(vs), np.array(owner)
+
+
+@pytest.mark.parametrize("rope", [(0, 0, 0), (24, 20, 20)])
+def test_prsink_equals_masked_full_attention(rope):
+    """Bounded-cache attention of block m equals dense attention over the whole
+    stream 0..m masked to the hand-derived context: static {0}, the bank's
+    retrieved blocks, the golden window and block m itself."""
+    cfg = synth.workload("tiny_fp32", rope=rope)
+    prov = SynthProvider(cfg)
+    ref = oracle.PRSinkReference(cfg, prov)
+    golden = {int(r[0]): r for r in read_table("prsink_schedule_w3_b8_s1.txt")}
+    F, gh, gw = cfg["frames"], cfg["grid_h"], cfg["grid_w"]
+    f, y, x = oracle.token_positions(F, gh, gw)
+    src = synth.repeat_sources(cfg)
+    for m in range(cfg["blocks"]):
+        sel = ref.selection(m)
+        if m in (7, 11):
+            assert sel == [src[m]]
+        allowed = set(ids(golden[m][1])) | set(sel) | set(ids(golden[m][3])) | {m}
+        assert set(sel) <= set(ids(golden[m][2]))
+        k_all, v_all, owner = _all_blocks_kv(cfg, prov, m)
+        q, _, _ = prov.qkv(0, m, 0)
+        qr = oracle.apply_rope(q, m * F + f, y, x, cfg["rope"])
+        mask = np.broadcast_to(np.isin(owner, sorted(allowed))[None, :], (q.shape[0], len(owner)))
+        want = oracle.masked_attention(qr, k_all, v_all, mask)
+        got = ref.attend(m, 0, 0)
+        assert np.allclose(got, want, atol=1e-12, rtol=0), m
+        if m <= 4:          # warm-up: the context is every block so far (plain block-causal)
+            assert allowed == set(range(m + 1))
+
+
+def test_prsink_block0_is_plain_attention():
+    import torch
+    cfg = synth.workload("tiny_fp32")
+    prov = SynthProvider(cfg)
+    q, k, v = prov.qkv(0, 0, 0)
+    got = oracle.PRSinkReference(cfg, prov).attend(0, 0, 0)
+    t = lambda a: torch.from_numpy(np.asarray(a, np.float64).transpose(1, 0, 2).copy())[None]
+    ref = torch.nn.functional.scaled_dot_product_attention(t(q), t(k), t(v))[0].numpy().transpose(1, 0, 2)
+    assert np.allclose(got, ref, atol=1e-12)
+
+
+def test_sliding_window_special_case():
+    """k = 0, bank 0, no static sink: the context is just the last 3 blocks + current."""
+    cfg = synth.workload("tiny_fp32", dynamic_k=0, bank=0, static=0, rope=(24, 20, 20))
+    prov = SynthProvider(cfg)
+    ref = oracle.PRSinkReference(cfg, prov)
+    F, gh, gw = cfg["frames"], cfg["grid_h"], cfg["grid_w"]
+    f, y, x = oracle.token_positions(F, gh, gw)
+    for m in (0, 2, 6, 9):
+        k_all, v_all, owner = _all_blocks_kv(cfg, prov, m)
+        q, _, _ = prov.qkv(0, m, 0)
+        qr = oracle.apply_rope(q, m * F + f, y, x, cfg["rope"])
+        mask = np.broadcast_to((owner >= m - 3)[None, :], (q.shape[0], len(owner)))
+        assert np.allclose(ref.attend(m, 0, 0), oracle.masked_attention(qr, k_all, v_all, mask),
+                           atol=1e-12)
+
+
+def _small_convkv(**kw):
+    return synth.workload("convkv_512", heads=2, head_dim=16, frames=3, grid_h=2, grid_w=3,
+                          rope=(6, 4, 6), blocks=9, **kw)
+
+
+def test_convkv_warmup_equals_absolute_positions():
+    """Before any memory exists, context-relative RoPE positions differ from
+    absolute ones by one shift for every token, so the output equals dense
+    attention over the window + current at absolute positions."""
+    cfg = _small_convkv()
+    prov = SynthProvider(cfg)
+    ref = oracle.ConvKVReference(cfg, prov)
+    F = cfg["frames"]
+    f, y, x = oracle.token_positions(F, cfg["grid_h"], cfg["grid_w"])
+    for m in range(5):
+        k_all, v_all, owner = _all_blocks_kv(cfg, prov, m)
+        q, _, _ = prov.qkv(0, m, 0)
+        qr = oracle.apply_rope(q, m * F + f, y, x, cfg["rope"])
+        mask = np.broadcast_to((owner >= m - 3)[None, :], (q.shape[0], len(owner)))
+        assert np.allclose(ref.attend(m, 0, 0), oracle.masked_attention(qr, k_all, v_all, mask),
+                           atol=1e-12), m
+
+
+def test_convkv_memory_with_onehot_weights():
+    """With tap-4 one-hot weights the memory frame is the newest evicted frame,
+    re-positioned at t = 0 (checked through the context K/V the oracle builds)."""
+    cfg = _small_convkv()
+    prov = SynthProvider(cfg)
+    H, D, K = cfg["heads"], cfg["head_dim"], cfg["conv_kernel"]
+    w = np.zeros((H, D, K), np.float32)
+    w[:, :, K - 1] = 1.0
+    prov._w[0] = (w, w)
+    ref = oracle.ConvKVReference(cfg, prov)
+    Tf = cfg["grid_h"] * cfg["grid_w"]
+    f, y, x = oracle.token_positions(1, cfg["grid_h"], cfg["grid_w"])
+    for m in (5, 6, 8):
+        newest = 3 * (m - 3) - 1                      # last frame of block m-4
+        b, fr = divmod(newest, 3)
+        _, k, v = prov.qkv(0, b, 0)
+        kv = ref.context_kv(m, 0, 0, list(range(H)))
+        assert kv[0][0] == "memory"
+        sl = slice(fr * Tf, (fr + 1) * Tf)
+        want_k = oracle.apply_rope(k[sl], np.zeros(Tf), y, x, cfg["rope"])
+        assert np.allclose(kv[0][2], want_k, atol=1e-13)
+        assert np.array_equal(kv[0][3], np.asarray(v[sl], np.float64))
+        assert [s[0] for s in kv] == ["memory", "window", "window", "window", "current"]

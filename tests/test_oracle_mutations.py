@@ -1,0 +1,189 @@
+"""Plant plausible mistakes in copies of the oracle's functions (on the CPU) and
+check that the pins catch each one: a pin that passes a broken oracle pins
+nothing."""
+from collections import deque
+from fractions import Fraction
+
+import numpy as np
+import pytest
+
+import oracle
+import oracle_pins as pins
+from oracle import retrieval as R
+
+
+def _fails(check, *args):
+    try:
+        check(*args)
+    except AssertionError:
+        return True
+    return False
+
+
+# -- schedule mutants ---------------------------------------------------------
+def _sched_window_off_by_one(m, window=3, bank=8, static=1):
+    s = oracle.prsink_schedule(m, window, bank, static)
+    s["window"] = list(range(max(static, m - window + 1), m))
+    return s
+
+
+def _sched_bank_lifo(m, window=3, bank=8, static=1):
+    s = oracle.prsink_schedule(m, window, bank, static)
+    ev = list(range(static, m - window))
+    s["bank"] = ev[:bank]                     # keeps the oldest instead of the newest
+    return s
+
+
+def _sched_static_in_window(m, window=3, bank=8, static=1):
+    s = oracle.prsink_schedule(m, window, bank, static)
+    s["window"] = list(range(max(0, m - window), m))
+    return s
+
+
+@pytest.mark.parametrize("mutant", [_sched_window_off_by_one, _sched_bank_lifo, _sched_static_in_window])
+def test_schedule_mutants_fail(mutant):
+    assert _fails(pins.check_prsink_golden, mutant)
+
+
+def _convkv_left_aligned(m, frames, window=3, kernel=5, memory_frames=1):
+    s = oracle.convkv_schedule(m, frames, window, kernel, memory_frames)
+    s["memory"] = [[j * kernel + i for i in range(kernel)] for j in range(len(s["memory"]))]
+    return s
+
+
+def _convkv_absolute_t(m, frames, window=3, kernel=5, memory_frames=1):
+    s = oracle.convkv_schedule(m, frames, window, kernel, memory_frames)
+    s["t0"] = {"memory": 0, "window": [b * frames for b in s["window"]], "current": m * frames}
+    return s
+
+
+@pytest.mark.parametrize("mutant", [_convkv_left_aligned, _convkv_absolute_t])
+def test_convkv_schedule_mutants_fail(mutant):
+    assert _fails(pins.check_convkv_golden, mutant)
+
+
+# -- retrieval mutants --------------------------------------------------------
+def _retrieve_high_id_ties(query, bank, k):
+    keys = R.exact_keys(query, bank)
+    order = sorted(range(len(bank)), key=lambda i: (-keys[i], -bank[i][0]))
+    return [bank[i][0] for i in order[:min(k, len(bank))]]
+
+
+def _retrieve_dot_only(query, bank, k):
+    q = np.asarray(query, np.float64)
+    order = sorted(range(len(bank)), key=lambda i: (-float(np.dot(q, bank[i][1])), bank[i][0]))
+    return [bank[i][0] for i in order[:min(k, len(bank))]]
+
+
+def _retrieve_unsigned(query, bank, k):
+    keys = [abs(x) for x in R.exact_keys(query, bank)]
+    order = sorted(range(len(bank)), key=lambda i: (-keys[i], bank[i][0]))
+    return [bank[i][0] for i in order[:min(k, len(bank))]]
+
+
+def _retrieve_ascending(query, bank, k):
+    keys = R.exact_keys(query, bank)
+    order = sorted(range(len(bank)), key=lambda i: (keys[i], bank[i][0]))
+    return [bank[i][0] for i in order[:min(k, len(bank))]]
+
+
+@pytest.mark.parametrize("mutant", [_retrieve_high_id_ties, _retrieve_dot_only, _retrieve_unsigned,
+                                    _retrieve_ascending])
+def test_retrieval_mutants_fail(mutant, rng):
+    caught = (_fails(pins.check_retrieval_hand, mutant) or _fails(pins.check_retrieval_ties, mutant, rng)
+              or _fails(pins.check_retrieval_vs_fp64, mutant, rng))
+    assert caught
+
+
+# -- rope mutants -------------------------------------------------------------
+def _rope_sign(x, pt, ph, pw, split, theta=10000.0):
+    return oracle.apply_rope(x, -np.asarray(pt, float), -np.asarray(ph, float), -np.asarray(pw, float),
+                             split, theta)
+
+
+def _rope_half_split(x, pt, ph, pw, split, theta=10000.0):
+    """Rotate (i, i + size/2) pairs instead of adjacent pairs."""
+    x = np.asarray(x, np.float64)
+    out = x.copy()
+    off = 0
+    for size, pos in zip(split, (pt, ph, pw)):
+        if size:
+            w = oracle.rope_frequencies(size, theta)
+            phi = np.asarray(pos, float)[:, None] * w[None, :]
+            c, s = np.cos(phi)[:, None, :], np.sin(phi)[:, None, :]
+            h = size // 2
+            u0, u1 = x[:, :, off:off + h], x[:, :, off + h:off + size]
+            out[:, :, off:off + h] = u0 * c - u1 * s
+            out[:, :, off + h:off + size] = u0 * s + u1 * c
+        off += size
+    return out
+
+
+def _rope_axes_swapped(x, pt, ph, pw, split, theta=10000.0):
+    return oracle.apply_rope(x, ph, pt, pw, split, theta)
+
+
+@pytest.mark.parametrize("mutant", [_rope_sign, _rope_half_split, _rope_axes_swapped])
+def test_rope_mutants_fail(mutant, rng):
+    assert _fails(pins.check_rope_properties, mutant, rng)
+
+
+def _freq_wrong_exponent(dim, theta=10000.0):
+    i = np.arange(dim // 2, dtype=np.float64)
+    return np.power(theta, -i / dim)
+
+
+def test_rope_frequency_mutant_fails():
+    assert _fails(pins.check_rope_frequencies, _freq_wrong_exponent)
+
+
+# -- attention mutants --------------------------------------------------------
+def _attn_no_scale(q, k, v, scale=None, heads=None, rows=None):
+    return oracle.attention(q, k, v, 1.0, heads, rows)
+
+
+def _attn_transposed_softmax(q, k, v, scale=None, heads=None, rows=None):
+    q = np.asarray(q, float); k = np.asarray(k, float); v = np.asarray(v, float)
+    out = np.zeros_like(q)
+    s = 1 / np.sqrt(q.shape[-1]) if scale is None else scale
+    for h in range(q.shape[1]):
+        z = q[:, h] @ k[:, h].T * s
+        p = np.exp(z - z.max(axis=0, keepdims=True))
+        p /= p.sum(axis=0, keepdims=True)                   # normalised over queries
+        out[:, h] = p @ v[:, h]
+    return out
+
+
+def _attn_unnormalised(q, k, v, scale=None, heads=None, rows=None):
+    q = np.asarray(q, float); k = np.asarray(k, float); v = np.asarray(v, float)
+    out = np.zeros_like(q)
+    s = 1 / np.sqrt(q.shape[-1]) if scale is None else scale
+    for h in range(q.shape[1]):
+        z = q[:, h] @ k[:, h].T * s
+        out[:, h] = np.exp(z - z.max(axis=1, keepdims=True)) @ v[:, h]
+    return out
+
+
+@pytest.mark.parametrize("mutant", [_attn_no_scale, _attn_transposed_softmax, _attn_unnormalised])
+def test_attention_mutants_fail(mutant, rng):
+    assert (_fails(pins.check_attention_vs_torch, mutant, rng)
+            or _fails(pins.check_attention_closed_forms, mutant, oracle.softmax_weights, rng))
+
+
+# -- conv mutants -------------------------------------------------------------
+def _conv_reversed_taps(frames, w, stride=None):
+    return oracle.conv_memory(frames, np.asarray(w)[..., ::-1], stride)
+
+
+def _conv_shared_weights(frames, w, stride=None):
+    w = np.asarray(w)
+    return oracle.conv_memory(frames, np.broadcast_to(w[:1, :1], w.shape), stride)
+
+
+def _conv_overlapping(frames, w, stride=None):
+    return oracle.conv_memory(frames, w, 1)
+
+
+@pytest.mark.parametrize("mutant", [_conv_reversed_taps, _conv_shared_weights, _conv_overlapping])
+def test_conv_mutants_fail(mutant, rng):
+    assert _fails(pins.check_conv_memory, mutant, rng)
