@@ -1,0 +1,250 @@
+#!/usr/bin/env python3
+"""Throughput of bounded-KV block attention on one MI355X.
+
+One step = one streaming block through the whole path: bkv_retrieve (pose
+top-k, block open), bkv_attend for every (sampling step, layer) -- K/V append
+with fused 3D RoPE and the flash-attention kernel over the bounded context --
+and bkv_commit (window/bank bookkeeping; ConvKV: memory rebuild).  Inputs
+(Q/K/V pools, poses) are resident in HBM before timing starts.
+
+Prints one JSON line: query tokens/s of the whole step (value), attention
+TFLOP/s and % of the bf16 MFMA peak, per-kernel event timings, the roofline
+of the dominant kernel, per-block latency percentiles and the CPU oracle
+timed on a bounded sample of the same workload.
+
+Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
+"""
+import argparse
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+METRIC = "query tokens/s & TFLOP/s of bounded-KV block attention (% bf16 MFMA peak)"
+PEAK_BF16_TFLOPS = 2500.0      # MI355X dense bf16 MFMA
+PEAK_FP32_TFLOPS = 157.3       # MI355X fp32 vector
+PEAK_HBM_GBS = 8000.0          # MI355X HBM3E
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=40)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--workload", default="prsink_512",
+                    choices=["prsink_512", "prsink_720x416", "prsink_long", "convkv_512", "tiny_fp32"])
+    ap.add_argument("--pool", type=int, default=4, help="distinct resident input blocks cycled through")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-seconds", type=float, default=12.0, help="target CPU-oracle sample time")
+    return ap.parse_args()
+
+
+def steady_block(cfg):
+    """First block whose context has its final size."""
+    if cfg["mode"] == "convkv":
+        return cfg["window"] + 2
+    return cfg["static"] + cfg["window"] + cfg["dynamic_k"]
+
+
+def cpu_baseline(cfg, run_inputs, poses, m, target_s):
+    """The oracle, as it stands, on block m of the same stream: retrieval plus
+    attention of whole heads (all queries) until about target_s seconds."""
+    import numpy as np
+    import oracle
+
+    class Prov:
+        def __init__(self):
+            self.cache = {}
+
+        def qkv(self, layer, block, step):
+            key = (layer, block, step)
+            if key not in self.cache:
+                self.cache[key] = tuple(t.float().cpu().numpy() for t in run_inputs(layer, block, step))
+            return self.cache[key]
+
+        def pose(self, b):
+            return poses[b]
+
+        def conv_weights(self, layer):
+            from bounded_kv_block_amd import synth
+            return synth.conv_weights(cfg, layer)
+
+    prov = Prov()
+    ref = (oracle.ConvKVReference if cfg["mode"] == "convkv" else oracle.PRSinkReference)(cfg, prov)
+    # fetch the inputs first (not part of the oracle's work)
+    for kind, b, _, _ in (ref.context(m) if cfg["mode"] == "convkv" else ref.context(m, ref.selection(m))):
+        if kind != "memory":
+            prov.qkv(0, b, cfg["steps"] - 1)
+    if cfg["mode"] == "convkv":
+        for grp in ref.schedule(m)["memory"]:
+            for e in grp:
+                prov.qkv(0, e // cfg["frames"], cfg["steps"] - 1)
+    prov.qkv(0, m, 0)
+    H = cfg["heads"]
+    t0 = time.perf_counter()
+    sel = ref.selection(m) if cfg["mode"] != "convkv" else None
+    done = 0
+    while done < H:
+        if cfg["mode"] == "convkv":
+            ref.attend(m, 0, 0, heads=[done])
+        else:
+            ref.attend(m, 0, 0, heads=[done], selection=sel)
+        done += 1
+        if time.perf_counter() - t0 >= target_s:
+            break
+    dt = time.perf_counter() - t0
+    T = cfg["frames"] * cfg["grid_h"] * cfg["grid_w"]
+    try:
+        from threadpoolctl import threadpool_info
+        blas = max([p.get("num_threads", 1) for p in threadpool_info()] or [1])
+    except Exception:
+        blas = 1
+    return {"value": T * done / H / dt, "unit": "query tokens/s", "cores": int(blas),
+            "host_cpus": len(os.sched_getaffinity(0)), "kind": "oracle",
+            "sample": f"block {m} of the {cfg['name']} stream: retrieval + fp64 attention of {done}/{H} heads "
+                      f"x all {T} queries over {ref.attend.__self__.__class__.__name__} context, "
+                      f"{dt:.1f} s; value scaled to the whole block (x{H}/{done})"}
+
+
+def main():
+    args = parse()
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print(f"bench.py runs on one GPU only (asked for --gpus {args.gpus}, WORLD_SIZE {world}): "
+              "the bounded-KV path shards by heads across GPUs, which this build does not run.",
+              file=sys.stderr)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+    from bounded_kv_block_amd import bkv, synth
+
+    cfg = synth.workload(args.workload)
+    dev = torch.device("cuda", 0)
+    torch.cuda.set_device(dev)
+    T = synth.tokens_per_block(cfg)
+    H, D, L, S = cfg["heads"], cfg["head_dim"], cfg["layers"], cfg["steps"]
+    cache = bkv.Cache(cfg, dev)
+    if cfg["mode"] == "convkv":
+        for l in range(L):
+            wk, wv = synth.conv_weights(cfg, l)
+            cache.set_conv_weights(l, torch.from_numpy(wk).to(dev), torch.from_numpy(wv).to(dev))
+
+    # resident inputs: a pool of blocks per (layer, step), cycled by block id
+    pool = max(1, args.pool if L * S == 1 else 1)
+    inputs = {}
+    for b in range(pool):
+        for l in range(L):
+            for s in range(S):
+                inputs[(l, b, s)] = synth.qkv_device(cfg, l, b, s, dev)
+
+    def block_inputs(layer, block, step):
+        return inputs[(layer, block % pool, step)]
+
+    prefix = steady_block(cfg)
+    n_blocks = prefix + args.warmup + args.steps
+    poses_np = synth.poses(cfg, n_blocks)
+    poses = torch.from_numpy(poses_np).to(dev) if cfg["pose_dim"] else None
+    out = torch.empty((T, H, D), dtype=inputs[(0, 0, 0)][0].dtype, device=dev)
+
+    def step(m):
+        cache.retrieve(poses[m] if poses is not None else None)
+        for s in range(S):
+            for l in range(L):
+                q, k, v = block_inputs(l, m, s)
+                cache.attend(l, q, k, v, out)
+        cache.commit()
+
+    m = 0
+    for _ in range(prefix + args.warmup):          # fill the cache, then warm up
+        step(m)
+        m += 1
+    torch.cuda.synchronize()
+    n_keys = []
+    launches = args.steps * (2 + 2 * L * S + L) + 16
+    cache.profile_start(launches)
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps + 1)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        ev[i].record()
+        cache.retrieve(poses[m] if poses is not None else None)
+        n_keys.append(cache.stats()["n_keys"])
+        for s in range(S):
+            for l in range(L):
+                q, k, v = block_inputs(l, m, s)
+                cache.attend(l, q, k, v, out)
+        cache.commit()
+        m += 1
+    ev[-1].record()
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+    kt = cache.profile_stop()
+    wall = t1 - t0
+    per_block = np.array([ev[i].elapsed_time(ev[i + 1]) for i in range(args.steps)])
+
+    bf16 = cfg["dtype"] == "bf16"
+    Nk = int(np.median(n_keys))
+    flop_attend = 4.0 * H * T * Nk * D
+    attn_n, attn_ms, _ = kt["attention"]
+    attn_avg_ms = attn_ms / attn_n
+    attn_tflops = flop_attend / (attn_avg_ms * 1e-3) / 1e12
+    peak = PEAK_BF16_TFLOPS if bf16 else PEAK_FP32_TFLOPS
+    esz = 2 if bf16 else 4
+    kernels = {}
+    for name, (n, tot, mx) in kt.items():
+        kernels[name] = {"launches": int(n), "avg_us": 1e3 * tot / n, "max_us": 1e3 * mx}
+    # algorithmic bytes of the HBM-bound kernels, per launch
+    app_bytes = 4.0 * T * H * D * esz                       # K, V read token-major; written to the cache
+    kernels["append"]["gbs"] = app_bytes / (kernels["append"]["avg_us"] * 1e-6) / 1e9
+    if "gather" in kernels:
+        ctx_rows = Nk - T
+        g_bytes = 2.0 * ctx_rows * H * D * esz
+        kernels["gather"]["gbs"] = g_bytes / (kernels["gather"]["avg_us"] * 1e-6) / 1e9
+    if "conv" in kernels:
+        Tf = cfg["grid_h"] * cfg["grid_w"]
+        c_bytes = (2 * cfg["conv_kernel"] + 2) * cfg["memory_frames"] * Tf * H * D * esz
+        kernels["conv"]["gbs"] = c_bytes / (kernels["conv"]["avg_us"] * 1e-6) / 1e9
+
+    attends_per_step = L * S
+    value = args.steps * T / wall
+    res = {
+        "metric": METRIC,
+        "value": value,
+        "unit": "query tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": 1e3 * wall / args.steps,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16" if bf16 else "f32",
+        "data": "synthetic",
+        "config": {"workload": cfg["name"], "mode": cfg["mode"], "heads": H, "head_dim": D,
+                   "queries_per_block": T, "keys_per_block": Nk, "layers": L, "steps_per_block": S,
+                   "attends_per_block": attends_per_step, "window": cfg["window"],
+                   "dynamic_k": cfg["dynamic_k"], "bank": cfg["bank"], "rope": list(cfg["rope"]),
+                   "timed_blocks": [m - args.steps, m - 1]},
+        "attention_tflops": attn_tflops,
+        "attention_pct_peak": 100.0 * attn_tflops / peak,
+        "step_tflops": flop_attend * attends_per_step * args.steps / wall / 1e12,
+        "latency_ms": {"p50": float(np.percentile(per_block, 50)), "p99": float(np.percentile(per_block, 99)),
+                       "max": float(per_block.max())},
+        "kernels": kernels,
+        "roofline": {"kernel": "attention", "bound": "mfma" if bf16 else "alu", "achieved": attn_tflops,
+                     "peak": peak, "unit": "TFLOP/s", "frac": attn_tflops / peak, "traffic": None,
+                     "flop_per_launch": flop_attend, "avg_launch_us": 1e3 * attn_avg_ms},
+        "workspace_bytes": int(cache.stats()["workspace_bytes"]),
+    }
+    if not args.no_cpu_baseline:
+        res["cpu_baseline"] = cpu_baseline(cfg, block_inputs, poses_np, m - 1, args.cpu_seconds)
+    print(json.dumps(res), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,713 @@
+// C-ABI of the bounded-KV block attention library: config validation,
+// workspace layout, call-order state machine and kernel launches.
+// The operations follow the PR-Sink description (LiveAnimate page, section 方法)
+// and the ConvKV Memory description (SoulX-LiveAct page, section 技术内核); the
+// exported calls and their contracts are documented in include/bkv.h.
+#include "bkv.h"
+
+#include <hip/hip_runtime.h>
+
+#include <cmath>
+#include <cstdarg>
+#include <cstdio>
+#include <cstring>
+#include <new>
+#include <string>
+#include <vector>
+
+#include "kernels.hpp"
+#include "schedule.hpp"
+
+namespace {
+
+thread_local std::string g_err;
+
+bkv_status fail(bkv_status s, const char* fmt, ...) __attribute__((format(printf, 2, 3)));
+bkv_status fail(bkv_status s, const char* fmt, ...) {
+  char buf[512];
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(buf, sizeof(buf), fmt, ap);
+  va_end(ap);
+  g_err = buf;
+  return s;
+}
+
+size_t align_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
+
+struct Layout {
+  int T, Tpad, Tf, tf_pad, esize;
+  int n_slots, ctx_ld, mem_ld;
+  int t_rows;                        // rows of the temporal RoPE table
+  size_t slot_bytes, slot_v_off, layer_kv_bytes;
+  size_t off_kv, off_ctx, ctx_layer_bytes, off_mem, mem_layer_bytes, mem_v_off;
+  size_t off_pose, off_sel, off_tt, off_th, off_tw, off_w, total;
+};
+
+bkv_status validate(const bkv_config* c) {
+  if (!c) return fail(BKV_ERR_ARG, "null config");
+  if (c->struct_size != sizeof(bkv_config))
+    return fail(BKV_ERR_ARG, "config struct_size %u != %zu", c->struct_size, sizeof(bkv_config));
+  if (c->mode != BKV_PR_SINK && c->mode != BKV_CONVKV) return fail(BKV_ERR_ARG, "bad mode %d", c->mode);
+  if (c->dtype != BKV_F32 && c->dtype != BKV_BF16) return fail(BKV_ERR_ARG, "bad dtype %d", c->dtype);
+  if (c->layers < 1 || c->heads < 1) return fail(BKV_ERR_ARG, "layers and heads must be >= 1");
+  if (c->dtype == BKV_BF16 && c->head_dim != 128)
+    return fail(BKV_ERR_UNSUPPORTED, "bf16 path supports head_dim 128 (got %d)", c->head_dim);
+  if (c->dtype == BKV_F32 && c->head_dim != 64 && c->head_dim != 128)
+    return fail(BKV_ERR_UNSUPPORTED, "fp32 path supports head_dim 64 or 128 (got %d)", c->head_dim);
+  if (c->frames_per_block < 1 || c->grid_h < 1 || c->grid_w < 1)
+    return fail(BKV_ERR_ARG, "frames_per_block, grid_h, grid_w must be >= 1");
+  const long long T = (long long)c->frames_per_block * c->grid_h * c->grid_w;
+  if (T > (1 << 20)) return fail(BKV_ERR_ARG, "block of %lld tokens is too large", T);
+  if (c->window_blocks < 1 || c->window_blocks > 8) return fail(BKV_ERR_ARG, "window_blocks must be 1..8");
+  const int rs = c->rope_t + c->rope_h + c->rope_w;
+  if (c->rope_t < 0 || c->rope_h < 0 || c->rope_w < 0 || (c->rope_t | c->rope_h | c->rope_w) & 1 ||
+      (rs != 0 && rs != c->head_dim))
+    return fail(BKV_ERR_ARG, "RoPE split must be even parts summing to head_dim (or all 0)");
+  if (rs != 0 && !(c->rope_theta > 0.0)) return fail(BKV_ERR_ARG, "rope_theta must be > 0");
+  if (c->softmax_scale < 0.f || !std::isfinite(c->softmax_scale))
+    return fail(BKV_ERR_ARG, "softmax_scale must be finite and >= 0");
+  if (c->mode == BKV_PR_SINK) {
+    if (c->static_blocks < 0 || c->static_blocks > 1) return fail(BKV_ERR_ARG, "static_blocks must be 0 or 1");
+    if (c->dynamic_k < 0 || c->dynamic_k > bkv::kMaxK) return fail(BKV_ERR_ARG, "dynamic_k must be 0..%d", bkv::kMaxK);
+    if (c->bank_blocks < 0 || c->bank_blocks > bkv::kMaxBank)
+      return fail(BKV_ERR_ARG, "bank_blocks must be 0..%d", bkv::kMaxBank);
+    if (c->dynamic_k > 0 && (c->pose_dim < 1 || c->pose_dim > 1024))
+      return fail(BKV_ERR_ARG, "pose_dim must be 1..1024 when dynamic_k > 0");
+    if (c->pose_dim < 0) return fail(BKV_ERR_ARG, "pose_dim must be >= 0");
+  } else {
+    if (c->static_blocks != 0 || c->dynamic_k != 0 || c->bank_blocks != 0)
+      return fail(BKV_ERR_ARG, "ConvKV takes no static/dynamic sinks or bank");
+    if (c->conv_kernel < 1 || c->conv_kernel > 8 || c->conv_stride != c->conv_kernel)
+      return fail(BKV_ERR_UNSUPPORTED, "ConvKV needs conv_stride == conv_kernel in 1..8");
+    if (c->memory_frames < 1 || c->memory_frames > 4) return fail(BKV_ERR_ARG, "memory_frames must be 1..4");
+    if (c->conv_kernel * c->memory_frames > bkv::kMaxTaps) return fail(BKV_ERR_ARG, "too many conv taps");
+  }
+  return BKV_OK;
+}
+
+bkv::Schedule::Shape shape_of(const bkv_config* c) {
+  bkv::Schedule::Shape s;
+  s.convkv = c->mode == BKV_CONVKV;
+  s.layers = c->layers;
+  s.frames = c->frames_per_block;
+  s.tokens_per_frame = c->grid_h * c->grid_w;
+  s.window = c->window_blocks;
+  s.statics = s.convkv ? 0 : c->static_blocks;
+  s.k = s.convkv ? 0 : c->dynamic_k;
+  s.bank = s.convkv ? 0 : c->bank_blocks;
+  s.kernel = s.convkv ? c->conv_kernel : 1;
+  s.memory_frames = s.convkv ? c->memory_frames : 0;
+  return s;
+}
+
+Layout layout_of(const bkv_config* c, const bkv::Schedule& sch) {
+  Layout L{};
+  const size_t H = c->heads, D = c->head_dim;
+  L.esize = c->dtype == BKV_BF16 ? 2 : 4;
+  L.T = sch.tokens();
+  L.Tpad = (int)align_up(L.T, bkv::kTokAlign);
+  L.Tf = c->grid_h * c->grid_w;
+  L.tf_pad = (int)align_up(L.Tf, bkv::kTokAlign);
+  L.n_slots = sch.n_slots();
+  L.slot_v_off = H * L.Tpad * D * L.esize;
+  L.slot_bytes = 2 * L.slot_v_off;
+  L.layer_kv_bytes = L.slot_bytes * L.n_slots;
+  size_t off = 0;
+  L.off_kv = off;
+  off = align_up(off + L.layer_kv_bytes * c->layers, 256);
+  L.off_ctx = off;
+  L.off_mem = off;
+  if (c->mode == BKV_CONVKV) {
+    L.ctx_ld = (int)align_up(sch.max_context_tokens(), bkv::kTokAlign);
+    L.ctx_layer_bytes = align_up(H * L.ctx_ld * D * L.esize, 256);
+    off = align_up(off + L.ctx_layer_bytes * c->layers, 256);
+    L.off_mem = off;
+    L.mem_ld = L.tf_pad * c->memory_frames;
+    L.mem_v_off = H * L.mem_ld * D * L.esize;
+    L.mem_layer_bytes = align_up(2 * L.mem_v_off, 256);
+    off = align_up(off + L.mem_layer_bytes * c->layers, 256);
+  }
+  L.off_pose = off;
+  const int P = (c->mode == BKV_PR_SINK) ? c->pose_dim : 0;
+  off = align_up(off + sizeof(float) * (size_t)L.n_slots * (P > 0 ? P : 1), 256);
+  L.off_sel = off;
+  off = align_up(off + 2 * sizeof(int) * bkv::kMaxK, 256);
+  L.t_rows = c->mode == BKV_CONVKV ? sch.max_context_frames() : c->frames_per_block;
+  L.off_tt = off;
+  off = align_up(off + sizeof(float2) * (size_t)L.t_rows * (c->rope_t / 2 + 1), 256);
+  L.off_th = off;
+  off = align_up(off + sizeof(float2) * (size_t)c->grid_h * (c->rope_h / 2 + 1), 256);
+  L.off_tw = off;
+  off = align_up(off + sizeof(float2) * (size_t)c->grid_w * (c->rope_w / 2 + 1), 256);
+  L.off_w = off;
+  if (c->mode == BKV_CONVKV) off = align_up(off + sizeof(float) * 2 * c->layers * H * D * c->conv_kernel, 256);
+  L.total = off;
+  return L;
+}
+
+}  // namespace
+
+struct bkv_cache_s {
+  bkv_config cfg;
+  bkv::Schedule sched;
+  Layout L;
+  char* ws;
+  int device;
+  bool error = false;
+  std::vector<bool> ctx_ready;      // ConvKV: context K of the layer gathered for the open block
+  std::vector<bool> weights_set;    // ConvKV: conv weights given per layer
+  struct Prof {                     // per-launch HIP event pairs (bkv_profile_start/stop)
+    bool on = false;
+    int cap = 0, used = 0;
+    std::vector<hipEvent_t> ev;
+    std::vector<int> tag;
+  } prof;
+
+  bkv_cache_s(const bkv_config& c, char* w)
+      : cfg(c), sched(shape_of(&c)), ws(w), device(0) {
+    L = layout_of(&c, sched);
+    ctx_ready.assign(c.layers, false);
+    weights_set.assign(c.layers, false);
+  }
+
+  bool bf16() const { return cfg.dtype == BKV_BF16; }
+  bool convkv() const { return cfg.mode == BKV_CONVKV; }
+  char* layer_kv(int l) const { return ws + L.off_kv + L.layer_kv_bytes * l; }
+  char* slot_k(int l, int s) const { return layer_kv(l) + L.slot_bytes * s; }
+  char* slot_vt(int l, int s) const { return slot_k(l, s) + L.slot_v_off; }
+  char* ctx_k(int l) const { return ws + L.off_ctx + L.ctx_layer_bytes * l; }
+  char* mem_k(int l) const { return ws + L.off_mem + L.mem_layer_bytes * l; }
+  char* mem_vt(int l) const { return mem_k(l) + L.mem_v_off; }
+  float* pose_store() const { return reinterpret_cast<float*>(ws + L.off_pose); }
+  int* sel_ids() const { return reinterpret_cast<int*>(ws + L.off_sel); }
+  int* sel_slots() const { return sel_ids() + bkv::kMaxK; }
+  float2* ttab() const { return reinterpret_cast<float2*>(ws + L.off_tt); }
+  float2* htab() const { return reinterpret_cast<float2*>(ws + L.off_th); }
+  float2* wtab() const { return reinterpret_cast<float2*>(ws + L.off_tw); }
+  float* conv_w(int l, int which) const {
+    const size_t n = (size_t)cfg.heads * cfg.head_dim * cfg.conv_kernel;
+    return reinterpret_cast<float*>(ws + L.off_w) + (2 * (size_t)l + which) * n;
+  }
+  long long slot_k_hs() const { return (long long)L.Tpad * cfg.head_dim; }
+  long long slot_v_hs() const { return (long long)L.Tpad * cfg.head_dim; }
+
+  bkv::Rope rope() const {
+    bkv::Rope r;
+    r.t = ttab();
+    r.h = htab();
+    r.w = wtab();
+    r.dt = cfg.rope_t;
+    r.dh = cfg.rope_h;
+    r.dw = cfg.rope_w;
+    r.grid_h = cfg.grid_h;
+    r.grid_w = cfg.grid_w;
+    return r;
+  }
+
+  // attention view of context segment i of the open block at layer l
+  bkv::Seg seg_arg(int l, const bkv::SegPlan& p) const {
+    bkv::Seg g{};
+    g.n = p.tokens;
+    g.dyn = p.dyn;
+    if (p.dyn >= 0) return g;
+    if (!convkv()) {
+      g.k = slot_k(l, p.slot);
+      g.v = slot_vt(l, p.slot);
+      g.k_hs = slot_k_hs();
+      g.v_hs = slot_v_hs();
+      g.v_ld = L.Tpad;
+    } else {
+      g.k = ctx_k(l) + (size_t)p.ctx_off * cfg.head_dim * L.esize;
+      g.k_hs = (long long)L.ctx_ld * cfg.head_dim;
+      if (p.kind == bkv::SEG_MEMORY) {
+        g.v = mem_vt(l) + (size_t)p.id * L.tf_pad * L.esize;
+        g.v_hs = (long long)L.mem_ld * cfg.head_dim;
+        g.v_ld = L.mem_ld;
+      } else {
+        g.v = slot_vt(l, p.slot);
+        g.v_hs = slot_v_hs();
+        g.v_ld = L.Tpad;
+      }
+    }
+    return g;
+  }
+};
+
+namespace {
+
+void profile_release(bkv_cache h) {
+  for (hipEvent_t e : h->prof.ev)
+    if (e) (void)hipEventDestroy(e);
+  h->prof = bkv_cache_s::Prof{};
+}
+
+bkv_status check_handle(bkv_cache h, bool need_ok = true) {
+  if (!h) return fail(BKV_ERR_ARG, "null handle");
+  if (need_ok && h->error) return fail(BKV_ERR_STATE, "handle is in error state; call bkv_reset");
+  return BKV_OK;
+}
+
+enum { K_RETRIEVE = 0, K_APPEND, K_ATTENTION, K_GATHER, K_CONV, K_EXPORT, K_COUNT };
+const char* const kKernelNames[K_COUNT] = {"retrieve", "append", "attention", "gather", "conv", "export"};
+
+// Run `launch`, bracketed by event records on `s` while a profile is recording.
+template <class F>
+hipError_t timed(bkv_cache h, int tag, hipStream_t s, F&& launch) {
+  auto& p = h->prof;
+  const bool rec = p.on && p.used < p.cap;
+  if (rec) (void)hipEventRecord(p.ev[2 * p.used], s);
+  hipError_t e = launch();
+  if (rec) {
+    (void)hipEventRecord(p.ev[2 * p.used + 1], s);
+    p.tag[p.used++] = tag;
+  }
+  return e;
+}
+
+bkv_status device_fail(bkv_cache h, hipError_t e, const char* what) {
+  h->error = true;
+  return fail(BKV_ERR_DEVICE, "%s: %s", what, hipGetErrorString(e));
+}
+
+bkv_status set_device(bkv_cache h) {
+  int cur = -1;
+  hipError_t e = hipGetDevice(&cur);
+  if (e != hipSuccess) return device_fail(h, e, "hipGetDevice");
+  if (cur != h->device) {
+    e = hipSetDevice(h->device);
+    if (e != hipSuccess) return device_fail(h, e, "hipSetDevice");
+  }
+  return BKV_OK;
+}
+
+// ConvKV: rotate memory + window K of layer l into the context-K buffer.
+bkv_status gather_context(bkv_cache h, int l, hipStream_t stream) {
+  bkv::GatherArgs g{};
+  g.dst = h->ctx_k(l);
+  g.dst_hs = (long long)h->L.ctx_ld * h->cfg.head_dim;
+  g.H = h->cfg.heads;
+  g.D = h->cfg.head_dim;
+  g.rope = h->rope();
+  for (const auto& p : h->sched.segments()) {
+    if (p.kind == bkv::SEG_CURRENT) continue;
+    bkv::GatherPart& gp = g.part[g.nparts++];
+    if (p.kind == bkv::SEG_MEMORY) {
+      gp.src = h->mem_k(l) + (size_t)p.id * h->L.tf_pad * h->cfg.head_dim * h->L.esize;
+      gp.src_hs = (long long)h->L.mem_ld * h->cfg.head_dim;
+    } else {
+      gp.src = h->slot_k(l, p.slot);
+      gp.src_hs = h->slot_k_hs();
+    }
+    gp.dst_off = p.ctx_off;
+    gp.n = p.tokens;
+    gp.t_row0 = (int)p.t0;
+    if (gp.n > g.max_n) g.max_n = gp.n;
+  }
+  hipError_t e = timed(h, K_GATHER, stream, [&] { return bkv::launch_gather(g, h->bf16(), stream); });
+  if (e != hipSuccess) return device_fail(h, e, "gather launch");
+  h->ctx_ready[l] = true;
+  return BKV_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* bkv_status_str(bkv_status s) {
+  switch (s) {
+    case BKV_OK: return "BKV_OK";
+    case BKV_ERR_ARG: return "BKV_ERR_ARG";
+    case BKV_ERR_STATE: return "BKV_ERR_STATE";
+    case BKV_ERR_WORKSPACE: return "BKV_ERR_WORKSPACE";
+    case BKV_ERR_DEVICE: return "BKV_ERR_DEVICE";
+    case BKV_ERR_UNSUPPORTED: return "BKV_ERR_UNSUPPORTED";
+  }
+  return "BKV_ERR_UNKNOWN";
+}
+
+const char* bkv_last_error(void) { return g_err.c_str(); }
+
+bkv_status bkv_workspace_size(const bkv_config* cfg, size_t* bytes) {
+  if (!bytes) return fail(BKV_ERR_ARG, "null bytes");
+  bkv_status st = validate(cfg);
+  if (st != BKV_OK) return st;
+  bkv::Schedule sch(shape_of(cfg));
+  *bytes = layout_of(cfg, sch).total;
+  return BKV_OK;
+}
+
+bkv_status bkv_create(const bkv_config* cfg, void* workspace, size_t bytes, hipStream_t stream,
+                      bkv_cache* out) {
+  if (!out) return fail(BKV_ERR_ARG, "null out");
+  *out = nullptr;
+  bkv_status st = validate(cfg);
+  if (st != BKV_OK) return st;
+  size_t need = 0;
+  bkv_workspace_size(cfg, &need);
+  if (!workspace) return fail(BKV_ERR_WORKSPACE, "null workspace");
+  if (bytes < need) return fail(BKV_ERR_WORKSPACE, "workspace %zu < needed %zu bytes", bytes, need);
+  if (reinterpret_cast<uintptr_t>(workspace) % 256 != 0)
+    return fail(BKV_ERR_WORKSPACE, "workspace must be 256-byte aligned");
+  bkv_cache h = new (std::nothrow) bkv_cache_s(*cfg, static_cast<char*>(workspace));
+  if (!h) return fail(BKV_ERR_ARG, "out of host memory");
+  hipError_t e = hipGetDevice(&h->device);
+  if (e != hipSuccess) {
+    delete h;
+    return fail(BKV_ERR_DEVICE, "hipGetDevice: %s", hipGetErrorString(e));
+  }
+  const double theta = cfg->rope_theta;
+  if (cfg->rope_h) e = bkv::launch_rope_table(h->htab(), cfg->grid_h, cfg->rope_h, 0, theta, stream);
+  if (e == hipSuccess && cfg->rope_w)
+    e = bkv::launch_rope_table(h->wtab(), cfg->grid_w, cfg->rope_w, 0, theta, stream);
+  if (e == hipSuccess && cfg->rope_t && h->convkv())
+    e = bkv::launch_rope_table(h->ttab(), h->L.t_rows, cfg->rope_t, 0, theta, stream);
+  if (e != hipSuccess) {
+    delete h;
+    return fail(BKV_ERR_DEVICE, "RoPE table launch: %s", hipGetErrorString(e));
+  }
+  *out = h;
+  return BKV_OK;
+}
+
+bkv_status bkv_destroy(bkv_cache h) {
+  if (!h) return fail(BKV_ERR_ARG, "null handle");
+  profile_release(h);
+  delete h;
+  return BKV_OK;
+}
+
+bkv_status bkv_reset(bkv_cache h) {
+  if (!h) return fail(BKV_ERR_ARG, "null handle");
+  h->sched.reset();
+  h->error = false;
+  h->ctx_ready.assign(h->cfg.layers, false);
+  return BKV_OK;
+}
+
+bkv_status bkv_set_conv_weights(bkv_cache h, int32_t layer, const float* wk, const float* wv,
+                                hipStream_t stream) {
+  bkv_status st = check_handle(h);
+  if (st != BKV_OK) return st;
+  if (!h->convkv()) return fail(BKV_ERR_UNSUPPORTED, "conv weights on a PR-Sink handle");
+  if (layer < 0 || layer >= h->cfg.layers) return fail(BKV_ERR_ARG, "layer %d out of range", layer);
+  if (!wk || !wv) return fail(BKV_ERR_ARG, "null weights");
+  if ((st = set_device(h)) != BKV_OK) return st;
+  const size_t n = sizeof(float) * h->cfg.heads * h->cfg.head_dim * h->cfg.conv_kernel;
+  hipError_t e = hipMemcpyAsync(h->conv_w(layer, 0), wk, n, hipMemcpyDeviceToDevice, stream);
+  if (e == hipSuccess) e = hipMemcpyAsync(h->conv_w(layer, 1), wv, n, hipMemcpyDeviceToDevice, stream);
+  if (e != hipSuccess) return device_fail(h, e, "conv weight copy");
+  h->weights_set[layer] = true;
+  return BKV_OK;
+}
+
+bkv_status bkv_retrieve(bkv_cache h, const float* pose, hipStream_t stream) {
+  bkv_status st = check_handle(h);
+  if (st != BKV_OK) return st;
+  if (h->sched.is_open()) return fail(BKV_ERR_STATE, "block %lld is already open", (long long)h->sched.block());
+  const bool prsink = !h->convkv();
+  const bool needs_pose = prsink && h->cfg.dynamic_k > 0;
+  if (needs_pose && !pose) return fail(BKV_ERR_ARG, "null pose");
+  if (h->convkv()) {
+    for (int l = 0; l < h->cfg.layers; ++l)
+      if (!h->weights_set[l]) return fail(BKV_ERR_STATE, "conv weights of layer %d not set", l);
+  }
+  if ((st = set_device(h)) != BKV_OK) return st;
+  if (!h->sched.open()) return fail(BKV_ERR_STATE, "no free slot (internal)");
+  h->ctx_ready.assign(h->cfg.layers, false);
+  if (prsink) {
+    bkv::OpenArgs a{};
+    a.pose_in = needs_pose ? pose : nullptr;
+    a.pose_store = h->pose_store();
+    a.P = h->cfg.pose_dim;
+    a.cur_slot = h->sched.cur_slot();
+    a.k = h->sched.n_dynamic();
+    a.nbank = a.k > 0 ? (int)h->sched.bank().size() : 0;
+    for (int i = 0; i < a.nbank; ++i) {
+      a.bank_id[i] = (int)h->sched.bank()[i].first;
+      a.bank_slot[i] = h->sched.bank()[i].second;
+    }
+    a.sel_ids = h->sel_ids();
+    a.sel_slots = h->sel_slots();
+    if (h->cfg.rope_t) {
+      a.ttab = h->ttab();
+      a.t_rows = h->cfg.frames_per_block;
+      a.t_dim = h->cfg.rope_t;
+      a.t_pos0 = h->sched.block() * h->cfg.frames_per_block;
+      a.theta = h->cfg.rope_theta;
+    }
+    if (a.pose_in || a.ttab || a.k > 0) {
+      hipError_t e = timed(h, K_RETRIEVE, stream, [&] { return bkv::launch_open(a, stream); });
+      if (e != hipSuccess) return device_fail(h, e, "retrieval launch");
+    }
+  }
+  return BKV_OK;
+}
+
+bkv_status bkv_attend(bkv_cache h, int32_t layer, const void* q, const void* k, const void* v,
+                      void* out, hipStream_t stream) {
+  bkv_status st = check_handle(h);
+  if (st != BKV_OK) return st;
+  if (!h->sched.is_open()) return fail(BKV_ERR_STATE, "attend with no open block");
+  if (layer < 0 || layer >= h->cfg.layers) return fail(BKV_ERR_ARG, "layer %d out of range", layer);
+  if (!q || !k || !v || !out) return fail(BKV_ERR_ARG, "null q/k/v/out");
+  if (out == q || out == k || out == v) return fail(BKV_ERR_ARG, "out aliases an input");
+  if ((st = set_device(h)) != BKV_OK) return st;
+  const auto& segs = h->sched.segments();
+  const bkv::SegPlan& cur = segs.back();
+  const int D = h->cfg.head_dim;
+
+  bkv::AppendArgs ap{};
+  ap.k_in = k;
+  ap.v_in = v;
+  ap.T = h->L.T;
+  ap.H = h->cfg.heads;
+  ap.D = D;
+  ap.rope = h->rope();
+  ap.vt = h->slot_vt(layer, cur.slot);
+  ap.vt_hs = h->slot_v_hs();
+  ap.vt_ld = h->L.Tpad;
+  if (!h->convkv()) {
+    ap.k_rot = h->slot_k(layer, cur.slot);
+    ap.k_rot_hs = h->slot_k_hs();
+    ap.k_rot_off = 0;
+    ap.t_row0 = 0;
+  } else {
+    ap.k_raw = h->slot_k(layer, cur.slot);
+    ap.k_raw_hs = h->slot_k_hs();
+    ap.k_rot = h->ctx_k(layer);
+    ap.k_rot_hs = (long long)h->L.ctx_ld * D;
+    ap.k_rot_off = cur.ctx_off;
+    ap.t_row0 = (int)cur.t0;
+  }
+  hipError_t e = timed(h, K_APPEND, stream, [&] { return bkv::launch_append(ap, h->bf16(), stream); });
+  if (e != hipSuccess) return device_fail(h, e, "append launch");
+  if (h->convkv() && !h->ctx_ready[layer]) {
+    if ((st = gather_context(h, layer, stream)) != BKV_OK) return st;
+  }
+
+  bkv::AttnArgs a{};
+  a.q = q;
+  a.out = out;
+  a.T = h->L.T;
+  a.H = h->cfg.heads;
+  a.D = D;
+  a.t_row0 = h->convkv() ? (int)cur.t0 : 0;
+  const float scale = h->cfg.softmax_scale > 0.f ? h->cfg.softmax_scale : 1.0f / std::sqrt((float)D);
+  a.qscale = h->bf16() ? scale * 1.4426950408889634f : scale;
+  a.rope = h->rope();
+  a.sel_slots = h->sel_slots();
+  a.slot_base = h->layer_kv(layer);
+  a.slot_bytes = (long long)h->L.slot_bytes;
+  a.slot_v_off = (long long)h->L.slot_v_off;
+  a.slot_k_hs = h->slot_k_hs();
+  a.slot_v_hs = h->slot_v_hs();
+  a.slot_v_ld = h->L.Tpad;
+  a.nseg = (int)segs.size();
+  for (int i = 0; i < a.nseg; ++i) a.seg[i] = h->seg_arg(layer, segs[i]);
+  e = timed(h, K_ATTENTION, stream, [&] { return bkv::launch_attention(a, h->bf16(), stream); });
+  if (e != hipSuccess) return device_fail(h, e, "attention launch");
+  h->sched.mark_attended(layer);
+  return BKV_OK;
+}
+
+bkv_status bkv_commit(bkv_cache h, hipStream_t stream) {
+  bkv_status st = check_handle(h);
+  if (st != BKV_OK) return st;
+  if (!h->sched.is_open()) return fail(BKV_ERR_STATE, "commit with no open block");
+  if (!h->sched.all_attended()) return fail(BKV_ERR_STATE, "commit before every layer was attended");
+  if ((st = set_device(h)) != BKV_OK) return st;
+  std::vector<bkv::ConvTap> taps;
+  h->sched.commit(&taps);
+  h->ctx_ready.assign(h->cfg.layers, false);
+  if (!taps.empty()) {
+    const int K = h->cfg.conv_kernel;
+    const int n_mem = (int)taps.size() / K;
+    const size_t esz = h->L.esize, D = h->cfg.head_dim;
+    for (int l = 0; l < h->cfg.layers; ++l) {
+      bkv::ConvArgs c{};
+      for (size_t i = 0; i < taps.size(); ++i) {
+        const size_t tok0 = (size_t)taps[i].frame * h->L.Tf;
+        c.k_src[i] = h->slot_k(l, taps[i].slot) + tok0 * D * esz;
+        c.vt_src[i] = h->slot_vt(l, taps[i].slot) + tok0 * esz;
+      }
+      c.k_hs = h->slot_k_hs();
+      c.vt_hs = h->slot_v_hs();
+      c.vt_ld = h->L.Tpad;
+      c.k_mem = h->mem_k(l);
+      c.k_mem_hs = (long long)h->L.mem_ld * D;
+      c.vt_mem = h->mem_vt(l);
+      c.vt_mem_hs = (long long)h->L.mem_ld * D;
+      c.vt_mem_ld = h->L.mem_ld;
+      c.wk = h->conv_w(l, 0);
+      c.wv = h->conv_w(l, 1);
+      c.H = h->cfg.heads;
+      c.D = (int)D;
+      c.Tf = h->L.Tf;
+      c.tf_pad = h->L.tf_pad;
+      c.kernel = K;
+      c.n_mem = n_mem;
+      hipError_t e = timed(h, K_CONV, stream, [&] { return bkv::launch_conv(c, h->bf16(), stream); });
+      if (e != hipSuccess) return device_fail(h, e, "conv launch");
+    }
+  }
+  return BKV_OK;
+}
+
+bkv_status bkv_selection(bkv_cache h, int32_t* ids, int32_t cap, int32_t* n, hipStream_t stream) {
+  bkv_status st = check_handle(h);
+  if (st != BKV_OK) return st;
+  if (!n) return fail(BKV_ERR_ARG, "null n");
+  if (!h->sched.is_open()) return fail(BKV_ERR_STATE, "no open block");
+  const int k = h->sched.n_dynamic();
+  if (k > 0 && (!ids || cap < k)) return fail(BKV_ERR_ARG, "ids capacity %d < %d", cap, k);
+  *n = k;
+  if (k == 0) return BKV_OK;
+  if ((st = set_device(h)) != BKV_OK) return st;
+  hipError_t e = hipMemcpyAsync(ids, h->sel_ids(), sizeof(int) * k, hipMemcpyDeviceToHost, stream);
+  if (e == hipSuccess) e = hipStreamSynchronize(stream);
+  if (e != hipSuccess) return device_fail(h, e, "selection copy");
+  return BKV_OK;
+}
+
+bkv_status bkv_context(bkv_cache h, bkv_segment* segs, int32_t cap, int32_t* n, hipStream_t stream) {
+  bkv_status st = check_handle(h, false);
+  if (st != BKV_OK) return st;
+  if (!n) return fail(BKV_ERR_ARG, "null n");
+  const auto& plan = h->sched.segments();
+  *n = (int)plan.size();
+  if (plan.empty()) return BKV_OK;
+  if (!segs || cap < (int)plan.size()) return fail(BKV_ERR_ARG, "segment capacity %d < %zu", cap, plan.size());
+  int ids[bkv::kMaxK] = {0};
+  const int k = h->sched.n_dynamic();
+  if (k > 0) {
+    int got = 0;
+    if ((st = bkv_selection(h, ids, bkv::kMaxK, &got, stream)) != BKV_OK) return st;
+  }
+  for (size_t i = 0; i < plan.size(); ++i) {
+    const auto& p = plan[i];
+    segs[i].kind = p.kind;
+    segs[i].tokens = p.tokens;
+    if (p.dyn >= 0) {
+      segs[i].id = ids[p.dyn];
+      segs[i].t0 = ids[p.dyn] * h->cfg.frames_per_block;
+    } else {
+      segs[i].id = (int32_t)p.id;
+      segs[i].t0 = (int32_t)p.t0;
+    }
+  }
+  return BKV_OK;
+}
+
+bkv_status bkv_stats(bkv_cache h, bkv_stats_t* out) {
+  if (!h || !out) return fail(BKV_ERR_ARG, "null handle or out");
+  out->block = h->sched.block();
+  out->open = h->sched.is_open() ? 1 : 0;
+  out->n_segments = (int32_t)h->sched.segments().size();
+  out->n_keys = h->sched.context_tokens();
+  out->last_evicted = h->sched.last_evicted();
+  out->bank_count = (int32_t)h->sched.bank().size();
+  out->memory_count = h->sched.memory_count();
+  out->workspace_bytes = h->L.total;
+  return BKV_OK;
+}
+
+bkv_status bkv_export_segment(bkv_cache h, int32_t layer, int32_t seg, void* k_out, void* v_out,
+                              hipStream_t stream) {
+  bkv_status st = check_handle(h);
+  if (st != BKV_OK) return st;
+  if (!h->sched.is_open()) return fail(BKV_ERR_STATE, "no open block");
+  if (layer < 0 || layer >= h->cfg.layers) return fail(BKV_ERR_ARG, "layer %d out of range", layer);
+  const auto& segs = h->sched.segments();
+  if (seg < 0 || seg >= (int)segs.size()) return fail(BKV_ERR_ARG, "segment %d out of range", seg);
+  if (!k_out || !v_out) return fail(BKV_ERR_ARG, "null output");
+  const auto& p = segs[seg];
+  if (p.kind == bkv::SEG_CURRENT && !h->sched.attended(layer))
+    return fail(BKV_ERR_STATE, "current block of layer %d not written yet", layer);
+  if ((st = set_device(h)) != BKV_OK) return st;
+  if (h->convkv() && !h->ctx_ready[layer]) {
+    if ((st = gather_context(h, layer, stream)) != BKV_OK) return st;
+  }
+  bkv::ExportArgs a{};
+  a.seg = h->seg_arg(layer, p);
+  a.sel_slots = h->sel_slots();
+  a.slot_base = h->layer_kv(layer);
+  a.slot_bytes = (long long)h->L.slot_bytes;
+  a.slot_v_off = (long long)h->L.slot_v_off;
+  a.slot_k_hs = h->slot_k_hs();
+  a.slot_v_hs = h->slot_v_hs();
+  a.slot_v_ld = h->L.Tpad;
+  a.k_out = k_out;
+  a.v_out = v_out;
+  a.H = h->cfg.heads;
+  a.D = h->cfg.head_dim;
+  hipError_t e = timed(h, K_EXPORT, stream, [&] { return bkv::launch_export(a, h->bf16(), stream); });
+  if (e != hipSuccess) return device_fail(h, e, "export launch");
+  return BKV_OK;
+}
+
+bkv_status bkv_profile_start(bkv_cache h, int32_t max_launches) {
+  if (!h) return fail(BKV_ERR_ARG, "null handle");
+  if (h->prof.on) return fail(BKV_ERR_STATE, "a profile is already recording");
+  if (max_launches < 1) return fail(BKV_ERR_ARG, "max_launches must be >= 1");
+  bkv_status st = set_device(h);
+  if (st != BKV_OK) return st;
+  h->prof.ev.assign(2 * (size_t)max_launches, nullptr);
+  h->prof.tag.assign(max_launches, -1);
+  for (auto& e : h->prof.ev) {
+    hipError_t r = hipEventCreate(&e);
+    if (r != hipSuccess) {
+      profile_release(h);
+      return fail(BKV_ERR_DEVICE, "hipEventCreate: %s", hipGetErrorString(r));
+    }
+  }
+  h->prof.cap = max_launches;
+  h->prof.used = 0;
+  h->prof.on = true;
+  return BKV_OK;
+}
+
+bkv_status bkv_profile_stop(bkv_cache h, bkv_kernel_time* out, int32_t cap, int32_t* n) {
+  if (!h || !n) return fail(BKV_ERR_ARG, "null handle or n");
+  if (!h->prof.on) return fail(BKV_ERR_STATE, "no profile is recording");
+  double tot[K_COUNT] = {0}, mx[K_COUNT] = {0};
+  int64_t cnt[K_COUNT] = {0};
+  bkv_status st = set_device(h);
+  if (st != BKV_OK) {
+    profile_release(h);
+    return st;
+  }
+  auto& p = h->prof;
+  if (p.used > 0) {
+    hipError_t r = hipEventSynchronize(p.ev[2 * p.used - 1]);
+    if (r != hipSuccess) {
+      profile_release(h);
+      return fail(BKV_ERR_DEVICE, "hipEventSynchronize: %s", hipGetErrorString(r));
+    }
+  }
+  for (int i = 0; i < p.used; ++i) {
+    float ms = 0.f;
+    if (hipEventElapsedTime(&ms, p.ev[2 * i], p.ev[2 * i + 1]) != hipSuccess) continue;
+    tot[p.tag[i]] += ms;
+    if (ms > mx[p.tag[i]]) mx[p.tag[i]] = ms;
+    cnt[p.tag[i]]++;
+  }
+  profile_release(h);
+  int k = 0;
+  for (int t = 0; t < K_COUNT; ++t) k += cnt[t] > 0;
+  *n = k;
+  if (k > cap || (k > 0 && !out)) return fail(BKV_ERR_ARG, "capacity %d < %d kernels", cap, k);
+  int j = 0;
+  for (int t = 0; t < K_COUNT; ++t) {
+    if (!cnt[t]) continue;
+    std::memset(&out[j], 0, sizeof(bkv_kernel_time));
+    std::snprintf(out[j].kernel, sizeof(out[j].kernel), "%s", kKernelNames[t]);
+    out[j].launches = cnt[t];
+    out[j].total_ms = tot[t];
+    out[j].max_ms = mx[t];
+    ++j;
+  }
+  return BKV_OK;
+}
+
+}  // extern "C"

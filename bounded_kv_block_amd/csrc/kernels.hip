@@ -1,0 +1,802 @@
+// gfx950 kernels of the bounded-KV block attention path.
+//
+//   rope_table_kernel  (cos, sin) tables of the 3D RoPE, computed in fp64
+//   open_kernel        block open: store the pose, cosine top-k over the bank
+//                      (fp64, one wavefront, ties to the lower stream id), and
+//                      the current block's temporal RoPE rows
+//   append_kernel      K with fused 3D RoPE -> cache rows; V -> cache V^T
+//   attn_bf16_kernel   flash attention on bf16 MFMA (32x32x16), K/V tiles
+//                      staged in LDS, online softmax in fp32
+//   attn_f32_kernel    the same contraction in fp32 on the vector ALUs
+//   gather_kernel      ConvKV: raw K of memory + window -> context-K rows,
+//                      rotated at context positions
+//   conv_kernel        ConvKV: depthwise temporal conv of evicted frames
+//   export_kernel      inspection copy of one context segment
+#include <math.h>
+#include <stdint.h>
+
+#include "kernels.hpp"
+
+namespace bkv {
+namespace {
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+
+__device__ __forceinline__ float to_f(float x) { return x; }
+__device__ __forceinline__ float to_f(__bf16 x) { return (float)x; }
+template <typename T> __device__ __forceinline__ T from_f(float x);
+template <> __device__ __forceinline__ float from_f<float>(float x) { return x; }
+template <> __device__ __forceinline__ __bf16 from_f<__bf16>(float x) { return (__bf16)x; }
+
+// Rotate the channel pair (ch, ch+1) of a token at (t-table row, y, x).
+__device__ __forceinline__ void rope_pair(float& u0, float& u1, int ch, const Rope& r, int trow,
+                                          int y, int x) {
+  float2 cs;
+  if (ch < r.dt) {
+    cs = r.t[trow * (r.dt >> 1) + (ch >> 1)];
+  } else if (ch < r.dt + r.dh) {
+    cs = r.h[y * (r.dh >> 1) + ((ch - r.dt) >> 1)];
+  } else {
+    cs = r.w[x * (r.dw >> 1) + ((ch - r.dt - r.dh) >> 1)];
+  }
+  const float a = u0 * cs.x - u1 * cs.y;
+  const float b = u0 * cs.y + u1 * cs.x;
+  u0 = a;
+  u1 = b;
+}
+
+__device__ __forceinline__ bool has_rope(const Rope& r) { return (r.dt + r.dh + r.dw) != 0; }
+
+// token index within a block -> (frame, y, x)
+__device__ __forceinline__ void token_fyx(int tok, int gh, int gw, int& f, int& y, int& x) {
+  const int per = gh * gw;
+  f = tok / per;
+  const int rem = tok - f * per;
+  y = rem / gw;
+  x = rem - y * gw;
+}
+
+// ------------------------------------------------------------------ tables
+__global__ void rope_table_kernel(float2* tab, int rows, int half, int dim, long long pos0,
+                                  double theta) {
+  const int idx = blockIdx.x * blockDim.x + threadIdx.x;
+  if (idx >= rows * half) return;
+  const int r = idx / half, i = idx - r * half;
+  const double w = pow(theta, -2.0 * (double)i / (double)dim);
+  const double phi = (double)(pos0 + r) * w;
+  double s, c;
+  sincos(phi, &s, &c);
+  tab[idx] = make_float2((float)c, (float)s);
+}
+
+// ------------------------------------------------------------------ block open
+// One wavefront.  Scores: cos = dot / (sqrt(|q|^2) sqrt(|b|^2)) in fp64 with a
+// fixed sequential summation order per candidate; 0 when either norm is 0.
+// Rank: (score desc, stream id asc), selected by k rounds of a wave arg-max.
+__global__ __launch_bounds__(64) void open_kernel(OpenArgs a) {
+  __shared__ double s_score[kMaxBank];
+  __shared__ int s_taken[kMaxBank];
+  const int lane = threadIdx.x;
+  if (a.pose_in) {
+    for (int i = lane; i < a.P; i += 64) a.pose_store[(size_t)a.cur_slot * a.P + i] = a.pose_in[i];
+  }
+  if (a.ttab) {
+    const int half = a.t_dim >> 1;
+    for (int idx = lane; idx < a.t_rows * half; idx += 64) {
+      const int r = idx / half, i = idx - r * half;
+      const double w = pow(a.theta, -2.0 * (double)i / (double)a.t_dim);
+      double s, c;
+      sincos((double)(a.t_pos0 + r) * w, &s, &c);
+      a.ttab[idx] = make_float2((float)c, (float)s);
+    }
+  }
+  if (a.k <= 0 || a.nbank <= 0) return;
+  double qq = 0.0;
+  for (int i = 0; i < a.P; ++i) {
+    const double x = (double)a.pose_in[i];
+    qq += x * x;
+  }
+  for (int c = lane; c < a.nbank; c += 64) {
+    const float* b = a.pose_store + (size_t)a.bank_slot[c] * a.P;
+    double dot = 0.0, bb = 0.0;
+    for (int i = 0; i < a.P; ++i) {
+      const double x = (double)a.pose_in[i];
+      const double y = (double)b[i];
+      dot += x * y;
+      bb += y * y;
+    }
+    double sc = 0.0;
+    if (qq > 0.0 && bb > 0.0) sc = dot / (sqrt(qq) * sqrt(bb));
+    s_score[c] = sc;
+    s_taken[c] = 0;
+  }
+  __syncthreads();
+  const int kk = a.k < a.nbank ? a.k : a.nbank;
+  for (int r = 0; r < kk; ++r) {
+    double best = -INFINITY;
+    int bid = 0x7fffffff, bc = -1;
+    for (int c = lane; c < a.nbank; c += 64) {
+      if (s_taken[c]) continue;
+      const double sc = s_score[c];
+      const int id = a.bank_id[c];
+      if (sc > best || (sc == best && id < bid)) {
+        best = sc;
+        bid = id;
+        bc = c;
+      }
+    }
+    for (int off = 32; off > 0; off >>= 1) {
+      const double ob = __shfl_xor(best, off);
+      const int oid = __shfl_xor(bid, off);
+      const int oc = __shfl_xor(bc, off);
+      if (ob > best || (ob == best && oid < bid)) {
+        best = ob;
+        bid = oid;
+        bc = oc;
+      }
+    }
+    if (lane == 0) {
+      a.sel_ids[r] = bid;
+      a.sel_slots[r] = a.bank_slot[bc];
+      s_taken[bc] = 1;
+    }
+    __syncthreads();
+  }
+}
+
+// ------------------------------------------------------------------ append
+// One workgroup per (64-token tile, head).  K: each thread moves 16-byte chunks
+// of a token's row, rotating pairs in fp32.  V: the tile goes through LDS and
+// leaves as rows of V^T (64 consecutive tokens of one channel).
+template <typename T, int D>
+__global__ __launch_bounds__(256) void append_kernel(AppendArgs a) {
+  constexpr int VEC = 16 / sizeof(T);          // elements per 16-byte chunk
+  constexpr int CPR = D / VEC;                 // chunks per row
+  constexpr int PAD = 2;
+  __shared__ T s_v[64][D + PAD];
+  const int tile0 = blockIdx.x * 64;
+  const int head = blockIdx.y;
+  const int tid = threadIdx.x;
+  const int ntok = min(64, a.T - tile0);
+  const bool rope = has_rope(a.rope);
+  for (int task = tid; task < 64 * CPR; task += 256) {
+    const int r = task / CPR, c = task - r * CPR;
+    if (r >= ntok) continue;
+    const int tok = tile0 + r;
+    const size_t src = ((size_t)tok * a.H + head) * D + c * VEC;
+    uint4 kraw = *reinterpret_cast<const uint4*>(static_cast<const T*>(a.k_in) + src);
+    uint4 vraw = *reinterpret_cast<const uint4*>(static_cast<const T*>(a.v_in) + src);
+    const T* vv = reinterpret_cast<const T*>(&vraw);
+#pragma unroll
+    for (int e = 0; e < VEC; ++e) s_v[r][c * VEC + e] = vv[e];
+    if (a.k_raw) {
+      T* dst = static_cast<T*>(a.k_raw) + head * a.k_raw_hs + (size_t)tok * D + c * VEC;
+      *reinterpret_cast<uint4*>(dst) = kraw;
+    }
+    if (a.k_rot) {
+      uint4 kout = kraw;
+      if (rope) {
+        int f, y, x;
+        token_fyx(tok, a.rope.grid_h, a.rope.grid_w, f, y, x);
+        const T* kin = reinterpret_cast<const T*>(&kraw);
+        T* ko = reinterpret_cast<T*>(&kout);
+#pragma unroll
+        for (int e = 0; e < VEC; e += 2) {
+          float u0 = to_f(kin[e]), u1 = to_f(kin[e + 1]);
+          rope_pair(u0, u1, c * VEC + e, a.rope, a.t_row0 + f, y, x);
+          ko[e] = from_f<T>(u0);
+          ko[e + 1] = from_f<T>(u1);
+        }
+      }
+      T* dst = static_cast<T*>(a.k_rot) + head * a.k_rot_hs + (size_t)(a.k_rot_off + tok) * D + c * VEC;
+      *reinterpret_cast<uint4*>(dst) = kout;
+    }
+  }
+  __syncthreads();
+  constexpr int TG = 64 / VEC;                 // token groups of VEC per V^T row tile
+  for (int task = tid; task < D * TG; task += 256) {
+    const int d = task / TG, g = task - d * TG;
+    T* dst = static_cast<T*>(a.vt) + head * a.vt_hs + (size_t)d * a.vt_ld + tile0 + g * VEC;
+    if ((g + 1) * VEC <= ntok) {
+      uint4 w;
+      T* wv = reinterpret_cast<T*>(&w);
+#pragma unroll
+      for (int e = 0; e < VEC; ++e) wv[e] = s_v[g * VEC + e][d];
+      *reinterpret_cast<uint4*>(dst) = w;
+    } else {
+      for (int e = 0; e < VEC; ++e)
+        if (g * VEC + e < ntok) dst[e] = s_v[g * VEC + e][d];
+    }
+  }
+}
+
+// ------------------------------------------------------------------ attention, bf16 MFMA
+// Workgroup = 4 waves x 32 queries (BM = 128) of one head; key tiles of 64.
+//
+// S^T = K Q^T with v_mfma_f32_32x32x16_bf16: A = 32 keys x 16 channels (one
+// 16-byte LDS read per lane), B = Q^T held in registers for the whole loop.
+// MFMA row r is mapped to tile key pi(r) = 16*((r>>2)&1) + 4*(r>>3) + (r&3), so
+// lane half h's 16 accumulators are the 16 consecutive keys 16h..16h+15 of the
+// 32-key block for query (lane & 31).  O^T += V^T P^T then reads A = V^T as 8
+// consecutive keys of one channel (one 16-byte LDS read) and B = P^T straight
+// from the accumulators: the contraction index k = 8h + e stands for key
+// 16h + 8*part + e on both operands.
+// Row statistics: a query's 64 scores of a tile sit in lanes l and l^32.
+constexpr int ABM = 128, ABN = 64, AD = 128;
+constexpr int KT_BYTES = ABN * AD * 2;
+constexpr int VT_BYTES = AD * ABN * 2;
+constexpr int STAGE_BYTES = KT_BYTES + VT_BYTES;
+
+__device__ __forceinline__ int kswz(int r) { return (r & 3) | ((r >> 2) & 4); }
+__device__ __forceinline__ int kperm(int r) { return ((r >> 2) & 1) * 16 + (r >> 3) * 4 + (r & 3); }
+
+__device__ __forceinline__ int xcd_remap(int bid, int nwg) {
+  // Consecutive workgroup ids are dispatched round-robin over the 8 XCDs; give
+  // each XCD a contiguous range of logical ids so one head's query tiles share
+  // an L2.
+  const int xcd = bid & 7, q = nwg >> 3, r = nwg & 7;
+  return xcd * q + min(xcd, r) + (bid >> 3);
+}
+
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2)))
+void attn_bf16_kernel(AttnArgs a) {
+  __shared__ __attribute__((aligned(16))) char lds[2 * STAGE_BYTES];
+  __shared__ const __bf16* s_k[kMaxSeg];
+  __shared__ const __bf16* s_v[kMaxSeg];
+  __shared__ int s_n[kMaxSeg];
+  __shared__ int s_ld[kMaxSeg];
+
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int hh = lane >> 5, col = lane & 31;
+  const int nqt = (a.T + ABM - 1) / ABM;
+  const int logical = xcd_remap(blockIdx.x, gridDim.x);
+  const int head = logical / nqt, qt = logical - head * nqt;
+
+  if (tid < a.nseg) {
+    const Seg sg = a.seg[tid];
+    const char* kb;
+    const char* vb;
+    long long khs, vhs;
+    int ld;
+    if (sg.dyn >= 0) {
+      const int slot = a.sel_slots[sg.dyn];
+      kb = a.slot_base + (long long)slot * a.slot_bytes;
+      vb = kb + a.slot_v_off;
+      khs = a.slot_k_hs;
+      vhs = a.slot_v_hs;
+      ld = a.slot_v_ld;
+    } else {
+      kb = static_cast<const char*>(sg.k);
+      vb = static_cast<const char*>(sg.v);
+      khs = sg.k_hs;
+      vhs = sg.v_hs;
+      ld = sg.v_ld;
+    }
+    s_k[tid] = reinterpret_cast<const __bf16*>(kb) + head * khs;
+    s_v[tid] = reinterpret_cast<const __bf16*>(vb) + head * vhs;
+    s_n[tid] = sg.n;
+    s_ld[tid] = ld;
+  }
+
+  // Q prologue: lane holds Q~[q][16s + 8h .. +7] for s = 0..7, rotated, scaled
+  // by softmax_scale*log2(e), rounded to bf16.
+  const int qrow = qt * ABM + wave * 32 + col;
+  bf16x8 qreg[8];
+  {
+    int f = 0, y = 0, x = 0;
+    const bool valid = qrow < a.T;
+    if (valid) token_fyx(qrow, a.rope.grid_h, a.rope.grid_w, f, y, x);
+    const bool rope = has_rope(a.rope);
+    const __bf16* qp = static_cast<const __bf16*>(a.q) + ((size_t)(valid ? qrow : 0) * a.H + head) * AD;
+#pragma unroll
+    for (int s = 0; s < 8; ++s) {
+      const int d0 = 16 * s + 8 * hh;
+      bf16x8 raw = valid ? *reinterpret_cast<const bf16x8*>(qp + d0) : bf16x8{};
+      float u[8];
+#pragma unroll
+      for (int e = 0; e < 8; ++e) u[e] = (float)raw[e];
+      if (rope && valid) {
+#pragma unroll
+        for (int e = 0; e < 8; e += 2) rope_pair(u[e], u[e + 1], d0 + e, a.rope, a.t_row0 + f, y, x);
+      }
+#pragma unroll
+      for (int e = 0; e < 8; ++e) qreg[s][e] = (__bf16)(u[e] * a.qscale);
+    }
+  }
+  __syncthreads();
+
+  uint4 kreg[4], vreg[4];
+  auto gload = [&](int sg, int j0) {
+    const __bf16* kb = s_k[sg];
+    const __bf16* vb = s_v[sg];
+    const int n = s_n[sg], ld = s_ld[sg];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int r = (tid >> 4) + 16 * i, c = tid & 15;
+      kreg[i] = (j0 + r < n) ? *reinterpret_cast<const uint4*>(kb + (size_t)(j0 + r) * AD + c * 8)
+                             : make_uint4(0, 0, 0, 0);
+    }
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int d = (tid >> 3) + 32 * i, c = tid & 7;
+      const int key0 = j0 + 8 * c;
+      uint4 v = make_uint4(0, 0, 0, 0);
+      if (key0 < n) {
+        v = *reinterpret_cast<const uint4*>(vb + (size_t)d * ld + key0);
+        const int valid = n - key0;
+        if (valid < 8) {
+          uint32_t* w = reinterpret_cast<uint32_t*>(&v);
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            if (2 * e >= valid) w[e] = 0u;
+            else if (2 * e + 1 >= valid) w[e] &= 0x0000ffffu;
+          }
+        }
+      }
+      vreg[i] = v;
+    }
+  };
+  auto lstore = [&](int stage) {
+    char* kt = lds + stage * STAGE_BYTES;
+    char* vt = kt + KT_BYTES;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int r = (tid >> 4) + 16 * i, c = tid & 15;
+      *reinterpret_cast<uint4*>(kt + r * 256 + ((c ^ kswz(r)) << 4)) = kreg[i];
+    }
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int d = (tid >> 3) + 32 * i, c = tid & 7;
+      *reinterpret_cast<uint4*>(vt + d * 128 + ((c ^ (d & 7)) << 4)) = vreg[i];
+    }
+  };
+
+  f32x16 o[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) o[i] = f32x16{};
+  float m_run = -INFINITY, l_run = 0.f;
+
+  int sg = 0, j0 = 0, stage = 0;
+  while (sg < a.nseg && s_n[sg] == 0) ++sg;
+  if (sg < a.nseg) {
+    gload(sg, 0);
+    lstore(0);
+  }
+  __syncthreads();
+  while (sg < a.nseg) {
+    int nsg = sg, nj0 = j0 + ABN;
+    if (nj0 >= s_n[sg]) {
+      nsg = sg + 1;
+      nj0 = 0;
+      while (nsg < a.nseg && s_n[nsg] == 0) ++nsg;
+    }
+    const bool more = nsg < a.nseg;
+    if (more) gload(nsg, nj0);
+
+    const char* kt = lds + stage * STAGE_BYTES;
+    const char* vt = kt + KT_BYTES;
+    const int nvalid = s_n[sg] - j0;
+    f32x16 sacc[2];
+#pragma unroll
+    for (int mb = 0; mb < 2; ++mb) {
+      sacc[mb] = f32x16{};
+      const int r = 32 * mb + kperm(col);
+#pragma unroll
+      for (int s = 0; s < 8; ++s) {
+        const int c = 2 * s + hh;
+        const bf16x8 kv = *reinterpret_cast<const bf16x8*>(kt + r * 256 + ((c ^ kswz(r)) << 4));
+        sacc[mb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kv, qreg[s], sacc[mb], 0, 0, 0);
+      }
+    }
+    if (nvalid < ABN) {
+#pragma unroll
+      for (int mb = 0; mb < 2; ++mb)
+#pragma unroll
+        for (int i = 0; i < 16; ++i)
+          if (32 * mb + 16 * hh + i >= nvalid) sacc[mb][i] = -INFINITY;
+    }
+    float mx = sacc[0][0];
+#pragma unroll
+    for (int mb = 0; mb < 2; ++mb)
+#pragma unroll
+      for (int i = 0; i < 16; ++i) mx = fmaxf(mx, sacc[mb][i]);
+    mx = fmaxf(mx, __shfl_xor(mx, 32));
+    const float m_new = fmaxf(m_run, mx);
+    const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);
+    m_run = m_new;
+    l_run *= alpha;
+#pragma unroll
+    for (int db = 0; db < 4; ++db) o[db] *= alpha;
+    bf16x8 pb[2][2];
+#pragma unroll
+    for (int mb = 0; mb < 2; ++mb)
+#pragma unroll
+      for (int i = 0; i < 16; ++i) {
+        const float p = __builtin_amdgcn_exp2f(sacc[mb][i] - m_new);
+        l_run += p;
+        pb[mb][i >> 3][i & 7] = (__bf16)p;
+      }
+#pragma unroll
+    for (int db = 0; db < 4; ++db) {
+      const int d = 32 * db + col;
+#pragma unroll
+      for (int mb = 0; mb < 2; ++mb)
+#pragma unroll
+        for (int part = 0; part < 2; ++part) {
+          const int c = 4 * mb + 2 * hh + part;
+          const bf16x8 vv = *reinterpret_cast<const bf16x8*>(vt + d * 128 + ((c ^ (d & 7)) << 4));
+          o[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vv, pb[mb][part], o[db], 0, 0, 0);
+        }
+    }
+    if (more) lstore(stage ^ 1);
+    __syncthreads();
+    sg = nsg;
+    j0 = nj0;
+    stage ^= 1;
+  }
+
+  const float lt = l_run + __shfl_xor(l_run, 32);
+  const float inv = lt > 0.f ? 1.f / lt : 0.f;
+  if (qrow < a.T) {
+    __bf16* op = static_cast<__bf16*>(a.out) + ((size_t)qrow * a.H + head) * AD;
+#pragma unroll
+    for (int db = 0; db < 4; ++db)
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        bf16x4 w;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) w[e] = (__bf16)(o[db][4 * j + e] * inv);
+        *reinterpret_cast<bf16x4*>(op + 32 * db + 8 * j + 4 * hh) = w;
+      }
+  }
+}
+
+// ------------------------------------------------------------------ attention, fp32
+// One or two lanes per query (D = 64 or 128): each lane keeps 64 channels of
+// q~ and of the output accumulator in registers; key tiles of 32 in LDS.
+template <int D>
+__global__ __launch_bounds__(128) void attn_f32_kernel(AttnArgs a) {
+  constexpr int LPQ = D / 64;
+  constexpr int QPB = 128 / LPQ;
+  constexpr int BNF = 32;
+  __shared__ float s_kt[BNF][D + 1];
+  __shared__ float s_vt[D][BNF + 1];
+  __shared__ const float* s_k[kMaxSeg];
+  __shared__ const float* s_v[kMaxSeg];
+  __shared__ int s_n[kMaxSeg];
+  __shared__ int s_ld[kMaxSeg];
+  const int tid = threadIdx.x;
+  const int nqt = (a.T + QPB - 1) / QPB;
+  const int head = blockIdx.x / nqt, qt = blockIdx.x - head * nqt;
+  if (tid < a.nseg) {
+    const Seg sg = a.seg[tid];
+    const char* kb;
+    const char* vb;
+    long long khs, vhs;
+    int ld;
+    if (sg.dyn >= 0) {
+      const int slot = a.sel_slots[sg.dyn];
+      kb = a.slot_base + (long long)slot * a.slot_bytes;
+      vb = kb + a.slot_v_off;
+      khs = a.slot_k_hs;
+      vhs = a.slot_v_hs;
+      ld = a.slot_v_ld;
+    } else {
+      kb = static_cast<const char*>(sg.k);
+      vb = static_cast<const char*>(sg.v);
+      khs = sg.k_hs;
+      vhs = sg.v_hs;
+      ld = sg.v_ld;
+    }
+    s_k[tid] = reinterpret_cast<const float*>(kb) + head * khs;
+    s_v[tid] = reinterpret_cast<const float*>(vb) + head * vhs;
+    s_n[tid] = sg.n;
+    s_ld[tid] = ld;
+  }
+  const int sub = tid % LPQ;
+  const int qrow = qt * QPB + tid / LPQ;
+  const bool valid = qrow < a.T;
+  float q[64], o[64];
+  {
+    int f = 0, y = 0, x = 0;
+    if (valid) token_fyx(qrow, a.rope.grid_h, a.rope.grid_w, f, y, x);
+    const float* qp = static_cast<const float*>(a.q) + ((size_t)(valid ? qrow : 0) * a.H + head) * D + sub * 64;
+#pragma unroll
+    for (int c = 0; c < 64; ++c) q[c] = valid ? qp[c] : 0.f;
+    if (valid && has_rope(a.rope)) {
+#pragma unroll
+      for (int c = 0; c < 64; c += 2) rope_pair(q[c], q[c + 1], sub * 64 + c, a.rope, a.t_row0 + f, y, x);
+    }
+#pragma unroll
+    for (int c = 0; c < 64; ++c) {
+      q[c] *= a.qscale;
+      o[c] = 0.f;
+    }
+  }
+  __syncthreads();
+  float m_run = -INFINITY, l_run = 0.f;
+  for (int sg = 0; sg < a.nseg; ++sg) {
+    const int n = s_n[sg], ld = s_ld[sg];
+    const float* kb = s_k[sg];
+    const float* vb = s_v[sg];
+    for (int j0 = 0; j0 < n; j0 += BNF) {
+      const int nv = min(BNF, n - j0);
+      for (int i = tid; i < BNF * D; i += 128) {
+        const int r = i / D, c = i - r * D;
+        s_kt[r][c] = (r < nv) ? kb[(size_t)(j0 + r) * D + c] : 0.f;
+      }
+      for (int i = tid; i < D * BNF; i += 128) {
+        const int d = i / BNF, j = i - d * BNF;
+        s_vt[d][j] = (j < nv) ? vb[(size_t)d * ld + j0 + j] : 0.f;
+      }
+      __syncthreads();
+      float s[BNF];
+      float mx = -INFINITY;
+#pragma unroll
+      for (int j = 0; j < BNF; ++j) {
+        float acc = 0.f;
+#pragma unroll
+        for (int c = 0; c < 64; ++c) acc = fmaf(q[c], s_kt[j][sub * 64 + c], acc);
+        if (LPQ == 2) acc += __shfl_xor(acc, 1);
+        s[j] = (j < nv) ? acc : -INFINITY;
+        mx = fmaxf(mx, s[j]);
+      }
+      const float m_new = fmaxf(m_run, mx);
+      const float alpha = expf(m_run - m_new);
+      m_run = m_new;
+      l_run *= alpha;
+#pragma unroll
+      for (int c = 0; c < 64; ++c) o[c] *= alpha;
+#pragma unroll
+      for (int j = 0; j < BNF; ++j) {
+        const float p = expf(s[j] - m_new);
+        l_run += p;
+#pragma unroll
+        for (int c = 0; c < 64; ++c) o[c] = fmaf(p, s_vt[sub * 64 + c][j], o[c]);
+      }
+      __syncthreads();
+    }
+  }
+  if (valid) {
+    const float inv = 1.f / l_run;
+    float* op = static_cast<float*>(a.out) + ((size_t)qrow * a.H + head) * D + sub * 64;
+#pragma unroll
+    for (int c = 0; c < 64; ++c) op[c] = o[c] * inv;
+  }
+}
+
+// ------------------------------------------------------------------ ConvKV gather
+template <typename T, int D>
+__global__ __launch_bounds__(256) void gather_kernel(GatherArgs a) {
+  constexpr int VEC = 16 / sizeof(T);
+  constexpr int CPR = D / VEC;
+  const GatherPart p = a.part[blockIdx.z];
+  const int head = blockIdx.y;
+  const int tile0 = blockIdx.x * 64;
+  if (tile0 >= p.n) return;
+  const int ntok = min(64, p.n - tile0);
+  const bool rope = has_rope(a.rope);
+  for (int task = threadIdx.x; task < 64 * CPR; task += 256) {
+    const int r = task / CPR, c = task - r * CPR;
+    if (r >= ntok) continue;
+    const int tok = tile0 + r;
+    uint4 raw = *reinterpret_cast<const uint4*>(static_cast<const T*>(p.src) + head * p.src_hs +
+                                                (size_t)tok * D + c * VEC);
+    if (rope) {
+      int f, y, x;
+      token_fyx(tok, a.rope.grid_h, a.rope.grid_w, f, y, x);
+      T* kv = reinterpret_cast<T*>(&raw);
+#pragma unroll
+      for (int e = 0; e < VEC; e += 2) {
+        float u0 = to_f(kv[e]), u1 = to_f(kv[e + 1]);
+        rope_pair(u0, u1, c * VEC + e, a.rope, p.t_row0 + f, y, x);
+        kv[e] = from_f<T>(u0);
+        kv[e + 1] = from_f<T>(u1);
+      }
+    }
+    T* dst = static_cast<T*>(a.dst) + head * a.dst_hs + (size_t)(p.dst_off + tok) * D + c * VEC;
+    *reinterpret_cast<uint4*>(dst) = raw;
+  }
+}
+
+// ------------------------------------------------------------------ ConvKV conv
+// blockIdx.z = memory frame j, blockIdx.y = 0 (K rows) / 1 (V^T rows).
+// mem[j][h][s][c] = sum_i w[h][c][i] * frame[j*kernel + i][h][s][c], fp32 sums.
+template <typename T, bool VEC_V>
+__global__ __launch_bounds__(256) void conv_kernel(ConvArgs a) {
+  constexpr int VEC = 16 / sizeof(T);
+  const int j = blockIdx.z;
+  const int D = a.D, Tf = a.Tf;
+  const long long gid = (long long)blockIdx.x * 256 + threadIdx.x;
+  if (blockIdx.y == 0) {
+    // K rows: chunks of VEC channels; index = (h * Tf + s) * (D / VEC) + c
+    const int cpr = D / VEC;
+    const long long total = (long long)a.H * Tf * cpr;
+    if (gid >= total) return;
+    const int c = (int)(gid % cpr);
+    const long long hs = gid / cpr;
+    const int s = (int)(hs % Tf), h = (int)(hs / Tf);
+    float acc[VEC];
+#pragma unroll
+    for (int e = 0; e < VEC; ++e) acc[e] = 0.f;
+    for (int i = 0; i < a.kernel; ++i) {
+      const T* src = static_cast<const T*>(a.k_src[j * a.kernel + i]) + h * a.k_hs + (size_t)s * D + c * VEC;
+      const uint4 raw = *reinterpret_cast<const uint4*>(src);
+      const T* v = reinterpret_cast<const T*>(&raw);
+      const float* w = a.wk + ((size_t)h * D + c * VEC) * a.kernel + i;
+#pragma unroll
+      for (int e = 0; e < VEC; ++e) acc[e] = fmaf(w[e * a.kernel], to_f(v[e]), acc[e]);
+    }
+    uint4 out;
+    T* ov = reinterpret_cast<T*>(&out);
+#pragma unroll
+    for (int e = 0; e < VEC; ++e) ov[e] = from_f<T>(acc[e]);
+    T* dst = static_cast<T*>(a.k_mem) + h * a.k_mem_hs + (size_t)(j * a.tf_pad + s) * D + c * VEC;
+    *reinterpret_cast<uint4*>(dst) = out;
+  } else {
+    // V^T rows: index = (h * D + d) * groups + g, groups of VEC tokens
+    const int groups = (Tf + VEC - 1) / VEC;
+    const long long total = (long long)a.H * D * groups;
+    if (gid >= total) return;
+    const int g = (int)(gid % groups);
+    const long long hd = gid / groups;
+    const int d = (int)(hd % D), h = (int)(hd / D);
+    const int s0 = g * VEC;
+    const int nv = min(VEC, Tf - s0);
+    float acc[VEC];
+#pragma unroll
+    for (int e = 0; e < VEC; ++e) acc[e] = 0.f;
+    for (int i = 0; i < a.kernel; ++i) {
+      const T* src = static_cast<const T*>(a.vt_src[j * a.kernel + i]) + h * a.vt_hs + (size_t)d * a.vt_ld + s0;
+      const float w = a.wv[((size_t)h * D + d) * a.kernel + i];
+      if (VEC_V && nv == VEC) {
+        const uint4 raw = *reinterpret_cast<const uint4*>(src);
+        const T* v = reinterpret_cast<const T*>(&raw);
+#pragma unroll
+        for (int e = 0; e < VEC; ++e) acc[e] = fmaf(w, to_f(v[e]), acc[e]);
+      } else {
+        for (int e = 0; e < nv; ++e) acc[e] = fmaf(w, to_f(src[e]), acc[e]);
+      }
+    }
+    T* dst = static_cast<T*>(a.vt_mem) + h * a.vt_mem_hs + (size_t)d * a.vt_mem_ld + j * a.tf_pad + s0;
+    if (nv == VEC) {
+      uint4 out;
+      T* ov = reinterpret_cast<T*>(&out);
+#pragma unroll
+      for (int e = 0; e < VEC; ++e) ov[e] = from_f<T>(acc[e]);
+      *reinterpret_cast<uint4*>(dst) = out;
+    } else {
+      for (int e = 0; e < nv; ++e) dst[e] = from_f<T>(acc[e]);
+    }
+  }
+}
+
+// ------------------------------------------------------------------ export
+template <typename T>
+__global__ void export_kernel(ExportArgs a) {
+  const long long gid = (long long)blockIdx.x * blockDim.x + threadIdx.x;
+  const long long total = (long long)a.seg.n * a.H * a.D;
+  if (gid >= total) return;
+  const int d = (int)(gid % a.D);
+  const long long th = gid / a.D;
+  const int h = (int)(th % a.H);
+  const int tok = (int)(th / a.H);
+  const char* kb;
+  const char* vb;
+  long long khs, vhs;
+  int ld;
+  if (a.seg.dyn >= 0) {
+    const int slot = a.sel_slots[a.seg.dyn];
+    kb = a.slot_base + (long long)slot * a.slot_bytes;
+    vb = kb + a.slot_v_off;
+    khs = a.slot_k_hs;
+    vhs = a.slot_v_hs;
+    ld = a.slot_v_ld;
+  } else {
+    kb = static_cast<const char*>(a.seg.k);
+    vb = static_cast<const char*>(a.seg.v);
+    khs = a.seg.k_hs;
+    vhs = a.seg.v_hs;
+    ld = a.seg.v_ld;
+  }
+  const T* k = reinterpret_cast<const T*>(kb) + h * khs + (size_t)tok * a.D + d;
+  const T* v = reinterpret_cast<const T*>(vb) + h * vhs + (size_t)d * ld + tok;
+  static_cast<T*>(a.k_out)[gid] = *k;
+  static_cast<T*>(a.v_out)[gid] = *v;
+}
+
+}  // namespace
+
+// ------------------------------------------------------------------ launchers
+hipError_t launch_rope_table(float2* tab, int rows, int dim, long long pos0, double theta,
+                             hipStream_t s) {
+  const int half = dim / 2;
+  const int n = rows * half;
+  if (n <= 0) return hipSuccess;
+  rope_table_kernel<<<(n + 255) / 256, 256, 0, s>>>(tab, rows, half, dim, pos0, theta);
+  return hipGetLastError();
+}
+
+hipError_t launch_open(const OpenArgs& a, hipStream_t s) {
+  open_kernel<<<1, 64, 0, s>>>(a);
+  return hipGetLastError();
+}
+
+hipError_t launch_append(const AppendArgs& a, bool bf16, hipStream_t s) {
+  dim3 grid((a.T + 63) / 64, a.H);
+  if (bf16) {
+    if (a.D != 128) return hipErrorInvalidValue;
+    append_kernel<__bf16, 128><<<grid, 256, 0, s>>>(a);
+  } else if (a.D == 64) {
+    append_kernel<float, 64><<<grid, 256, 0, s>>>(a);
+  } else if (a.D == 128) {
+    append_kernel<float, 128><<<grid, 256, 0, s>>>(a);
+  } else {
+    return hipErrorInvalidValue;
+  }
+  return hipGetLastError();
+}
+
+hipError_t launch_attention(const AttnArgs& a, bool bf16, hipStream_t s) {
+  if (bf16) {
+    if (a.D != AD) return hipErrorInvalidValue;
+    const int nwg = ((a.T + ABM - 1) / ABM) * a.H;
+    attn_bf16_kernel<<<nwg, 256, 0, s>>>(a);
+  } else if (a.D == 64) {
+    const int nwg = ((a.T + 127) / 128) * a.H;
+    attn_f32_kernel<64><<<nwg, 128, 0, s>>>(a);
+  } else if (a.D == 128) {
+    const int nwg = ((a.T + 63) / 64) * a.H;
+    attn_f32_kernel<128><<<nwg, 128, 0, s>>>(a);
+  } else {
+    return hipErrorInvalidValue;
+  }
+  return hipGetLastError();
+}
+
+hipError_t launch_gather(const GatherArgs& a, bool bf16, hipStream_t s) {
+  if (a.nparts == 0) return hipSuccess;
+  dim3 grid((a.max_n + 63) / 64, a.H, a.nparts);
+  if (bf16) {
+    if (a.D != 128) return hipErrorInvalidValue;
+    gather_kernel<__bf16, 128><<<grid, 256, 0, s>>>(a);
+  } else if (a.D == 64) {
+    gather_kernel<float, 64><<<grid, 256, 0, s>>>(a);
+  } else if (a.D == 128) {
+    gather_kernel<float, 128><<<grid, 256, 0, s>>>(a);
+  } else {
+    return hipErrorInvalidValue;
+  }
+  return hipGetLastError();
+}
+
+hipError_t launch_conv(const ConvArgs& a, bool bf16, hipStream_t s) {
+  const int vec = bf16 ? 8 : 4;
+  const long long nk = (long long)a.H * a.Tf * (a.D / vec);
+  const long long nv = (long long)a.H * a.D * ((a.Tf + vec - 1) / vec);
+  const long long n = nk > nv ? nk : nv;
+  dim3 grid((unsigned)((n + 255) / 256), 2, a.n_mem);
+  const size_t esz = bf16 ? 2 : 4;
+  const bool vec_v = ((size_t)a.Tf * esz) % 16 == 0;
+  if (bf16) {
+    if (vec_v) conv_kernel<__bf16, true><<<grid, 256, 0, s>>>(a);
+    else conv_kernel<__bf16, false><<<grid, 256, 0, s>>>(a);
+  } else {
+    if (vec_v) conv_kernel<float, true><<<grid, 256, 0, s>>>(a);
+    else conv_kernel<float, false><<<grid, 256, 0, s>>>(a);
+  }
+  return hipGetLastError();
+}
+
+hipError_t launch_export(const ExportArgs& a, bool bf16, hipStream_t s) {
+  const long long n = (long long)a.seg.n * a.H * a.D;
+  if (n == 0) return hipSuccess;
+  const unsigned blocks = (unsigned)((n + 255) / 256);
+  if (bf16) export_kernel<__bf16><<<blocks, 256, 0, s>>>(a);
+  else export_kernel<float><<<blocks, 256, 0, s>>>(a);
+  return hipGetLastError();
+}
+
+}  // namespace bkv

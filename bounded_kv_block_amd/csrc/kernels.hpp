@@ -1,0 +1,125 @@
+// Launch interface of the gfx950 kernels (host <-> device argument structs).
+//
+// Device memory layout used by every kernel (elements of the cache dtype):
+//   K rows   [H][ld][D]  -- a head's keys are contiguous rows of D values
+//   V^T      [H][D][ld]  -- values stored transposed, so the P.V MFMA reads
+//                           8 consecutive keys of one channel as one 16-byte word
+// ld (the token stride) is a multiple of 64, so tile loads never leave a row.
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace bkv {
+
+constexpr int kMaxSeg = 16;     // context segments per block (static+dynamic+window+current)
+constexpr int kMaxBank = 256;   // PR-Sink bank capacity
+constexpr int kMaxK = 8;        // dynamic sinks per block
+constexpr int kMaxTaps = 32;    // ConvKV: conv_kernel * memory_frames source frames
+constexpr int kTokAlign = 64;   // token-stride alignment of every K / V^T buffer
+
+struct Rope {                   // 3D RoPE tables: (cos, sin) fp32 pairs, built in fp64
+  const float2* t;              // [rows][dt/2]; row r <-> temporal position of row r
+  const float2* h;              // [grid_h][dh/2]
+  const float2* w;              // [grid_w][dw/2]
+  int dt, dh, dw;               // channel split, all 0 = no RoPE
+  int grid_h, grid_w;
+};
+
+// One context segment for attention: keys [0, n).  K rows at k + head*k_hs,
+// V^T at v + head*v_hs with row stride v_ld.  dyn >= 0: the segment is a
+// retrieved bank block; its slot is sel_slots[dyn] and k/v are derived from
+// slot_base (set on device by the retrieval kernel, unknown to the host).
+struct Seg {
+  const void* k;
+  const void* v;
+  long long k_hs, v_hs;
+  int v_ld, n, dyn, pad_;
+};
+
+struct AttnArgs {
+  const void* q;            // [T][H][D] caller's queries (rotated and scaled in-kernel)
+  void* out;                // [T][H][D]
+  int T, H, D;
+  int t_row0;               // RoPE t-table row of the current block's frame 0
+  float qscale;             // softmax scale * log2(e) (bf16 path) or softmax scale (fp32 path)
+  int nseg;
+  Rope rope;
+  const int* sel_slots;     // device, written by the retrieval kernel
+  const char* slot_base;    // layer's slot 0 (bytes); slot s at slot_base + s*slot_bytes
+  long long slot_bytes;
+  long long slot_v_off;     // byte offset of V^T inside a slot
+  long long slot_k_hs, slot_v_hs;
+  int slot_v_ld, pad_;
+  Seg seg[kMaxSeg];
+};
+
+// K/V append with fused RoPE on K (one launch per attend).
+struct AppendArgs {
+  const void* k_in;         // [T][H][D]
+  const void* v_in;         // [T][H][D]
+  void* k_rot; long long k_rot_hs; int k_rot_off;   // rotated K rows [H][..][D] at row offset (or null)
+  void* k_raw; long long k_raw_hs;                  // raw K rows (ConvKV slot) or null
+  void* vt; long long vt_hs; int vt_ld;             // V^T destination
+  int T, H, D;
+  int t_row0;
+  Rope rope;
+};
+
+// Retrieval + block-open work, one workgroup.
+struct OpenArgs {
+  const float* pose_in;     // [P] caller's pose (null: none)
+  float* pose_store;        // [n_slots][P]
+  int P, cur_slot, nbank, k;
+  int* sel_ids;             // [k] out
+  int* sel_slots;           // [k] out
+  float2* ttab;             // t table rows to (re)build, or null
+  int t_rows, t_dim;
+  long long t_pos0;
+  double theta;
+  int bank_id[kMaxBank];
+  int bank_slot[kMaxBank];
+};
+
+// ConvKV: rotate raw K rows of memory frames / window blocks into the
+// contiguous context-K buffer at context positions.
+struct GatherPart {
+  const void* src; long long src_hs;   // raw K rows [H][..][D]
+  int dst_off, n, t_row0, pad_;        // dst row offset, tokens, t-table row of frame 0
+};
+struct GatherArgs {
+  void* dst; long long dst_hs;
+  int H, D, nparts, max_n;
+  Rope rope;
+  GatherPart part[kMaxSeg];
+};
+
+// ConvKV: depthwise temporal conv (stride = kernel) of raw evicted frames.
+struct ConvArgs {
+  const void* k_src[kMaxTaps];   // frame i's raw K rows (head 0, first token of the frame)
+  const void* vt_src[kMaxTaps];  // frame i's V^T (head 0, row 0, first token column)
+  long long k_hs, vt_hs; int vt_ld;
+  void* k_mem; long long k_mem_hs;          // memory K rows, frame j at row j*tf_pad
+  void* vt_mem; long long vt_mem_hs; int vt_mem_ld;
+  const float* wk; const float* wv;         // [H][D][kernel]
+  int H, D, Tf, tf_pad, kernel, n_mem;
+};
+
+// Inspection copy of one segment to token-major [n][H][D].
+struct ExportArgs {
+  Seg seg;
+  const int* sel_slots;
+  const char* slot_base; long long slot_bytes, slot_v_off, slot_k_hs, slot_v_hs; int slot_v_ld;
+  void* k_out; void* v_out;
+  int H, D;
+};
+
+hipError_t launch_rope_table(float2* tab, int rows, int dim, long long pos0, double theta,
+                             hipStream_t s);
+hipError_t launch_open(const OpenArgs& a, hipStream_t s);
+hipError_t launch_append(const AppendArgs& a, bool bf16, hipStream_t s);
+hipError_t launch_attention(const AttnArgs& a, bool bf16, hipStream_t s);
+hipError_t launch_gather(const GatherArgs& a, bool bf16, hipStream_t s);
+hipError_t launch_conv(const ConvArgs& a, bool bf16, hipStream_t s);
+hipError_t launch_export(const ExportArgs& a, bool bf16, hipStream_t s);
+
+}  // namespace bkv

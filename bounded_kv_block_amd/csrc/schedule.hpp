@@ -1,0 +1,237 @@
+// Host bookkeeping of the bounded cache: slots, static sink, rolling window,
+// FIFO bank (PR-Sink) or staged evicted blocks + memory (ConvKV), the call
+// order and the context of the open block.  Pure C++ (no HIP): the library
+// drives it, and the CPU tests build it alone.
+//
+// PR-Sink (LiveAnimate page, section 方法, PR-Sink bullets): static sink =
+// block 0, kept for good; rolling window = last `window` blocks; retrievable
+// history = a FIFO bank of the last `bank` blocks that left the window (the
+// page keeps a fixed number of blocks).  ConvKV (SoulX-LiveAct page, section
+// 技术内核, ConvKV Memory bullet): window of exact KV; evicted frames feed a
+// stride=kernel temporal conv whose output (memory_frames frames) is rebuilt
+// at each commit from the newest kernel*memory_frames evicted frames.
+//
+// Slots: every block in the cache occupies one slot (K and V of every layer).
+// A block keeps its slot until it leaves the cache, so a commit moves ids
+// between lists and never copies tensor data.
+#pragma once
+#include <algorithm>
+#include <cstdint>
+#include <deque>
+#include <utility>
+#include <vector>
+
+namespace bkv {
+
+enum SegKind { SEG_STATIC = 0, SEG_DYNAMIC = 1, SEG_WINDOW = 2, SEG_CURRENT = 3, SEG_MEMORY = 4 };
+
+struct SegPlan {
+  int kind;
+  int64_t id;       // block id; memory: frame index; dynamic: -1 (known on device only)
+  int tokens;
+  int64_t t0;       // temporal RoPE position of the segment's first frame
+  int slot;         // slot id, -1 for memory and dynamic segments
+  int dyn;          // dynamic: rank index into the device selection, else -1
+  int ctx_off;      // ConvKV: row offset in the context-K buffer, else 0
+};
+
+struct ConvTap { int slot; int frame; };   // one source frame of the conv memory
+
+class Schedule {
+ public:
+  struct Shape {
+    bool convkv;
+    int layers, frames, tokens_per_frame;   // T = frames * tokens_per_frame
+    int window, statics, k, bank;
+    int kernel, memory_frames;
+  };
+
+  explicit Schedule(const Shape& s) : s_(s) {
+    T_ = s.frames * s.tokens_per_frame;
+    if (s.convkv) {
+      int need = s.kernel * s.memory_frames;
+      staged_max_ = (need + s.frames - 1) / s.frames;
+      n_slots_ = s.window + 1 + staged_max_;
+    } else {
+      staged_max_ = 0;
+      n_slots_ = s.statics + s.window + 1 + s.bank;
+    }
+    reset();
+  }
+
+  int n_slots() const { return n_slots_; }
+  int staged_max() const { return staged_max_; }
+  int tokens() const { return T_; }
+  // Largest context the handle can see: sizes the ConvKV context-K buffer.
+  int max_context_tokens() const {
+    if (s_.convkv) return s_.memory_frames * s_.tokens_per_frame + (s_.window + 1) * T_;
+    return (s_.statics + s_.k + s_.window + 1) * T_;
+  }
+  int max_segments() const {
+    return s_.convkv ? s_.memory_frames + s_.window + 1 : s_.statics + s_.k + s_.window + 1;
+  }
+  // Temporal positions the ConvKV context uses: 0 .. max_context_frames()-1.
+  int max_context_frames() const { return s_.memory_frames + (s_.window + 1) * s_.frames; }
+
+  void reset() {
+    next_ = 0;
+    open_ = false;
+    cur_slot_ = -1;
+    static_.clear();
+    window_.clear();
+    bank_.clear();
+    staged_.clear();
+    free_.clear();
+    for (int i = n_slots_ - 1; i >= 0; --i) free_.push_back(i);   // pop_back hands out 0, 1, ...
+    evicted_frames_ = 0;
+    last_evicted_ = -1;
+    attended_.assign(s_.layers, false);
+    segs_.clear();
+  }
+
+  bool is_open() const { return open_; }
+  int64_t block() const { return next_; }
+  int cur_slot() const { return cur_slot_; }
+  int64_t last_evicted() const { return last_evicted_; }
+  const std::vector<SegPlan>& segments() const { return segs_; }
+  const std::deque<std::pair<int64_t, int>>& bank() const { return bank_; }
+  int n_dynamic() const {
+    return s_.convkv ? 0 : (int)std::min<size_t>((size_t)s_.k, bank_.size());
+  }
+  int memory_count() const {
+    if (!s_.convkv) return 0;
+    int64_t m = evicted_frames_ / s_.kernel;
+    return (int)std::min<int64_t>(s_.memory_frames, m);
+  }
+  int64_t context_tokens() const {
+    int64_t n = 0;
+    for (auto& g : segs_) n += g.tokens;
+    return n;
+  }
+  bool attended(int layer) const { return attended_[layer]; }
+
+  // Open the next block: take a free slot, lay out its context.  false if open.
+  bool open() {
+    if (open_ || free_.empty()) return false;
+    cur_slot_ = free_.back();
+    free_.pop_back();
+    open_ = true;
+    attended_.assign(s_.layers, false);
+    build_segments();
+    return true;
+  }
+
+  bool mark_attended(int layer) {
+    if (!open_ || layer < 0 || layer >= s_.layers) return false;
+    attended_[layer] = true;
+    return true;
+  }
+
+  bool all_attended() const {
+    for (bool a : attended_)
+      if (!a) return false;
+    return true;
+  }
+
+  // Close the open block.  On success fills `taps` (ConvKV: the frames the
+  // memory is rebuilt from, tap order, n_mem*kernel entries; empty = none).
+  bool commit(std::vector<ConvTap>* taps) {
+    if (!open_ || !all_attended()) return false;
+    taps->clear();
+    const int64_t m = next_;
+    last_evicted_ = -1;
+    if (!s_.convkv) {
+      if ((int)static_.size() < s_.statics) {
+        static_.push_back({m, cur_slot_});
+      } else {
+        window_.push_back({m, cur_slot_});
+        if ((int)window_.size() > s_.window) {
+          auto e = window_.front();
+          window_.pop_front();
+          last_evicted_ = e.first;
+          if (s_.bank > 0) {
+            bank_.push_back(e);
+            if ((int)bank_.size() > s_.bank) {
+              free_.push_back(bank_.front().second);
+              bank_.pop_front();
+            }
+          } else {
+            free_.push_back(e.second);
+          }
+        }
+      }
+    } else {
+      window_.push_back({m, cur_slot_});
+      if ((int)window_.size() > s_.window) {
+        auto e = window_.front();
+        window_.pop_front();
+        last_evicted_ = e.first;
+        staged_.push_back(e);
+        evicted_frames_ += s_.frames;
+        if ((int)staged_.size() > staged_max_) {
+          free_.push_back(staged_.front().second);
+          staged_.pop_front();
+        }
+        int n_mem = memory_count();
+        if (n_mem > 0) {
+          // newest n_mem*kernel evicted frames, oldest first
+          int64_t first = evicted_frames_ - (int64_t)n_mem * s_.kernel;
+          for (int64_t f = first; f < evicted_frames_; ++f) {
+            int64_t b = f / s_.frames;
+            int slot = -1;
+            for (auto& st : staged_)
+              if (st.first == b) slot = st.second;
+            taps->push_back({slot, (int)(f % s_.frames)});
+          }
+        }
+      }
+    }
+    open_ = false;
+    cur_slot_ = -1;
+    segs_.clear();
+    ++next_;
+    return true;
+  }
+
+ private:
+  void build_segments() {
+    segs_.clear();
+    const int64_t m = next_;
+    const int F = s_.frames;
+    if (!s_.convkv) {
+      for (auto& st : static_) segs_.push_back({SEG_STATIC, st.first, T_, st.first * F, st.second, -1, 0});
+      for (int j = 0; j < n_dynamic(); ++j) segs_.push_back({SEG_DYNAMIC, -1, T_, -1, -1, j, 0});
+      for (auto& w : window_) segs_.push_back({SEG_WINDOW, w.first, T_, w.first * F, w.second, -1, 0});
+      segs_.push_back({SEG_CURRENT, m, T_, m * F, cur_slot_, -1, 0});
+    } else {
+      const int n_mem = memory_count();
+      const int Tf = s_.tokens_per_frame;
+      int off = 0;
+      for (int j = 0; j < n_mem; ++j) {
+        segs_.push_back({SEG_MEMORY, j, Tf, j, -1, -1, off});
+        off += Tf;
+      }
+      int64_t t = n_mem;
+      for (auto& w : window_) {
+        segs_.push_back({SEG_WINDOW, w.first, T_, t, w.second, -1, off});
+        off += T_;
+        t += F;
+      }
+      segs_.push_back({SEG_CURRENT, m, T_, t, cur_slot_, -1, off});
+    }
+  }
+
+  Shape s_;
+  int T_ = 0, n_slots_ = 0, staged_max_ = 0;
+  int64_t next_ = 0;
+  bool open_ = false;
+  int cur_slot_ = -1;
+  std::deque<std::pair<int64_t, int>> static_, window_, bank_, staged_;
+  std::vector<int> free_;
+  int64_t evicted_frames_ = 0;
+  int64_t last_evicted_ = -1;
+  std::vector<bool> attended_;
+  std::vector<SegPlan> segs_;
+};
+
+}  // namespace bkv

@@ -1,0 +1,223 @@
+/*
+ * bkv.h -- C ABI of the bounded-KV block attention library (libbkv.so), MI355X / gfx950.
+ *
+ * What it computes.  Streaming block-causal attention for autoregressive
+ * video-DiT avatar generation over a cache of constant size:
+ *
+ *   PR-Sink (LiveAnimate page, section 方法, the three PR-Sink bullets; section
+ *   关键发现, constant memory and per-block latency): block m's queries attend
+ *   to a static sink (the first generated block, kept for good), dynamic sink
+ *   blocks retrieved by pose similarity (same page, section 局限), a rolling
+ *   window of the last three blocks, and block m itself (full attention inside
+ *   the block).
+ *
+ *   ConvKV (Soul App开源实时数字人生成框架SoulX-LiveAct详解 page, section 技术内核,
+ *   ConvKV Memory bullet): the last blocks keep exact KV; older frames are
+ *   compressed along time by a 1D conv (stride = kernel, 5:1) into a fixed
+ *   memory, and RoPE positions restart from 0 over [memory, window, current].
+ *
+ * One stream of blocks per handle.  Per block: bkv_retrieve (opens block m,
+ * runs the pose top-k), then bkv_attend for every (sampling step, layer), then
+ * bkv_commit (appends block m, evicts, compresses).  The sampling steps of a
+ * block all read the same context; a block's K/V enter the cache as written by
+ * its last bkv_attend per layer (LiveAnimate page, section 方法: three steps).
+ *
+ * Memory.  The library never allocates device memory.  The caller provides one
+ * device workspace of bkv_workspace_size() bytes at create time; the cache,
+ * pose bank, RoPE tables, selection and scratch are carved from it, so cache
+ * bytes are constant over the stream by construction.  Q/K/V/out, the pose and
+ * the conv weights are caller-owned device buffers, read or written only
+ * during the call's stream work.  The handle holds a little host state.
+ *
+ * Streams.  Every device operation is enqueued on the caller's stream; no
+ * call synchronizes except those documented as synchronizing.  A handle is
+ * not thread-safe; use one handle per host thread.
+ *
+ * Errors.  Every call returns bkv_status and never throws.  BKV_ERR_ARG and
+ * BKV_ERR_STATE leave the handle unchanged.  BKV_ERR_DEVICE (a failed launch
+ * or runtime call) puts the handle in an error state in which everything but
+ * bkv_reset/bkv_destroy/bkv_stats returns BKV_ERR_STATE.  bkv_last_error()
+ * returns a message for the last non-OK status of the calling thread.
+ */
+#ifndef BKV_H_
+#define BKV_H_
+
+#include <stddef.h>
+#include <stdint.h>
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef struct bkv_cache_s* bkv_cache; /* opaque handle: one per stream of blocks */
+
+typedef enum {
+  BKV_OK = 0,
+  BKV_ERR_ARG = 1,         /* null pointer, bad size/shape/dtype, layer out of range, bad config */
+  BKV_ERR_STATE = 2,       /* call out of order (see each call), or handle in error state */
+  BKV_ERR_WORKSPACE = 3,   /* workspace too small or misaligned (256-byte alignment needed) */
+  BKV_ERR_DEVICE = 4,      /* HIP launch or runtime error */
+  BKV_ERR_UNSUPPORTED = 5  /* valid request this build does not implement */
+} bkv_status;
+
+typedef enum { BKV_PR_SINK = 0, BKV_CONVKV = 1 } bkv_mode;
+typedef enum { BKV_F32 = 0, BKV_BF16 = 1 } bkv_dtype;
+
+typedef enum {
+  BKV_SEG_STATIC = 0,   /* static sink block */
+  BKV_SEG_DYNAMIC = 1,  /* pose-retrieved bank block */
+  BKV_SEG_WINDOW = 2,   /* rolling-window block */
+  BKV_SEG_CURRENT = 3,  /* the open block */
+  BKV_SEG_MEMORY = 4    /* ConvKV compressed memory frame */
+} bkv_segment_kind;
+
+/* Cache configuration.  Set struct_size = sizeof(bkv_config) (ABI guard). */
+typedef struct {
+  uint32_t struct_size;
+  int32_t mode;             /* bkv_mode */
+  int32_t dtype;            /* bkv_dtype of Q/K/V/out and of the cache */
+  int32_t layers;           /* >= 1; each layer has its own cache */
+  int32_t heads;            /* >= 1 */
+  int32_t head_dim;         /* 64 or 128 (bf16 path: 128) */
+  int32_t frames_per_block; /* latent frames per block, >= 1 */
+  int32_t grid_h, grid_w;   /* latent grid; tokens per block T = frames*grid_h*grid_w */
+  int32_t window_blocks;    /* rolling window length, >= 1 (3 on the pages) */
+  int32_t static_blocks;    /* PR-Sink: 0 or 1 (block 0 is the sink); ConvKV: 0 */
+  int32_t dynamic_k;        /* PR-Sink: blocks retrieved per block, 0..8; ConvKV: 0 */
+  int32_t bank_blocks;      /* PR-Sink: FIFO bank of evicted blocks, 0..256; ConvKV: 0 */
+  int32_t pose_dim;         /* PR-Sink with dynamic_k > 0: 1..1024 fp32 values per pose */
+  int32_t rope_t, rope_h, rope_w; /* RoPE channel split [t|h|w]; all 0 = none, else each
+                                     even and summing to head_dim */
+  double rope_theta;        /* RoPE base, > 0 (10000) */
+  int32_t conv_kernel;      /* ConvKV: taps (5); must equal conv_stride */
+  int32_t conv_stride;      /* ConvKV: stride (5) */
+  int32_t memory_frames;    /* ConvKV: compressed frames kept, 1..4 */
+  float softmax_scale;      /* 0 -> 1/sqrt(head_dim) */
+} bkv_config;
+
+/* One context segment as the open block sees it (host view). */
+typedef struct {
+  int32_t kind;    /* bkv_segment_kind */
+  int32_t id;      /* block stream id; memory: memory-frame index */
+  int32_t tokens;  /* keys contributed */
+  int32_t t0;      /* RoPE temporal position of the segment's first frame (PR-Sink: absolute
+                      id*frames_per_block; ConvKV: context-relative) */
+} bkv_segment;
+
+typedef struct {
+  int64_t block;           /* id of the open block, or of the next block if none is open */
+  int32_t open;            /* 1 between bkv_retrieve and bkv_commit */
+  int32_t n_segments;      /* segments of the open block's context (0 if closed) */
+  int64_t n_keys;          /* keys of the open block's context (0 if closed) */
+  int64_t last_evicted;    /* id that left the window at the last commit, -1 if none */
+  int32_t bank_count;      /* PR-Sink: blocks in the bank */
+  int32_t memory_count;    /* ConvKV: memory frames present */
+  size_t workspace_bytes;  /* bytes of workspace in use (constant for the handle's life) */
+} bkv_stats_t;
+
+/* Workspace bytes needed for cfg.  Pure host call.
+   Errors: BKV_ERR_ARG for a null pointer or an invalid config. */
+bkv_status bkv_workspace_size(const bkv_config* cfg, size_t* bytes);
+
+/* Create a handle on the current HIP device over a caller-owned device
+   workspace (>= bkv_workspace_size bytes, 256-byte aligned; the caller frees it
+   after bkv_destroy).  Builds the RoPE tables in the workspace on `stream`.
+   The new handle is at block 0 with no block open.
+   Errors: BKV_ERR_ARG (config), BKV_ERR_WORKSPACE, BKV_ERR_DEVICE. */
+bkv_status bkv_create(const bkv_config* cfg, void* workspace, size_t bytes, hipStream_t stream,
+                      bkv_cache* out);
+
+/* Destroy the handle (host state only).  The caller must make sure work
+   enqueued on the handle's streams has finished before freeing the workspace. */
+bkv_status bkv_destroy(bkv_cache h);
+
+/* Back to block 0, empty cache, error state cleared.  No (de)allocation; conv
+   weights already set are kept. */
+bkv_status bkv_reset(bkv_cache h);
+
+/* ConvKV: set layer's depthwise conv weights from device buffers wk, wv, each
+   fp32 [heads][head_dim][conv_kernel] (tap 0 multiplies the oldest frame).
+   Copied into the workspace on `stream`; the caller's buffers may be reused
+   once that copy ran.  Errors: BKV_ERR_UNSUPPORTED on a PR-Sink handle. */
+bkv_status bkv_set_conv_weights(bkv_cache h, int32_t layer, const float* wk, const float* wv,
+                                hipStream_t stream);
+
+/* Open the next block m (pose retrieval; LiveAnimate page, section 方法, Dynamic
+   Sink bullet).  pose: device fp32 [pose_dim], the block's pose embedding; it is
+   stored with the block for later retrieval.  Selects the top-min(dynamic_k,
+   bank_count) bank blocks by cosine similarity to `pose` (fp64 arithmetic;
+   exact ties to the lower stream id; a zero-norm pose scores 0) on the device:
+   the host is not synchronized.  ConvKV: pose may be NULL.
+   Errors: BKV_ERR_STATE if a block is already open; BKV_ERR_ARG if pose is NULL
+   where needed. */
+bkv_status bkv_retrieve(bkv_cache h, const float* pose, hipStream_t stream);
+
+/* Attention of the open block at `layer` for one sampling step.  q, k, v, out:
+   device, dtype, contiguous [T][heads][head_dim] token-major (token index
+   (f*grid_h + y)*grid_w + x).  Rotates K (3D RoPE at the block's positions) and
+   stores K, V as the open block's entry of `layer` (a later call for the same
+   layer in the same block overwrites it), then writes
+       out[i] = sum_j softmax_j(scale * q~_i . k~_j) v_j
+   over every key j of the context (q~, k~ rotated), accumulating in fp32.
+   out must not alias q, k or v.
+   Errors: BKV_ERR_STATE if no block is open; BKV_ERR_ARG (layer, null). */
+bkv_status bkv_attend(bkv_cache h, int32_t layer, const void* q, const void* k, const void* v,
+                      void* out, hipStream_t stream);
+
+/* Close the open block: it joins the window; the oldest window block leaves
+   (PR-Sink: into the FIFO bank, the oldest bank block dropped when full;
+   ConvKV: its raw frames feed the conv memory, rebuilt here on `stream` once
+   conv_kernel frames were evicted).  Errors: BKV_ERR_STATE if no block is open
+   or some layer was not attended in this block. */
+bkv_status bkv_commit(bkv_cache h, hipStream_t stream);
+
+/* Stream ids retrieved for the open block, in rank order (cosine descending,
+   id ascending).  Synchronizes `stream`.  ids: host, capacity cap; *n = count.
+   Errors: BKV_ERR_STATE if no block is open; BKV_ERR_ARG if cap < count. */
+bkv_status bkv_selection(bkv_cache h, int32_t* ids, int32_t cap, int32_t* n, hipStream_t stream);
+
+/* Context of the open block in attention order: static, dynamic (rank order),
+   window (oldest first), current; ConvKV: memory, window, current.  segs: host,
+   capacity cap.  Synchronizes `stream` when the context has dynamic segments. */
+bkv_status bkv_context(bkv_cache h, bkv_segment* segs, int32_t cap, int32_t* n, hipStream_t stream);
+
+/* Counters of the handle (host only). */
+bkv_status bkv_stats(bkv_cache h, bkv_stats_t* out);
+
+/* Inspection: copy context segment `seg` of the open block at `layer` as
+   attention reads it -- K rotated, V as stored -- into device k_out, v_out
+   [tokens][heads][head_dim] in the cache dtype.  For the current segment this
+   needs an earlier bkv_attend of `layer` in this block.
+   Errors: BKV_ERR_STATE (no open block / current block not yet written). */
+bkv_status bkv_export_segment(bkv_cache h, int32_t layer, int32_t seg, void* k_out, void* v_out,
+                              hipStream_t stream);
+
+/* Per-kernel device time, measured with HIP events recorded on the caller's
+   stream immediately before and after each kernel the handle launches. */
+typedef struct {
+  char kernel[24];         /* "retrieve", "append", "attention", "gather", "conv", "export" */
+  int64_t launches;
+  double total_ms;         /* sum of per-launch event intervals */
+  double max_ms;
+} bkv_kernel_time;
+
+/* Start recording per-launch kernel times for up to max_launches launches
+   (later launches are not timed).  Creates 2*max_launches HIP events (host
+   call, no device memory from the workspace).  Errors: BKV_ERR_STATE if a
+   recording is already running; BKV_ERR_ARG if max_launches < 1. */
+bkv_status bkv_profile_start(bkv_cache h, int32_t max_launches);
+
+/* Stop recording: waits for the recorded events, sums the intervals per
+   kernel into out[0..*n) (capacity cap) and releases the events.
+   Errors: BKV_ERR_STATE if no recording is running; BKV_ERR_ARG if cap is too small. */
+bkv_status bkv_profile_stop(bkv_cache h, bkv_kernel_time* out, int32_t cap, int32_t* n);
+
+/* Human-readable name of a status; message of the calling thread's last error. */
+const char* bkv_status_str(bkv_status s);
+const char* bkv_last_error(void);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* BKV_H_ */

@@ -1,0 +1,131 @@
+"""GPU parity of the PR-Sink path (through the C-ABI) against the CPU oracle.
+
+Retrieval and eviction indices must match exactly; attention outputs within
+max-abs 1e-5 (fp32 path) and 2e-2 (bf16 path) of the fp64 oracle."""
+import numpy as np
+import pytest
+
+import oracle
+from bounded_kv_block_amd import synth
+from gpu_helpers import TOL, Run, max_err
+
+pytestmark = pytest.mark.gpu
+
+
+def _check_block(run, ref, m, layer=0, step=0, heads=None, rows=None, out=None):
+    cfg = run.cfg
+    want_sel = ref.selection(m)
+    got_sel = run.cache.selection()
+    assert got_sel == want_sel, (m, got_sel, want_sel)
+    ctx = run.cache.context()
+    want_ctx = ref.context(m, want_sel)
+    assert ctx == [(k, b, t, t0) for k, b, t, t0 in want_ctx], (m, ctx, want_ctx)
+    if out is None:
+        out = run.attend(m, layer, step)
+    want = ref.attend(m, layer, step, heads=heads, rows=rows, selection=want_sel)
+    err = max_err(out, want, heads, rows)
+    print(f"block {m} layer {layer} step {step}: keys {sum(c[2] for c in ctx)} max|err| {err:.3e}", flush=True)
+    assert err <= TOL[cfg["dtype"]], (m, err)
+    return out
+
+
+def _stream(cfg, host_inputs=True, check=None, heads=None, rows=None):
+    run = Run(cfg, host_inputs)
+    ref = oracle.PRSinkReference(cfg, run)
+    for m in range(cfg["blocks"]):
+        run.open(m)
+        if check is None or m in check:
+            _check_block(run, ref, m, heads=heads, rows=rows)
+        else:
+            assert run.cache.selection() == ref.selection(m)
+            run.attend(m, 0, 0)
+        run.cache.commit()
+        st = run.cache.stats()
+        want_ev = oracle.prsink_schedule(m, cfg["window"], cfg["bank"], cfg["static"])["evicted"]
+        assert st["last_evicted"] == (-1 if want_ev is None else want_ev)
+        if not host_inputs:
+            run.drop(set(range(m - 70, m + 2)))
+    return run
+
+
+def test_tiny_fp32_stream():
+    """12-block fp32 stream, 2 heads x 64, top-1 over 32-d poses: every block, every output."""
+    cfg = synth.workload("tiny_fp32")
+    src = synth.repeat_sources(cfg)
+    run = Run(cfg)
+    ref = oracle.PRSinkReference(cfg, run)
+    for m in range(cfg["blocks"]):
+        run.open(m)
+        _check_block(run, ref, m)
+        if m in (7, 11):
+            assert run.cache.selection() == [src[m]]          # repeat pose -> that block
+        run.cache.commit()
+    st = run.cache.stats()
+    assert st["block"] == 12 and st["bank_count"] == 8
+
+
+def test_tiny_fp32_rope_and_d128():
+    for kw in (dict(rope=(24, 20, 20)), dict(head_dim=128, rope=(44, 42, 42))):
+        cfg = synth.workload("tiny_fp32", **kw)
+        _stream(cfg)
+
+
+def test_bf16_small_ragged():
+    """bf16, 3 heads, 3 frames of 6x10 = 180 tokens (two full 64-key tiles and a
+    52-key tail per segment, a ragged query tile), RoPE 44/42/42, top-2 over a
+    bank of 4, 14 blocks: every output of every block."""
+    cfg = synth.workload("prsink_512", heads=3, grid_h=6, grid_w=10, bank=4, blocks=14, pose_dim=16,
+                         keyframes=5)
+    _stream(cfg)
+
+
+def test_bf16_single_token_blocks():
+    """Degenerate block of one token (one key per segment, one query)."""
+    cfg = synth.workload("prsink_512", heads=2, frames=1, grid_h=1, grid_w=1, bank=3, blocks=10,
+                         pose_dim=8, keyframes=3, rope=(44, 42, 42))
+    _stream(cfg)
+
+
+def test_prsink_512_full_shape_sampled():
+    """512x512-shaped workload at full size (40 x 128, 3072 queries, 21504 keys
+    once warm): indices on every block, outputs sampled (2 heads, 160 query rows
+    including the last) on blocks 0, 4, 6 and 9."""
+    cfg = synth.workload("prsink_512", blocks=10)
+    rows = np.r_[0:64, 1500:1532, 3008:3072]
+    _stream(cfg, host_inputs=False, check={0, 4, 6, 9}, heads=[0, 39], rows=rows)
+
+
+def test_multistep_multilayer_commit_after_last_step():
+    """3 layers x 3 steps per block; the cache keeps each layer's last-step K/V."""
+    cfg = synth.workload("prsink_512", heads=2, grid_h=4, grid_w=10, bank=3, blocks=9, pose_dim=16,
+                         keyframes=4, layers=3, steps=3)
+    run = Run(cfg)
+    ref = oracle.PRSinkReference(cfg, run)
+    for m in range(cfg["blocks"]):
+        run.open(m)
+        sel = ref.selection(m)
+        assert run.cache.selection() == sel
+        for s in range(3):
+            for l in range(3):
+                out = run.attend(m, l, s)
+                want = ref.attend(m, l, s, selection=sel)
+                err = max_err(out, want)
+                assert err <= TOL["bf16"], (m, l, s, err)
+        run.cache.commit()
+
+
+def test_export_segments_match_oracle_context():
+    """Stored K (rotated at absolute positions) and V of every context segment."""
+    cfg = synth.workload("prsink_512", heads=2, grid_h=4, grid_w=6, bank=4, blocks=9, pose_dim=16, keyframes=4)
+    run = Run(cfg)
+    ref = oracle.PRSinkReference(cfg, run)
+    for m in range(cfg["blocks"]):
+        run.open(m)
+        run.attend(m, 0, 0)
+        kv = ref.context_kv(m, 0, 0, [0, 1], ref.selection(m))
+        for i, (_, _, kr, v) in enumerate(kv):
+            gk, gv = run.cache.export_segment(0, i)
+            # K: rotation in fp32 then rounding to bf16: within one bf16 ulp
+            assert np.max(np.abs(gk.float().cpu().numpy() - kr)) <= 2.0 ** -7 * np.max(np.abs(kr)) + 1e-6
+            assert np.array_equal(gv.float().cpu().numpy(), v)
+        run.cache.commit()

@@ -1,0 +1,220 @@
+"""CPU tests of the host side: the state machine in schedule.hpp (built with g++
+through a test shim) against the oracle's schedules, and the C-ABI library's
+exports and pure-host calls (no device work)."""
+import ctypes
+import os
+import re
+import subprocess
+
+import numpy as np
+import pytest
+
+import oracle
+from conftest import ROOT
+
+CSRC = os.path.join(ROOT, "bounded_kv_block_amd", "csrc")
+SHIM_SRC = os.path.join(ROOT, "tests", "csrc", "schedule_shim.cpp")
+
+
+@pytest.fixture(scope="module")
+def shim(tmp_path_factory):
+    out = str(tmp_path_factory.mktemp("shim") / "libschedshim.so")
+    subprocess.run(["g++", "-std=c++17", "-O1", "-shared", "-fPIC", f"-I{CSRC}", SHIM_SRC, "-o", out],
+                   check=True)
+    L = ctypes.CDLL(out)
+    L.sched_new.restype = ctypes.c_void_p
+    L.sched_new.argtypes = [ctypes.c_int] * 10
+    for n in ("sched_free",):
+        getattr(L, n).argtypes = [ctypes.c_void_p]
+    for n in ("sched_n_slots", "sched_open", "sched_cur_slot", "sched_memory_count", "sched_n_dynamic"):
+        getattr(L, n).argtypes = [ctypes.c_void_p]
+        getattr(L, n).restype = ctypes.c_int
+    L.sched_mark.argtypes = [ctypes.c_void_p, ctypes.c_int]
+    L.sched_last_evicted.argtypes = [ctypes.c_void_p]
+    L.sched_last_evicted.restype = ctypes.c_int64
+    L.sched_commit.argtypes = [ctypes.c_void_p, ctypes.POINTER(ctypes.c_int), ctypes.POINTER(ctypes.c_int),
+                               ctypes.c_int, ctypes.POINTER(ctypes.c_int)]
+    L.sched_segments.argtypes = [ctypes.c_void_p, ctypes.POINTER(ctypes.c_int64), ctypes.c_int]
+    L.sched_bank.argtypes = [ctypes.c_void_p, ctypes.POINTER(ctypes.c_int64), ctypes.POINTER(ctypes.c_int),
+                             ctypes.c_int]
+    return L
+
+
+class Sched:
+    def __init__(self, L, **kw):
+        self.L = L
+        self.layers = kw.get("layers", 1)
+        args = [kw.get("convkv", 0), self.layers, kw["frames"], kw["tpf"], kw["window"], kw.get("statics", 0),
+                kw.get("k", 0), kw.get("bank", 0), kw.get("kernel", 1), kw.get("memory_frames", 0)]
+        self.p = L.sched_new(*args)
+
+    def __del__(self):
+        self.L.sched_free(self.p)
+
+    def segments(self):
+        buf = (ctypes.c_int64 * (7 * 32))()
+        n = self.L.sched_segments(self.p, buf, 32)
+        return [tuple(buf[7 * i:7 * i + 7]) for i in range(n)]
+
+    def bank(self):
+        ids = (ctypes.c_int64 * 300)()
+        slots = (ctypes.c_int * 300)()
+        n = self.L.sched_bank(self.p, ids, slots, 300)
+        return [int(ids[i]) for i in range(n)], [int(slots[i]) for i in range(n)]
+
+    def commit(self):
+        ts = (ctypes.c_int * 64)()
+        tf = (ctypes.c_int * 64)()
+        n = ctypes.c_int(0)
+        ok = self.L.sched_commit(self.p, ts, tf, 64, ctypes.byref(n))
+        return ok, [(ts[i], tf[i]) for i in range(n.value)]
+
+
+STATIC, DYNAMIC, WINDOW, CURRENT, MEMORY = range(5)
+
+
+@pytest.mark.parametrize("W,B,S,k", [(3, 8, 1, 1), (3, 56, 1, 2), (3, 16, 1, 2), (3, 64, 1, 2), (3, 0, 0, 0),
+                                     (2, 3, 1, 3), (1, 1, 0, 1), (4, 5, 1, 0)])
+def test_prsink_state_machine_matches_oracle(shim, W, B, S, k):
+    F, tpf = 3, 4
+    T = F * tpf
+    s = Sched(shim, frames=F, tpf=tpf, window=W, statics=S, k=k, bank=B)
+    n_slots = shim.sched_n_slots(s.p)
+    assert n_slots == S + W + 1 + B
+    slot_of = {}
+    for m in range(90):
+        assert shim.sched_open(s.p) == 1
+        assert shim.sched_open(s.p) == 0                     # already open
+        want = oracle.prsink_schedule(m, W, B, S)
+        segs = s.segments()
+        kinds = [g[0] for g in segs]
+        nd = min(k, len(want["bank"]))
+        assert kinds == [STATIC] * len(want["static"]) + [DYNAMIC] * nd + [WINDOW] * len(want["window"]) + [CURRENT]
+        assert [g[1] for g in segs if g[0] == STATIC] == want["static"]
+        assert [g[1] for g in segs if g[0] == WINDOW] == want["window"]
+        assert [g[5] for g in segs if g[0] == DYNAMIC] == list(range(nd))
+        assert all(g[2] == T for g in segs)
+        for g in segs:
+            if g[0] != DYNAMIC:
+                assert g[3] == g[1] * F                      # absolute temporal position
+        bank_ids, bank_slots = s.bank()
+        assert bank_ids == want["bank"]
+        cur = shim.sched_cur_slot(s.p)
+        slot_of[m] = cur
+        # every block in the cache owns its slot; slots are never shared
+        live = [g[4] for g in segs if g[0] != DYNAMIC] + bank_slots
+        assert len(set(live)) == len(live) and all(0 <= x < n_slots for x in live)
+        for g in segs:
+            if g[0] in (STATIC, WINDOW):
+                assert g[4] == slot_of[g[1]]                 # a block keeps its slot
+        for b, sl in zip(bank_ids, bank_slots):
+            assert sl == slot_of[b]
+        ok, taps = s.commit()
+        assert ok == 0                                       # not every layer attended
+        shim.sched_mark(s.p, 0)
+        ok, taps = s.commit()
+        assert ok == 1 and taps == []
+        ev = shim.sched_last_evicted(s.p)
+        assert ev == (-1 if want["evicted"] is None else want["evicted"])
+
+
+@pytest.mark.parametrize("F,tpf,W,K,M", [(3, 4, 3, 5, 1), (2, 3, 3, 5, 1), (1, 5, 2, 3, 2), (4, 2, 3, 5, 2),
+                                         (3, 1024, 3, 5, 1)])
+def test_convkv_state_machine_matches_oracle(shim, F, tpf, W, K, M):
+    T = F * tpf
+    s = Sched(shim, convkv=1, frames=F, tpf=tpf, window=W, kernel=K, memory_frames=M, layers=2)
+    n_slots = shim.sched_n_slots(s.p)
+    staged = -(-K * M // F)
+    assert n_slots == W + 1 + staged
+    slot_of = {}
+    for m in range(40):
+        assert shim.sched_open(s.p) == 1
+        want = oracle.convkv_schedule(m, F, W, K, M)
+        segs = s.segments()
+        n_mem = len(want["memory"])
+        assert shim.sched_memory_count(s.p) == n_mem
+        assert [g[0] for g in segs] == [MEMORY] * n_mem + [WINDOW] * len(want["window"]) + [CURRENT]
+        assert [g[1] for g in segs if g[0] == WINDOW] == want["window"]
+        assert [g[3] for g in segs if g[0] == WINDOW] == want["t0"]["window"]
+        assert segs[-1][3] == want["t0"]["current"]
+        assert [g[3] for g in segs if g[0] == MEMORY] == list(range(n_mem))
+        offs = np.cumsum([0] + [g[2] for g in segs])[:-1]
+        assert [g[6] for g in segs] == list(offs)             # contiguous context-K rows
+        assert [g[2] for g in segs] == [tpf] * n_mem + [T] * (len(segs) - n_mem)
+        slot_of[m] = shim.sched_cur_slot(s.p)
+        shim.sched_mark(s.p, 0)
+        ok, _ = s.commit()
+        assert ok == 0                                       # layer 1 not attended
+        shim.sched_mark(s.p, 1)
+        ok, taps = s.commit()
+        assert ok == 1
+        nxt = oracle.convkv_schedule(m + 1, F, W, K, M)
+        want_taps = [(slot_of[e // F], e % F) for grp in nxt["memory"] for e in grp]
+        if m - W >= 0:                                       # something was evicted: memory rebuilt
+            assert taps == want_taps, m
+        else:
+            assert taps == []
+        # taps only read blocks that are no longer in the window (staged slots)
+        win_slots = {slot_of[b] for b in nxt["window"]}
+        assert not (set(t[0] for t in taps) & win_slots)
+
+
+# ------------------------------------------------------------------ C-ABI exports
+def _declared():
+    with open(os.path.join(ROOT, "include", "bkv.h")) as fh:
+        text = fh.read()
+    return sorted(set(re.findall(r"^\s*(?:bkv_status|const char\*)\s+(bkv_\w+)\s*\(", text, re.M)))
+
+
+def test_library_exports_every_declared_symbol():
+    from bounded_kv_block_amd import bkv
+    declared = _declared()
+    assert set(declared) == set(bkv.EXPORTS)
+    out = subprocess.run(["nm", "-D", "--defined-only", bkv.LIB_PATH], capture_output=True, text=True,
+                         check=True).stdout
+    exported = set(re.findall(r"\bT (bkv_\w+)", out))
+    assert set(declared) <= exported, set(declared) - exported
+    L = bkv.lib()
+    for name in declared:
+        assert hasattr(L, name)
+
+
+def test_workspace_size_and_validation():
+    from bounded_kv_block_amd import bkv, synth
+    c2 = bkv.config_from_workload(synth.workload("prsink_512"))
+    n = bkv.workspace_size(c2)
+    slot = 2 * 40 * 3072 * 128 * 2
+    assert 61 * slot <= n < 61 * slot + (1 << 20)            # 61 slots of 62.9 MB
+    c3 = bkv.config_from_workload(synth.workload("prsink_720x416"))
+    assert bkv.workspace_size(c3) >= 40 * 21 * 2 * 40 * 3520 * 128 * 2
+    c5 = bkv.config_from_workload(synth.workload("convkv_512"))
+    n5 = bkv.workspace_size(c5)
+    ctx = 13312 * 40 * 128 * 2                               # rotated context K
+    mem = 2 * 1024 * 40 * 128 * 2                            # memory frame K + V
+    assert 6 * slot + ctx + mem <= n5 < 6 * slot + ctx + mem + (1 << 20)
+    c1 = bkv.config_from_workload(synth.workload("tiny_fp32"))
+    assert bkv.workspace_size(c1) > 13 * 2 * 2 * 128 * 64 * 4
+    bad = [dict(rope=(44, 42, 40)), dict(rope=(43, 43, 42)), dict(window=0), dict(dynamic_k=9),
+           dict(bank=257), dict(head_dim=64), dict(layers=0)]
+    for b in bad:
+        with pytest.raises(bkv.BkvError) as ei:
+            bkv.workspace_size(bkv.config_from_workload(synth.workload("prsink_512", **b)))
+        assert ei.value.status in (bkv.BKV_ERR_ARG, bkv.BKV_ERR_UNSUPPORTED), b
+    c = bkv.config_from_workload(synth.workload("prsink_512"))
+    c.struct_size = 12
+    with pytest.raises(bkv.BkvError):
+        bkv.workspace_size(c)
+    bad5 = bkv.config_from_workload(synth.workload("convkv_512", conv_stride=4))
+    with pytest.raises(bkv.BkvError):
+        bkv.workspace_size(bad5)
+    assert bkv.lib().bkv_status_str(bkv.BKV_ERR_STATE) == b"BKV_ERR_STATE"
+
+
+def test_workspace_is_constant_in_stream_length():
+    """Cache bytes do not depend on how long the stream runs: no config field
+    names a stream length, and the 1080-block workload needs the same bytes as
+    a 60-block one with the same bank."""
+    from bounded_kv_block_amd import bkv, synth
+    a = bkv.workspace_size(bkv.config_from_workload(synth.workload("prsink_long")))
+    b = bkv.workspace_size(bkv.config_from_workload(synth.workload("prsink_long", blocks=60)))
+    assert a == b
