@@ -40,7 +40,28 @@ def parse():
     ap.add_argument("--pool", type=int, default=4, help="distinct resident input blocks cycled through")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=12.0, help="target CPU-oracle sample time")
+    ap.add_argument("--calibrate-copy", type=int, default=0, metavar="MIB",
+                    help="only run a plain device-to-device copy of MIB MiB (a known-size reference "
+                         "for the HBM byte counters) and exit")
     return ap.parse_args()
+
+
+def calibrate_copy(mib):
+    import torch
+    n = mib << 20
+    src = torch.empty(n, dtype=torch.uint8, device="cuda").fill_(1)
+    dst = torch.empty_like(src)
+    torch.cuda.synchronize()
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
+    dst.copy_(src)
+    ev[0].record()
+    for _ in range(5):
+        dst.copy_(src)
+    ev[1].record()
+    torch.cuda.synchronize()
+    ms = ev[0].elapsed_time(ev[1]) / 5
+    print(json.dumps({"copy_bytes_read": n, "copy_bytes_written": n, "avg_ms": ms,
+                      "gbs": 2 * n / (ms * 1e-3) / 1e9}), flush=True)
 
 
 def steady_block(cfg):
@@ -106,7 +127,7 @@ def cpu_baseline(cfg, run_inputs, poses, m, target_s):
     return {"value": T * done / H / dt, "unit": "query tokens/s", "cores": int(blas),
             "host_cpus": len(os.sched_getaffinity(0)), "kind": "oracle",
             "sample": f"block {m} of the {cfg['name']} stream: retrieval + fp64 attention of {done}/{H} heads "
-                      f"x all {T} queries over {ref.attend.__self__.__class__.__name__} context, "
+                      f"x all {T} queries over the block's bounded context, "
                       f"{dt:.1f} s; value scaled to the whole block (x{H}/{done})"}
 
 
@@ -118,6 +139,10 @@ def main():
               "the bounded-KV path shards by heads across GPUs, which this build does not run.",
               file=sys.stderr)
         sys.exit(2)
+
+    if args.calibrate_copy:
+        calibrate_copy(args.calibrate_copy)
+        return
 
     import numpy as np
     import torch

@@ -119,7 +119,8 @@ Layout layout_of(const bkv_config* c, const bkv::Schedule& sch) {
   L.off_ctx = off;
   L.off_mem = off;
   if (c->mode == BKV_CONVKV) {
-    L.ctx_ld = (int)align_up(sch.max_context_tokens(), bkv::kTokAlign);
+    // + one tile: the last segment's partial tile reads up to 63 rows past its end
+    L.ctx_ld = (int)align_up(sch.max_context_tokens(), bkv::kTokAlign) + bkv::kTokAlign;
     L.ctx_layer_bytes = align_up(H * L.ctx_ld * D * L.esize, 256);
     off = align_up(off + L.ctx_layer_bytes * c->layers, 256);
     L.off_mem = off;
@@ -355,6 +356,13 @@ bkv_status bkv_create(const bkv_config* cfg, void* workspace, size_t bytes, hipS
   if (e != hipSuccess) {
     delete h;
     return fail(BKV_ERR_DEVICE, "hipGetDevice: %s", hipGetErrorString(e));
+  }
+  // Zero once: attention tiles read the pad columns of V^T buffers (never
+  // written afterwards) and must see finite values there.
+  e = hipMemsetAsync(workspace, 0, need, stream);
+  if (e != hipSuccess) {
+    delete h;
+    return fail(BKV_ERR_DEVICE, "workspace clear: %s", hipGetErrorString(e));
   }
   const double theta = cfg->rope_theta;
   if (cfg->rope_h) e = bkv::launch_rope_table(h->htab(), cfg->grid_h, cfg->rope_h, 0, theta, stream);

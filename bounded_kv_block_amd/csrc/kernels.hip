@@ -15,6 +15,8 @@
 #include <math.h>
 #include <stdint.h>
 
+#include <type_traits>
+
 #include "kernels.hpp"
 
 namespace bkv {
@@ -224,12 +226,26 @@ __global__ __launch_bounds__(256) void append_kernel(AppendArgs a) {
 // from the accumulators: the contraction index k = 8h + e stands for key
 // 16h + 8*part + e on both operands.
 // Row statistics: a query's 64 scores of a tile sit in lanes l and l^32.
+//
+// K/V tiles move HBM -> LDS with global_load_lds_dwordx4 (no register
+// staging), double-buffered: tile t+1 is in flight while tile t is computed.
+// LDS layouts are XOR-swizzled so that every 16-lane phase of a ds_read_b128
+// touches all 64 banks once (gfx950 LDS: 64 banks x 4 B, 16 lanes per cycle).
+// Loads are unpredicated: a partial tile reads the zeroed pad rows/columns
+// of its buffer, and its scores beyond the segment are masked to -inf.
+// The running max is only moved when a tile's max exceeds it by more than
+// 2^8 (scores are in log2 units), so O is rarely rescaled.
 constexpr int ABM = 128, ABN = 64, AD = 128;
 constexpr int KT_BYTES = ABN * AD * 2;
 constexpr int VT_BYTES = AD * ABN * 2;
 constexpr int STAGE_BYTES = KT_BYTES + VT_BYTES;
+constexpr float kRescaleSlack = 8.0f;
 
-__device__ __forceinline__ int kswz(int r) { return (r & 3) | ((r >> 2) & 4); }
+// K tile: 64 rows x 16 chunks of 16 B.  Rows read together by a 16-lane phase
+// are {0-7, 16-23} (+8, +32): (r & 7) | ((r & 16) >> 1) separates all 16.
+__device__ __forceinline__ int kswz(int r) { return (r & 7) | ((r & 16) >> 1); }
+// V^T tile: 128 rows x 8 chunks; two rows share a 256-B bank line.
+__device__ __forceinline__ int vswz(int d) { return (d >> 1) & 7; }
 __device__ __forceinline__ int kperm(int r) { return ((r >> 2) & 1) * 16 + (r >> 3) * 4 + (r & 3); }
 
 __device__ __forceinline__ int xcd_remap(int bid, int nwg) {
@@ -240,11 +256,20 @@ __device__ __forceinline__ int xcd_remap(int bid, int nwg) {
   return xcd * q + min(xcd, r) + (bid >> 3);
 }
 
+typedef __attribute__((address_space(3))) void* lds_ptr_t;
+
+__device__ __forceinline__ const char* uniform_ptr(const void* p) {
+  const unsigned long long v = reinterpret_cast<unsigned long long>(p);
+  const unsigned lo = __builtin_amdgcn_readfirstlane((unsigned)v);
+  const unsigned hi = __builtin_amdgcn_readfirstlane((unsigned)(v >> 32));
+  return reinterpret_cast<const char*>(((unsigned long long)hi << 32) | lo);
+}
+
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2)))
 void attn_bf16_kernel(AttnArgs a) {
-  __shared__ __attribute__((aligned(16))) char lds[2 * STAGE_BYTES];
-  __shared__ const __bf16* s_k[kMaxSeg];
-  __shared__ const __bf16* s_v[kMaxSeg];
+  __shared__ __attribute__((aligned(1024))) char lds[2 * STAGE_BYTES];
+  __shared__ const char* s_k[kMaxSeg];
+  __shared__ const char* s_v[kMaxSeg];
   __shared__ int s_n[kMaxSeg];
   __shared__ int s_ld[kMaxSeg];
 
@@ -274,8 +299,8 @@ void attn_bf16_kernel(AttnArgs a) {
       vhs = sg.v_hs;
       ld = sg.v_ld;
     }
-    s_k[tid] = reinterpret_cast<const __bf16*>(kb) + head * khs;
-    s_v[tid] = reinterpret_cast<const __bf16*>(vb) + head * vhs;
+    s_k[tid] = kb + 2 * head * khs;
+    s_v[tid] = vb + 2 * head * vhs;
     s_n[tid] = sg.n;
     s_ld[tid] = ld;
   }
@@ -307,50 +332,35 @@ void attn_bf16_kernel(AttnArgs a) {
   }
   __syncthreads();
 
-  uint4 kreg[4], vreg[4];
-  auto gload = [&](int sg, int j0) {
-    const __bf16* kb = s_k[sg];
-    const __bf16* vb = s_v[sg];
-    const int n = s_n[sg], ld = s_ld[sg];
+  // Per-lane byte offsets of this lane's 16-byte chunks in a tile (LDS side
+  // fixed by the DMA: chunk p = (4i + wave)*64 + lane lands at LDS p*16).
+  unsigned koff[4], voff[4];
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int r = (tid >> 4) + 16 * i, c = tid & 15;
-      kreg[i] = (j0 + r < n) ? *reinterpret_cast<const uint4*>(kb + (size_t)(j0 + r) * AD + c * 8)
-                             : make_uint4(0, 0, 0, 0);
-    }
+  for (int i = 0; i < 4; ++i) {
+    const int p = (4 * i + wave) * 64 + lane;
+    koff[i] = (unsigned)((p >> 4) * 256 + (((p & 15) ^ kswz(p >> 4)) << 4));
+  }
+  int cur_ld = -1;
+  auto issue = [&](int sg, int j0, int stage) {
+    const char* kb = uniform_ptr(s_k[sg]) + (size_t)j0 * 256;
+    const char* vb = uniform_ptr(s_v[sg]) + (size_t)j0 * 2;
+    const int ld = __builtin_amdgcn_readfirstlane(s_ld[sg]);
+    if (ld != cur_ld) {
+      cur_ld = ld;
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int d = (tid >> 3) + 32 * i, c = tid & 7;
-      const int key0 = j0 + 8 * c;
-      uint4 v = make_uint4(0, 0, 0, 0);
-      if (key0 < n) {
-        v = *reinterpret_cast<const uint4*>(vb + (size_t)d * ld + key0);
-        const int valid = n - key0;
-        if (valid < 8) {
-          uint32_t* w = reinterpret_cast<uint32_t*>(&v);
-#pragma unroll
-          for (int e = 0; e < 4; ++e) {
-            if (2 * e >= valid) w[e] = 0u;
-            else if (2 * e + 1 >= valid) w[e] &= 0x0000ffffu;
-          }
-        }
+      for (int i = 0; i < 4; ++i) {
+        const int p = (4 * i + wave) * 64 + lane;
+        voff[i] = (unsigned)((p >> 3) * ld * 2 + (((p & 7) ^ vswz(p >> 3)) << 4));
       }
-      vreg[i] = v;
     }
-  };
-  auto lstore = [&](int stage) {
     char* kt = lds + stage * STAGE_BYTES;
     char* vt = kt + KT_BYTES;
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int r = (tid >> 4) + 16 * i, c = tid & 15;
-      *reinterpret_cast<uint4*>(kt + r * 256 + ((c ^ kswz(r)) << 4)) = kreg[i];
-    }
+    for (int i = 0; i < 4; ++i)
+      __builtin_amdgcn_global_load_lds(kb + koff[i], (lds_ptr_t)(kt + (4 * i + wave) * 1024), 16, 0, 0);
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int d = (tid >> 3) + 32 * i, c = tid & 7;
-      *reinterpret_cast<uint4*>(vt + d * 128 + ((c ^ (d & 7)) << 4)) = vreg[i];
-    }
+    for (int i = 0; i < 4; ++i)
+      __builtin_amdgcn_global_load_lds(vb + voff[i], (lds_ptr_t)(vt + (4 * i + wave) * 1024), 16, 0, 0);
   };
 
   f32x16 o[4];
@@ -358,79 +368,137 @@ void attn_bf16_kernel(AttnArgs a) {
   for (int i = 0; i < 4; ++i) o[i] = f32x16{};
   float m_run = -INFINITY, l_run = 0.f;
 
-  int sg = 0, j0 = 0, stage = 0;
-  while (sg < a.nseg && s_n[sg] == 0) ++sg;
-  if (sg < a.nseg) {
-    gload(sg, 0);
-    lstore(0);
-  }
-  __syncthreads();
-  while (sg < a.nseg) {
-    int nsg = sg, nj0 = j0 + ABN;
-    if (nj0 >= s_n[sg]) {
-      nsg = sg + 1;
-      nj0 = 0;
-      while (nsg < a.nseg && s_n[nsg] == 0) ++nsg;
-    }
-    const bool more = nsg < a.nseg;
-    if (more) gload(nsg, nj0);
-
-    const char* kt = lds + stage * STAGE_BYTES;
-    const char* vt = kt + KT_BYTES;
-    const int nvalid = s_n[sg] - j0;
-    f32x16 sacc[2];
+  auto tile = [&](const char* kt, const char* vt, int nvalid, auto masked) {
+    // S^T: two independent accumulators (keys 0-31, 32-63) advanced in
+    // lockstep so consecutive MFMAs never wait on each other.
+    f32x16 sacc[2] = {f32x16{}, f32x16{}};
+    const int r0 = kperm(col), r1 = 32 + kperm(col);
 #pragma unroll
-    for (int mb = 0; mb < 2; ++mb) {
-      sacc[mb] = f32x16{};
-      const int r = 32 * mb + kperm(col);
-#pragma unroll
-      for (int s = 0; s < 8; ++s) {
-        const int c = 2 * s + hh;
-        const bf16x8 kv = *reinterpret_cast<const bf16x8*>(kt + r * 256 + ((c ^ kswz(r)) << 4));
-        sacc[mb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kv, qreg[s], sacc[mb], 0, 0, 0);
-      }
+    for (int s = 0; s < 8; ++s) {
+      const int c = 2 * s + hh;
+      const bf16x8 k0 = *reinterpret_cast<const bf16x8*>(kt + r0 * 256 + ((c ^ kswz(r0)) << 4));
+      const bf16x8 k1 = *reinterpret_cast<const bf16x8*>(kt + r1 * 256 + ((c ^ kswz(r1)) << 4));
+      sacc[0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(k0, qreg[s], sacc[0], 0, 0, 0);
+      sacc[1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(k1, qreg[s], sacc[1], 0, 0, 0);
     }
-    if (nvalid < ABN) {
+    if constexpr (decltype(masked)::value) {
 #pragma unroll
       for (int mb = 0; mb < 2; ++mb)
 #pragma unroll
         for (int i = 0; i < 16; ++i)
           if (32 * mb + 16 * hh + i >= nvalid) sacc[mb][i] = -INFINITY;
     }
-    float mx = sacc[0][0];
+    // row max: a tree over the 32 scores this lane holds, then the partner lane
+    float t8[8];
 #pragma unroll
-    for (int mb = 0; mb < 2; ++mb)
+    for (int i = 0; i < 8; ++i)
+      t8[i] = fmaxf(fmaxf(sacc[0][2 * i], sacc[0][2 * i + 1]), fmaxf(sacc[1][2 * i], sacc[1][2 * i + 1]));
 #pragma unroll
-      for (int i = 0; i < 16; ++i) mx = fmaxf(mx, sacc[mb][i]);
-    mx = fmaxf(mx, __shfl_xor(mx, 32));
-    const float m_new = fmaxf(m_run, mx);
-    const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);
-    m_run = m_new;
-    l_run *= alpha;
+    for (int w = 4; w >= 1; w >>= 1)
 #pragma unroll
-    for (int db = 0; db < 4; ++db) o[db] *= alpha;
+      for (int i = 0; i < w; ++i) t8[i] = fmaxf(t8[i], t8[i + w]);
+    float mx = fmaxf(t8[0], __shfl_xor(t8[0], 32));
+    if (__any(mx > m_run + kRescaleSlack)) {
+      const float m_new = fmaxf(m_run, mx);
+      const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);
+      m_run = m_new;
+      l_run *= alpha;
+#pragma unroll
+      for (int db = 0; db < 4; ++db) o[db] *= alpha;
+    }
     bf16x8 pb[2][2];
+    float pr[32];
 #pragma unroll
     for (int mb = 0; mb < 2; ++mb)
 #pragma unroll
       for (int i = 0; i < 16; ++i) {
-        const float p = __builtin_amdgcn_exp2f(sacc[mb][i] - m_new);
-        l_run += p;
-        pb[mb][i >> 3][i & 7] = (__bf16)p;
+        pr[16 * mb + i] = __builtin_amdgcn_exp2f(sacc[mb][i] - m_run);
+        pb[mb][i >> 3][i & 7] = (__bf16)pr[16 * mb + i];
       }
+    // O^T += V^T P^T: the 4 channel blocks are independent accumulators
 #pragma unroll
-    for (int db = 0; db < 4; ++db) {
-      const int d = 32 * db + col;
+    for (int mb = 0; mb < 2; ++mb)
 #pragma unroll
-      for (int mb = 0; mb < 2; ++mb)
+      for (int part = 0; part < 2; ++part) {
+        const int c = 4 * mb + 2 * hh + part;
 #pragma unroll
-        for (int part = 0; part < 2; ++part) {
-          const int c = 4 * mb + 2 * hh + part;
-          const bf16x8 vv = *reinterpret_cast<const bf16x8*>(vt + d * 128 + ((c ^ (d & 7)) << 4));
+        for (int db = 0; db < 4; ++db) {
+          const int d = 32 * db + col;
+          const bf16x8 vv = *reinterpret_cast<const bf16x8*>(vt + d * 128 + ((c ^ vswz(d)) << 4));
           o[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vv, pb[mb][part], o[db], 0, 0, 0);
         }
+      }
+    // row-sum partials: a tree instead of one serial chain
+#pragma unroll
+    for (int w = 16; w >= 1; w >>= 1)
+#pragma unroll
+      for (int i = 0; i < w; ++i) pr[i] += pr[i + w];
+    l_run += pr[0];
+  };
+
+  // Tile order: every full 64-key tile of every segment first (phase 0), then
+  // the partial tail tile of each segment whose length is not a multiple of 64
+  // (phase 1).  Attention does not depend on key order, and the mask code then
+  // lives in its own loop.  Cursor = (phase, segment, first key); all uniform.
+  const int nseg = a.nseg;
+  auto first_tail = [&](int from) {
+    int g = from;
+    while (g < nseg && (s_n[g] & (ABN - 1)) == 0) ++g;
+    return g;
+  };
+  auto first_full = [&](int from) {
+    int g = from;
+    while (g < nseg && s_n[g] < ABN) ++g;
+    return g;
+  };
+  int phase = 0, sg = first_full(0), j0 = 0;
+  if (sg >= nseg) {
+    phase = 1;
+    sg = first_tail(0);
+    j0 = sg < nseg ? (s_n[sg] & ~(ABN - 1)) : 0;
+  }
+  auto advance = [&](int& ph, int& g, int& j) {
+    if (ph == 0) {
+      j += ABN;
+      if (j + ABN > s_n[g]) {
+        g = first_full(g + 1);
+        j = 0;
+        if (g >= nseg) {
+          ph = 1;
+          g = first_tail(0);
+          j = g < nseg ? (s_n[g] & ~(ABN - 1)) : 0;
+        }
+      }
+    } else {
+      g = first_tail(g + 1);
+      j = g < nseg ? (s_n[g] & ~(ABN - 1)) : 0;
     }
-    if (more) lstore(stage ^ 1);
+  };
+
+  int stage = 0;
+  if (sg < nseg) issue(sg, j0, 0);
+  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+  __syncthreads();
+  while (phase == 0) {
+    int nph = phase, nsg = sg, nj0 = j0;
+    advance(nph, nsg, nj0);
+    if (nsg < nseg) issue(nsg, nj0, stage ^ 1);
+    const char* kt = lds + stage * STAGE_BYTES;
+    tile(kt, kt + KT_BYTES, ABN, std::false_type{});
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    __syncthreads();
+    phase = nph;
+    sg = nsg;
+    j0 = nj0;
+    stage ^= 1;
+  }
+  while (sg < nseg) {
+    int nph = phase, nsg = sg, nj0 = j0;
+    advance(nph, nsg, nj0);
+    if (nsg < nseg) issue(nsg, nj0, stage ^ 1);
+    const char* kt = lds + stage * STAGE_BYTES;
+    tile(kt, kt + KT_BYTES, s_n[sg] - j0, std::true_type{});
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
     __syncthreads();
     sg = nsg;
     j0 = nj0;

@@ -122,7 +122,8 @@ bkv_status bkv_workspace_size(const bkv_config* cfg, size_t* bytes);
 
 /* Create a handle on the current HIP device over a caller-owned device
    workspace (>= bkv_workspace_size bytes, 256-byte aligned; the caller frees it
-   after bkv_destroy).  Builds the RoPE tables in the workspace on `stream`.
+   after bkv_destroy).  Clears the workspace and builds the RoPE tables in it
+   on `stream`.
    The new handle is at block 0 with no block open.
    Errors: BKV_ERR_ARG (config), BKV_ERR_WORKSPACE, BKV_ERR_DEVICE. */
 bkv_status bkv_create(const bkv_config* cfg, void* workspace, size_t bytes, hipStream_t stream,

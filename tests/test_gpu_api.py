@@ -94,7 +94,17 @@ def test_reset_replay_is_bitwise_identical():
 
 
 def test_memory_is_flat_over_the_stream():
+    import gc
     import torch
+    gc.collect()                     # objects of earlier tests must not be freed mid-loop
+    gc.disable()
+    try:
+        _memory_flat(torch)
+    finally:
+        gc.enable()
+
+
+def _memory_flat(torch):
     cfg = _small(blocks=40)
     run = Run(cfg)
     q, k, v = run.qkv_dev(0, 0, 0)
