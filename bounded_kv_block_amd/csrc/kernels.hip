@@ -215,30 +215,39 @@ __global__ __launch_bounds__(256) void append_kernel(AppendArgs a) {
 }
 
 // ------------------------------------------------------------------ attention, bf16 MFMA
-// Workgroup = 4 waves x 32 queries (BM = 128) of one head; key tiles of 64.
+// Workgroup = 8 waves x 32 queries (BM = 256) of one head; key tiles of 64.
 //
-// S^T = K Q^T with v_mfma_f32_32x32x16_bf16: A = 32 keys x 16 channels (one
-// 16-byte LDS read per lane), B = Q^T held in registers for the whole loop.
-// MFMA row r is mapped to tile key pi(r) = 16*((r>>2)&1) + 4*(r>>3) + (r&3), so
-// lane half h's 16 accumulators are the 16 consecutive keys 16h..16h+15 of the
-// 32-key block for query (lane & 31).  O^T += V^T P^T then reads A = V^T as 8
-// consecutive keys of one channel (one 16-byte LDS read) and B = P^T straight
-// from the accumulators: the contraction index k = 8h + e stands for key
-// 16h + 8*part + e on both operands.
-// Row statistics: a query's 64 scores of a tile sit in lanes l and l^32.
+// Per wave and tile t: S(t) = K(t) Q^T (16 MFMA), softmax(t) (VALU: max,
+// exp2, bf16 pack, row sum), PV(t) = V^T(t) P^T(t) (16 MFMA).  The waves form
+// two groups of four (one wave of each group per SIMD) that run the same
+// program half a tile apart: while group A issues its MFMA block [PV(t-1),
+// S(t)] group B runs its softmax block, then they swap.  Whole-workgroup
+// barriers between blocks keep the two groups in antiphase, so each SIMD's
+// matrix core and vector ALU work at the same time.
 //
-// K/V tiles move HBM -> LDS with global_load_lds_dwordx4 (no register
-// staging), double-buffered: tile t+1 is in flight while tile t is computed.
-// LDS layouts are XOR-swizzled so that every 16-lane phase of a ds_read_b128
+// MFMA layouts (v_mfma_f32_32x32x16_bf16).  S^T: A = 32 keys x 16 channels
+// (one 16-byte LDS read per lane), B = Q^T kept in registers.  MFMA row r is
+// tile key pi(r) = 16*((r>>2)&1) + 4*(r>>3) + (r&3), so lane half h holds the
+// 16 consecutive keys 16h..16h+15 of a 32-key block for query (lane & 31).
+// O^T += V^T P^T reads A = V^T as 8 consecutive keys of one channel (one
+// 16-byte LDS read) and B = P^T straight from registers: contraction index
+// k = 8h + e stands for key 16h + 8*part + e on both operands.  A query's
+// scores sit in lanes l and l^32.
+//
+// K/V tiles move HBM -> LDS with buffer_load ... lds (no register staging),
+// three stages deep: tile t+2 is loaded while tiles t and t-1 are read.  LDS
+// layouts are XOR-swizzled so that every 16-lane phase of a ds_read_b128
 // touches all 64 banks once (gfx950 LDS: 64 banks x 4 B, 16 lanes per cycle).
 // Loads are unpredicated: a partial tile reads the zeroed pad rows/columns
-// of its buffer, and its scores beyond the segment are masked to -inf.
-// The running max is only moved when a tile's max exceeds it by more than
-// 2^8 (scores are in log2 units), so O is rarely rescaled.
-constexpr int ABM = 128, ABN = 64, AD = 128;
+// of its buffer and its scores beyond the segment are masked to -inf.
+// Scores come out of the S MFMA already relative to the running max m (the
+// chain starts from C = -m); m only moves when a tile's max exceeds it by
+// more than 2^8, so O is rarely rescaled.
+constexpr int ABM = 256, ABN = 64, AD = 128, AWAVES = 8;
 constexpr int KT_BYTES = ABN * AD * 2;
 constexpr int VT_BYTES = AD * ABN * 2;
 constexpr int STAGE_BYTES = KT_BYTES + VT_BYTES;
+constexpr int NSTAGE = 3;
 constexpr float kRescaleSlack = 8.0f;
 
 // K tile: 64 rows x 16 chunks of 16 B.  Rows read together by a 16-lane phase
@@ -265,21 +274,72 @@ __device__ __forceinline__ const char* uniform_ptr(const void* p) {
   return reinterpret_cast<const char*>(((unsigned long long)hi << 32) | lo);
 }
 
-__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2)))
+// Workgroup barrier without a memory fence (tile loads are waited for
+// explicitly with vmcnt before the barrier that publishes them).  The
+// scheduling fences keep each block's instructions on its side.
+__device__ __forceinline__ void wg_barrier() {
+  __builtin_amdgcn_sched_barrier(0);
+  asm volatile("" ::: "memory");
+  __builtin_amdgcn_s_barrier();
+  asm volatile("" ::: "memory");
+  __builtin_amdgcn_sched_barrier(0);
+}
+
+typedef int i32x4 __attribute__((ext_vector_type(4)));
+
+// Raw buffer descriptor over [base, base + 2 GiB), stride 0 (base uniform).
+__device__ __forceinline__ i32x4 buffer_rsrc(const char* base) {
+  const unsigned long long b = reinterpret_cast<unsigned long long>(base);
+  i32x4 r;
+  r[0] = (int)__builtin_amdgcn_readfirstlane((unsigned)b);
+  r[1] = (int)__builtin_amdgcn_readfirstlane((unsigned)(b >> 32) & 0xffffu);
+  r[2] = 0x7fffffff;
+  r[3] = 0x00020000;
+  return r;
+}
+
+// 16 bytes per lane from buffer (voff + soff) into LDS at lds_base + 16*lane
+// (buffer_load_dwordx4 ... lds).  Written in asm so that the compiler does
+// not treat every later LDS read as waiting on it: the caller waits with
+// vmcnt(0) before the barrier that publishes the tile.  No register output.
+__device__ __forceinline__ void dma16(i32x4 rsrc, unsigned voff, unsigned soff, unsigned lds_base) {
+  // every scalar operand must sit in SGPRs, never a folded literal
+  asm volatile("" : "+s"(soff), "+s"(rsrc), "+s"(lds_base));
+  asm volatile(
+      "s_mov_b32 m0, %0\n\t"
+      "s_nop 0\n\t"
+      "buffer_load_dwordx4 %1, %2, %3 offen lds"
+      :
+      : "s"(lds_base), "v"(voff), "s"(rsrc), "s"(soff)
+      : "memory", "m0");
+}
+
+// Tile cursor over the context segments: every full 64-key tile of every
+// segment first (phase 0), then the partial tail tile of each segment whose
+// length is not a multiple of 64 (phase 1).  Attention does not depend on
+// key order.  All fields are wave-uniform.
+struct TileCursor {
+  int phase, sg, j0;
+};
+
+__global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2)))
 void attn_bf16_kernel(AttnArgs a) {
-  __shared__ __attribute__((aligned(1024))) char lds[2 * STAGE_BYTES];
+  __shared__ __attribute__((aligned(1024))) char lds[NSTAGE * STAGE_BYTES];
   __shared__ const char* s_k[kMaxSeg];
   __shared__ const char* s_v[kMaxSeg];
   __shared__ int s_n[kMaxSeg];
   __shared__ int s_ld[kMaxSeg];
 
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);   // uniform by construction
+  const int group = wave >> 2, gw = wave & 3;           // ping-pong group, wave in group
   const int hh = lane >> 5, col = lane & 31;
   const int nqt = (a.T + ABM - 1) / ABM;
   const int logical = xcd_remap(blockIdx.x, gridDim.x);
   const int head = logical / nqt, qt = logical - head * nqt;
+  const int nseg = a.nseg;
 
-  if (tid < a.nseg) {
+  if (tid < nseg) {
     const Seg sg = a.seg[tid];
     const char* kb;
     const char* vb;
@@ -332,90 +392,107 @@ void attn_bf16_kernel(AttnArgs a) {
   }
   __syncthreads();
 
-  // Per-lane byte offsets of this lane's 16-byte chunks in a tile (LDS side
-  // fixed by the DMA: chunk p = (4i + wave)*64 + lane lands at LDS p*16).
+  // ---- tile enumeration (segment metadata read as wave-uniform values)
+  auto seg_n = [&](int g) { return __builtin_amdgcn_readfirstlane(s_n[g]); };
+  auto first_tail = [&](int from) {
+    int g = from;
+    while (g < nseg && (seg_n(g) & (ABN - 1)) == 0) ++g;
+    return g;
+  };
+  auto first_full = [&](int from) {
+    int g = from;
+    while (g < nseg && seg_n(g) < ABN) ++g;
+    return g;
+  };
+  auto cursor_begin = [&]() {
+    TileCursor c{0, first_full(0), 0};
+    if (c.sg >= nseg) {
+      c.phase = 1;
+      c.sg = first_tail(0);
+      c.j0 = c.sg < nseg ? (seg_n(c.sg) & ~(ABN - 1)) : 0;
+    }
+    return c;
+  };
+  auto advance = [&](TileCursor& c) {
+    if (c.sg >= nseg) return;
+    if (c.phase == 0) {
+      c.j0 += ABN;
+      if (c.j0 + ABN > seg_n(c.sg)) {
+        c.sg = first_full(c.sg + 1);
+        c.j0 = 0;
+        if (c.sg >= nseg) {
+          c.phase = 1;
+          c.sg = first_tail(0);
+          c.j0 = c.sg < nseg ? (seg_n(c.sg) & ~(ABN - 1)) : 0;
+        }
+      }
+    } else {
+      c.sg = first_tail(c.sg + 1);
+      c.j0 = c.sg < nseg ? (seg_n(c.sg) & ~(ABN - 1)) : 0;
+    }
+  };
+  int NT = 0;
+  for (int g = 0; g < nseg; ++g) NT += (seg_n(g) + ABN - 1) / ABN;
+
+  // ---- tile loads: chunk p = (4i + w)*64 + lane of a tile lands at LDS p*16
+  // (w = wave within the loading group of four); the tile's first key enters
+  // as the scalar offset of the buffer load.
   unsigned koff[4], voff[4];
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
-    const int p = (4 * i + wave) * 64 + lane;
+    const int p = (4 * i + gw) * 64 + lane;
     koff[i] = (unsigned)((p >> 4) * 256 + (((p & 15) ^ kswz(p >> 4)) << 4));
   }
-  int cur_ld = -1;
-  auto issue = [&](int sg, int j0, int stage) {
-    const char* kb = uniform_ptr(s_k[sg]) + (size_t)j0 * 256;
-    const char* vb = uniform_ptr(s_v[sg]) + (size_t)j0 * 2;
-    const int ld = __builtin_amdgcn_readfirstlane(s_ld[sg]);
-    if (ld != cur_ld) {
-      cur_ld = ld;
+  int cur_ld = -1, cur_sg = -1;
+  i32x4 krs = {0, 0, 0, 0}, vrs = {0, 0, 0, 0};
+  const unsigned lds0 = (unsigned)(uintptr_t)(lds_ptr_t)lds;
+  auto issue = [&](const TileCursor& c, int stage) {   // by one group of four waves
+    if (c.sg != cur_sg) {
+      cur_sg = c.sg;
+      krs = buffer_rsrc(uniform_ptr(s_k[c.sg]));
+      vrs = buffer_rsrc(uniform_ptr(s_v[c.sg]));
+      const int ld = __builtin_amdgcn_readfirstlane(s_ld[c.sg]);
+      if (ld != cur_ld) {
+        cur_ld = ld;
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const int p = (4 * i + wave) * 64 + lane;
-        voff[i] = (unsigned)((p >> 3) * ld * 2 + (((p & 7) ^ vswz(p >> 3)) << 4));
+        for (int i = 0; i < 4; ++i) {
+          const int p = (4 * i + gw) * 64 + lane;
+          voff[i] = (unsigned)((p >> 3) * ld * 2 + (((p & 7) ^ vswz(p >> 3)) << 4));
+        }
       }
     }
-    char* kt = lds + stage * STAGE_BYTES;
-    char* vt = kt + KT_BYTES;
+    const unsigned kt = __builtin_amdgcn_readfirstlane(lds0 + stage * STAGE_BYTES + gw * 1024);
+    const unsigned vt = kt + KT_BYTES;
+    const unsigned j0 = __builtin_amdgcn_readfirstlane((unsigned)c.j0);
 #pragma unroll
-    for (int i = 0; i < 4; ++i)
-      __builtin_amdgcn_global_load_lds(kb + koff[i], (lds_ptr_t)(kt + (4 * i + wave) * 1024), 16, 0, 0);
+    for (int i = 0; i < 4; ++i) dma16(krs, koff[i], j0 * 256u, kt + i * 4096);
 #pragma unroll
-    for (int i = 0; i < 4; ++i)
-      __builtin_amdgcn_global_load_lds(vb + voff[i], (lds_ptr_t)(vt + (4 * i + wave) * 1024), 16, 0, 0);
+    for (int i = 0; i < 4; ++i) dma16(vrs, voff[i], j0 * 2u, vt + i * 4096);
   };
 
+  // ---- per-wave state
   f32x16 o[4];
 #pragma unroll
   for (int i = 0; i < 4; ++i) o[i] = f32x16{};
-  float m_run = -INFINITY, l_run = 0.f;
+  float m_run = 0.f, l_run = 0.f;
+  f32x16 negm = f32x16{};
+  bool first = true;
+  f32x16 sacc[2];
+  bf16x8 pb[2][2];
+  typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
 
-  auto tile = [&](const char* kt, const char* vt, int nvalid, auto masked) {
-    // S^T: two independent accumulators (keys 0-31, 32-63) advanced in
-    // lockstep so consecutive MFMAs never wait on each other.
-    f32x16 sacc[2] = {f32x16{}, f32x16{}};
+  auto s_mfma = [&](const char* kt) {
     const int r0 = kperm(col), r1 = 32 + kperm(col);
 #pragma unroll
     for (int s = 0; s < 8; ++s) {
       const int c = 2 * s + hh;
       const bf16x8 k0 = *reinterpret_cast<const bf16x8*>(kt + r0 * 256 + ((c ^ kswz(r0)) << 4));
       const bf16x8 k1 = *reinterpret_cast<const bf16x8*>(kt + r1 * 256 + ((c ^ kswz(r1)) << 4));
-      sacc[0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(k0, qreg[s], sacc[0], 0, 0, 0);
-      sacc[1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(k1, qreg[s], sacc[1], 0, 0, 0);
+      sacc[0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(k0, qreg[s], s ? sacc[0] : negm, 0, 0, 0);
+      sacc[1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(k1, qreg[s], s ? sacc[1] : negm, 0, 0, 0);
     }
-    if constexpr (decltype(masked)::value) {
-#pragma unroll
-      for (int mb = 0; mb < 2; ++mb)
-#pragma unroll
-        for (int i = 0; i < 16; ++i)
-          if (32 * mb + 16 * hh + i >= nvalid) sacc[mb][i] = -INFINITY;
-    }
-    // row max: a tree over the 32 scores this lane holds, then the partner lane
-    float t8[8];
-#pragma unroll
-    for (int i = 0; i < 8; ++i)
-      t8[i] = fmaxf(fmaxf(sacc[0][2 * i], sacc[0][2 * i + 1]), fmaxf(sacc[1][2 * i], sacc[1][2 * i + 1]));
-#pragma unroll
-    for (int w = 4; w >= 1; w >>= 1)
-#pragma unroll
-      for (int i = 0; i < w; ++i) t8[i] = fmaxf(t8[i], t8[i + w]);
-    float mx = fmaxf(t8[0], __shfl_xor(t8[0], 32));
-    if (__any(mx > m_run + kRescaleSlack)) {
-      const float m_new = fmaxf(m_run, mx);
-      const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);
-      m_run = m_new;
-      l_run *= alpha;
-#pragma unroll
-      for (int db = 0; db < 4; ++db) o[db] *= alpha;
-    }
-    bf16x8 pb[2][2];
-    float pr[32];
-#pragma unroll
-    for (int mb = 0; mb < 2; ++mb)
-#pragma unroll
-      for (int i = 0; i < 16; ++i) {
-        pr[16 * mb + i] = __builtin_amdgcn_exp2f(sacc[mb][i] - m_run);
-        pb[mb][i >> 3][i & 7] = (__bf16)pr[16 * mb + i];
-      }
-    // O^T += V^T P^T: the 4 channel blocks are independent accumulators
+  };
+  auto pv_mfma = [&](const char* vt) {
 #pragma unroll
     for (int mb = 0; mb < 2; ++mb)
 #pragma unroll
@@ -428,81 +505,103 @@ void attn_bf16_kernel(AttnArgs a) {
           o[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vv, pb[mb][part], o[db], 0, 0, 0);
         }
       }
-    // row-sum partials: a tree instead of one serial chain
+  };
+  auto softmax = [&](int nvalid) {
+    if (nvalid < ABN) {
+      asm volatile("" ::: "memory");     // keep the tail mask a real branch
 #pragma unroll
-    for (int w = 16; w >= 1; w >>= 1)
+      for (int mb = 0; mb < 2; ++mb)
 #pragma unroll
-      for (int i = 0; i < w; ++i) pr[i] += pr[i + w];
-    l_run += pr[0];
-  };
-
-  // Tile order: every full 64-key tile of every segment first (phase 0), then
-  // the partial tail tile of each segment whose length is not a multiple of 64
-  // (phase 1).  Attention does not depend on key order, and the mask code then
-  // lives in its own loop.  Cursor = (phase, segment, first key); all uniform.
-  const int nseg = a.nseg;
-  auto first_tail = [&](int from) {
-    int g = from;
-    while (g < nseg && (s_n[g] & (ABN - 1)) == 0) ++g;
-    return g;
-  };
-  auto first_full = [&](int from) {
-    int g = from;
-    while (g < nseg && s_n[g] < ABN) ++g;
-    return g;
-  };
-  int phase = 0, sg = first_full(0), j0 = 0;
-  if (sg >= nseg) {
-    phase = 1;
-    sg = first_tail(0);
-    j0 = sg < nseg ? (s_n[sg] & ~(ABN - 1)) : 0;
-  }
-  auto advance = [&](int& ph, int& g, int& j) {
-    if (ph == 0) {
-      j += ABN;
-      if (j + ABN > s_n[g]) {
-        g = first_full(g + 1);
-        j = 0;
-        if (g >= nseg) {
-          ph = 1;
-          g = first_tail(0);
-          j = g < nseg ? (s_n[g] & ~(ABN - 1)) : 0;
-        }
-      }
-    } else {
-      g = first_tail(g + 1);
-      j = g < nseg ? (s_n[g] & ~(ABN - 1)) : 0;
+        for (int i = 0; i < 16; ++i)
+          if (32 * mb + 16 * hh + i >= nvalid) sacc[mb][i] = -INFINITY;
     }
+    // row max: four independent max3 chains over the lane's 32 scores
+    float c4[4];
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      const f32x16& v = sacc[q >> 1];
+      const int b = (q & 1) * 8;
+      float x = __builtin_fmaxf(__builtin_fmaxf(v[b], v[b + 1]), v[b + 2]);
+      x = __builtin_fmaxf(__builtin_fmaxf(x, v[b + 3]), v[b + 4]);
+      x = __builtin_fmaxf(__builtin_fmaxf(x, v[b + 5]), v[b + 6]);
+      c4[q] = __builtin_fmaxf(x, v[b + 7]);
+    }
+    float mx = __builtin_fmaxf(__builtin_fmaxf(c4[0], c4[1]), __builtin_fmaxf(c4[2], c4[3]));
+    mx = fmaxf(mx, __shfl_xor(mx, 32));                   // max of (s - m) over the row's tile
+    if (first) {
+      first = false;                                      // m := this tile's row max
+      m_run += mx;
+#pragma unroll
+      for (int i = 0; i < 16; ++i) {
+        negm[i] = -m_run;
+        sacc[0][i] -= mx;
+        sacc[1][i] -= mx;
+      }
+    } else if (__any(mx > kRescaleSlack)) {
+      const float dm = fmaxf(mx, 0.f);
+      const float alpha = __builtin_amdgcn_exp2f(-dm);
+      m_run += dm;
+      l_run *= alpha;
+#pragma unroll
+      for (int db = 0; db < 4; ++db) o[db] *= alpha;
+#pragma unroll
+      for (int i = 0; i < 16; ++i) {
+        negm[i] = -m_run;
+        sacc[0][i] -= dm;
+        sacc[1][i] -= dm;
+      }
+    }
+#pragma unroll
+    for (int mb = 0; mb < 2; ++mb)
+#pragma unroll
+      for (int i = 0; i < 16; ++i) pb[mb][i >> 3][i & 7] = (__bf16)__builtin_amdgcn_exp2f(sacc[mb][i]);
+    // row sum of the bf16 P actually fed to the MFMA, two bf16 per dot2
+    const bf16x2_t one2 = {(__bf16)1.0f, (__bf16)1.0f};
+    float ls[4] = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int q = 0; q < 4; ++q)
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const bf16x2_t pr = {pb[q >> 1][q & 1][2 * e], pb[q >> 1][q & 1][2 * e + 1]};
+        ls[q] = __builtin_amdgcn_fdot2_f32_bf16(pr, one2, ls[q], false);
+      }
+    l_run += (ls[0] + ls[1]) + (ls[2] + ls[3]);
   };
+  auto stage_of = [](int t) { return t % NSTAGE; };
 
-  int stage = 0;
-  if (sg < nseg) issue(sg, j0, 0);
+  // ---- prologue: tiles 0 and 1 loaded by group 0 (all waves wait)
+  TileCursor xc = cursor_begin();          // tile of the next softmax
+  TileCursor lc = xc;                      // tile of the next load
+  if (group == 0) {
+    if (NT > 0) issue(lc, 0);
+    advance(lc);
+    if (NT > 1) issue(lc, 1);
+  } else {
+    advance(lc);
+  }
+  advance(lc);                             // lc -> tile 2
   asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
   __syncthreads();
-  while (phase == 0) {
-    int nph = phase, nsg = sg, nj0 = j0;
-    advance(nph, nsg, nj0);
-    if (nsg < nseg) issue(nsg, nj0, stage ^ 1);
-    const char* kt = lds + stage * STAGE_BYTES;
-    tile(kt, kt + KT_BYTES, ABN, std::false_type{});
-    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-    __syncthreads();
-    phase = nph;
-    sg = nsg;
-    j0 = nj0;
-    stage ^= 1;
-  }
-  while (sg < nseg) {
-    int nph = phase, nsg = sg, nj0 = j0;
-    advance(nph, nsg, nj0);
-    if (nsg < nseg) issue(nsg, nj0, stage ^ 1);
-    const char* kt = lds + stage * STAGE_BYTES;
-    tile(kt, kt + KT_BYTES, s_n[sg] - j0, std::true_type{});
-    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-    __syncthreads();
-    sg = nsg;
-    j0 = nj0;
-    stage ^= 1;
+
+  if (NT > 0) {
+    if (group == 1) wg_barrier();          // group B runs half a tile behind
+    // M(0) = S(0)
+    s_mfma(lds + stage_of(0) * STAGE_BYTES);
+    wg_barrier();
+    for (int t = 0; t < NT; ++t) {
+      // X(t): softmax of tile t; group B also loads tile t+2
+      if (group == 1 && t + 2 < NT) issue(lc, stage_of(t + 2));
+      advance(lc);
+      softmax(seg_n(xc.sg) - xc.j0);
+      advance(xc);
+      wg_barrier();
+      // M(t+1) = PV(t) [+ S(t+1)]
+      pv_mfma(lds + stage_of(t) * STAGE_BYTES + KT_BYTES);
+      if (t + 1 < NT) s_mfma(lds + stage_of(t + 1) * STAGE_BYTES);
+      asm volatile("s_waitcnt vmcnt(0)" ::: "memory");   // tile t+2 (group B's loads) has landed
+      wg_barrier();
+    }
+    if (group == 0) wg_barrier();          // match group B's extra leading barrier
   }
 
   const float lt = l_run + __shfl_xor(l_run, 32);
@@ -811,7 +910,7 @@ hipError_t launch_attention(const AttnArgs& a, bool bf16, hipStream_t s) {
   if (bf16) {
     if (a.D != AD) return hipErrorInvalidValue;
     const int nwg = ((a.T + ABM - 1) / ABM) * a.H;
-    attn_bf16_kernel<<<nwg, 256, 0, s>>>(a);
+    attn_bf16_kernel<<<nwg, 64 * AWAVES, 0, s>>>(a);
   } else if (a.D == 64) {
     const int nwg = ((a.T + 127) / 128) * a.H;
     attn_f32_kernel<64><<<nwg, 128, 0, s>>>(a);
