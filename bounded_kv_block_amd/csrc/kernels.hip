@@ -240,15 +240,15 @@ __global__ __launch_bounds__(256) void append_kernel(AppendArgs a) {
 // touches all 64 banks once (gfx950 LDS: 64 banks x 4 B, 16 lanes per cycle).
 // Loads are unpredicated: a partial tile reads the zeroed pad rows/columns
 // of its buffer and its scores beyond the segment are masked to -inf.
-// Scores come out of the S MFMA already relative to the running max m (the
-// chain starts from C = -m); m only moves when a tile's max exceeds it by
-// more than 2^8, so O is rarely rescaled.
+// The running max m only moves when a tile's max exceeds it by more than 2^8
+// (scores are in log2 units), so O is rarely rescaled.
 constexpr int ABM = 256, ABN = 64, AD = 128, AWAVES = 8;
 constexpr int KT_BYTES = ABN * AD * 2;
 constexpr int VT_BYTES = AD * ABN * 2;
 constexpr int STAGE_BYTES = KT_BYTES + VT_BYTES;
 constexpr int NSTAGE = 3;
 constexpr float kRescaleSlack = 8.0f;
+constexpr int kFragAhead = 3;            // LDS reads in flight ahead of the MFMA that uses them
 
 // K tile: 64 rows x 16 chunks of 16 B.  Rows read together by a 16-lane phase
 // are {0-7, 16-23} (+8, +32): (r & 7) | ((r & 16) >> 1) separates all 16.
@@ -319,7 +319,7 @@ __device__ __forceinline__ void dma16(i32x4 rsrc, unsigned voff, unsigned soff, 
 // length is not a multiple of 64 (phase 1).  Attention does not depend on
 // key order.  All fields are wave-uniform.
 struct TileCursor {
-  int phase, sg, j0;
+  int phase, sg, j0, n;   // n: length of segment sg (0 past the end)
 };
 
 __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2)))
@@ -405,31 +405,32 @@ void attn_bf16_kernel(AttnArgs a) {
     return g;
   };
   auto cursor_begin = [&]() {
-    TileCursor c{0, first_full(0), 0};
+    TileCursor c{0, first_full(0), 0, 0};
     if (c.sg >= nseg) {
       c.phase = 1;
       c.sg = first_tail(0);
-      c.j0 = c.sg < nseg ? (seg_n(c.sg) & ~(ABN - 1)) : 0;
     }
+    c.n = c.sg < nseg ? seg_n(c.sg) : 0;
+    if (c.phase == 1) c.j0 = c.n & ~(ABN - 1);
     return c;
   };
+  // Common case (next full tile of the same segment) touches no LDS.
   auto advance = [&](TileCursor& c) {
     if (c.sg >= nseg) return;
     if (c.phase == 0) {
       c.j0 += ABN;
-      if (c.j0 + ABN > seg_n(c.sg)) {
-        c.sg = first_full(c.sg + 1);
-        c.j0 = 0;
-        if (c.sg >= nseg) {
-          c.phase = 1;
-          c.sg = first_tail(0);
-          c.j0 = c.sg < nseg ? (seg_n(c.sg) & ~(ABN - 1)) : 0;
-        }
+      if (c.j0 + ABN <= c.n) return;
+      c.sg = first_full(c.sg + 1);
+      c.j0 = 0;
+      if (c.sg >= nseg) {
+        c.phase = 1;
+        c.sg = first_tail(0);
       }
     } else {
       c.sg = first_tail(c.sg + 1);
-      c.j0 = c.sg < nseg ? (seg_n(c.sg) & ~(ABN - 1)) : 0;
     }
+    c.n = c.sg < nseg ? seg_n(c.sg) : 0;
+    if (c.phase == 1) c.j0 = c.n & ~(ABN - 1);
   };
   int NT = 0;
   for (int g = 0; g < nseg; ++g) NT += (seg_n(g) + ABN - 1) / ABN;
@@ -437,13 +438,9 @@ void attn_bf16_kernel(AttnArgs a) {
   // ---- tile loads: chunk p = (4i + w)*64 + lane of a tile lands at LDS p*16
   // (w = wave within the loading group of four); the tile's first key enters
   // as the scalar offset of the buffer load.
-  unsigned koff[4], voff[4];
-#pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    const int p = (4 * i + gw) * 64 + lane;
-    koff[i] = (unsigned)((p >> 4) * 256 + (((p & 15) ^ kswz(p >> 4)) << 4));
-  }
-  int cur_ld = -1, cur_sg = -1;
+  // Offsets are recomputed per load (a few VALU ops on the softmax side)
+  // rather than held in registers across the MFMA blocks.
+  int cur_sg = -1, cur_ld = 0;
   i32x4 krs = {0, 0, 0, 0}, vrs = {0, 0, 0, 0};
   const unsigned lds0 = (unsigned)(uintptr_t)(lds_ptr_t)lds;
   auto issue = [&](const TileCursor& c, int stage) {   // by one group of four waves
@@ -451,60 +448,88 @@ void attn_bf16_kernel(AttnArgs a) {
       cur_sg = c.sg;
       krs = buffer_rsrc(uniform_ptr(s_k[c.sg]));
       vrs = buffer_rsrc(uniform_ptr(s_v[c.sg]));
-      const int ld = __builtin_amdgcn_readfirstlane(s_ld[c.sg]);
-      if (ld != cur_ld) {
-        cur_ld = ld;
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          const int p = (4 * i + gw) * 64 + lane;
-          voff[i] = (unsigned)((p >> 3) * ld * 2 + (((p & 7) ^ vswz(p >> 3)) << 4));
-        }
-      }
+      cur_ld = __builtin_amdgcn_readfirstlane(s_ld[c.sg]);
     }
     const unsigned kt = __builtin_amdgcn_readfirstlane(lds0 + stage * STAGE_BYTES + gw * 1024);
     const unsigned vt = kt + KT_BYTES;
     const unsigned j0 = __builtin_amdgcn_readfirstlane((unsigned)c.j0);
 #pragma unroll
-    for (int i = 0; i < 4; ++i) dma16(krs, koff[i], j0 * 256u, kt + i * 4096);
+    for (int i = 0; i < 4; ++i) {
+      const int p = (4 * i + gw) * 64 + lane;
+      dma16(krs, (unsigned)((p >> 4) * 256 + (((p & 15) ^ kswz(p >> 4)) << 4)), j0 * 256u, kt + i * 4096);
+    }
 #pragma unroll
-    for (int i = 0; i < 4; ++i) dma16(vrs, voff[i], j0 * 2u, vt + i * 4096);
+    for (int i = 0; i < 4; ++i) {
+      const int p = (4 * i + gw) * 64 + lane;
+      dma16(vrs, (unsigned)((p >> 3) * cur_ld * 2 + (((p & 7) ^ vswz(p >> 3)) << 4)), j0 * 2u, vt + i * 4096);
+    }
   };
 
   // ---- per-wave state
   f32x16 o[4];
 #pragma unroll
   for (int i = 0; i < 4; ++i) o[i] = f32x16{};
-  float m_run = 0.f, l_run = 0.f;
-  f32x16 negm = f32x16{};
-  bool first = true;
+  // m starts finite and far below any score: the first tile takes the rescale
+  // path with alpha = 0 (o and l are still zero), so no separate first-tile code.
+  float m_run = -1.0e30f, l_run = 0.f;
   f32x16 sacc[2];
   bf16x8 pb[2][2];
   typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
 
-  auto s_mfma = [&](const char* kt) {
+  // MFMA block: PV of one tile (16 MFMA, V^T fragments) then, optionally, S of
+  // the next (16 MFMA, K fragments).  Fragments rotate through 4 registers
+  // sets with LDS reads issued 3 MFMAs ahead, so the matrix core does not
+  // wait on LDS latency; consecutive MFMAs target different accumulators.
+  auto m_block = [&](const char* vt, const char* kt, auto with_s) {
+    constexpr int NSTEP = decltype(with_s)::value ? 32 : 16;
+    const int r0 = kperm(col), r1 = 32 + kperm(col);
+    auto frag = [&](int i) -> bf16x8 {
+      if (i < 16) {                      // PV step: (mb, part, db), db fastest
+        const int mb = i >> 3, part = (i >> 2) & 1, db = i & 3;
+        const int d = 32 * db + col, c = 4 * mb + 2 * hh + part;
+        return *reinterpret_cast<const bf16x8*>(vt + d * 128 + ((c ^ vswz(d)) << 4));
+      }
+      const int j = i - 16, st = j >> 1, r = (j & 1) ? r1 : r0;   // S step: (s, key block)
+      const int c = 2 * st + hh;
+      return *reinterpret_cast<const bf16x8*>(kt + r * 256 + ((c ^ kswz(r)) << 4));
+    };
+    auto step = [&](int i, const bf16x8& f) {
+      if (i < 16) {
+        const int mb = i >> 3, part = (i >> 2) & 1, db = i & 3;
+        o[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(f, pb[mb][part], o[db], 0, 0, 0);
+      } else {
+        const int j = i - 16, st = j >> 1, blk = j & 1;
+        sacc[blk] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(f, qreg[st], st ? sacc[blk] : f32x16{}, 0, 0, 0);
+      }
+    };
+    constexpr int AHEAD = kFragAhead;
+    bf16x8 fr[AHEAD + 1];
+#pragma unroll
+    for (int i = 0; i < AHEAD; ++i) fr[i] = frag(i);
+#pragma unroll
+    for (int i = 0; i < NSTEP; ++i) {
+      if (i + AHEAD < NSTEP) fr[(i + AHEAD) % (AHEAD + 1)] = frag(i + AHEAD);
+      step(i, fr[i % (AHEAD + 1)]);
+    }
+    // instruction order: AHEAD reads, then (read, MFMA) pairs, then the last MFMAs
+    __builtin_amdgcn_sched_group_barrier(0x100, AHEAD, 0);
+#pragma unroll
+    for (int i = 0; i < NSTEP - AHEAD; ++i) {
+      __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+    }
+    __builtin_amdgcn_sched_group_barrier(0x008, AHEAD, 0);
+  };
+  auto s_only = [&](const char* kt) {    // S of the first tile (no PV yet)
     const int r0 = kperm(col), r1 = 32 + kperm(col);
 #pragma unroll
-    for (int s = 0; s < 8; ++s) {
-      const int c = 2 * s + hh;
+    for (int st = 0; st < 8; ++st) {
+      const int c = 2 * st + hh;
       const bf16x8 k0 = *reinterpret_cast<const bf16x8*>(kt + r0 * 256 + ((c ^ kswz(r0)) << 4));
       const bf16x8 k1 = *reinterpret_cast<const bf16x8*>(kt + r1 * 256 + ((c ^ kswz(r1)) << 4));
-      sacc[0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(k0, qreg[s], s ? sacc[0] : negm, 0, 0, 0);
-      sacc[1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(k1, qreg[s], s ? sacc[1] : negm, 0, 0, 0);
+      sacc[0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(k0, qreg[st], st ? sacc[0] : f32x16{}, 0, 0, 0);
+      sacc[1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(k1, qreg[st], st ? sacc[1] : f32x16{}, 0, 0, 0);
     }
-  };
-  auto pv_mfma = [&](const char* vt) {
-#pragma unroll
-    for (int mb = 0; mb < 2; ++mb)
-#pragma unroll
-      for (int part = 0; part < 2; ++part) {
-        const int c = 4 * mb + 2 * hh + part;
-#pragma unroll
-        for (int db = 0; db < 4; ++db) {
-          const int d = 32 * db + col;
-          const bf16x8 vv = *reinterpret_cast<const bf16x8*>(vt + d * 128 + ((c ^ vswz(d)) << 4));
-          o[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vv, pb[mb][part], o[db], 0, 0, 0);
-        }
-      }
   };
   auto softmax = [&](int nvalid) {
     if (nvalid < ABN) {
@@ -527,34 +552,19 @@ void attn_bf16_kernel(AttnArgs a) {
       c4[q] = __builtin_fmaxf(x, v[b + 7]);
     }
     float mx = __builtin_fmaxf(__builtin_fmaxf(c4[0], c4[1]), __builtin_fmaxf(c4[2], c4[3]));
-    mx = fmaxf(mx, __shfl_xor(mx, 32));                   // max of (s - m) over the row's tile
-    if (first) {
-      first = false;                                      // m := this tile's row max
-      m_run += mx;
-#pragma unroll
-      for (int i = 0; i < 16; ++i) {
-        negm[i] = -m_run;
-        sacc[0][i] -= mx;
-        sacc[1][i] -= mx;
-      }
-    } else if (__any(mx > kRescaleSlack)) {
-      const float dm = fmaxf(mx, 0.f);
-      const float alpha = __builtin_amdgcn_exp2f(-dm);
-      m_run += dm;
+    mx = fmaxf(mx, __shfl_xor(mx, 32));                   // the row's max over this tile
+    if (__any(mx > m_run + kRescaleSlack)) {
+      const float m_new = fmaxf(m_run, mx);
+      const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);
+      m_run = m_new;
       l_run *= alpha;
 #pragma unroll
       for (int db = 0; db < 4; ++db) o[db] *= alpha;
-#pragma unroll
-      for (int i = 0; i < 16; ++i) {
-        negm[i] = -m_run;
-        sacc[0][i] -= dm;
-        sacc[1][i] -= dm;
-      }
     }
 #pragma unroll
     for (int mb = 0; mb < 2; ++mb)
 #pragma unroll
-      for (int i = 0; i < 16; ++i) pb[mb][i >> 3][i & 7] = (__bf16)__builtin_amdgcn_exp2f(sacc[mb][i]);
+      for (int i = 0; i < 16; ++i) pb[mb][i >> 3][i & 7] = (__bf16)__builtin_amdgcn_exp2f(sacc[mb][i] - m_run);
     // row sum of the bf16 P actually fed to the MFMA, two bf16 per dot2
     const bf16x2_t one2 = {(__bf16)1.0f, (__bf16)1.0f};
     float ls[4] = {0.f, 0.f, 0.f, 0.f};
@@ -586,21 +596,26 @@ void attn_bf16_kernel(AttnArgs a) {
   if (NT > 0) {
     if (group == 1) wg_barrier();          // group B runs half a tile behind
     // M(0) = S(0)
-    s_mfma(lds + stage_of(0) * STAGE_BYTES);
+    s_only(lds + stage_of(0) * STAGE_BYTES);
     wg_barrier();
-    for (int t = 0; t < NT; ++t) {
+    // Full periods: X(t) then M(t+1) = [PV(t), S(t+1)].  The last tile is
+    // peeled so the loop body holds a single MFMA-block variant.
+    for (int t = 0; t + 1 < NT; ++t) {
       // X(t): softmax of tile t; group B also loads tile t+2
       if (group == 1 && t + 2 < NT) issue(lc, stage_of(t + 2));
       advance(lc);
-      softmax(seg_n(xc.sg) - xc.j0);
+      softmax(xc.n - xc.j0);
       advance(xc);
       wg_barrier();
-      // M(t+1) = PV(t) [+ S(t+1)]
-      pv_mfma(lds + stage_of(t) * STAGE_BYTES + KT_BYTES);
-      if (t + 1 < NT) s_mfma(lds + stage_of(t + 1) * STAGE_BYTES);
+      m_block(lds + stage_of(t) * STAGE_BYTES + KT_BYTES, lds + stage_of(t + 1) * STAGE_BYTES,
+              std::true_type{});
       asm volatile("s_waitcnt vmcnt(0)" ::: "memory");   // tile t+2 (group B's loads) has landed
       wg_barrier();
     }
+    softmax(xc.n - xc.j0);                 // X(NT-1)
+    wg_barrier();
+    m_block(lds + stage_of(NT - 1) * STAGE_BYTES + KT_BYTES, nullptr, std::false_type{});
+    wg_barrier();
     if (group == 0) wg_barrier();          // match group B's extra leading barrier
   }
 
