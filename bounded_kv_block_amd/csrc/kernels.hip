@@ -552,7 +552,10 @@ void attn_bf16_kernel(AttnArgs a) {
       c4[q] = __builtin_fmaxf(x, v[b + 7]);
     }
     float mx = __builtin_fmaxf(__builtin_fmaxf(c4[0], c4[1]), __builtin_fmaxf(c4[2], c4[3]));
-    mx = fmaxf(mx, __shfl_xor(mx, 32));                   // the row's max over this tile
+    {   // the row's max over this tile: lanes l and l^32 hold the same query
+      const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(mx), __float_as_uint(mx), false, false);
+      mx = fmaxf(__uint_as_float(sw[0]), __uint_as_float(sw[1]));
+    }
     if (__any(mx > m_run + kRescaleSlack)) {
       const float m_new = fmaxf(m_run, mx);
       const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);
