@@ -64,6 +64,27 @@ def calibrate_copy(mib):
                       "gbs": 2 * n / (ms * 1e-3) / 1e9}), flush=True)
 
 
+def measured_traffic(workload):
+    """HBM bytes per attention launch from the committed rocprofv3 byte-counter
+    summary of this workload (FETCH_SIZE and WRITE_SIZE, each scaled by what
+    the counter reads for a plain copy of known size), or None when there is
+    no summary or the kernel source has changed since the counters were taken."""
+    import hashlib
+    path = os.path.join(ROOT, "profiles", f"attention_{workload}_hbm_traffic.txt")
+    if not os.path.exists(path):
+        return None
+    kv = {}
+    for ln in open(path):
+        parts = ln.split()
+        if len(parts) == 2 and parts[0] in ("traffic_bytes", "kernels_hip_sha256"):
+            kv[parts[0]] = parts[1]
+    src = os.path.join(ROOT, "bounded_kv_block_amd", "csrc", "kernels.hip")
+    sha = hashlib.sha256(open(src, "rb").read()).hexdigest()
+    if kv.get("kernels_hip_sha256") != sha or "traffic_bytes" not in kv:
+        return None
+    return float(kv["traffic_bytes"])
+
+
 def steady_block(cfg):
     """First block whose context has its final size."""
     if cfg["mode"] == "convkv":
@@ -236,6 +257,9 @@ def main():
         kernels["conv"]["gbs"] = c_bytes / (kernels["conv"]["avg_us"] * 1e-6) / 1e9
 
     attends_per_step = L * S
+    # algorithmic bytes of one attention launch: Q and the output once, K and V
+    # of the whole bounded context once
+    attn_bytes = 2.0 * T * H * D * esz + 2.0 * Nk * H * D * esz
     value = args.steps * T / wall
     res = {
         "metric": METRIC,
@@ -262,7 +286,8 @@ def main():
                        "max": float(per_block.max())},
         "kernels": kernels,
         "roofline": {"kernel": "attention", "bound": "mfma" if bf16 else "alu", "achieved": attn_tflops,
-                     "peak": peak, "unit": "TFLOP/s", "frac": attn_tflops / peak, "traffic": None,
+                     "peak": peak, "unit": "TFLOP/s", "frac": attn_tflops / peak, "traffic": measured_traffic(cfg["name"]),
+                     "traffic_unit": "HBM bytes per launch", "algorithmic_bytes": attn_bytes,
                      "flop_per_launch": flop_attend, "avg_launch_us": 1e3 * attn_avg_ms},
         "workspace_bytes": int(cache.stats()["workspace_bytes"]),
     }
