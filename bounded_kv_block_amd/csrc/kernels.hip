@@ -240,14 +240,19 @@ __global__ __launch_bounds__(256) void append_kernel(AppendArgs a) {
 // touches all 64 banks once (gfx950 LDS: 64 banks x 4 B, 16 lanes per cycle).
 // Loads are unpredicated: a partial tile reads the zeroed pad rows/columns
 // of its buffer and its scores beyond the segment are masked to -inf.
-// The running max m only moves when a tile's max exceeds it by more than 2^8
-// (scores are in log2 units), so O is rarely rescaled.
+// Softmax in log2 units with a lazily moved running max m: the S product
+// starts from C = -m, so the accumulators hold s - m and P = exp2(S) needs
+// no subtraction.  The first tile sets m to its exact row max.  Later tiles
+// keep m unless a lane's partial row sum of P exceeds 2^8 (which any
+// P > 2^8 forces); only then is the row max taken, m raised to it, O and l
+// rescaled and P recomputed.  So P <= 2^8 always, and m never exceeds the
+// true running max (l >= 1, no underflow).
 constexpr int ABM = 256, ABN = 64, AD = 128, AWAVES = 8;
 constexpr int KT_BYTES = ABN * AD * 2;
 constexpr int VT_BYTES = AD * ABN * 2;
 constexpr int STAGE_BYTES = KT_BYTES + VT_BYTES;
 constexpr int NSTAGE = 3;
-constexpr float kRescaleSlack = 8.0f;
+constexpr float kSumLimit = 256.0f;     // lane partial row sum of P that forces a rescale
 constexpr int kFragAhead = 3;            // LDS reads in flight ahead of the MFMA that uses them
 
 // K tile: 64 rows x 16 chunks of 16 B.  Rows read together by a 16-lane phase
@@ -469,9 +474,10 @@ void attn_bf16_kernel(AttnArgs a) {
   f32x16 o[4];
 #pragma unroll
   for (int i = 0; i < 4; ++i) o[i] = f32x16{};
-  // m starts finite and far below any score: the first tile takes the rescale
-  // path with alpha = 0 (o and l are still zero), so no separate first-tile code.
-  float m_run = -1.0e30f, l_run = 0.f;
+  // m_run: running row max (log2 units); negm = -m_run in every element, the
+  // C operand of the S product.  Both are set by the first tile.
+  float m_run = 0.f, l_run = 0.f;
+  f32x16 negm = f32x16{};
   f32x16 sacc[2];
   bf16x8 pb[2][2];
   typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
@@ -499,7 +505,7 @@ void attn_bf16_kernel(AttnArgs a) {
         o[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(f, pb[mb][part], o[db], 0, 0, 0);
       } else {
         const int j = i - 16, st = j >> 1, blk = j & 1;
-        sacc[blk] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(f, qreg[st], st ? sacc[blk] : f32x16{}, 0, 0, 0);
+        sacc[blk] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(f, qreg[st], st ? sacc[blk] : negm, 0, 0, 0);
       }
     };
     constexpr int AHEAD = kFragAhead;
@@ -531,7 +537,7 @@ void attn_bf16_kernel(AttnArgs a) {
       sacc[1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(k1, qreg[st], st ? sacc[1] : f32x16{}, 0, 0, 0);
     }
   };
-  auto softmax = [&](int nvalid) {
+  auto mask_tail = [&](int nvalid) {
     if (nvalid < ABN) {
       asm volatile("" ::: "memory");     // keep the tail mask a real branch
 #pragma unroll
@@ -540,7 +546,10 @@ void attn_bf16_kernel(AttnArgs a) {
         for (int i = 0; i < 16; ++i)
           if (32 * mb + 16 * hh + i >= nvalid) sacc[mb][i] = -INFINITY;
     }
-    // row max: four independent max3 chains over the lane's 32 scores
+  };
+  // row max of the tile's S: four max3 chains over the lane's 32 scores, then
+  // lanes l and l^32 (same query) exchange
+  auto row_max = [&]() {
     float c4[4];
 #pragma unroll
     for (int q = 0; q < 4; ++q) {
@@ -552,24 +561,20 @@ void attn_bf16_kernel(AttnArgs a) {
       c4[q] = __builtin_fmaxf(x, v[b + 7]);
     }
     float mx = __builtin_fmaxf(__builtin_fmaxf(c4[0], c4[1]), __builtin_fmaxf(c4[2], c4[3]));
-    {   // the row's max over this tile: lanes l and l^32 hold the same query
-      const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(mx), __float_as_uint(mx), false, false);
-      mx = fmaxf(__uint_as_float(sw[0]), __uint_as_float(sw[1]));
-    }
-    if (__any(mx > m_run + kRescaleSlack)) {
-      const float m_new = fmaxf(m_run, mx);
-      const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);
-      m_run = m_new;
-      l_run *= alpha;
-#pragma unroll
-      for (int db = 0; db < 4; ++db) o[db] *= alpha;
-    }
+    const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(mx), __float_as_uint(mx), false, false);
+    return fmaxf(__uint_as_float(sw[0]), __uint_as_float(sw[1]));
+  };
+  // P = exp2(S - shift) packed to bf16; returns the lane's partial row sum of
+  // the bf16 P actually fed to the MFMA (two bf16 per dot2)
+  const bf16x2_t one2 = {(__bf16)1.0f, (__bf16)1.0f};
+  auto exp_pack = [&](float shift, auto shifted) {
 #pragma unroll
     for (int mb = 0; mb < 2; ++mb)
 #pragma unroll
-      for (int i = 0; i < 16; ++i) pb[mb][i >> 3][i & 7] = (__bf16)__builtin_amdgcn_exp2f(sacc[mb][i] - m_run);
-    // row sum of the bf16 P actually fed to the MFMA, two bf16 per dot2
-    const bf16x2_t one2 = {(__bf16)1.0f, (__bf16)1.0f};
+      for (int i = 0; i < 16; ++i) {
+        const float x = decltype(shifted)::value ? sacc[mb][i] - shift : sacc[mb][i];
+        pb[mb][i >> 3][i & 7] = (__bf16)__builtin_amdgcn_exp2f(x);
+      }
     float ls[4] = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int q = 0; q < 4; ++q)
@@ -578,7 +583,34 @@ void attn_bf16_kernel(AttnArgs a) {
         const bf16x2_t pr = {pb[q >> 1][q & 1][2 * e], pb[q >> 1][q & 1][2 * e + 1]};
         ls[q] = __builtin_amdgcn_fdot2_f32_bf16(pr, one2, ls[q], false);
       }
-    l_run += (ls[0] + ls[1]) + (ls[2] + ls[3]);
+    return (ls[0] + ls[1]) + (ls[2] + ls[3]);
+  };
+  auto set_m = [&](float m) {
+    m_run = m;
+#pragma unroll
+    for (int i = 0; i < 16; ++i) negm[i] = -m;
+  };
+  // first tile: S holds raw scores; m = the exact row max
+  auto softmax_first = [&](int nvalid) {
+    mask_tail(nvalid);
+    const float mx = row_max();
+    set_m(mx);
+    l_run = exp_pack(mx, std::true_type{});
+  };
+  // later tiles: S holds s - m
+  auto softmax = [&](int nvalid) {
+    mask_tail(nvalid);
+    float part = exp_pack(0.f, std::false_type{});
+    if (__any(!(part <= kSumLimit))) {
+      const float d = fmaxf(row_max(), 0.f);
+      const float alpha = __builtin_amdgcn_exp2f(-d);
+      set_m(m_run + d);
+      l_run *= alpha;
+#pragma unroll
+      for (int db = 0; db < 4; ++db) o[db] *= alpha;
+      part = exp_pack(d, std::true_type{});
+    }
+    l_run += part;
   };
   auto stage_of = [](int t) { return t % NSTAGE; };
 
@@ -601,21 +633,29 @@ void attn_bf16_kernel(AttnArgs a) {
     // M(0) = S(0)
     s_only(lds + stage_of(0) * STAGE_BYTES);
     wg_barrier();
-    // Full periods: X(t) then M(t+1) = [PV(t), S(t+1)].  The last tile is
-    // peeled so the loop body holds a single MFMA-block variant.
-    for (int t = 0; t + 1 < NT; ++t) {
+    // Full periods: X(t) then M(t+1) = [PV(t), S(t+1)].  The first period
+    // (exact max) and the last tile are peeled, so the loop body holds a
+    // single softmax and a single MFMA-block variant.
+    auto period = [&](int t, auto first) {
       // X(t): softmax of tile t; group B also loads tile t+2
       if (group == 1 && t + 2 < NT) issue(lc, stage_of(t + 2));
       advance(lc);
-      softmax(xc.n - xc.j0);
+      if constexpr (decltype(first)::value) softmax_first(xc.n - xc.j0);
+      else softmax(xc.n - xc.j0);
       advance(xc);
       wg_barrier();
       m_block(lds + stage_of(t) * STAGE_BYTES + KT_BYTES, lds + stage_of(t + 1) * STAGE_BYTES,
               std::true_type{});
       asm volatile("s_waitcnt vmcnt(0)" ::: "memory");   // tile t+2 (group B's loads) has landed
       wg_barrier();
+    };
+    if (NT > 1) {
+      period(0, std::true_type{});
+      for (int t = 1; t + 1 < NT; ++t) period(t, std::false_type{});
+      softmax(xc.n - xc.j0);               // X(NT-1)
+    } else {
+      softmax_first(xc.n - xc.j0);
     }
-    softmax(xc.n - xc.j0);                 // X(NT-1)
     wg_barrier();
     m_block(lds + stage_of(NT - 1) * STAGE_BYTES + KT_BYTES, nullptr, std::false_type{});
     wg_barrier();
