@@ -217,8 +217,8 @@ __global__ __launch_bounds__(256) void append_kernel(AppendArgs a) {
 // ------------------------------------------------------------------ attention, bf16 MFMA
 // Workgroup = 8 waves x 32 queries (BM = 256) of one head; key tiles of 64.
 //
-// Per wave and tile t: S(t) = K(t) Q^T (16 MFMA), softmax(t) (VALU: max,
-// exp2, bf16 pack, row sum), PV(t) = V^T(t) P^T(t) (16 MFMA).  The waves form
+// Per wave and tile t: S(t) = K(t) Q^T (16 MFMA), softmax(t) (VALU: exp2,
+// bf16 pack, fp32 row sum), PV(t) = V^T(t) P^T(t) (16 MFMA).  The waves form
 // two groups of four (one wave of each group per SIMD) that run the same
 // program half a tile apart: while group A issues its MFMA block [PV(t-1),
 // S(t)] group B runs its softmax block, then they swap.  Whole-workgroup
@@ -235,7 +235,8 @@ __global__ __launch_bounds__(256) void append_kernel(AppendArgs a) {
 // scores sit in lanes l and l^32.
 //
 // K/V tiles move HBM -> LDS with buffer_load ... lds (no register staging),
-// three stages deep: tile t+2 is loaded while tiles t and t-1 are read.  LDS
+// three stages deep: tile t+2 is loaded (by group B, its 8 chunk loads per
+// wave spread over its exponentials) while tiles t and t-1 are read.  LDS
 // layouts are XOR-swizzled so that every 16-lane phase of a ds_read_b128
 // touches all 64 banks once (gfx950 LDS: 64 banks x 4 B, 16 lanes per cycle).
 // Loads are unpredicated: a partial tile reads the zeroed pad rows/columns
@@ -448,26 +449,43 @@ void attn_bf16_kernel(AttnArgs a) {
   int cur_sg = -1, cur_ld = 0;
   i32x4 krs = {0, 0, 0, 0}, vrs = {0, 0, 0, 0};
   const unsigned lds0 = (unsigned)(uintptr_t)(lds_ptr_t)lds;
-  auto issue = [&](const TileCursor& c, int stage) {   // by one group of four waves
+  // A tile's load = scalar set-up (segment descriptors, LDS and key offsets)
+  // then 8 chunk loads (4 of K, 4 of V) that the softmax interleaves with its
+  // exponentials: the CU's address unit takes each 1 KB chunk in ~16 cycles,
+  // so issuing all 32 of a tile back to back would stall the loading waves.
+  unsigned ld_kt = 0, ld_j0 = 0;
+  auto issue_setup = [&](const TileCursor& c, int stage) {
     if (c.sg != cur_sg) {
       cur_sg = c.sg;
       krs = buffer_rsrc(uniform_ptr(s_k[c.sg]));
       vrs = buffer_rsrc(uniform_ptr(s_v[c.sg]));
       cur_ld = __builtin_amdgcn_readfirstlane(s_ld[c.sg]);
     }
-    const unsigned kt = __builtin_amdgcn_readfirstlane(lds0 + stage * STAGE_BYTES + gw * 1024);
-    const unsigned vt = kt + KT_BYTES;
-    const unsigned j0 = __builtin_amdgcn_readfirstlane((unsigned)c.j0);
+    ld_kt = __builtin_amdgcn_readfirstlane(lds0 + stage * STAGE_BYTES + gw * 1024);
+    ld_j0 = __builtin_amdgcn_readfirstlane((unsigned)c.j0);
+  };
+  auto uni4 = [](i32x4 r) {
+    i32x4 u;
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int p = (4 * i + gw) * 64 + lane;
-      dma16(krs, (unsigned)((p >> 4) * 256 + (((p & 15) ^ kswz(p >> 4)) << 4)), j0 * 256u, kt + i * 4096);
-    }
+    for (int e = 0; e < 4; ++e) u[e] = (int)__builtin_amdgcn_readfirstlane((unsigned)r[e]);
+    return u;
+  };
+  auto issue_chunk = [&](int k) {          // k = 0..3: K, 4..7: V
+    const int i = k & 3;
+    const int p = (4 * i + gw) * 64 + lane;
+    const unsigned j0 = __builtin_amdgcn_readfirstlane(ld_j0);
+    const unsigned kt = __builtin_amdgcn_readfirstlane(ld_kt);
+    if (k < 4)
+      dma16(uni4(krs), (unsigned)((p >> 4) * 256 + (((p & 15) ^ kswz(p >> 4)) << 4)), j0 * 256u,
+            kt + i * 4096);
+    else
+      dma16(uni4(vrs), (unsigned)((p >> 3) * cur_ld * 2 + (((p & 7) ^ vswz(p >> 3)) << 4)), j0 * 2u,
+            kt + KT_BYTES + i * 4096);
+  };
+  auto issue = [&](const TileCursor& c, int stage) {   // by one group of four waves
+    issue_setup(c, stage);
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int p = (4 * i + gw) * 64 + lane;
-      dma16(vrs, (unsigned)((p >> 3) * cur_ld * 2 + (((p & 7) ^ vswz(p >> 3)) << 4)), j0 * 2u, vt + i * 4096);
-    }
+    for (int k = 0; k < 8; ++k) issue_chunk(k);
   };
 
   // ---- per-wave state
@@ -480,21 +498,30 @@ void attn_bf16_kernel(AttnArgs a) {
   f32x16 negm = f32x16{};
   f32x16 sacc[2];
   bf16x8 pb[2][2];
-  typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
 
   // MFMA block: PV of one tile (16 MFMA, V^T fragments) then, optionally, S of
   // the next (16 MFMA, K fragments).  Fragments rotate through 4 registers
   // sets with LDS reads issued 3 MFMAs ahead, so the matrix core does not
   // wait on LDS latency; consecutive MFMAs target different accumulators.
+  // fragment registers of the MFMA block; the first kFragAhead are read by
+  // m_prefetch before the barrier that opens the block (its V tile was
+  // published a period earlier), so the block starts without LDS latency
+  constexpr int AHEAD = kFragAhead;
+  bf16x8 fr[AHEAD + 1];
+  auto pv_frag = [&](const char* vt, int i) -> bf16x8 {   // PV step: (mb, part, db), db fastest
+    const int mb = i >> 3, part = (i >> 2) & 1, db = i & 3;
+    const int d = 32 * db + col, c = 4 * mb + 2 * hh + part;
+    return *reinterpret_cast<const bf16x8*>(vt + d * 128 + ((c ^ vswz(d)) << 4));
+  };
+  auto m_prefetch = [&](const char* vt) {
+#pragma unroll
+    for (int i = 0; i < AHEAD; ++i) fr[i] = pv_frag(vt, i);
+  };
   auto m_block = [&](const char* vt, const char* kt, auto with_s) {
     constexpr int NSTEP = decltype(with_s)::value ? 32 : 16;
     const int r0 = kperm(col), r1 = 32 + kperm(col);
     auto frag = [&](int i) -> bf16x8 {
-      if (i < 16) {                      // PV step: (mb, part, db), db fastest
-        const int mb = i >> 3, part = (i >> 2) & 1, db = i & 3;
-        const int d = 32 * db + col, c = 4 * mb + 2 * hh + part;
-        return *reinterpret_cast<const bf16x8*>(vt + d * 128 + ((c ^ vswz(d)) << 4));
-      }
+      if (i < 16) return pv_frag(vt, i);
       const int j = i - 16, st = j >> 1, r = (j & 1) ? r1 : r0;   // S step: (s, key block)
       const int c = 2 * st + hh;
       return *reinterpret_cast<const bf16x8*>(kt + r * 256 + ((c ^ kswz(r)) << 4));
@@ -508,17 +535,12 @@ void attn_bf16_kernel(AttnArgs a) {
         sacc[blk] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(f, qreg[st], st ? sacc[blk] : negm, 0, 0, 0);
       }
     };
-    constexpr int AHEAD = kFragAhead;
-    bf16x8 fr[AHEAD + 1];
-#pragma unroll
-    for (int i = 0; i < AHEAD; ++i) fr[i] = frag(i);
 #pragma unroll
     for (int i = 0; i < NSTEP; ++i) {
       if (i + AHEAD < NSTEP) fr[(i + AHEAD) % (AHEAD + 1)] = frag(i + AHEAD);
       step(i, fr[i % (AHEAD + 1)]);
     }
-    // instruction order: AHEAD reads, then (read, MFMA) pairs, then the last MFMAs
-    __builtin_amdgcn_sched_group_barrier(0x100, AHEAD, 0);
+    // instruction order: (read, MFMA) pairs, then the last MFMAs
 #pragma unroll
     for (int i = 0; i < NSTEP - AHEAD; ++i) {
       __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
@@ -565,42 +587,39 @@ void attn_bf16_kernel(AttnArgs a) {
     return fmaxf(__uint_as_float(sw[0]), __uint_as_float(sw[1]));
   };
   // P = exp2(S - shift) packed to bf16; returns the lane's partial row sum of
-  // the bf16 P actually fed to the MFMA (two bf16 per dot2)
-  const bf16x2_t one2 = {(__bf16)1.0f, (__bf16)1.0f};
-  auto exp_pack = [&](float shift, auto shifted) {
+  // P in fp32 (four chains of plain adds: the bf16 dot instructions would
+  // share the matrix core with the other group's MFMAs)
+  auto exp_pack = [&](float shift, auto shifted, auto&& hook) {
+    float ls[4] = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int mb = 0; mb < 2; ++mb)
 #pragma unroll
       for (int i = 0; i < 16; ++i) {
         const float x = decltype(shifted)::value ? sacc[mb][i] - shift : sacc[mb][i];
-        pb[mb][i >> 3][i & 7] = (__bf16)__builtin_amdgcn_exp2f(x);
-      }
-    float ls[4] = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-    for (int q = 0; q < 4; ++q)
-#pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        const bf16x2_t pr = {pb[q >> 1][q & 1][2 * e], pb[q >> 1][q & 1][2 * e + 1]};
-        ls[q] = __builtin_amdgcn_fdot2_f32_bf16(pr, one2, ls[q], false);
+        const float e = __builtin_amdgcn_exp2f(x);
+        pb[mb][i >> 3][i & 7] = (__bf16)e;
+        ls[2 * mb + (i >> 3)] += e;
+        if ((i & 3) == 3) hook(4 * mb + (i >> 2));
       }
     return (ls[0] + ls[1]) + (ls[2] + ls[3]);
   };
+  auto no_hook = [](int) {};
   auto set_m = [&](float m) {
     m_run = m;
 #pragma unroll
     for (int i = 0; i < 16; ++i) negm[i] = -m;
   };
   // first tile: S holds raw scores; m = the exact row max
-  auto softmax_first = [&](int nvalid) {
+  auto softmax_first = [&](int nvalid, auto&& load_hook) {
     mask_tail(nvalid);
     const float mx = row_max();
     set_m(mx);
-    l_run = exp_pack(mx, std::true_type{});
+    l_run = exp_pack(mx, std::true_type{}, load_hook);
   };
   // later tiles: S holds s - m
-  auto softmax = [&](int nvalid) {
+  auto softmax = [&](int nvalid, auto&& load_hook) {
     mask_tail(nvalid);
-    float part = exp_pack(0.f, std::false_type{});
+    float part = exp_pack(0.f, std::false_type{}, load_hook);
     if (__any(!(part <= kSumLimit))) {
       const float d = fmaxf(row_max(), 0.f);
       const float alpha = __builtin_amdgcn_exp2f(-d);
@@ -608,7 +627,7 @@ void attn_bf16_kernel(AttnArgs a) {
       l_run *= alpha;
 #pragma unroll
       for (int db = 0; db < 4; ++db) o[db] *= alpha;
-      part = exp_pack(d, std::true_type{});
+      part = exp_pack(d, std::true_type{}, no_hook);
     }
     l_run += part;
   };
@@ -634,28 +653,49 @@ void attn_bf16_kernel(AttnArgs a) {
     s_only(lds + stage_of(0) * STAGE_BYTES);
     wg_barrier();
     // Full periods: X(t) then M(t+1) = [PV(t), S(t+1)].  The first period
-    // (exact max) and the last tile are peeled, so the loop body holds a
-    // single softmax and a single MFMA-block variant.
-    auto period = [&](int t, auto first) {
-      // X(t): softmax of tile t; group B also loads tile t+2
-      if (group == 1 && t + 2 < NT) issue(lc, stage_of(t + 2));
+    // (exact max), the last loading period and the last tile are peeled, and
+    // each group runs its own copy of the loop, so the steady loop body holds
+    // a single softmax and MFMA-block variant and group B's chunk loads are
+    // unconditional (pinned between the exponentials).
+    // load: 0 = none, 1 = group B loads tile t+2
+    auto period = [&](int t, auto first, auto load) {
+      constexpr int LOAD = decltype(load)::value;
+      if (LOAD == 1) issue_setup(lc, stage_of(t + 2));
       advance(lc);
-      if constexpr (decltype(first)::value) softmax_first(xc.n - xc.j0);
-      else softmax(xc.n - xc.j0);
+      auto hook = [&](int k) {
+        if constexpr (LOAD == 1) {
+          __builtin_amdgcn_sched_barrier(0);
+          issue_chunk(k);
+          __builtin_amdgcn_sched_barrier(0);
+        }
+      };
+      if constexpr (decltype(first)::value) softmax_first(xc.n - xc.j0, hook);
+      else softmax(xc.n - xc.j0, hook);
       advance(xc);
+      m_prefetch(lds + stage_of(t) * STAGE_BYTES + KT_BYTES);
       wg_barrier();
       m_block(lds + stage_of(t) * STAGE_BYTES + KT_BYTES, lds + stage_of(t + 1) * STAGE_BYTES,
               std::true_type{});
       asm volatile("s_waitcnt vmcnt(0)" ::: "memory");   // tile t+2 (group B's loads) has landed
       wg_barrier();
     };
+    using L0 = std::integral_constant<int, 0>;
+    using L1 = std::integral_constant<int, 1>;
     if (NT > 1) {
-      period(0, std::true_type{});
-      for (int t = 1; t + 1 < NT; ++t) period(t, std::false_type{});
-      softmax(xc.n - xc.j0);               // X(NT-1)
+      int t = 1;
+      if (group == 1 && NT > 2) {
+        period(0, std::true_type{}, L1{});
+        for (; t + 2 < NT; ++t) period(t, std::false_type{}, L1{});
+      } else {
+        period(0, std::true_type{}, L0{});
+        for (; t + 2 < NT; ++t) period(t, std::false_type{}, L0{});
+      }
+      if (t + 1 < NT) period(t, std::false_type{}, L0{});   // t = NT-2: nothing left to load
+      softmax(xc.n - xc.j0, no_hook);      // X(NT-1)
     } else {
-      softmax_first(xc.n - xc.j0);
+      softmax_first(xc.n - xc.j0, no_hook);
     }
+    m_prefetch(lds + stage_of(NT - 1) * STAGE_BYTES + KT_BYTES);
     wg_barrier();
     m_block(lds + stage_of(NT - 1) * STAGE_BYTES + KT_BYTES, nullptr, std::false_type{});
     wg_barrier();
