@@ -42,6 +42,8 @@ struct Layout {
   size_t slot_bytes, slot_v_off, layer_kv_bytes;
   size_t off_kv, off_ctx, ctx_layer_bytes, off_mem, mem_layer_bytes, mem_v_off;
   size_t off_pose, off_sel, off_tt, off_th, off_tw, off_w, total;
+  bool split;                        // bf16 attention shares key tiles across workgroups
+  size_t off_split, off_cnt;
 };
 
 bkv_status validate(const bkv_config* c) {
@@ -143,6 +145,12 @@ Layout layout_of(const bkv_config* c, const bkv::Schedule& sch) {
   off = align_up(off + sizeof(float2) * (size_t)c->grid_w * (c->rope_w / 2 + 1), 256);
   L.off_w = off;
   if (c->mode == BKV_CONVKV) off = align_up(off + sizeof(float) * 2 * c->layers * H * D * c->conv_kernel, 256);
+  const long long units = (long long)H * ((L.T + bkv::kAttnBM - 1) / bkv::kAttnBM);
+  L.split = c->dtype == BKV_BF16 && units > bkv::kStreamWG;
+  L.off_split = off;
+  if (L.split) off = align_up(off + bkv::kSplitSlotBytes * 2 * (bkv::kStreamWG + 1), 256);
+  L.off_cnt = off;
+  if (L.split) off = align_up(off + sizeof(int) * (bkv::kStreamWG + 1), 256);
   L.total = off;
   return L;
 }
@@ -390,6 +398,14 @@ bkv_status bkv_reset(bkv_cache h) {
   h->sched.reset();
   h->error = false;
   h->ctx_ready.assign(h->cfg.layers, false);
+  if (h->L.split) {
+    // arrival counters return to 0 at the end of every launch; a launch cut
+    // short by a device error may leave them set
+    if (set_device(h) != BKV_OK) return fail(BKV_ERR_DEVICE, "reset: set device");
+    hipError_t e = hipMemset(h->ws + h->L.off_cnt, 0, sizeof(int) * (bkv::kStreamWG + 1));
+    if (e == hipSuccess) e = hipDeviceSynchronize();
+    if (e != hipSuccess) return fail(BKV_ERR_DEVICE, "reset: counter clear: %s", hipGetErrorString(e));
+  }
   return BKV_OK;
 }
 
@@ -511,6 +527,9 @@ bkv_status bkv_attend(bkv_cache h, int32_t layer, const void* q, const void* k, 
   a.slot_k_hs = h->slot_k_hs();
   a.slot_v_hs = h->slot_v_hs();
   a.slot_v_ld = h->L.Tpad;
+  a.split = h->L.split ? 1 : 0;
+  a.part = reinterpret_cast<float*>(h->ws + h->L.off_split);
+  a.cnt = reinterpret_cast<int*>(h->ws + h->L.off_cnt);
   a.nseg = (int)segs.size();
   for (int i = 0; i < a.nseg; ++i) a.seg[i] = h->seg_arg(layer, segs[i]);
   e = timed(h, K_ATTENTION, stream, [&] { return bkv::launch_attention(a, h->bf16(), stream); });

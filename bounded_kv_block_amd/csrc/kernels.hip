@@ -249,6 +249,7 @@ __global__ __launch_bounds__(256) void append_kernel(AppendArgs a) {
 // rescaled and P recomputed.  So P <= 2^8 always, and m never exceeds the
 // true running max (l >= 1, no underflow).
 constexpr int ABM = 256, ABN = 64, AD = 128, AWAVES = 8;
+static_assert(ABM == kAttnBM, "unit rows");
 constexpr int KT_BYTES = ABN * AD * 2;
 constexpr int VT_BYTES = AD * ABN * 2;
 constexpr int STAGE_BYTES = KT_BYTES + VT_BYTES;
@@ -328,74 +329,67 @@ struct TileCursor {
   int phase, sg, j0, n;   // n: length of segment sg (0 past the end)
 };
 
+template <bool SPLIT>
 __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2)))
 void attn_bf16_kernel(AttnArgs a) {
   __shared__ __attribute__((aligned(1024))) char lds[NSTAGE * STAGE_BYTES];
-  __shared__ const char* s_k[kMaxSeg];
+  __shared__ const char* s_k[kMaxSeg];      // segment K / V^T of the current head
   __shared__ const char* s_v[kMaxSeg];
+  __shared__ const char* s_kb[kMaxSeg];     // head 0, with per-head strides
+  __shared__ const char* s_vb[kMaxSeg];
+  __shared__ long long s_khs[kMaxSeg];
+  __shared__ long long s_vhs[kMaxSeg];
   __shared__ int s_n[kMaxSeg];
   __shared__ int s_ld[kMaxSeg];
+  __shared__ int s_arrived;
 
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);   // uniform by construction
   const int group = wave >> 2, gw = wave & 3;           // ping-pong group, wave in group
   const int hh = lane >> 5, col = lane & 31;
   const int nqt = (a.T + ABM - 1) / ABM;
-  const int logical = xcd_remap(blockIdx.x, gridDim.x);
-  const int head = logical / nqt, qt = logical - head * nqt;
-  const int nseg = a.nseg;
+  const int nseg = __builtin_amdgcn_readfirstlane(a.nseg);
 
-  if (tid < nseg) {
-    const Seg sg = a.seg[tid];
-    const char* kb;
-    const char* vb;
-    long long khs, vhs;
-    int ld;
-    if (sg.dyn >= 0) {
-      const int slot = a.sel_slots[sg.dyn];
-      kb = a.slot_base + (long long)slot * a.slot_bytes;
-      vb = kb + a.slot_v_off;
-      khs = a.slot_k_hs;
-      vhs = a.slot_v_hs;
-      ld = a.slot_v_ld;
-    } else {
-      kb = static_cast<const char*>(sg.k);
-      vb = static_cast<const char*>(sg.v);
-      khs = sg.k_hs;
-      vhs = sg.v_hs;
-      ld = sg.v_ld;
-    }
-    s_k[tid] = kb + 2 * head * khs;
-    s_v[tid] = vb + 2 * head * vhs;
-    s_n[tid] = sg.n;
-    s_ld[tid] = ld;
-  }
-
-  // Q prologue: lane holds Q~[q][16s + 8h .. +7] for s = 0..7, rotated, scaled
-  // by softmax_scale*log2(e), rounded to bf16.
-  const int qrow = qt * ABM + wave * 32 + col;
-  bf16x8 qreg[8];
-  {
-    int f = 0, y = 0, x = 0;
-    const bool valid = qrow < a.T;
-    if (valid) token_fyx(qrow, a.rope.grid_h, a.rope.grid_w, f, y, x);
-    const bool rope = has_rope(a.rope);
-    const __bf16* qp = static_cast<const __bf16*>(a.q) + ((size_t)(valid ? qrow : 0) * a.H + head) * AD;
+  // segment table into LDS; one segment per wave, compile-time indices into
+  // the argument block (a run-time index would copy it to scratch memory)
 #pragma unroll
-    for (int s = 0; s < 8; ++s) {
-      const int d0 = 16 * s + 8 * hh;
-      bf16x8 raw = valid ? *reinterpret_cast<const bf16x8*>(qp + d0) : bf16x8{};
-      float u[8];
+  for (int g = 0; g < kMaxSeg; g += AWAVES) {
+    const int gg = g + wave;
+    if (gg < nseg && lane == 0) {
+      Seg sg;
 #pragma unroll
-      for (int e = 0; e < 8; ++e) u[e] = (float)raw[e];
-      if (rope && valid) {
-#pragma unroll
-        for (int e = 0; e < 8; e += 2) rope_pair(u[e], u[e + 1], d0 + e, a.rope, a.t_row0 + f, y, x);
+      for (int w = 0; w < AWAVES; ++w)
+        if (w == wave) sg = a.seg[g + w];
+      const char* kb;
+      const char* vb;
+      long long khs, vhs;
+      int ld;
+      if (sg.dyn >= 0) {
+        const int slot = a.sel_slots[sg.dyn];
+        kb = a.slot_base + (long long)slot * a.slot_bytes;
+        vb = kb + a.slot_v_off;
+        khs = a.slot_k_hs;
+        vhs = a.slot_v_hs;
+        ld = a.slot_v_ld;
+      } else {
+        kb = static_cast<const char*>(sg.k);
+        vb = static_cast<const char*>(sg.v);
+        khs = sg.k_hs;
+        vhs = sg.v_hs;
+        ld = sg.v_ld;
       }
-#pragma unroll
-      for (int e = 0; e < 8; ++e) qreg[s][e] = (__bf16)(u[e] * a.qscale);
+      s_kb[gg] = kb;
+      s_vb[gg] = vb;
+      s_khs[gg] = khs;
+      s_vhs[gg] = vhs;
+      s_n[gg] = sg.n;
+      s_ld[gg] = ld;
     }
   }
+
+  // Q of a unit: lane holds Q~[q][16s + 8h .. +7] for s = 0..7, rotated,
+  // scaled by softmax_scale*log2(e), rounded to bf16.
+  bf16x8 qreg[8];
   __syncthreads();
 
   // ---- tile enumeration (segment metadata read as wave-uniform values)
@@ -410,19 +404,51 @@ void attn_bf16_kernel(AttnArgs a) {
     while (g < nseg && seg_n(g) < ABN) ++g;
     return g;
   };
-  auto cursor_begin = [&]() {
-    TileCursor c{0, first_full(0), 0, 0};
-    if (c.sg >= nseg) {
-      c.phase = 1;
-      c.sg = first_tail(0);
+  // cursor at tile k of the enumeration (full tiles of each segment in
+  // order, then the partial tails)
+  auto cursor_find = [&](int k) {
+    TileCursor c{0, nseg, 0, 0};
+    for (int g = 0; g < nseg; ++g) {
+      const int f = seg_n(g) / ABN;
+      if (k < f) {
+        c.sg = g;
+        c.j0 = k * ABN;
+        c.n = seg_n(g);
+        return c;
+      }
+      k -= f;
     }
-    c.n = c.sg < nseg ? seg_n(c.sg) : 0;
-    if (c.phase == 1) c.j0 = c.n & ~(ABN - 1);
+    c.phase = 1;
+    for (int g = 0; g < nseg; ++g) {
+      if (seg_n(g) & (ABN - 1)) {
+        if (k == 0) {
+          c.sg = g;
+          c.n = seg_n(g);
+          c.j0 = c.n & ~(ABN - 1);
+          return c;
+        }
+        --k;
+      }
+    }
     return c;
   };
-  // Common case (next full tile of the same segment) touches no LDS.
+  // (the fields are re-read as wave-uniform: the cursor is carried across
+  // the piece loop, where the compiler no longer proves it uniform)
+  auto cursor_seek = [&](int k) {
+    TileCursor c = cursor_find(__builtin_amdgcn_readfirstlane(k));
+    c.phase = __builtin_amdgcn_readfirstlane(c.phase);
+    c.sg = __builtin_amdgcn_readfirstlane(c.sg);
+    c.j0 = __builtin_amdgcn_readfirstlane(c.j0);
+    c.n = __builtin_amdgcn_readfirstlane(c.n);
+    return c;
+  };
+  // Common case (next full tile of the same segment) touches no LDS.  Past
+  // the last tile the enumeration wraps to the first (a piece may start
+  // anywhere in the cycle).
   auto advance = [&](TileCursor& c) {
-    if (c.sg >= nseg) return;
+    if constexpr (!SPLIT) {
+      if (c.sg >= nseg) return;
+    }
     if (c.phase == 0) {
       c.j0 += ABN;
       if (c.j0 + ABN <= c.n) return;
@@ -435,8 +461,20 @@ void attn_bf16_kernel(AttnArgs a) {
     } else {
       c.sg = first_tail(c.sg + 1);
     }
-    c.n = c.sg < nseg ? seg_n(c.sg) : 0;
-    if (c.phase == 1) c.j0 = c.n & ~(ABN - 1);
+    if constexpr (SPLIT) {
+      if (c.sg >= nseg) {
+        c.phase = 0;
+        c.sg = first_full(0);
+        if (c.sg >= nseg) {
+          c.phase = 1;
+          c.sg = first_tail(0);
+        }
+      }
+    } else {
+      if (c.sg >= nseg) return;            // past the unit's last tile (load cursor only)
+    }
+    c.n = seg_n(c.sg);
+    c.j0 = c.phase == 1 ? c.n & ~(ABN - 1) : 0;
   };
   int NT = 0;
   for (int g = 0; g < nseg; ++g) NT += (seg_n(g) + ABN - 1) / ABN;
@@ -444,8 +482,6 @@ void attn_bf16_kernel(AttnArgs a) {
   // ---- tile loads: chunk p = (4i + w)*64 + lane of a tile lands at LDS p*16
   // (w = wave within the loading group of four); the tile's first key enters
   // as the scalar offset of the buffer load.
-  // Offsets are recomputed per load (a few VALU ops on the softmax side)
-  // rather than held in registers across the MFMA blocks.
   int cur_sg = -1, cur_ld = 0;
   i32x4 krs = {0, 0, 0, 0}, vrs = {0, 0, 0, 0};
   const unsigned lds0 = (unsigned)(uintptr_t)(lds_ptr_t)lds;
@@ -454,12 +490,24 @@ void attn_bf16_kernel(AttnArgs a) {
   // exponentials: the CU's address unit takes each 1 KB chunk in ~16 cycles,
   // so issuing all 32 of a tile back to back would stall the loading waves.
   unsigned ld_kt = 0, ld_j0 = 0;
+  // Per-lane chunk offsets.  Chunk i of a K tile sits at vk[i & 1] + (i >> 1)
+  // * 8192 and chunk i of a V^T tile at vv + i * 32 rows: every i-dependent
+  // part is uniform and goes into the scalar offset, so three registers
+  // serve all eight loads (vv changes with the segment's row stride).
+  auto k_off = [&](int i) {
+    const int p = (4 * i + gw) * 64 + lane;
+    return (unsigned)((p >> 4) * 256 + (((p & 15) ^ kswz(p >> 4)) << 4));
+  };
+  const unsigned vk0 = k_off(0), vk1 = k_off(1);
+  unsigned vv = 0;
   auto issue_setup = [&](const TileCursor& c, int stage) {
     if (c.sg != cur_sg) {
       cur_sg = c.sg;
       krs = buffer_rsrc(uniform_ptr(s_k[c.sg]));
       vrs = buffer_rsrc(uniform_ptr(s_v[c.sg]));
       cur_ld = __builtin_amdgcn_readfirstlane(s_ld[c.sg]);
+      const int p = gw * 64 + lane;
+      vv = (unsigned)((p >> 3) * cur_ld * 2 + (((p & 7) ^ vswz(p >> 3)) << 4));
     }
     ld_kt = __builtin_amdgcn_readfirstlane(lds0 + stage * STAGE_BYTES + gw * 1024);
     ld_j0 = __builtin_amdgcn_readfirstlane((unsigned)c.j0);
@@ -472,15 +520,13 @@ void attn_bf16_kernel(AttnArgs a) {
   };
   auto issue_chunk = [&](int k) {          // k = 0..3: K, 4..7: V
     const int i = k & 3;
-    const int p = (4 * i + gw) * 64 + lane;
     const unsigned j0 = __builtin_amdgcn_readfirstlane(ld_j0);
     const unsigned kt = __builtin_amdgcn_readfirstlane(ld_kt);
+    const unsigned ld = __builtin_amdgcn_readfirstlane((unsigned)cur_ld);
     if (k < 4)
-      dma16(uni4(krs), (unsigned)((p >> 4) * 256 + (((p & 15) ^ kswz(p >> 4)) << 4)), j0 * 256u,
-            kt + i * 4096);
+      dma16(uni4(krs), (i & 1) ? vk1 : vk0, j0 * 256u + (unsigned)(i >> 1) * 8192u, kt + i * 4096);
     else
-      dma16(uni4(vrs), (unsigned)((p >> 3) * cur_ld * 2 + (((p & 7) ^ vswz(p >> 3)) << 4)), j0 * 2u,
-            kt + KT_BYTES + i * 4096);
+      dma16(uni4(vrs), vv, j0 * 2u + (unsigned)i * 64u * ld, kt + KT_BYTES + i * 4096);
   };
   auto issue = [&](const TileCursor& c, int stage) {   // by one group of four waves
     issue_setup(c, stage);
@@ -632,89 +678,204 @@ void attn_bf16_kernel(AttnArgs a) {
     l_run += part;
   };
   auto stage_of = [](int t) { return t % NSTAGE; };
+  TileCursor xc{}, lc{};                   // next softmax tile, next load tile
 
-  // ---- prologue: tiles 0 and 1 loaded by group 0 (all waves wait)
-  TileCursor xc = cursor_begin();          // tile of the next softmax
-  TileCursor lc = xc;                      // tile of the next load
-  if (group == 0) {
-    if (NT > 0) issue(lc, 0);
-    advance(lc);
-    if (NT > 1) issue(lc, 1);
-  } else {
-    advance(lc);
-  }
-  advance(lc);                             // lc -> tile 2
-  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-  __syncthreads();
-
-  if (NT > 0) {
-    if (group == 1) wg_barrier();          // group B runs half a tile behind
-    // M(0) = S(0)
-    s_only(lds + stage_of(0) * STAGE_BYTES);
-    wg_barrier();
-    // Full periods: X(t) then M(t+1) = [PV(t), S(t+1)].  The first period
-    // (exact max), the last loading period and the last tile are peeled, and
-    // each group runs its own copy of the loop, so the steady loop body holds
-    // a single softmax and MFMA-block variant and group B's chunk loads are
-    // unconditional (pinned between the exponentials).
-    // load: 0 = none, 1 = group B loads tile t+2
-    auto period = [&](int t, auto first, auto load) {
-      constexpr int LOAD = decltype(load)::value;
-      if (LOAD == 1) issue_setup(lc, stage_of(t + 2));
-      advance(lc);
-      auto hook = [&](int k) {
-        if constexpr (LOAD == 1) {
-          __builtin_amdgcn_sched_barrier(0);
-          issue_chunk(k);
-          __builtin_amdgcn_sched_barrier(0);
+  // final output of a unit's 256 rows: O / l in bf16
+  auto write_out = [&](int head, int qrow) {
+    const float lt = l_run + __shfl_xor(l_run, 32);
+    const float inv = lt > 0.f ? 1.f / lt : 0.f;
+    if (qrow < a.T) {
+      __bf16* op = static_cast<__bf16*>(a.out) + ((size_t)qrow * a.H + head) * AD;
+#pragma unroll
+      for (int db = 0; db < 4; ++db)
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          bf16x4 w;
+#pragma unroll
+          for (int e = 0; e < 4; ++e) w[e] = (__bf16)(o[db][4 * j + e] * inv);
+          *reinterpret_cast<bf16x4*>(op + 32 * db + 8 * j + 4 * hh) = w;
         }
-      };
-      if constexpr (decltype(first)::value) softmax_first(xc.n - xc.j0, hook);
-      else softmax(xc.n - xc.j0, hook);
-      advance(xc);
-      m_prefetch(lds + stage_of(t) * STAGE_BYTES + KT_BYTES);
-      wg_barrier();
-      m_block(lds + stage_of(t) * STAGE_BYTES + KT_BYTES, lds + stage_of(t + 1) * STAGE_BYTES,
-              std::true_type{});
-      asm volatile("s_waitcnt vmcnt(0)" ::: "memory");   // tile t+2 (group B's loads) has landed
-      wg_barrier();
-    };
-    using L0 = std::integral_constant<int, 0>;
-    using L1 = std::integral_constant<int, 1>;
-    if (NT > 1) {
-      int t = 1;
-      if (group == 1 && NT > 2) {
-        period(0, std::true_type{}, L1{});
-        for (; t + 2 < NT; ++t) period(t, std::false_type{}, L1{});
-      } else {
-        period(0, std::true_type{}, L0{});
-        for (; t + 2 < NT; ++t) period(t, std::false_type{}, L0{});
-      }
-      if (t + 1 < NT) period(t, std::false_type{}, L0{});   // t = NT-2: nothing left to load
-      softmax(xc.n - xc.j0, no_hook);      // X(NT-1)
-    } else {
-      softmax_first(xc.n - xc.j0, no_hook);
     }
-    m_prefetch(lds + stage_of(NT - 1) * STAGE_BYTES + KT_BYTES);
-    wg_barrier();
-    m_block(lds + stage_of(NT - 1) * STAGE_BYTES + KT_BYTES, nullptr, std::false_type{});
-    wg_barrier();
-    if (group == 0) wg_barrier();          // match group B's extra leading barrier
-  }
+  };
 
-  const float lt = l_run + __shfl_xor(l_run, 32);
-  const float inv = lt > 0.f ? 1.f / lt : 0.f;
-  if (qrow < a.T) {
-    __bf16* op = static_cast<__bf16*>(a.out) + ((size_t)qrow * a.H + head) * AD;
+  // ---- one piece: key tiles [ka, kb) of unit u = head * nqt + qt (NT tiles
+  // per unit), started at time i0 of this workgroup's share
+  auto piece = [&](int u, int ka, int kb, int i0) {
+    const int head = __builtin_amdgcn_readfirstlane(u / nqt);
+    const int qt = u - head * nqt;
+    const int qrow = qt * ABM + wave * 32 + col;
+    const int NP = kb - ka;                // key tiles of this piece, >= 1
+
+    __syncthreads();                       // the previous piece is done with LDS
+    if (tid < nseg) {
+      s_k[tid] = s_kb[tid] + 2 * head * s_khs[tid];
+      s_v[tid] = s_vb[tid] + 2 * head * s_vhs[tid];
+    }
+    {   // Q of the unit
+      int f = 0, y = 0, x = 0;
+      const bool valid = qrow < a.T;
+      if (valid) token_fyx(qrow, a.rope.grid_h, a.rope.grid_w, f, y, x);
+      const bool rope = has_rope(a.rope);
+      const __bf16* qp = static_cast<const __bf16*>(a.q) + ((size_t)(valid ? qrow : 0) * a.H + head) * AD;
 #pragma unroll
-    for (int db = 0; db < 4; ++db)
+      for (int s = 0; s < 8; ++s) {
+        const int d0 = 16 * s + 8 * hh;
+        bf16x8 raw = valid ? *reinterpret_cast<const bf16x8*>(qp + d0) : bf16x8{};
+        float u[8];
 #pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        bf16x4 w;
+        for (int e = 0; e < 8; ++e) u[e] = (float)raw[e];
+        if (rope && valid) {
 #pragma unroll
-        for (int e = 0; e < 4; ++e) w[e] = (__bf16)(o[db][4 * j + e] * inv);
-        *reinterpret_cast<bf16x4*>(op + 32 * db + 8 * j + 4 * hh) = w;
+          for (int e = 0; e < 8; e += 2) rope_pair(u[e], u[e + 1], d0 + e, a.rope, a.t_row0 + f, y, x);
+        }
+#pragma unroll
+        for (int e = 0; e < 8; ++e) qreg[s][e] = (__bf16)(u[e] * a.qscale);
       }
+    }
+    __syncthreads();
+    cur_sg = -1;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) o[i] = f32x16{};
+    m_run = 0.f;
+    l_run = 0.f;
+    negm = f32x16{};
+
+    // Key order: a unit's tiles are taken in a rotated cycle so that, at
+    // time i of the launch, every workgroup on this head reads key tile
+    // i mod NT (one K/V stream per head through L2).  Both pieces of a cut
+    // unit use the same rotation, so between them they cover every tile once.
+    const int shift = (ka == 0 && kb == NT) ? i0 % NT : (NT - (ka > 0 ? ka : kb)) % NT;
+    // ---- prologue: tiles 0 and 1 of the piece loaded by group 0 (all waves wait)
+    xc = cursor_seek((ka + shift) % NT);
+    lc = xc;
+    if (group == 0) {
+      issue(lc, 0);
+      advance(lc);
+      if (NP > 1) issue(lc, 1);
+    } else {
+      advance(lc);
+    }
+    advance(lc);                           // lc -> tile 2
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    __syncthreads();
+
+      if (NP > 0) {
+        if (group == 1) wg_barrier();          // group B runs half a tile behind
+        // M(0) = S(0)
+        s_only(lds + stage_of(0) * STAGE_BYTES);
+        wg_barrier();
+        // Full periods: X(t) then M(t+1) = [PV(t), S(t+1)].  The first period
+        // (exact max), the last loading period and the last tile are peeled, and
+        // each group runs its own copy of the loop, so the steady loop body holds
+        // a single softmax and MFMA-block variant and group B's chunk loads are
+        // unconditional (pinned between the exponentials).
+        // load: 0 = none, 1 = group B loads tile t+2
+        auto period = [&](int t, auto first, auto load) {
+          constexpr int LOAD = decltype(load)::value;
+          if (LOAD == 1) issue_setup(lc, stage_of(t + 2));
+          advance(lc);
+          auto hook = [&](int k) {
+            if constexpr (LOAD == 1) {
+              __builtin_amdgcn_sched_barrier(0);
+              issue_chunk(k);
+              __builtin_amdgcn_sched_barrier(0);
+            }
+          };
+          if constexpr (decltype(first)::value) softmax_first(xc.n - xc.j0, hook);
+          else softmax(xc.n - xc.j0, hook);
+          advance(xc);
+          m_prefetch(lds + stage_of(t) * STAGE_BYTES + KT_BYTES);
+          wg_barrier();
+          m_block(lds + stage_of(t) * STAGE_BYTES + KT_BYTES, lds + stage_of(t + 1) * STAGE_BYTES,
+                  std::true_type{});
+          asm volatile("s_waitcnt vmcnt(0)" ::: "memory");   // tile t+2 (group B's loads) has landed
+          wg_barrier();
+        };
+        using L0 = std::integral_constant<int, 0>;
+        using L1 = std::integral_constant<int, 1>;
+        if (NP > 1) {
+          int t = 1;
+          if (group == 1 && NP > 2) {
+            period(0, std::true_type{}, L1{});
+            for (; t + 2 < NP; ++t) period(t, std::false_type{}, L1{});
+          } else {
+            period(0, std::true_type{}, L0{});
+            for (; t + 2 < NP; ++t) period(t, std::false_type{}, L0{});
+          }
+          if (t + 1 < NP) period(t, std::false_type{}, L0{});   // t = NP-2: nothing left to load
+          softmax(xc.n - xc.j0, no_hook);      // X(NP-1)
+        } else {
+          softmax_first(xc.n - xc.j0, no_hook);
+        }
+        m_prefetch(lds + stage_of(NP - 1) * STAGE_BYTES + KT_BYTES);
+        wg_barrier();
+        m_block(lds + stage_of(NP - 1) * STAGE_BYTES + KT_BYTES, nullptr, std::false_type{});
+        wg_barrier();
+        if (group == 0) wg_barrier();          // match group B's extra leading barrier
+      }
+
+
+    if (!SPLIT || (ka == 0 && kb == NT)) {
+      write_out(head, qrow);
+      return;
+    }
+    if constexpr (SPLIT) {
+    // A piece of a cut unit: its fp32 state (O, m, l in register order) goes
+    // to the slot of its side of the share boundary; the second piece to
+    // arrive merges the first one's and writes the unit's output.
+    const int xcd = blockIdx.x & 7, j = blockIdx.x >> 3;
+    const int side = ka > 0 ? 1 : 0;       // 1: the unit's later tiles (start of this share)
+    const int bidx = xcd * kStreamPerXcd + j + (side ? 0 : 1);
+    constexpr int SLOT = (int)(kSplitSlotBytes / 4), ML = 8 * 64 * 64;
+    float* mine = a.part + (size_t)(2 * bidx + side) * SLOT;
+    const float* other = a.part + (size_t)(2 * bidx + 1 - side) * SLOT;
+#pragma unroll
+    for (int r = 0; r < 64; ++r) mine[(wave * 64 + r) * 64 + lane] = o[r >> 4][r & 15];
+    mine[ML + (wave * 2) * 64 + lane] = m_run;
+    mine[ML + (wave * 2 + 1) * 64 + lane] = l_run;
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "agent");
+    __syncthreads();
+    if (tid == 0) s_arrived = __hip_atomic_fetch_add(a.cnt + bidx, 1, __ATOMIC_ACQ_REL, __HIP_MEMORY_SCOPE_AGENT);
+    __syncthreads();
+    if (__builtin_amdgcn_readfirstlane(s_arrived) == 1) {
+      __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
+      const float m2 = other[ML + (wave * 2) * 64 + lane];
+      const float l2 = other[ML + (wave * 2 + 1) * 64 + lane];
+      const float mm = fmaxf(m_run, m2);
+      const float al = __builtin_amdgcn_exp2f(m_run - mm), be = __builtin_amdgcn_exp2f(m2 - mm);
+#pragma unroll
+      for (int r = 0; r < 64; ++r)
+        o[r >> 4][r & 15] = al * o[r >> 4][r & 15] + be * other[(wave * 64 + r) * 64 + lane];
+      l_run = al * l_run + be * l2;
+      if (tid == 0) __hip_atomic_store(a.cnt + bidx, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      write_out(head, qrow);
+    }
+    }
+  };
+
+  if constexpr (!SPLIT) {
+    // one unit per workgroup, XCD-contiguous (the query tiles of a head share an L2)
+    const int u = __builtin_amdgcn_readfirstlane(xcd_remap(blockIdx.x, gridDim.x));
+    piece(u, 0, NT, 0);
+  } else {
+    // An equal share of the (unit, key tile) work of the workgroup's XCD:
+    // XCD x owns units [x U/8, (x+1) U/8) and its 32 workgroups cut them at
+    // share boundaries, so a cut unit's two pieces meet in one XCD's L2.
+    // (32-bit: units * tiles stays far below 2^31; every per-piece scalar is
+    // re-read as wave-uniform so the loop control stays on the scalar unit.)
+    const int xcd = blockIdx.x & 7, j = blockIdx.x >> 3;
+    const int U = a.H * nqt;
+    const int u0 = (xcd * U) >> 3, u1 = ((xcd + 1) * U) >> 3;
+    const int tt = (u1 - u0) * NT;
+    const int t0 = __builtin_amdgcn_readfirstlane(u0 * NT + (int)((long long)tt * j / kStreamPerXcd));
+    const int t1 = __builtin_amdgcn_readfirstlane(u0 * NT + (int)((long long)tt * (j + 1) / kStreamPerXcd));
+    for (int pos = t0; pos < t1;) {
+      const int u = __builtin_amdgcn_readfirstlane(pos / NT);
+      const int ka = __builtin_amdgcn_readfirstlane(pos - u * NT);
+      const int kb = __builtin_amdgcn_readfirstlane(min(NT, t1 - u * NT));
+      piece(u, ka, kb, pos - t0);
+      pos = u * NT + kb;
+    }
   }
 }
 
@@ -1007,8 +1168,14 @@ hipError_t launch_append(const AppendArgs& a, bool bf16, hipStream_t s) {
 hipError_t launch_attention(const AttnArgs& a, bool bf16, hipStream_t s) {
   if (bf16) {
     if (a.D != AD) return hipErrorInvalidValue;
-    const int nwg = ((a.T + ABM - 1) / ABM) * a.H;
-    attn_bf16_kernel<<<nwg, 64 * AWAVES, 0, s>>>(a);
+    // One unit per workgroup unless whole-unit rounds would leave more than
+    // 15% of kStreamWG workgroup slots idle; then the workgroups share the
+    // key tiles (needs the split slots of the workspace).
+    const int units = ((a.T + ABM - 1) / ABM) * a.H;
+    const long long rounds = (units + kStreamWG - 1) / kStreamWG;
+    const bool split = a.split && units > kStreamWG && rounds * kStreamWG * 100 > (long long)units * 115;
+    if (split) attn_bf16_kernel<true><<<kStreamWG, 64 * AWAVES, 0, s>>>(a);
+    else attn_bf16_kernel<false><<<units, 64 * AWAVES, 0, s>>>(a);
   } else if (a.D == 64) {
     const int nwg = ((a.T + 127) / 128) * a.H;
     attn_f32_kernel<64><<<nwg, 128, 0, s>>>(a);

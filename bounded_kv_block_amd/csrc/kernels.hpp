@@ -17,6 +17,16 @@ constexpr int kMaxK = 8;        // dynamic sinks per block
 constexpr int kMaxTaps = 32;    // ConvKV: conv_kernel * memory_frames source frames
 constexpr int kTokAlign = 64;   // token-stride alignment of every K / V^T buffer
 
+// bf16 attention work split.  A unit is (head, 256-query tile).  With more
+// units than kStreamWG, the kernel runs kStreamWG workgroups (8 XCDs x 32)
+// that each take an equal share of the (unit, 64-key tile) work of their
+// XCD; a unit cut by a share boundary is finished by two workgroups whose
+// fp32 partial results meet in a split slot (one per side of a boundary).
+constexpr int kAttnBM = 256;
+constexpr int kStreamWG = 256;
+constexpr int kStreamPerXcd = kStreamWG / 8;
+constexpr size_t kSplitSlotBytes = 8 * 64 * 64 * 4 + 8 * 2 * 64 * 4;   // O registers + (m, l)
+
 struct Rope {                   // 3D RoPE tables: (cos, sin) fp32 pairs, built in fp64
   const float2* t;              // [rows][dt/2]; row r <-> temporal position of row r
   const float2* h;              // [grid_h][dh/2]
@@ -49,7 +59,10 @@ struct AttnArgs {
   long long slot_bytes;
   long long slot_v_off;     // byte offset of V^T inside a slot
   long long slot_k_hs, slot_v_hs;
-  int slot_v_ld, pad_;
+  int slot_v_ld;
+  int split;                // 1: kStreamWG workgroups share the units' key tiles
+  float* part;              // split slots: 2 per share boundary, kSplitSlotBytes each
+  int* cnt;                 // arrival counter per share boundary (0 between launches)
   Seg seg[kMaxSeg];
 };
 
