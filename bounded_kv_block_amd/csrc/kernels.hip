@@ -442,13 +442,9 @@ void attn_bf16_kernel(AttnArgs a) {
     c.n = __builtin_amdgcn_readfirstlane(c.n);
     return c;
   };
-  // Common case (next full tile of the same segment) touches no LDS.  Past
-  // the last tile the enumeration wraps to the first (a piece may start
-  // anywhere in the cycle).
+  // Common case (next full tile of the same segment) touches no LDS.
   auto advance = [&](TileCursor& c) {
-    if constexpr (!SPLIT) {
-      if (c.sg >= nseg) return;
-    }
+    if (c.sg >= nseg) return;
     if (c.phase == 0) {
       c.j0 += ABN;
       if (c.j0 + ABN <= c.n) return;
@@ -461,23 +457,17 @@ void attn_bf16_kernel(AttnArgs a) {
     } else {
       c.sg = first_tail(c.sg + 1);
     }
-    if constexpr (SPLIT) {
-      if (c.sg >= nseg) {
-        c.phase = 0;
-        c.sg = first_full(0);
-        if (c.sg >= nseg) {
-          c.phase = 1;
-          c.sg = first_tail(0);
-        }
-      }
-    } else {
-      if (c.sg >= nseg) return;            // past the unit's last tile (load cursor only)
-    }
+    if (c.sg >= nseg) return;              // past the unit's last tile (load cursor only)
     c.n = seg_n(c.sg);
     c.j0 = c.phase == 1 ? c.n & ~(ABN - 1) : 0;
   };
   int NT = 0;
   for (int g = 0; g < nseg; ++g) NT += (seg_n(g) + ABN - 1) / ABN;
+  // split launch: R full rounds, then Ur remainder units each cut into rP
+  // key-tile parts (part p = tiles [NT p / rP, NT (p+1) / rP))
+  const int rR = SPLIT ? a.H * nqt / kStreamWG : 0;
+  const int rU = SPLIT ? a.H * nqt - rR * kStreamWG : 0;
+  const int rP = SPLIT && rU > 0 ? min(NT, max(1, kStreamWG / rU)) : 1;
 
   // ---- tile loads: chunk p = (4i + w)*64 + lane of a tile lands at LDS p*16
   // (w = wave within the loading group of four); the tile's first key enters
@@ -699,8 +689,9 @@ void attn_bf16_kernel(AttnArgs a) {
   };
 
   // ---- one piece: key tiles [ka, kb) of unit u = head * nqt + qt (NT tiles
-  // per unit), started at time i0 of this workgroup's share
-  auto piece = [&](int u, int ka, int kb, int i0) {
+  // per unit).  A piece of a cut unit (split launch only) is part j of
+  // remainder unit v.
+  auto piece = [&](int u, int ka, int kb, int v, int j) __attribute__((always_inline)) {
     const int head = __builtin_amdgcn_readfirstlane(u / nqt);
     const int qt = u - head * nqt;
     const int qrow = qt * ABM + wave * 32 + col;
@@ -740,13 +731,8 @@ void attn_bf16_kernel(AttnArgs a) {
     l_run = 0.f;
     negm = f32x16{};
 
-    // Key order: a unit's tiles are taken in a rotated cycle so that, at
-    // time i of the launch, every workgroup on this head reads key tile
-    // i mod NT (one K/V stream per head through L2).  Both pieces of a cut
-    // unit use the same rotation, so between them they cover every tile once.
-    const int shift = (ka == 0 && kb == NT) ? i0 % NT : (NT - (ka > 0 ? ka : kb)) % NT;
     // ---- prologue: tiles 0 and 1 of the piece loaded by group 0 (all waves wait)
-    xc = cursor_seek((ka + shift) % NT);
+    xc = cursor_seek(ka);
     lc = xc;
     if (group == 0) {
       issue(lc, 0);
@@ -819,62 +805,57 @@ void attn_bf16_kernel(AttnArgs a) {
       write_out(head, qrow);
       return;
     }
+    (void)v;
+    (void)j;
     if constexpr (SPLIT) {
-    // A piece of a cut unit: its fp32 state (O, m, l in register order) goes
-    // to the slot of its side of the share boundary; the second piece to
-    // arrive merges the first one's and writes the unit's output.
-    const int xcd = blockIdx.x & 7, j = blockIdx.x >> 3;
-    const int side = ka > 0 ? 1 : 0;       // 1: the unit's later tiles (start of this share)
-    const int bidx = xcd * kStreamPerXcd + j + (side ? 0 : 1);
-    constexpr int SLOT = (int)(kSplitSlotBytes / 4), ML = 8 * 64 * 64;
-    float* mine = a.part + (size_t)(2 * bidx + side) * SLOT;
-    const float* other = a.part + (size_t)(2 * bidx + 1 - side) * SLOT;
+      // Part j of cut remainder unit v: its fp32 state (O, m, l in register
+      // order) goes to slot j * rU + v; the last of the unit's rP parts to
+      // arrive merges the others and writes the output.
+      constexpr int SLOT = (int)(kSplitSlotBytes / 4), ML = 8 * 64 * 64;
+      float* mine = a.part + (size_t)(j * rU + v) * SLOT;
 #pragma unroll
-    for (int r = 0; r < 64; ++r) mine[(wave * 64 + r) * 64 + lane] = o[r >> 4][r & 15];
-    mine[ML + (wave * 2) * 64 + lane] = m_run;
-    mine[ML + (wave * 2 + 1) * 64 + lane] = l_run;
-    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "agent");
-    __syncthreads();
-    if (tid == 0) s_arrived = __hip_atomic_fetch_add(a.cnt + bidx, 1, __ATOMIC_ACQ_REL, __HIP_MEMORY_SCOPE_AGENT);
-    __syncthreads();
-    if (__builtin_amdgcn_readfirstlane(s_arrived) == 1) {
-      __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
-      const float m2 = other[ML + (wave * 2) * 64 + lane];
-      const float l2 = other[ML + (wave * 2 + 1) * 64 + lane];
-      const float mm = fmaxf(m_run, m2);
-      const float al = __builtin_amdgcn_exp2f(m_run - mm), be = __builtin_amdgcn_exp2f(m2 - mm);
+      for (int r = 0; r < 64; ++r) mine[(wave * 64 + r) * 64 + lane] = o[r >> 4][r & 15];
+      mine[ML + (wave * 2) * 64 + lane] = m_run;
+      mine[ML + (wave * 2 + 1) * 64 + lane] = l_run;
+      __builtin_amdgcn_fence(__ATOMIC_RELEASE, "agent");
+      __syncthreads();
+      if (tid == 0) s_arrived = __hip_atomic_fetch_add(a.cnt + v, 1, __ATOMIC_ACQ_REL, __HIP_MEMORY_SCOPE_AGENT);
+      __syncthreads();
+      if (__builtin_amdgcn_readfirstlane(s_arrived) == rP - 1) {
+        __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
+        for (int q = 0; q < rP; ++q) {
+          if (q == j) continue;
+          const float* other = a.part + (size_t)(q * rU + v) * SLOT;
+          const float m2 = other[ML + (wave * 2) * 64 + lane];
+          const float l2 = other[ML + (wave * 2 + 1) * 64 + lane];
+          const float mm = fmaxf(m_run, m2);
+          const float al = __builtin_amdgcn_exp2f(m_run - mm), be = __builtin_amdgcn_exp2f(m2 - mm);
 #pragma unroll
-      for (int r = 0; r < 64; ++r)
-        o[r >> 4][r & 15] = al * o[r >> 4][r & 15] + be * other[(wave * 64 + r) * 64 + lane];
-      l_run = al * l_run + be * l2;
-      if (tid == 0) __hip_atomic_store(a.cnt + bidx, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-      write_out(head, qrow);
-    }
+          for (int r = 0; r < 64; ++r)
+            o[r >> 4][r & 15] = al * o[r >> 4][r & 15] + be * other[(wave * 64 + r) * 64 + lane];
+          l_run = al * l_run + be * l2;
+          m_run = mm;
+        }
+        if (tid == 0) __hip_atomic_store(a.cnt + v, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        write_out(head, qrow);
+      }
     }
   };
 
   if constexpr (!SPLIT) {
     // one unit per workgroup, XCD-contiguous (the query tiles of a head share an L2)
     const int u = __builtin_amdgcn_readfirstlane(xcd_remap(blockIdx.x, gridDim.x));
-    piece(u, 0, NT, 0);
+    piece(u, 0, NT, -1, 0);
   } else {
-    // An equal share of the (unit, key tile) work of the workgroup's XCD:
-    // XCD x owns units [x U/8, (x+1) U/8) and its 32 workgroups cut them at
-    // share boundaries, so a cut unit's two pieces meet in one XCD's L2.
-    // (32-bit: units * tiles stays far below 2^31; every per-piece scalar is
-    // re-read as wave-uniform so the loop control stays on the scalar unit.)
-    const int xcd = blockIdx.x & 7, j = blockIdx.x >> 3;
-    const int U = a.H * nqt;
-    const int u0 = (xcd * U) >> 3, u1 = ((xcd + 1) * U) >> 3;
-    const int tt = (u1 - u0) * NT;
-    const int t0 = __builtin_amdgcn_readfirstlane(u0 * NT + (int)((long long)tt * j / kStreamPerXcd));
-    const int t1 = __builtin_amdgcn_readfirstlane(u0 * NT + (int)((long long)tt * (j + 1) / kStreamPerXcd));
-    for (int pos = t0; pos < t1;) {
-      const int u = __builtin_amdgcn_readfirstlane(pos / NT);
-      const int ka = __builtin_amdgcn_readfirstlane(pos - u * NT);
-      const int kb = __builtin_amdgcn_readfirstlane(min(NT, t1 - u * NT));
-      piece(u, ka, kb, pos - t0);
-      pos = u * NT + kb;
+    // kStreamWG workgroups: rR full rounds of one unit each (XCD-contiguous,
+    // all workgroups of a round in step on the same key tiles), then part
+    // p of remainder unit v on workgroup p * rU + v: the query tiles of a head
+    // read the same key part at the same time.
+    const int jw = __builtin_amdgcn_readfirstlane(xcd_remap(blockIdx.x, kStreamWG));
+    for (int r = 0; r < rR; ++r) piece(r * kStreamWG + jw, 0, NT, -1, 0);
+    if (jw < rU * rP) {
+      const int v = jw % rU, p = jw / rU;
+      piece(rR * kStreamWG + v, NT * p / rP, NT * (p + 1) / rP, v, p);
     }
   }
 }
