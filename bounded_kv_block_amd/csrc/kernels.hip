@@ -74,52 +74,67 @@ __global__ void rope_table_kernel(float2* tab, int rows, int half, int dim, long
 }
 
 // ------------------------------------------------------------------ block open
-// One wavefront.  Scores: cos = dot / (sqrt(|q|^2) sqrt(|b|^2)) in fp64 with a
-// fixed sequential summation order per candidate; 0 when either norm is 0.
-// Rank: (score desc, stream id asc), selected by k rounds of a wave arg-max.
-__global__ __launch_bounds__(64) void open_kernel(OpenArgs a) {
+// 256 threads, one per bank candidate.  Scores: cos = dot / (sqrt(|q|^2)
+// sqrt(|b|^2)) in fp64, each candidate's sums in one fixed sequential order
+// over the pose dimensions (staged through LDS 64 dimensions at a time, rows
+// padded so that the 256 lanes hit distinct banks); 0 when either norm is 0.
+// Rank: (score desc, stream id asc), k rounds of an arg-max by wave 0.
+constexpr int kOpenThreads = 256;
+constexpr int kOpenChunk = 64;
+__global__ __launch_bounds__(kOpenThreads) void open_kernel(OpenArgs a) {
   __shared__ double s_score[kMaxBank];
   __shared__ int s_taken[kMaxBank];
-  const int lane = threadIdx.x;
+  __shared__ float s_q[kOpenChunk];
+  __shared__ float s_b[kMaxBank][kOpenChunk + 1];
+  const int tid = threadIdx.x, lane = tid & 63;
   if (a.pose_in) {
-    for (int i = lane; i < a.P; i += 64) a.pose_store[(size_t)a.cur_slot * a.P + i] = a.pose_in[i];
+    for (int i = tid; i < a.P; i += kOpenThreads) a.pose_store[(size_t)a.cur_slot * a.P + i] = a.pose_in[i];
   }
   if (a.ttab) {
     const int half = a.t_dim >> 1;
-    for (int idx = lane; idx < a.t_rows * half; idx += 64) {
+    for (int idx = tid; idx < a.t_rows * half; idx += kOpenThreads) {
       const int r = idx / half, i = idx - r * half;
       const double w = pow(a.theta, -2.0 * (double)i / (double)a.t_dim);
-      double s, c;
-      sincos((double)(a.t_pos0 + r) * w, &s, &c);
-      a.ttab[idx] = make_float2((float)c, (float)s);
+      double sn, cs;
+      sincos((double)(a.t_pos0 + r) * w, &sn, &cs);
+      a.ttab[idx] = make_float2((float)cs, (float)sn);
     }
   }
   if (a.k <= 0 || a.nbank <= 0) return;
-  double qq = 0.0;
-  for (int i = 0; i < a.P; ++i) {
-    const double x = (double)a.pose_in[i];
-    qq += x * x;
-  }
-  for (int c = lane; c < a.nbank; c += 64) {
-    const float* b = a.pose_store + (size_t)a.bank_slot[c] * a.P;
-    double dot = 0.0, bb = 0.0;
-    for (int i = 0; i < a.P; ++i) {
-      const double x = (double)a.pose_in[i];
-      const double y = (double)b[i];
-      dot += x * y;
-      bb += y * y;
+  const int nb = a.nbank;
+  double qq = 0.0, dot = 0.0, bb = 0.0;
+  for (int c0 = 0; c0 < a.P; c0 += kOpenChunk) {
+    const int w = min(kOpenChunk, a.P - c0);
+    __syncthreads();                       // the previous chunk has been consumed
+    if (tid < w) s_q[tid] = a.pose_in[c0 + tid];
+    for (int idx = tid; idx < nb * w; idx += kOpenThreads) {
+      const int c = idx / w, i = idx - c * w;
+      s_b[c][i] = a.pose_store[(size_t)a.bank_slot[c] * a.P + c0 + i];
     }
+    __syncthreads();
+    if (tid < nb) {
+      for (int i = 0; i < w; ++i) {
+        const double x = (double)s_q[i];
+        const double y = (double)s_b[tid][i];
+        qq += x * x;
+        dot += x * y;
+        bb += y * y;
+      }
+    }
+  }
+  if (tid < nb) {
     double sc = 0.0;
     if (qq > 0.0 && bb > 0.0) sc = dot / (sqrt(qq) * sqrt(bb));
-    s_score[c] = sc;
-    s_taken[c] = 0;
+    s_score[tid] = sc;
+    s_taken[tid] = 0;
   }
   __syncthreads();
-  const int kk = a.k < a.nbank ? a.k : a.nbank;
+  if (tid >= 64) return;
+  const int kk = a.k < nb ? a.k : nb;
   for (int r = 0; r < kk; ++r) {
     double best = -INFINITY;
     int bid = 0x7fffffff, bc = -1;
-    for (int c = lane; c < a.nbank; c += 64) {
+    for (int c = lane; c < nb; c += 64) {
       if (s_taken[c]) continue;
       const double sc = s_score[c];
       const int id = a.bank_id[c];
@@ -144,7 +159,8 @@ __global__ __launch_bounds__(64) void open_kernel(OpenArgs a) {
       a.sel_slots[r] = a.bank_slot[bc];
       s_taken[bc] = 1;
     }
-    __syncthreads();
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
   }
 }
 
@@ -1127,7 +1143,7 @@ hipError_t launch_rope_table(float2* tab, int rows, int dim, long long pos0, dou
 }
 
 hipError_t launch_open(const OpenArgs& a, hipStream_t s) {
-  open_kernel<<<1, 64, 0, s>>>(a);
+  open_kernel<<<1, kOpenThreads, 0, s>>>(a);
   return hipGetLastError();
 }
 
