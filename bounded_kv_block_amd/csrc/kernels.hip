@@ -166,14 +166,21 @@ __global__ __launch_bounds__(kOpenThreads) void open_kernel(OpenArgs a) {
 
 // ------------------------------------------------------------------ append
 // One workgroup per (64-token tile, head).  K: each thread moves 16-byte chunks
-// of a token's row, rotating pairs in fp32.  V: the tile goes through LDS and
-// leaves as rows of V^T (64 consecutive tokens of one channel).
+// of a token's row, rotating pairs in fp32.  V: the tile goes into LDS as
+// whole 16-byte chunks (chunk c of row r at c ^ ((r >> 3) & 7)), then each
+// thread reads 8-byte slices of TOK consecutive tokens and writes CH rows of
+// V^T (TOK tokens of one channel, 16 bytes each); consecutive lanes take
+// consecutive token groups, so each V^T row is written in contiguous runs.
+// Tokens past the block's end are never written, so the V^T pad columns
+// keep their zeros.
 template <typename T, int D>
 __global__ __launch_bounds__(256) void append_kernel(AppendArgs a) {
   constexpr int VEC = 16 / sizeof(T);          // elements per 16-byte chunk
   constexpr int CPR = D / VEC;                 // chunks per row
-  constexpr int PAD = 2;
-  __shared__ T s_v[64][D + PAD];
+  constexpr int RS = D * (int)sizeof(T);       // LDS row stride (bytes)
+  constexpr int CH = 8 / sizeof(T);            // channels per 8-byte slice
+  constexpr int TOK = VEC;                     // tokens per 16-byte V^T store
+  __shared__ __attribute__((aligned(16))) char s_v[64 * RS];
   const int tile0 = blockIdx.x * 64;
   const int head = blockIdx.y;
   const int tid = threadIdx.x;
@@ -184,11 +191,9 @@ __global__ __launch_bounds__(256) void append_kernel(AppendArgs a) {
     if (r >= ntok) continue;
     const int tok = tile0 + r;
     const size_t src = ((size_t)tok * a.H + head) * D + c * VEC;
-    uint4 kraw = *reinterpret_cast<const uint4*>(static_cast<const T*>(a.k_in) + src);
-    uint4 vraw = *reinterpret_cast<const uint4*>(static_cast<const T*>(a.v_in) + src);
-    const T* vv = reinterpret_cast<const T*>(&vraw);
-#pragma unroll
-    for (int e = 0; e < VEC; ++e) s_v[r][c * VEC + e] = vv[e];
+    const uint4 kraw = *reinterpret_cast<const uint4*>(static_cast<const T*>(a.k_in) + src);
+    const uint4 vraw = *reinterpret_cast<const uint4*>(static_cast<const T*>(a.v_in) + src);
+    *reinterpret_cast<uint4*>(s_v + r * RS + ((c ^ ((r >> 3) & 7)) << 4)) = vraw;
     if (a.k_raw) {
       T* dst = static_cast<T*>(a.k_raw) + head * a.k_raw_hs + (size_t)tok * D + c * VEC;
       *reinterpret_cast<uint4*>(dst) = kraw;
@@ -213,19 +218,32 @@ __global__ __launch_bounds__(256) void append_kernel(AppendArgs a) {
     }
   }
   __syncthreads();
-  constexpr int TG = 64 / VEC;                 // token groups of VEC per V^T row tile
-  for (int task = tid; task < D * TG; task += 256) {
-    const int d = task / TG, g = task - d * TG;
-    T* dst = static_cast<T*>(a.vt) + head * a.vt_hs + (size_t)d * a.vt_ld + tile0 + g * VEC;
-    if ((g + 1) * VEC <= ntok) {
-      uint4 w;
-      T* wv = reinterpret_cast<T*>(&w);
+  constexpr int NCG = D / CH, NTG = 64 / TOK;  // channel groups, token groups
+  for (int task = tid; task < NCG * NTG; task += 256) {
+    const int tg = task % NTG, cg = task / NTG;
+    const int t0 = tg * TOK;
+    if (t0 >= ntok) continue;
+    typedef T rowv __attribute__((ext_vector_type(TOK)));
+    typedef T slicev __attribute__((ext_vector_type(CH)));
+    rowv col[CH];
 #pragma unroll
-      for (int e = 0; e < VEC; ++e) wv[e] = s_v[g * VEC + e][d];
-      *reinterpret_cast<uint4*>(dst) = w;
-    } else {
-      for (int e = 0; e < VEC; ++e)
-        if (g * VEC + e < ntok) dst[e] = s_v[g * VEC + e][d];
+    for (int e = 0; e < TOK; ++e) {
+      const int t = t0 + e;
+      const slicev w = *reinterpret_cast<const slicev*>(s_v + t * RS + (((cg >> 1) ^ ((t >> 3) & 7)) << 4) + (cg & 1) * 8);
+#pragma unroll
+      for (int ch = 0; ch < CH; ++ch) col[ch][e] = w[ch];
+    }
+    const int nv = ntok - t0;
+#pragma unroll
+    for (int ch = 0; ch < CH; ++ch) {
+      T* dst = static_cast<T*>(a.vt) + head * a.vt_hs + (size_t)(cg * CH + ch) * a.vt_ld + tile0 + t0;
+      if (nv >= TOK) {
+        *reinterpret_cast<rowv*>(dst) = col[ch];
+      } else {
+#pragma unroll
+        for (int e = 0; e < TOK; ++e)
+          if (e < nv) dst[e] = col[ch][e];
+      }
     }
   }
 }
