@@ -46,7 +46,7 @@ class Stats(ctypes.Structure):
     _fields_ = [("block", ctypes.c_int64), ("open", ctypes.c_int32), ("n_segments", ctypes.c_int32),
                 ("n_keys", ctypes.c_int64), ("last_evicted", ctypes.c_int64),
                 ("bank_count", ctypes.c_int32), ("memory_count", ctypes.c_int32),
-                ("workspace_bytes", ctypes.c_size_t)]
+                ("workspace_bytes", ctypes.c_size_t), ("split_attends", ctypes.c_int64)]
 
 
 class KernelTime(ctypes.Structure):

@@ -166,6 +166,7 @@ struct bkv_cache_s {
   bool error = false;
   std::vector<bool> ctx_ready;      // ConvKV: context K of the layer gathered for the open block
   std::vector<bool> weights_set;    // ConvKV: conv weights given per layer
+  int64_t split_attends = 0;        // bf16 attention launches that used the split launch
   struct Prof {                     // per-launch HIP event pairs (bkv_profile_start/stop)
     bool on = false;
     int cap = 0, used = 0;
@@ -398,6 +399,7 @@ bkv_status bkv_reset(bkv_cache h) {
   h->sched.reset();
   h->error = false;
   h->ctx_ready.assign(h->cfg.layers, false);
+  h->split_attends = 0;
   if (h->L.split) {
     // arrival counters return to 0 at the end of every launch; a launch cut
     // short by a device error may leave them set
@@ -534,6 +536,7 @@ bkv_status bkv_attend(bkv_cache h, int32_t layer, const void* q, const void* k, 
   for (int i = 0; i < a.nseg; ++i) a.seg[i] = h->seg_arg(layer, segs[i]);
   e = timed(h, K_ATTENTION, stream, [&] { return bkv::launch_attention(a, h->bf16(), stream); });
   if (e != hipSuccess) return device_fail(h, e, "attention launch");
+  if (h->bf16() && bkv::attention_split(a.T, a.H, a.split != 0)) ++h->split_attends;
   h->sched.mark_attended(layer);
   return BKV_OK;
 }
@@ -636,6 +639,7 @@ bkv_status bkv_stats(bkv_cache h, bkv_stats_t* out) {
   out->bank_count = (int32_t)h->sched.bank().size();
   out->memory_count = h->sched.memory_count();
   out->workspace_bytes = h->L.total;
+  out->split_attends = h->split_attends;
   return BKV_OK;
 }
 

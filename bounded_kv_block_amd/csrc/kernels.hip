@@ -1187,9 +1187,7 @@ hipError_t launch_attention(const AttnArgs& a, bool bf16, hipStream_t s) {
     // 15% of kStreamWG workgroup slots idle; then the workgroups share the
     // key tiles (needs the split slots of the workspace).
     const int units = ((a.T + ABM - 1) / ABM) * a.H;
-    const long long rounds = (units + kStreamWG - 1) / kStreamWG;
-    const bool split = a.split && units > kStreamWG && rounds * kStreamWG * 100 > (long long)units * 115;
-    if (split) attn_bf16_kernel<true><<<kStreamWG, 64 * AWAVES, 0, s>>>(a);
+    if (attention_split(a.T, a.H, a.split != 0)) attn_bf16_kernel<true><<<kStreamWG, 64 * AWAVES, 0, s>>>(a);
     else attn_bf16_kernel<false><<<units, 64 * AWAVES, 0, s>>>(a);
   } else if (a.D == 64) {
     const int nwg = ((a.T + 127) / 128) * a.H;

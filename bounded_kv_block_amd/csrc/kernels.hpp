@@ -131,6 +131,15 @@ hipError_t launch_rope_table(float2* tab, int rows, int dim, long long pos0, dou
 hipError_t launch_open(const OpenArgs& a, hipStream_t s);
 hipError_t launch_append(const AppendArgs& a, bool bf16, hipStream_t s);
 hipError_t launch_attention(const AttnArgs& a, bool bf16, hipStream_t s);
+
+// The bf16 attention shares key tiles across kStreamWG workgroups when its
+// (head, kAttnBM-query) units would leave more than 15% of whole-unit rounds
+// idle and the workspace holds split slots.
+inline bool attention_split(int T, int H, bool slots) {
+  const long long units = (long long)((T + kAttnBM - 1) / kAttnBM) * H;
+  const long long rounds = (units + kStreamWG - 1) / kStreamWG;
+  return slots && units > kStreamWG && rounds * kStreamWG * 100 > units * 115;
+}
 hipError_t launch_gather(const GatherArgs& a, bool bf16, hipStream_t s);
 hipError_t launch_conv(const ConvArgs& a, bool bf16, hipStream_t s);
 hipError_t launch_export(const ExportArgs& a, bool bf16, hipStream_t s);

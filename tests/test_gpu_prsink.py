@@ -92,7 +92,30 @@ def test_prsink_512_full_shape_sampled():
     including the last) on blocks 0, 4, 6 and 9."""
     cfg = synth.workload("prsink_512", blocks=10)
     rows = np.r_[0:64, 1500:1532, 3008:3072]
-    _stream(cfg, host_inputs=False, check={0, 4, 6, 9}, heads=[0, 39], rows=rows)
+    run = _stream(cfg, host_inputs=False, check={0, 4, 6, 9}, heads=[0, 39], rows=rows)
+    assert run.cache.stats()["split_attends"] == 0        # 480 units: 6% idle, one unit per workgroup
+
+
+def test_split_launch_key_parts_ragged_tile():
+    """1800-query blocks with 40 heads: 320 (head, 256-query) units leave the
+    second round of 256 workgroups 75% idle, so the attention runs its split
+    launch: one full round, then the 64 remainder units (heads 32..39) each
+    cut into 4 key parts whose fp32 states are merged.  Outputs of heads in
+    the full round and in the remainder, rows in several query tiles incl.
+    the ragged last one (8 rows), against the oracle."""
+    cfg = synth.workload("prsink_512", frames=2, grid_h=30, grid_w=30, blocks=8)
+    run = _stream(cfg, host_inputs=False, check={0, 4, 7}, heads=[0, 33, 39],
+                  rows=np.r_[0:64, 900:964, 1736:1800])
+    assert run.cache.stats()["split_attends"] == cfg["blocks"]
+
+
+def test_split_launch_whole_remainder_units():
+    """2560-query blocks with 40 heads: 400 units; the split launch runs one
+    full round and the 144 remainder units whole (one key part each)."""
+    cfg = synth.workload("prsink_512", frames=2, grid_h=32, grid_w=40, blocks=8)
+    run = _stream(cfg, host_inputs=False, check={0, 7}, heads=[0, 25, 39],
+                  rows=np.r_[0:64, 1536:1600, 2496:2560])
+    assert run.cache.stats()["split_attends"] == cfg["blocks"]
 
 
 def test_multistep_multilayer_commit_after_last_step():

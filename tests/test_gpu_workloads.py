@@ -42,6 +42,8 @@ def test_prsink_720x416_layers_steps_sampled():
         run.cache.commit()
         run._host.clear()
     assert checked == 6 and n_keys == 7 * 3510
+    # 560 units (2.19 rounds of 256 workgroups): every attend used the split launch
+    assert run.cache.stats()["split_attends"] == cfg["blocks"] * L * S
 
 
 def test_prsink_long_stream_1080_blocks():
