@@ -18,7 +18,9 @@ Sources (pages, by title and section):
     (constant cache size), section 局限 (retrieval by pose similarity).
   * Soul App开源实时数字人生成框架SoulX-LiveAct详解 -- section 技术内核,
     ConvKV Memory bullet (exact recent KV, older history compressed by a 1D
-    conv up to 5:1 into fixed-length memory, RoPE positions reset).
+    conv up to 5:1 into fixed-length memory, RoPE positions reset); sections
+    关键信息速览 and 上手实践 (FP8 attention in deployment; the E4M3 key cache
+    scheme in ``fp8`` is this package's reading).
 
 Where the pages leave a step open, the reading taken is stated in the
 function that implements it.  Every function is pinned by a CPU test against
@@ -31,10 +33,11 @@ from .rope import rope_frequencies, apply_rope
 from .attention import attention, masked_attention, softmax_weights
 from .convkv import conv_memory
 from .stream import PRSinkReference, ConvKVReference
+from . import fp8
 
 __all__ = [
     "prsink_schedule", "simulate_prsink", "convkv_schedule", "simulate_convkv",
     "token_positions", "retrieve", "exact_keys", "fp64_cosines", "boundary_gap",
     "rope_frequencies", "apply_rope", "attention", "masked_attention", "softmax_weights",
-    "conv_memory", "PRSinkReference", "ConvKVReference",
+    "conv_memory", "PRSinkReference", "ConvKVReference", "fp8",
 ]

@@ -15,11 +15,14 @@ Readings (beyond those stated in the modules used here):
     three steps), a committed block contributes the K/V of its last step.
   * ConvKV context order is [memory frames, window blocks oldest first,
     current block]; temporal positions run 0, 1, 2, ... over those frames.
+  * PR-Sink with an FP8 key cache (dtype "bf16_fp8k"): K and Q are quantised
+    to E4M3 as ``fp8`` states before Q K^T; V and the softmax are unchanged.
 """
 from __future__ import annotations
 
 import numpy as np
 
+from . import fp8
 from .attention import attention
 from .convkv import conv_memory
 from .retrieval import retrieve
@@ -102,7 +105,19 @@ class PRSinkReference(_Base):
         q, _, _ = self.p.qkv(layer, m, step)
         q_rot = self._rot(q, lambda f: m * self.F + f, heads)
         kv = self.context_kv(m, layer, step, heads, selection)
-        return self._attend(q_rot, [x[2] for x in kv], [x[3] for x in kv], heads, rows)
+        if self.cfg["dtype"] != "bf16_fp8k":
+            return self._attend(q_rot, [x[2] for x in kv], [x[3] for x in kv], heads, rows)
+        # FP8 key cache: logits from E4M3 Q (in log2 units, per-row scale) and
+        # E4M3 K (per 64-token tile scale); quantising Q row by row lets the
+        # unrequested rows stay zero.
+        log2e = 1.0 / np.log(2.0)
+        s = _scale(self.cfg)
+        rs = np.arange(self.T) if rows is None else np.asarray(rows)
+        qe = np.zeros_like(q_rot)
+        qe[rs] = fp8.quantize_queries(q_rot[rs] * (s * log2e)) / log2e
+        k = np.concatenate([fp8.quantize_keys(x[2]) for x in kv], axis=0)
+        v = np.concatenate([x[3] for x in kv], axis=0)
+        return attention(qe, k, v, 1.0, rows=rows)
 
 
 class ConvKVReference(_Base):

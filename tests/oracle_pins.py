@@ -226,3 +226,72 @@ def check_conv_memory(conv_memory, rng):
     two = rng.standard_normal((2 * K, H, S, D))                       # two output frames, stride K
     out = conv_memory(two, w)
     assert out.shape[0] == 2 and np.allclose(out[1], conv_memory(two[K:], w)[0], atol=1e-14)
+
+
+# -- FP8 (E4M3) quantisation ----------------------------------------------------
+def _e4m3_sweep():
+    """Every bf16 magnitude in [2^-12, 448], the midpoints between neighbours,
+    the subnormal grid and its midpoints, both signs, and zero."""
+    mags = [np.ldexp(1.0 + m / 128.0, e) for e in range(-12, 9) for m in range(128)]
+    mags += [np.ldexp(1.0 + (m + 0.5) / 128.0, e) for e in range(-12, 9) for m in range(128)]
+    mags += [j * 2.0 ** -10 for j in range(0, 16)]
+    x = np.array(mags, np.float64)
+    x = x[x <= 448.0]
+    return np.concatenate([x, -x, [0.0]])
+
+
+def check_e4m3_vs_torch(e4m3_round):
+    """Library pin: torch's float8_e4m3fn conversion (OCP E4M3, nearest-even)."""
+    import torch
+    x = _e4m3_sweep()
+    want = torch.from_numpy(x).to(torch.float8_e4m3fn).to(torch.float64).numpy()
+    got = e4m3_round(x)
+    assert np.array_equal(got, want), np.nonzero(got != want)[0][:5]
+
+
+def check_e4m3_hand(e4m3_round):
+    """Values worked by hand from the format (3 mantissa bits, bias 7, max 448)."""
+    cases = [(1.0, 1.0), (1.0625, 1.0), (1.1875, 1.25), (-1.0625, -1.0), (448.0, 448.0),
+             (440.0, 448.0), (424.0, 416.0), (2.0 ** -6, 2.0 ** -6), (1.5 * 2.0 ** -9, 2.0 ** -8),
+             (0.5 * 2.0 ** -9, 0.0), (0.75 * 2.0 ** -9, 2.0 ** -9), (3.0 * 2.0 ** -10, 2.0 ** -8)]
+    for x, want in cases:
+        assert e4m3_round(np.array([x]))[0] == want, (x, want)
+
+
+def check_pow2_exponent(pow2_exponents, rng):
+    """The smallest e with amax * 2^-e <= 448: hand values and the defining
+    inequalities on random magnitudes."""
+    hand = [(448.0, 0), (449.0, 1), (224.0, -1), (224.5, 0), (1.0, -8), (0.0, 0), (3.5, -7)]
+    for a, e in hand:
+        assert pow2_exponents(np.array([a]))[0] == e, (a, e)
+    a = np.exp(rng.uniform(-20, 20, 2000))
+    e = pow2_exponents(a)
+    assert np.all(a * 2.0 ** -e.astype(float) <= 448.0)
+    assert np.all(a * 2.0 ** -(e - 1).astype(float) > 448.0)
+
+
+def check_fp8_groups(quantize_keys, quantize_queries, rng):
+    """Group structure: K has one scale per (64-token tile, head), Q one per
+    (token, head); values representable at the group's scale are kept exactly;
+    relative rounding error of normal values is at most 2^-4."""
+    T, H, D = 150, 3, 16
+    k = rng.standard_normal((T, H, D))
+    qk = quantize_keys(k)
+    # a tile's values depend only on that tile: scaling tile 1 of head 2 by 2^10
+    k2 = k.copy()
+    k2[64:128, 2] *= 2.0 ** 10
+    qk2 = quantize_keys(k2)
+    assert np.array_equal(np.delete(qk2, np.s_[64:128], axis=0), np.delete(qk, np.s_[64:128], axis=0))
+    assert np.array_equal(qk2[64:128, :2], qk[64:128, :2])
+    assert np.array_equal(qk2[64:128, 2], qk[64:128, 2] * 2.0 ** 10)
+    big = np.abs(k) > np.abs(k).max() * 2.0 ** -6
+    assert np.all(np.abs(qk - k)[big] <= 2.0 ** -4 * np.abs(k)[big] + 1e-300)
+    # a row of E4M3 values whose largest magnitude is 448 is unchanged
+    q = rng.integers(-8, 9, (4, 2, D)).astype(np.float64)
+    q[:, :, 0] = 448.0
+    assert np.array_equal(quantize_queries(q), q)
+    # per-row scales: one row's magnitude does not affect another row
+    q3 = rng.standard_normal((5, 2, D))
+    q4 = q3.copy()
+    q4[2] *= 1e4
+    assert np.array_equal(np.delete(quantize_queries(q4), 2, axis=0), np.delete(quantize_queries(q3), 2, axis=0))

@@ -217,3 +217,19 @@ def test_convkv_memory_with_onehot_weights():
         assert np.allclose(kv[0][2], want_k, atol=1e-13)
         assert np.array_equal(kv[0][3], np.asarray(v[sl], np.float64))
         assert [s[0] for s in kv] == ["memory", "window", "window", "window", "current"]
+
+
+def test_e4m3_rounding_vs_torch():
+    pins.check_e4m3_vs_torch(oracle.fp8.e4m3_round)
+
+
+def test_e4m3_hand_values():
+    pins.check_e4m3_hand(oracle.fp8.e4m3_round)
+
+
+def test_pow2_scale_exponent(rng):
+    pins.check_pow2_exponent(oracle.fp8.pow2_exponents, rng)
+
+
+def test_fp8_group_scales(rng):
+    pins.check_fp8_groups(oracle.fp8.quantize_keys, oracle.fp8.quantize_queries, rng)

@@ -187,3 +187,53 @@ def _conv_overlapping(frames, w, stride=None):
 @pytest.mark.parametrize("mutant", [_conv_reversed_taps, _conv_shared_weights, _conv_overlapping])
 def test_conv_mutants_fail(mutant, rng):
     assert _fails(pins.check_conv_memory, mutant, rng)
+
+
+# -- FP8 mutants ----------------------------------------------------------------
+def _e4m3_half_up(x):
+    x = np.asarray(x, np.float64)
+    a = np.abs(x)
+    _, ex = np.frexp(np.where(a > 0, a, 1.0))
+    quantum = np.where(a >= 2.0 ** -6, np.ldexp(1.0, ex - 4), 2.0 ** -9)
+    return np.copysign(np.floor(a / quantum + 0.5) * quantum, x)
+
+
+def _e4m3_no_subnormals(x):
+    x = np.asarray(x, np.float64)
+    y = oracle.fp8.e4m3_round(x)
+    return np.where(np.abs(y) < 2.0 ** -6, 0.0, y)
+
+
+def _e4m3_fnuz_bias(x):                 # exponent bias 8: the grid one binade lower, max 224
+    x = np.clip(np.asarray(x, np.float64) * 2.0, -448.0, 448.0)
+    return oracle.fp8.e4m3_round(x) / 2.0
+
+
+@pytest.mark.parametrize("mutant", [_e4m3_half_up, _e4m3_no_subnormals, _e4m3_fnuz_bias])
+def test_e4m3_mutants_fail(mutant):
+    assert _fails(pins.check_e4m3_vs_torch, mutant) or _fails(pins.check_e4m3_hand, mutant)
+
+
+def _pow2_off_by_one(a):
+    return oracle.fp8.pow2_exponents(a) - 1
+
+
+def _pow2_ceil_log(a):                  # ceil(log2(a / 256)): too coarse a scale
+    a = np.asarray(a, np.float64)
+    return np.where(a > 0, np.ceil(np.log2(np.where(a > 0, a, 1.0) / 256.0)), 0).astype(np.int64)
+
+
+@pytest.mark.parametrize("mutant", [_pow2_off_by_one, _pow2_ceil_log])
+def test_pow2_mutants_fail(mutant, rng):
+    assert _fails(pins.check_pow2_exponent, mutant, rng)
+
+
+def _keys_per_head(k):                  # one scale per head over the whole block
+    k = np.asarray(k, np.float64)
+    sc = np.ldexp(1.0, oracle.fp8.pow2_exponents(np.abs(k).max(axis=(0, 2))))[None, :, None]
+    return oracle.fp8.e4m3_round(k / sc) * sc
+
+
+@pytest.mark.parametrize("mutant", [_keys_per_head])
+def test_fp8_group_mutants_fail(mutant, rng):
+    assert _fails(pins.check_fp8_groups, mutant, oracle.fp8.quantize_queries, rng)
