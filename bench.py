@@ -26,6 +26,7 @@ if ROOT not in sys.path:
 
 METRIC = "query tokens/s & TFLOP/s of bounded-KV block attention (% bf16 MFMA peak)"
 PEAK_BF16_TFLOPS = 2500.0      # MI355X dense bf16 MFMA
+PEAK_FP8_TFLOPS = 5000.0       # MI355X dense fp8 MFMA
 PEAK_FP32_TFLOPS = 157.3       # MI355X fp32 vector
 PEAK_HBM_GBS = 8000.0          # MI355X HBM3E
 
@@ -36,7 +37,8 @@ def parse():
     ap.add_argument("--steps", type=int, default=40)
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--workload", default="prsink_512",
-                    choices=["prsink_512", "prsink_720x416", "prsink_long", "convkv_512", "tiny_fp32"])
+                    choices=["prsink_512", "prsink_512_fp8k", "prsink_720x416", "prsink_long", "convkv_512",
+                             "tiny_fp32"])
     ap.add_argument("--pool", type=int, default=4, help="distinct resident input blocks cycled through")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=12.0, help="target CPU-oracle sample time")
@@ -233,19 +235,25 @@ def main():
     wall = t1 - t0
     per_block = np.array([ev[i].elapsed_time(ev[i + 1]) for i in range(args.steps)])
 
-    bf16 = cfg["dtype"] == "bf16"
+    bf16 = cfg["dtype"] != "f32"
+    fp8k = cfg["dtype"] == "bf16_fp8k"
     Nk = int(np.median(n_keys))
     flop_attend = 4.0 * H * T * Nk * D
     attn_n, attn_ms, _ = kt["attention"]
     attn_avg_ms = attn_ms / attn_n
     attn_tflops = flop_attend / (attn_avg_ms * 1e-3) / 1e12
     peak = PEAK_BF16_TFLOPS if bf16 else PEAK_FP32_TFLOPS
+    if fp8k:
+        # half the flops (Q K^T) on fp8 MFMA, half (P V) on bf16: the peak of
+        # that mix is the harmonic mean of the two
+        peak = 1.0 / (0.5 / PEAK_FP8_TFLOPS + 0.5 / PEAK_BF16_TFLOPS)
     esz = 2 if bf16 else 4
+    kesz = 1 if fp8k else esz                               # bytes per cached K value
     kernels = {}
     for name, (n, tot, mx) in kt.items():
         kernels[name] = {"launches": int(n), "avg_us": 1e3 * tot / n, "max_us": 1e3 * mx}
     # algorithmic bytes of the HBM-bound kernels, per launch
-    app_bytes = 4.0 * T * H * D * esz                       # K, V read token-major; written to the cache
+    app_bytes = 2.0 * T * H * D * esz + T * H * D * (kesz + esz)   # K, V read token-major; written to the cache
     kernels["append"]["gbs"] = app_bytes / (kernels["append"]["avg_us"] * 1e-6) / 1e9
     if "gather" in kernels:
         ctx_rows = Nk - T
@@ -259,7 +267,7 @@ def main():
     attends_per_step = L * S
     # algorithmic bytes of one attention launch: Q and the output once, K and V
     # of the whole bounded context once
-    attn_bytes = 2.0 * T * H * D * esz + 2.0 * Nk * H * D * esz
+    attn_bytes = 2.0 * T * H * D * esz + Nk * H * D * (kesz + esz)
     value = args.steps * T / wall
     res = {
         "metric": METRIC,
@@ -272,7 +280,7 @@ def main():
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "bf16" if bf16 else "f32",
+        "dtype": ("fp8_e4m3 QK^T + bf16 PV" if fp8k else "bf16") if bf16 else "f32",
         "data": "synthetic",
         "config": {"workload": cfg["name"], "mode": cfg["mode"], "heads": H, "head_dim": D,
                    "queries_per_block": T, "keys_per_block": Nk, "layers": L, "steps_per_block": S,
@@ -281,6 +289,7 @@ def main():
                    "timed_blocks": [m - args.steps, m - 1]},
         "attention_tflops": attn_tflops,
         "attention_pct_peak": 100.0 * attn_tflops / peak,
+        "attention_peak_tflops": peak,
         "step_tflops": flop_attend * attends_per_step * args.steps / wall / 1e12,
         "latency_ms": {"p50": float(np.percentile(per_block, 50)), "p99": float(np.percentile(per_block, 99)),
                        "max": float(per_block.max())},

@@ -15,7 +15,8 @@ LIB_PATH = os.path.join(HERE, "libbkv.so")
 
 BKV_OK, BKV_ERR_ARG, BKV_ERR_STATE, BKV_ERR_WORKSPACE, BKV_ERR_DEVICE, BKV_ERR_UNSUPPORTED = range(6)
 PR_SINK, CONVKV = 0, 1
-F32, BF16 = 0, 1
+F32, BF16, BF16_FP8K = 0, 1, 2
+DTYPES = {"f32": F32, "bf16": BF16, "bf16_fp8k": BF16_FP8K}
 SEG_KINDS = {0: "static", 1: "dynamic", 2: "window", 3: "current", 4: "memory"}
 
 # every symbol include/bkv.h declares
@@ -117,7 +118,7 @@ def config_from_workload(w: dict) -> Config:
     c = Config()
     c.struct_size = ctypes.sizeof(Config)
     c.mode = CONVKV if w["mode"] == "convkv" else PR_SINK
-    c.dtype = BF16 if w["dtype"] == "bf16" else F32
+    c.dtype = DTYPES[w["dtype"]]
     c.layers, c.heads, c.head_dim = w["layers"], w["heads"], w["head_dim"]
     c.frames_per_block, c.grid_h, c.grid_w = w["frames"], w["grid_h"], w["grid_w"]
     c.window_blocks, c.static_blocks = w["window"], w["static"]
@@ -154,7 +155,8 @@ class Cache:
             self.device = torch.device("cuda", torch.cuda.current_device())
         c = self.config
         self.T = c.frames_per_block * c.grid_h * c.grid_w
-        self.dtype = torch.bfloat16 if c.dtype == BF16 else torch.float32
+        # Q/K/V/out are bf16 also with the FP8 key cache
+        self.dtype = torch.float32 if c.dtype == F32 else torch.bfloat16
         nbytes = workspace_size(c)
         # 256-byte alignment: torch's allocator hands out 512-byte aligned blocks
         self.workspace = torch.empty(nbytes, dtype=torch.uint8, device=self.device)

@@ -44,6 +44,8 @@ struct Layout {
   size_t off_pose, off_sel, off_tt, off_th, off_tw, off_w, total;
   bool split;                        // bf16 attention shares key tiles across workgroups
   size_t off_split, off_cnt;
+  bool kf8;                          // FP8 key cache: E4M3 K rows + tile exponents in a slot
+  size_t slot_kx_off;                // byte offset of the exponents [H][Tpad/64] inside a slot
 };
 
 bkv_status validate(const bkv_config* c) {
@@ -51,10 +53,13 @@ bkv_status validate(const bkv_config* c) {
   if (c->struct_size != sizeof(bkv_config))
     return fail(BKV_ERR_ARG, "config struct_size %u != %zu", c->struct_size, sizeof(bkv_config));
   if (c->mode != BKV_PR_SINK && c->mode != BKV_CONVKV) return fail(BKV_ERR_ARG, "bad mode %d", c->mode);
-  if (c->dtype != BKV_F32 && c->dtype != BKV_BF16) return fail(BKV_ERR_ARG, "bad dtype %d", c->dtype);
+  if (c->dtype != BKV_F32 && c->dtype != BKV_BF16 && c->dtype != BKV_BF16_FP8K)
+    return fail(BKV_ERR_ARG, "bad dtype %d", c->dtype);
   if (c->layers < 1 || c->heads < 1) return fail(BKV_ERR_ARG, "layers and heads must be >= 1");
-  if (c->dtype == BKV_BF16 && c->head_dim != 128)
+  if (c->dtype != BKV_F32 && c->head_dim != 128)
     return fail(BKV_ERR_UNSUPPORTED, "bf16 path supports head_dim 128 (got %d)", c->head_dim);
+  if (c->dtype == BKV_BF16_FP8K && c->mode != BKV_PR_SINK)
+    return fail(BKV_ERR_UNSUPPORTED, "the FP8 key cache is implemented for PR-Sink only");
   if (c->dtype == BKV_F32 && c->head_dim != 64 && c->head_dim != 128)
     return fail(BKV_ERR_UNSUPPORTED, "fp32 path supports head_dim 64 or 128 (got %d)", c->head_dim);
   if (c->frames_per_block < 1 || c->grid_h < 1 || c->grid_w < 1)
@@ -106,14 +111,22 @@ bkv::Schedule::Shape shape_of(const bkv_config* c) {
 Layout layout_of(const bkv_config* c, const bkv::Schedule& sch) {
   Layout L{};
   const size_t H = c->heads, D = c->head_dim;
-  L.esize = c->dtype == BKV_BF16 ? 2 : 4;
+  L.esize = c->dtype == BKV_F32 ? 4 : 2;
+  L.kf8 = c->dtype == BKV_BF16_FP8K;
   L.T = sch.tokens();
   L.Tpad = (int)align_up(L.T, bkv::kTokAlign);
   L.Tf = c->grid_h * c->grid_w;
   L.tf_pad = (int)align_up(L.Tf, bkv::kTokAlign);
   L.n_slots = sch.n_slots();
-  L.slot_v_off = H * L.Tpad * D * L.esize;
-  L.slot_bytes = 2 * L.slot_v_off;
+  if (L.kf8) {
+    // [E4M3 K rows H x Tpad x D][int32 exponents H x Tpad/64][bf16 V^T H x D x Tpad]
+    L.slot_kx_off = H * L.Tpad * D;
+    L.slot_v_off = align_up(L.slot_kx_off + sizeof(int) * H * (L.Tpad / bkv::kTokAlign), 256);
+    L.slot_bytes = L.slot_v_off + H * L.Tpad * D * 2;
+  } else {
+    L.slot_v_off = H * L.Tpad * D * L.esize;
+    L.slot_bytes = 2 * L.slot_v_off;
+  }
   L.layer_kv_bytes = L.slot_bytes * L.n_slots;
   size_t off = 0;
   L.off_kv = off;
@@ -146,7 +159,7 @@ Layout layout_of(const bkv_config* c, const bkv::Schedule& sch) {
   L.off_w = off;
   if (c->mode == BKV_CONVKV) off = align_up(off + sizeof(float) * 2 * c->layers * H * D * c->conv_kernel, 256);
   const long long units = (long long)H * ((L.T + bkv::kAttnBM - 1) / bkv::kAttnBM);
-  L.split = c->dtype == BKV_BF16 && units > bkv::kStreamWG;
+  L.split = c->dtype != BKV_F32 && units > bkv::kStreamWG;
   L.off_split = off;
   if (L.split) off = align_up(off + bkv::kSplitSlotBytes * 2 * (bkv::kStreamWG + 1), 256);
   L.off_cnt = off;
@@ -181,11 +194,14 @@ struct bkv_cache_s {
     weights_set.assign(c.layers, false);
   }
 
-  bool bf16() const { return cfg.dtype == BKV_BF16; }
+  bool bf16() const { return cfg.dtype != BKV_F32; }   // bf16 Q/K/V/out and V cache
+  bool kf8() const { return L.kf8; }
   bool convkv() const { return cfg.mode == BKV_CONVKV; }
   char* layer_kv(int l) const { return ws + L.off_kv + L.layer_kv_bytes * l; }
   char* slot_k(int l, int s) const { return layer_kv(l) + L.slot_bytes * s; }
   char* slot_vt(int l, int s) const { return slot_k(l, s) + L.slot_v_off; }
+  int* slot_kx(int l, int s) const { return reinterpret_cast<int*>(slot_k(l, s) + L.slot_kx_off); }
+  long long slot_kx_hs() const { return L.Tpad / bkv::kTokAlign; }
   char* ctx_k(int l) const { return ws + L.off_ctx + L.ctx_layer_bytes * l; }
   char* mem_k(int l) const { return ws + L.off_mem + L.mem_layer_bytes * l; }
   char* mem_vt(int l) const { return mem_k(l) + L.mem_v_off; }
@@ -227,6 +243,10 @@ struct bkv_cache_s {
       g.k_hs = slot_k_hs();
       g.v_hs = slot_v_hs();
       g.v_ld = L.Tpad;
+      if (kf8()) {
+        g.kx = slot_kx(l, p.slot);
+        g.kx_hs = slot_kx_hs();
+      }
     } else {
       g.k = ctx_k(l) + (size_t)p.ctx_off * cfg.head_dim * L.esize;
       g.k_hs = (long long)L.ctx_ld * cfg.head_dim;
@@ -493,7 +513,13 @@ bkv_status bkv_attend(bkv_cache h, int32_t layer, const void* q, const void* k, 
   ap.vt = h->slot_vt(layer, cur.slot);
   ap.vt_hs = h->slot_v_hs();
   ap.vt_ld = h->L.Tpad;
-  if (!h->convkv()) {
+  if (h->kf8()) {
+    ap.k8 = h->slot_k(layer, cur.slot);
+    ap.k8_hs = h->slot_k_hs();
+    ap.kx = h->slot_kx(layer, cur.slot);
+    ap.kx_hs = h->slot_kx_hs();
+    ap.t_row0 = 0;
+  } else if (!h->convkv()) {
     ap.k_rot = h->slot_k(layer, cur.slot);
     ap.k_rot_hs = h->slot_k_hs();
     ap.k_rot_off = 0;
@@ -529,6 +555,9 @@ bkv_status bkv_attend(bkv_cache h, int32_t layer, const void* q, const void* k, 
   a.slot_k_hs = h->slot_k_hs();
   a.slot_v_hs = h->slot_v_hs();
   a.slot_v_ld = h->L.Tpad;
+  a.kf8 = h->kf8() ? 1 : 0;
+  a.slot_kx_off = (long long)h->L.slot_kx_off;
+  a.slot_kx_hs = h->slot_kx_hs();
   a.split = h->L.split ? 1 : 0;
   a.part = reinterpret_cast<float*>(h->ws + h->L.off_split);
   a.cnt = reinterpret_cast<int*>(h->ws + h->L.off_cnt);
@@ -668,6 +697,9 @@ bkv_status bkv_export_segment(bkv_cache h, int32_t layer, int32_t seg, void* k_o
   a.slot_k_hs = h->slot_k_hs();
   a.slot_v_hs = h->slot_v_hs();
   a.slot_v_ld = h->L.Tpad;
+  a.kf8 = h->kf8() ? 1 : 0;
+  a.slot_kx_off = (long long)h->L.slot_kx_off;
+  a.slot_kx_hs = h->slot_kx_hs();
   a.k_out = k_out;
   a.v_out = v_out;
   a.H = h->cfg.heads;

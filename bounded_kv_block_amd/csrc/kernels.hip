@@ -5,8 +5,10 @@
 //                      (fp64, one wavefront, ties to the lower stream id), and
 //                      the current block's temporal RoPE rows
 //   append_kernel      K with fused 3D RoPE -> cache rows; V -> cache V^T
+//   append_k8_kernel   the same with K stored as E4M3 + per-tile exponents
 //   attn_bf16_kernel   flash attention on bf16 MFMA (32x32x16), K/V tiles
-//                      staged in LDS, online softmax in fp32
+//                      staged in LDS, online softmax in fp32; with an FP8
+//                      key cache Q K^T runs on scaled E4M3 MFMA (32x32x64)
 //   attn_f32_kernel    the same contraction in fp32 on the vector ALUs
 //   gather_kernel      ConvKV: raw K of memory + window -> context-K rows,
 //                      rotated at context positions
@@ -25,6 +27,7 @@ namespace {
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef int i32x8 __attribute__((ext_vector_type(8)));
 
 __device__ __forceinline__ float to_f(float x) { return x; }
 __device__ __forceinline__ float to_f(__bf16 x) { return (float)x; }
@@ -165,21 +168,58 @@ __global__ __launch_bounds__(kOpenThreads) void open_kernel(OpenArgs a) {
 }
 
 // ------------------------------------------------------------------ append
+// V^T rows of one (64-token tile, head) from the token-major V tile in LDS
+// (16-byte chunk c of row r at c ^ ((r >> 3) & 7)): each thread reads 8-byte
+// slices of TOK consecutive tokens and writes CH rows of V^T (TOK tokens of
+// one channel, 16 bytes each); consecutive lanes take consecutive token
+// groups, so each V^T row is written in contiguous runs.  Tokens past the
+// block's end are never written, so the V^T pad columns keep their zeros.
+template <typename T, int D>
+__device__ __forceinline__ void store_vt(const AppendArgs& a, const char* s_v, int tile0, int head,
+                                         int ntok) {
+  constexpr int VEC = 16 / sizeof(T);
+  constexpr int RS = D * (int)sizeof(T);
+  constexpr int CH = 8 / sizeof(T);
+  constexpr int TOK = VEC;
+  const int tid = threadIdx.x;
+  constexpr int NCG = D / CH, NTG = 64 / TOK;  // channel groups, token groups
+  for (int task = tid; task < NCG * NTG; task += 256) {
+    const int tg = task % NTG, cg = task / NTG;
+    const int t0 = tg * TOK;
+    if (t0 >= ntok) continue;
+    typedef T rowv __attribute__((ext_vector_type(TOK)));
+    typedef T slicev __attribute__((ext_vector_type(CH)));
+    rowv col[CH];
+#pragma unroll
+    for (int e = 0; e < TOK; ++e) {
+      const int t = t0 + e;
+      const slicev w = *reinterpret_cast<const slicev*>(s_v + t * RS + (((cg >> 1) ^ ((t >> 3) & 7)) << 4) + (cg & 1) * 8);
+#pragma unroll
+      for (int ch = 0; ch < CH; ++ch) col[ch][e] = w[ch];
+    }
+    const int nv = ntok - t0;
+#pragma unroll
+    for (int ch = 0; ch < CH; ++ch) {
+      T* dst = static_cast<T*>(a.vt) + head * a.vt_hs + (size_t)(cg * CH + ch) * a.vt_ld + tile0 + t0;
+      if (nv >= TOK) {
+        *reinterpret_cast<rowv*>(dst) = col[ch];
+      } else {
+#pragma unroll
+        for (int e = 0; e < TOK; ++e)
+          if (e < nv) dst[e] = col[ch][e];
+      }
+    }
+  }
+}
+
 // One workgroup per (64-token tile, head).  K: each thread moves 16-byte chunks
 // of a token's row, rotating pairs in fp32.  V: the tile goes into LDS as
-// whole 16-byte chunks (chunk c of row r at c ^ ((r >> 3) & 7)), then each
-// thread reads 8-byte slices of TOK consecutive tokens and writes CH rows of
-// V^T (TOK tokens of one channel, 16 bytes each); consecutive lanes take
-// consecutive token groups, so each V^T row is written in contiguous runs.
-// Tokens past the block's end are never written, so the V^T pad columns
-// keep their zeros.
+// whole 16-byte chunks, then to V^T (store_vt).
 template <typename T, int D>
 __global__ __launch_bounds__(256) void append_kernel(AppendArgs a) {
   constexpr int VEC = 16 / sizeof(T);          // elements per 16-byte chunk
   constexpr int CPR = D / VEC;                 // chunks per row
   constexpr int RS = D * (int)sizeof(T);       // LDS row stride (bytes)
-  constexpr int CH = 8 / sizeof(T);            // channels per 8-byte slice
-  constexpr int TOK = VEC;                     // tokens per 16-byte V^T store
   __shared__ __attribute__((aligned(16))) char s_v[64 * RS];
   const int tile0 = blockIdx.x * 64;
   const int head = blockIdx.y;
@@ -218,34 +258,82 @@ __global__ __launch_bounds__(256) void append_kernel(AppendArgs a) {
     }
   }
   __syncthreads();
-  constexpr int NCG = D / CH, NTG = 64 / TOK;  // channel groups, token groups
-  for (int task = tid; task < NCG * NTG; task += 256) {
-    const int tg = task % NTG, cg = task / NTG;
-    const int t0 = tg * TOK;
-    if (t0 >= ntok) continue;
-    typedef T rowv __attribute__((ext_vector_type(TOK)));
-    typedef T slicev __attribute__((ext_vector_type(CH)));
-    rowv col[CH];
+  store_vt<T, D>(a, s_v, tile0, head, ntok);
+}
+
+// OCP E4M3 ("fn": bias 7, 3 mantissa bits, largest finite 448).  Exponent of
+// the power-of-two scale of a group whose largest magnitude is a: the
+// smallest e with a * 2^-e <= 448 (0 for a = 0), clamped to [-120, 120], so
+// values / 2^e never overflow E4M3 and the division is exact.
+__device__ __forceinline__ int e4m3_exponent(float a) {
+  if (!(a > 0.f)) return 0;
+  int e = __builtin_amdgcn_frexp_expf(a) - 9;          // a * 2^-e in [256, 512)
+  if (__builtin_amdgcn_ldexpf(a, -e) > 448.f) ++e;
+  return min(120, max(-120, e));
+}
+
+// Four fp32 values (already divided by the scale) -> four E4M3 bytes, first
+// value in the low byte; v_cvt_pk_fp8_f32 rounds to nearest, ties to even.
+__device__ __forceinline__ int e4m3_pack4(float x0, float x1, float x2, float x3) {
+  int w = __builtin_amdgcn_cvt_pk_fp8_f32(x0, x1, 0, false);
+  return __builtin_amdgcn_cvt_pk_fp8_f32(x2, x3, w, true);
+}
+
+// FP8 key cache append (bf16 inputs, D = 128): K rotated in fp32, then stored
+// as E4M3 with one power-of-two scale per (64-token tile, head) -- the
+// tile's largest |K~| reduced over the workgroup -- and the tile exponent
+// written beside the rows.  V goes to V^T as in append_kernel.
+__global__ __launch_bounds__(256) void append_k8_kernel(AppendArgs a) {
+  constexpr int D = 128, VEC = 8, CPR = D / VEC, RS = D * 2, IT = 64 * CPR / 256;
+  __shared__ __attribute__((aligned(16))) char s_v[64 * RS];
+  __shared__ float s_max[4];
+  const int tile0 = blockIdx.x * 64;
+  const int head = blockIdx.y;
+  const int tid = threadIdx.x;
+  const int ntok = min(64, a.T - tile0);
+  const bool rope = has_rope(a.rope);
+  float kr[IT][VEC];
+  float amax = 0.f;
 #pragma unroll
-    for (int e = 0; e < TOK; ++e) {
-      const int t = t0 + e;
-      const slicev w = *reinterpret_cast<const slicev*>(s_v + t * RS + (((cg >> 1) ^ ((t >> 3) & 7)) << 4) + (cg & 1) * 8);
+  for (int it = 0; it < IT; ++it) {
+    const int task = tid + 256 * it, r = task / CPR, c = task % CPR;
 #pragma unroll
-      for (int ch = 0; ch < CH; ++ch) col[ch][e] = w[ch];
+    for (int e = 0; e < VEC; ++e) kr[it][e] = 0.f;
+    if (r >= ntok) continue;
+    const int tok = tile0 + r;
+    const size_t src = ((size_t)tok * a.H + head) * D + c * VEC;
+    const bf16x8 kraw = *reinterpret_cast<const bf16x8*>(static_cast<const __bf16*>(a.k_in) + src);
+    const uint4 vraw = *reinterpret_cast<const uint4*>(static_cast<const __bf16*>(a.v_in) + src);
+    *reinterpret_cast<uint4*>(s_v + r * RS + ((c ^ ((r >> 3) & 7)) << 4)) = vraw;
+#pragma unroll
+    for (int e = 0; e < VEC; ++e) kr[it][e] = (float)kraw[e];
+    if (rope) {
+      int f, y, x;
+      token_fyx(tok, a.rope.grid_h, a.rope.grid_w, f, y, x);
+#pragma unroll
+      for (int e = 0; e < VEC; e += 2) rope_pair(kr[it][e], kr[it][e + 1], c * VEC + e, a.rope, a.t_row0 + f, y, x);
     }
-    const int nv = ntok - t0;
 #pragma unroll
-    for (int ch = 0; ch < CH; ++ch) {
-      T* dst = static_cast<T*>(a.vt) + head * a.vt_hs + (size_t)(cg * CH + ch) * a.vt_ld + tile0 + t0;
-      if (nv >= TOK) {
-        *reinterpret_cast<rowv*>(dst) = col[ch];
-      } else {
-#pragma unroll
-        for (int e = 0; e < TOK; ++e)
-          if (e < nv) dst[e] = col[ch][e];
-      }
-    }
+    for (int e = 0; e < VEC; ++e) amax = fmaxf(amax, fabsf(kr[it][e]));
   }
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) amax = fmaxf(amax, __shfl_xor(amax, o));
+  if ((tid & 63) == 0) s_max[tid >> 6] = amax;
+  __syncthreads();
+  amax = fmaxf(fmaxf(s_max[0], s_max[1]), fmaxf(s_max[2], s_max[3]));
+  const int ex = e4m3_exponent(amax);
+  const float inv = __builtin_amdgcn_ldexpf(1.f, -ex);
+#pragma unroll
+  for (int it = 0; it < IT; ++it) {
+    const int task = tid + 256 * it, r = task / CPR, c = task % CPR;
+    if (r >= ntok) continue;
+    uint2 w;
+    w.x = (unsigned)e4m3_pack4(kr[it][0] * inv, kr[it][1] * inv, kr[it][2] * inv, kr[it][3] * inv);
+    w.y = (unsigned)e4m3_pack4(kr[it][4] * inv, kr[it][5] * inv, kr[it][6] * inv, kr[it][7] * inv);
+    *reinterpret_cast<uint2*>(static_cast<char*>(a.k8) + head * a.k8_hs + (size_t)(tile0 + r) * D + c * VEC) = w;
+  }
+  if (tid == 0) a.kx[head * a.kx_hs + blockIdx.x] = ex;
+  store_vt<__bf16, D>(a, s_v, tile0, head, ntok);
 }
 
 // ------------------------------------------------------------------ attention, bf16 MFMA
@@ -287,6 +375,7 @@ static_assert(ABM == kAttnBM, "unit rows");
 constexpr int KT_BYTES = ABN * AD * 2;
 constexpr int VT_BYTES = AD * ABN * 2;
 constexpr int STAGE_BYTES = KT_BYTES + VT_BYTES;
+constexpr int KT8_BYTES = ABN * AD;      // FP8 K tile: 64 rows x 128 bytes
 constexpr int NSTAGE = 3;
 constexpr float kSumLimit = 256.0f;     // lane partial row sum of P that forces a rescale
 constexpr int kFragAhead = 3;            // LDS reads in flight ahead of the MFMA that uses them
@@ -297,6 +386,11 @@ __device__ __forceinline__ int kswz(int r) { return (r & 7) | ((r & 16) >> 1); }
 // V^T tile: 128 rows x 8 chunks; two rows share a 256-B bank line.
 __device__ __forceinline__ int vswz(int d) { return (d >> 1) & 7; }
 __device__ __forceinline__ int kperm(int r) { return ((r >> 2) & 1) * 16 + (r >> 3) * 4 + (r & 3); }
+// FP8 K tile: 64 rows x 8 chunks of 16 B (two rows per 256-B bank line).  A
+// 16-lane phase reads one chunk from each of the rows {0-7, 16-23} (+8,
+// +32); (r & 1) picks the bank half and this swizzle the chunk position, so
+// the 16 reads cover the 64 banks once.
+__device__ __forceinline__ int k8swz(int r) { return ((r >> 1) & 3) | (((r >> 4) & 1) << 2); }
 
 __device__ __forceinline__ int xcd_remap(int bid, int nwg) {
   // Consecutive workgroup ids are dispatched round-robin over the 8 XCDs; give
@@ -363,10 +457,12 @@ struct TileCursor {
   int phase, sg, j0, n;   // n: length of segment sg (0 past the end)
 };
 
-template <bool SPLIT>
+template <bool SPLIT, bool KF8>
 __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2)))
 void attn_bf16_kernel(AttnArgs a) {
-  __shared__ __attribute__((aligned(1024))) char lds[NSTAGE * STAGE_BYTES];
+  constexpr int KTB = KF8 ? KT8_BYTES : KT_BYTES;   // K tile bytes in LDS
+  constexpr int SB = KTB + VT_BYTES;                  // stage bytes
+  __shared__ __attribute__((aligned(1024))) char lds[NSTAGE * SB];
   __shared__ const char* s_k[kMaxSeg];      // segment K / V^T of the current head
   __shared__ const char* s_v[kMaxSeg];
   __shared__ const char* s_kb[kMaxSeg];     // head 0, with per-head strides
@@ -375,6 +471,9 @@ void attn_bf16_kernel(AttnArgs a) {
   __shared__ long long s_vhs[kMaxSeg];
   __shared__ int s_n[kMaxSeg];
   __shared__ int s_ld[kMaxSeg];
+  __shared__ const int* s_x[kMaxSeg];       // FP8 K: tile exponents of the current head
+  __shared__ const int* s_xb[kMaxSeg];
+  __shared__ long long s_xhs[kMaxSeg];
   __shared__ int s_arrived;
 
   const int tid = threadIdx.x, lane = tid & 63;
@@ -405,12 +504,20 @@ void attn_bf16_kernel(AttnArgs a) {
         khs = a.slot_k_hs;
         vhs = a.slot_v_hs;
         ld = a.slot_v_ld;
+        if constexpr (KF8) {
+          s_xb[gg] = reinterpret_cast<const int*>(kb + a.slot_kx_off);
+          s_xhs[gg] = a.slot_kx_hs;
+        }
       } else {
         kb = static_cast<const char*>(sg.k);
         vb = static_cast<const char*>(sg.v);
         khs = sg.k_hs;
         vhs = sg.v_hs;
         ld = sg.v_ld;
+        if constexpr (KF8) {
+          s_xb[gg] = sg.kx;
+          s_xhs[gg] = sg.kx_hs;
+        }
       }
       s_kb[gg] = kb;
       s_vb[gg] = vb;
@@ -424,6 +531,11 @@ void attn_bf16_kernel(AttnArgs a) {
   // Q of a unit: lane holds Q~[q][16s + 8h .. +7] for s = 0..7, rotated,
   // scaled by softmax_scale*log2(e), rounded to bf16.
   bf16x8 qreg[8];
+  // FP8 K: the same Q~ as E4M3 with one power-of-two scale per query, lane
+  // holding channels 64 s2 + 32 h .. +31 (s2 = 0, 1) as 32 bytes; qsc is the
+  // query's scale as an E8M0 exponent (127 + e).
+  i32x8 qreg8[2];
+  int qsc = 127;
   __syncthreads();
 
   // ---- tile enumeration (segment metadata read as wave-uniform values)
@@ -523,6 +635,11 @@ void attn_bf16_kernel(AttnArgs a) {
     return (unsigned)((p >> 4) * 256 + (((p & 15) ^ kswz(p >> 4)) << 4));
   };
   const unsigned vk0 = k_off(0), vk1 = k_off(1);
+  // FP8 K (64 rows of 128 B): chunk p = (4i + w)*64 + lane of a tile holds row
+  // p >> 3 = 32i + 8w + (lane >> 3), chunk (p & 7) ^ k8swz(row); that swizzle
+  // does not depend on i, so one register serves both loads (+4096 i).
+  const unsigned vk8 = (unsigned)(gw * 1024 + (lane >> 3) * 128 +
+                                  (((lane & 7) ^ (((lane >> 4) & 3) | (((gw >> 1) & 1) << 2))) << 4));
   unsigned vv = 0;
   auto issue_setup = [&](const TileCursor& c, int stage) {
     if (c.sg != cur_sg) {
@@ -533,7 +650,7 @@ void attn_bf16_kernel(AttnArgs a) {
       const int p = gw * 64 + lane;
       vv = (unsigned)((p >> 3) * cur_ld * 2 + (((p & 7) ^ vswz(p >> 3)) << 4));
     }
-    ld_kt = __builtin_amdgcn_readfirstlane(lds0 + stage * STAGE_BYTES + gw * 1024);
+    ld_kt = __builtin_amdgcn_readfirstlane(lds0 + stage * SB + gw * 1024);
     ld_j0 = __builtin_amdgcn_readfirstlane((unsigned)c.j0);
   };
   auto uni4 = [](i32x4 r) {
@@ -542,20 +659,29 @@ void attn_bf16_kernel(AttnArgs a) {
     for (int e = 0; e < 4; ++e) u[e] = (int)__builtin_amdgcn_readfirstlane((unsigned)r[e]);
     return u;
   };
-  auto issue_chunk = [&](int k) {          // k = 0..3: K, 4..7: V
-    const int i = k & 3;
+  // bf16 K: k = 0..3 K chunks, 4..7 V chunks.  FP8 K: 0..1 K, 2..5 V, 6..7 none.
+  constexpr int NCHUNK = KF8 ? 6 : 8;
+  auto issue_chunk = [&](int k) {
     const unsigned j0 = __builtin_amdgcn_readfirstlane(ld_j0);
     const unsigned kt = __builtin_amdgcn_readfirstlane(ld_kt);
     const unsigned ld = __builtin_amdgcn_readfirstlane((unsigned)cur_ld);
-    if (k < 4)
-      dma16(uni4(krs), (i & 1) ? vk1 : vk0, j0 * 256u + (unsigned)(i >> 1) * 8192u, kt + i * 4096);
-    else
-      dma16(uni4(vrs), vv, j0 * 2u + (unsigned)i * 64u * ld, kt + KT_BYTES + i * 4096);
+    if constexpr (KF8) {
+      if (k < 2)
+        dma16(uni4(krs), vk8, j0 * 128u + (unsigned)k * 4096u, kt + k * 4096);
+      else if (k < 6)
+        dma16(uni4(vrs), vv, j0 * 2u + (unsigned)(k - 2) * 64u * ld, kt + KTB + (k - 2) * 4096);
+    } else {
+      const int i = k & 3;
+      if (k < 4)
+        dma16(uni4(krs), (i & 1) ? vk1 : vk0, j0 * 256u + (unsigned)(i >> 1) * 8192u, kt + i * 4096);
+      else
+        dma16(uni4(vrs), vv, j0 * 2u + (unsigned)i * 64u * ld, kt + KTB + i * 4096);
+    }
   };
   auto issue = [&](const TileCursor& c, int stage) {   // by one group of four waves
     issue_setup(c, stage);
 #pragma unroll
-    for (int k = 0; k < 8; ++k) issue_chunk(k);
+    for (int k = 0; k < NCHUNK; ++k) issue_chunk(k);
   };
 
   // ---- per-wave state
@@ -568,6 +694,7 @@ void attn_bf16_kernel(AttnArgs a) {
   f32x16 negm = f32x16{};
   f32x16 sacc[2];
   bf16x8 pb[2][2];
+  i32x8 kf[4];                             // FP8 K fragments of the S product
 
   // MFMA block: PV of one tile (16 MFMA, V^T fragments) then, optionally, S of
   // the next (16 MFMA, K fragments).  Fragments rotate through 4 registers
@@ -628,6 +755,84 @@ void attn_bf16_kernel(AttnArgs a) {
       sacc[0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(k0, qreg[st], st ? sacc[0] : f32x16{}, 0, 0, 0);
       sacc[1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(k1, qreg[st], st ? sacc[1] : f32x16{}, 0, 0, 0);
     }
+  };
+  // FP8 K: S^T = K Q^T as 4 scaled MFMAs (32x32x64, E4M3 x E4M3) per tile.
+  // Fragment j = 2 s2 + blk: A = 32 keys (MFMA row r = tile row kperm(r) +
+  // 32 blk) x channels 64 s2 .. +63, lane (col, h) holding channels
+  // 64 s2 + 32 h .. +31 of its row (two 16-byte chunks); B = qreg8[s2].  The
+  // A scale is the tile's exponent (uniform), the B scale the query's, so
+  // the product is the dequantised one.  Row and lane layout of the result
+  // are those of the bf16 product.
+  auto k8_frag = [&](const char* kt, int j) -> i32x8 {
+    const int r = 32 * (j & 1) + kperm(col);
+    const int p = (4 * (j >> 1) + 2 * hh) ^ k8swz(r);
+    const i32x4 lo = *reinterpret_cast<const i32x4*>(kt + r * 128 + (p << 4));
+    const i32x4 hi = *reinterpret_cast<const i32x4*>(kt + r * 128 + ((p ^ 1) << 4));
+    return __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
+  };
+  auto s8_step = [&](int j, int sa, const f32x16& c0) {
+    const int blk = j & 1, s2 = j >> 1;
+    sacc[blk] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(kf[j], qreg8[s2], s2 ? sacc[blk] : c0,
+                                                               0, 0, 0, sa, 0, qsc);
+  };
+  // first tile (no PV yet); sa = 127 + the tile's exponent
+  auto s_only8 = [&](const char* kt, int sa) {
+#pragma unroll
+    for (int j = 0; j < 4; ++j) kf[j] = k8_frag(kt, j);
+#pragma unroll
+    for (int j = 0; j < 4; ++j) s8_step(j, sa, f32x16{});
+  };
+  // MFMA block of the FP8 path: PV (16 MFMA, V^T fragments 3 ahead as in
+  // m_block) then S (4 scaled MFMA).  K fragment 0 comes with m_prefetch8;
+  // the other six K reads follow the PV reads, one per PV MFMA and two per
+  // scaled MFMA (which takes twice as long), so the LDS reads stay spread.
+  auto m_prefetch8 = [&](const char* vt, const char* kt) {
+#pragma unroll
+    for (int i = 0; i < AHEAD; ++i) fr[i] = pv_frag(vt, i);
+    kf[0] = k8_frag(kt, 0);
+  };
+  auto m_block8 = [&](const char* vt, const char* kt, int sa) {
+    static_assert(AHEAD == 3, "read slots below assume 3 reads ahead");
+    const int r1 = 32 + kperm(col), r2 = kperm(col), r3 = 32 + kperm(col);
+    const int p1 = (2 * hh) ^ k8swz(r1), p2 = (4 + 2 * hh) ^ k8swz(r2), p3 = (4 + 2 * hh) ^ k8swz(r3);
+    i32x4 h1a, h1b, h2a, h2b, h3a, h3b;
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+      if (i + AHEAD < 16) fr[(i + AHEAD) % (AHEAD + 1)] = pv_frag(vt, i + AHEAD);
+      if (i == 13) h1a = *reinterpret_cast<const i32x4*>(kt + r1 * 128 + (p1 << 4));
+      if (i == 14) h1b = *reinterpret_cast<const i32x4*>(kt + r1 * 128 + ((p1 ^ 1) << 4));
+      if (i == 15) h2a = *reinterpret_cast<const i32x4*>(kt + r2 * 128 + (p2 << 4));
+      const int mb = i >> 3, part = (i >> 2) & 1, db = i & 3;
+      o[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fr[i % (AHEAD + 1)], pb[mb][part], o[db], 0, 0, 0);
+    }
+    h2b = *reinterpret_cast<const i32x4*>(kt + r2 * 128 + ((p2 ^ 1) << 4));
+    h3a = *reinterpret_cast<const i32x4*>(kt + r3 * 128 + (p3 << 4));
+    s8_step(0, sa, negm);
+    kf[1] = __builtin_shufflevector(h1a, h1b, 0, 1, 2, 3, 4, 5, 6, 7);
+    h3b = *reinterpret_cast<const i32x4*>(kt + r3 * 128 + ((p3 ^ 1) << 4));
+    s8_step(1, sa, negm);
+    kf[2] = __builtin_shufflevector(h2a, h2b, 0, 1, 2, 3, 4, 5, 6, 7);
+    s8_step(2, sa, negm);
+    kf[3] = __builtin_shufflevector(h3a, h3b, 0, 1, 2, 3, 4, 5, 6, 7);
+    s8_step(3, sa, negm);
+    // instruction order: (read, MFMA) pairs over the PV part, then
+    // (2 reads, MFMA), (read, MFMA), MFMA, MFMA
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+      __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+    }
+    __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
+    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+    __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+    __builtin_amdgcn_sched_group_barrier(0x008, 3, 0);
+  };
+  // E8M0 A scale (127 + exponent) of the FP8 K tile at cursor c, read through
+  // the scalar cache: the exponents were written by an earlier launch.
+  auto tile_scale = [&](const TileCursor& c) -> int {
+    typedef const __attribute__((address_space(4))) int* const_int_ptr;
+    const char* xp = uniform_ptr(s_x[c.sg]);
+    return 127 + reinterpret_cast<const_int_ptr>(reinterpret_cast<uintptr_t>(xp))[c.j0 >> 6];
   };
   auto mask_tail = [&](int nvalid) {
     if (nvalid < ABN) {
@@ -733,10 +938,50 @@ void attn_bf16_kernel(AttnArgs a) {
 
     __syncthreads();                       // the previous piece is done with LDS
     if (tid < nseg) {
-      s_k[tid] = s_kb[tid] + 2 * head * s_khs[tid];
+      s_k[tid] = s_kb[tid] + (KF8 ? 1 : 2) * head * s_khs[tid];
       s_v[tid] = s_vb[tid] + 2 * head * s_vhs[tid];
+      if constexpr (KF8) s_x[tid] = s_xb[tid] + head * s_xhs[tid];
     }
-    {   // Q of the unit
+    if constexpr (KF8) {   // Q of the unit as E4M3, one scale per query
+      int f = 0, y = 0, x = 0;
+      const bool valid = qrow < a.T;
+      if (valid) token_fyx(qrow, a.rope.grid_h, a.rope.grid_w, f, y, x);
+      const bool rope = has_rope(a.rope);
+      const __bf16* qp = static_cast<const __bf16*>(a.q) + ((size_t)(valid ? qrow : 0) * a.H + head) * AD;
+      float u[2][32];
+      float mx = 0.f;
+#pragma unroll
+      for (int s2 = 0; s2 < 2; ++s2)
+#pragma unroll
+        for (int c4 = 0; c4 < 4; ++c4) {
+          const int d0 = 64 * s2 + 32 * hh + 8 * c4;
+          const bf16x8 raw = valid ? *reinterpret_cast<const bf16x8*>(qp + d0) : bf16x8{};
+          float* w = &u[s2][8 * c4];
+#pragma unroll
+          for (int e = 0; e < 8; ++e) w[e] = (float)raw[e];
+          if (rope && valid) {
+#pragma unroll
+            for (int e = 0; e < 8; e += 2) rope_pair(w[e], w[e + 1], d0 + e, a.rope, a.t_row0 + f, y, x);
+          }
+#pragma unroll
+          for (int e = 0; e < 8; ++e) {
+            w[e] *= a.qscale;
+            mx = fmaxf(mx, fabsf(w[e]));
+          }
+        }
+      // the query's other 64 channels sit in lane l ^ 32
+      const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(mx), __float_as_uint(mx), false, false);
+      mx = fmaxf(__uint_as_float(sw[0]), __uint_as_float(sw[1]));
+      const int eq = e4m3_exponent(mx);
+      const float inv = __builtin_amdgcn_ldexpf(1.f, -eq);
+      qsc = 127 + eq;
+#pragma unroll
+      for (int s2 = 0; s2 < 2; ++s2)
+#pragma unroll
+        for (int w = 0; w < 8; ++w)
+          qreg8[s2][w] = e4m3_pack4(u[s2][4 * w] * inv, u[s2][4 * w + 1] * inv, u[s2][4 * w + 2] * inv,
+                                    u[s2][4 * w + 3] * inv);
+    } else {   // Q of the unit
       int f = 0, y = 0, x = 0;
       const bool valid = qrow < a.T;
       if (valid) token_fyx(qrow, a.rope.grid_h, a.rope.grid_w, f, y, x);
@@ -782,7 +1027,8 @@ void attn_bf16_kernel(AttnArgs a) {
       if (NP > 0) {
         if (group == 1) wg_barrier();          // group B runs half a tile behind
         // M(0) = S(0)
-        s_only(lds + stage_of(0) * STAGE_BYTES);
+        if constexpr (KF8) s_only8(lds + stage_of(0) * SB, tile_scale(xc));
+        else s_only(lds + stage_of(0) * SB);
         wg_barrier();
         // Full periods: X(t) then M(t+1) = [PV(t), S(t+1)].  The first period
         // (exact max), the last loading period and the last tile are peeled, and
@@ -801,13 +1047,27 @@ void attn_bf16_kernel(AttnArgs a) {
               __builtin_amdgcn_sched_barrier(0);
             }
           };
-          if constexpr (decltype(first)::value) softmax_first(xc.n - xc.j0, hook);
-          else softmax(xc.n - xc.j0, hook);
-          advance(xc);
-          m_prefetch(lds + stage_of(t) * STAGE_BYTES + KT_BYTES);
-          wg_barrier();
-          m_block(lds + stage_of(t) * STAGE_BYTES + KT_BYTES, lds + stage_of(t + 1) * STAGE_BYTES,
-                  std::true_type{});
+          if constexpr (KF8) {
+            // the next tile's scale is read before the softmax, so its
+            // scalar load has returned by the MFMA block
+            const int nvalid = xc.n - xc.j0;
+            advance(xc);
+            const int sa = tile_scale(xc);
+            if constexpr (decltype(first)::value) softmax_first(nvalid, hook);
+            else softmax(nvalid, hook);
+            asm volatile("" ::"s"(sa));
+            m_prefetch8(lds + stage_of(t) * SB + KTB, lds + stage_of(t + 1) * SB);
+            wg_barrier();
+            m_block8(lds + stage_of(t) * SB + KTB, lds + stage_of(t + 1) * SB, sa);
+          } else {
+            if constexpr (decltype(first)::value) softmax_first(xc.n - xc.j0, hook);
+            else softmax(xc.n - xc.j0, hook);
+            advance(xc);
+            m_prefetch(lds + stage_of(t) * SB + KTB);
+            wg_barrier();
+            m_block(lds + stage_of(t) * SB + KTB, lds + stage_of(t + 1) * SB,
+                    std::true_type{});
+          }
           asm volatile("s_waitcnt vmcnt(0)" ::: "memory");   // tile t+2 (group B's loads) has landed
           wg_barrier();
         };
@@ -827,9 +1087,9 @@ void attn_bf16_kernel(AttnArgs a) {
         } else {
           softmax_first(xc.n - xc.j0, no_hook);
         }
-        m_prefetch(lds + stage_of(NP - 1) * STAGE_BYTES + KT_BYTES);
+        m_prefetch(lds + stage_of(NP - 1) * SB + KTB);
         wg_barrier();
-        m_block(lds + stage_of(NP - 1) * STAGE_BYTES + KT_BYTES, nullptr, std::false_type{});
+        m_block(lds + stage_of(NP - 1) * SB + KTB, nullptr, std::false_type{});
         wg_barrier();
         if (group == 0) wg_barrier();          // match group B's extra leading barrier
       }
@@ -1142,10 +1402,20 @@ __global__ void export_kernel(ExportArgs a) {
     vhs = a.seg.v_hs;
     ld = a.seg.v_ld;
   }
-  const T* k = reinterpret_cast<const T*>(kb) + h * khs + (size_t)tok * a.D + d;
   const T* v = reinterpret_cast<const T*>(vb) + h * vhs + (size_t)d * ld + tok;
-  static_cast<T*>(a.k_out)[gid] = *k;
   static_cast<T*>(a.v_out)[gid] = *v;
+  if constexpr (std::is_same<T, __bf16>::value) {
+    if (a.kf8) {   // E4M3 byte times 2^(tile exponent): exact in bf16
+      const int* xb = a.seg.dyn >= 0 ? reinterpret_cast<const int*>(kb + a.slot_kx_off) : a.seg.kx;
+      const long long xhs = a.seg.dyn >= 0 ? a.slot_kx_hs : a.seg.kx_hs;
+      const int byte = reinterpret_cast<const unsigned char*>(kb)[h * khs + (size_t)tok * a.D + d];
+      const float kv = __builtin_amdgcn_ldexpf(__builtin_amdgcn_cvt_f32_fp8(byte, 0), xb[h * xhs + tok / 64]);
+      static_cast<T*>(a.k_out)[gid] = (T)kv;
+      return;
+    }
+  }
+  const T* k = reinterpret_cast<const T*>(kb) + h * khs + (size_t)tok * a.D + d;
+  static_cast<T*>(a.k_out)[gid] = *k;
 }
 
 }  // namespace
@@ -1167,7 +1437,10 @@ hipError_t launch_open(const OpenArgs& a, hipStream_t s) {
 
 hipError_t launch_append(const AppendArgs& a, bool bf16, hipStream_t s) {
   dim3 grid((a.T + 63) / 64, a.H);
-  if (bf16) {
+  if (a.k8) {
+    if (!bf16 || a.D != 128) return hipErrorInvalidValue;
+    append_k8_kernel<<<grid, 256, 0, s>>>(a);
+  } else if (bf16) {
     if (a.D != 128) return hipErrorInvalidValue;
     append_kernel<__bf16, 128><<<grid, 256, 0, s>>>(a);
   } else if (a.D == 64) {
@@ -1187,8 +1460,14 @@ hipError_t launch_attention(const AttnArgs& a, bool bf16, hipStream_t s) {
     // 15% of kStreamWG workgroup slots idle; then the workgroups share the
     // key tiles (needs the split slots of the workspace).
     const int units = ((a.T + ABM - 1) / ABM) * a.H;
-    if (attention_split(a.T, a.H, a.split != 0)) attn_bf16_kernel<true><<<kStreamWG, 64 * AWAVES, 0, s>>>(a);
-    else attn_bf16_kernel<false><<<units, 64 * AWAVES, 0, s>>>(a);
+    const bool split = attention_split(a.T, a.H, a.split != 0);
+    if (a.kf8) {
+      if (split) attn_bf16_kernel<true, true><<<kStreamWG, 64 * AWAVES, 0, s>>>(a);
+      else attn_bf16_kernel<false, true><<<units, 64 * AWAVES, 0, s>>>(a);
+    } else {
+      if (split) attn_bf16_kernel<true, false><<<kStreamWG, 64 * AWAVES, 0, s>>>(a);
+      else attn_bf16_kernel<false, false><<<units, 64 * AWAVES, 0, s>>>(a);
+    }
   } else if (a.D == 64) {
     const int nwg = ((a.T + 127) / 128) * a.H;
     attn_f32_kernel<64><<<nwg, 128, 0, s>>>(a);

@@ -5,6 +5,8 @@
 //   V^T      [H][D][ld]  -- values stored transposed, so the P.V MFMA reads
 //                           8 consecutive keys of one channel as one 16-byte word
 // ld (the token stride) is a multiple of 64, so tile loads never leave a row.
+// FP8 key cache: K rows hold E4M3 bytes, and an int32 power-of-two exponent
+// per (head, 64-token tile) sits at kx [H][ld/64]; V^T stays bf16.
 #pragma once
 #include <hip/hip_runtime.h>
 #include <stdint.h>
@@ -42,7 +44,8 @@ struct Rope {                   // 3D RoPE tables: (cos, sin) fp32 pairs, built 
 struct Seg {
   const void* k;
   const void* v;
-  long long k_hs, v_hs;
+  const int* kx;            // FP8 key cache: tile exponents, head h at kx + h*kx_hs
+  long long k_hs, v_hs, kx_hs;
   int v_ld, n, dyn, pad_;
 };
 
@@ -59,7 +62,9 @@ struct AttnArgs {
   long long slot_bytes;
   long long slot_v_off;     // byte offset of V^T inside a slot
   long long slot_k_hs, slot_v_hs;
+  long long slot_kx_off, slot_kx_hs;   // FP8 key cache: exponents inside a slot
   int slot_v_ld;
+  int kf8;                  // 1: K is E4M3 with tile exponents (bf16 path only)
   int split;                // 1: kStreamWG workgroups share the units' key tiles
   float* part;              // split slots: 2 per share boundary, kSplitSlotBytes each
   int* cnt;                 // arrival counter per share boundary (0 between launches)
@@ -73,6 +78,8 @@ struct AppendArgs {
   void* k_rot; long long k_rot_hs; int k_rot_off;   // rotated K rows [H][..][D] at row offset (or null)
   void* k_raw; long long k_raw_hs;                  // raw K rows (ConvKV slot) or null
   void* vt; long long vt_hs; int vt_ld;             // V^T destination
+  void* k8; long long k8_hs;                        // FP8 key cache: E4M3 K rows (or null)
+  int* kx; long long kx_hs;                         //   and their tile exponents
   int T, H, D;
   int t_row0;
   Rope rope;
@@ -122,6 +129,7 @@ struct ExportArgs {
   Seg seg;
   const int* sel_slots;
   const char* slot_base; long long slot_bytes, slot_v_off, slot_k_hs, slot_v_hs; int slot_v_ld;
+  long long slot_kx_off, slot_kx_hs; int kf8;   // FP8 key cache: K exported dequantised
   void* k_out; void* v_out;
   int H, D;
 };

@@ -39,6 +39,8 @@ WORKLOADS = {
     # 512x512-shaped bf16 PR-Sink: 40 x 128, 3 frames of 32x32 = 3072 queries,
     # 7-block context = 21504 keys, top-2 over 128-d poses, bank of 56.
     "prsink_512": dict(_BASE),
+    # the same with the FP8 key cache (K as E4M3 with per-tile scales)
+    "prsink_512_fp8k": dict(_BASE, dtype="bf16_fp8k"),
     # 720x416-shaped bf16: 3 frames of 26x45 = 3510 queries, 40 layers x 3 steps,
     # commit after the third step, bank of 16.
     "prsink_720x416": dict(_BASE, grid_h=26, grid_w=45, layers=40, steps=3, bank=16, seed=3),
@@ -83,7 +85,7 @@ def qkv(cfg: dict, layer: int, block: int, step: int = 0):
     out = []
     for tid in (TENSOR_Q, TENSOR_K, TENSOR_V):
         x = _rng(cfg, layer, block, step, tid).standard_normal(shape, dtype=np.float32)
-        out.append(round_to_bf16(x) if cfg["dtype"] == "bf16" else x)
+        out.append(x if cfg["dtype"] == "f32" else round_to_bf16(x))
     return tuple(out)
 
 
@@ -192,7 +194,7 @@ def qkv_device(cfg: dict, layer: int, block: int, step: int = 0, device="cuda"):
     """
     import torch
     shape = (tokens_per_block(cfg), cfg["heads"], cfg["head_dim"])
-    dt = torch.bfloat16 if cfg["dtype"] == "bf16" else torch.float32
+    dt = torch.float32 if cfg["dtype"] == "f32" else torch.bfloat16
     out = []
     for tid in (TENSOR_Q, TENSOR_K, TENSOR_V):
         g = torch.Generator(device=device)

@@ -62,7 +62,18 @@ typedef enum {
 } bkv_status;
 
 typedef enum { BKV_PR_SINK = 0, BKV_CONVKV = 1 } bkv_mode;
-typedef enum { BKV_F32 = 0, BKV_BF16 = 1 } bkv_dtype;
+/* BKV_BF16_FP8K: bf16 Q/K/V/out and V cache, with an FP8 key cache (PR-Sink
+   only, head_dim 128).  The SoulX-LiveAct page (sections 关键信息速览 and
+   上手实践) runs attention in FP8 without fixing a scheme; this library reads
+   it as: K after RoPE is stored as OCP E4M3 (bias 7, largest finite 448,
+   round to nearest even) with one power-of-two scale 2^e per (head, 64-token
+   tile of a block), e the smallest integer with max|K~| * 2^-e <= 448 (0 for
+   an all-zero tile), clamped to [-120, 120]; Q after RoPE, times
+   softmax_scale * log2(e), is quantised the same way with one scale per
+   (token, head); the logits Q K^T are formed from these E4M3 values (the
+   products are exact, accumulated in fp32); softmax and P V are as for
+   BKV_BF16.  Cache bytes per token and head: 128 (K) + 256 (V) + 4/64. */
+typedef enum { BKV_F32 = 0, BKV_BF16 = 1, BKV_BF16_FP8K = 2 } bkv_dtype;
 
 typedef enum {
   BKV_SEG_STATIC = 0,   /* static sink block */
@@ -79,7 +90,7 @@ typedef struct {
   int32_t dtype;            /* bkv_dtype of Q/K/V/out and of the cache */
   int32_t layers;           /* >= 1; each layer has its own cache */
   int32_t heads;            /* >= 1 */
-  int32_t head_dim;         /* 64 or 128 (bf16 path: 128) */
+  int32_t head_dim;         /* 64 or 128 (bf16 and FP8-key paths: 128) */
   int32_t frames_per_block; /* latent frames per block, >= 1 */
   int32_t grid_h, grid_w;   /* latent grid; tokens per block T = frames*grid_h*grid_w */
   int32_t window_blocks;    /* rolling window length, >= 1 (3 on the pages) */
@@ -191,7 +202,8 @@ bkv_status bkv_stats(bkv_cache h, bkv_stats_t* out);
 
 /* Inspection: copy context segment `seg` of the open block at `layer` as
    attention reads it -- K rotated, V as stored -- into device k_out, v_out
-   [tokens][heads][head_dim] in the cache dtype.  For the current segment this
+   [tokens][heads][head_dim] in the cache dtype (BKV_BF16_FP8K: bf16, K as
+   its dequantised E4M3 value code * 2^e, which bf16 holds exactly).  For the current segment this
    needs an earlier bkv_attend of `layer` in this block.
    Errors: BKV_ERR_STATE (no open block / current block not yet written). */
 bkv_status bkv_export_segment(bkv_cache h, int32_t layer, int32_t seg, void* k_out, void* v_out,

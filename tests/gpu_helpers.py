@@ -6,7 +6,7 @@ import numpy as np
 
 from bounded_kv_block_amd import bkv, synth
 
-TOL = {"f32": 1e-5, "bf16": 2e-2}
+TOL = {"f32": 1e-5, "bf16": 2e-2, "bf16_fp8k": 2e-2}
 
 
 class Run:
@@ -28,7 +28,7 @@ class Run:
         self._dev = {}
         self._host = {}
         self._w = {}
-        self.dt = torch.bfloat16 if cfg["dtype"] == "bf16" else torch.float32
+        self.dt = torch.float32 if cfg["dtype"] == "f32" else torch.bfloat16
         if cfg["mode"] == "convkv":
             for l in range(cfg["layers"]):
                 wk, wv = synth.conv_weights(cfg, l)

@@ -215,6 +215,29 @@ def test_workspace_size_and_validation():
     assert bkv.lib().bkv_status_str(bkv.BKV_ERR_STATE) == b"BKV_ERR_STATE"
 
 
+def test_fp8_key_cache_workspace_and_validation():
+    """FP8 key cache: a slot holds E4M3 K (1 byte per value), one int32
+    exponent per (head, 64-token tile) and the bf16 V^T; PR-Sink and
+    head_dim 128 only."""
+    from bounded_kv_block_amd import bkv, synth
+    n16 = bkv.workspace_size(bkv.config_from_workload(synth.workload("prsink_512")))
+    n8 = bkv.workspace_size(bkv.config_from_workload(synth.workload("prsink_512_fp8k")))
+    H, Tp, D = 40, 3072, 128
+    kx = -(-(4 * H * Tp // 64) // 256) * 256          # exponents, 256-byte aligned
+    slot8 = H * Tp * D + kx + H * Tp * D * 2
+    slot16 = 2 * H * Tp * D * 2
+    assert n16 - n8 == 61 * (slot16 - slot8)            # same 61 slots, same tables and split slots
+    for b in (dict(head_dim=64), dict(mode="convkv", static=0, dynamic_k=0, bank=0, pose_dim=0)):
+        with pytest.raises(bkv.BkvError) as ei:
+            bkv.workspace_size(bkv.config_from_workload(synth.workload("prsink_512_fp8k", **b)))
+        assert ei.value.status == bkv.BKV_ERR_UNSUPPORTED, b
+    c = bkv.config_from_workload(synth.workload("prsink_512"))
+    c.dtype = 3
+    with pytest.raises(bkv.BkvError) as ei:
+        bkv.workspace_size(c)
+    assert ei.value.status == bkv.BKV_ERR_ARG
+
+
 def test_workspace_is_constant_in_stream_length():
     """Cache bytes do not depend on how long the stream runs: no config field
     names a stream length, and the 1080-block workload needs the same bytes as
