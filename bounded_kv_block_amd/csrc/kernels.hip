@@ -374,7 +374,6 @@ constexpr int ABM = 256, ABN = 64, AD = 128, AWAVES = 8;
 static_assert(ABM == kAttnBM, "unit rows");
 constexpr int KT_BYTES = ABN * AD * 2;
 constexpr int VT_BYTES = AD * ABN * 2;
-constexpr int STAGE_BYTES = KT_BYTES + VT_BYTES;
 constexpr int KT8_BYTES = ABN * AD;      // FP8 K tile: 64 rows x 128 bytes
 constexpr int NSTAGE = 3;
 constexpr float kSumLimit = 256.0f;     // lane partial row sum of P that forces a rescale
@@ -613,7 +612,7 @@ void attn_bf16_kernel(AttnArgs a) {
   // key-tile parts (part p = tiles [NT p / rP, NT (p+1) / rP))
   const int rR = SPLIT ? a.H * nqt / kStreamWG : 0;
   const int rU = SPLIT ? a.H * nqt - rR * kStreamWG : 0;
-  const int rP = SPLIT && rU > 0 ? min(NT, max(1, kStreamWG / rU)) : 1;
+  const int rP = SPLIT && rU > 0 ? min(NT, max(1, kStreamWG / max(rU, 1))) : 1;
 
   // ---- tile loads: chunk p = (4i + w)*64 + lane of a tile lands at LDS p*16
   // (w = wave within the loading group of four); the tile's first key enters
@@ -783,49 +782,54 @@ void attn_bf16_kernel(AttnArgs a) {
     for (int j = 0; j < 4; ++j) s8_step(j, sa, f32x16{});
   };
   // MFMA block of the FP8 path: PV (16 MFMA, V^T fragments 3 ahead as in
-  // m_block) then S (4 scaled MFMA).  K fragment 0 comes with m_prefetch8;
-  // the other six K reads follow the PV reads, one per PV MFMA and two per
-  // scaled MFMA (which takes twice as long), so the LDS reads stay spread.
-  auto m_prefetch8 = [&](const char* vt, const char* kt) {
-#pragma unroll
-    for (int i = 0; i < AHEAD; ++i) fr[i] = pv_frag(vt, i);
-    kf[0] = k8_frag(kt, 0);
-  };
+  // m_block) then S (4 scaled MFMA).  The K tile is read only inside the
+  // block: it is published by the barrier that opens the block (the loading
+  // group waits for its chunks before that barrier), unlike the V^T tile,
+  // which m_prefetch may read earlier.  The eight K chunk reads follow the
+  // PV reads from step 10 on (two reads at steps 10-12, two more with the
+  // first scaled MFMA, which takes twice as long as a PV MFMA).
   auto m_block8 = [&](const char* vt, const char* kt, int sa) {
     static_assert(AHEAD == 3, "read slots below assume 3 reads ahead");
-    const int r1 = 32 + kperm(col), r2 = kperm(col), r3 = 32 + kperm(col);
-    const int p1 = (2 * hh) ^ k8swz(r1), p2 = (4 + 2 * hh) ^ k8swz(r2), p3 = (4 + 2 * hh) ^ k8swz(r3);
-    i32x4 h1a, h1b, h2a, h2b, h3a, h3b;
+    i32x4 h[8];                          // chunk 2j + half of fragment j
+    auto k8_half = [&](int c) {
+      const int j = c >> 1, r = 32 * (j & 1) + kperm(col);
+      const int p = ((4 * (j >> 1) + 2 * hh) ^ k8swz(r)) ^ (c & 1);
+      return *reinterpret_cast<const i32x4*>(kt + r * 128 + (p << 4));
+    };
 #pragma unroll
     for (int i = 0; i < 16; ++i) {
       if (i + AHEAD < 16) fr[(i + AHEAD) % (AHEAD + 1)] = pv_frag(vt, i + AHEAD);
-      if (i == 13) h1a = *reinterpret_cast<const i32x4*>(kt + r1 * 128 + (p1 << 4));
-      if (i == 14) h1b = *reinterpret_cast<const i32x4*>(kt + r1 * 128 + ((p1 ^ 1) << 4));
-      if (i == 15) h2a = *reinterpret_cast<const i32x4*>(kt + r2 * 128 + (p2 << 4));
+      if (i >= 10) h[i - 10] = k8_half(i - 10);
       const int mb = i >> 3, part = (i >> 2) & 1, db = i & 3;
       o[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fr[i % (AHEAD + 1)], pb[mb][part], o[db], 0, 0, 0);
     }
-    h2b = *reinterpret_cast<const i32x4*>(kt + r2 * 128 + ((p2 ^ 1) << 4));
-    h3a = *reinterpret_cast<const i32x4*>(kt + r3 * 128 + (p3 << 4));
-    s8_step(0, sa, negm);
-    kf[1] = __builtin_shufflevector(h1a, h1b, 0, 1, 2, 3, 4, 5, 6, 7);
-    h3b = *reinterpret_cast<const i32x4*>(kt + r3 * 128 + ((p3 ^ 1) << 4));
-    s8_step(1, sa, negm);
-    kf[2] = __builtin_shufflevector(h2a, h2b, 0, 1, 2, 3, 4, 5, 6, 7);
-    s8_step(2, sa, negm);
-    kf[3] = __builtin_shufflevector(h3a, h3b, 0, 1, 2, 3, 4, 5, 6, 7);
-    s8_step(3, sa, negm);
-    // instruction order: (read, MFMA) pairs over the PV part, then
-    // (2 reads, MFMA), (read, MFMA), MFMA, MFMA
 #pragma unroll
-    for (int i = 0; i < 16; ++i) {
+    for (int j = 0; j < 3; ++j) kf[j] = __builtin_shufflevector(h[2 * j], h[2 * j + 1], 0, 1, 2, 3, 4, 5, 6, 7);
+    h[6] = k8_half(6);
+    h[7] = k8_half(7);
+    kf[3] = __builtin_shufflevector(h[6], h[7], 0, 1, 2, 3, 4, 5, 6, 7);
+#pragma unroll
+    for (int j = 0; j < 4; ++j) s8_step(j, sa, negm);
+    // instruction order: (read, MFMA) pairs up to step 9, (2 reads, MFMA)
+    // for steps 10-12, (read, MFMA) for 13-15, then (2 reads, MFMA) and the
+    // last three MFMAs
+#pragma unroll
+    for (int i = 0; i < 10; ++i) {
+      __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+    }
+#pragma unroll
+    for (int i = 10; i < 13; ++i) {
+      __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+    }
+#pragma unroll
+    for (int i = 13; i < 16; ++i) {
       __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
       __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
     }
     __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
-    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-    __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
-    __builtin_amdgcn_sched_group_barrier(0x008, 3, 0);
+    __builtin_amdgcn_sched_group_barrier(0x008, 4, 0);
   };
   // E8M0 A scale (127 + exponent) of the FP8 K tile at cursor c, read through
   // the scalar cache: the exponents were written by an earlier launch.
@@ -1056,7 +1060,7 @@ void attn_bf16_kernel(AttnArgs a) {
             if constexpr (decltype(first)::value) softmax_first(nvalid, hook);
             else softmax(nvalid, hook);
             asm volatile("" ::"s"(sa));
-            m_prefetch8(lds + stage_of(t) * SB + KTB, lds + stage_of(t + 1) * SB);
+            m_prefetch(lds + stage_of(t) * SB + KTB);
             wg_barrier();
             m_block8(lds + stage_of(t) * SB + KTB, lds + stage_of(t + 1) * SB, sa);
           } else {
