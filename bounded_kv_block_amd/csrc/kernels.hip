@@ -454,6 +454,8 @@ __device__ __forceinline__ void dma16(i32x4 rsrc, unsigned voff, unsigned soff, 
 // key order.  All fields are wave-uniform.
 struct TileCursor {
   int phase, sg, j0, n;   // n: length of segment sg (0 past the end)
+  int lim;                // n in phase 0, else 0: the next tile is j0 + 64 of the
+                          // same segment when j0 + 128 <= lim (the common case)
 };
 
 template <bool SPLIT, bool KF8>
@@ -552,7 +554,7 @@ void attn_bf16_kernel(AttnArgs a) {
   // cursor at tile k of the enumeration (full tiles of each segment in
   // order, then the partial tails)
   auto cursor_find = [&](int k) {
-    TileCursor c{0, nseg, 0, 0};
+    TileCursor c{0, nseg, 0, 0, 0};
     for (int g = 0; g < nseg; ++g) {
       const int f = seg_n(g) / ABN;
       if (k < f) {
@@ -585,26 +587,45 @@ void attn_bf16_kernel(AttnArgs a) {
     c.sg = __builtin_amdgcn_readfirstlane(c.sg);
     c.j0 = __builtin_amdgcn_readfirstlane(c.j0);
     c.n = __builtin_amdgcn_readfirstlane(c.n);
+    c.lim = (c.phase == 0 && c.sg < nseg) ? c.n : 0;
     return c;
   };
-  // Common case (next full tile of the same segment) touches no LDS.
-  auto advance = [&](TileCursor& c) {
-    if (c.sg >= nseg) return;
-    if (c.phase == 0) {
-      c.j0 += ABN;
-      if (c.j0 + ABN <= c.n) return;
-      c.sg = first_full(c.sg + 1);
-      c.j0 = 0;
-      if (c.sg >= nseg) {
-        c.phase = 1;
-        c.sg = first_tail(0);
+  // The next tile of a cursor.  The common case (the next full tile of the
+  // same segment) is one compare that falls through; segment changes take
+  // the out-of-line path.
+  auto advance_slow = [&](TileCursor& c) {
+    if (c.sg < nseg) {
+      if (c.phase == 0) {
+        c.j0 += ABN;
+        if (c.j0 + ABN > c.n) {
+          c.sg = first_full(c.sg + 1);
+          c.j0 = 0;
+          if (c.sg >= nseg) {
+            c.phase = 1;
+            c.sg = first_tail(0);
+          }
+          if (c.sg < nseg) {               // else past the unit's last tile (load cursor only)
+            c.n = seg_n(c.sg);
+            c.j0 = c.phase == 1 ? c.n & ~(ABN - 1) : 0;
+          }
+        }
+      } else {
+        c.sg = first_tail(c.sg + 1);
+        if (c.sg < nseg) {
+          c.n = seg_n(c.sg);
+          c.j0 = c.n & ~(ABN - 1);
+        }
       }
-    } else {
-      c.sg = first_tail(c.sg + 1);
     }
-    if (c.sg >= nseg) return;              // past the unit's last tile (load cursor only)
-    c.n = seg_n(c.sg);
-    c.j0 = c.phase == 1 ? c.n & ~(ABN - 1) : 0;
+    c.lim = (c.phase == 0 && c.sg < nseg) ? c.n : 0;
+  };
+  auto advance = [&](TileCursor& c) {
+    const int nj = c.j0 + ABN;
+    if (__builtin_expect(nj + ABN <= c.lim, 1)) {
+      c.j0 = nj;
+      return;
+    }
+    advance_slow(c);
   };
   int NT = 0;
   for (int g = 0; g < nseg; ++g) NT += (seg_n(g) + ABN - 1) / ABN;
@@ -833,10 +854,17 @@ void attn_bf16_kernel(AttnArgs a) {
   };
   // E8M0 A scale (127 + exponent) of the FP8 K tile at cursor c, read through
   // the scalar cache: the exponents were written by an earlier launch.
+  // The segment's exponent pointer is re-read from LDS only when the segment
+  // changes (x_sg is reset with each piece's table).
+  int x_sg = -1;
+  const char* x_ptr = nullptr;
   auto tile_scale = [&](const TileCursor& c) -> int {
     typedef const __attribute__((address_space(4))) int* const_int_ptr;
-    const char* xp = uniform_ptr(s_x[c.sg]);
-    return 127 + reinterpret_cast<const_int_ptr>(reinterpret_cast<uintptr_t>(xp))[c.j0 >> 6];
+    if (__builtin_expect(c.sg != x_sg, 0)) {
+      x_sg = c.sg;
+      x_ptr = uniform_ptr(s_x[c.sg]);
+    }
+    return 127 + reinterpret_cast<const_int_ptr>(reinterpret_cast<uintptr_t>(x_ptr))[c.j0 >> 6];
   };
   auto mask_tail = [&](int nvalid) {
     if (nvalid < ABN) {
@@ -1008,6 +1036,7 @@ void attn_bf16_kernel(AttnArgs a) {
     }
     __syncthreads();
     cur_sg = -1;
+    x_sg = -1;
 #pragma unroll
     for (int i = 0; i < 4; ++i) o[i] = f32x16{};
     m_run = 0.f;
