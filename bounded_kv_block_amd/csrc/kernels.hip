@@ -1071,13 +1071,7 @@ void attn_bf16_kernel(AttnArgs a) {
         // load: 0 = none, 1 = group B loads tile t+2
         auto period = [&](int t, auto first, auto load) {
           constexpr int LOAD = decltype(load)::value;
-          if (LOAD == 1) {
-            issue_setup(lc, stage_of(t + 2));
-            // The four loading waves leave the barrier together; staggering
-            // them by ~20 cycles each keeps their chunk loads (16 cycles of
-            // the CU's address unit per 1 KB) from queueing behind each other.
-            for (int d = 0; d < gw; ++d) asm volatile("s_nop 15");
-          }
+          if (LOAD == 1) issue_setup(lc, stage_of(t + 2));
           advance(lc);
           auto hook = [&](int k) {
             if constexpr (LOAD == 1) {
