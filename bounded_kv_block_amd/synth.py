@@ -22,13 +22,14 @@ from __future__ import annotations
 import copy
 import numpy as np
 
-TENSOR_Q, TENSOR_K, TENSOR_V, TENSOR_POSE, TENSOR_KEYFRAMES, TENSOR_CONV, TENSOR_SCHED = range(7)
+(TENSOR_Q, TENSOR_K, TENSOR_V, TENSOR_POSE, TENSOR_KEYFRAMES, TENSOR_CONV, TENSOR_SCHED, TENSOR_HIDDEN,
+ TENSOR_WQKV, TENSOR_BQKV) = range(10)
 
 # Workload shapes.  Keys mirror the C-ABI config struct field names.
 _BASE = dict(mode="pr_sink", dtype="bf16", layers=1, steps=1, heads=40, head_dim=128,
              frames=3, grid_h=32, grid_w=32, window=3, static=1, dynamic_k=2, bank=56,
              pose_dim=128, rope=(44, 42, 42), theta=10000.0, conv_kernel=5, conv_stride=5,
-             memory_frames=1, blocks=60, seed=2, pose_kind="walk", keyframes=16)
+             memory_frames=1, blocks=60, seed=2, pose_kind="walk", keyframes=16, model_dim=5120)
 
 WORKLOADS = {
     # tiny fp32 stream: 2 heads x 64, 2 frames of 8x8, top-1 over 32-d poses,
@@ -41,6 +42,9 @@ WORKLOADS = {
     "prsink_512": dict(_BASE),
     # the same with the FP8 key cache (K as E4M3 with per-tile scales)
     "prsink_512_fp8k": dict(_BASE, dtype="bf16_fp8k"),
+    # the same driven from hidden states: q, k, v projected in the fused path
+    # from x [3072, 5120] (40 heads x 128 = 5120, a 14B-class DiT's width)
+    "prsink_512_qkv": dict(_BASE, qkv=True),
     # 720x416-shaped bf16: 3 frames of 26x45 = 3510 queries, 40 layers x 3 steps,
     # commit after the third step, bank of 16.
     "prsink_720x416": dict(_BASE, grid_h=26, grid_w=45, layers=40, steps=3, bank=16, seed=3),
@@ -201,3 +205,42 @@ def qkv_device(cfg: dict, layer: int, block: int, step: int = 0, device="cuda"):
         g.manual_seed(_torch_seed(cfg, layer, block, step, tid))
         out.append(torch.randn(shape, generator=g, device=device, dtype=torch.float32).to(dt))
     return tuple(out)
+
+
+# ---- hidden states and QKV projection weights (fused-projection path) -------
+def hidden(cfg: dict, layer: int, block: int, step: int = 0) -> np.ndarray:
+    """Hidden states x [T, model_dim] fp32 holding bf16 values, N(0, 1)."""
+    shape = (tokens_per_block(cfg), cfg["model_dim"])
+    return round_to_bf16(_rng(cfg, layer, block, step, TENSOR_HIDDEN).standard_normal(shape, dtype=np.float32))
+
+
+def qkv_weights(cfg: dict, layer: int):
+    """W [3*H*D, model_dim] ~ N(0, 1/model_dim) and bias [3*H*D] ~ N(0, 0.01),
+    both fp32 holding bf16 values (so q, k, v come out about N(0, 1))."""
+    n = 3 * cfg["heads"] * cfg["head_dim"]
+    C = cfg["model_dim"]
+    w = _rng(cfg, layer, 0, 0, TENSOR_WQKV).standard_normal((n, C), dtype=np.float32) / np.float32(np.sqrt(C))
+    b = _rng(cfg, layer, 0, 0, TENSOR_BQKV).standard_normal(n, dtype=np.float32) * np.float32(0.1)
+    return round_to_bf16(w), round_to_bf16(b)
+
+
+def hidden_device(cfg: dict, layer: int, block: int, step: int = 0, device="cuda"):
+    """hidden() drawn on the device with torch's seeded generator (bf16)."""
+    import torch
+    g = torch.Generator(device=device)
+    g.manual_seed(_torch_seed(cfg, layer, block, step, TENSOR_HIDDEN))
+    shape = (tokens_per_block(cfg), cfg["model_dim"])
+    return torch.randn(shape, generator=g, device=device, dtype=torch.float32).to(torch.bfloat16)
+
+
+def qkv_weights_device(cfg: dict, layer: int, device="cuda"):
+    """qkv_weights() drawn on the device with torch's seeded generator (bf16)."""
+    import torch
+    n = 3 * cfg["heads"] * cfg["head_dim"]
+    C = cfg["model_dim"]
+    g = torch.Generator(device=device)
+    g.manual_seed(_torch_seed(cfg, layer, 0, 0, TENSOR_WQKV))
+    w = torch.randn((n, C), generator=g, device=device, dtype=torch.float32) / float(np.sqrt(C))
+    g.manual_seed(_torch_seed(cfg, layer, 0, 0, TENSOR_BQKV))
+    b = torch.randn(n, generator=g, device=device, dtype=torch.float32) * 0.1
+    return w.to(torch.bfloat16), b.to(torch.bfloat16)

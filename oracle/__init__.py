@@ -20,7 +20,8 @@ Sources (pages, by title and section):
     ConvKV Memory bullet (exact recent KV, older history compressed by a 1D
     conv up to 5:1 into fixed-length memory, RoPE positions reset); sections
     关键信息速览 and 上手实践 (FP8 attention in deployment; the E4M3 key cache
-    scheme in ``fp8`` is this package's reading).
+    scheme in ``fp8`` is this package's reading; the fused-QKV build, read in
+    ``projection`` as the plain linear projection of the hidden states).
 
 Where the pages leave a step open, the reading taken is stated in the
 function that implements it.  Every function is pinned by a CPU test against
@@ -33,9 +34,11 @@ from .rope import rope_frequencies, apply_rope
 from .attention import attention, masked_attention, softmax_weights
 from .convkv import conv_memory
 from .stream import PRSinkReference, ConvKVReference
+from .projection import qkv_projection
 from . import fp8
 
 __all__ = [
+    "qkv_projection",
     "prsink_schedule", "simulate_prsink", "convkv_schedule", "simulate_convkv",
     "token_positions", "retrieve", "exact_keys", "fp64_cosines", "boundary_gap",
     "rope_frequencies", "apply_rope", "attention", "masked_attention", "softmax_weights",

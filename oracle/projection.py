@@ -1,0 +1,31 @@
+"""QKV projection of a block's hidden states, fp64 (test infrastructure).
+
+The LiveAnimate page (section 方法) reaches its frame rate with operator
+fusion, and the SoulX-LiveAct page (section 上手实践) offers a fused-QKV build;
+neither writes the operation out.  Reading taken here: an attention layer's q,
+k and v are the plain linear projection of the block's hidden states,
+
+    [q | k | v] = x W^T + b,
+
+with x [T, C], W [3*heads*head_dim, C] whose rows are the q heads' features,
+then the k heads', then the v heads' (head-major, a head's head_dim rows
+together), and an optional bias b [3*heads*head_dim].  A fused path must
+equal the unfused path fed with these q, k and v.
+"""
+from __future__ import annotations
+
+import numpy as np
+
+
+def qkv_projection(x, w, b, heads: int, head_dim: int):
+    """q, k, v, each [T, heads, head_dim] fp64."""
+    x = np.asarray(x, np.float64)
+    w = np.asarray(w, np.float64)
+    n = heads * head_dim
+    if w.shape != (3 * n, x.shape[1]):
+        raise ValueError(f"w has shape {w.shape}, expected {(3 * n, x.shape[1])}")
+    y = x @ w.T                                        # a library matmul, one step
+    if b is not None:
+        y = y + np.asarray(b, np.float64)[None, :]
+    T = x.shape[0]
+    return tuple(y[:, i * n:(i + 1) * n].reshape(T, heads, head_dim) for i in range(3))

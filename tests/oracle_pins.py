@@ -295,3 +295,39 @@ def check_fp8_groups(quantize_keys, quantize_queries, rng):
     q4 = q3.copy()
     q4[2] *= 1e4
     assert np.array_equal(np.delete(quantize_queries(q4), 2, axis=0), np.delete(quantize_queries(q3), 2, axis=0))
+
+
+# ---------------------------------------------------------------- QKV projection
+def check_projection_brute_force(qkv_projection, rng):
+    """Every output element against an explicit sum over the hidden channels
+    on a tiny case (loops, not a matmul)."""
+    T, C, H, D = 3, 5, 2, 4
+    x, w, b = rng.normal(size=(T, C)), rng.normal(size=(3 * H * D, C)), rng.normal(size=3 * H * D)
+    q, k, v = qkv_projection(x, w, b, H, D)
+    for which, out in enumerate((q, k, v)):
+        for t in range(T):
+            for h in range(H):
+                for d in range(D):
+                    o = which * H * D + h * D + d
+                    want = b[o]
+                    for c in range(C):
+                        want += x[t, c] * w[o, c]
+                    assert abs(out[t, h, d] - want) <= 1e-12 * (1 + abs(want)), (which, t, h, d)
+
+
+def check_projection_layout(qkv_projection):
+    """A one-hot hidden state picks one column of W: row o = which*H*D + h*D + d
+    of W lands in q/k/v[which][., h, d]; a zero state returns the bias."""
+    C, H, D = 6, 3, 4
+    w = np.arange(3 * H * D * C, dtype=np.float64).reshape(3 * H * D, C)
+    for c in range(C):
+        x = np.zeros((1, C))
+        x[0, c] = 1.0
+        q, k, v = qkv_projection(x, w, None, H, D)
+        for which, out in enumerate((q, k, v)):
+            for h in range(H):
+                for d in range(D):
+                    assert out[0, h, d] == w[which * H * D + h * D + d, c], (c, which, h, d)
+    b = np.arange(3 * H * D, dtype=np.float64) + 0.5
+    q, k, v = qkv_projection(np.zeros((2, C)), w, b, H, D)
+    assert np.array_equal(np.concatenate([a.reshape(2, -1) for a in (q, k, v)], axis=1), np.tile(b, (2, 1)))

@@ -233,3 +233,11 @@ def test_pow2_scale_exponent(rng):
 
 def test_fp8_group_scales(rng):
     pins.check_fp8_groups(oracle.fp8.quantize_keys, oracle.fp8.quantize_queries, rng)
+
+
+def test_projection_brute_force(rng):
+    pins.check_projection_brute_force(oracle.qkv_projection, rng)
+
+
+def test_projection_layout():
+    pins.check_projection_layout(oracle.qkv_projection)

@@ -237,3 +237,23 @@ def _keys_per_head(k):                  # one scale per head over the whole bloc
 @pytest.mark.parametrize("mutant", [_keys_per_head])
 def test_fp8_group_mutants_fail(mutant, rng):
     assert _fails(pins.check_fp8_groups, mutant, oracle.fp8.quantize_queries, rng)
+
+
+def _proj_kv_swapped(x, w, b, H, D):
+    q, k, v = oracle.qkv_projection(x, w, b, H, D)
+    return q, v, k
+
+
+def _proj_dim_major(x, w, b, H, D):     # rows read as (d, h) instead of (h, d)
+    q, k, v = oracle.qkv_projection(x, w, b, H, D)
+    T = q.shape[0]
+    return tuple(a.reshape(T, D, H).transpose(0, 2, 1) for a in (q, k, v))
+
+
+def _proj_no_bias(x, w, b, H, D):
+    return oracle.qkv_projection(x, w, None, H, D)
+
+
+@pytest.mark.parametrize("mutant", [_proj_kv_swapped, _proj_dim_major, _proj_no_bias])
+def test_projection_mutants_fail(mutant, rng):
+    assert _fails(pins.check_projection_brute_force, mutant, rng) or _fails(pins.check_projection_layout, mutant)
