@@ -22,7 +22,7 @@ SEG_KINDS = {0: "static", 1: "dynamic", 2: "window", 3: "current", 4: "memory"}
 # every symbol include/bkv.h declares
 EXPORTS = ("bkv_workspace_size", "bkv_create", "bkv_destroy", "bkv_reset", "bkv_set_conv_weights",
            "bkv_profile_start", "bkv_profile_stop",
-           "bkv_retrieve", "bkv_attend", "bkv_commit", "bkv_selection", "bkv_context", "bkv_stats",
+           "bkv_retrieve", "bkv_attend", "bkv_attend_qkv", "bkv_commit", "bkv_selection", "bkv_context", "bkv_stats",
            "bkv_export_segment", "bkv_status_str", "bkv_last_error")
 
 
@@ -81,6 +81,7 @@ def lib() -> ctypes.CDLL:
             "bkv_set_conv_weights": [vp, i32, vp, vp, vp],
             "bkv_retrieve": [vp, vp, vp],
             "bkv_attend": [vp, i32, vp, vp, vp, vp, vp],
+            "bkv_attend_qkv": [vp, i32, vp, vp, vp, i32, vp, vp],
             "bkv_commit": [vp, vp],
             "bkv_selection": [vp, ctypes.POINTER(i32), i32, ctypes.POINTER(i32), vp],
             "bkv_context": [vp, ctypes.POINTER(Segment), i32, ctypes.POINTER(i32), vp],
@@ -209,6 +210,24 @@ class Cache:
         _check(lib().bkv_attend(self._h, layer, self._tensor(q, "q", shp, self.dtype),
                                 self._tensor(k, "k", shp, self.dtype), self._tensor(v, "v", shp, self.dtype),
                                 self._tensor(out, "out", shp, self.dtype), self._s()), "bkv_attend")
+        return out
+
+    def attend_qkv(self, layer: int, x, w, b=None, out=None):
+        """Fused projection + attention: q|k|v = x w^T + b inside the library.
+        x [T, model_dim], w [3*H*D, model_dim], b [3*H*D] or None, all bf16."""
+        c = self.config
+        bf = self._torch.bfloat16
+        if not isinstance(x, self._torch.Tensor) or x.dim() != 2:
+            raise ValueError("x must be a 2-D tensor [T, model_dim]")
+        C = int(x.shape[1])
+        n = 3 * c.heads * c.head_dim
+        shp = self.qkv_shape
+        if out is None:
+            out = self._torch.empty(shp, dtype=self.dtype, device=self.device)
+        bp = None if b is None else self._tensor(b, "b", (n,), bf)
+        _check(lib().bkv_attend_qkv(self._h, layer, self._tensor(x, "x", (self.T, C), bf),
+                                    self._tensor(w, "w", (n, C), bf), bp, C,
+                                    self._tensor(out, "out", shp, self.dtype), self._s()), "bkv_attend_qkv")
         return out
 
     def commit(self):

@@ -46,6 +46,7 @@ struct Layout {
   size_t off_split, off_cnt;
   bool kf8;                          // FP8 key cache: E4M3 K rows + tile exponents in a slot
   size_t slot_kx_off;                // byte offset of the exponents [H][Tpad/64] inside a slot
+  size_t off_q;                      // bf16: q scratch [T][H][D] of the fused projection path
 };
 
 bkv_status validate(const bkv_config* c) {
@@ -164,6 +165,8 @@ Layout layout_of(const bkv_config* c, const bkv::Schedule& sch) {
   if (L.split) off = align_up(off + bkv::kSplitSlotBytes * 2 * (bkv::kStreamWG + 1), 256);
   L.off_cnt = off;
   if (L.split) off = align_up(off + sizeof(int) * (bkv::kStreamWG + 1), 256);
+  L.off_q = off;
+  if (c->dtype == BKV_BF16) off = align_up(off + (size_t)L.T * H * D * 2, 256);
   L.total = off;
   return L;
 }
@@ -278,8 +281,9 @@ bkv_status check_handle(bkv_cache h, bool need_ok = true) {
   return BKV_OK;
 }
 
-enum { K_RETRIEVE = 0, K_APPEND, K_ATTENTION, K_GATHER, K_CONV, K_EXPORT, K_COUNT };
-const char* const kKernelNames[K_COUNT] = {"retrieve", "append", "attention", "gather", "conv", "export"};
+enum { K_RETRIEVE = 0, K_APPEND, K_ATTENTION, K_GATHER, K_CONV, K_EXPORT, K_QKV, K_COUNT };
+const char* const kKernelNames[K_COUNT] = {"retrieve", "append", "attention", "gather", "conv", "export",
+                                           "qkv"};
 
 // Run `launch`, bracketed by event records on `s` while a profile is recording.
 template <class F>
@@ -490,22 +494,16 @@ bkv_status bkv_retrieve(bkv_cache h, const float* pose, hipStream_t stream) {
   return BKV_OK;
 }
 
-bkv_status bkv_attend(bkv_cache h, int32_t layer, const void* q, const void* k, const void* v,
-                      void* out, hipStream_t stream) {
-  bkv_status st = check_handle(h);
-  if (st != BKV_OK) return st;
-  if (!h->sched.is_open()) return fail(BKV_ERR_STATE, "attend with no open block");
-  if (layer < 0 || layer >= h->cfg.layers) return fail(BKV_ERR_ARG, "layer %d out of range", layer);
-  if (!q || !k || !v || !out) return fail(BKV_ERR_ARG, "null q/k/v/out");
-  if (out == q || out == k || out == v) return fail(BKV_ERR_ARG, "out aliases an input");
-  if ((st = set_device(h)) != BKV_OK) return st;
-  const auto& segs = h->sched.segments();
-  const bkv::SegPlan& cur = segs.back();
-  const int D = h->cfg.head_dim;
+}  // extern "C"
 
+namespace {
+
+// Destinations of the current block's K and V at `layer` (append kernel or
+// the fused projection's epilogue).
+bkv::AppendArgs append_args(bkv_cache h, int layer) {
+  const auto& cur = h->sched.segments().back();
+  const int D = h->cfg.head_dim;
   bkv::AppendArgs ap{};
-  ap.k_in = k;
-  ap.v_in = v;
   ap.T = h->L.T;
   ap.H = h->cfg.heads;
   ap.D = D;
@@ -532,12 +530,19 @@ bkv_status bkv_attend(bkv_cache h, int32_t layer, const void* q, const void* k, 
     ap.k_rot_off = cur.ctx_off;
     ap.t_row0 = (int)cur.t0;
   }
-  hipError_t e = timed(h, K_APPEND, stream, [&] { return bkv::launch_append(ap, h->bf16(), stream); });
-  if (e != hipSuccess) return device_fail(h, e, "append launch");
+  return ap;
+}
+
+// After the current block's K/V are in the cache: ConvKV context gather (once
+// per layer and block), then attention of q over the context into out.
+bkv_status attend_context(bkv_cache h, int layer, const void* q, void* out, hipStream_t stream) {
+  bkv_status st;
   if (h->convkv() && !h->ctx_ready[layer]) {
     if ((st = gather_context(h, layer, stream)) != BKV_OK) return st;
   }
-
+  const auto& segs = h->sched.segments();
+  const auto& cur = segs.back();
+  const int D = h->cfg.head_dim;
   bkv::AttnArgs a{};
   a.q = q;
   a.out = out;
@@ -563,11 +568,64 @@ bkv_status bkv_attend(bkv_cache h, int32_t layer, const void* q, const void* k, 
   a.cnt = reinterpret_cast<int*>(h->ws + h->L.off_cnt);
   a.nseg = (int)segs.size();
   for (int i = 0; i < a.nseg; ++i) a.seg[i] = h->seg_arg(layer, segs[i]);
-  e = timed(h, K_ATTENTION, stream, [&] { return bkv::launch_attention(a, h->bf16(), stream); });
+  hipError_t e = timed(h, K_ATTENTION, stream, [&] { return bkv::launch_attention(a, h->bf16(), stream); });
   if (e != hipSuccess) return device_fail(h, e, "attention launch");
   if (h->bf16() && bkv::attention_split(a.T, a.H, a.split != 0)) ++h->split_attends;
   h->sched.mark_attended(layer);
   return BKV_OK;
+}
+
+// handle, open block and layer checks shared by the attend calls
+bkv_status attend_checks(bkv_cache h, int32_t layer) {
+  bkv_status st = check_handle(h);
+  if (st != BKV_OK) return st;
+  if (!h->sched.is_open()) return fail(BKV_ERR_STATE, "attend with no open block");
+  if (layer < 0 || layer >= h->cfg.layers) return fail(BKV_ERR_ARG, "layer %d out of range", layer);
+  return BKV_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+bkv_status bkv_attend(bkv_cache h, int32_t layer, const void* q, const void* k, const void* v,
+                      void* out, hipStream_t stream) {
+  bkv_status st = attend_checks(h, layer);
+  if (st != BKV_OK) return st;
+  if (!q || !k || !v || !out) return fail(BKV_ERR_ARG, "null q/k/v/out");
+  if (out == q || out == k || out == v) return fail(BKV_ERR_ARG, "out aliases an input");
+  if ((st = set_device(h)) != BKV_OK) return st;
+  bkv::AppendArgs ap = append_args(h, layer);
+  ap.k_in = k;
+  ap.v_in = v;
+  hipError_t e = timed(h, K_APPEND, stream, [&] { return bkv::launch_append(ap, h->bf16(), stream); });
+  if (e != hipSuccess) return device_fail(h, e, "append launch");
+  return attend_context(h, layer, q, out, stream);
+}
+
+bkv_status bkv_attend_qkv(bkv_cache h, int32_t layer, const void* x, const void* w, const void* b,
+                          int32_t model_dim, void* out, hipStream_t stream) {
+  bkv_status st = attend_checks(h, layer);
+  if (st != BKV_OK) return st;
+  if (h->cfg.dtype != BKV_BF16)
+    return fail(BKV_ERR_UNSUPPORTED, "the fused QKV projection is implemented for the bf16 cache dtype");
+  if (!x || !w || !out) return fail(BKV_ERR_ARG, "null x, w or out");
+  if (out == x || out == w || out == b) return fail(BKV_ERR_ARG, "out aliases an input");
+  if (model_dim <= 0 || model_dim % 32 != 0) return fail(BKV_ERR_ARG, "model_dim must be a positive multiple of 32");
+  const long long rows = 3LL * h->cfg.heads * h->cfg.head_dim;
+  if ((long long)h->L.T * model_dim * 2 >= (1LL << 31) || rows * model_dim * 2 >= (1LL << 31))
+    return fail(BKV_ERR_UNSUPPORTED, "x or w exceeds 2 GiB");
+  if ((st = set_device(h)) != BKV_OK) return st;
+  bkv::QkvArgs g{};
+  g.x = x;
+  g.w = w;
+  g.b = b;
+  g.C = model_dim;
+  g.q = h->ws + h->L.off_q;
+  g.ap = append_args(h, layer);
+  hipError_t e = timed(h, K_QKV, stream, [&] { return bkv::launch_qkv(g, stream); });
+  if (e != hipSuccess) return device_fail(h, e, "qkv projection launch");
+  return attend_context(h, layer, g.q, out, stream);
 }
 
 bkv_status bkv_commit(bkv_cache h, hipStream_t stream) {

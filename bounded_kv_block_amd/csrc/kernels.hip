@@ -6,6 +6,8 @@
 //                      the current block's temporal RoPE rows
 //   append_kernel      K with fused 3D RoPE -> cache rows; V -> cache V^T
 //   append_k8_kernel   the same with K stored as E4M3 + per-tile exponents
+//   qkv_gemm_kernel    fused QKV projection (bf16 MFMA) with the append's
+//                      epilogue: q to scratch, K rotated into the cache, V^T
 //   attn_bf16_kernel   flash attention on bf16 MFMA (32x32x16), K/V tiles
 //                      staged in LDS, online softmax in fp32; with an FP8
 //                      key cache Q K^T runs on scaled E4M3 MFMA (32x32x64)
@@ -1407,6 +1409,154 @@ __global__ __launch_bounds__(256) void conv_kernel(ConvArgs a) {
   }
 }
 
+// ------------------------------------------------------------------ QKV projection
+// out^T = W x^T on v_mfma_f32_32x32x16_bf16: A = 32 rows of W (features) x 16
+// channels, B = x^T, 16 channels x 32 tokens, so a lane's accumulator holds
+// groups of 4 consecutive features of one token (MFMA rows 8g + 4h .. +3 for
+// lane half h) and RoPE's channel pairs never cross lanes.
+//
+// Workgroup: 256 features x 256 tokens, 8 waves as 2 x 4 (128 features x 64
+// tokens each: 4 x 2 blocks of 32 x 32), 32 channels per step.  Both operand
+// tiles are rows of 32 channels (64 B) in LDS, chunk c of row r at
+// c ^ ((r >> 2) & 3): the 16 rows a 16-lane phase reads (same chunk index)
+// then cover the 64 banks once.  Tiles move with buffer_load ... lds, four
+// stages deep, issued three steps ahead; one barrier per step publishes
+// step s and retires the reads of step s-1 before its buffer is refilled.
+// Rows past the last token or feature are loaded clamped to the last valid
+// row and never stored.
+constexpr int GF = 256, GT = 256, GK = 32, GSTAGE = 4;
+constexpr int G_OPB = GF * GK * 2;          // bytes of one operand tile per step (16 KB)
+static_assert(GF == GT, "both operand tiles share the load mapping");
+
+__global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2)))
+void qkv_gemm_kernel(QkvArgs a) {
+  __shared__ __attribute__((aligned(1024))) char lds[GSTAGE * 2 * G_OPB];
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int wf = wave >> 2, wt = wave & 3;
+  const int hh = lane >> 5, col = lane & 31;
+  const int H = a.ap.H, T = a.ap.T, C = a.C;
+  const int HD = H * AD, NF = 3 * HD;
+  const int ntb = (T + GT - 1) / GT;
+  const int u = __builtin_amdgcn_readfirstlane(xcd_remap(blockIdx.x, gridDim.x));
+  const int fb = u / ntb, tb = u - fb * ntb;
+  const int f0 = fb * GF, t0 = tb * GT;
+
+  // loads: chunk p = (8i + wave)*64 + lane of an operand tile (i = 0, 1) lands
+  // at LDS p*16 = row 128i + 16 wave + (lane >> 2), position lane & 3, which
+  // holds the row's chunk (lane & 3) ^ ((lane >> 4) & 3)
+  const int rl = 16 * wave + (lane >> 2);
+  const unsigned cpos = (unsigned)(((lane & 3) ^ ((lane >> 4) & 3)) << 4);
+  unsigned vw[2], vx[2];
+#pragma unroll
+  for (int i = 0; i < 2; ++i) {
+    vw[i] = (unsigned)min(f0 + 128 * i + rl, NF - 1) * (unsigned)C * 2u + cpos;
+    vx[i] = (unsigned)min(t0 + 128 * i + rl, T - 1) * (unsigned)C * 2u + cpos;
+  }
+  const i32x4 rw = buffer_rsrc(uniform_ptr(a.w)), rx = buffer_rsrc(uniform_ptr(a.x));
+  const unsigned lds0 = (unsigned)(uintptr_t)(lds_ptr_t)lds;
+  const int S = C / GK;
+  auto issue = [&](int s) {
+    const unsigned base = __builtin_amdgcn_readfirstlane(lds0 + (unsigned)(s & (GSTAGE - 1)) * 2 * G_OPB);
+    const unsigned soff = __builtin_amdgcn_readfirstlane((unsigned)s * GK * 2u);
+#pragma unroll
+    for (int i = 0; i < 2; ++i) dma16(rw, vw[i], soff, base + (8 * i + wave) * 1024);
+#pragma unroll
+    for (int i = 0; i < 2; ++i) dma16(rx, vx[i], soff, base + G_OPB + (8 * i + wave) * 1024);
+  };
+  auto frag = [&](const char* tile, int row, int c) {
+    return *reinterpret_cast<const bf16x8*>(tile + row * 64 + ((c ^ ((row >> 2) & 3)) << 4));
+  };
+
+  f32x16 acc[4][2];
+#pragma unroll
+  for (int bm = 0; bm < 4; ++bm)
+#pragma unroll
+    for (int bn = 0; bn < 2; ++bn) acc[bm][bn] = f32x16{};
+
+  issue(0);
+  if (S > 1) issue(1);
+  if (S > 2) issue(2);
+  for (int s = 0; s < S; ++s) {
+    // this wave's chunks of step s have landed (later steps still in flight)
+    if (s + 2 < S) asm volatile("s_waitcnt vmcnt(8)" ::: "memory");
+    else if (s + 1 < S) asm volatile("s_waitcnt vmcnt(4)" ::: "memory");
+    else asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    wg_barrier();
+    if (s + 3 < S) issue(s + 3);
+    const char* A = lds + (s & (GSTAGE - 1)) * 2 * G_OPB;
+    const char* B = A + G_OPB;
+#pragma unroll
+    for (int ss = 0; ss < 2; ++ss) {
+      bf16x8 af[4], bx[2];
+#pragma unroll
+      for (int bm = 0; bm < 4; ++bm) af[bm] = frag(A, 128 * wf + 32 * bm + col, 2 * ss + hh);
+#pragma unroll
+      for (int bn = 0; bn < 2; ++bn) bx[bn] = frag(B, 64 * wt + 32 * bn + col, 2 * ss + hh);
+#pragma unroll
+      for (int bm = 0; bm < 4; ++bm)
+#pragma unroll
+        for (int bn = 0; bn < 2; ++bn)
+          acc[bm][bn] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[bm], bx[bn], acc[bm][bn], 0, 0, 0);
+    }
+  }
+
+  // epilogue: + bias; q -> scratch [T][H][D]; k -> (raw copy,) RoPE -> cache
+  // rows; v -> V^T.  A 32-feature block lies in one head of one of q, k, v.
+  const AppendArgs& ap = a.ap;
+  const bool rope = has_rope(ap.rope);
+  const __bf16* bias = static_cast<const __bf16*>(a.b);
+#pragma unroll
+  for (int bn = 0; bn < 2; ++bn) {
+    const int t = t0 + 64 * wt + 32 * bn + col;
+    if (t >= T) continue;
+    int fy = 0, yy = 0, xx = 0;
+    if (rope) token_fyx(t, ap.rope.grid_h, ap.rope.grid_w, fy, yy, xx);
+#pragma unroll
+    for (int bm = 0; bm < 4; ++bm) {
+      const int fbase = f0 + 128 * wf + 32 * bm;
+      if (fbase >= NF) continue;
+      const int which = fbase / HD, head = (fbase - which * HD) / AD, db = fbase % AD;
+#pragma unroll
+      for (int g = 0; g < 4; ++g) {
+        const int d0 = db + 8 * g + 4 * hh;
+        float v[4];
+#pragma unroll
+        for (int j = 0; j < 4; ++j) v[j] = acc[bm][bn][4 * g + j];
+        if (bias) {
+          const bf16x4 bb = *reinterpret_cast<const bf16x4*>(bias + fbase + 8 * g + 4 * hh);
+#pragma unroll
+          for (int j = 0; j < 4; ++j) v[j] += (float)bb[j];
+        }
+        bf16x4 o;
+        if (which == 0) {
+#pragma unroll
+          for (int j = 0; j < 4; ++j) o[j] = (__bf16)v[j];
+          *reinterpret_cast<bf16x4*>(static_cast<__bf16*>(a.q) + ((size_t)t * H + head) * AD + d0) = o;
+        } else if (which == 1) {
+          if (ap.k_raw) {
+#pragma unroll
+            for (int j = 0; j < 4; ++j) o[j] = (__bf16)v[j];
+            *reinterpret_cast<bf16x4*>(static_cast<__bf16*>(ap.k_raw) + head * ap.k_raw_hs + (size_t)t * AD + d0) = o;
+          }
+          if (rope) {
+            rope_pair(v[0], v[1], d0, ap.rope, ap.t_row0 + fy, yy, xx);
+            rope_pair(v[2], v[3], d0 + 2, ap.rope, ap.t_row0 + fy, yy, xx);
+          }
+#pragma unroll
+          for (int j = 0; j < 4; ++j) o[j] = (__bf16)v[j];
+          *reinterpret_cast<bf16x4*>(static_cast<__bf16*>(ap.k_rot) + head * ap.k_rot_hs +
+                                     (size_t)(ap.k_rot_off + t) * AD + d0) = o;
+        } else {
+#pragma unroll
+          for (int j = 0; j < 4; ++j)
+            static_cast<__bf16*>(ap.vt)[head * ap.vt_hs + (size_t)(d0 + j) * ap.vt_ld + t] = (__bf16)v[j];
+        }
+      }
+    }
+  }
+}
+
 // ------------------------------------------------------------------ export
 template <typename T>
 __global__ void export_kernel(ExportArgs a) {
@@ -1483,6 +1633,14 @@ hipError_t launch_append(const AppendArgs& a, bool bf16, hipStream_t s) {
   } else {
     return hipErrorInvalidValue;
   }
+  return hipGetLastError();
+}
+
+hipError_t launch_qkv(const QkvArgs& a, hipStream_t s) {
+  if (a.ap.D != AD || a.C <= 0 || a.C % GK != 0 || !a.ap.k_rot || !a.ap.vt || !a.q)
+    return hipErrorInvalidValue;
+  const int nf = (3 * a.ap.H * AD + GF - 1) / GF, nt = (a.ap.T + GT - 1) / GT;
+  qkv_gemm_kernel<<<nf * nt, 512, 0, s>>>(a);
   return hipGetLastError();
 }
 

@@ -85,6 +85,18 @@ struct AppendArgs {
   Rope rope;
 };
 
+// Fused QKV projection: [q | k | v] = x W^T + b on bf16 MFMA (fp32
+// accumulation), with the append kernel's epilogue (K rotated into the
+// cache, V into V^T) and q written un-rotated to a scratch buffer.
+struct QkvArgs {
+  const void* x;            // [T][C] bf16 hidden states
+  const void* w;            // [3*H*D][C] bf16: q heads' rows, then k heads', then v heads'
+  const void* b;            // [3*H*D] bf16 bias, or null
+  int C;                    // hidden width, a multiple of 32
+  void* q;                  // [T][H][D] bf16 scratch for the attention kernel
+  AppendArgs ap;            // K / V destinations and RoPE, as for the append (k_in, v_in unused)
+};
+
 // Retrieval + block-open work, one workgroup.
 struct OpenArgs {
   const float* pose_in;     // [P] caller's pose (null: none)
@@ -138,6 +150,7 @@ hipError_t launch_rope_table(float2* tab, int rows, int dim, long long pos0, dou
                              hipStream_t s);
 hipError_t launch_open(const OpenArgs& a, hipStream_t s);
 hipError_t launch_append(const AppendArgs& a, bool bf16, hipStream_t s);
+hipError_t launch_qkv(const QkvArgs& a, hipStream_t s);
 hipError_t launch_attention(const AttnArgs& a, bool bf16, hipStream_t s);
 
 // The bf16 attention shares key tiles across kStreamWG workgroups when its

@@ -180,6 +180,23 @@ bkv_status bkv_retrieve(bkv_cache h, const float* pose, hipStream_t stream);
 bkv_status bkv_attend(bkv_cache h, int32_t layer, const void* q, const void* k, const void* v,
                       void* out, hipStream_t stream);
 
+/* Fused QKV projection + attention of the open block at `layer` for one sampling
+   step (the operator fusion of the LiveAnimate page, section 方法, and the
+   fused-QKV build of the SoulX-LiveAct page, section 上手实践; neither writes the
+   operation out, the plain reading is taken).  x: device bf16 [T][model_dim] hidden
+   states of the block (token order as in bkv_attend); w: device bf16
+   [3*heads*head_dim][model_dim] projection weights, rows ordered q heads, k heads,
+   v heads (a head's head_dim rows together: the nn.Linear layout); b: device bf16
+   [3*heads*head_dim] bias or NULL.  Computes [q | k | v] = x w^T + b with fp32
+   accumulation (q, k, v rounded to bf16 as they are stored) and then does what
+   bkv_attend does with them: K rotated and stored with V as the block's entry of
+   `layer`, attention written to out [T][heads][head_dim] bf16.  q goes through a
+   workspace scratch; k and v never leave the cache.  model_dim: a positive multiple
+   of 32; x and w each below 2 GiB.
+   Errors: as bkv_attend; BKV_ERR_UNSUPPORTED unless the cache dtype is BKV_BF16. */
+bkv_status bkv_attend_qkv(bkv_cache h, int32_t layer, const void* x, const void* w, const void* b,
+                          int32_t model_dim, void* out, hipStream_t stream);
+
 /* Close the open block: it joins the window; the oldest window block leaves
    (PR-Sink: into the FIFO bank, the oldest bank block dropped when full;
    ConvKV: its raw frames feed the conv memory, rebuilt here on `stream` once
@@ -212,7 +229,7 @@ bkv_status bkv_export_segment(bkv_cache h, int32_t layer, int32_t seg, void* k_o
 /* Per-kernel device time, measured with HIP events recorded on the caller's
    stream immediately before and after each kernel the handle launches. */
 typedef struct {
-  char kernel[24];         /* "retrieve", "append", "attention", "gather", "conv", "export" */
+  char kernel[24];         /* "retrieve", "append", "attention", "gather", "conv", "export", "qkv" */
   int64_t launches;
   double total_ms;         /* sum of per-launch event intervals */
   double max_ms;

@@ -1,0 +1,149 @@
+"""GPU parity of the fused QKV projection path (bkv_attend_qkv) against the
+CPU oracle: q, k, v are the oracle's fp64 projection x W^T + b of the same
+bf16 hidden states and weights, fed to the same stream references.  Outputs
+within max-abs 2e-2; the stored K (rotated) and V within bf16 rounding of
+the oracle's."""
+import numpy as np
+import pytest
+
+import oracle
+from bounded_kv_block_amd import synth
+from gpu_helpers import TOL, Run, max_err
+
+pytestmark = pytest.mark.gpu
+
+
+class QkvRun(Run):
+    """A stream driven through bkv_attend_qkv.  The oracle provider's qkv() is
+    the oracle's projection of the same hidden states (only `heads` filled,
+    the rest zero: the references read only the heads they are asked for)."""
+
+    def __init__(self, cfg, host_inputs=True, heads=None, bias=True):
+        super().__init__(cfg, host_inputs)
+        torch = self.torch
+        H, D = cfg["heads"], cfg["head_dim"]
+        self.heads = list(range(H)) if heads is None else list(heads)
+        self._x_dev, self._x_host = {}, {}
+        self._pw = {}
+        for l in range(cfg["layers"]):
+            if host_inputs:
+                w, b = synth.qkv_weights(cfg, l)
+                wd = torch.from_numpy(w).to(self.device).to(torch.bfloat16)
+                bd = torch.from_numpy(b).to(self.device).to(torch.bfloat16)
+            else:
+                wd, bd = synth.qkv_weights_device(cfg, l, self.device)
+            w64 = wd.float().cpu().numpy().astype(np.float64)
+            b64 = bd.float().cpu().numpy().astype(np.float64)
+            rows = np.concatenate([np.arange(i * H * D + h * D, i * H * D + (h + 1) * D)
+                                   for i in range(3) for h in self.heads])
+            self._pw[l] = (wd, bd if bias else None, w64[rows], b64[rows] if bias else None)
+
+    def x_dev(self, layer, block, step):
+        key = (layer, block, step)
+        if key not in self._x_dev:
+            if self.host_inputs:
+                x = synth.hidden(self.cfg, layer, block, step)
+                self._x_dev[key] = self.torch.from_numpy(x).to(self.device).to(self.torch.bfloat16)
+            else:
+                self._x_dev[key] = synth.hidden_device(self.cfg, layer, block, step, self.device)
+        return self._x_dev[key]
+
+    def qkv(self, layer, block, step):
+        key = (layer, block, step)
+        if key not in self._host:
+            H, D = self.cfg["heads"], self.cfg["head_dim"]
+            x = self.x_dev(layer, block, step).float().cpu().numpy()
+            _, _, wsel, bsel = self._pw[layer]
+            parts = oracle.qkv_projection(x, wsel, bsel, len(self.heads), D)
+            full = []
+            for p in parts:
+                a = np.zeros((x.shape[0], H, D))
+                a[:, self.heads, :] = p
+                full.append(a)
+            self._host[key] = tuple(full)
+        return self._host[key]
+
+    def attend(self, m, layer, step):
+        wd, bd, _, _ = self._pw[layer]
+        return self.cache.attend_qkv(layer, self.x_dev(layer, m, step), wd, bd)
+
+    def drop(self, keep_blocks):
+        for key in list(self._x_dev):
+            if key[1] not in keep_blocks:
+                del self._x_dev[key]
+
+
+def _stream(cfg, run, check=None, heads=None, rows=None, export=False):
+    Ref = oracle.ConvKVReference if cfg["mode"] == "convkv" else oracle.PRSinkReference
+    ref = Ref(cfg, run)
+    worst = 0.0
+    for m in range(cfg["blocks"]):
+        run.open(m)
+        if cfg["mode"] == "convkv":
+            out = run.attend(m, 0, 0)
+            want = ref.attend(m, 0, 0, heads=heads, rows=rows) if check is None or m in check else None
+        else:
+            sel = ref.selection(m)
+            assert run.cache.selection() == sel, m
+            out = run.attend(m, 0, 0)
+            want = ref.attend(m, 0, 0, heads=heads, rows=rows, selection=sel) if check is None or m in check else None
+        if want is not None:
+            err = max_err(out, want, heads, rows)
+            worst = max(worst, err)
+            print(f"block {m}: max|err| {err:.3e}", flush=True)
+            assert err <= TOL["bf16"], (m, err)
+        if export and cfg["mode"] != "convkv":
+            kv = ref.context_kv(m, 0, 0, run.heads, ref.selection(m))
+            for i, (_, _, kr, v) in enumerate(kv):
+                gk, gv = run.cache.export_segment(0, i)
+                gk = gk.float().cpu().numpy()[:, run.heads]
+                gv = gv.float().cpu().numpy()[:, run.heads]
+                # bf16 rounding of fp32-accumulated values: half an ulp plus accumulation noise
+                assert np.all(np.abs(gk - kr) <= 2.0 ** -8 * np.abs(kr) + 1e-3), (m, i)
+                assert np.all(np.abs(gv - v) <= 2.0 ** -8 * np.abs(v) + 1e-3), (m, i)
+        run.cache.commit()
+        if not run.host_inputs:
+            run.drop(set(range(m - 70, m + 2)))
+            run._host.clear()                 # oracle projections are recomputed when needed
+    return worst
+
+
+def test_qkv_small_ragged_with_export():
+    """3 heads (3*3*128 = 1152 projected features: 4.5 feature tiles of 256),
+    3 frames of 6x10 = 180 tokens (one partial token tile), model_dim 256,
+    bias, RoPE 44/42/42, top-2 over a bank of 4, 12 blocks: every output, and
+    the stored K and V of every context segment."""
+    cfg = synth.workload("prsink_512_qkv", heads=3, grid_h=6, grid_w=10, bank=4, blocks=12, pose_dim=16,
+                         keyframes=5, model_dim=256)
+    _stream(cfg, QkvRun(cfg), export=True)
+
+
+def test_qkv_odd_width_no_bias_single_token():
+    """model_dim 96 (three 32-channel steps, fewer than the pipeline depth),
+    no bias, one-token blocks."""
+    cfg = synth.workload("prsink_512_qkv", heads=2, frames=1, grid_h=1, grid_w=1, bank=3, blocks=9,
+                         pose_dim=8, keyframes=3, model_dim=96)
+    _stream(cfg, QkvRun(cfg, bias=False))
+    cfg = synth.workload("prsink_512_qkv", heads=2, grid_h=4, grid_w=10, bank=3, blocks=8,
+                         pose_dim=16, keyframes=4, model_dim=32)
+    _stream(cfg, QkvRun(cfg, bias=False))
+
+
+def test_qkv_convkv_small():
+    """ConvKV through the fused path: the epilogue writes raw K to the slot and
+    K rotated at context positions into the context buffer; 8 blocks (the
+    memory frame appears at block 5)."""
+    cfg = synth.workload("convkv_512", heads=2, grid_h=4, grid_w=6, blocks=8, model_dim=128)
+    run = QkvRun(cfg)
+    _stream(cfg, run)
+    assert run.cache.stats()["memory_count"] == 1
+
+
+def test_qkv_prsink_512_full_shape_sampled():
+    """512x512 shapes at full size with model_dim 5120 (x [3072, 5120], W
+    [15360, 5120]): indices on every block, outputs of heads 0 and 39 on
+    sampled rows of blocks 0 and 7."""
+    cfg = synth.workload("prsink_512_qkv", blocks=8)
+    heads = [0, 39]
+    run = QkvRun(cfg, host_inputs=False, heads=heads)
+    _stream(cfg, run, check={0, 7}, heads=heads, rows=np.r_[0:64, 1500:1532, 3008:3072])

@@ -187,16 +187,17 @@ def test_workspace_size_and_validation():
     # 480 (head, 256-query) units > 256 workgroups: the attention shares key
     # tiles, with two fp32 split slots (O, m, l of 256 rows) per share boundary
     split = 2 * 257 * (8 * 64 * 64 * 4 + 8 * 2 * 64 * 4)
-    assert 61 * slot + split <= n < 61 * slot + split + (1 << 20)   # 61 slots of 62.9 MB
+    qs = 3072 * 40 * 128 * 2                 # bf16 q scratch of the fused projection path
+    assert 61 * slot + split + qs <= n < 61 * slot + split + qs + (1 << 20)   # 61 slots of 62.9 MB
     n8 = bkv.workspace_size(bkv.config_from_workload(synth.workload("prsink_512", heads=8)))
-    assert 61 * slot // 5 <= n8 < 61 * slot // 5 + (1 << 20)        # 96 units: no split slots
+    assert (61 * slot + qs) // 5 <= n8 < (61 * slot + qs) // 5 + (1 << 20)    # 96 units: no split slots
     c3 = bkv.config_from_workload(synth.workload("prsink_720x416"))
     assert bkv.workspace_size(c3) >= 40 * 21 * 2 * 40 * 3520 * 128 * 2
     c5 = bkv.config_from_workload(synth.workload("convkv_512"))
     n5 = bkv.workspace_size(c5)
     ctx = 13312 * 40 * 128 * 2                               # rotated context K
     mem = 2 * 1024 * 40 * 128 * 2                            # memory frame K + V
-    assert 6 * slot + ctx + mem + split <= n5 < 6 * slot + ctx + mem + split + (1 << 20)
+    assert 6 * slot + ctx + mem + split + qs <= n5 < 6 * slot + ctx + mem + split + qs + (1 << 20)
     c1 = bkv.config_from_workload(synth.workload("tiny_fp32"))
     assert bkv.workspace_size(c1) > 13 * 2 * 2 * 128 * 64 * 4
     bad = [dict(rope=(44, 42, 40)), dict(rope=(43, 43, 42)), dict(window=0), dict(dynamic_k=9),
@@ -226,7 +227,8 @@ def test_fp8_key_cache_workspace_and_validation():
     kx = -(-(4 * H * Tp // 64) // 256) * 256          # exponents, 256-byte aligned
     slot8 = H * Tp * D + kx + H * Tp * D * 2
     slot16 = 2 * H * Tp * D * 2
-    assert n16 - n8 == 61 * (slot16 - slot8)            # same 61 slots, same tables and split slots
+    qs = H * Tp * D * 2                                 # bf16 q scratch (fused projection path only)
+    assert n16 - n8 == 61 * (slot16 - slot8) + qs       # same 61 slots, tables and split slots
     for b in (dict(head_dim=64), dict(mode="convkv", static=0, dynamic_k=0, bank=0, pose_dim=0)):
         with pytest.raises(bkv.BkvError) as ei:
             bkv.workspace_size(bkv.config_from_workload(synth.workload("prsink_512_fp8k", **b)))
