@@ -37,8 +37,8 @@ def parse():
     ap.add_argument("--steps", type=int, default=40)
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--workload", default="prsink_512",
-                    choices=["prsink_512", "prsink_512_fp8k", "prsink_720x416", "prsink_long", "convkv_512",
-                             "tiny_fp32"])
+                    choices=["prsink_512", "prsink_512_fp8k", "prsink_512_qkv", "prsink_720x416", "prsink_long",
+                             "convkv_512", "tiny_fp32"])
     ap.add_argument("--pool", type=int, default=4, help="distinct resident input blocks cycled through")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=12.0, help="target CPU-oracle sample time")
@@ -94,17 +94,42 @@ def steady_block(cfg):
     return cfg["static"] + cfg["window"] + cfg["dynamic_k"]
 
 
-def cpu_baseline(cfg, run_inputs, poses, m, target_s):
+def cpu_baseline(cfg, run_inputs, poses, m, target_s, weights=None):
     """The oracle, as it stands, on block m of the same stream: retrieval plus
-    attention of whole heads (all queries) until about target_s seconds."""
+    attention of whole heads (all queries) until about target_s seconds.  With
+    `weights` (the fused-projection workload), run_inputs gives hidden states
+    and the oracle also projects each head's q, k, v inside the timed region."""
     import numpy as np
     import oracle
+
+    H, D = cfg["heads"], cfg["head_dim"]
 
     class Prov:
         def __init__(self):
             self.cache = {}
+            self.head = 0
+            if weights is not None:
+                self.w = weights[0].float().cpu().numpy().astype(np.float64)
+                self.b = weights[1].float().cpu().numpy().astype(np.float64)
+
+        def hidden(self, layer, block, step):
+            key = ("x", layer, block, step)
+            if key not in self.cache:
+                self.cache[key] = run_inputs(layer, block, step).float().cpu().numpy()
+            return self.cache[key]
 
         def qkv(self, layer, block, step):
+            if weights is not None:       # this head's projection (timed: it is the oracle's work)
+                h = self.head
+                x = self.hidden(layer, block, step)
+                rows = np.concatenate([np.arange(i * H * D + h * D, i * H * D + (h + 1) * D) for i in range(3)])
+                parts = oracle.qkv_projection(x, self.w[rows], self.b[rows], 1, D)
+                out = []
+                for part in parts:
+                    a = np.zeros((x.shape[0], H, D))
+                    a[:, h:h + 1, :] = part
+                    out.append(a)
+                return tuple(out)
             key = (layer, block, step)
             if key not in self.cache:
                 self.cache[key] = tuple(t.float().cpu().numpy() for t in run_inputs(layer, block, step))
@@ -120,19 +145,20 @@ def cpu_baseline(cfg, run_inputs, poses, m, target_s):
     prov = Prov()
     ref = (oracle.ConvKVReference if cfg["mode"] == "convkv" else oracle.PRSinkReference)(cfg, prov)
     # fetch the inputs first (not part of the oracle's work)
+    fetch = prov.hidden if weights is not None else prov.qkv
     for kind, b, _, _ in (ref.context(m) if cfg["mode"] == "convkv" else ref.context(m, ref.selection(m))):
         if kind != "memory":
-            prov.qkv(0, b, cfg["steps"] - 1)
+            fetch(0, b, cfg["steps"] - 1)
     if cfg["mode"] == "convkv":
         for grp in ref.schedule(m)["memory"]:
             for e in grp:
-                prov.qkv(0, e // cfg["frames"], cfg["steps"] - 1)
-    prov.qkv(0, m, 0)
-    H = cfg["heads"]
+                fetch(0, e // cfg["frames"], cfg["steps"] - 1)
+    fetch(0, m, 0)
     t0 = time.perf_counter()
     sel = ref.selection(m) if cfg["mode"] != "convkv" else None
     done = 0
     while done < H:
+        prov.head = done
         if cfg["mode"] == "convkv":
             ref.attend(m, 0, 0, heads=[done])
         else:
@@ -149,7 +175,8 @@ def cpu_baseline(cfg, run_inputs, poses, m, target_s):
         blas = 1
     return {"value": T * done / H / dt, "unit": "query tokens/s", "cores": int(blas),
             "host_cpus": len(os.sched_getaffinity(0)), "kind": "oracle",
-            "sample": f"block {m} of the {cfg['name']} stream: retrieval + fp64 attention of {done}/{H} heads "
+            "sample": f"block {m} of the {cfg['name']} stream: retrieval + "
+                      f"{'fp64 QKV projection + ' if weights is not None else ''}fp64 attention of {done}/{H} heads "
                       f"x all {T} queries over the block's bounded context, "
                       f"{dt:.1f} s; value scaled to the whole block (x{H}/{done})"}
 
@@ -183,12 +210,16 @@ def main():
             cache.set_conv_weights(l, torch.from_numpy(wk).to(dev), torch.from_numpy(wv).to(dev))
 
     # resident inputs: a pool of blocks per (layer, step), cycled by block id
+    # (q, k, v; or hidden states and per-layer projection weights)
+    fused = bool(cfg.get("qkv"))
     pool = max(1, args.pool if L * S == 1 else 1)
     inputs = {}
     for b in range(pool):
         for l in range(L):
             for s in range(S):
-                inputs[(l, b, s)] = synth.qkv_device(cfg, l, b, s, dev)
+                inputs[(l, b, s)] = (synth.hidden_device(cfg, l, b, s, dev) if fused
+                                     else synth.qkv_device(cfg, l, b, s, dev))
+    weights = {l: synth.qkv_weights_device(cfg, l, dev) for l in range(L)} if fused else {}
 
     def block_inputs(layer, block, step):
         return inputs[(layer, block % pool, step)]
@@ -197,14 +228,21 @@ def main():
     n_blocks = prefix + args.warmup + args.steps
     poses_np = synth.poses(cfg, n_blocks)
     poses = torch.from_numpy(poses_np).to(dev) if cfg["pose_dim"] else None
-    out = torch.empty((T, H, D), dtype=inputs[(0, 0, 0)][0].dtype, device=dev)
+    out = torch.empty((T, H, D), dtype=torch.float32 if cfg["dtype"] == "f32" else torch.bfloat16, device=dev)
+
+    def attend(l, m, s):
+        if fused:
+            w, b = weights[l]
+            cache.attend_qkv(l, block_inputs(l, m, s), w, b, out)
+        else:
+            q, k, v = block_inputs(l, m, s)
+            cache.attend(l, q, k, v, out)
 
     def step(m):
         cache.retrieve(poses[m] if poses is not None else None)
         for s in range(S):
             for l in range(L):
-                q, k, v = block_inputs(l, m, s)
-                cache.attend(l, q, k, v, out)
+                attend(l, m, s)
         cache.commit()
 
     m = 0
@@ -224,8 +262,7 @@ def main():
         n_keys.append(cache.stats()["n_keys"])
         for s in range(S):
             for l in range(L):
-                q, k, v = block_inputs(l, m, s)
-                cache.attend(l, q, k, v, out)
+                attend(l, m, s)
         cache.commit()
         m += 1
     ev[-1].record()
@@ -254,7 +291,13 @@ def main():
         kernels[name] = {"launches": int(n), "avg_us": 1e3 * tot / n, "max_us": 1e3 * mx}
     # algorithmic bytes of the HBM-bound kernels, per launch
     app_bytes = 2.0 * T * H * D * esz + T * H * D * (kesz + esz)   # K, V read token-major; written to the cache
-    kernels["append"]["gbs"] = app_bytes / (kernels["append"]["avg_us"] * 1e-6) / 1e9
+    if "append" in kernels:
+        kernels["append"]["gbs"] = app_bytes / (kernels["append"]["avg_us"] * 1e-6) / 1e9
+    if "qkv" in kernels:
+        g_flop = 2.0 * T * cfg["model_dim"] * 3 * H * D
+        kernels["qkv"]["tflops"] = g_flop / (kernels["qkv"]["avg_us"] * 1e-6) / 1e12
+        kernels["qkv"]["pct_peak"] = 100.0 * kernels["qkv"]["tflops"] / PEAK_BF16_TFLOPS
+        kernels["qkv"]["flop_per_launch"] = g_flop
     if "gather" in kernels:
         ctx_rows = Nk - T
         g_bytes = 2.0 * ctx_rows * H * D * esz
@@ -286,7 +329,8 @@ def main():
                    "queries_per_block": T, "keys_per_block": Nk, "layers": L, "steps_per_block": S,
                    "attends_per_block": attends_per_step, "window": cfg["window"],
                    "dynamic_k": cfg["dynamic_k"], "bank": cfg["bank"], "rope": list(cfg["rope"]),
-                   "timed_blocks": [m - args.steps, m - 1]},
+                   "timed_blocks": [m - args.steps, m - 1],
+                   **({"model_dim": cfg["model_dim"], "qkv_projection": "fused (bkv_attend_qkv)"} if fused else {})},
         "attention_tflops": attn_tflops,
         "attention_pct_peak": 100.0 * attn_tflops / peak,
         "attention_peak_tflops": peak,
@@ -301,7 +345,8 @@ def main():
         "workspace_bytes": int(cache.stats()["workspace_bytes"]),
     }
     if not args.no_cpu_baseline:
-        res["cpu_baseline"] = cpu_baseline(cfg, block_inputs, poses_np, m - 1, args.cpu_seconds)
+        res["cpu_baseline"] = cpu_baseline(cfg, block_inputs, poses_np, m - 1, args.cpu_seconds,
+                                           weights[0] if fused else None)
     print(json.dumps(res), flush=True)
 
 

@@ -1420,10 +1420,11 @@ __global__ __launch_bounds__(256) void conv_kernel(ConvArgs a) {
 // tiles are rows of 32 channels (64 B) in LDS, chunk c of row r at
 // c ^ ((r >> 2) & 3): the 16 rows a 16-lane phase reads (same chunk index)
 // then cover the 64 banks once.  Tiles move with buffer_load ... lds, four
-// stages deep, issued three steps ahead; one barrier per step publishes
-// step s and retires the reads of step s-1 before its buffer is refilled.
-// Rows past the last token or feature are loaded clamped to the last valid
-// row and never stored.
+// stages deep, three steps ahead.  Only waves 0-3 issue loads (eight per step
+// each, four between the MFMAs of each half-step): every load blocks its
+// wave until the CU's address unit takes it, so the loads are kept off half
+// of the waves and spread over the step.  Rows past the last token or
+// feature are loaded clamped to the last valid row and never stored.
 constexpr int GF = 256, GT = 256, GK = 32, GSTAGE = 4;
 constexpr int G_OPB = GF * GK * 2;          // bytes of one operand tile per step (16 KB)
 static_assert(GF == GT, "both operand tiles share the load mapping");
@@ -1445,24 +1446,33 @@ void qkv_gemm_kernel(QkvArgs a) {
   // loads: chunk p = (8i + wave)*64 + lane of an operand tile (i = 0, 1) lands
   // at LDS p*16 = row 128i + 16 wave + (lane >> 2), position lane & 3, which
   // holds the row's chunk (lane & 3) ^ ((lane >> 4) & 3)
-  const int rl = 16 * wave + (lane >> 2);
+  // waves 0-3 load (each for wave slots w and w + 4); waves 4-7 issue no loads
   const unsigned cpos = (unsigned)(((lane & 3) ^ ((lane >> 4) & 3)) << 4);
-  unsigned vw[2], vx[2];
+  unsigned vw[2][2], vx[2][2];
 #pragma unroll
-  for (int i = 0; i < 2; ++i) {
-    vw[i] = (unsigned)min(f0 + 128 * i + rl, NF - 1) * (unsigned)C * 2u + cpos;
-    vx[i] = (unsigned)min(t0 + 128 * i + rl, T - 1) * (unsigned)C * 2u + cpos;
-  }
+  for (int i = 0; i < 2; ++i)
+#pragma unroll
+    for (int k = 0; k < 2; ++k) {
+      const int rl = 16 * ((wave & 3) + 4 * k) + (lane >> 2);
+      vw[i][k] = (unsigned)min(f0 + 128 * i + rl, NF - 1) * (unsigned)C * 2u + cpos;
+      vx[i][k] = (unsigned)min(t0 + 128 * i + rl, T - 1) * (unsigned)C * 2u + cpos;
+    }
+  const bool loader = wave < 4;
   const i32x4 rw = buffer_rsrc(uniform_ptr(a.w)), rx = buffer_rsrc(uniform_ptr(a.x));
   const unsigned lds0 = (unsigned)(uintptr_t)(lds_ptr_t)lds;
   const int S = C / GK;
-  auto issue = [&](int s) {
+  // load j (0..7) of step s: operand j >> 2 (W, x), i = (j >> 1) & 1, slot k = j & 1
+  auto issue_one = [&](int s, int j) {
     const unsigned base = __builtin_amdgcn_readfirstlane(lds0 + (unsigned)(s & (GSTAGE - 1)) * 2 * G_OPB);
     const unsigned soff = __builtin_amdgcn_readfirstlane((unsigned)s * GK * 2u);
+    const int i = (j >> 1) & 1, k = j & 1, w = (wave & 3) + 4 * k;
+    if (!loader) return;
+    if (j < 4) dma16(rw, vw[i][k], soff, base + (8 * i + w) * 1024);
+    else dma16(rx, vx[i][k], soff, base + G_OPB + (8 * i + w) * 1024);
+  };
+  auto issue = [&](int s) {
 #pragma unroll
-    for (int i = 0; i < 2; ++i) dma16(rw, vw[i], soff, base + (8 * i + wave) * 1024);
-#pragma unroll
-    for (int i = 0; i < 2; ++i) dma16(rx, vx[i], soff, base + G_OPB + (8 * i + wave) * 1024);
+    for (int j = 0; j < 8; ++j) issue_one(s, j);
   };
   auto frag = [&](const char* tile, int row, int c) {
     return *reinterpret_cast<const bf16x8*>(tile + row * 64 + ((c ^ ((row >> 2) & 3)) << 4));
@@ -1474,31 +1484,59 @@ void qkv_gemm_kernel(QkvArgs a) {
 #pragma unroll
     for (int bn = 0; bn < 2; ++bn) acc[bm][bn] = f32x16{};
 
-  issue(0);
-  if (S > 1) issue(1);
-  if (S > 2) issue(2);
-  for (int s = 0; s < S; ++s) {
-    // this wave's chunks of step s have landed (later steps still in flight)
-    if (s + 2 < S) asm volatile("s_waitcnt vmcnt(8)" ::: "memory");
-    else if (s + 1 < S) asm volatile("s_waitcnt vmcnt(4)" ::: "memory");
-    else asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-    wg_barrier();
-    if (s + 3 < S) issue(s + 3);
+  // Fragments of half-step (s, ss) are read one half-step ahead of their
+  // MFMAs.  Step s+1 is published by a barrier between the two halves of step
+  // s, which each wave reaches with its chunks of step s+1 landed and all its
+  // LDS reads returned; the first reads of s+1 then overlap the MFMAs of
+  // (s, 1).  The reads of step s-1 end before the barrier of step s-1, so
+  // from there on step s+3 may refill that buffer: its loads go in during
+  // both halves of step s.
+  auto read_half = [&](int s, int ss, bf16x8 (&af)[4], bf16x8 (&bx)[2]) {
     const char* A = lds + (s & (GSTAGE - 1)) * 2 * G_OPB;
     const char* B = A + G_OPB;
 #pragma unroll
-    for (int ss = 0; ss < 2; ++ss) {
-      bf16x8 af[4], bx[2];
+    for (int bm = 0; bm < 4; ++bm) af[bm] = frag(A, 128 * wf + 32 * bm + col, 2 * ss + hh);
 #pragma unroll
-      for (int bm = 0; bm < 4; ++bm) af[bm] = frag(A, 128 * wf + 32 * bm + col, 2 * ss + hh);
+    for (int bn = 0; bn < 2; ++bn) bx[bn] = frag(B, 64 * wt + 32 * bn + col, 2 * ss + hh);
+  };
+  // eight MFMAs; with load_step >= 0, loads load_j0 .. load_j0 + 3 of that
+  // step go in after MFMAs 1, 3, 5, 7 (loading waves only)
+  auto mfma_half = [&](const bf16x8 (&af)[4], const bf16x8 (&bx)[2], int load_step, int load_j0) {
 #pragma unroll
-      for (int bn = 0; bn < 2; ++bn) bx[bn] = frag(B, 64 * wt + 32 * bn + col, 2 * ss + hh);
+    for (int bm = 0; bm < 4; ++bm)
 #pragma unroll
-      for (int bm = 0; bm < 4; ++bm)
-#pragma unroll
-        for (int bn = 0; bn < 2; ++bn)
-          acc[bm][bn] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[bm], bx[bn], acc[bm][bn], 0, 0, 0);
+      for (int bn = 0; bn < 2; ++bn) {
+        acc[bm][bn] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[bm], bx[bn], acc[bm][bn], 0, 0, 0);
+        if (load_step >= 0 && bn == 1) {
+          __builtin_amdgcn_sched_barrier(0);
+          issue_one(load_step, load_j0 + bm);
+          __builtin_amdgcn_sched_barrier(0);
+        }
+      }
+  };
+  bf16x8 a0[4], b0[2], a1[4], b1[2];
+  issue(0);
+  if (S > 1) issue(1);
+  if (S > 2) issue(2);
+  // this wave's chunks of step 0 have landed
+  if (S > 2) asm volatile("s_waitcnt vmcnt(16)" ::: "memory");
+  else if (S > 1) asm volatile("s_waitcnt vmcnt(8)" ::: "memory");
+  else asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+  wg_barrier();
+  read_half(0, 0, a0, b0);
+  for (int s = 0; s < S; ++s) {
+    read_half(s, 1, a1, b1);
+    mfma_half(a0, b0, s + 3 < S ? s + 3 : -1, 0);
+    if (s + 1 < S) {
+      // this wave's chunks of step s+1 have landed (step s+2 may be in flight)
+      // loads after step s+1's: step s+2 (8) and the first 4 of step s+3
+      if (s + 3 < S) asm volatile("s_waitcnt vmcnt(12) lgkmcnt(0)" ::: "memory");
+      else if (s + 2 < S) asm volatile("s_waitcnt vmcnt(8) lgkmcnt(0)" ::: "memory");
+      else asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)" ::: "memory");
+      wg_barrier();
+      read_half(s + 1, 0, a0, b0);
     }
+    mfma_half(a1, b1, s + 3 < S ? s + 3 : -1, 4);
   }
 
   // epilogue: + bias; q -> scratch [T][H][D]; k -> (raw copy,) RoPE -> cache
