@@ -23,13 +23,13 @@ import copy
 import numpy as np
 
 (TENSOR_Q, TENSOR_K, TENSOR_V, TENSOR_POSE, TENSOR_KEYFRAMES, TENSOR_CONV, TENSOR_SCHED, TENSOR_HIDDEN,
- TENSOR_WQKV, TENSOR_BQKV) = range(10)
+ TENSOR_WQKV, TENSOR_BQKV, TENSOR_REF) = range(11)
 
 # Workload shapes.  Keys mirror the C-ABI config struct field names.
 _BASE = dict(mode="pr_sink", dtype="bf16", layers=1, steps=1, heads=40, head_dim=128,
              frames=3, grid_h=32, grid_w=32, window=3, static=1, dynamic_k=2, bank=56,
              pose_dim=128, rope=(44, 42, 42), theta=10000.0, conv_kernel=5, conv_stride=5,
-             memory_frames=1, blocks=60, seed=2, pose_kind="walk", keyframes=16, model_dim=5120)
+             memory_frames=1, blocks=60, seed=2, pose_kind="walk", keyframes=16, model_dim=5120, reference_frames=0)
 
 WORKLOADS = {
     # tiny fp32 stream: 2 heads x 64, 2 frames of 8x8, top-1 over 32-d poses,
@@ -42,6 +42,8 @@ WORKLOADS = {
     "prsink_512": dict(_BASE),
     # the same with the FP8 key cache (K as E4M3 with per-tile scales)
     "prsink_512_fp8k": dict(_BASE, dtype="bf16_fp8k"),
+    # the same with one reference frame (1024 tokens) as a permanent sink
+    "prsink_512_ref": dict(_BASE, reference_frames=1),
     # the same driven from hidden states: q, k, v projected in the fused path
     # from x [3072, 5120] (40 heads x 128 = 5120, a 14B-class DiT's width)
     "prsink_512_qkv": dict(_BASE, qkv=True),
@@ -244,3 +246,16 @@ def qkv_weights_device(cfg: dict, layer: int, device="cuda"):
     g.manual_seed(_torch_seed(cfg, layer, 0, 0, TENSOR_BQKV))
     b = torch.randn(n, generator=g, device=device, dtype=torch.float32) * 0.1
     return w.to(torch.bfloat16), b.to(torch.bfloat16)
+
+
+# ---- reference frames (reference-sink variant) --------------------------------
+def reference(cfg: dict, layer: int):
+    """K, V [reference_frames * grid_h * grid_w, H, D] of the reference frames
+    (fp32 holding bf16 values for bf16 workloads), N(0, 1)."""
+    shape = (cfg["reference_frames"] * cfg["grid_h"] * cfg["grid_w"], cfg["heads"], cfg["head_dim"])
+    g = _rng(cfg, layer, 0, 0, TENSOR_REF)
+    k = g.standard_normal(shape, dtype=np.float32)
+    v = g.standard_normal(shape, dtype=np.float32)
+    if cfg["dtype"] != "f32":
+        k, v = round_to_bf16(k), round_to_bf16(v)
+    return k, v

@@ -2,7 +2,8 @@
 
 A *provider* hands the oracle the stream's inputs, exactly as the GPU path got
 them: ``provider.qkv(layer, block, step) -> (q, k, v)`` each [T, H, D];
-``provider.pose(block) -> [P]``; ``provider.conv_weights(layer) -> (wk, wv)``.
+``provider.pose(block) -> [P]``; ``provider.conv_weights(layer) -> (wk, wv)``;
+``provider.reference(layer) -> (k, v)`` each [R * grid_h * grid_w, H, D].
 The oracle keeps no cache: a context block's K/V are asked for again when
 needed, which keeps memory flat and the code short.
 
@@ -17,6 +18,12 @@ Readings (beyond those stated in the modules used here):
     current block]; temporal positions run 0, 1, 2, ... over those frames.
   * PR-Sink with an FP8 key cache (dtype "bf16_fp8k"): K and Q are quantised
     to E4M3 as ``fp8`` states before Q K^T; V and the softmax are unchanged.
+  * PR-Sink with reference_frames = R > 0 (the LiveAnimate page, section 方法,
+    conditions every block on the reference image; the Live Avatar page's
+    abstract recalibrates appearance from a cached reference image): the R
+    reference frames are a permanent first context segment at temporal
+    positions 0..R-1, and generated frame f of block b moves to t = R + b *
+    frames + f.  R = 0 is the plain reading above.
 """
 from __future__ import annotations
 
@@ -46,6 +53,7 @@ class _Base:
         self.f_tok, self.y_tok, self.x_tok = token_positions(F, gh, gw)
         self.split = tuple(cfg["rope"])
         self.theta = float(cfg.get("theta", 10000.0))
+        self.R = int(cfg.get("reference_frames", 0) or 0)
 
     def _rot(self, x, t_of_frame, heads, tok=None):
         """Rotate x [N, H, D] (tokens ``tok`` of a block, default all) with t = t_of_frame(f)."""
@@ -81,20 +89,31 @@ class PRSinkReference(_Base):
         sch = self.schedule(m)
         sel = self.selection(m) if selection is None else selection
         F, T = self.F, self.T
-        segs = [("static", b, T, b * F) for b in sch["static"]]
-        segs += [("dynamic", b, T, b * F) for b in sel]
-        segs += [("window", b, T, b * F) for b in sch["window"]]
-        segs.append(("current", m, T, m * F))
+        t = self.block_t0
+        segs = [("reference", -1, self.R * self.Tf, 0)] if self.R > 0 else []
+        segs += [("static", b, T, t(b)) for b in sch["static"]]
+        segs += [("dynamic", b, T, t(b)) for b in sel]
+        segs += [("window", b, T, t(b)) for b in sch["window"]]
+        segs.append(("current", m, T, t(m)))
         return segs
+
+    def block_t0(self, b: int) -> int:
+        """Temporal position of block b's first frame (after the reference frames)."""
+        return self.R + b * self.F
 
     def context_kv(self, m: int, layer: int, step: int, heads, selection=None):
         """Rotated K and raw V of every context segment, each [T, len(heads), D] fp64."""
         last = self.cfg["steps"] - 1
         out = []
-        for kind, b, _, _ in self.context(m, selection):
-            s = step if kind == "current" else last
-            _, k, v = self.p.qkv(layer, b, s)
-            kr = self._rot(k, lambda f, b=b: b * self.F + f, heads)
+        for kind, b, _, t0 in self.context(m, selection):
+            if kind == "reference":
+                k, v = self.p.reference(layer)
+                f, y, x = token_positions(self.R, self.cfg["grid_h"], self.cfg["grid_w"])
+                kr = apply_rope(np.asarray(k)[:, heads, :], f.astype(np.float64), y, x, self.split, self.theta)
+            else:
+                s = step if kind == "current" else last
+                _, k, v = self.p.qkv(layer, b, s)
+                kr = self._rot(k, lambda f, t0=t0: t0 + f, heads)
             out.append((kind, b, kr, np.asarray(v, np.float64)[:, heads, :]))
         return out
 
@@ -103,7 +122,7 @@ class PRSinkReference(_Base):
         H = self.cfg["heads"]
         heads = list(range(H)) if heads is None else list(heads)
         q, _, _ = self.p.qkv(layer, m, step)
-        q_rot = self._rot(q, lambda f: m * self.F + f, heads)
+        q_rot = self._rot(q, lambda f: self.block_t0(m) + f, heads)
         kv = self.context_kv(m, layer, step, heads, selection)
         if self.cfg["dtype"] != "bf16_fp8k":
             return self._attend(q_rot, [x[2] for x in kv], [x[3] for x in kv], heads, rows)

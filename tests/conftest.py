@@ -55,6 +55,9 @@ class SynthProvider:
             self._w[layer] = self._synth.conv_weights(self.cfg, layer)
         return self._w[layer]
 
+    def reference(self, layer):
+        return self._synth.reference(self.cfg, layer)
+
 
 @pytest.fixture
 def rng():

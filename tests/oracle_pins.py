@@ -331,3 +331,41 @@ def check_projection_layout(qkv_projection):
     b = np.arange(3 * H * D, dtype=np.float64) + 0.5
     q, k, v = qkv_projection(np.zeros((2, C)), w, b, H, D)
     assert np.array_equal(np.concatenate([a.reshape(2, -1) for a in (q, k, v)], axis=1), np.tile(b, (2, 1)))
+
+
+# ---------------------------------------------------------- reference sink
+def check_prsink_reference(Ref, token_positions, apply_rope, masked_attention, make_cfg, make_provider):
+    """PR-Sink with R reference frames: block m's output equals dense attention
+    over [the R reference frames at t = 0..R-1, then every block 0..m with
+    frame f of block b at t = R + b * frames + f], masked to the reference
+    (always), the hand-derived static and window blocks, the retrieved blocks
+    and block m itself; the query sits at t = R + m * frames + f."""
+    golden = {int(r[0]): r for r in read_table("prsink_schedule_w3_b8_s1.txt")}
+    for R in (1, 2):
+        cfg = make_cfg(R)
+        prov = make_provider(cfg)
+        ref = Ref(cfg, prov)
+        F, gh, gw = cfg["frames"], cfg["grid_h"], cfg["grid_w"]
+        f, y, x = token_positions(F, gh, gw)
+        fr, yr, xr = token_positions(R, gh, gw)
+        k_ref, v_ref = prov.reference(0)
+        assert k_ref.shape[0] == R * gh * gw
+        last = cfg["steps"] - 1
+        for m in range(cfg["blocks"]):
+            sel = ref.selection(m)
+            allowed = set(ids(golden[m][1])) | set(sel) | set(ids(golden[m][3])) | {m}
+            ks = [apply_rope(k_ref, fr.astype(np.float64), yr, xr, cfg["rope"])]
+            vs = [np.asarray(v_ref, np.float64)]
+            keep = [np.ones(k_ref.shape[0], bool)]
+            for b in range(m + 1):
+                _, k, v = prov.qkv(0, b, last if b < m else 0)
+                ks.append(apply_rope(k, R + b * F + f, y, x, cfg["rope"]))
+                vs.append(np.asarray(v, np.float64))
+                keep.append(np.full(k.shape[0], b in allowed))
+            q, _, _ = prov.qkv(0, m, 0)
+            qr = apply_rope(q, R + m * F + f, y, x, cfg["rope"])
+            keep = np.concatenate(keep)
+            mask = np.broadcast_to(keep[None, :], (q.shape[0], keep.size))
+            want = masked_attention(qr, np.concatenate(ks), np.concatenate(vs), mask)
+            got = ref.attend(m, 0, 0)
+            assert np.allclose(got, want, atol=1e-12, rtol=0), (R, m)

@@ -144,6 +144,29 @@ def test_prsink_equals_masked_full_attention(rope):
             assert allowed == set(range(m + 1))
 
 
+def _ref_cfg(R):
+    return synth.workload("tiny_fp32", rope=(24, 20, 20), reference_frames=R)
+
+
+def test_prsink_reference_equals_masked_full_attention():
+    pins.check_prsink_reference(oracle.PRSinkReference, oracle.token_positions, oracle.apply_rope,
+                                oracle.masked_attention, _ref_cfg, SynthProvider)
+
+
+def test_prsink_reference_block0_is_plain_attention():
+    """Block 0 with R reference frames and RoPE off: SDPA over [reference, block 0]."""
+    import torch
+    cfg = synth.workload("tiny_fp32", reference_frames=2)
+    prov = SynthProvider(cfg)
+    q, k, v = prov.qkv(0, 0, 0)
+    kr, vr = prov.reference(0)
+    got = oracle.PRSinkReference(cfg, prov).attend(0, 0, 0)
+    t = lambda a: torch.from_numpy(np.asarray(a, np.float64).transpose(1, 0, 2).copy())[None]
+    ref = torch.nn.functional.scaled_dot_product_attention(
+        t(q), t(np.concatenate([kr, k])), t(np.concatenate([vr, v])))[0].numpy().transpose(1, 0, 2)
+    assert np.allclose(got, ref, atol=1e-12)
+
+
 def test_prsink_block0_is_plain_attention():
     import torch
     cfg = synth.workload("tiny_fp32")

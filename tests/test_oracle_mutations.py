@@ -257,3 +257,40 @@ def _proj_no_bias(x, w, b, H, D):
 @pytest.mark.parametrize("mutant", [_proj_kv_swapped, _proj_dim_major, _proj_no_bias])
 def test_projection_mutants_fail(mutant, rng):
     assert _fails(pins.check_projection_brute_force, mutant, rng) or _fails(pins.check_projection_layout, mutant)
+
+
+# -- reference-sink mutants ---------------------------------------------------
+class _RefUnshifted(oracle.PRSinkReference):
+    """Generated blocks keep t = b * frames (not moved past the reference)."""
+
+    def block_t0(self, b):
+        return b * self.F
+
+
+class _RefDropped(oracle.PRSinkReference):
+    """The reference segment left out of the context (positions still shifted)."""
+
+    def context(self, m, selection=None):
+        return [s for s in super().context(m, selection) if s[0] != "reference"]
+
+
+class _RefFramesAtZero(oracle.PRSinkReference):
+    """Every reference frame rotated at t = 0 instead of t = f."""
+
+    def context_kv(self, m, layer, step, heads, selection=None):
+        out = super().context_kv(m, layer, step, heads, selection)
+        if out and out[0][0] == "reference":
+            k, _ = self.p.reference(layer)
+            f, y, x = oracle.token_positions(self.R, self.cfg["grid_h"], self.cfg["grid_w"])
+            kr = oracle.apply_rope(np.asarray(k)[:, heads, :], np.zeros(len(f)), y, x, self.split, self.theta)
+            out[0] = (out[0][0], out[0][1], kr, out[0][3])
+        return out
+
+
+@pytest.mark.parametrize("mutant", [_RefUnshifted, _RefDropped, _RefFramesAtZero])
+def test_reference_mutants_fail(mutant):
+    from bounded_kv_block_amd import synth
+    from conftest import SynthProvider
+    cfg = lambda R: synth.workload("tiny_fp32", rope=(24, 20, 20), reference_frames=R, blocks=6)
+    assert _fails(pins.check_prsink_reference, mutant, oracle.token_positions, oracle.apply_rope,
+                  oracle.masked_attention, cfg, SynthProvider)
