@@ -37,8 +37,8 @@ def parse():
     ap.add_argument("--steps", type=int, default=40)
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--workload", default="prsink_512",
-                    choices=["prsink_512", "prsink_512_fp8k", "prsink_512_qkv", "prsink_720x416", "prsink_long",
-                             "convkv_512", "tiny_fp32"])
+                    choices=["prsink_512", "prsink_512_fp8k", "prsink_512_qkv", "prsink_512_ref", "prsink_720x416",
+                             "prsink_long", "convkv_512", "tiny_fp32"])
     ap.add_argument("--pool", type=int, default=4, help="distinct resident input blocks cycled through")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=12.0, help="target CPU-oracle sample time")
@@ -142,6 +142,13 @@ def cpu_baseline(cfg, run_inputs, poses, m, target_s, weights=None):
             from bounded_kv_block_amd import synth
             return synth.conv_weights(cfg, layer)
 
+        def reference(self, layer):
+            key = ("ref", layer)
+            if key not in self.cache:
+                from bounded_kv_block_amd import synth
+                self.cache[key] = synth.reference(cfg, layer)
+            return self.cache[key]
+
     prov = Prov()
     ref = (oracle.ConvKVReference if cfg["mode"] == "convkv" else oracle.PRSinkReference)(cfg, prov)
     # fetch the inputs first (not part of the oracle's work)
@@ -154,6 +161,8 @@ def cpu_baseline(cfg, run_inputs, poses, m, target_s, weights=None):
             for e in grp:
                 fetch(0, e // cfg["frames"], cfg["steps"] - 1)
     fetch(0, m, 0)
+    if cfg.get("reference_frames"):
+        prov.reference(0)
     t0 = time.perf_counter()
     sel = ref.selection(m) if cfg["mode"] != "convkv" else None
     done = 0
@@ -208,6 +217,10 @@ def main():
         for l in range(L):
             wk, wv = synth.conv_weights(cfg, l)
             cache.set_conv_weights(l, torch.from_numpy(wk).to(dev), torch.from_numpy(wv).to(dev))
+    if cfg.get("reference_frames"):
+        dt_in = torch.float32 if cfg["dtype"] == "f32" else torch.bfloat16
+        for l in range(L):
+            cache.set_reference(l, *(torch.from_numpy(a).to(dev).to(dt_in) for a in synth.reference(cfg, l)))
 
     # resident inputs: a pool of blocks per (layer, step), cycled by block id
     # (q, k, v; or hidden states and per-layer projection weights)
@@ -330,7 +343,8 @@ def main():
                    "attends_per_block": attends_per_step, "window": cfg["window"],
                    "dynamic_k": cfg["dynamic_k"], "bank": cfg["bank"], "rope": list(cfg["rope"]),
                    "timed_blocks": [m - args.steps, m - 1],
-                   **({"model_dim": cfg["model_dim"], "qkv_projection": "fused (bkv_attend_qkv)"} if fused else {})},
+                   **({"model_dim": cfg["model_dim"], "qkv_projection": "fused (bkv_attend_qkv)"} if fused else {}),
+                   **({"reference_frames": cfg["reference_frames"]} if cfg.get("reference_frames") else {})},
         "attention_tflops": attn_tflops,
         "attention_pct_peak": 100.0 * attn_tflops / peak,
         "attention_peak_tflops": peak,

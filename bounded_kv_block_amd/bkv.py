@@ -17,10 +17,11 @@ BKV_OK, BKV_ERR_ARG, BKV_ERR_STATE, BKV_ERR_WORKSPACE, BKV_ERR_DEVICE, BKV_ERR_U
 PR_SINK, CONVKV = 0, 1
 F32, BF16, BF16_FP8K = 0, 1, 2
 DTYPES = {"f32": F32, "bf16": BF16, "bf16_fp8k": BF16_FP8K}
-SEG_KINDS = {0: "static", 1: "dynamic", 2: "window", 3: "current", 4: "memory"}
+SEG_KINDS = {0: "static", 1: "dynamic", 2: "window", 3: "current", 4: "memory", 5: "reference"}
 
 # every symbol include/bkv.h declares
 EXPORTS = ("bkv_workspace_size", "bkv_create", "bkv_destroy", "bkv_reset", "bkv_set_conv_weights",
+           "bkv_set_reference",
            "bkv_profile_start", "bkv_profile_stop",
            "bkv_retrieve", "bkv_attend", "bkv_attend_qkv", "bkv_commit", "bkv_selection", "bkv_context", "bkv_stats",
            "bkv_export_segment", "bkv_status_str", "bkv_last_error")
@@ -35,7 +36,7 @@ class Config(ctypes.Structure):
                 ("rope_t", ctypes.c_int32), ("rope_h", ctypes.c_int32), ("rope_w", ctypes.c_int32),
                 ("rope_theta", ctypes.c_double), ("conv_kernel", ctypes.c_int32),
                 ("conv_stride", ctypes.c_int32), ("memory_frames", ctypes.c_int32),
-                ("softmax_scale", ctypes.c_float)]
+                ("softmax_scale", ctypes.c_float), ("reference_frames", ctypes.c_int32)]
 
 
 class Segment(ctypes.Structure):
@@ -79,6 +80,7 @@ def lib() -> ctypes.CDLL:
             "bkv_destroy": [vp],
             "bkv_reset": [vp],
             "bkv_set_conv_weights": [vp, i32, vp, vp, vp],
+            "bkv_set_reference": [vp, i32, vp, vp, vp],
             "bkv_retrieve": [vp, vp, vp],
             "bkv_attend": [vp, i32, vp, vp, vp, vp, vp],
             "bkv_attend_qkv": [vp, i32, vp, vp, vp, i32, vp, vp],
@@ -128,6 +130,7 @@ def config_from_workload(w: dict) -> Config:
     c.rope_theta = float(w.get("theta", 10000.0))
     c.conv_kernel, c.conv_stride, c.memory_frames = w["conv_kernel"], w["conv_stride"], w["memory_frames"]
     c.softmax_scale = float(w.get("softmax_scale", 0.0))
+    c.reference_frames = int(w.get("reference_frames", 0) or 0)
     return c
 
 
@@ -198,6 +201,16 @@ class Cache:
                                           self._tensor(wk, "wk", shp, self._torch.float32),
                                           self._tensor(wv, "wv", shp, self._torch.float32), self._s()),
                "bkv_set_conv_weights")
+
+    @property
+    def reference_shape(self):
+        c = self.config
+        return (c.reference_frames * c.grid_h * c.grid_w, c.heads, c.head_dim)
+
+    def set_reference(self, layer: int, k, v):
+        shp = self.reference_shape
+        _check(lib().bkv_set_reference(self._h, layer, self._tensor(k, "k", shp, self.dtype),
+                                       self._tensor(v, "v", shp, self.dtype), self._s()), "bkv_set_reference")
 
     def retrieve(self, pose=None):
         p = None if pose is None else self._tensor(pose, "pose", (self.config.pose_dim,), self._torch.float32)

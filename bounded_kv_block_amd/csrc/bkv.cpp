@@ -47,6 +47,8 @@ struct Layout {
   bool kf8;                          // FP8 key cache: E4M3 K rows + tile exponents in a slot
   size_t slot_kx_off;                // byte offset of the exponents [H][Tpad/64] inside a slot
   size_t off_q;                      // bf16: q scratch [T][H][D] of the fused projection path
+  int ref_tok, ref_pad;              // reference frames: tokens, padded to whole key tiles
+  size_t ref_bytes, ref_v_off, ref_kx_off, off_ref, off_tref;   // per layer, slot-shaped
 };
 
 bkv_status validate(const bkv_config* c) {
@@ -83,7 +85,12 @@ bkv_status validate(const bkv_config* c) {
     if (c->dynamic_k > 0 && (c->pose_dim < 1 || c->pose_dim > 1024))
       return fail(BKV_ERR_ARG, "pose_dim must be 1..1024 when dynamic_k > 0");
     if (c->pose_dim < 0) return fail(BKV_ERR_ARG, "pose_dim must be >= 0");
+    if (c->reference_frames < 0 || c->reference_frames > 8)
+      return fail(BKV_ERR_ARG, "reference_frames must be 0..8");
+    if ((c->reference_frames > 0) + c->static_blocks + c->dynamic_k + c->window_blocks + 1 > bkv::kMaxSeg)
+      return fail(BKV_ERR_ARG, "more than %d context segments", bkv::kMaxSeg);
   } else {
+    if (c->reference_frames != 0) return fail(BKV_ERR_UNSUPPORTED, "reference frames are implemented for PR-Sink only");
     if (c->static_blocks != 0 || c->dynamic_k != 0 || c->bank_blocks != 0)
       return fail(BKV_ERR_ARG, "ConvKV takes no static/dynamic sinks or bank");
     if (c->conv_kernel < 1 || c->conv_kernel > 8 || c->conv_stride != c->conv_kernel)
@@ -106,6 +113,7 @@ bkv::Schedule::Shape shape_of(const bkv_config* c) {
   s.bank = s.convkv ? 0 : c->bank_blocks;
   s.kernel = s.convkv ? c->conv_kernel : 1;
   s.memory_frames = s.convkv ? c->memory_frames : 0;
+  s.ref_frames = s.convkv ? 0 : c->reference_frames;
   return s;
 }
 
@@ -129,9 +137,22 @@ Layout layout_of(const bkv_config* c, const bkv::Schedule& sch) {
     L.slot_bytes = 2 * L.slot_v_off;
   }
   L.layer_kv_bytes = L.slot_bytes * L.n_slots;
+  // reference frames: one slot-shaped region per layer holding ref_pad tokens
+  L.ref_tok = sch.ref_tokens();
+  L.ref_pad = (int)align_up(L.ref_tok, bkv::kTokAlign);
+  if (L.kf8) {
+    L.ref_kx_off = H * L.ref_pad * D;
+    L.ref_v_off = align_up(L.ref_kx_off + sizeof(int) * H * (L.ref_pad / bkv::kTokAlign), 256);
+    L.ref_bytes = align_up(L.ref_v_off + H * L.ref_pad * D * 2, 256);
+  } else {
+    L.ref_v_off = align_up(H * L.ref_pad * D * L.esize, 256);
+    L.ref_bytes = align_up(L.ref_v_off + H * L.ref_pad * D * L.esize, 256);
+  }
   size_t off = 0;
   L.off_kv = off;
   off = align_up(off + L.layer_kv_bytes * c->layers, 256);
+  L.off_ref = off;
+  if (L.ref_tok > 0) off = align_up(off + L.ref_bytes * c->layers, 256);
   L.off_ctx = off;
   L.off_mem = off;
   if (c->mode == BKV_CONVKV) {
@@ -153,6 +174,8 @@ Layout layout_of(const bkv_config* c, const bkv::Schedule& sch) {
   L.t_rows = c->mode == BKV_CONVKV ? sch.max_context_frames() : c->frames_per_block;
   L.off_tt = off;
   off = align_up(off + sizeof(float2) * (size_t)L.t_rows * (c->rope_t / 2 + 1), 256);
+  L.off_tref = off;
+  if (L.ref_tok > 0) off = align_up(off + sizeof(float2) * (size_t)c->reference_frames * (c->rope_t / 2 + 1), 256);
   L.off_th = off;
   off = align_up(off + sizeof(float2) * (size_t)c->grid_h * (c->rope_h / 2 + 1), 256);
   L.off_tw = off;
@@ -182,6 +205,7 @@ struct bkv_cache_s {
   bool error = false;
   std::vector<bool> ctx_ready;      // ConvKV: context K of the layer gathered for the open block
   std::vector<bool> weights_set;    // ConvKV: conv weights given per layer
+  std::vector<bool> ref_set;        // PR-Sink: reference frames given per layer
   int64_t split_attends = 0;        // bf16 attention launches that used the split launch
   struct Prof {                     // per-launch HIP event pairs (bkv_profile_start/stop)
     bool on = false;
@@ -195,6 +219,7 @@ struct bkv_cache_s {
     L = layout_of(&c, sched);
     ctx_ready.assign(c.layers, false);
     weights_set.assign(c.layers, false);
+    ref_set.assign(c.layers, false);
   }
 
   bool bf16() const { return cfg.dtype != BKV_F32; }   // bf16 Q/K/V/out and V cache
@@ -218,6 +243,10 @@ struct bkv_cache_s {
     const size_t n = (size_t)cfg.heads * cfg.head_dim * cfg.conv_kernel;
     return reinterpret_cast<float*>(ws + L.off_w) + (2 * (size_t)l + which) * n;
   }
+  char* ref_k(int l) const { return ws + L.off_ref + L.ref_bytes * l; }
+  char* ref_vt(int l) const { return ref_k(l) + L.ref_v_off; }
+  int* ref_kx(int l) const { return reinterpret_cast<int*>(ref_k(l) + L.ref_kx_off); }
+  float2* tref() const { return reinterpret_cast<float2*>(ws + L.off_tref); }
   long long slot_k_hs() const { return (long long)L.Tpad * cfg.head_dim; }
   long long slot_v_hs() const { return (long long)L.Tpad * cfg.head_dim; }
 
@@ -240,7 +269,16 @@ struct bkv_cache_s {
     g.n = p.tokens;
     g.dyn = p.dyn;
     if (p.dyn >= 0) return g;
-    if (!convkv()) {
+    if (p.kind == bkv::SEG_REFERENCE) {
+      g.k = ref_k(l);
+      g.v = ref_vt(l);
+      g.k_hs = g.v_hs = (long long)L.ref_pad * cfg.head_dim;
+      g.v_ld = L.ref_pad;
+      if (kf8()) {
+        g.kx = ref_kx(l);
+        g.kx_hs = L.ref_pad / bkv::kTokAlign;
+      }
+    } else if (!convkv()) {
       g.k = slot_k(l, p.slot);
       g.v = slot_vt(l, p.slot);
       g.k_hs = slot_k_hs();
@@ -403,6 +441,8 @@ bkv_status bkv_create(const bkv_config* cfg, void* workspace, size_t bytes, hipS
     e = bkv::launch_rope_table(h->wtab(), cfg->grid_w, cfg->rope_w, 0, theta, stream);
   if (e == hipSuccess && cfg->rope_t && h->convkv())
     e = bkv::launch_rope_table(h->ttab(), h->L.t_rows, cfg->rope_t, 0, theta, stream);
+  if (e == hipSuccess && cfg->rope_t && h->L.ref_tok > 0)
+    e = bkv::launch_rope_table(h->tref(), cfg->reference_frames, cfg->rope_t, 0, theta, stream);
   if (e != hipSuccess) {
     delete h;
     return fail(BKV_ERR_DEVICE, "RoPE table launch: %s", hipGetErrorString(e));
@@ -451,6 +491,43 @@ bkv_status bkv_set_conv_weights(bkv_cache h, int32_t layer, const float* wk, con
   return BKV_OK;
 }
 
+bkv_status bkv_set_reference(bkv_cache h, int32_t layer, const void* k, const void* v, hipStream_t stream) {
+  bkv_status st = check_handle(h);
+  if (st != BKV_OK) return st;
+  if (h->L.ref_tok == 0) return fail(BKV_ERR_UNSUPPORTED, "the handle has no reference frames");
+  if (h->sched.is_open()) return fail(BKV_ERR_STATE, "reference set while block %lld is open",
+                                      (long long)h->sched.block());
+  if (layer < 0 || layer >= h->cfg.layers) return fail(BKV_ERR_ARG, "layer %d out of range", layer);
+  if (!k || !v) return fail(BKV_ERR_ARG, "null k or v");
+  if (k == v) return fail(BKV_ERR_ARG, "k aliases v");
+  if ((st = set_device(h)) != BKV_OK) return st;
+  bkv::AppendArgs ap{};
+  ap.k_in = k;
+  ap.v_in = v;
+  ap.T = h->L.ref_tok;
+  ap.H = h->cfg.heads;
+  ap.D = h->cfg.head_dim;
+  ap.rope = h->rope();
+  ap.rope.t = h->tref();              // frame f of the reference at t = f
+  ap.t_row0 = 0;
+  ap.vt = h->ref_vt(layer);
+  ap.vt_hs = (long long)h->L.ref_pad * h->cfg.head_dim;
+  ap.vt_ld = h->L.ref_pad;
+  if (h->kf8()) {
+    ap.k8 = h->ref_k(layer);
+    ap.k8_hs = ap.vt_hs;
+    ap.kx = h->ref_kx(layer);
+    ap.kx_hs = h->L.ref_pad / bkv::kTokAlign;
+  } else {
+    ap.k_rot = h->ref_k(layer);
+    ap.k_rot_hs = ap.vt_hs;
+  }
+  hipError_t e = timed(h, K_APPEND, stream, [&] { return bkv::launch_append(ap, h->bf16(), stream); });
+  if (e != hipSuccess) return device_fail(h, e, "reference append launch");
+  h->ref_set[layer] = true;
+  return BKV_OK;
+}
+
 bkv_status bkv_retrieve(bkv_cache h, const float* pose, hipStream_t stream) {
   bkv_status st = check_handle(h);
   if (st != BKV_OK) return st;
@@ -461,6 +538,10 @@ bkv_status bkv_retrieve(bkv_cache h, const float* pose, hipStream_t stream) {
   if (h->convkv()) {
     for (int l = 0; l < h->cfg.layers; ++l)
       if (!h->weights_set[l]) return fail(BKV_ERR_STATE, "conv weights of layer %d not set", l);
+  }
+  if (h->L.ref_tok > 0) {
+    for (int l = 0; l < h->cfg.layers; ++l)
+      if (!h->ref_set[l]) return fail(BKV_ERR_STATE, "reference frames of layer %d not set", l);
   }
   if ((st = set_device(h)) != BKV_OK) return st;
   if (!h->sched.open()) return fail(BKV_ERR_STATE, "no free slot (internal)");
@@ -483,7 +564,7 @@ bkv_status bkv_retrieve(bkv_cache h, const float* pose, hipStream_t stream) {
       a.ttab = h->ttab();
       a.t_rows = h->cfg.frames_per_block;
       a.t_dim = h->cfg.rope_t;
-      a.t_pos0 = h->sched.block() * h->cfg.frames_per_block;
+      a.t_pos0 = h->sched.block_t0(h->sched.block());
       a.theta = h->cfg.rope_theta;
     }
     if (a.pose_in || a.ttab || a.k > 0) {
@@ -707,7 +788,7 @@ bkv_status bkv_context(bkv_cache h, bkv_segment* segs, int32_t cap, int32_t* n, 
     segs[i].tokens = p.tokens;
     if (p.dyn >= 0) {
       segs[i].id = ids[p.dyn];
-      segs[i].t0 = ids[p.dyn] * h->cfg.frames_per_block;
+      segs[i].t0 = (int32_t)h->sched.block_t0(ids[p.dyn]);
     } else {
       segs[i].id = (int32_t)p.id;
       segs[i].t0 = (int32_t)p.t0;

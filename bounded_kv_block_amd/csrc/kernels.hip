@@ -495,7 +495,7 @@ void attn_bf16_kernel(AttnArgs a) {
       Seg sg;
 #pragma unroll
       for (int w = 0; w < AWAVES; ++w)
-        if (w == wave) sg = a.seg[g + w];
+        if (g + w < kMaxSeg && w == wave) sg = a.seg[g + w];
       const char* kb;
       const char* vb;
       long long khs, vhs;

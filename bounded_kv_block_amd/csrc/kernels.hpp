@@ -13,7 +13,7 @@
 
 namespace bkv {
 
-constexpr int kMaxSeg = 16;     // context segments per block (static+dynamic+window+current)
+constexpr int kMaxSeg = 20;     // context segments per block (reference+static+dynamic+window+current)
 constexpr int kMaxBank = 256;   // PR-Sink bank capacity
 constexpr int kMaxK = 8;        // dynamic sinks per block
 constexpr int kMaxTaps = 32;    // ConvKV: conv_kernel * memory_frames source frames

@@ -11,6 +11,10 @@
 // stride=kernel temporal conv whose output (memory_frames frames) is rebuilt
 // at each commit from the newest kernel*memory_frames evicted frames.
 //
+// Reference frames (PR-Sink, ref_frames = R > 0): a permanent first segment
+// (outside the slots) at temporal positions 0..R-1; generated blocks then sit
+// at t0 = R + id * frames.
+//
 // Slots: every block in the cache occupies one slot (K and V of every layer).
 // A block keeps its slot until it leaves the cache, so a commit moves ids
 // between lists and never copies tensor data.
@@ -23,14 +27,15 @@
 
 namespace bkv {
 
-enum SegKind { SEG_STATIC = 0, SEG_DYNAMIC = 1, SEG_WINDOW = 2, SEG_CURRENT = 3, SEG_MEMORY = 4 };
+enum SegKind { SEG_STATIC = 0, SEG_DYNAMIC = 1, SEG_WINDOW = 2, SEG_CURRENT = 3, SEG_MEMORY = 4,
+               SEG_REFERENCE = 5 };
 
 struct SegPlan {
   int kind;
-  int64_t id;       // block id; memory: frame index; dynamic: -1 (known on device only)
+  int64_t id;       // block id; memory: frame index; dynamic, reference: -1
   int tokens;
   int64_t t0;       // temporal RoPE position of the segment's first frame
-  int slot;         // slot id, -1 for memory and dynamic segments
+  int slot;         // slot id, -1 for memory, dynamic and reference segments
   int dyn;          // dynamic: rank index into the device selection, else -1
   int ctx_off;      // ConvKV: row offset in the context-K buffer, else 0
 };
@@ -44,6 +49,7 @@ class Schedule {
     int layers, frames, tokens_per_frame;   // T = frames * tokens_per_frame
     int window, statics, k, bank;
     int kernel, memory_frames;
+    int ref_frames;                         // PR-Sink reference frames (0 = none)
   };
 
   explicit Schedule(const Shape& s) : s_(s) {
@@ -65,11 +71,15 @@ class Schedule {
   // Largest context the handle can see: sizes the ConvKV context-K buffer.
   int max_context_tokens() const {
     if (s_.convkv) return s_.memory_frames * s_.tokens_per_frame + (s_.window + 1) * T_;
-    return (s_.statics + s_.k + s_.window + 1) * T_;
+    return ref_tokens() + (s_.statics + s_.k + s_.window + 1) * T_;
   }
   int max_segments() const {
-    return s_.convkv ? s_.memory_frames + s_.window + 1 : s_.statics + s_.k + s_.window + 1;
+    return s_.convkv ? s_.memory_frames + s_.window + 1
+                     : (s_.ref_frames > 0) + s_.statics + s_.k + s_.window + 1;
   }
+  int ref_tokens() const { return s_.convkv ? 0 : s_.ref_frames * s_.tokens_per_frame; }
+  // Temporal position of block b's first frame (PR-Sink).
+  int64_t block_t0(int64_t b) const { return (s_.convkv ? 0 : s_.ref_frames) + b * s_.frames; }
   // Temporal positions the ConvKV context uses: 0 .. max_context_frames()-1.
   int max_context_frames() const { return s_.memory_frames + (s_.window + 1) * s_.frames; }
 
@@ -199,10 +209,11 @@ class Schedule {
     const int64_t m = next_;
     const int F = s_.frames;
     if (!s_.convkv) {
-      for (auto& st : static_) segs_.push_back({SEG_STATIC, st.first, T_, st.first * F, st.second, -1, 0});
+      if (s_.ref_frames > 0) segs_.push_back({SEG_REFERENCE, -1, ref_tokens(), 0, -1, -1, 0});
+      for (auto& st : static_) segs_.push_back({SEG_STATIC, st.first, T_, block_t0(st.first), st.second, -1, 0});
       for (int j = 0; j < n_dynamic(); ++j) segs_.push_back({SEG_DYNAMIC, -1, T_, -1, -1, j, 0});
-      for (auto& w : window_) segs_.push_back({SEG_WINDOW, w.first, T_, w.first * F, w.second, -1, 0});
-      segs_.push_back({SEG_CURRENT, m, T_, m * F, cur_slot_, -1, 0});
+      for (auto& w : window_) segs_.push_back({SEG_WINDOW, w.first, T_, block_t0(w.first), w.second, -1, 0});
+      segs_.push_back({SEG_CURRENT, m, T_, block_t0(m), cur_slot_, -1, 0});
     } else {
       const int n_mem = memory_count();
       const int Tf = s_.tokens_per_frame;

@@ -80,7 +80,8 @@ typedef enum {
   BKV_SEG_DYNAMIC = 1,  /* pose-retrieved bank block */
   BKV_SEG_WINDOW = 2,   /* rolling-window block */
   BKV_SEG_CURRENT = 3,  /* the open block */
-  BKV_SEG_MEMORY = 4    /* ConvKV compressed memory frame */
+  BKV_SEG_MEMORY = 4,   /* ConvKV compressed memory frame */
+  BKV_SEG_REFERENCE = 5 /* PR-Sink reference frames (reference_frames > 0), id -1 */
 } bkv_segment_kind;
 
 /* Cache configuration.  Set struct_size = sizeof(bkv_config) (ABI guard). */
@@ -105,6 +106,9 @@ typedef struct {
   int32_t conv_stride;      /* ConvKV: stride (5) */
   int32_t memory_frames;    /* ConvKV: compressed frames kept, 1..4 */
   float softmax_scale;      /* 0 -> 1/sqrt(head_dim) */
+  int32_t reference_frames; /* PR-Sink: reference latent frames R kept as a permanent first
+                               context segment, 0..8 (0 = none); ConvKV: 0.  See
+                               bkv_set_reference. */
 } bkv_config;
 
 /* One context segment as the open block sees it (host view). */
@@ -113,7 +117,8 @@ typedef struct {
   int32_t id;      /* block stream id; memory: memory-frame index */
   int32_t tokens;  /* keys contributed */
   int32_t t0;      /* RoPE temporal position of the segment's first frame (PR-Sink: absolute
-                      id*frames_per_block; ConvKV: context-relative) */
+                      reference_frames + id*frames_per_block, the reference segment 0;
+                      ConvKV: context-relative) */
 } bkv_segment;
 
 typedef struct {
@@ -158,8 +163,26 @@ bkv_status bkv_reset(bkv_cache h);
 bkv_status bkv_set_conv_weights(bkv_cache h, int32_t layer, const float* wk, const float* wv,
                                 hipStream_t stream);
 
+/* PR-Sink with reference_frames R > 0: set layer's reference frames.  The
+   LiveAnimate page (section 方法) conditions every block on the reference
+   image, and the Live Avatar page (abstract) recalibrates appearance from a
+   cached reference image; this library reads that as R latent frames of
+   grid_h x grid_w tokens that every block attends to, first in its context,
+   at temporal RoPE positions 0..R-1 (token (f*grid_h + y)*grid_w + x at
+   (f, y, x)), while frame f of generated block b moves to R + b*frames_per_block
+   + f.  k, v: device, dtype, contiguous [R*grid_h*grid_w][heads][head_dim];
+   K is rotated and stored (E4M3 with per-64-token tile scales for
+   BKV_BF16_FP8K, as for blocks) and V stored on `stream`; the caller's
+   buffers may be reused once that work ran.  Call it for every layer before
+   the first bkv_retrieve; it may be called again (no block open) to replace
+   the reference.  bkv_reset keeps it.
+   Errors: BKV_ERR_UNSUPPORTED if reference_frames is 0; BKV_ERR_STATE while a
+   block is open; BKV_ERR_ARG (layer, null pointer, k aliasing v). */
+bkv_status bkv_set_reference(bkv_cache h, int32_t layer, const void* k, const void* v, hipStream_t stream);
+
 /* Open the next block m (pose retrieval; LiveAnimate page, section 方法, Dynamic
-   Sink bullet).  pose: device fp32 [pose_dim], the block's pose embedding; it is
+   Sink bullet).  With reference_frames > 0, BKV_ERR_STATE until the reference
+   of every layer is set.  pose: device fp32 [pose_dim], the block's pose embedding; it is
    stored with the block for later retrieval.  Selects the top-min(dynamic_k,
    bank_count) bank blocks by cosine similarity to `pose` (fp64 arithmetic;
    exact ties to the lower stream id; a zero-norm pose scores 0) on the device:

@@ -14,6 +14,10 @@ void* sched_new(int convkv, int layers, int frames, int tpf, int window, int sta
   Schedule::Shape s{convkv != 0, layers, frames, tpf, window, statics, k, bank, kernel, memory_frames};
   return new Schedule(s);
 }
+void* sched_new_ref(int layers, int frames, int tpf, int window, int statics, int k, int bank, int ref_frames) {
+  Schedule::Shape s{false, layers, frames, tpf, window, statics, k, bank, 1, 0, ref_frames};
+  return new Schedule(s);
+}
 void sched_free(void* p) { delete static_cast<Schedule*>(p); }
 int sched_n_slots(void* p) { return static_cast<Schedule*>(p)->n_slots(); }
 int sched_open(void* p) { return static_cast<Schedule*>(p)->open() ? 1 : 0; }

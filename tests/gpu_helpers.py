@@ -35,6 +35,15 @@ class Run:
                 self._w[l] = (wk, wv)
                 self.cache.set_conv_weights(l, torch.from_numpy(wk).to(self.device),
                                             torch.from_numpy(wv).to(self.device))
+        self._ref = {}
+        if cfg.get("reference_frames"):
+            for l in range(cfg["layers"]):
+                self._ref[l] = synth.reference(cfg, l)
+                self.set_reference(l)
+
+    def set_reference(self, layer):
+        k, v = (self.torch.from_numpy(a).to(self.device).to(self.dt) for a in self._ref[layer])
+        self.cache.set_reference(layer, k, v)
 
     # ---- inputs
     def qkv_dev(self, layer, block, step):
@@ -74,6 +83,9 @@ class Run:
 
     def conv_weights(self, layer):
         return self._w[layer]
+
+    def reference(self, layer):
+        return self._ref[layer]
 
     # ---- driving
     def open(self, m):

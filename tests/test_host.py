@@ -24,6 +24,8 @@ def shim(tmp_path_factory):
     L = ctypes.CDLL(out)
     L.sched_new.restype = ctypes.c_void_p
     L.sched_new.argtypes = [ctypes.c_int] * 10
+    L.sched_new_ref.restype = ctypes.c_void_p
+    L.sched_new_ref.argtypes = [ctypes.c_int] * 8
     for n in ("sched_free",):
         getattr(L, n).argtypes = [ctypes.c_void_p]
     for n in ("sched_n_slots", "sched_open", "sched_cur_slot", "sched_memory_count", "sched_n_dynamic"):
@@ -44,6 +46,10 @@ class Sched:
     def __init__(self, L, **kw):
         self.L = L
         self.layers = kw.get("layers", 1)
+        if kw.get("ref_frames"):
+            self.p = L.sched_new_ref(self.layers, kw["frames"], kw["tpf"], kw["window"], kw.get("statics", 0),
+                                     kw.get("k", 0), kw.get("bank", 0), kw["ref_frames"])
+            return
         args = [kw.get("convkv", 0), self.layers, kw["frames"], kw["tpf"], kw["window"], kw.get("statics", 0),
                 kw.get("k", 0), kw.get("bank", 0), kw.get("kernel", 1), kw.get("memory_frames", 0)]
         self.p = L.sched_new(*args)
@@ -70,7 +76,7 @@ class Sched:
         return ok, [(ts[i], tf[i]) for i in range(n.value)]
 
 
-STATIC, DYNAMIC, WINDOW, CURRENT, MEMORY = range(5)
+STATIC, DYNAMIC, WINDOW, CURRENT, MEMORY, REFERENCE = range(6)
 
 
 @pytest.mark.parametrize("W,B,S,k", [(3, 8, 1, 1), (3, 56, 1, 2), (3, 16, 1, 2), (3, 64, 1, 2), (3, 0, 0, 0),
@@ -116,6 +122,28 @@ def test_prsink_state_machine_matches_oracle(shim, W, B, S, k):
         assert ok == 1 and taps == []
         ev = shim.sched_last_evicted(s.p)
         assert ev == (-1 if want["evicted"] is None else want["evicted"])
+
+
+@pytest.mark.parametrize("R", [1, 3])
+def test_prsink_reference_segment(shim, R):
+    """Reference frames: one permanent first segment of R * tokens-per-frame
+    keys at t0 = 0 (no slot); every block's t0 moves to R + id * frames; slots
+    and the rest of the context are as without it."""
+    F, tpf, W, B, S, k = 3, 4, 3, 8, 1, 2
+    s = Sched(shim, frames=F, tpf=tpf, window=W, statics=S, k=k, bank=B, ref_frames=R)
+    s0 = Sched(shim, frames=F, tpf=tpf, window=W, statics=S, k=k, bank=B)
+    assert shim.sched_n_slots(s.p) == shim.sched_n_slots(s0.p) == S + W + 1 + B
+    for m in range(30):
+        assert shim.sched_open(s.p) == 1 and shim.sched_open(s0.p) == 1
+        segs, segs0 = s.segments(), s0.segments()
+        assert segs[0] == (REFERENCE, -1, R * tpf, 0, -1, -1, 0)
+        assert len(segs) == len(segs0) + 1
+        for g, g0 in zip(segs[1:], segs0):
+            assert g[:3] == g0[:3] and g[4:] == g0[4:]
+            assert g[3] == (-1 if g[0] == DYNAMIC else R + g[1] * F)
+        for x in (s, s0):
+            shim.sched_mark(x.p, 0)
+            assert x.commit()[0] == 1
 
 
 @pytest.mark.parametrize("F,tpf,W,K,M", [(3, 4, 3, 5, 1), (2, 3, 3, 5, 1), (1, 5, 2, 3, 2), (4, 2, 3, 5, 2),
@@ -248,3 +276,32 @@ def test_workspace_is_constant_in_stream_length():
     a = bkv.workspace_size(bkv.config_from_workload(synth.workload("prsink_long")))
     b = bkv.workspace_size(bkv.config_from_workload(synth.workload("prsink_long", blocks=60)))
     assert a == b
+
+
+def test_reference_frames_workspace_and_validation():
+    """Reference frames: one slot-shaped region per layer of R * grid_h * grid_w
+    keys padded to a 64-key tile, plus an R-row temporal RoPE table; PR-Sink
+    only, 0..8 frames; the largest context (reference, static, 8 dynamic, a
+    window of 8, current) fits the segment limit."""
+    from bounded_kv_block_amd import bkv, synth
+    n0 = bkv.workspace_size(bkv.config_from_workload(synth.workload("prsink_512")))
+    n1 = bkv.workspace_size(bkv.config_from_workload(synth.workload("prsink_512_ref")))
+    H, D = 40, 128
+    assert n1 - n0 == 2 * H * 1024 * D * 2 + 256        # K + V^T of 1024 tokens, 1-row table (one 256 B block)
+    n8 = bkv.workspace_size(bkv.config_from_workload(synth.workload("prsink_512_fp8k")))
+    n8r = bkv.workspace_size(bkv.config_from_workload(synth.workload("prsink_512_fp8k", reference_frames=2)))
+    kx = -(-(4 * H * 2048 // 64) // 256) * 256
+    assert n8r - n8 == H * 2048 * D + kx + H * 2048 * D * 2 + 512   # 2 x 23 (cos, sin) pairs -> 512 B
+    nodd = bkv.workspace_size(bkv.config_from_workload(synth.workload("tiny_fp32", grid_h=3, grid_w=5,
+                                                                      reference_frames=1)))
+    n0dd = bkv.workspace_size(bkv.config_from_workload(synth.workload("tiny_fp32", grid_h=3, grid_w=5)))
+    assert nodd - n0dd >= 2 * 2 * 64 * 64 * 4            # 15 keys padded to one 64-key tile
+    big = synth.workload("prsink_512", reference_frames=8, window=8, dynamic_k=8, bank=64)
+    assert bkv.workspace_size(bkv.config_from_workload(big)) > 0
+    for b, st in ((dict(reference_frames=9), bkv.BKV_ERR_ARG), (dict(reference_frames=-1), bkv.BKV_ERR_ARG)):
+        with pytest.raises(bkv.BkvError) as ei:
+            bkv.workspace_size(bkv.config_from_workload(synth.workload("prsink_512", **b)))
+        assert ei.value.status == st, b
+    with pytest.raises(bkv.BkvError) as ei:
+        bkv.workspace_size(bkv.config_from_workload(synth.workload("convkv_512", reference_frames=1)))
+    assert ei.value.status == bkv.BKV_ERR_UNSUPPORTED
