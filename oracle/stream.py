@@ -24,6 +24,13 @@ Readings (beyond those stated in the modules used here):
     reference frames are a permanent first context segment at temporal
     positions 0..R-1, and generated frame f of block b moves to t = R + b *
     frames + f.  R = 0 is the plain reading above.
+  * PR-Sink with positions = "relative" (the alternative to absolute
+    positions: the SoulX-LiveAct page, section 技术内核, restarts RoPE over
+    the retained context for ConvKV): the context's blocks keep their temporal
+    order with the gaps between them removed -- the i-th context block by
+    stream id (static, retrieved, window, current) has its frame f at
+    t = R + i * frames + f.  Keys are rotated per block at these positions,
+    not once at append.
 """
 from __future__ import annotations
 
@@ -54,6 +61,7 @@ class _Base:
         self.split = tuple(cfg["rope"])
         self.theta = float(cfg.get("theta", 10000.0))
         self.R = int(cfg.get("reference_frames", 0) or 0)
+        self.relative = cfg.get("positions", "absolute") == "relative"
 
     def _rot(self, x, t_of_frame, heads, tok=None):
         """Rotate x [N, H, D] (tokens ``tok`` of a block, default all) with t = t_of_frame(f)."""
@@ -90,6 +98,10 @@ class PRSinkReference(_Base):
         sel = self.selection(m) if selection is None else selection
         F, T = self.F, self.T
         t = self.block_t0
+        if self.relative:       # consecutive frames in stream-id order, after the reference
+            ids = sorted(set(sch["static"]) | set(sel) | set(sch["window"]) | {m})
+            rank = {b: i for i, b in enumerate(ids)}
+            t = lambda b: self.R + rank[b] * F
         segs = [("reference", -1, self.R * self.Tf, 0)] if self.R > 0 else []
         segs += [("static", b, T, t(b)) for b in sch["static"]]
         segs += [("dynamic", b, T, t(b)) for b in sel]
@@ -98,7 +110,7 @@ class PRSinkReference(_Base):
         return segs
 
     def block_t0(self, b: int) -> int:
-        """Temporal position of block b's first frame (after the reference frames)."""
+        """Absolute temporal position of block b's first frame (after the reference frames)."""
         return self.R + b * self.F
 
     def context_kv(self, m: int, layer: int, step: int, heads, selection=None):
@@ -121,8 +133,11 @@ class PRSinkReference(_Base):
         """Output [T, len(heads), D] fp64 of block m at (layer, step)."""
         H = self.cfg["heads"]
         heads = list(range(H)) if heads is None else list(heads)
+        if selection is None:
+            selection = self.selection(m)
+        t0 = self.context(m, selection)[-1][3]
         q, _, _ = self.p.qkv(layer, m, step)
-        q_rot = self._rot(q, lambda f: self.block_t0(m) + f, heads)
+        q_rot = self._rot(q, lambda f: t0 + f, heads)
         kv = self.context_kv(m, layer, step, heads, selection)
         if self.cfg["dtype"] != "bf16_fp8k":
             return self._attend(q_rot, [x[2] for x in kv], [x[3] for x in kv], heads, rows)

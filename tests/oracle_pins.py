@@ -369,3 +369,49 @@ def check_prsink_reference(Ref, token_positions, apply_rope, masked_attention, m
             want = masked_attention(qr, np.concatenate(ks), np.concatenate(vs), mask)
             got = ref.attend(m, 0, 0)
             assert np.allclose(got, want, atol=1e-12, rtol=0), (R, m)
+
+
+# ------------------------------------------------- context-relative positions
+def check_prsink_relative(Ref, token_positions, apply_rope, make_cfg, make_provider):
+    """PR-Sink with context-relative positions: block m's output equals torch
+    SDPA (fp64) over one clip made of the context's frames -- the reference
+    frames, then the frames of every context block in stream-id order (the
+    hand-derived static and window blocks, the retrieved ones, block m) --
+    rotated by plain 3D RoPE at the clip's own frame indices, with the
+    queries at the clip's last frames.  The stream must retrieve out of id
+    order at least once, so that the order is pinned."""
+    import torch
+    golden = {int(r[0]): r for r in read_table("prsink_schedule_w3_b8_s1.txt")}
+    for R in (0, 1):
+        cfg = make_cfg(R)
+        prov = make_provider(cfg)
+        ref = Ref(cfg, prov)
+        F, gh, gw = cfg["frames"], cfg["grid_h"], cfg["grid_w"]
+        last = cfg["steps"] - 1
+        unordered = 0
+        for m in range(cfg["blocks"]):
+            sel = ref.selection(m)
+            unordered += sel != sorted(sel)
+            blocks = sorted(set(ids(golden[m][1])) | set(sel) | set(ids(golden[m][3])) | {m})
+            ks, vs = [], []
+            if R:
+                k_ref, v_ref = prov.reference(0)
+                ks.append(np.asarray(k_ref, np.float64))
+                vs.append(np.asarray(v_ref, np.float64))
+            for b in blocks:
+                _, k, v = prov.qkv(0, b, last if b < m else 0)
+                ks.append(np.asarray(k, np.float64))
+                vs.append(np.asarray(v, np.float64))
+            k_clip, v_clip = np.concatenate(ks), np.concatenate(vs)
+            n_frames = R + len(blocks) * F
+            f, y, x = token_positions(n_frames, gh, gw)
+            assert f.size == k_clip.shape[0]
+            kr = apply_rope(k_clip, f.astype(np.float64), y, x, cfg["rope"])
+            q, _, _ = prov.qkv(0, m, 0)
+            nq = q.shape[0]
+            qr = apply_rope(np.asarray(q, np.float64), f[-nq:].astype(np.float64), y[-nq:], x[-nq:], cfg["rope"])
+            t = lambda a: torch.from_numpy(np.ascontiguousarray(a.transpose(1, 0, 2)))[None]
+            want = torch.nn.functional.scaled_dot_product_attention(t(qr), t(kr), t(v_clip))[0].numpy()
+            got = ref.attend(m, 0, 0)
+            assert np.allclose(got, want.transpose(1, 0, 2), atol=1e-12, rtol=0), (R, m)
+        assert unordered > 0

@@ -167,6 +167,26 @@ def test_prsink_reference_block0_is_plain_attention():
     assert np.allclose(got, ref, atol=1e-12)
 
 
+def _rel_cfg(R):
+    return synth.workload("tiny_fp32", rope=(24, 20, 20), reference_frames=R, dynamic_k=2, positions="relative")
+
+
+def test_prsink_relative_equals_compacted_clip():
+    pins.check_prsink_relative(oracle.PRSinkReference, oracle.token_positions, oracle.apply_rope, _rel_cfg,
+                               SynthProvider)
+
+
+def test_prsink_relative_equals_absolute_in_warmup():
+    """While the context is every block so far (no gaps), context-relative and
+    absolute positions coincide, so the outputs are identical."""
+    a = synth.workload("tiny_fp32", rope=(24, 20, 20), dynamic_k=2)
+    r = dict(a, positions="relative")
+    ra, rr = oracle.PRSinkReference(a, SynthProvider(a)), oracle.PRSinkReference(r, SynthProvider(r))
+    for m in range(5):
+        assert np.array_equal(ra.attend(m, 0, 0), rr.attend(m, 0, 0)), m
+    assert not np.allclose(ra.attend(8, 0, 0), rr.attend(8, 0, 0), atol=1e-6)
+
+
 def test_prsink_block0_is_plain_attention():
     import torch
     cfg = synth.workload("tiny_fp32")
