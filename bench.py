@@ -37,7 +37,8 @@ def parse():
     ap.add_argument("--steps", type=int, default=40)
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--workload", default="prsink_512",
-                    choices=["prsink_512", "prsink_512_fp8k", "prsink_512_qkv", "prsink_512_ref", "prsink_720x416",
+                    choices=["prsink_512", "prsink_512_fp8k", "prsink_512_qkv", "prsink_512_ref", "prsink_512_rel",
+                             "prsink_720x416",
                              "prsink_long", "convkv_512", "tiny_fp32"])
     ap.add_argument("--pool", type=int, default=4, help="distinct resident input blocks cycled through")
     ap.add_argument("--no-cpu-baseline", action="store_true")
@@ -311,8 +312,8 @@ def main():
         kernels["qkv"]["tflops"] = g_flop / (kernels["qkv"]["avg_us"] * 1e-6) / 1e12
         kernels["qkv"]["pct_peak"] = 100.0 * kernels["qkv"]["tflops"] / PEAK_BF16_TFLOPS
         kernels["qkv"]["flop_per_launch"] = g_flop
-    if "gather" in kernels:
-        ctx_rows = Nk - T
+    if "gather" in kernels:         # re-rotated rows: the context less the current block and the reference
+        ctx_rows = Nk - T - cfg.get("reference_frames", 0) * cfg["grid_h"] * cfg["grid_w"]
         g_bytes = 2.0 * ctx_rows * H * D * esz
         kernels["gather"]["gbs"] = g_bytes / (kernels["gather"]["avg_us"] * 1e-6) / 1e9
     if "conv" in kernels:
@@ -344,7 +345,8 @@ def main():
                    "dynamic_k": cfg["dynamic_k"], "bank": cfg["bank"], "rope": list(cfg["rope"]),
                    "timed_blocks": [m - args.steps, m - 1],
                    **({"model_dim": cfg["model_dim"], "qkv_projection": "fused (bkv_attend_qkv)"} if fused else {}),
-                   **({"reference_frames": cfg["reference_frames"]} if cfg.get("reference_frames") else {})},
+                   **({"reference_frames": cfg["reference_frames"]} if cfg.get("reference_frames") else {}),
+                   **({"positions": "context-relative"} if cfg.get("positions") == "relative" else {})},
         "attention_tflops": attn_tflops,
         "attention_pct_peak": 100.0 * attn_tflops / peak,
         "attention_peak_tflops": peak,

@@ -36,7 +36,8 @@ class Config(ctypes.Structure):
                 ("rope_t", ctypes.c_int32), ("rope_h", ctypes.c_int32), ("rope_w", ctypes.c_int32),
                 ("rope_theta", ctypes.c_double), ("conv_kernel", ctypes.c_int32),
                 ("conv_stride", ctypes.c_int32), ("memory_frames", ctypes.c_int32),
-                ("softmax_scale", ctypes.c_float), ("reference_frames", ctypes.c_int32)]
+                ("softmax_scale", ctypes.c_float), ("reference_frames", ctypes.c_int32),
+                ("rope_relative", ctypes.c_int32)]
 
 
 class Segment(ctypes.Structure):
@@ -131,6 +132,7 @@ def config_from_workload(w: dict) -> Config:
     c.conv_kernel, c.conv_stride, c.memory_frames = w["conv_kernel"], w["conv_stride"], w["memory_frames"]
     c.softmax_scale = float(w.get("softmax_scale", 0.0))
     c.reference_frames = int(w.get("reference_frames", 0) or 0)
+    c.rope_relative = 1 if w.get("positions", "absolute") == "relative" else 0
     return c
 
 

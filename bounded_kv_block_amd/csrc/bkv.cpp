@@ -87,10 +87,14 @@ bkv_status validate(const bkv_config* c) {
     if (c->pose_dim < 0) return fail(BKV_ERR_ARG, "pose_dim must be >= 0");
     if (c->reference_frames < 0 || c->reference_frames > 8)
       return fail(BKV_ERR_ARG, "reference_frames must be 0..8");
+    if (c->rope_relative != 0 && c->rope_relative != 1) return fail(BKV_ERR_ARG, "rope_relative must be 0 or 1");
+    if (c->rope_relative && c->dtype == BKV_BF16_FP8K)
+      return fail(BKV_ERR_UNSUPPORTED, "context-relative positions are implemented without the FP8 key cache");
     if ((c->reference_frames > 0) + c->static_blocks + c->dynamic_k + c->window_blocks + 1 > bkv::kMaxSeg)
       return fail(BKV_ERR_ARG, "more than %d context segments", bkv::kMaxSeg);
   } else {
     if (c->reference_frames != 0) return fail(BKV_ERR_UNSUPPORTED, "reference frames are implemented for PR-Sink only");
+    if (c->rope_relative != 0) return fail(BKV_ERR_ARG, "ConvKV positions are context-relative by definition; rope_relative must be 0");
     if (c->static_blocks != 0 || c->dynamic_k != 0 || c->bank_blocks != 0)
       return fail(BKV_ERR_ARG, "ConvKV takes no static/dynamic sinks or bank");
     if (c->conv_kernel < 1 || c->conv_kernel > 8 || c->conv_stride != c->conv_kernel)
@@ -114,6 +118,7 @@ bkv::Schedule::Shape shape_of(const bkv_config* c) {
   s.kernel = s.convkv ? c->conv_kernel : 1;
   s.memory_frames = s.convkv ? c->memory_frames : 0;
   s.ref_frames = s.convkv ? 0 : c->reference_frames;
+  s.relative = !s.convkv && c->rope_relative != 0;
   return s;
 }
 
@@ -155,12 +160,14 @@ Layout layout_of(const bkv_config* c, const bkv::Schedule& sch) {
   if (L.ref_tok > 0) off = align_up(off + L.ref_bytes * c->layers, 256);
   L.off_ctx = off;
   L.off_mem = off;
-  if (c->mode == BKV_CONVKV) {
+  if (sch.ctx_mode()) {
     // + one tile: the last segment's partial tile reads up to 63 rows past its end
-    L.ctx_ld = (int)align_up(sch.max_context_tokens(), bkv::kTokAlign) + bkv::kTokAlign;
+    L.ctx_ld = (int)align_up(sch.ctx_tokens(), bkv::kTokAlign) + bkv::kTokAlign;
     L.ctx_layer_bytes = align_up(H * L.ctx_ld * D * L.esize, 256);
     off = align_up(off + L.ctx_layer_bytes * c->layers, 256);
     L.off_mem = off;
+  }
+  if (c->mode == BKV_CONVKV) {
     L.mem_ld = L.tf_pad * c->memory_frames;
     L.mem_v_off = H * L.mem_ld * D * L.esize;
     L.mem_layer_bytes = align_up(2 * L.mem_v_off, 256);
@@ -171,7 +178,7 @@ Layout layout_of(const bkv_config* c, const bkv::Schedule& sch) {
   off = align_up(off + sizeof(float) * (size_t)L.n_slots * (P > 0 ? P : 1), 256);
   L.off_sel = off;
   off = align_up(off + 2 * sizeof(int) * bkv::kMaxK, 256);
-  L.t_rows = c->mode == BKV_CONVKV ? sch.max_context_frames() : c->frames_per_block;
+  L.t_rows = sch.ctx_mode() ? sch.max_context_frames() : c->frames_per_block;
   L.off_tt = off;
   off = align_up(off + sizeof(float2) * (size_t)L.t_rows * (c->rope_t / 2 + 1), 256);
   L.off_tref = off;
@@ -225,6 +232,9 @@ struct bkv_cache_s {
   bool bf16() const { return cfg.dtype != BKV_F32; }   // bf16 Q/K/V/out and V cache
   bool kf8() const { return L.kf8; }
   bool convkv() const { return cfg.mode == BKV_CONVKV; }
+  // ConvKV or context-relative PR-Sink: slots hold raw K; the context's K is
+  // rotated per block into the context-K buffer at context positions.
+  bool ctx_mode() const { return sched.ctx_mode(); }
   char* layer_kv(int l) const { return ws + L.off_kv + L.layer_kv_bytes * l; }
   char* slot_k(int l, int s) const { return layer_kv(l) + L.slot_bytes * s; }
   char* slot_vt(int l, int s) const { return slot_k(l, s) + L.slot_v_off; }
@@ -268,7 +278,13 @@ struct bkv_cache_s {
     bkv::Seg g{};
     g.n = p.tokens;
     g.dyn = p.dyn;
-    if (p.dyn >= 0) return g;
+    if (p.dyn >= 0) {                 // slot known on device; K from the context buffer if rotated there
+      if (ctx_mode()) {
+        g.k = ctx_k(l) + (size_t)p.ctx_off * cfg.head_dim * L.esize;
+        g.k_hs = (long long)L.ctx_ld * cfg.head_dim;
+      }
+      return g;
+    }
     if (p.kind == bkv::SEG_REFERENCE) {
       g.k = ref_k(l);
       g.v = ref_vt(l);
@@ -278,7 +294,7 @@ struct bkv_cache_s {
         g.kx = ref_kx(l);
         g.kx_hs = L.ref_pad / bkv::kTokAlign;
       }
-    } else if (!convkv()) {
+    } else if (!ctx_mode()) {
       g.k = slot_k(l, p.slot);
       g.v = slot_vt(l, p.slot);
       g.k_hs = slot_k_hs();
@@ -353,7 +369,9 @@ bkv_status set_device(bkv_cache h) {
   return BKV_OK;
 }
 
-// ConvKV: rotate memory + window K of layer l into the context-K buffer.
+// ConvKV / context-relative PR-Sink: rotate the raw K of the context's cached
+// segments (memory frames; static, retrieved and window blocks) of layer l
+// into the context-K buffer at their context positions.
 bkv_status gather_context(bkv_cache h, int l, hipStream_t stream) {
   bkv::GatherArgs g{};
   g.dst = h->ctx_k(l);
@@ -361,10 +379,21 @@ bkv_status gather_context(bkv_cache h, int l, hipStream_t stream) {
   g.H = h->cfg.heads;
   g.D = h->cfg.head_dim;
   g.rope = h->rope();
+  g.sel_ids = h->sel_ids();
+  g.sel_slots = h->sel_slots();
+  g.slot_base = h->layer_kv(l);
+  g.slot_bytes = (long long)h->L.slot_bytes;
+  g.slot_k_hs = h->slot_k_hs();
+  g.n_dyn = h->sched.n_dynamic();
+  g.frames = h->cfg.frames_per_block;
   for (const auto& p : h->sched.segments()) {
-    if (p.kind == bkv::SEG_CURRENT) continue;
+    if (p.kind == bkv::SEG_CURRENT || p.kind == bkv::SEG_REFERENCE) continue;
     bkv::GatherPart& gp = g.part[g.nparts++];
-    if (p.kind == bkv::SEG_MEMORY) {
+    gp.dyn = p.dyn;
+    if (p.dyn >= 0) {
+      gp.src = nullptr;                 // the selected slot, on device
+      gp.src_hs = 0;
+    } else if (p.kind == bkv::SEG_MEMORY) {
       gp.src = h->mem_k(l) + (size_t)p.id * h->L.tf_pad * h->cfg.head_dim * h->L.esize;
       gp.src_hs = (long long)h->L.mem_ld * h->cfg.head_dim;
     } else {
@@ -439,7 +468,7 @@ bkv_status bkv_create(const bkv_config* cfg, void* workspace, size_t bytes, hipS
   if (cfg->rope_h) e = bkv::launch_rope_table(h->htab(), cfg->grid_h, cfg->rope_h, 0, theta, stream);
   if (e == hipSuccess && cfg->rope_w)
     e = bkv::launch_rope_table(h->wtab(), cfg->grid_w, cfg->rope_w, 0, theta, stream);
-  if (e == hipSuccess && cfg->rope_t && h->convkv())
+  if (e == hipSuccess && cfg->rope_t && h->ctx_mode())
     e = bkv::launch_rope_table(h->ttab(), h->L.t_rows, cfg->rope_t, 0, theta, stream);
   if (e == hipSuccess && cfg->rope_t && h->L.ref_tok > 0)
     e = bkv::launch_rope_table(h->tref(), cfg->reference_frames, cfg->rope_t, 0, theta, stream);
@@ -560,7 +589,7 @@ bkv_status bkv_retrieve(bkv_cache h, const float* pose, hipStream_t stream) {
     }
     a.sel_ids = h->sel_ids();
     a.sel_slots = h->sel_slots();
-    if (h->cfg.rope_t) {
+    if (h->cfg.rope_t && !h->ctx_mode()) {   // absolute positions: this block's t rows
       a.ttab = h->ttab();
       a.t_rows = h->cfg.frames_per_block;
       a.t_dim = h->cfg.rope_t;
@@ -598,7 +627,7 @@ bkv::AppendArgs append_args(bkv_cache h, int layer) {
     ap.kx = h->slot_kx(layer, cur.slot);
     ap.kx_hs = h->slot_kx_hs();
     ap.t_row0 = 0;
-  } else if (!h->convkv()) {
+  } else if (!h->ctx_mode()) {
     ap.k_rot = h->slot_k(layer, cur.slot);
     ap.k_rot_hs = h->slot_k_hs();
     ap.k_rot_off = 0;
@@ -618,7 +647,7 @@ bkv::AppendArgs append_args(bkv_cache h, int layer) {
 // per layer and block), then attention of q over the context into out.
 bkv_status attend_context(bkv_cache h, int layer, const void* q, void* out, hipStream_t stream) {
   bkv_status st;
-  if (h->convkv() && !h->ctx_ready[layer]) {
+  if (h->ctx_mode() && !h->ctx_ready[layer]) {
     if ((st = gather_context(h, layer, stream)) != BKV_OK) return st;
   }
   const auto& segs = h->sched.segments();
@@ -630,7 +659,7 @@ bkv_status attend_context(bkv_cache h, int layer, const void* q, void* out, hipS
   a.T = h->L.T;
   a.H = h->cfg.heads;
   a.D = D;
-  a.t_row0 = h->convkv() ? (int)cur.t0 : 0;
+  a.t_row0 = h->ctx_mode() ? (int)cur.t0 : 0;
   const float scale = h->cfg.softmax_scale > 0.f ? h->cfg.softmax_scale : 1.0f / std::sqrt((float)D);
   a.qscale = h->bf16() ? scale * 1.4426950408889634f : scale;
   a.rope = h->rope();
@@ -788,7 +817,13 @@ bkv_status bkv_context(bkv_cache h, bkv_segment* segs, int32_t cap, int32_t* n, 
     segs[i].tokens = p.tokens;
     if (p.dyn >= 0) {
       segs[i].id = ids[p.dyn];
-      segs[i].t0 = (int32_t)h->sched.block_t0(ids[p.dyn]);
+      if (h->ctx_mode()) {            // the run's first position + frames x rank by stream id
+        int rank = 0;
+        for (int j = 0; j < k; ++j) rank += ids[j] < ids[p.dyn];
+        segs[i].t0 = (int32_t)(p.t0 + (int64_t)rank * h->cfg.frames_per_block);
+      } else {
+        segs[i].t0 = (int32_t)h->sched.block_t0(ids[p.dyn]);
+      }
     } else {
       segs[i].id = (int32_t)p.id;
       segs[i].t0 = (int32_t)p.t0;
@@ -824,7 +859,7 @@ bkv_status bkv_export_segment(bkv_cache h, int32_t layer, int32_t seg, void* k_o
   if (p.kind == bkv::SEG_CURRENT && !h->sched.attended(layer))
     return fail(BKV_ERR_STATE, "current block of layer %d not written yet", layer);
   if ((st = set_device(h)) != BKV_OK) return st;
-  if (h->convkv() && !h->ctx_ready[layer]) {
+  if (h->ctx_mode() && !h->ctx_ready[layer]) {
     if ((st = gather_context(h, layer, stream)) != BKV_OK) return st;
   }
   bkv::ExportArgs a{};

@@ -511,6 +511,10 @@ void attn_bf16_kernel(AttnArgs a) {
           s_xb[gg] = reinterpret_cast<const int*>(kb + a.slot_kx_off);
           s_xhs[gg] = a.slot_kx_hs;
         }
+        if (sg.k) {                      // K rotated into the context-K buffer
+          kb = static_cast<const char*>(sg.k);
+          khs = sg.k_hs;
+        }
       } else {
         kb = static_cast<const char*>(sg.k);
         vb = static_cast<const char*>(sg.v);
@@ -1219,6 +1223,10 @@ __global__ __launch_bounds__(128) void attn_f32_kernel(AttnArgs a) {
       khs = a.slot_k_hs;
       vhs = a.slot_v_hs;
       ld = a.slot_v_ld;
+      if (sg.k) {                        // K rotated into the context-K buffer
+        kb = static_cast<const char*>(sg.k);
+        khs = sg.k_hs;
+      }
     } else {
       kb = static_cast<const char*>(sg.k);
       vb = static_cast<const char*>(sg.v);
@@ -1314,11 +1322,22 @@ __global__ __launch_bounds__(256) void gather_kernel(GatherArgs a) {
   if (tile0 >= p.n) return;
   const int ntok = min(64, p.n - tile0);
   const bool rope = has_rope(a.rope);
+  const void* src = p.src;
+  long long src_hs = p.src_hs;
+  int t_row0 = p.t_row0;
+  if (p.dyn >= 0) {     // retrieved block: its slot, and its place among the retrieved by stream id
+    src = a.slot_base + (long long)a.sel_slots[p.dyn] * a.slot_bytes;
+    src_hs = a.slot_k_hs;
+    const int id = a.sel_ids[p.dyn];
+    int rank = 0;
+    for (int j = 0; j < a.n_dyn; ++j) rank += a.sel_ids[j] < id;
+    t_row0 += rank * a.frames;
+  }
   for (int task = threadIdx.x; task < 64 * CPR; task += 256) {
     const int r = task / CPR, c = task - r * CPR;
     if (r >= ntok) continue;
     const int tok = tile0 + r;
-    uint4 raw = *reinterpret_cast<const uint4*>(static_cast<const T*>(p.src) + head * p.src_hs +
+    uint4 raw = *reinterpret_cast<const uint4*>(static_cast<const T*>(src) + head * src_hs +
                                                 (size_t)tok * D + c * VEC);
     if (rope) {
       int f, y, x;
@@ -1327,7 +1346,7 @@ __global__ __launch_bounds__(256) void gather_kernel(GatherArgs a) {
 #pragma unroll
       for (int e = 0; e < VEC; e += 2) {
         float u0 = to_f(kv[e]), u1 = to_f(kv[e + 1]);
-        rope_pair(u0, u1, c * VEC + e, a.rope, p.t_row0 + f, y, x);
+        rope_pair(u0, u1, c * VEC + e, a.rope, t_row0 + f, y, x);
         kv[e] = from_f<T>(u0);
         kv[e + 1] = from_f<T>(u1);
       }
@@ -1616,6 +1635,10 @@ __global__ void export_kernel(ExportArgs a) {
     khs = a.slot_k_hs;
     vhs = a.slot_v_hs;
     ld = a.slot_v_ld;
+    if (a.seg.k) {                       // K rotated into the context-K buffer
+      kb = static_cast<const char*>(a.seg.k);
+      khs = a.seg.k_hs;
+    }
   } else {
     kb = static_cast<const char*>(a.seg.k);
     vb = static_cast<const char*>(a.seg.v);

@@ -39,8 +39,9 @@ struct Rope {                   // 3D RoPE tables: (cos, sin) fp32 pairs, built 
 
 // One context segment for attention: keys [0, n).  K rows at k + head*k_hs,
 // V^T at v + head*v_hs with row stride v_ld.  dyn >= 0: the segment is a
-// retrieved bank block; its slot is sel_slots[dyn] and k/v are derived from
-// slot_base (set on device by the retrieval kernel, unknown to the host).
+// retrieved bank block; its slot is sel_slots[dyn] (set on device by the
+// retrieval kernel, unknown to the host) and V^T comes from that slot; so
+// does K unless k is set (K rotated into the context-K buffer).
 struct Seg {
   const void* k;
   const void* v;
@@ -112,16 +113,22 @@ struct OpenArgs {
   int bank_slot[kMaxBank];
 };
 
-// ConvKV: rotate raw K rows of memory frames / window blocks into the
-// contiguous context-K buffer at context positions.
+// ConvKV and context-relative PR-Sink: rotate raw K rows of the context's
+// cached segments into the contiguous context-K buffer at context positions.
 struct GatherPart {
-  const void* src; long long src_hs;   // raw K rows [H][..][D]
-  int dst_off, n, t_row0, pad_;        // dst row offset, tokens, t-table row of frame 0
+  const void* src; long long src_hs;   // raw K rows [H][..][D] (dyn >= 0: from the selected slot)
+  int dst_off, n, t_row0;              // dst row offset, tokens, t-table row of frame 0
+  int dyn;                             // >= 0: retrieved block of rank dyn; t_row0 is then the
+                                       // run's first row, plus frames x (its rank by stream id)
 };
 struct GatherArgs {
   void* dst; long long dst_hs;
   int H, D, nparts, max_n;
   Rope rope;
+  const int* sel_ids;                  // retrieved ids and slots (device), n_dyn of each
+  const int* sel_slots;
+  const char* slot_base; long long slot_bytes, slot_k_hs;
+  int n_dyn, frames;
   GatherPart part[kMaxSeg];
 };
 

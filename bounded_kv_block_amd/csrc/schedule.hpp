@@ -15,6 +15,13 @@
 // (outside the slots) at temporal positions 0..R-1; generated blocks then sit
 // at t0 = R + id * frames.
 //
+// Context-relative PR-Sink (relative = true): the context's blocks sit at
+// consecutive frames in stream-id order (static, retrieved, window, current)
+// after the reference; each segment gets a row range of the context-K buffer
+// (ctx_off), as for ConvKV.  A retrieved block's id is known on the device
+// only, so its segment carries the first position of the retrieved run and
+// the device adds its rank among the selected ids.
+//
 // Slots: every block in the cache occupies one slot (K and V of every layer).
 // A block keeps its slot until it leaves the cache, so a commit moves ids
 // between lists and never copies tensor data.
@@ -35,9 +42,10 @@ struct SegPlan {
   int64_t id;       // block id; memory: frame index; dynamic, reference: -1
   int tokens;
   int64_t t0;       // temporal RoPE position of the segment's first frame
+                    // (relative PR-Sink, dynamic: first position of the retrieved run)
   int slot;         // slot id, -1 for memory, dynamic and reference segments
   int dyn;          // dynamic: rank index into the device selection, else -1
-  int ctx_off;      // ConvKV: row offset in the context-K buffer, else 0
+  int ctx_off;      // ConvKV, relative PR-Sink: row offset in the context-K buffer, else 0
 };
 
 struct ConvTap { int slot; int frame; };   // one source frame of the conv memory
@@ -50,6 +58,7 @@ class Schedule {
     int window, statics, k, bank;
     int kernel, memory_frames;
     int ref_frames;                         // PR-Sink reference frames (0 = none)
+    bool relative;                          // PR-Sink context-relative positions
   };
 
   explicit Schedule(const Shape& s) : s_(s) {
@@ -80,8 +89,14 @@ class Schedule {
   int ref_tokens() const { return s_.convkv ? 0 : s_.ref_frames * s_.tokens_per_frame; }
   // Temporal position of block b's first frame (PR-Sink).
   int64_t block_t0(int64_t b) const { return (s_.convkv ? 0 : s_.ref_frames) + b * s_.frames; }
-  // Temporal positions the ConvKV context uses: 0 .. max_context_frames()-1.
-  int max_context_frames() const { return s_.memory_frames + (s_.window + 1) * s_.frames; }
+  // Rows of the context-K buffer (ConvKV, relative PR-Sink): the context less the reference.
+  int ctx_tokens() const { return max_context_tokens() - ref_tokens(); }
+  // Temporal positions a context-relative context uses: 0 .. max_context_frames()-1.
+  int max_context_frames() const {
+    if (s_.convkv) return s_.memory_frames + (s_.window + 1) * s_.frames;
+    return s_.ref_frames + (s_.statics + s_.k + s_.window + 1) * s_.frames;
+  }
+  bool ctx_mode() const { return s_.convkv || s_.relative; }
 
   void reset() {
     next_ = 0;
@@ -208,7 +223,28 @@ class Schedule {
     segs_.clear();
     const int64_t m = next_;
     const int F = s_.frames;
-    if (!s_.convkv) {
+    if (!s_.convkv && s_.relative) {
+      if (s_.ref_frames > 0) segs_.push_back({SEG_REFERENCE, -1, ref_tokens(), 0, -1, -1, 0});
+      int64_t t = s_.ref_frames;
+      int off = 0;
+      for (auto& st : static_) {
+        segs_.push_back({SEG_STATIC, st.first, T_, t, st.second, -1, off});
+        t += F;
+        off += T_;
+      }
+      const int nd = n_dynamic();
+      for (int j = 0; j < nd; ++j) {
+        segs_.push_back({SEG_DYNAMIC, -1, T_, t, -1, j, off});
+        off += T_;
+      }
+      t += (int64_t)nd * F;
+      for (auto& w : window_) {
+        segs_.push_back({SEG_WINDOW, w.first, T_, t, w.second, -1, off});
+        t += F;
+        off += T_;
+      }
+      segs_.push_back({SEG_CURRENT, m, T_, t, cur_slot_, -1, off});
+    } else if (!s_.convkv) {
       if (s_.ref_frames > 0) segs_.push_back({SEG_REFERENCE, -1, ref_tokens(), 0, -1, -1, 0});
       for (auto& st : static_) segs_.push_back({SEG_STATIC, st.first, T_, block_t0(st.first), st.second, -1, 0});
       for (int j = 0; j < n_dynamic(); ++j) segs_.push_back({SEG_DYNAMIC, -1, T_, -1, -1, j, 0});

@@ -109,6 +109,15 @@ typedef struct {
   int32_t reference_frames; /* PR-Sink: reference latent frames R kept as a permanent first
                                context segment, 0..8 (0 = none); ConvKV: 0.  See
                                bkv_set_reference. */
+  int32_t rope_relative;    /* PR-Sink: 0 = absolute temporal positions (frame f of block b at
+                               reference_frames + b*frames_per_block + f; K rotated once, at
+                               append); 1 = context-relative: the open block's context blocks
+                               (static, retrieved, window, current) sit at consecutive frames in
+                               stream-id order after the reference frames, with the gaps between
+                               them removed, and their K is re-rotated at those positions every
+                               block (the SoulX-LiveAct page, section 技术内核, restarts RoPE over
+                               the kept context for ConvKV; this applies it to PR-Sink).  Not with
+                               BKV_BF16_FP8K.  ConvKV: 0 (its positions are context-relative). */
 } bkv_config;
 
 /* One context segment as the open block sees it (host view). */
@@ -117,8 +126,8 @@ typedef struct {
   int32_t id;      /* block stream id; memory: memory-frame index */
   int32_t tokens;  /* keys contributed */
   int32_t t0;      /* RoPE temporal position of the segment's first frame (PR-Sink: absolute
-                      reference_frames + id*frames_per_block, the reference segment 0;
-                      ConvKV: context-relative) */
+                      reference_frames + id*frames_per_block, or context-relative with
+                      rope_relative; the reference segment 0; ConvKV: context-relative) */
 } bkv_segment;
 
 typedef struct {

@@ -14,8 +14,9 @@ void* sched_new(int convkv, int layers, int frames, int tpf, int window, int sta
   Schedule::Shape s{convkv != 0, layers, frames, tpf, window, statics, k, bank, kernel, memory_frames};
   return new Schedule(s);
 }
-void* sched_new_ref(int layers, int frames, int tpf, int window, int statics, int k, int bank, int ref_frames) {
-  Schedule::Shape s{false, layers, frames, tpf, window, statics, k, bank, 1, 0, ref_frames};
+void* sched_new_ref(int layers, int frames, int tpf, int window, int statics, int k, int bank, int ref_frames,
+                    int relative) {
+  Schedule::Shape s{false, layers, frames, tpf, window, statics, k, bank, 1, 0, ref_frames, relative != 0};
   return new Schedule(s);
 }
 void sched_free(void* p) { delete static_cast<Schedule*>(p); }

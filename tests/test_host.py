@@ -25,7 +25,7 @@ def shim(tmp_path_factory):
     L.sched_new.restype = ctypes.c_void_p
     L.sched_new.argtypes = [ctypes.c_int] * 10
     L.sched_new_ref.restype = ctypes.c_void_p
-    L.sched_new_ref.argtypes = [ctypes.c_int] * 8
+    L.sched_new_ref.argtypes = [ctypes.c_int] * 9
     for n in ("sched_free",):
         getattr(L, n).argtypes = [ctypes.c_void_p]
     for n in ("sched_n_slots", "sched_open", "sched_cur_slot", "sched_memory_count", "sched_n_dynamic"):
@@ -46,9 +46,10 @@ class Sched:
     def __init__(self, L, **kw):
         self.L = L
         self.layers = kw.get("layers", 1)
-        if kw.get("ref_frames"):
+        if kw.get("ref_frames") or kw.get("relative"):
             self.p = L.sched_new_ref(self.layers, kw["frames"], kw["tpf"], kw["window"], kw.get("statics", 0),
-                                     kw.get("k", 0), kw.get("bank", 0), kw["ref_frames"])
+                                     kw.get("k", 0), kw.get("bank", 0), kw.get("ref_frames", 0),
+                                     int(kw.get("relative", 0)))
             return
         args = [kw.get("convkv", 0), self.layers, kw["frames"], kw["tpf"], kw["window"], kw.get("statics", 0),
                 kw.get("k", 0), kw.get("bank", 0), kw.get("kernel", 1), kw.get("memory_frames", 0)]
@@ -141,6 +142,34 @@ def test_prsink_reference_segment(shim, R):
         for g, g0 in zip(segs[1:], segs0):
             assert g[:3] == g0[:3] and g[4:] == g0[4:]
             assert g[3] == (-1 if g[0] == DYNAMIC else R + g[1] * F)
+        for x in (s, s0):
+            shim.sched_mark(x.p, 0)
+            assert x.commit()[0] == 1
+
+
+@pytest.mark.parametrize("R,k", [(0, 2), (2, 3), (1, 0)])
+def test_prsink_relative_segments(shim, R, k):
+    """Context-relative PR-Sink: the same blocks, slots and order as with
+    absolute positions; block segments take consecutive frames after the
+    reference (the retrieved run's first position on each retrieved segment:
+    the device adds frames x rank by id) and contiguous context-K rows."""
+    F, tpf, W, B, S = 3, 4, 3, 8, 1
+    T = F * tpf
+    s = Sched(shim, frames=F, tpf=tpf, window=W, statics=S, k=k, bank=B, ref_frames=R, relative=1)
+    s0 = Sched(shim, frames=F, tpf=tpf, window=W, statics=S, k=k, bank=B, ref_frames=R)
+    for m in range(30):
+        assert shim.sched_open(s.p) == 1 and shim.sched_open(s0.p) == 1
+        segs, segs0 = s.segments(), s0.segments()
+        assert [g[:3] + g[4:6] for g in segs] == [g[:3] + g[4:6] for g in segs0]
+        blocks = [g for g in segs if g[0] != REFERENCE]
+        nd = sum(g[0] == DYNAMIC for g in blocks)
+        t, want_t = R, []
+        for g in blocks:
+            want_t.append(t if g[0] != DYNAMIC else R + S * F)
+            t += F
+        assert [g[3] for g in blocks] == want_t
+        assert [g[6] for g in blocks] == [i * T for i in range(len(blocks))]
+        assert blocks[-1][3] == R + (len(blocks) - 1) * F and nd <= k
         for x in (s, s0):
             shim.sched_mark(x.p, 0)
             assert x.commit()[0] == 1
@@ -305,3 +334,24 @@ def test_reference_frames_workspace_and_validation():
     with pytest.raises(bkv.BkvError) as ei:
         bkv.workspace_size(bkv.config_from_workload(synth.workload("convkv_512", reference_frames=1)))
     assert ei.value.status == bkv.BKV_ERR_UNSUPPORTED
+
+
+def test_relative_positions_workspace_and_validation():
+    """Context-relative PR-Sink adds a context-K buffer of the largest context
+    (less the reference) plus one key tile, per layer, and a temporal table
+    of its frames; not with the FP8 key cache, not for ConvKV."""
+    from bounded_kv_block_amd import bkv, synth
+    n0 = bkv.workspace_size(bkv.config_from_workload(synth.workload("prsink_512")))
+    n1 = bkv.workspace_size(bkv.config_from_workload(synth.workload("prsink_512_rel")))
+    ctx = (21504 + 64) * 40 * 128 * 2
+    al = lambda n: -(-n // 256) * 256
+    tt = al(8 * 21 * 23) - al(8 * 3 * 23)                # 21 t rows of 23 (cos, sin) pairs instead of 3
+    assert n1 - n0 == ctx + tt
+    with pytest.raises(bkv.BkvError) as ei:
+        bkv.workspace_size(bkv.config_from_workload(synth.workload("prsink_512_fp8k", positions="relative")))
+    assert ei.value.status == bkv.BKV_ERR_UNSUPPORTED
+    c = bkv.config_from_workload(synth.workload("convkv_512"))
+    c.rope_relative = 1
+    with pytest.raises(bkv.BkvError) as ei:
+        bkv.workspace_size(c)
+    assert ei.value.status == bkv.BKV_ERR_ARG
