@@ -54,6 +54,23 @@ __device__ __forceinline__ void rope_pair(float& u0, float& u1, int ch, const Ro
   u1 = b;
 }
 
+// The same rotation with the table picked by selects rather than branches, so
+// that lanes whose channels fall on different axes issue one load each
+// instead of taking the three paths in turn.
+__device__ __forceinline__ void rope_pair_sel(float& u0, float& u1, int ch, const Rope& r, int trow,
+                                              int y, int x) {
+  const bool in_t = ch < r.dt, in_h = ch < r.dt + r.dh;
+  const float2* tab = in_t ? r.t : (in_h ? r.h : r.w);
+  const int row = in_t ? trow : (in_h ? y : x);
+  const int half = (in_t ? r.dt : (in_h ? r.dh : r.dw)) >> 1;
+  const int col = (ch - (in_t ? 0 : (in_h ? r.dt : r.dt + r.dh))) >> 1;
+  const float2 cs = tab[row * half + col];
+  const float a = u0 * cs.x - u1 * cs.y;
+  const float b = u0 * cs.y + u1 * cs.x;
+  u0 = a;
+  u1 = b;
+}
+
 __device__ __forceinline__ bool has_rope(const Rope& r) { return (r.dt + r.dh + r.dw) != 0; }
 
 // token index within a block -> (frame, y, x)
@@ -1333,26 +1350,39 @@ __global__ __launch_bounds__(256) void gather_kernel(GatherArgs a) {
     for (int j = 0; j < a.n_dyn; ++j) rank += a.sel_ids[j] < id;
     t_row0 += rank * a.frames;
   }
-  for (int task = threadIdx.x; task < 64 * CPR; task += 256) {
-    const int r = task / CPR, c = task - r * CPR;
-    if (r >= ntok) continue;
-    const int tok = tile0 + r;
-    uint4 raw = *reinterpret_cast<const uint4*>(static_cast<const T*>(src) + head * src_hs +
-                                                (size_t)tok * D + c * VEC);
-    if (rope) {
+  // every chunk's load first, then the rotations, then the stores: IT
+  // independent 16-byte loads in flight per thread
+  constexpr int IT = 64 * CPR / 256;
+  static_assert(IT * 256 == 64 * CPR, "tile of 64 rows in whole passes of 256 threads");
+  const T* sbase = static_cast<const T*>(src) + head * src_hs;
+  uint4 raw[IT];
+#pragma unroll
+  for (int it = 0; it < IT; ++it) {
+    const int task = threadIdx.x + 256 * it, r = task / CPR, c = task % CPR;
+    if (r < ntok) raw[it] = *reinterpret_cast<const uint4*>(sbase + (size_t)(tile0 + r) * D + c * VEC);
+  }
+  if (rope) {
+#pragma unroll
+    for (int it = 0; it < IT; ++it) {
+      const int task = threadIdx.x + 256 * it, r = task / CPR, c = task % CPR;
+      if (r >= ntok) continue;
       int f, y, x;
-      token_fyx(tok, a.rope.grid_h, a.rope.grid_w, f, y, x);
-      T* kv = reinterpret_cast<T*>(&raw);
+      token_fyx(tile0 + r, a.rope.grid_h, a.rope.grid_w, f, y, x);
+      T* kv = reinterpret_cast<T*>(&raw[it]);
 #pragma unroll
       for (int e = 0; e < VEC; e += 2) {
         float u0 = to_f(kv[e]), u1 = to_f(kv[e + 1]);
-        rope_pair(u0, u1, c * VEC + e, a.rope, t_row0 + f, y, x);
+        rope_pair_sel(u0, u1, c * VEC + e, a.rope, t_row0 + f, y, x);
         kv[e] = from_f<T>(u0);
         kv[e + 1] = from_f<T>(u1);
       }
     }
-    T* dst = static_cast<T*>(a.dst) + head * a.dst_hs + (size_t)(p.dst_off + tok) * D + c * VEC;
-    *reinterpret_cast<uint4*>(dst) = raw;
+  }
+  T* dbase = static_cast<T*>(a.dst) + head * a.dst_hs + (size_t)(p.dst_off + tile0) * D;
+#pragma unroll
+  for (int it = 0; it < IT; ++it) {
+    const int task = threadIdx.x + 256 * it, r = task / CPR, c = task % CPR;
+    if (r < ntok) *reinterpret_cast<uint4*>(dbase + (size_t)r * D + c * VEC) = raw[it];
   }
 }
 
