@@ -30,7 +30,7 @@ _BASE = dict(mode="pr_sink", dtype="bf16", layers=1, steps=1, heads=40, head_dim
              frames=3, grid_h=32, grid_w=32, window=3, static=1, dynamic_k=2, bank=56,
              pose_dim=128, rope=(44, 42, 42), theta=10000.0, conv_kernel=5, conv_stride=5,
              memory_frames=1, blocks=60, seed=2, pose_kind="walk", keyframes=16, model_dim=5120, reference_frames=0,
-             positions="absolute")
+             positions="default")
 
 WORKLOADS = {
     # tiny fp32 stream: 2 heads x 64, 2 frames of 8x8, top-1 over 32-d poses,
@@ -60,6 +60,9 @@ WORKLOADS = {
     # 1024-token memory frame; 200 blocks.
     "convkv_512": dict(_BASE, mode="convkv", static=0, dynamic_k=0, bank=0, pose_dim=0,
                        blocks=200, seed=5, pose_kind="none"),
+    # the same with only the memory's positions restarted (window and current absolute)
+    "convkv_512_abs": dict(_BASE, mode="convkv", static=0, dynamic_k=0, bank=0, pose_dim=0,
+                           blocks=200, seed=5, pose_kind="none", positions="absolute"),
 }
 
 

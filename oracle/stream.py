@@ -31,6 +31,9 @@ Readings (beyond those stated in the modules used here):
     stream id (static, retrieved, window, current) has its frame f at
     t = R + i * frames + f.  Keys are rotated per block at these positions,
     not once at append.
+  * ConvKV with positions = "absolute" (the literal alternative of the same
+    passage: only the memory's positions restart): memory frame j at t = j,
+    window and current blocks at their absolute t = b * frames + f.
 """
 from __future__ import annotations
 
@@ -163,11 +166,19 @@ class ConvKVReference(_Base):
             raise ValueError("the oracle follows the stride == kernel reading")
         return convkv_schedule(m, self.F, c["window"], c["conv_kernel"], c["memory_frames"])
 
+    def positions(self, m: int):
+        """(t0 of each window block, t0 of the current block)."""
+        sch = self.schedule(m)
+        if self.cfg.get("positions") == "absolute":
+            return [b * self.F for b in sch["window"]], m * self.F
+        return sch["t0"]["window"], sch["t0"]["current"]
+
     def context(self, m: int) -> list:
         sch = self.schedule(m)
+        tw, tc = self.positions(m)
         segs = [("memory", j, self.Tf, j) for j in range(len(sch["memory"]))]
-        segs += [("window", b, self.T, t0) for b, t0 in zip(sch["window"], sch["t0"]["window"])]
-        segs.append(("current", m, self.T, sch["t0"]["current"]))
+        segs += [("window", b, self.T, t0) for b, t0 in zip(sch["window"], tw)]
+        segs.append(("current", m, self.T, tc))
         return segs
 
     def _frame(self, layer: int, e: int, heads):
@@ -205,11 +216,11 @@ class ConvKVReference(_Base):
         for j in range(len(sch["memory"])):
             kr = self._rot(mk[j], lambda f, j=j: j, list(range(len(heads))), tok=tok_frame0)
             out.append(("memory", j, kr, mv[j]))
-        for b, t0 in zip(sch["window"], sch["t0"]["window"]):
+        tw, t0 = self.positions(m)
+        for b, tb in zip(sch["window"], tw):
             _, k, v = self.p.qkv(layer, b, last)
-            kr = self._rot(k, lambda f, t0=t0: t0 + f, heads)
+            kr = self._rot(k, lambda f, tb=tb: tb + f, heads)
             out.append(("window", b, kr, np.asarray(v, np.float64)[:, heads, :]))
-        t0 = sch["t0"]["current"]
         _, k, v = self.p.qkv(layer, m, step)
         kr = self._rot(k, lambda f: t0 + f, heads)
         out.append(("current", m, kr, np.asarray(v, np.float64)[:, heads, :]))
@@ -218,7 +229,7 @@ class ConvKVReference(_Base):
     def attend(self, m: int, layer: int, step: int, heads=None, rows=None):
         H = self.cfg["heads"]
         heads = list(range(H)) if heads is None else list(heads)
-        t0 = self.schedule(m)["t0"]["current"]
+        t0 = self.positions(m)[1]
         q, _, _ = self.p.qkv(layer, m, step)
         q_rot = self._rot(q, lambda f: t0 + f, heads)
         kv = self.context_kv(m, layer, step, heads)

@@ -415,3 +415,57 @@ def check_prsink_relative(Ref, token_positions, apply_rope, make_cfg, make_provi
             got = ref.attend(m, 0, 0)
             assert np.allclose(got, want.transpose(1, 0, 2), atol=1e-12, rtol=0), (R, m)
         assert unordered > 0
+
+
+# ------------------------------------------- ConvKV, memory-only position reset
+def check_convkv_absolute(Ref, token_positions, apply_rope, make_cfg, make_provider):
+    """ConvKV with only the memory's positions restarted.  With one-hot weights
+    on the newest tap the memory frame is the newest evicted frame (frame
+    3(m-3)-1 overall, for 3-frame blocks and a window of 3), so block m's
+    output equals torch SDPA (fp64) over [that raw frame rotated at t = 0,
+    the hand-derived window blocks and block m rotated at their absolute
+    frame indices b*3 + f], with the queries at m*3 + f.  Before any memory
+    exists the output equals the context-relative reading's (the positions
+    differ by one shift at most, which RoPE logits do not see)."""
+    import torch
+    golden = {int(r[0]): r for r in read_table("convkv_schedule_f3_w3_k5_m1.txt")}
+    cfg = make_cfg("absolute")
+    F, gh, gw, K = cfg["frames"], cfg["grid_h"], cfg["grid_w"], cfg["conv_kernel"]
+    assert F == 3 and cfg["window"] == 3 and K == 5 and cfg["memory_frames"] == 1
+    Tf = gh * gw
+    prov = make_provider(cfg)
+    w = np.zeros((cfg["heads"], cfg["head_dim"], K), np.float32)
+    w[:, :, K - 1] = 1.0
+    prov._w[0] = (w, w)
+    ref = Ref(cfg, prov)
+    last = cfg["steps"] - 1
+    f, y, x = token_positions(F, gh, gw)
+    f1, y1, x1 = token_positions(1, gh, gw)
+    t = lambda a: torch.from_numpy(np.ascontiguousarray(np.asarray(a, np.float64).transpose(1, 0, 2)))[None]
+    for m in range(cfg["blocks"]):
+        ks, vs = [], []
+        if golden[m][3] != "-":
+            newest = ids(golden[m][3])[-1]
+            assert newest == 3 * (m - 3) - 1
+            b, fr = divmod(newest, F)
+            _, k, v = prov.qkv(0, b, last)
+            sl = slice(fr * Tf, (fr + 1) * Tf)
+            ks.append(apply_rope(np.asarray(k[sl], np.float64), np.zeros(Tf), y1, x1, cfg["rope"]))
+            vs.append(np.asarray(v[sl], np.float64))
+        for b in ids(golden[m][1]) + [m]:
+            _, k, v = prov.qkv(0, b, last if b < m else 0)
+            ks.append(apply_rope(np.asarray(k, np.float64), b * F + f, y, x, cfg["rope"]))
+            vs.append(np.asarray(v, np.float64))
+        q, _, _ = prov.qkv(0, m, 0)
+        qr = apply_rope(np.asarray(q, np.float64), m * F + f, y, x, cfg["rope"])
+        want = torch.nn.functional.scaled_dot_product_attention(t(qr), t(np.concatenate(ks)),
+                                                                t(np.concatenate(vs)))[0].numpy()
+        got = ref.attend(m, 0, 0)
+        assert np.allclose(got, want.transpose(1, 0, 2), atol=1e-12, rtol=0), m
+    cfg_d = make_cfg("default")
+    prov_d = make_provider(cfg_d)
+    prov_d._w[0] = (w, w)
+    ref_d = Ref(cfg_d, prov_d)
+    for m in range(5):        # blocks 0-3: the same positions; block 4: all shifted by one block
+        assert np.allclose(ref.attend(m, 0, 0), ref_d.attend(m, 0, 0), atol=1e-12, rtol=0), m
+    assert not np.allclose(ref.attend(8, 0, 0), ref_d.attend(8, 0, 0), atol=1e-6)

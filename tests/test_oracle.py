@@ -262,6 +262,11 @@ def test_convkv_memory_with_onehot_weights():
         assert [s[0] for s in kv] == ["memory", "window", "window", "window", "current"]
 
 
+def test_convkv_absolute_positions():
+    pins.check_convkv_absolute(oracle.ConvKVReference, oracle.token_positions, oracle.apply_rope,
+                               lambda pos: _small_convkv(positions=pos), SynthProvider)
+
+
 def test_e4m3_rounding_vs_torch():
     pins.check_e4m3_vs_torch(oracle.fp8.e4m3_round)
 

@@ -337,3 +337,44 @@ def test_relative_position_mutants_fail(mutant):
                                    positions="relative")
     assert _fails(pins.check_prsink_relative, mutant, oracle.token_positions, oracle.apply_rope, cfg,
                   SynthProvider)
+
+
+# -- ConvKV memory-only reset mutants ------------------------------------------
+class _ConvAbsIgnored(oracle.ConvKVReference):
+    """The alternative reading ignored: context-relative positions throughout."""
+
+    def positions(self, m):
+        sch = self.schedule(m)
+        return sch["t0"]["window"], sch["t0"]["current"]
+
+
+class _ConvAbsWindowRelative(oracle.ConvKVReference):
+    """Current block absolute, but the window left at context-relative positions."""
+
+    def positions(self, m):
+        _, tc = super().positions(m)
+        return self.schedule(m)["t0"]["window"], tc
+
+
+class _ConvAbsMemoryAtSource(oracle.ConvKVReference):
+    """The memory frame kept at its newest source frame's absolute position."""
+
+    def context_kv(self, m, layer, step, heads):
+        out = super().context_kv(m, layer, step, heads)
+        sch = self.schedule(m)
+        if out and out[0][0] == "memory":
+            newest = sch["memory"][0][-1]
+            mk, _ = self.memory(m, layer, heads)
+            kr = self._rot(mk[0], lambda f: newest, list(range(len(heads))), tok=np.arange(self.Tf))
+            out[0] = ("memory", 0, kr, out[0][3])
+        return out
+
+
+@pytest.mark.parametrize("mutant", [_ConvAbsIgnored, _ConvAbsWindowRelative, _ConvAbsMemoryAtSource])
+def test_convkv_absolute_mutants_fail(mutant):
+    from bounded_kv_block_amd import synth
+    from conftest import SynthProvider
+    cfg = lambda pos: synth.workload("convkv_512", heads=2, head_dim=16, frames=3, grid_h=2, grid_w=3,
+                                     rope=(6, 4, 6), blocks=9, positions=pos)
+    assert _fails(pins.check_convkv_absolute, mutant, oracle.token_positions, oracle.apply_rope, cfg,
+                  SynthProvider)
