@@ -39,7 +39,7 @@ def parse():
     ap.add_argument("--workload", default="prsink_512",
                     choices=["prsink_512", "prsink_512_fp8k", "prsink_512_qkv", "prsink_512_ref", "prsink_512_rel",
                              "prsink_720x416",
-                             "prsink_long", "convkv_512", "tiny_fp32"])
+                             "prsink_long", "convkv_512", "convkv_512_abs", "tiny_fp32"])
     ap.add_argument("--pool", type=int, default=4, help="distinct resident input blocks cycled through")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=12.0, help="target CPU-oracle sample time")
@@ -346,7 +346,7 @@ def main():
                    "timed_blocks": [m - args.steps, m - 1],
                    **({"model_dim": cfg["model_dim"], "qkv_projection": "fused (bkv_attend_qkv)"} if fused else {}),
                    **({"reference_frames": cfg["reference_frames"]} if cfg.get("reference_frames") else {}),
-                   **({"positions": "context-relative"} if cfg.get("positions") == "relative" else {})},
+                   **({"positions": cfg["positions"]} if cfg.get("positions", "default") != "default" else {})},
         "attention_tflops": attn_tflops,
         "attention_pct_peak": 100.0 * attn_tflops / peak,
         "attention_peak_tflops": peak,

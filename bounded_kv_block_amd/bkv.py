@@ -17,6 +17,7 @@ BKV_OK, BKV_ERR_ARG, BKV_ERR_STATE, BKV_ERR_WORKSPACE, BKV_ERR_DEVICE, BKV_ERR_U
 PR_SINK, CONVKV = 0, 1
 F32, BF16, BF16_FP8K = 0, 1, 2
 DTYPES = {"f32": F32, "bf16": BF16, "bf16_fp8k": BF16_FP8K}
+POSITIONS = {"default": 0, "relative": 1, "absolute": 2}     # bkv_positions
 SEG_KINDS = {0: "static", 1: "dynamic", 2: "window", 3: "current", 4: "memory", 5: "reference"}
 
 # every symbol include/bkv.h declares
@@ -37,7 +38,7 @@ class Config(ctypes.Structure):
                 ("rope_theta", ctypes.c_double), ("conv_kernel", ctypes.c_int32),
                 ("conv_stride", ctypes.c_int32), ("memory_frames", ctypes.c_int32),
                 ("softmax_scale", ctypes.c_float), ("reference_frames", ctypes.c_int32),
-                ("rope_relative", ctypes.c_int32)]
+                ("rope_positions", ctypes.c_int32)]
 
 
 class Segment(ctypes.Structure):
@@ -132,7 +133,7 @@ def config_from_workload(w: dict) -> Config:
     c.conv_kernel, c.conv_stride, c.memory_frames = w["conv_kernel"], w["conv_stride"], w["memory_frames"]
     c.softmax_scale = float(w.get("softmax_scale", 0.0))
     c.reference_frames = int(w.get("reference_frames", 0) or 0)
-    c.rope_relative = 1 if w.get("positions", "absolute") == "relative" else 0
+    c.rope_positions = POSITIONS[w.get("positions", "default")]
     return c
 
 

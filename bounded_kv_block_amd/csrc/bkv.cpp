@@ -59,6 +59,9 @@ bkv_status validate(const bkv_config* c) {
   if (c->dtype != BKV_F32 && c->dtype != BKV_BF16 && c->dtype != BKV_BF16_FP8K)
     return fail(BKV_ERR_ARG, "bad dtype %d", c->dtype);
   if (c->layers < 1 || c->heads < 1) return fail(BKV_ERR_ARG, "layers and heads must be >= 1");
+  if (c->rope_positions != BKV_POS_DEFAULT && c->rope_positions != BKV_POS_CONTEXT &&
+      c->rope_positions != BKV_POS_ABSOLUTE)
+    return fail(BKV_ERR_ARG, "bad rope_positions %d", c->rope_positions);
   if (c->dtype != BKV_F32 && c->head_dim != 128)
     return fail(BKV_ERR_UNSUPPORTED, "bf16 path supports head_dim 128 (got %d)", c->head_dim);
   if (c->dtype == BKV_BF16_FP8K && c->mode != BKV_PR_SINK)
@@ -87,14 +90,12 @@ bkv_status validate(const bkv_config* c) {
     if (c->pose_dim < 0) return fail(BKV_ERR_ARG, "pose_dim must be >= 0");
     if (c->reference_frames < 0 || c->reference_frames > 8)
       return fail(BKV_ERR_ARG, "reference_frames must be 0..8");
-    if (c->rope_relative != 0 && c->rope_relative != 1) return fail(BKV_ERR_ARG, "rope_relative must be 0 or 1");
-    if (c->rope_relative && c->dtype == BKV_BF16_FP8K)
+    if (c->rope_positions == BKV_POS_CONTEXT && c->dtype == BKV_BF16_FP8K)
       return fail(BKV_ERR_UNSUPPORTED, "context-relative positions are implemented without the FP8 key cache");
     if ((c->reference_frames > 0) + c->static_blocks + c->dynamic_k + c->window_blocks + 1 > bkv::kMaxSeg)
       return fail(BKV_ERR_ARG, "more than %d context segments", bkv::kMaxSeg);
   } else {
     if (c->reference_frames != 0) return fail(BKV_ERR_UNSUPPORTED, "reference frames are implemented for PR-Sink only");
-    if (c->rope_relative != 0) return fail(BKV_ERR_ARG, "ConvKV positions are context-relative by definition; rope_relative must be 0");
     if (c->static_blocks != 0 || c->dynamic_k != 0 || c->bank_blocks != 0)
       return fail(BKV_ERR_ARG, "ConvKV takes no static/dynamic sinks or bank");
     if (c->conv_kernel < 1 || c->conv_kernel > 8 || c->conv_stride != c->conv_kernel)
@@ -118,7 +119,7 @@ bkv::Schedule::Shape shape_of(const bkv_config* c) {
   s.kernel = s.convkv ? c->conv_kernel : 1;
   s.memory_frames = s.convkv ? c->memory_frames : 0;
   s.ref_frames = s.convkv ? 0 : c->reference_frames;
-  s.relative = !s.convkv && c->rope_relative != 0;
+  s.relative = !s.convkv && c->rope_positions == BKV_POS_CONTEXT;
   return s;
 }
 
@@ -235,6 +236,9 @@ struct bkv_cache_s {
   // ConvKV or context-relative PR-Sink: slots hold raw K; the context's K is
   // rotated per block into the context-K buffer at context positions.
   bool ctx_mode() const { return sched.ctx_mode(); }
+  // ConvKV with only the memory's positions restarted: the t-table rows keep
+  // the context-relative layout, their values are rewritten every block.
+  bool conv_abs() const { return convkv() && cfg.rope_positions == BKV_POS_ABSOLUTE; }
   char* layer_kv(int l) const { return ws + L.off_kv + L.layer_kv_bytes * l; }
   char* slot_k(int l, int s) const { return layer_kv(l) + L.slot_bytes * s; }
   char* slot_vt(int l, int s) const { return slot_k(l, s) + L.slot_v_off; }
@@ -468,7 +472,7 @@ bkv_status bkv_create(const bkv_config* cfg, void* workspace, size_t bytes, hipS
   if (cfg->rope_h) e = bkv::launch_rope_table(h->htab(), cfg->grid_h, cfg->rope_h, 0, theta, stream);
   if (e == hipSuccess && cfg->rope_w)
     e = bkv::launch_rope_table(h->wtab(), cfg->grid_w, cfg->rope_w, 0, theta, stream);
-  if (e == hipSuccess && cfg->rope_t && h->ctx_mode())
+  if (e == hipSuccess && cfg->rope_t && h->ctx_mode() && !h->conv_abs())
     e = bkv::launch_rope_table(h->ttab(), h->L.t_rows, cfg->rope_t, 0, theta, stream);
   if (e == hipSuccess && cfg->rope_t && h->L.ref_tok > 0)
     e = bkv::launch_rope_table(h->tref(), cfg->reference_frames, cfg->rope_t, 0, theta, stream);
@@ -575,6 +579,27 @@ bkv_status bkv_retrieve(bkv_cache h, const float* pose, hipStream_t stream) {
   if ((st = set_device(h)) != BKV_OK) return st;
   if (!h->sched.open()) return fail(BKV_ERR_STATE, "no free slot (internal)");
   h->ctx_ready.assign(h->cfg.layers, false);
+  if (h->conv_abs() && h->cfg.rope_t) {
+    // rows [0, n_mem): memory frames at 0..n_mem-1; the rows after them: the
+    // window's first block onward at absolute frame indices
+    const auto& segs = h->sched.segments();
+    int n_mem = 0;
+    while (n_mem < (int)segs.size() && segs[n_mem].kind == bkv::SEG_MEMORY) ++n_mem;
+    const int64_t first = segs[n_mem].id;          // oldest window block, or the current block
+    const int rows = (int)(segs.size() - n_mem) * h->cfg.frames_per_block;
+    const int half = h->cfg.rope_t / 2;
+    hipError_t e = hipSuccess;
+    if (n_mem > 0)
+      e = timed(h, K_RETRIEVE, stream, [&] {
+        return bkv::launch_rope_table(h->ttab(), n_mem, h->cfg.rope_t, 0, h->cfg.rope_theta, stream);
+      });
+    if (e == hipSuccess)
+      e = timed(h, K_RETRIEVE, stream, [&] {
+        return bkv::launch_rope_table(h->ttab() + (size_t)n_mem * half, rows, h->cfg.rope_t,
+                                      first * h->cfg.frames_per_block, h->cfg.rope_theta, stream);
+      });
+    if (e != hipSuccess) return device_fail(h, e, "RoPE table launch");
+  }
   if (prsink) {
     bkv::OpenArgs a{};
     a.pose_in = needs_pose ? pose : nullptr;
@@ -827,6 +852,7 @@ bkv_status bkv_context(bkv_cache h, bkv_segment* segs, int32_t cap, int32_t* n, 
     } else {
       segs[i].id = (int32_t)p.id;
       segs[i].t0 = (int32_t)p.t0;
+      if (h->conv_abs() && p.kind != bkv::SEG_MEMORY) segs[i].t0 = (int32_t)(p.id * h->cfg.frames_per_block);
     }
   }
   return BKV_OK;

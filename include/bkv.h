@@ -75,6 +75,24 @@ typedef enum { BKV_PR_SINK = 0, BKV_CONVKV = 1 } bkv_mode;
    BKV_BF16.  Cache bytes per token and head: 128 (K) + 256 (V) + 4/64. */
 typedef enum { BKV_F32 = 0, BKV_BF16 = 1, BKV_BF16_FP8K = 2 } bkv_dtype;
 
+/* Temporal RoPE positions (bkv_config.rope_positions).
+   BKV_POS_DEFAULT: PR-Sink absolute (frame f of block b at
+     reference_frames + b*frames_per_block + f; K rotated once, at append);
+     ConvKV context-relative (SoulX-LiveAct page, section 技术内核: memory
+     frames at 0..M-1, then the window blocks and the current block at
+     consecutive frames).
+   BKV_POS_CONTEXT: PR-Sink context-relative: the open block's context blocks
+     (static, retrieved, window, current) sit at consecutive frames in
+     stream-id order after the reference frames, the gaps between them
+     removed, and their K is re-rotated at those positions every block (the
+     ConvKV page's position reset applied to PR-Sink).  Not with
+     BKV_BF16_FP8K.  ConvKV: as BKV_POS_DEFAULT.
+   BKV_POS_ABSOLUTE: PR-Sink: as BKV_POS_DEFAULT.  ConvKV: only the memory's
+     positions restart (memory frame j at t = j); the window and current
+     blocks keep their absolute frame indices b*frames_per_block + f (the
+     literal alternative reading of the same passage). */
+typedef enum { BKV_POS_DEFAULT = 0, BKV_POS_CONTEXT = 1, BKV_POS_ABSOLUTE = 2 } bkv_positions;
+
 typedef enum {
   BKV_SEG_STATIC = 0,   /* static sink block */
   BKV_SEG_DYNAMIC = 1,  /* pose-retrieved bank block */
@@ -109,15 +127,8 @@ typedef struct {
   int32_t reference_frames; /* PR-Sink: reference latent frames R kept as a permanent first
                                context segment, 0..8 (0 = none); ConvKV: 0.  See
                                bkv_set_reference. */
-  int32_t rope_relative;    /* PR-Sink: 0 = absolute temporal positions (frame f of block b at
-                               reference_frames + b*frames_per_block + f; K rotated once, at
-                               append); 1 = context-relative: the open block's context blocks
-                               (static, retrieved, window, current) sit at consecutive frames in
-                               stream-id order after the reference frames, with the gaps between
-                               them removed, and their K is re-rotated at those positions every
-                               block (the SoulX-LiveAct page, section 技术内核, restarts RoPE over
-                               the kept context for ConvKV; this applies it to PR-Sink).  Not with
-                               BKV_BF16_FP8K.  ConvKV: 0 (its positions are context-relative). */
+  int32_t rope_positions;   /* bkv_positions: temporal RoPE positions of the context (0 = the
+                               mode's own reading) */
 } bkv_config;
 
 /* One context segment as the open block sees it (host view). */
@@ -125,9 +136,8 @@ typedef struct {
   int32_t kind;    /* bkv_segment_kind */
   int32_t id;      /* block stream id; memory: memory-frame index */
   int32_t tokens;  /* keys contributed */
-  int32_t t0;      /* RoPE temporal position of the segment's first frame (PR-Sink: absolute
-                      reference_frames + id*frames_per_block, or context-relative with
-                      rope_relative; the reference segment 0; ConvKV: context-relative) */
+  int32_t t0;      /* RoPE temporal position of the segment's first frame, as rope_positions
+                      sets it (the reference segment: 0) */
 } bkv_segment;
 
 typedef struct {

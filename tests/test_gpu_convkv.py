@@ -65,3 +65,25 @@ def test_convkv_512_full_shape_sampled():
     cfg = synth.workload("convkv_512", blocks=8)
     rows = np.r_[0:64, 3008:3072]
     _run(cfg, host_inputs=False, check={0, 4, 5, 7}, heads=[0, 21], rows=rows)
+
+
+# ---- only the memory's positions restarted (window and current absolute)
+def test_convkv_absolute_small_every_block():
+    """The memory-only reset: per-block temporal rows (memory at 0, window and
+    current at absolute frame indices), reported positions, outputs and every
+    segment's K/V on 14 blocks of the ragged bf16 stream."""
+    cfg = synth.workload("convkv_512_abs", heads=2, grid_h=4, grid_w=6, blocks=14)
+    _run(cfg, export=True)
+
+
+def test_convkv_absolute_fp32_two_memory_frames():
+    cfg = synth.workload("convkv_512_abs", dtype="f32", heads=2, head_dim=64, rope=(24, 20, 20), frames=2,
+                         grid_h=4, grid_w=4, memory_frames=2, blocks=16)
+    _run(cfg, export=True)
+
+
+def test_convkv_absolute_full_shape_sampled():
+    """512x512 shapes at full size, blocks 0..39 (absolute positions up to
+    117): outputs of 2 heads on sampled rows of blocks 4, 5 and 39."""
+    cfg = synth.workload("convkv_512_abs", blocks=40)
+    _run(cfg, host_inputs=False, check={4, 5, 39}, heads=[0, 39], rows=np.r_[0:64, 1500:1532, 3008:3072])

@@ -339,7 +339,8 @@ def test_reference_frames_workspace_and_validation():
 def test_relative_positions_workspace_and_validation():
     """Context-relative PR-Sink adds a context-K buffer of the largest context
     (less the reference) plus one key tile, per layer, and a temporal table
-    of its frames; not with the FP8 key cache, not for ConvKV."""
+    of its frames; not with the FP8 key cache.  ConvKV's memory-only reset
+    needs no extra bytes; an unknown positions value is rejected."""
     from bounded_kv_block_amd import bkv, synth
     n0 = bkv.workspace_size(bkv.config_from_workload(synth.workload("prsink_512")))
     n1 = bkv.workspace_size(bkv.config_from_workload(synth.workload("prsink_512_rel")))
@@ -350,8 +351,10 @@ def test_relative_positions_workspace_and_validation():
     with pytest.raises(bkv.BkvError) as ei:
         bkv.workspace_size(bkv.config_from_workload(synth.workload("prsink_512_fp8k", positions="relative")))
     assert ei.value.status == bkv.BKV_ERR_UNSUPPORTED
+    assert (bkv.workspace_size(bkv.config_from_workload(synth.workload("convkv_512_abs")))
+            == bkv.workspace_size(bkv.config_from_workload(synth.workload("convkv_512"))))
     c = bkv.config_from_workload(synth.workload("convkv_512"))
-    c.rope_relative = 1
+    c.rope_positions = 3
     with pytest.raises(bkv.BkvError) as ei:
         bkv.workspace_size(c)
     assert ei.value.status == bkv.BKV_ERR_ARG
