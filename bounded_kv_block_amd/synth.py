@@ -30,7 +30,7 @@ _BASE = dict(mode="pr_sink", dtype="bf16", layers=1, steps=1, heads=40, head_dim
              frames=3, grid_h=32, grid_w=32, window=3, static=1, dynamic_k=2, bank=56,
              pose_dim=128, rope=(44, 42, 42), theta=10000.0, conv_kernel=5, conv_stride=5,
              memory_frames=1, blocks=60, seed=2, pose_kind="walk", keyframes=16, model_dim=5120, reference_frames=0,
-             positions="default")
+             positions="default", bank_policy="fifo")
 
 WORKLOADS = {
     # tiny fp32 stream: 2 heads x 64, 2 frames of 8x8, top-1 over 32-d poses,
@@ -47,6 +47,9 @@ WORKLOADS = {
     "prsink_512_ref": dict(_BASE, reference_frames=1),
     # the same with context-relative RoPE positions (keys re-rotated per block)
     "prsink_512_rel": dict(_BASE, positions="relative"),
+    # the same with a bank of 8 and pose-aware replacement (the entering block
+    # displaces the member with the most similar pose)
+    "prsink_512_posebank": dict(_BASE, bank=8, bank_policy="pose"),
     # the same driven from hidden states: q, k, v projected in the fused path
     # from x [3072, 5120] (40 heads x 128 = 5120, a 14B-class DiT's width)
     "prsink_512_qkv": dict(_BASE, qkv=True),

@@ -27,8 +27,8 @@ Where the pages leave a step open, the reading taken is stated in the
 function that implements it.  Every function is pinned by a CPU test against
 closed forms, library routines, hand-derived fixtures or brute force.
 """
-from .schedule import (prsink_schedule, simulate_prsink, convkv_schedule, simulate_convkv,
-                       token_positions)
+from .schedule import (prsink_schedule, simulate_prsink, simulate_prsink_pose_bank, convkv_schedule,
+                       simulate_convkv, token_positions)
 from .retrieval import retrieve, exact_keys, fp64_cosines, boundary_gap
 from .rope import rope_frequencies, apply_rope
 from .attention import attention, masked_attention, softmax_weights
@@ -39,7 +39,7 @@ from . import fp8
 
 __all__ = [
     "qkv_projection",
-    "prsink_schedule", "simulate_prsink", "convkv_schedule", "simulate_convkv",
+    "prsink_schedule", "simulate_prsink", "simulate_prsink_pose_bank", "convkv_schedule", "simulate_convkv",
     "token_positions", "retrieve", "exact_keys", "fp64_cosines", "boundary_gap",
     "rope_frequencies", "apply_rope", "attention", "masked_attention", "softmax_weights",
     "conv_memory", "PRSinkReference", "ConvKVReference", "fp8",

@@ -63,6 +63,39 @@ def simulate_prsink(n_blocks: int, window: int = 3, bank: int = 8, static: int =
     return out
 
 
+def simulate_prsink_pose_bank(n_blocks: int, pose, window: int = 3, bank: int = 8, static: int = 1) -> list:
+    """PR-Sink bookkeeping with pose-aware bank replacement (same keys as
+    :func:`prsink_schedule`; ``pose(b)`` gives block b's pose).
+
+    Reading (alternative to the FIFO bank): the bank still holds a fixed
+    number of blocks (LiveAnimate page, section 关键发现), but when a block
+    leaves the window into a full bank, the member it makes most redundant
+    leaves -- the one whose pose has the largest cosine with the entering
+    block's pose, ranked exactly as retrieval ranks (section 局限: retrieval
+    by pose similarity), so exact ties drop the lower stream id and a zero
+    pose scores 0.  The entering block joins at the end (admission order).
+    """
+    from .retrieval import retrieve
+    statics, win, bnk = [], deque(), []
+    out = []
+    for m in range(n_blocks):
+        rec = {"static": list(statics), "bank": list(bnk), "window": list(win), "evicted": None}
+        if len(statics) < static:
+            statics.append(m)
+        else:
+            win.append(m)
+            if len(win) > window:
+                e = win.popleft()
+                rec["evicted"] = e
+                if bank > 0:
+                    if len(bnk) == bank:
+                        victim = retrieve(pose(e), [(b, pose(b)) for b in bnk], 1)[0]
+                        bnk.remove(victim)
+                    bnk.append(e)
+        out.append(rec)
+    return out
+
+
 def convkv_schedule(m: int, frames: int, window: int = 3, kernel: int = 5,
                     memory_frames: int = 1) -> dict:
     """Closed-form ConvKV schedule for block m.

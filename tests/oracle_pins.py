@@ -469,3 +469,50 @@ def check_convkv_absolute(Ref, token_positions, apply_rope, make_cfg, make_provi
     for m in range(5):        # blocks 0-3: the same positions; block 4: all shifted by one block
         assert np.allclose(ref.attend(m, 0, 0), ref_d.attend(m, 0, 0), atol=1e-12, rtol=0), m
     assert not np.allclose(ref.attend(8, 0, 0), ref_d.attend(8, 0, 0), atol=1e-6)
+
+
+# --------------------------------------------------- pose-aware bank replacement
+def check_pose_bank_golden(simulate_pose_bank):
+    """Hand-derived table (tests/golden/prsink_pose_bank_w1_b2_s1.txt): window
+    1, bank 2, one static block, 2-D poses with exact ties, a zero pose and
+    replacements of the newer member."""
+    rows = read_table("prsink_pose_bank_w1_b2_s1.txt")
+    poses = {int(r[0]): np.array([float(r[1]), float(r[2])], np.float32) for r in rows}
+    sim = simulate_pose_bank(len(rows), lambda b: poses[b], 1, 2, 1)
+    for r in rows:
+        m = int(r[0])
+        s = sim[m]
+        assert s["static"] == ids(r[3]), (m, s)
+        assert s["bank"] == ids(r[4]), (m, s)
+        assert s["window"] == ids(r[5]), (m, s)
+        assert s["evicted"] == (None if r[6] == "-" else int(r[6])), (m, s)
+
+
+def check_pose_bank_properties(simulate_pose_bank, prsink_schedule, rng):
+    """Random poses: static and window as the FIFO schedule; the bank equals
+    the FIFO bank while it has never been full; afterwards it holds exactly B
+    distinct blocks that left the window, always including the newest one;
+    each replacement removes a member whose cosine to the entering block's
+    pose is the largest (fp64 on tie-free data)."""
+    for W, B, S in ((3, 4, 1), (1, 1, 0), (2, 5, 1), (3, 2, 1)):
+        n = 40
+        P = rng.standard_normal((n, 6)).astype(np.float32)
+        sim = simulate_pose_bank(n, lambda b: P[b], W, B, S)
+        full = False
+        for m in range(n):
+            s, f = sim[m], prsink_schedule(m, W, B, S)
+            assert s["static"] == f["static"] and s["window"] == f["window"] and s["evicted"] == f["evicted"]
+            if not full:
+                assert s["bank"] == f["bank"], (W, B, S, m)
+            full = full or len(s["bank"]) == B
+            if full:
+                assert len(s["bank"]) == B == len(set(s["bank"]))
+                assert all(b < (m - W) for b in s["bank"]) and max(s["bank"]) == m - W - 1
+            if m + 1 < n and s["evicted"] is not None and len(s["bank"]) == B:
+                gone = set(s["bank"]) - set(sim[m + 1]["bank"])
+                assert len(gone) == 1
+                e = s["evicted"]
+                cos = {b: float(P[b].astype(np.float64) @ P[e] / (np.linalg.norm(P[b].astype(np.float64))
+                                                                  * np.linalg.norm(P[e].astype(np.float64))))
+                       for b in s["bank"]}
+                assert gone.pop() == max(cos, key=cos.get), (W, B, S, m)

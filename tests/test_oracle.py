@@ -46,6 +46,45 @@ def test_constant_context_size():
     assert all(x == 13312 for x in n[5:]) and n[4] != 13312
 
 
+def test_pose_bank_golden():
+    pins.check_pose_bank_golden(oracle.simulate_prsink_pose_bank)
+
+
+def test_pose_bank_properties(rng):
+    pins.check_pose_bank_properties(oracle.simulate_prsink_pose_bank, oracle.prsink_schedule, rng)
+
+
+def test_pose_bank_without_replacement_is_fifo():
+    """A bank that never fills never replaces: outputs equal the FIFO stream's."""
+    cfg = synth.workload("tiny_fp32", rope=(24, 20, 20), dynamic_k=2, bank=16)
+    pcfg = dict(cfg, bank_policy="pose")
+    a, b = oracle.PRSinkReference(cfg, SynthProvider(cfg)), oracle.PRSinkReference(pcfg, SynthProvider(pcfg))
+    for m in range(cfg["blocks"]):
+        assert a.selection(m) == b.selection(m)
+        assert np.array_equal(a.attend(m, 0, 0), b.attend(m, 0, 0)), m
+
+
+@pytest.mark.parametrize("name", ["prsink_512_posebank"])
+def test_pose_bank_stream_has_no_near_ties(name):
+    """Every replacement and every retrieval of the pose-aware stream is
+    decided by a gap far above fp64 resolution (or an exact tie)."""
+    cfg = synth.workload(name)
+    n = cfg["blocks"]
+    P = synth.poses(cfg, n)
+    sim = oracle.simulate_prsink_pose_bank(n, lambda b: P[b], cfg["window"], cfg["bank"], cfg["static"])
+    replaced = 0
+    for m in range(n):
+        s = sim[m]
+        bank = [(b, P[b]) for b in s["bank"]]
+        g = oracle.boundary_gap(P[m], bank, cfg["dynamic_k"])
+        assert g is None or g == 0 or g > 2.0 ** -40, (m, float(g))
+        if s["evicted"] is not None and len(s["bank"]) == cfg["bank"]:
+            g = oracle.boundary_gap(P[s["evicted"]], bank, 1)
+            assert g is None or g == 0 or g > 2.0 ** -40, (m, float(g))
+            replaced += 1
+    assert replaced > 30
+
+
 def test_retrieval_hand_values():
     pins.check_retrieval_hand(oracle.retrieve)
 

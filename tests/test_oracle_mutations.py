@@ -378,3 +378,53 @@ def test_convkv_absolute_mutants_fail(mutant):
                                      rope=(6, 4, 6), blocks=9, positions=pos)
     assert _fails(pins.check_convkv_absolute, mutant, oracle.token_positions, oracle.apply_rope, cfg,
                   SynthProvider)
+
+
+# -- pose-aware bank mutants ---------------------------------------------------
+def _pose_bank_fifo(n, pose, window=3, bank=8, static=1):
+    return oracle.simulate_prsink(n, window, bank, static)
+
+
+def _pose_bank_least_similar(n, pose, window=3, bank=8, static=1):
+    statics, win, bnk, out = [], deque(), [], []
+    for m in range(n):
+        rec = {"static": list(statics), "bank": list(bnk), "window": list(win), "evicted": None}
+        if len(statics) < static:
+            statics.append(m)
+        else:
+            win.append(m)
+            if len(win) > window:
+                e = win.popleft()
+                rec["evicted"] = e
+                if bank > 0:
+                    if len(bnk) == bank:
+                        keys = R.exact_keys(pose(e), [(b, pose(b)) for b in bnk])
+                        bnk.remove(bnk[min(range(len(bnk)), key=lambda i: (keys[i], bnk[i]))])
+                    bnk.append(e)
+        out.append(rec)
+    return out
+
+
+def _pose_bank_ties_high(n, pose, window=3, bank=8, static=1):
+    statics, win, bnk, out = [], deque(), [], []
+    for m in range(n):
+        rec = {"static": list(statics), "bank": list(bnk), "window": list(win), "evicted": None}
+        if len(statics) < static:
+            statics.append(m)
+        else:
+            win.append(m)
+            if len(win) > window:
+                e = win.popleft()
+                rec["evicted"] = e
+                if bank > 0:
+                    if len(bnk) == bank:
+                        keys = R.exact_keys(pose(e), [(b, pose(b)) for b in bnk])
+                        bnk.remove(bnk[max(range(len(bnk)), key=lambda i: (keys[i], bnk[i]))])
+                    bnk.append(e)
+        out.append(rec)
+    return out
+
+
+@pytest.mark.parametrize("mutant", [_pose_bank_fifo, _pose_bank_least_similar, _pose_bank_ties_high])
+def test_pose_bank_mutants_fail(mutant):
+    assert _fails(pins.check_pose_bank_golden, mutant)
