@@ -37,7 +37,7 @@ def parse():
     ap.add_argument("--steps", type=int, default=40)
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--workload", default="prsink_512",
-                    choices=["prsink_512", "prsink_512_fp8k", "prsink_512_qkv", "prsink_512_ref", "prsink_512_rel",
+                    choices=["prsink_512", "prsink_512_fp8k", "prsink_512_qkv", "prsink_512_ref", "prsink_512_rel", "prsink_512_posebank",
                              "prsink_720x416",
                              "prsink_long", "convkv_512", "convkv_512_abs", "tiny_fp32"])
     ap.add_argument("--pool", type=int, default=4, help="distinct resident input blocks cycled through")
@@ -265,7 +265,7 @@ def main():
         m += 1
     torch.cuda.synchronize()
     n_keys = []
-    launches = args.steps * (2 + 2 * L * S + L) + 16
+    launches = args.steps * (3 + 2 * L * S + L) + 16
     cache.profile_start(launches)
     ev = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps + 1)]
     torch.cuda.synchronize()
@@ -346,7 +346,8 @@ def main():
                    "timed_blocks": [m - args.steps, m - 1],
                    **({"model_dim": cfg["model_dim"], "qkv_projection": "fused (bkv_attend_qkv)"} if fused else {}),
                    **({"reference_frames": cfg["reference_frames"]} if cfg.get("reference_frames") else {}),
-                   **({"positions": cfg["positions"]} if cfg.get("positions", "default") != "default" else {})},
+                   **({"positions": cfg["positions"]} if cfg.get("positions", "default") != "default" else {}),
+                   **({"bank_policy": cfg["bank_policy"]} if cfg.get("bank_policy", "fifo") != "fifo" else {})},
         "attention_tflops": attn_tflops,
         "attention_pct_peak": 100.0 * attn_tflops / peak,
         "attention_peak_tflops": peak,

@@ -18,6 +18,7 @@ PR_SINK, CONVKV = 0, 1
 F32, BF16, BF16_FP8K = 0, 1, 2
 DTYPES = {"f32": F32, "bf16": BF16, "bf16_fp8k": BF16_FP8K}
 POSITIONS = {"default": 0, "relative": 1, "absolute": 2}     # bkv_positions
+BANK_POLICIES = {"fifo": 0, "pose": 1}                        # bkv_bank_policy
 SEG_KINDS = {0: "static", 1: "dynamic", 2: "window", 3: "current", 4: "memory", 5: "reference"}
 
 # every symbol include/bkv.h declares
@@ -38,7 +39,7 @@ class Config(ctypes.Structure):
                 ("rope_theta", ctypes.c_double), ("conv_kernel", ctypes.c_int32),
                 ("conv_stride", ctypes.c_int32), ("memory_frames", ctypes.c_int32),
                 ("softmax_scale", ctypes.c_float), ("reference_frames", ctypes.c_int32),
-                ("rope_positions", ctypes.c_int32)]
+                ("rope_positions", ctypes.c_int32), ("bank_policy", ctypes.c_int32)]
 
 
 class Segment(ctypes.Structure):
@@ -134,6 +135,7 @@ def config_from_workload(w: dict) -> Config:
     c.softmax_scale = float(w.get("softmax_scale", 0.0))
     c.reference_frames = int(w.get("reference_frames", 0) or 0)
     c.rope_positions = POSITIONS[w.get("positions", "default")]
+    c.bank_policy = BANK_POLICIES[w.get("bank_policy", "fifo")]
     return c
 
 

@@ -41,7 +41,7 @@ struct Layout {
   int t_rows;                        // rows of the temporal RoPE table
   size_t slot_bytes, slot_v_off, layer_kv_bytes;
   size_t off_kv, off_ctx, ctx_layer_bytes, off_mem, mem_layer_bytes, mem_v_off;
-  size_t off_pose, off_sel, off_tt, off_th, off_tw, off_w, total;
+  size_t off_pose, off_sel, off_victim, off_tt, off_th, off_tw, off_w, total;
   bool split;                        // bf16 attention shares key tiles across workgroups
   size_t off_split, off_cnt;
   bool kf8;                          // FP8 key cache: E4M3 K rows + tile exponents in a slot
@@ -90,12 +90,17 @@ bkv_status validate(const bkv_config* c) {
     if (c->pose_dim < 0) return fail(BKV_ERR_ARG, "pose_dim must be >= 0");
     if (c->reference_frames < 0 || c->reference_frames > 8)
       return fail(BKV_ERR_ARG, "reference_frames must be 0..8");
+    if (c->bank_policy != BKV_BANK_FIFO && c->bank_policy != BKV_BANK_POSE)
+      return fail(BKV_ERR_ARG, "bad bank_policy %d", c->bank_policy);
+    if (c->bank_policy == BKV_BANK_POSE && (c->pose_dim < 1 || c->bank_blocks < 1))
+      return fail(BKV_ERR_ARG, "pose-aware bank replacement needs pose_dim >= 1 and bank_blocks >= 1");
     if (c->rope_positions == BKV_POS_CONTEXT && c->dtype == BKV_BF16_FP8K)
       return fail(BKV_ERR_UNSUPPORTED, "context-relative positions are implemented without the FP8 key cache");
     if ((c->reference_frames > 0) + c->static_blocks + c->dynamic_k + c->window_blocks + 1 > bkv::kMaxSeg)
       return fail(BKV_ERR_ARG, "more than %d context segments", bkv::kMaxSeg);
   } else {
     if (c->reference_frames != 0) return fail(BKV_ERR_UNSUPPORTED, "reference frames are implemented for PR-Sink only");
+    if (c->bank_policy != BKV_BANK_FIFO) return fail(BKV_ERR_ARG, "ConvKV has no bank");
     if (c->static_blocks != 0 || c->dynamic_k != 0 || c->bank_blocks != 0)
       return fail(BKV_ERR_ARG, "ConvKV takes no static/dynamic sinks or bank");
     if (c->conv_kernel < 1 || c->conv_kernel > 8 || c->conv_stride != c->conv_kernel)
@@ -179,6 +184,8 @@ Layout layout_of(const bkv_config* c, const bkv::Schedule& sch) {
   off = align_up(off + sizeof(float) * (size_t)L.n_slots * (P > 0 ? P : 1), 256);
   L.off_sel = off;
   off = align_up(off + 2 * sizeof(int) * bkv::kMaxK, 256);
+  L.off_victim = off;                // pose-aware replacement: displaced id and slot
+  if (c->mode == BKV_PR_SINK && c->bank_policy == BKV_BANK_POSE) off = align_up(off + 2 * sizeof(int), 256);
   L.t_rows = sch.ctx_mode() ? sch.max_context_frames() : c->frames_per_block;
   L.off_tt = off;
   off = align_up(off + sizeof(float2) * (size_t)L.t_rows * (c->rope_t / 2 + 1), 256);
@@ -339,9 +346,9 @@ bkv_status check_handle(bkv_cache h, bool need_ok = true) {
   return BKV_OK;
 }
 
-enum { K_RETRIEVE = 0, K_APPEND, K_ATTENTION, K_GATHER, K_CONV, K_EXPORT, K_QKV, K_COUNT };
+enum { K_RETRIEVE = 0, K_APPEND, K_ATTENTION, K_GATHER, K_CONV, K_EXPORT, K_QKV, K_REPLACE, K_COUNT };
 const char* const kKernelNames[K_COUNT] = {"retrieve", "append", "attention", "gather", "conv", "export",
-                                           "qkv"};
+                                           "qkv", "replace"};
 
 // Run `launch`, bracketed by event records on `s` while a profile is recording.
 template <class F>
@@ -769,8 +776,40 @@ bkv_status bkv_commit(bkv_cache h, hipStream_t stream) {
   if (!h->sched.is_open()) return fail(BKV_ERR_STATE, "commit with no open block");
   if (!h->sched.all_attended()) return fail(BKV_ERR_STATE, "commit before every layer was attended");
   if ((st = set_device(h)) != BKV_OK) return st;
+  int displace = -1;
+  if (h->cfg.mode == BKV_PR_SINK && h->cfg.bank_policy == BKV_BANK_POSE && h->sched.bank_full()) {
+    const auto ev = h->sched.pending_eviction();
+    if (ev.first >= 0) {
+      // rank the bank against the leaving block's stored pose, top 1
+      bkv::OpenArgs a{};
+      a.query = h->pose_store() + (size_t)ev.second * h->cfg.pose_dim;
+      a.pose_store = h->pose_store();
+      a.P = h->cfg.pose_dim;
+      a.cur_slot = -1;
+      a.k = 1;
+      a.nbank = (int)h->sched.bank().size();
+      for (int i = 0; i < a.nbank; ++i) {
+        a.bank_id[i] = (int)h->sched.bank()[i].first;
+        a.bank_slot[i] = h->sched.bank()[i].second;
+      }
+      int* vic = reinterpret_cast<int*>(h->ws + h->L.off_victim);
+      a.sel_ids = vic;
+      a.sel_slots = vic + 1;
+      int got = -1;
+      hipError_t e = timed(h, K_REPLACE, stream, [&] { return bkv::launch_open(a, stream); });
+      if (e == hipSuccess) e = hipMemcpyAsync(&got, vic, sizeof(int), hipMemcpyDeviceToHost, stream);
+      if (e == hipSuccess) e = hipStreamSynchronize(stream);
+      if (e != hipSuccess) return device_fail(h, e, "bank replacement");
+      for (int i = 0; i < a.nbank; ++i)
+        if (a.bank_id[i] == got) displace = i;
+      if (displace < 0) {
+        h->error = true;
+        return fail(BKV_ERR_DEVICE, "bank replacement returned id %d, not a bank member", got);
+      }
+    }
+  }
   std::vector<bkv::ConvTap> taps;
-  h->sched.commit(&taps);
+  h->sched.commit(&taps, displace);
   h->ctx_ready.assign(h->cfg.layers, false);
   if (!taps.empty()) {
     const int K = h->cfg.conv_kernel;

@@ -124,11 +124,12 @@ __global__ __launch_bounds__(kOpenThreads) void open_kernel(OpenArgs a) {
   }
   if (a.k <= 0 || a.nbank <= 0) return;
   const int nb = a.nbank;
+  const float* qsrc = a.query ? a.query : a.pose_in;
   double qq = 0.0, dot = 0.0, bb = 0.0;
   for (int c0 = 0; c0 < a.P; c0 += kOpenChunk) {
     const int w = min(kOpenChunk, a.P - c0);
     __syncthreads();                       // the previous chunk has been consumed
-    if (tid < w) s_q[tid] = a.pose_in[c0 + tid];
+    if (tid < w) s_q[tid] = qsrc[c0 + tid];
     for (int idx = tid; idx < nb * w; idx += kOpenThreads) {
       const int c = idx / w, i = idx - c * w;
       s_b[c][i] = a.pose_store[(size_t)a.bank_slot[c] * a.P + c0 + i];

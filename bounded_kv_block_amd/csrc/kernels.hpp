@@ -100,7 +100,8 @@ struct QkvArgs {
 
 // Retrieval + block-open work, one workgroup.
 struct OpenArgs {
-  const float* pose_in;     // [P] caller's pose (null: none)
+  const float* pose_in;     // [P] caller's pose, stored at cur_slot (null: none)
+  const float* query;       // [P] pose ranked against the bank (null: pose_in)
   float* pose_store;        // [n_slots][P]
   int P, cur_slot, nbank, k;
   int* sel_ids;             // [k] out

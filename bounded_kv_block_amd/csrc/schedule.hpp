@@ -152,6 +152,15 @@ class Schedule {
     return true;
   }
 
+  // The block that would leave the window at the next commit, with its slot
+  // ({-1, -1} if none), and whether the bank is full.
+  std::pair<int64_t, int> pending_eviction() const {
+    if (!open_ || s_.convkv || (int)static_.size() < s_.statics) return {-1, -1};
+    if ((int)window_.size() + 1 <= s_.window) return {-1, -1};
+    return window_.front();
+  }
+  bool bank_full() const { return s_.bank > 0 && (int)bank_.size() == s_.bank; }
+
   bool all_attended() const {
     for (bool a : attended_)
       if (!a) return false;
@@ -160,7 +169,9 @@ class Schedule {
 
   // Close the open block.  On success fills `taps` (ConvKV: the frames the
   // memory is rebuilt from, tap order, n_mem*kernel entries; empty = none).
-  bool commit(std::vector<ConvTap>* taps) {
+  // PR-Sink: `displace` >= 0 names the bank position the leaving block
+  // replaces when the bank is full (pose-aware replacement); -1 = FIFO.
+  bool commit(std::vector<ConvTap>* taps, int displace = -1) {
     if (!open_ || !all_attended()) return false;
     taps->clear();
     const int64_t m = next_;
@@ -175,6 +186,10 @@ class Schedule {
           window_.pop_front();
           last_evicted_ = e.first;
           if (s_.bank > 0) {
+            if (displace >= 0 && displace < (int)bank_.size() && (int)bank_.size() == s_.bank) {
+              free_.push_back(bank_[displace].second);
+              bank_.erase(bank_.begin() + displace);
+            }
             bank_.push_back(e);
             if ((int)bank_.size() > s_.bank) {
               free_.push_back(bank_.front().second);

@@ -93,6 +93,16 @@ typedef enum { BKV_F32 = 0, BKV_BF16 = 1, BKV_BF16_FP8K = 2 } bkv_dtype;
      literal alternative reading of the same passage). */
 typedef enum { BKV_POS_DEFAULT = 0, BKV_POS_CONTEXT = 1, BKV_POS_ABSOLUTE = 2 } bkv_positions;
 
+/* PR-Sink bank replacement (bkv_config.bank_policy).  The LiveAnimate page
+   (section 关键发现) keeps a fixed number of blocks without saying which
+   leave.  BKV_BANK_FIFO: the bank holds the last bank_blocks blocks that left
+   the window.  BKV_BANK_POSE: a block leaving the window into a full bank
+   displaces the member whose pose has the largest cosine with its own
+   (fp64, ranked as retrieval ranks: exact ties displace the lower stream id;
+   a zero pose scores 0), and joins the bank; needs pose_dim >= 1 and
+   bank_blocks >= 1. */
+typedef enum { BKV_BANK_FIFO = 0, BKV_BANK_POSE = 1 } bkv_bank_policy;
+
 typedef enum {
   BKV_SEG_STATIC = 0,   /* static sink block */
   BKV_SEG_DYNAMIC = 1,  /* pose-retrieved bank block */
@@ -129,6 +139,7 @@ typedef struct {
                                bkv_set_reference. */
   int32_t rope_positions;   /* bkv_positions: temporal RoPE positions of the context (0 = the
                                mode's own reading) */
+  int32_t bank_policy;      /* PR-Sink: bkv_bank_policy (0 = FIFO); ConvKV: 0 */
 } bkv_config;
 
 /* One context segment as the open block sees it (host view). */
@@ -240,8 +251,10 @@ bkv_status bkv_attend_qkv(bkv_cache h, int32_t layer, const void* x, const void*
                           int32_t model_dim, void* out, hipStream_t stream);
 
 /* Close the open block: it joins the window; the oldest window block leaves
-   (PR-Sink: into the FIFO bank, the oldest bank block dropped when full;
-   ConvKV: its raw frames feed the conv memory, rebuilt here on `stream` once
+   (PR-Sink: into the bank, the oldest bank block dropped when full -- or,
+   with BKV_BANK_POSE, the member most similar by pose, found on `stream`;
+   the call then synchronizes `stream` to read that member's id; ConvKV: its
+   raw frames feed the conv memory, rebuilt here on `stream` once
    conv_kernel frames were evicted).  Errors: BKV_ERR_STATE if no block is open
    or some layer was not attended in this block. */
 bkv_status bkv_commit(bkv_cache h, hipStream_t stream);

@@ -19,6 +19,13 @@ void* sched_new_ref(int layers, int frames, int tpf, int window, int statics, in
   Schedule::Shape s{false, layers, frames, tpf, window, statics, k, bank, 1, 0, ref_frames, relative != 0};
   return new Schedule(s);
 }
+// commit with the bank position the leaving block displaces (-1: FIFO)
+int sched_commit_displace(void* p, int displace) {
+  std::vector<bkv::ConvTap> taps;
+  return static_cast<Schedule*>(p)->commit(&taps, displace) ? 1 : 0;
+}
+int64_t sched_pending(void* p) { return static_cast<Schedule*>(p)->pending_eviction().first; }
+int sched_bank_full(void* p) { return static_cast<Schedule*>(p)->bank_full() ? 1 : 0; }
 void sched_free(void* p) { delete static_cast<Schedule*>(p); }
 int sched_n_slots(void* p) { return static_cast<Schedule*>(p)->n_slots(); }
 int sched_open(void* p) { return static_cast<Schedule*>(p)->open() ? 1 : 0; }

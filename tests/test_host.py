@@ -39,6 +39,10 @@ def shim(tmp_path_factory):
     L.sched_segments.argtypes = [ctypes.c_void_p, ctypes.POINTER(ctypes.c_int64), ctypes.c_int]
     L.sched_bank.argtypes = [ctypes.c_void_p, ctypes.POINTER(ctypes.c_int64), ctypes.POINTER(ctypes.c_int),
                              ctypes.c_int]
+    L.sched_commit_displace.argtypes = [ctypes.c_void_p, ctypes.c_int]
+    L.sched_pending.argtypes = [ctypes.c_void_p]
+    L.sched_pending.restype = ctypes.c_int64
+    L.sched_bank_full.argtypes = [ctypes.c_void_p]
     return L
 
 
@@ -145,6 +149,39 @@ def test_prsink_reference_segment(shim, R):
         for x in (s, s0):
             shim.sched_mark(x.p, 0)
             assert x.commit()[0] == 1
+
+
+@pytest.mark.parametrize("W,B,S", [(3, 4, 1), (1, 2, 1), (2, 1, 0)])
+def test_prsink_pose_bank_state_machine(shim, W, B, S):
+    """Pose-aware replacement in the host state machine: the pending
+    eviction and bank-full flags, and commits with the displaced bank
+    position the oracle's exact ranking picks, reproduce the oracle's bank
+    on every block; slots stay distinct and a block keeps its slot."""
+    rng = np.random.default_rng(7)
+    P = rng.standard_normal((60, 5)).astype(np.float32)
+    sim = oracle.simulate_prsink_pose_bank(60, lambda b: P[b], W, B, S)
+    s = Sched(shim, frames=2, tpf=4, window=W, statics=S, k=1, bank=B)
+    n_slots = shim.sched_n_slots(s.p)
+    slot_of = {}
+    for m in range(59):
+        assert shim.sched_open(s.p) == 1
+        bank_ids, bank_slots = s.bank()
+        assert bank_ids == sim[m]["bank"], m
+        slot_of[m] = shim.sched_cur_slot(s.p)
+        for b, sl in zip(bank_ids, bank_slots):
+            assert sl == slot_of[b]
+        live = [g[4] for g in s.segments() if g[0] != DYNAMIC] + bank_slots
+        assert len(set(live)) == len(live) and all(0 <= x < n_slots for x in live)
+        ev = shim.sched_pending(s.p)
+        assert ev == (-1 if sim[m]["evicted"] is None else sim[m]["evicted"])
+        full = shim.sched_bank_full(s.p) == 1
+        assert full == (len(bank_ids) == B)
+        displace = -1
+        if ev >= 0 and full:
+            victim = oracle.retrieve(P[ev], [(b, P[b]) for b in bank_ids], 1)[0]
+            displace = bank_ids.index(victim)
+        shim.sched_mark(s.p, 0)
+        assert shim.sched_commit_displace(s.p, displace) == 1
 
 
 @pytest.mark.parametrize("R,k", [(0, 2), (2, 3), (1, 0)])
@@ -355,6 +392,30 @@ def test_relative_positions_workspace_and_validation():
             == bkv.workspace_size(bkv.config_from_workload(synth.workload("convkv_512"))))
     c = bkv.config_from_workload(synth.workload("convkv_512"))
     c.rope_positions = 3
+    with pytest.raises(bkv.BkvError) as ei:
+        bkv.workspace_size(c)
+    assert ei.value.status == bkv.BKV_ERR_ARG
+
+
+def test_pose_bank_validation():
+    """Pose-aware replacement needs poses and a bank; ConvKV has no bank; an
+    unknown policy is rejected.  It adds one 256-byte block to the workspace."""
+    from bounded_kv_block_amd import bkv, synth
+    n0 = bkv.workspace_size(bkv.config_from_workload(synth.workload("prsink_512", bank=8)))
+    n1 = bkv.workspace_size(bkv.config_from_workload(synth.workload("prsink_512_posebank")))
+    assert n1 - n0 == 256
+    for w in (synth.workload("prsink_512_posebank", bank=0), synth.workload("prsink_512_posebank", pose_dim=0,
+                                                                          dynamic_k=0)):
+        with pytest.raises(bkv.BkvError) as ei:
+            bkv.workspace_size(bkv.config_from_workload(w))
+        assert ei.value.status == bkv.BKV_ERR_ARG
+    c = bkv.config_from_workload(synth.workload("convkv_512"))
+    c.bank_policy = 1
+    with pytest.raises(bkv.BkvError) as ei:
+        bkv.workspace_size(c)
+    assert ei.value.status == bkv.BKV_ERR_ARG
+    c = bkv.config_from_workload(synth.workload("prsink_512"))
+    c.bank_policy = 2
     with pytest.raises(bkv.BkvError) as ei:
         bkv.workspace_size(c)
     assert ei.value.status == bkv.BKV_ERR_ARG
