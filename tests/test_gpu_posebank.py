@@ -87,3 +87,33 @@ def test_posebank_prsink_512_full_shape_sampled():
     _, replaced = _stream(cfg, host_inputs=False, check={6, 20, 39}, heads=[0, 39],
                           rows=np.r_[0:64, 1500:1532, 3008:3072])
     assert replaced >= 25
+
+
+@pytest.mark.parametrize("variant", [
+    dict(dtype="bf16_fp8k", reference_frames=1),
+    dict(positions="relative", reference_frames=2),
+    dict(positions="relative", layers=2, steps=2),
+])
+def test_posebank_combined_with_other_variants(variant):
+    """Pose-aware replacement together with the FP8 key cache and a reference
+    frame, with context-relative positions and two reference frames, and with
+    context-relative positions over 2 layers x 2 steps: the bank, the
+    retrieved ids and every output of a 24-block stream (6x10 grid, 3 frames,
+    bank 3, top-2)."""
+    cfg = synth.workload("prsink_512_posebank", heads=2, grid_h=6, grid_w=10, bank=3, blocks=24, pose_dim=16,
+                         keyframes=4, **variant)
+    run = Run(cfg)
+    ref = oracle.PRSinkReference(cfg, run)
+    tol = TOL[cfg["dtype"]]
+    for m in range(cfg["blocks"]):
+        run.open(m)
+        sel = ref.selection(m)
+        assert run.cache.selection() == sel, m
+        assert run.cache.stats()["bank_count"] == len(ref.schedule(m)["bank"])
+        assert run.cache.context() == ref.context(m, sel), m
+        for s in range(cfg["steps"]):
+            for l in range(cfg["layers"]):
+                out = run.attend(m, l, s)
+                err = max_err(out, ref.attend(m, l, s, selection=sel))
+                assert err <= tol, (m, l, s, err)
+        run.cache.commit()
