@@ -361,6 +361,31 @@ def main():
                      "flop_per_launch": flop_attend, "avg_launch_us": 1e3 * attn_avg_ms},
         "workspace_bytes": int(cache.stats()["workspace_bytes"]),
     }
+    # what the device sustains right after the timed region: the bf16 MFMA
+    # rate of an MFMA-only loop (same instruction, 2 waves per SIMD) and a
+    # 1 GiB device copy
+    mfma_s = bkv.probe_mfma(1024, 40000, dev)
+    src = torch.empty(1 << 30, dtype=torch.uint8, device=dev).fill_(1)
+    dst = torch.empty_like(src)
+    dst.copy_(src)
+    cev = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
+    cev[0].record()
+    for _ in range(5):
+        dst.copy_(src)
+    cev[1].record()
+    torch.cuda.synchronize()
+    copy_gbs = 2 * (1 << 30) * 5 / (cev[0].elapsed_time(cev[1]) * 1e-3) / 1e9
+    del src, dst
+    res["sustained"] = {"mfma_bf16_tflops": mfma_s, "copy_gbs": copy_gbs,
+                        "how": "bkv_probe_mfma(1024 workgroups x 8 waves, 40000 rounds of 8 independent "
+                               "v_mfma_f32_32x32x16_bf16 on pseudo-random full-mantissa operands) and 5 "
+                               "device-to-device copies of 1 GiB, event-timed after the timed region"}
+    if bf16 and not fp8k:
+        res["roofline"]["frac_sustained"] = attn_tflops / mfma_s
+    for name in ("append", "gather", "conv"):
+        if name in kernels and "gbs" in kernels[name]:
+            kernels[name]["frac_hbm_peak"] = kernels[name]["gbs"] / PEAK_HBM_GBS
+            kernels[name]["frac_copy"] = kernels[name]["gbs"] / copy_gbs
     if not args.no_cpu_baseline:
         res["cpu_baseline"] = cpu_baseline(cfg, block_inputs, poses_np, m - 1, args.cpu_seconds,
                                            weights[0] if fused else None)

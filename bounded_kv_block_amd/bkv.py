@@ -26,7 +26,7 @@ EXPORTS = ("bkv_workspace_size", "bkv_create", "bkv_destroy", "bkv_reset", "bkv_
            "bkv_set_reference",
            "bkv_profile_start", "bkv_profile_stop",
            "bkv_retrieve", "bkv_attend", "bkv_attend_qkv", "bkv_commit", "bkv_selection", "bkv_context", "bkv_stats",
-           "bkv_export_segment", "bkv_status_str", "bkv_last_error")
+           "bkv_export_segment", "bkv_status_str", "bkv_last_error", "bkv_probe_mfma")
 
 
 class Config(ctypes.Structure):
@@ -94,6 +94,7 @@ def lib() -> ctypes.CDLL:
             "bkv_export_segment": [vp, i32, i32, vp, vp, vp],
             "bkv_profile_start": [vp, i32],
             "bkv_profile_stop": [vp, ctypes.POINTER(KernelTime), i32, ctypes.POINTER(i32)],
+            "bkv_probe_mfma": [i32, i32, ctypes.POINTER(ctypes.c_double), vp],
         }
         for name, args in sig.items():
             fn = getattr(L, name)
@@ -304,3 +305,13 @@ class Cache:
             self.close()
         except Exception:
             pass
+
+
+def probe_mfma(workgroups: int = 1024, iters: int = 4000, device="cuda") -> float:
+    """Sustained bf16 MFMA rate in TFLOP/s (bkv_probe_mfma) on ``device``."""
+    import torch
+    dev = torch.device(device)
+    with torch.cuda.device(dev):
+        t = ctypes.c_double()
+        _check(lib().bkv_probe_mfma(workgroups, iters, ctypes.byref(t), _stream(torch, dev)), "bkv_probe_mfma")
+    return t.value

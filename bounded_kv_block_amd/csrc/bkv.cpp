@@ -948,6 +948,28 @@ bkv_status bkv_export_segment(bkv_cache h, int32_t layer, int32_t seg, void* k_o
   return BKV_OK;
 }
 
+bkv_status bkv_probe_mfma(int32_t workgroups, int32_t iters, double* tflops, hipStream_t stream) {
+  if (workgroups < 1 || iters < 1 || !tflops) return fail(BKV_ERR_ARG, "workgroups and iters must be >= 1, tflops non-null");
+  float* sink = nullptr;
+  hipEvent_t e0 = nullptr, e1 = nullptr;
+  hipError_t e = hipMalloc(&sink, sizeof(float));
+  if (e == hipSuccess) e = hipEventCreate(&e0);
+  if (e == hipSuccess) e = hipEventCreate(&e1);
+  if (e == hipSuccess) e = bkv::launch_mfma_probe(workgroups, 1, sink, stream);   // warm the code path
+  if (e == hipSuccess) e = hipEventRecord(e0, stream);
+  if (e == hipSuccess) e = bkv::launch_mfma_probe(workgroups, iters, sink, stream);
+  if (e == hipSuccess) e = hipEventRecord(e1, stream);
+  if (e == hipSuccess) e = hipEventSynchronize(e1);
+  float ms = 0.f;
+  if (e == hipSuccess) e = hipEventElapsedTime(&ms, e0, e1);
+  if (e0) (void)hipEventDestroy(e0);
+  if (e1) (void)hipEventDestroy(e1);
+  if (sink) (void)hipFree(sink);
+  if (e != hipSuccess) return fail(BKV_ERR_DEVICE, "MFMA probe: %s", hipGetErrorString(e));
+  *tflops = (double)workgroups * 8.0 * iters * 8.0 * 32768.0 / (ms * 1e-3) / 1e12;
+  return BKV_OK;
+}
+
 bkv_status bkv_profile_start(bkv_cache h, int32_t max_launches) {
   if (!h) return fail(BKV_ERR_ARG, "null handle");
   if (h->prof.on) return fail(BKV_ERR_STATE, "a profile is already recording");

@@ -1797,6 +1797,42 @@ hipError_t launch_conv(const ConvArgs& a, bool bf16, hipStream_t s) {
   return hipGetLastError();
 }
 
+// Sustained-rate probe: 8 independent accumulator chains per wave, operands
+// in registers, no memory traffic in the loop.  The operands are
+// full-mantissa pseudo-random values in [-2, 2) (a multiplicative hash of the
+// thread and element), since the matrix core's power -- and so the clock it
+// sustains -- depends on the data.  The sum is written only if it is NaN,
+// which finite operands cannot produce, so the work stays live.
+__global__ __launch_bounds__(512) void mfma_probe_kernel(float* sink, int iters) {
+  bf16x8 x, y;
+  const unsigned t = blockIdx.x * 512u + threadIdx.x;
+#pragma unroll
+  for (int e = 0; e < 8; ++e) {
+    const unsigned hx = (t * 2654435761u) ^ ((unsigned)e * 2246822519u);
+    const unsigned hy = (t * 3266489917u) ^ ((unsigned)e * 668265263u);
+    x[e] = (__bf16)((float)(int)((hx >> 8) & 0xffff) / 16384.f - 2.f);
+    y[e] = (__bf16)((float)(int)((hy >> 8) & 0xffff) / 16384.f - 2.f);
+  }
+  f32x16 c[8];
+#pragma unroll
+  for (int j = 0; j < 8; ++j) c[j] = f32x16{};
+  for (int i = 0; i < iters; ++i) {
+#pragma unroll
+    for (int j = 0; j < 8; ++j) c[j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(x, y, c[j], 0, 0, 0);
+  }
+  float s = 0.f;
+#pragma unroll
+  for (int j = 0; j < 8; ++j)
+#pragma unroll
+    for (int e = 0; e < 16; ++e) s += c[j][e];
+  if (s != s) sink[0] = s;
+}
+
+hipError_t launch_mfma_probe(int workgroups, int iters, float* sink, hipStream_t s) {
+  mfma_probe_kernel<<<workgroups, 512, 0, s>>>(sink, iters);
+  return hipGetLastError();
+}
+
 hipError_t launch_export(const ExportArgs& a, bool bf16, hipStream_t s) {
   const long long n = (long long)a.seg.n * a.H * a.D;
   if (n == 0) return hipSuccess;

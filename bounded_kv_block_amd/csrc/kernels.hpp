@@ -172,5 +172,6 @@ inline bool attention_split(int T, int H, bool slots) {
 hipError_t launch_gather(const GatherArgs& a, bool bf16, hipStream_t s);
 hipError_t launch_conv(const ConvArgs& a, bool bf16, hipStream_t s);
 hipError_t launch_export(const ExportArgs& a, bool bf16, hipStream_t s);
+hipError_t launch_mfma_probe(int workgroups, int iters, float* sink, hipStream_t s);
 
 }  // namespace bkv

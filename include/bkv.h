@@ -22,7 +22,8 @@
  * block all read the same context; a block's K/V enter the cache as written by
  * its last bkv_attend per layer (LiveAnimate page, section 方法: three steps).
  *
- * Memory.  The library never allocates device memory.  The caller provides one
+ * Memory.  The path never allocates device memory (the measurement aid
+ * bkv_probe_mfma allocates a 4-byte sink per call).  The caller provides one
  * device workspace of bkv_workspace_size() bytes at create time; the cache,
  * pose bank, RoPE tables, selection and scratch are carved from it, so cache
  * bytes are constant over the stream by construction.  Q/K/V/out, the pose and
@@ -300,6 +301,21 @@ bkv_status bkv_profile_start(bkv_cache h, int32_t max_launches);
    kernel into out[0..*n) (capacity cap) and releases the events.
    Errors: BKV_ERR_STATE if no recording is running; BKV_ERR_ARG if cap is too small. */
 bkv_status bkv_profile_stop(bkv_cache h, bkv_kernel_time* out, int32_t cap, int32_t* n);
+
+/* Measurement aid, not a step of the path: the sustained rate of the bf16
+   matrix instruction the attention and projection kernels use
+   (v_mfma_f32_32x32x16_bf16), for normalising their throughput to what the
+   device sustains under its power limit rather than its nominal clock.
+   Launches `workgroups` workgroups of 8 waves (2 per SIMD, as the attention
+   kernel runs), each wave issuing `iters` rounds of 8 independent MFMAs on
+   register operands holding full-mantissa pseudo-random values (the matrix
+   core's power, and so the sustained clock, depends on the data), between
+   two events on `stream`, and waits for them.
+   *tflops = workgroups * 8 * iters * 8 * 32768 flop / elapsed time.
+   Uses the current device; allocates 4 bytes of device memory per call (the
+   kernel's result sink) and frees it.  Errors: BKV_ERR_ARG for workgroups or
+   iters < 1 or a null tflops; BKV_ERR_DEVICE. */
+bkv_status bkv_probe_mfma(int32_t workgroups, int32_t iters, double* tflops, hipStream_t stream);
 
 /* Human-readable name of a status; message of the calling thread's last error. */
 const char* bkv_status_str(bkv_status s);

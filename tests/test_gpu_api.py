@@ -119,3 +119,15 @@ def _memory_flat(torch):
         seen.add(torch.cuda.memory_allocated())
         assert run.cache.stats()["workspace_bytes"] == ws
     assert len(seen) == 1
+
+
+def test_mfma_probe_rate():
+    """The sustained-rate probe reports a plausible bf16 MFMA rate (between a
+    tenth of and just above the 2.5 PFLOP/s nominal peak), and bad arguments
+    are refused."""
+    from bounded_kv_block_amd import bkv
+    t = bkv.probe_mfma(512, 2000)
+    assert 250.0 < t < 2600.0, t
+    with pytest.raises(bkv.BkvError) as ei:
+        bkv.probe_mfma(0, 10)
+    assert ei.value.status == bkv.BKV_ERR_ARG
