@@ -16,8 +16,12 @@ Readings (beyond those stated in the modules used here):
     three steps), a committed block contributes the K/V of its last step.
   * ConvKV context order is [memory frames, window blocks oldest first,
     current block]; temporal positions run 0, 1, 2, ... over those frames.
-  * PR-Sink with an FP8 key cache (dtype "bf16_fp8k"): K and Q are quantised
-    to E4M3 as ``fp8`` states before Q K^T; V and the softmax are unchanged.
+  * An FP8 key cache (dtype "bf16_fp8k", either policy): the rotated K of
+    each context segment and Q are quantised to E4M3 as ``fp8`` states (K in
+    64-token tiles counted from the segment's first token) before Q K^T; V
+    and the softmax are unchanged.  For ConvKV the memory frames, window
+    blocks and current block are the segments (the SoulX-LiveAct page runs
+    its ConvKV attention in FP8, sections 关键信息速览 and 上手实践).
   * PR-Sink with reference_frames = R > 0 (the LiveAnimate page, section 方法,
     conditions every block on the reference image; the Live Avatar page's
     abstract recalibrates appearance from a cached reference image): the R
@@ -76,10 +80,25 @@ class _Base:
         return apply_rope(xs, t, self.y_tok[tok], self.x_tok[tok], self.split, self.theta)
 
     def _attend(self, q_rot, ks, vs, heads, rows):
+        if self.cfg["dtype"] == "bf16_fp8k":
+            return self._attend_fp8(q_rot, ks, vs, rows)
         k = np.concatenate(ks, axis=0)
         v = np.concatenate([np.asarray(x, np.float64) for x in vs], axis=0)
         o_sub = attention(q_rot, k, v, _scale(self.cfg), rows=rows)
         return o_sub
+
+    def _attend_fp8(self, q_rot, ks, vs, rows):
+        """FP8 key cache: logits from E4M3 Q (in log2 units, one scale per row)
+        and E4M3 K (one scale per 64-token tile of each context segment);
+        quantising Q row by row lets the unrequested rows stay zero."""
+        log2e = 1.0 / np.log(2.0)
+        s = _scale(self.cfg)
+        rs = np.arange(self.T) if rows is None else np.asarray(rows)
+        qe = np.zeros_like(q_rot)
+        qe[rs] = fp8.quantize_queries(q_rot[rs] * (s * log2e)) / log2e
+        k = np.concatenate([fp8.quantize_keys(x) for x in ks], axis=0)
+        v = np.concatenate([np.asarray(x, np.float64) for x in vs], axis=0)
+        return attention(qe, k, v, 1.0, rows=rows)
 
 
 class PRSinkReference(_Base):
@@ -151,19 +170,7 @@ class PRSinkReference(_Base):
         q, _, _ = self.p.qkv(layer, m, step)
         q_rot = self._rot(q, lambda f: t0 + f, heads)
         kv = self.context_kv(m, layer, step, heads, selection)
-        if self.cfg["dtype"] != "bf16_fp8k":
-            return self._attend(q_rot, [x[2] for x in kv], [x[3] for x in kv], heads, rows)
-        # FP8 key cache: logits from E4M3 Q (in log2 units, per-row scale) and
-        # E4M3 K (per 64-token tile scale); quantising Q row by row lets the
-        # unrequested rows stay zero.
-        log2e = 1.0 / np.log(2.0)
-        s = _scale(self.cfg)
-        rs = np.arange(self.T) if rows is None else np.asarray(rows)
-        qe = np.zeros_like(q_rot)
-        qe[rs] = fp8.quantize_queries(q_rot[rs] * (s * log2e)) / log2e
-        k = np.concatenate([fp8.quantize_keys(x[2]) for x in kv], axis=0)
-        v = np.concatenate([x[3] for x in kv], axis=0)
-        return attention(qe, k, v, 1.0, rows=rows)
+        return self._attend(q_rot, [x[2] for x in kv], [x[3] for x in kv], heads, rows)
 
 
 class ConvKVReference(_Base):

@@ -516,3 +516,42 @@ def check_pose_bank_properties(simulate_pose_bank, prsink_schedule, rng):
                                                                   * np.linalg.norm(P[e].astype(np.float64))))
                        for b in s["bank"]}
                 assert gone.pop() == max(cos, key=cos.get), (W, B, S, m)
+
+
+# ------------------------------------------------ FP8 keys at stream level
+def check_fp8_pow2_invariance(Ref, cfgs, make_provider):
+    """FP8 key cache, either policy: multiplying every K by 2^a and every Q by
+    2^-a moves each tile's and each row's power-of-two scale but no E4M3 code
+    (the conv memory is linear in K), so every output is bit-identical; with
+    a = 0 the FP8 output differs from the bf16 reading's (the codes round)."""
+    for cfg in cfgs:
+        base = make_provider(cfg)
+
+        class Scaled:
+            def __init__(self, a):
+                self.a = a
+
+            def qkv(self, layer, block, step):
+                q, k, v = base.qkv(layer, block, step)
+                return (np.asarray(q, np.float64) * 2.0 ** -self.a, np.asarray(k, np.float64) * 2.0 ** self.a,
+                        v)
+
+            def pose(self, b):
+                return base.pose(b)
+
+            def conv_weights(self, layer):
+                return base.conv_weights(layer)
+
+            def reference(self, layer):
+                k, v = base.reference(layer)
+                return np.asarray(k, np.float64) * 2.0 ** self.a, v
+
+        outs = {}
+        for a in (0, 5, -7):
+            ref = Ref(cfg, Scaled(a))
+            outs[a] = [ref.attend(m, 0, 0) for m in (0, cfg["blocks"] - 1)]
+        for a in (5, -7):
+            for x, y in zip(outs[0], outs[a]):
+                assert np.array_equal(x, y), (cfg["name"], a)
+        plain = Ref(dict(cfg, dtype="bf16"), Scaled(0)).attend(cfg["blocks"] - 1, 0, 0)
+        assert not np.array_equal(plain, outs[0][1])

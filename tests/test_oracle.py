@@ -322,6 +322,16 @@ def test_fp8_group_scales(rng):
     pins.check_fp8_groups(oracle.fp8.quantize_keys, oracle.fp8.quantize_queries, rng)
 
 
+def test_fp8_stream_pow2_invariance():
+    small = dict(heads=2, head_dim=128, frames=3, grid_h=2, grid_w=5, rope=(44, 42, 42))
+    cfgs = [synth.workload("prsink_512_fp8k", bank=4, pose_dim=16, keyframes=4, blocks=9, **small),
+            synth.workload("prsink_512_fp8k", bank=4, pose_dim=16, keyframes=4, blocks=9, reference_frames=1,
+                           positions="relative", **small),
+            synth.workload("convkv_512", dtype="bf16_fp8k", blocks=8, **small)]
+    pins.check_fp8_pow2_invariance(oracle.PRSinkReference, cfgs[:2], SynthProvider)
+    pins.check_fp8_pow2_invariance(oracle.ConvKVReference, cfgs[2:], SynthProvider)
+
+
 def test_projection_brute_force(rng):
     pins.check_projection_brute_force(oracle.qkv_projection, rng)
 

@@ -428,3 +428,25 @@ def _pose_bank_ties_high(n, pose, window=3, bank=8, static=1):
 @pytest.mark.parametrize("mutant", [_pose_bank_fifo, _pose_bank_least_similar, _pose_bank_ties_high])
 def test_pose_bank_mutants_fail(mutant):
     assert _fails(pins.check_pose_bank_golden, mutant)
+
+
+# -- FP8 stream mutant: keys rounded to E4M3 without a tile scale ---------------
+class _Fp8Unscaled(oracle.ConvKVReference):
+    """Keys rounded to E4M3 as they are (no per-tile power-of-two scale)."""
+
+    def _attend_fp8(self, q_rot, ks, vs, rows):
+        log2e = 1.0 / np.log(2.0)
+        s = 1.0 / np.sqrt(self.cfg["head_dim"])
+        rs = np.arange(self.T) if rows is None else np.asarray(rows)
+        qe = np.zeros_like(q_rot)
+        qe[rs] = oracle.fp8.quantize_queries(q_rot[rs] * (s * log2e)) / log2e
+        k = np.concatenate([oracle.fp8.e4m3_round(np.asarray(x, np.float64)) for x in ks], axis=0)
+        v = np.concatenate([np.asarray(x, np.float64) for x in vs], axis=0)
+        return oracle.attention(qe, k, v, 1.0, rows=rows)
+
+
+def test_fp8_stream_mutant_fails():
+    from bounded_kv_block_amd import synth
+    from conftest import SynthProvider
+    cfg = synth.workload("convkv_512", dtype="bf16_fp8k", blocks=8, heads=2, frames=3, grid_h=2, grid_w=5)
+    assert _fails(pins.check_fp8_pow2_invariance, _Fp8Unscaled, [cfg], SynthProvider)
