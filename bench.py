@@ -39,7 +39,7 @@ def parse():
     ap.add_argument("--workload", default="prsink_512",
                     choices=["prsink_512", "prsink_512_fp8k", "prsink_512_qkv", "prsink_512_ref", "prsink_512_rel", "prsink_512_posebank",
                              "prsink_720x416",
-                             "prsink_long", "convkv_512", "convkv_512_abs", "tiny_fp32"])
+                             "prsink_long", "convkv_512", "convkv_512_abs", "convkv_512_fp8k", "tiny_fp32"])
     ap.add_argument("--pool", type=int, default=4, help="distinct resident input blocks cycled through")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=12.0, help="target CPU-oracle sample time")
@@ -304,7 +304,10 @@ def main():
     for name, (n, tot, mx) in kt.items():
         kernels[name] = {"launches": int(n), "avg_us": 1e3 * tot / n, "max_us": 1e3 * mx}
     # algorithmic bytes of the HBM-bound kernels, per launch
-    app_bytes = 2.0 * T * H * D * esz + T * H * D * (kesz + esz)   # K, V read token-major; written to the cache
+    # K, V read token-major; rotated K and V^T written (a context gathered per
+    # block -- ConvKV, relative positions -- also keeps the raw K in the slot)
+    ctx_mode = cfg["mode"] == "convkv" or cfg.get("positions") == "relative"
+    app_bytes = 2.0 * T * H * D * esz + T * H * D * (kesz + esz) + (T * H * D * esz if ctx_mode else 0)
     if "append" in kernels:
         kernels["append"]["gbs"] = app_bytes / (kernels["append"]["avg_us"] * 1e-6) / 1e9
     if "qkv" in kernels:
@@ -314,7 +317,7 @@ def main():
         kernels["qkv"]["flop_per_launch"] = g_flop
     if "gather" in kernels:         # re-rotated rows: the context less the current block and the reference
         ctx_rows = Nk - T - cfg.get("reference_frames", 0) * cfg["grid_h"] * cfg["grid_w"]
-        g_bytes = 2.0 * ctx_rows * H * D * esz
+        g_bytes = ctx_rows * H * D * (esz + kesz)      # raw K read, rotated K written (E4M3 with FP8 keys)
         kernels["gather"]["gbs"] = g_bytes / (kernels["gather"]["avg_us"] * 1e-6) / 1e9
     if "conv" in kernels:
         Tf = cfg["grid_h"] * cfg["grid_w"]

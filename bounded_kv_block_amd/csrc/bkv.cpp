@@ -44,8 +44,12 @@ struct Layout {
   size_t off_pose, off_sel, off_victim, off_tt, off_th, off_tw, off_w, total;
   bool split;                        // bf16 attention shares key tiles across workgroups
   size_t off_split, off_cnt;
-  bool kf8;                          // FP8 key cache: E4M3 K rows + tile exponents in a slot
+  bool kf8;                          // FP8 key cache: attention reads E4M3 K with tile exponents
+  bool slot8;                        //   held in the slots (K rotated once, at append); else
+                                     //   slots keep bf16 raw K and the context buffer is FP8
   size_t slot_kx_off;                // byte offset of the exponents [H][Tpad/64] inside a slot
+  int ctx_xtiles;                    // FP8 context buffer: exponents [H][ctx_xtiles] per layer
+  size_t ctx_x_off;                  //   at this byte offset inside the layer's buffer
   size_t off_q;                      // bf16: q scratch [T][H][D] of the fused projection path
   int ref_tok, ref_pad;              // reference frames: tokens, padded to whole key tiles
   size_t ref_bytes, ref_v_off, ref_kx_off, off_ref, off_tref;   // per layer, slot-shaped
@@ -64,8 +68,6 @@ bkv_status validate(const bkv_config* c) {
     return fail(BKV_ERR_ARG, "bad rope_positions %d", c->rope_positions);
   if (c->dtype != BKV_F32 && c->head_dim != 128)
     return fail(BKV_ERR_UNSUPPORTED, "bf16 path supports head_dim 128 (got %d)", c->head_dim);
-  if (c->dtype == BKV_BF16_FP8K && c->mode != BKV_PR_SINK)
-    return fail(BKV_ERR_UNSUPPORTED, "the FP8 key cache is implemented for PR-Sink only");
   if (c->dtype == BKV_F32 && c->head_dim != 64 && c->head_dim != 128)
     return fail(BKV_ERR_UNSUPPORTED, "fp32 path supports head_dim 64 or 128 (got %d)", c->head_dim);
   if (c->frames_per_block < 1 || c->grid_h < 1 || c->grid_w < 1)
@@ -94,8 +96,6 @@ bkv_status validate(const bkv_config* c) {
       return fail(BKV_ERR_ARG, "bad bank_policy %d", c->bank_policy);
     if (c->bank_policy == BKV_BANK_POSE && (c->pose_dim < 1 || c->bank_blocks < 1))
       return fail(BKV_ERR_ARG, "pose-aware bank replacement needs pose_dim >= 1 and bank_blocks >= 1");
-    if (c->rope_positions == BKV_POS_CONTEXT && c->dtype == BKV_BF16_FP8K)
-      return fail(BKV_ERR_UNSUPPORTED, "context-relative positions are implemented without the FP8 key cache");
     if ((c->reference_frames > 0) + c->static_blocks + c->dynamic_k + c->window_blocks + 1 > bkv::kMaxSeg)
       return fail(BKV_ERR_ARG, "more than %d context segments", bkv::kMaxSeg);
   } else {
@@ -133,12 +133,13 @@ Layout layout_of(const bkv_config* c, const bkv::Schedule& sch) {
   const size_t H = c->heads, D = c->head_dim;
   L.esize = c->dtype == BKV_F32 ? 4 : 2;
   L.kf8 = c->dtype == BKV_BF16_FP8K;
+  L.slot8 = L.kf8 && !sch.ctx_mode();
   L.T = sch.tokens();
   L.Tpad = (int)align_up(L.T, bkv::kTokAlign);
   L.Tf = c->grid_h * c->grid_w;
   L.tf_pad = (int)align_up(L.Tf, bkv::kTokAlign);
   L.n_slots = sch.n_slots();
-  if (L.kf8) {
+  if (L.slot8) {
     // [E4M3 K rows H x Tpad x D][int32 exponents H x Tpad/64][bf16 V^T H x D x Tpad]
     L.slot_kx_off = H * L.Tpad * D;
     L.slot_v_off = align_up(L.slot_kx_off + sizeof(int) * H * (L.Tpad / bkv::kTokAlign), 256);
@@ -169,7 +170,9 @@ Layout layout_of(const bkv_config* c, const bkv::Schedule& sch) {
   if (sch.ctx_mode()) {
     // + one tile: the last segment's partial tile reads up to 63 rows past its end
     L.ctx_ld = (int)align_up(sch.ctx_tokens(), bkv::kTokAlign) + bkv::kTokAlign;
-    L.ctx_layer_bytes = align_up(H * L.ctx_ld * D * L.esize, 256);
+    L.ctx_xtiles = sch.ctx_xtiles();
+    L.ctx_x_off = align_up(H * L.ctx_ld * D * (L.kf8 ? 1 : L.esize), 256);
+    L.ctx_layer_bytes = align_up(L.ctx_x_off + (L.kf8 ? sizeof(int) * H * L.ctx_xtiles : 0), 256);
     off = align_up(off + L.ctx_layer_bytes * c->layers, 256);
     L.off_mem = off;
   }
@@ -239,6 +242,7 @@ struct bkv_cache_s {
 
   bool bf16() const { return cfg.dtype != BKV_F32; }   // bf16 Q/K/V/out and V cache
   bool kf8() const { return L.kf8; }
+  bool slot8() const { return L.slot8; }
   bool convkv() const { return cfg.mode == BKV_CONVKV; }
   // ConvKV or context-relative PR-Sink: slots hold raw K; the context's K is
   // rotated per block into the context-K buffer at context positions.
@@ -252,6 +256,17 @@ struct bkv_cache_s {
   int* slot_kx(int l, int s) const { return reinterpret_cast<int*>(slot_k(l, s) + L.slot_kx_off); }
   long long slot_kx_hs() const { return L.Tpad / bkv::kTokAlign; }
   char* ctx_k(int l) const { return ws + L.off_ctx + L.ctx_layer_bytes * l; }
+  int* ctx_x(int l) const { return reinterpret_cast<int*>(ctx_k(l) + L.ctx_x_off); }
+  size_t ctx_esize() const { return kf8() ? 1 : L.esize; }   // bytes per context K value
+  // context-buffer view of a segment's K (rows from ctx_off; FP8: its exponents)
+  void ctx_seg_k(int l, const bkv::SegPlan& p, bkv::Seg& g) const {
+    g.k = ctx_k(l) + (size_t)p.ctx_off * cfg.head_dim * ctx_esize();
+    g.k_hs = (long long)L.ctx_ld * cfg.head_dim;
+    if (kf8()) {
+      g.kx = ctx_x(l) + p.x_off;
+      g.kx_hs = L.ctx_xtiles;
+    }
+  }
   char* mem_k(int l) const { return ws + L.off_mem + L.mem_layer_bytes * l; }
   char* mem_vt(int l) const { return mem_k(l) + L.mem_v_off; }
   float* pose_store() const { return reinterpret_cast<float*>(ws + L.off_pose); }
@@ -290,10 +305,7 @@ struct bkv_cache_s {
     g.n = p.tokens;
     g.dyn = p.dyn;
     if (p.dyn >= 0) {                 // slot known on device; K from the context buffer if rotated there
-      if (ctx_mode()) {
-        g.k = ctx_k(l) + (size_t)p.ctx_off * cfg.head_dim * L.esize;
-        g.k_hs = (long long)L.ctx_ld * cfg.head_dim;
-      }
+      if (ctx_mode()) ctx_seg_k(l, p, g);
       return g;
     }
     if (p.kind == bkv::SEG_REFERENCE) {
@@ -311,13 +323,12 @@ struct bkv_cache_s {
       g.k_hs = slot_k_hs();
       g.v_hs = slot_v_hs();
       g.v_ld = L.Tpad;
-      if (kf8()) {
+      if (slot8()) {
         g.kx = slot_kx(l, p.slot);
         g.kx_hs = slot_kx_hs();
       }
     } else {
-      g.k = ctx_k(l) + (size_t)p.ctx_off * cfg.head_dim * L.esize;
-      g.k_hs = (long long)L.ctx_ld * cfg.head_dim;
+      ctx_seg_k(l, p, g);
       if (p.kind == bkv::SEG_MEMORY) {
         g.v = mem_vt(l) + (size_t)p.id * L.tf_pad * L.esize;
         g.v_hs = (long long)L.mem_ld * cfg.head_dim;
@@ -387,6 +398,9 @@ bkv_status gather_context(bkv_cache h, int l, hipStream_t stream) {
   bkv::GatherArgs g{};
   g.dst = h->ctx_k(l);
   g.dst_hs = (long long)h->L.ctx_ld * h->cfg.head_dim;
+  g.kf8 = h->kf8() ? 1 : 0;
+  g.dx = h->kf8() ? h->ctx_x(l) : nullptr;
+  g.dx_hs = h->L.ctx_xtiles;
   g.H = h->cfg.heads;
   g.D = h->cfg.head_dim;
   g.rope = h->rope();
@@ -412,6 +426,7 @@ bkv_status gather_context(bkv_cache h, int l, hipStream_t stream) {
       gp.src_hs = h->slot_k_hs();
     }
     gp.dst_off = p.ctx_off;
+    gp.x_off = p.x_off;
     gp.n = p.tokens;
     gp.t_row0 = (int)p.t0;
     if (gp.n > g.max_n) g.max_n = gp.n;
@@ -653,12 +668,20 @@ bkv::AppendArgs append_args(bkv_cache h, int layer) {
   ap.vt = h->slot_vt(layer, cur.slot);
   ap.vt_hs = h->slot_v_hs();
   ap.vt_ld = h->L.Tpad;
-  if (h->kf8()) {
+  if (h->slot8()) {
     ap.k8 = h->slot_k(layer, cur.slot);
     ap.k8_hs = h->slot_k_hs();
     ap.kx = h->slot_kx(layer, cur.slot);
     ap.kx_hs = h->slot_kx_hs();
     ap.t_row0 = 0;
+  } else if (h->kf8()) {              // raw K to the slot, E4M3 K~ into the context buffer
+    ap.k_raw = h->slot_k(layer, cur.slot);
+    ap.k_raw_hs = h->slot_k_hs();
+    ap.k8 = h->ctx_k(layer) + (size_t)cur.ctx_off * D;
+    ap.k8_hs = (long long)h->L.ctx_ld * D;
+    ap.kx = h->ctx_x(layer) + cur.x_off;
+    ap.kx_hs = h->L.ctx_xtiles;
+    ap.t_row0 = (int)cur.t0;
   } else if (!h->ctx_mode()) {
     ap.k_rot = h->slot_k(layer, cur.slot);
     ap.k_rot_hs = h->slot_k_hs();

@@ -325,6 +325,8 @@ __global__ __launch_bounds__(256) void append_k8_kernel(AppendArgs a) {
     const bf16x8 kraw = *reinterpret_cast<const bf16x8*>(static_cast<const __bf16*>(a.k_in) + src);
     const uint4 vraw = *reinterpret_cast<const uint4*>(static_cast<const __bf16*>(a.v_in) + src);
     *reinterpret_cast<uint4*>(s_v + r * RS + ((c ^ ((r >> 3) & 7)) << 4)) = vraw;
+    if (a.k_raw)                         // raw K for a context rotated per block (and the conv)
+      *reinterpret_cast<bf16x8*>(static_cast<__bf16*>(a.k_raw) + head * a.k_raw_hs + (size_t)tok * D + c * VEC) = kraw;
 #pragma unroll
     for (int e = 0; e < VEC; ++e) kr[it][e] = (float)kraw[e];
     if (rope) {
@@ -532,6 +534,10 @@ void attn_bf16_kernel(AttnArgs a) {
         if (sg.k) {                      // K rotated into the context-K buffer
           kb = static_cast<const char*>(sg.k);
           khs = sg.k_hs;
+          if constexpr (KF8) {
+            s_xb[gg] = sg.kx;
+            s_xhs[gg] = sg.kx_hs;
+          }
         }
       } else {
         kb = static_cast<const char*>(sg.k);
@@ -1387,6 +1393,77 @@ __global__ __launch_bounds__(256) void gather_kernel(GatherArgs a) {
   }
 }
 
+// FP8 keys: the same gather into E4M3 rows.  One workgroup = one 64-row tile
+// of one head of one part: rotate in fp32, reduce the tile's largest |K~|,
+// store E4M3 with that tile's power-of-two scale and the exponent beside it
+// (the append_k8_kernel rule, tiles counted from the segment's first row).
+__global__ __launch_bounds__(256) void gather_k8_kernel(GatherArgs a) {
+  constexpr int D = 128, VEC = 8, CPR = D / VEC, IT = 64 * CPR / 256;
+  __shared__ float s_max[4];
+  const GatherPart p = a.part[blockIdx.z];
+  const int head = blockIdx.y;
+  const int tile0 = blockIdx.x * 64;
+  if (tile0 >= p.n) return;
+  const int ntok = min(64, p.n - tile0);
+  const int tid = threadIdx.x;
+  const bool rope = has_rope(a.rope);
+  const void* src = p.src;
+  long long src_hs = p.src_hs;
+  int t_row0 = p.t_row0;
+  if (p.dyn >= 0) {
+    src = a.slot_base + (long long)a.sel_slots[p.dyn] * a.slot_bytes;
+    src_hs = a.slot_k_hs;
+    const int id = a.sel_ids[p.dyn];
+    int rank = 0;
+    for (int j = 0; j < a.n_dyn; ++j) rank += a.sel_ids[j] < id;
+    t_row0 += rank * a.frames;
+  }
+  const __bf16* sbase = static_cast<const __bf16*>(src) + head * src_hs;
+  float kr[IT][VEC];
+  bf16x8 raw[IT];
+#pragma unroll
+  for (int it = 0; it < IT; ++it) {
+    const int task = tid + 256 * it, r = task / CPR, c = task % CPR;
+    if (r < ntok) raw[it] = *reinterpret_cast<const bf16x8*>(sbase + (size_t)(tile0 + r) * D + c * VEC);
+  }
+  float amax = 0.f;
+#pragma unroll
+  for (int it = 0; it < IT; ++it) {
+    const int task = tid + 256 * it, r = task / CPR, c = task % CPR;
+#pragma unroll
+    for (int e = 0; e < VEC; ++e) kr[it][e] = 0.f;
+    if (r >= ntok) continue;
+#pragma unroll
+    for (int e = 0; e < VEC; ++e) kr[it][e] = (float)raw[it][e];
+    if (rope) {
+      int f, y, x;
+      token_fyx(tile0 + r, a.rope.grid_h, a.rope.grid_w, f, y, x);
+#pragma unroll
+      for (int e = 0; e < VEC; e += 2) rope_pair_sel(kr[it][e], kr[it][e + 1], c * VEC + e, a.rope, t_row0 + f, y, x);
+    }
+#pragma unroll
+    for (int e = 0; e < VEC; ++e) amax = fmaxf(amax, fabsf(kr[it][e]));
+  }
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) amax = fmaxf(amax, __shfl_xor(amax, o));
+  if ((tid & 63) == 0) s_max[tid >> 6] = amax;
+  __syncthreads();
+  amax = fmaxf(fmaxf(s_max[0], s_max[1]), fmaxf(s_max[2], s_max[3]));
+  const int ex = e4m3_exponent(amax);
+  const float inv = __builtin_amdgcn_ldexpf(1.f, -ex);
+  char* dbase = static_cast<char*>(a.dst) + head * a.dst_hs + (size_t)(p.dst_off + tile0) * D;
+#pragma unroll
+  for (int it = 0; it < IT; ++it) {
+    const int task = tid + 256 * it, r = task / CPR, c = task % CPR;
+    if (r >= ntok) continue;
+    uint2 w;
+    w.x = (unsigned)e4m3_pack4(kr[it][0] * inv, kr[it][1] * inv, kr[it][2] * inv, kr[it][3] * inv);
+    w.y = (unsigned)e4m3_pack4(kr[it][4] * inv, kr[it][5] * inv, kr[it][6] * inv, kr[it][7] * inv);
+    *reinterpret_cast<uint2*>(dbase + (size_t)r * D + c * VEC) = w;
+  }
+  if (tid == 0) a.dx[head * a.dx_hs + p.x_off + blockIdx.x] = ex;
+}
+
 // ------------------------------------------------------------------ ConvKV conv
 // blockIdx.z = memory frame j, blockIdx.y = 0 (K rows) / 1 (V^T rows).
 // mem[j][h][s][c] = sum_i w[h][c][i] * frame[j*kernel + i][h][s][c], fp32 sums.
@@ -1681,8 +1758,9 @@ __global__ void export_kernel(ExportArgs a) {
   static_cast<T*>(a.v_out)[gid] = *v;
   if constexpr (std::is_same<T, __bf16>::value) {
     if (a.kf8) {   // E4M3 byte times 2^(tile exponent): exact in bf16
-      const int* xb = a.seg.dyn >= 0 ? reinterpret_cast<const int*>(kb + a.slot_kx_off) : a.seg.kx;
-      const long long xhs = a.seg.dyn >= 0 ? a.slot_kx_hs : a.seg.kx_hs;
+      const bool in_slot = a.seg.dyn >= 0 && !a.seg.k;
+      const int* xb = in_slot ? reinterpret_cast<const int*>(kb + a.slot_kx_off) : a.seg.kx;
+      const long long xhs = in_slot ? a.slot_kx_hs : a.seg.kx_hs;
       const int byte = reinterpret_cast<const unsigned char*>(kb)[h * khs + (size_t)tok * a.D + d];
       const float kv = __builtin_amdgcn_ldexpf(__builtin_amdgcn_cvt_f32_fp8(byte, 0), xb[h * xhs + tok / 64]);
       static_cast<T*>(a.k_out)[gid] = (T)kv;
@@ -1766,7 +1844,10 @@ hipError_t launch_attention(const AttnArgs& a, bool bf16, hipStream_t s) {
 hipError_t launch_gather(const GatherArgs& a, bool bf16, hipStream_t s) {
   if (a.nparts == 0) return hipSuccess;
   dim3 grid((a.max_n + 63) / 64, a.H, a.nparts);
-  if (bf16) {
+  if (a.kf8) {
+    if (!bf16 || a.D != 128 || !a.dx) return hipErrorInvalidValue;
+    gather_k8_kernel<<<grid, 256, 0, s>>>(a);
+  } else if (bf16) {
     if (a.D != 128) return hipErrorInvalidValue;
     gather_kernel<__bf16, 128><<<grid, 256, 0, s>>>(a);
   } else if (a.D == 64) {

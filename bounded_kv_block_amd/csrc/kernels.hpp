@@ -121,6 +121,7 @@ struct GatherPart {
   int dst_off, n, t_row0;              // dst row offset, tokens, t-table row of frame 0
   int dyn;                             // >= 0: retrieved block of rank dyn; t_row0 is then the
                                        // run's first row, plus frames x (its rank by stream id)
+  int x_off;                           // FP8 keys: the segment's first tile exponent
 };
 struct GatherArgs {
   void* dst; long long dst_hs;
@@ -130,6 +131,8 @@ struct GatherArgs {
   const int* sel_slots;
   const char* slot_base; long long slot_bytes, slot_k_hs;
   int n_dyn, frames;
+  int kf8;                             // 1: dst holds E4M3 rows, tile exponents at dx
+  int* dx; long long dx_hs;            //   exponents [H][dx_hs]
   GatherPart part[kMaxSeg];
 };
 

@@ -46,6 +46,7 @@ struct SegPlan {
   int slot;         // slot id, -1 for memory, dynamic and reference segments
   int dyn;          // dynamic: rank index into the device selection, else -1
   int ctx_off;      // ConvKV, relative PR-Sink: row offset in the context-K buffer, else 0
+  int x_off;        // the same, FP8 keys: first 64-token tile exponent of the segment
 };
 
 struct ConvTap { int slot; int frame; };   // one source frame of the conv memory
@@ -97,6 +98,12 @@ class Schedule {
     return s_.ref_frames + (s_.statics + s_.k + s_.window + 1) * s_.frames;
   }
   bool ctx_mode() const { return s_.convkv || s_.relative; }
+  // 64-token tiles of the largest context-K buffer (FP8 keys: one exponent each per head)
+  int ctx_xtiles() const {
+    const int tb = (T_ + 63) / 64;
+    if (s_.convkv) return s_.memory_frames * ((s_.tokens_per_frame + 63) / 64) + (s_.window + 1) * tb;
+    return (s_.statics + s_.k + s_.window + 1) * tb;
+  }
 
   void reset() {
     next_ = 0;
@@ -241,24 +248,28 @@ class Schedule {
     if (!s_.convkv && s_.relative) {
       if (s_.ref_frames > 0) segs_.push_back({SEG_REFERENCE, -1, ref_tokens(), 0, -1, -1, 0});
       int64_t t = s_.ref_frames;
-      int off = 0;
+      int off = 0, xo = 0;
+      const int tb = (T_ + 63) / 64;
       for (auto& st : static_) {
-        segs_.push_back({SEG_STATIC, st.first, T_, t, st.second, -1, off});
+        segs_.push_back({SEG_STATIC, st.first, T_, t, st.second, -1, off, xo});
         t += F;
         off += T_;
+        xo += tb;
       }
       const int nd = n_dynamic();
       for (int j = 0; j < nd; ++j) {
-        segs_.push_back({SEG_DYNAMIC, -1, T_, t, -1, j, off});
+        segs_.push_back({SEG_DYNAMIC, -1, T_, t, -1, j, off, xo});
         off += T_;
+        xo += tb;
       }
       t += (int64_t)nd * F;
       for (auto& w : window_) {
-        segs_.push_back({SEG_WINDOW, w.first, T_, t, w.second, -1, off});
+        segs_.push_back({SEG_WINDOW, w.first, T_, t, w.second, -1, off, xo});
         t += F;
         off += T_;
+        xo += tb;
       }
-      segs_.push_back({SEG_CURRENT, m, T_, t, cur_slot_, -1, off});
+      segs_.push_back({SEG_CURRENT, m, T_, t, cur_slot_, -1, off, xo});
     } else if (!s_.convkv) {
       if (s_.ref_frames > 0) segs_.push_back({SEG_REFERENCE, -1, ref_tokens(), 0, -1, -1, 0});
       for (auto& st : static_) segs_.push_back({SEG_STATIC, st.first, T_, block_t0(st.first), st.second, -1, 0});
@@ -268,18 +279,21 @@ class Schedule {
     } else {
       const int n_mem = memory_count();
       const int Tf = s_.tokens_per_frame;
-      int off = 0;
+      const int tf = (Tf + 63) / 64, tb = (T_ + 63) / 64;
+      int off = 0, xo = 0;
       for (int j = 0; j < n_mem; ++j) {
-        segs_.push_back({SEG_MEMORY, j, Tf, j, -1, -1, off});
+        segs_.push_back({SEG_MEMORY, j, Tf, j, -1, -1, off, xo});
         off += Tf;
+        xo += tf;
       }
       int64_t t = n_mem;
       for (auto& w : window_) {
-        segs_.push_back({SEG_WINDOW, w.first, T_, t, w.second, -1, off});
+        segs_.push_back({SEG_WINDOW, w.first, T_, t, w.second, -1, off, xo});
         off += T_;
+        xo += tb;
         t += F;
       }
-      segs_.push_back({SEG_CURRENT, m, T_, t, cur_slot_, -1, off});
+      segs_.push_back({SEG_CURRENT, m, T_, t, cur_slot_, -1, off, xo});
     }
   }
 

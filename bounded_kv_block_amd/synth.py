@@ -63,6 +63,9 @@ WORKLOADS = {
     # 1024-token memory frame; 200 blocks.
     "convkv_512": dict(_BASE, mode="convkv", static=0, dynamic_k=0, bank=0, pose_dim=0,
                        blocks=200, seed=5, pose_kind="none"),
+    # the same with the FP8 key cache (the rotated context quantised as it is gathered)
+    "convkv_512_fp8k": dict(_BASE, mode="convkv", dtype="bf16_fp8k", static=0, dynamic_k=0, bank=0, pose_dim=0,
+                            blocks=200, seed=5, pose_kind="none"),
     # the same with only the memory's positions restarted (window and current absolute)
     "convkv_512_abs": dict(_BASE, mode="convkv", static=0, dynamic_k=0, bank=0, pose_dim=0,
                            blocks=200, seed=5, pose_kind="none", positions="absolute"),

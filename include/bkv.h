@@ -63,17 +63,22 @@ typedef enum {
 } bkv_status;
 
 typedef enum { BKV_PR_SINK = 0, BKV_CONVKV = 1 } bkv_mode;
-/* BKV_BF16_FP8K: bf16 Q/K/V/out and V cache, with an FP8 key cache (PR-Sink
-   only, head_dim 128).  The SoulX-LiveAct page (sections 关键信息速览 and
-   上手实践) runs attention in FP8 without fixing a scheme; this library reads
-   it as: K after RoPE is stored as OCP E4M3 (bias 7, largest finite 448,
-   round to nearest even) with one power-of-two scale 2^e per (head, 64-token
-   tile of a block), e the smallest integer with max|K~| * 2^-e <= 448 (0 for
-   an all-zero tile), clamped to [-120, 120]; Q after RoPE, times
-   softmax_scale * log2(e), is quantised the same way with one scale per
-   (token, head); the logits Q K^T are formed from these E4M3 values (the
-   products are exact, accumulated in fp32); softmax and P V are as for
-   BKV_BF16.  Cache bytes per token and head: 128 (K) + 256 (V) + 4/64. */
+/* BKV_BF16_FP8K: bf16 Q/K/V/out and V cache, with an FP8 key cache (head_dim
+   128).  The SoulX-LiveAct page (sections 关键信息速览 and 上手实践) runs
+   attention in FP8 without fixing a scheme; this library reads it as: K
+   after RoPE is held as OCP E4M3 (bias 7, largest finite 448, round to
+   nearest even) with one power-of-two scale 2^e per (head, 64-token tile of
+   a context segment, counted from the segment's first token), e the
+   smallest integer with max|K~| * 2^-e <= 448 (0 for an all-zero tile),
+   clamped to [-120, 120]; Q after RoPE, times softmax_scale * log2(e), is
+   quantised the same way with one scale per (token, head); the logits Q K^T
+   are formed from these E4M3 values (the products are exact, accumulated in
+   fp32); softmax and P V are as for BKV_BF16.  PR-Sink with absolute
+   positions stores the E4M3 K in the slots (cache bytes per token and head:
+   128 (K) + 256 (V) + 4/64).  ConvKV and context-relative PR-Sink keep raw
+   bf16 K in the slots (the conv and the per-block rotation read it) and
+   quantise the rotated context, segment by segment (memory frames, blocks),
+   as they gather it.  Not with bkv_attend_qkv. */
 typedef enum { BKV_F32 = 0, BKV_BF16 = 1, BKV_BF16_FP8K = 2 } bkv_dtype;
 
 /* Temporal RoPE positions (bkv_config.rope_positions).
@@ -86,8 +91,8 @@ typedef enum { BKV_F32 = 0, BKV_BF16 = 1, BKV_BF16_FP8K = 2 } bkv_dtype;
      (static, retrieved, window, current) sit at consecutive frames in
      stream-id order after the reference frames, the gaps between them
      removed, and their K is re-rotated at those positions every block (the
-     ConvKV page's position reset applied to PR-Sink).  Not with
-     BKV_BF16_FP8K.  ConvKV: as BKV_POS_DEFAULT.
+     ConvKV page's position reset applied to PR-Sink).  ConvKV: as
+     BKV_POS_DEFAULT.
    BKV_POS_ABSOLUTE: PR-Sink: as BKV_POS_DEFAULT.  ConvKV: only the memory's
      positions restart (memory frame j at t = j); the window and current
      blocks keep their absolute frame indices b*frames_per_block + f (the

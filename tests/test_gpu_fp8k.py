@@ -176,3 +176,123 @@ def test_fp8k_split_launch_key_parts():
     run, _ = _stream(cfg, host_inputs=False, check={0, 4, 7}, heads=[0, 33, 39],
                      rows=np.r_[0:64, 900:964, 1736:1800])
     assert run.cache.stats()["split_attends"] == cfg["blocks"]
+
+
+# ---- FP8 keys in a context gathered per block (ConvKV, context-relative PR-Sink)
+def _check_stored_keys(run, kv, layer=0):
+    """Every segment's stored K (E4M3 x 2^e, exact in bf16) against the
+    oracle's quantisation of its rotated K, one E4M3 step apart at most and
+    only at rounding ties within the fp32-vs-fp64 rotation error (for memory
+    frames, whose raw K the caller passes bf16-rounded as stored, within a
+    bf16 step of the fp32-vs-fp64 conv sum: 2^-4 of an E4M3 step); V exact
+    up to bf16 storage of the conv memory."""
+    n_total = n_tie = 0
+    for i, (kind, _, kr, v) in enumerate(kv):
+        gk, gv = run.cache.export_segment(layer, i)
+        got = gk.float().cpu().numpy().astype(np.float64)
+        want = oracle.fp8.quantize_keys(kr)
+        T = kr.shape[0]
+        nt = (T + 63) // 64
+        pad = np.zeros((nt * 64,) + kr.shape[1:])
+        pad[:T] = kr
+        amax = np.abs(pad).reshape(nt, 64, *kr.shape[1:]).max(axis=(1, 3))
+        sc = np.repeat(np.ldexp(1.0, oracle.fp8.pow2_exponents(amax)), 64, axis=0)[:T][:, :, None]
+        y = kr / sc
+        q = _e4m3_quantum(y)
+        frac = np.abs(y) / q - np.floor(np.abs(y) / q)
+        near_tie = np.abs(frac - 0.5) < (2.0 ** -4 if kind == "memory" else 1e-4)
+        diff = got != want
+        assert np.all(near_tie[diff]), (i, kind, int(diff.sum()))
+        assert np.all(np.abs(got - want)[diff] <= (q * sc * (1 + 1e-12))[diff]), (i, kind)
+        n_total += diff.size
+        n_tie += int(diff.sum())
+        gv = gv.float().cpu().numpy().astype(np.float64)
+        if kind == "memory":
+            assert np.max(np.abs(gv - v)) <= 2.0 ** -7 * np.max(np.abs(v)) + 1e-6, (i, kind)
+        else:
+            assert np.array_equal(gv, v), (i, kind)
+    return n_total, n_tie
+
+
+def _bf16_memory_kv(cfg, ref, m, heads):
+    """The oracle's context K/V with the memory frames' raw K rounded to bf16
+    before rotation, as the library stores the conv memory (fp32 sums, bf16
+    store)."""
+    import torch
+    kv = ref.context_kv(m, 0, 0, heads)
+    mk, _ = ref.memory(m, 0, heads)
+    f, y, x = oracle.token_positions(1, cfg["grid_h"], cfg["grid_w"])
+    for j in range(len(ref.schedule(m)["memory"])):
+        kb = torch.from_numpy(mk[j]).to(torch.bfloat16).double().numpy()
+        kr = oracle.apply_rope(kb, np.full(f.size, float(j)), y, x, cfg["rope"], cfg.get("theta", 10000.0))
+        kv[j] = (kv[j][0], kv[j][1], kr, kv[j][3])
+    return kv
+
+
+def _convkv_stream(cfg, check=None, heads=None, rows=None, host_inputs=True, keys=False):
+    run = Run(cfg, host_inputs)
+    ref = oracle.ConvKVReference(cfg, run)
+    n_total = n_tie = 0
+    for m in range(cfg["blocks"]):
+        run.open(m)
+        assert run.cache.context() == ref.context(m), m
+        out = run.attend(m, 0, 0)
+        if check is None or m in check:
+            err = max_err(out, ref.attend(m, 0, 0, heads=heads, rows=rows), heads, rows)
+            print(f"block {m}: max|err| {err:.3e}", flush=True)
+            assert err <= TOL["bf16_fp8k"], (m, err)
+        if keys:
+            a, b = _check_stored_keys(run, _bf16_memory_kv(cfg, ref, m, list(range(cfg["heads"]))))
+            n_total += a
+            n_tie += b
+        run.cache.commit()
+        if not host_inputs:
+            run.drop(set(range(m - 8, m + 2)))
+    assert n_tie <= 1e-3 * max(n_total, 1)
+    return run
+
+
+def test_fp8k_convkv_small_ragged_with_keys():
+    """ConvKV with the FP8 key cache: 2 heads, 3 frames of 4x6 (a 24-token
+    memory frame and 72-token blocks: a partial tile in every segment), 12
+    blocks; every output, and every segment's stored E4M3 keys and V."""
+    cfg = synth.workload("convkv_512", dtype="bf16_fp8k", heads=2, grid_h=4, grid_w=6, blocks=12)
+    run = _convkv_stream(cfg, keys=True)
+    assert run.cache.stats()["memory_count"] == 1
+
+
+def test_fp8k_convkv_memory_only_reset_two_memory_frames():
+    """The memory-only position reset (window and current absolute) with two
+    memory frames of 6x10 tokens and FP8 keys, 16 blocks."""
+    cfg = synth.workload("convkv_512_abs", dtype="bf16_fp8k", heads=2, grid_h=6, grid_w=10, frames=2,
+                         memory_frames=2, blocks=16)
+    _convkv_stream(cfg, keys=True)
+
+
+def test_fp8k_relative_prsink_with_keys():
+    """Context-relative PR-Sink with FP8 keys and one reference frame: the
+    gather quantises the re-rotated context per segment, retrieved blocks
+    included; indices, positions, outputs and stored keys on 14 blocks."""
+    cfg = synth.workload("prsink_512_fp8k", heads=2, grid_h=6, grid_w=10, bank=4, blocks=14, pose_dim=16,
+                         keyframes=5, positions="relative", reference_frames=1)
+    run = Run(cfg)
+    ref = oracle.PRSinkReference(cfg, run)
+    for m in range(cfg["blocks"]):
+        run.open(m)
+        sel = ref.selection(m)
+        assert run.cache.selection() == sel, m
+        assert run.cache.context() == ref.context(m, sel), m
+        out = run.attend(m, 0, 0)
+        err = max_err(out, ref.attend(m, 0, 0, selection=sel))
+        assert err <= TOL["bf16_fp8k"], (m, err)
+        _check_stored_keys(run, ref.context_kv(m, 0, 0, [0, 1], sel))
+        run.cache.commit()
+
+
+def test_fp8k_convkv_512_full_shape_sampled():
+    """ConvKV 512x512 at full size with FP8 keys (13312 keys once warm, the
+    1024-token memory frame quantised in 16 tiles): outputs of 2 heads on
+    sampled rows of blocks 0, 4, 5 and 11."""
+    cfg = synth.workload("convkv_512", dtype="bf16_fp8k", blocks=12)
+    _convkv_stream(cfg, host_inputs=False, check={0, 4, 5, 11}, heads=[0, 21],
+                   rows=np.r_[0:64, 1500:1532, 3008:3072])

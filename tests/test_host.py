@@ -311,9 +311,10 @@ def test_workspace_size_and_validation():
 
 
 def test_fp8_key_cache_workspace_and_validation():
-    """FP8 key cache: a slot holds E4M3 K (1 byte per value), one int32
-    exponent per (head, 64-token tile) and the bf16 V^T; PR-Sink and
-    head_dim 128 only."""
+    """FP8 key cache: a PR-Sink slot holds E4M3 K (1 byte per value), one
+    int32 exponent per (head, 64-token tile) and the bf16 V^T; ConvKV keeps
+    bf16 slots and an E4M3 context buffer with one exponent per (head, tile
+    of a segment); head_dim 128 only."""
     from bounded_kv_block_amd import bkv, synth
     n16 = bkv.workspace_size(bkv.config_from_workload(synth.workload("prsink_512")))
     n8 = bkv.workspace_size(bkv.config_from_workload(synth.workload("prsink_512_fp8k")))
@@ -323,10 +324,17 @@ def test_fp8_key_cache_workspace_and_validation():
     slot16 = 2 * H * Tp * D * 2
     qs = H * Tp * D * 2                                 # bf16 q scratch (fused projection path only)
     assert n16 - n8 == 61 * (slot16 - slot8) + qs       # same 61 slots, tables and split slots
-    for b in (dict(head_dim=64), dict(mode="convkv", static=0, dynamic_k=0, bank=0, pose_dim=0)):
-        with pytest.raises(bkv.BkvError) as ei:
-            bkv.workspace_size(bkv.config_from_workload(synth.workload("prsink_512_fp8k", **b)))
-        assert ei.value.status == bkv.BKV_ERR_UNSUPPORTED, b
+    with pytest.raises(bkv.BkvError) as ei:
+        bkv.workspace_size(bkv.config_from_workload(synth.workload("prsink_512_fp8k", head_dim=64)))
+    assert ei.value.status == bkv.BKV_ERR_UNSUPPORTED
+    c16 = bkv.workspace_size(bkv.config_from_workload(synth.workload("convkv_512")))
+    c8 = bkv.workspace_size(bkv.config_from_workload(synth.workload("convkv_512", dtype="bf16_fp8k")))
+    al = lambda n: -(-n // 256) * 256
+    rows = 13312 + 64                                   # largest context + one key tile
+    xt = 1024 // 64 + 4 * (3072 // 64)                  # tiles: the memory frame, 3 windows + current
+    ctx16 = al(H * rows * D * 2)
+    ctx8 = al(al(H * rows * D) + 4 * H * xt)
+    assert c16 - c8 == (ctx16 - ctx8) + qs              # same bf16 slots and memory, no q scratch
     c = bkv.config_from_workload(synth.workload("prsink_512"))
     c.dtype = 3
     with pytest.raises(bkv.BkvError) as ei:
@@ -376,8 +384,9 @@ def test_reference_frames_workspace_and_validation():
 def test_relative_positions_workspace_and_validation():
     """Context-relative PR-Sink adds a context-K buffer of the largest context
     (less the reference) plus one key tile, per layer, and a temporal table
-    of its frames; not with the FP8 key cache.  ConvKV's memory-only reset
-    needs no extra bytes; an unknown positions value is rejected."""
+    of its frames (with the FP8 key cache: E4M3 rows and tile exponents, and
+    bf16 slots).  ConvKV's memory-only reset needs no extra bytes; an
+    unknown positions value is rejected."""
     from bounded_kv_block_amd import bkv, synth
     n0 = bkv.workspace_size(bkv.config_from_workload(synth.workload("prsink_512")))
     n1 = bkv.workspace_size(bkv.config_from_workload(synth.workload("prsink_512_rel")))
@@ -385,9 +394,9 @@ def test_relative_positions_workspace_and_validation():
     al = lambda n: -(-n // 256) * 256
     tt = al(8 * 21 * 23) - al(8 * 3 * 23)                # 21 t rows of 23 (cos, sin) pairs instead of 3
     assert n1 - n0 == ctx + tt
-    with pytest.raises(bkv.BkvError) as ei:
-        bkv.workspace_size(bkv.config_from_workload(synth.workload("prsink_512_fp8k", positions="relative")))
-    assert ei.value.status == bkv.BKV_ERR_UNSUPPORTED
+    r8 = bkv.workspace_size(bkv.config_from_workload(synth.workload("prsink_512_fp8k", positions="relative")))
+    ctx8 = al(al((21504 + 64) * 40 * 128) + 4 * 40 * 7 * 48)
+    assert n1 - r8 == (ctx - ctx8) + 3072 * 40 * 128 * 2   # bf16 slots in both; no q scratch with FP8
     assert (bkv.workspace_size(bkv.config_from_workload(synth.workload("convkv_512_abs")))
             == bkv.workspace_size(bkv.config_from_workload(synth.workload("convkv_512"))))
     c = bkv.config_from_workload(synth.workload("convkv_512"))
