@@ -37,7 +37,7 @@ def parse():
     ap.add_argument("--steps", type=int, default=40)
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--workload", default="prsink_512",
-                    choices=["prsink_512", "prsink_512_fp8k", "prsink_512_qkv", "prsink_512_ref", "prsink_512_rel", "prsink_512_posebank",
+                    choices=["prsink_512", "prsink_512_fp8k", "prsink_512_qkv", "prsink_512_ref", "prsink_512_rel", "prsink_512_posebank", "prsink_512_qkv_fp8k",
                              "prsink_720x416",
                              "prsink_long", "convkv_512", "convkv_512_abs", "convkv_512_fp8k", "tiny_fp32"])
     ap.add_argument("--pool", type=int, default=4, help="distinct resident input blocks cycled through")

@@ -207,7 +207,7 @@ Layout layout_of(const bkv_config* c, const bkv::Schedule& sch) {
   L.off_cnt = off;
   if (L.split) off = align_up(off + sizeof(int) * (bkv::kStreamWG + 1), 256);
   L.off_q = off;
-  if (c->dtype == BKV_BF16) off = align_up(off + (size_t)L.T * H * D * 2, 256);
+  if (c->dtype != BKV_F32) off = align_up(off + (size_t)L.T * H * D * 2, 256);
   L.total = off;
   return L;
 }
@@ -772,8 +772,8 @@ bkv_status bkv_attend_qkv(bkv_cache h, int32_t layer, const void* x, const void*
                           int32_t model_dim, void* out, hipStream_t stream) {
   bkv_status st = attend_checks(h, layer);
   if (st != BKV_OK) return st;
-  if (h->cfg.dtype != BKV_BF16)
-    return fail(BKV_ERR_UNSUPPORTED, "the fused QKV projection is implemented for the bf16 cache dtype");
+  if (h->cfg.dtype == BKV_F32)
+    return fail(BKV_ERR_UNSUPPORTED, "the fused QKV projection is implemented for the bf16 cache dtypes");
   if (!x || !w || !out) return fail(BKV_ERR_ARG, "null x, w or out");
   if (out == x || out == w || out == b) return fail(BKV_ERR_ARG, "out aliases an input");
   if (model_dim <= 0 || model_dim % 32 != 0) return fail(BKV_ERR_ARG, "model_dim must be a positive multiple of 32");

@@ -1671,6 +1671,75 @@ void qkv_gemm_kernel(QkvArgs a) {
   const AppendArgs& ap = a.ap;
   const bool rope = has_rope(ap.rope);
   const __bf16* bias = static_cast<const __bf16*>(a.b);
+  // FP8 key cache: a wave's 128 features x 64 tokens are one head's K over
+  // one 64-token tile of the block (both aligned), so the tile's scale is a
+  // reduction within the wave: rotate every K value in place, take the
+  // largest magnitude over the valid tokens, then store E4M3 and the tile
+  // exponent.
+  if (ap.k8) {
+    const int fw = f0 + 128 * wf, tw = t0 + 64 * wt;
+    if (fw < NF && fw / HD == 1 && tw < T) {
+      const int head = (fw - HD) / AD;
+      float amax = 0.f;
+#pragma unroll
+      for (int bn = 0; bn < 2; ++bn) {
+        const int t = tw + 32 * bn + col;
+        int fy = 0, yy = 0, xx = 0;
+        if (rope && t < T) token_fyx(t, ap.rope.grid_h, ap.rope.grid_w, fy, yy, xx);
+#pragma unroll
+        for (int bm = 0; bm < 4; ++bm)
+#pragma unroll
+          for (int g = 0; g < 4; ++g) {
+            const int d0 = 32 * bm + 8 * g + 4 * hh;
+            float v[4];
+#pragma unroll
+            for (int j = 0; j < 4; ++j) v[j] = acc[bm][bn][4 * g + j];
+            if (bias) {
+              const bf16x4 bb = *reinterpret_cast<const bf16x4*>(bias + fw + d0);
+#pragma unroll
+              for (int j = 0; j < 4; ++j) v[j] += (float)bb[j];
+            }
+#pragma unroll
+            for (int j = 0; j < 4; ++j) v[j] = (float)(__bf16)v[j];   // k in bf16, as for the bf16 cache
+            if (t < T && ap.k_raw) {
+              bf16x4 o;
+#pragma unroll
+              for (int j = 0; j < 4; ++j) o[j] = (__bf16)v[j];
+              *reinterpret_cast<bf16x4*>(static_cast<__bf16*>(ap.k_raw) + head * ap.k_raw_hs + (size_t)t * AD + d0) = o;
+            }
+            if (rope && t < T) {
+              rope_pair(v[0], v[1], d0, ap.rope, ap.t_row0 + fy, yy, xx);
+              rope_pair(v[2], v[3], d0 + 2, ap.rope, ap.t_row0 + fy, yy, xx);
+            }
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+              acc[bm][bn][4 * g + j] = v[j];
+              if (t < T) amax = fmaxf(amax, fabsf(v[j]));
+            }
+          }
+      }
+#pragma unroll
+      for (int o = 32; o > 0; o >>= 1) amax = fmaxf(amax, __shfl_xor(amax, o));
+      const int ex = e4m3_exponent(amax);
+      const float inv = __builtin_amdgcn_ldexpf(1.f, -ex);
+#pragma unroll
+      for (int bn = 0; bn < 2; ++bn) {
+        const int t = tw + 32 * bn + col;
+        if (t >= T) continue;
+#pragma unroll
+        for (int bm = 0; bm < 4; ++bm)
+#pragma unroll
+          for (int g = 0; g < 4; ++g) {
+            const int d0 = 32 * bm + 8 * g + 4 * hh;
+            const f32x16& c = acc[bm][bn];
+            *reinterpret_cast<int*>(static_cast<char*>(ap.k8) + head * ap.k8_hs + (size_t)t * AD + d0) =
+                e4m3_pack4(c[4 * g] * inv, c[4 * g + 1] * inv, c[4 * g + 2] * inv, c[4 * g + 3] * inv);
+          }
+      }
+      if (lane == 0) ap.kx[head * ap.kx_hs + tw / 64] = ex;
+      return;                              // this wave held K only
+    }
+  }
 #pragma unroll
   for (int bn = 0; bn < 2; ++bn) {
     const int t = t0 + 64 * wt + 32 * bn + col;
@@ -1699,11 +1768,15 @@ void qkv_gemm_kernel(QkvArgs a) {
           for (int j = 0; j < 4; ++j) o[j] = (__bf16)v[j];
           *reinterpret_cast<bf16x4*>(static_cast<__bf16*>(a.q) + ((size_t)t * H + head) * AD + d0) = o;
         } else if (which == 1) {
-          if (ap.k_raw) {
+          // k leaves the projection in bf16, as the unfused path receives it;
+          // the rotation then starts from that value
 #pragma unroll
-            for (int j = 0; j < 4; ++j) o[j] = (__bf16)v[j];
-            *reinterpret_cast<bf16x4*>(static_cast<__bf16*>(ap.k_raw) + head * ap.k_raw_hs + (size_t)t * AD + d0) = o;
+          for (int j = 0; j < 4; ++j) {
+            o[j] = (__bf16)v[j];
+            v[j] = (float)o[j];
           }
+          if (ap.k_raw)
+            *reinterpret_cast<bf16x4*>(static_cast<__bf16*>(ap.k_raw) + head * ap.k_raw_hs + (size_t)t * AD + d0) = o;
           if (rope) {
             rope_pair(v[0], v[1], d0, ap.rope, ap.t_row0 + fy, yy, xx);
             rope_pair(v[2], v[3], d0 + 2, ap.rope, ap.t_row0 + fy, yy, xx);
@@ -1807,7 +1880,7 @@ hipError_t launch_append(const AppendArgs& a, bool bf16, hipStream_t s) {
 }
 
 hipError_t launch_qkv(const QkvArgs& a, hipStream_t s) {
-  if (a.ap.D != AD || a.C <= 0 || a.C % GK != 0 || !a.ap.k_rot || !a.ap.vt || !a.q)
+  if (a.ap.D != AD || a.C <= 0 || a.C % GK != 0 || !(a.ap.k_rot || (a.ap.k8 && a.ap.kx)) || !a.ap.vt || !a.q)
     return hipErrorInvalidValue;
   const int nf = (3 * a.ap.H * AD + GF - 1) / GF, nt = (a.ap.T + GT - 1) / GT;
   qkv_gemm_kernel<<<nf * nt, 512, 0, s>>>(a);

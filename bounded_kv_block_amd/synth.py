@@ -53,6 +53,8 @@ WORKLOADS = {
     # the same driven from hidden states: q, k, v projected in the fused path
     # from x [3072, 5120] (40 heads x 128 = 5120, a 14B-class DiT's width)
     "prsink_512_qkv": dict(_BASE, qkv=True),
+    # the same with the FP8 key cache (K quantised in the projection's epilogue)
+    "prsink_512_qkv_fp8k": dict(_BASE, qkv=True, dtype="bf16_fp8k"),
     # 720x416-shaped bf16: 3 frames of 26x45 = 3510 queries, 40 layers x 3 steps,
     # commit after the third step, bank of 16.
     "prsink_720x416": dict(_BASE, grid_h=26, grid_w=45, layers=40, steps=3, bank=16, seed=3),

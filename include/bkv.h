@@ -78,7 +78,7 @@ typedef enum { BKV_PR_SINK = 0, BKV_CONVKV = 1 } bkv_mode;
    128 (K) + 256 (V) + 4/64).  ConvKV and context-relative PR-Sink keep raw
    bf16 K in the slots (the conv and the per-block rotation read it) and
    quantise the rotated context, segment by segment (memory frames, blocks),
-   as they gather it.  Not with bkv_attend_qkv. */
+   as they gather it. */
 typedef enum { BKV_F32 = 0, BKV_BF16 = 1, BKV_BF16_FP8K = 2 } bkv_dtype;
 
 /* Temporal RoPE positions (bkv_config.rope_positions).
@@ -252,7 +252,9 @@ bkv_status bkv_attend(bkv_cache h, int32_t layer, const void* q, const void* k, 
    `layer`, attention written to out [T][heads][head_dim] bf16.  q goes through a
    workspace scratch; k and v never leave the cache.  model_dim: a positive multiple
    of 32; x and w each below 2 GiB.
-   Errors: as bkv_attend; BKV_ERR_UNSUPPORTED unless the cache dtype is BKV_BF16. */
+   With BKV_BF16_FP8K the rotated k is quantised to E4M3 in the projection's
+   epilogue (one tile scale per head and 64 tokens, as the append does).
+   Errors: as bkv_attend; BKV_ERR_UNSUPPORTED for BKV_F32. */
 bkv_status bkv_attend_qkv(bkv_cache h, int32_t layer, const void* x, const void* w, const void* b,
                           int32_t model_dim, void* out, hipStream_t stream);
 

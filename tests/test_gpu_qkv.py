@@ -1,6 +1,7 @@
 """GPU parity of the fused QKV projection path (bkv_attend_qkv) against the
 CPU oracle: q, k, v are the oracle's fp64 projection x W^T + b of the same
-bf16 hidden states and weights, fed to the same stream references.  Outputs
+bf16 hidden states and weights, rounded to bf16 where the unfused path
+receives its bf16 inputs, fed to the same stream references.  Outputs
 within max-abs 2e-2; the stored K (rotated) and V within bf16 rounding of
 the oracle's."""
 import numpy as np
@@ -56,9 +57,11 @@ class QkvRun(Run):
             _, _, wsel, bsel = self._pw[layer]
             parts = oracle.qkv_projection(x, wsel, bsel, len(self.heads), D)
             full = []
-            for p in parts:
+            for i, p in enumerate(parts):
                 a = np.zeros((x.shape[0], H, D))
-                a[:, self.heads, :] = p
+                # q, k and v leave the projection in bf16, where the unfused
+                # path receives its bf16 inputs
+                a[:, self.heads, :] = self.torch.from_numpy(p).to(self.torch.bfloat16).double().numpy()
                 full.append(a)
             self._host[key] = tuple(full)
         return self._host[key]
@@ -98,9 +101,20 @@ def _stream(cfg, run, check=None, heads=None, rows=None, export=False):
                 gk, gv = run.cache.export_segment(0, i)
                 gk = gk.float().cpu().numpy()[:, run.heads]
                 gv = gv.float().cpu().numpy()[:, run.heads]
-                # bf16 rounding of fp32-accumulated values: half an ulp plus accumulation noise
-                assert np.all(np.abs(gk - kr) <= 2.0 ** -8 * np.abs(kr) + 1e-3), (m, i)
-                assert np.all(np.abs(gv - v) <= 2.0 ** -8 * np.abs(v) + 1e-3), (m, i)
+                # Half an ulp of the stored rotated value (2^-8 |K~|), plus the
+                # projection's own bf16 rounding: where the fp32 and fp64 sums
+                # straddle a rounding boundary, each input of a RoPE pair may
+                # differ by one ulp (up to 2^-7 of it), which the orthonormal
+                # rotation carries over as at most sqrt(2) 2^-7 of the pair's
+                # norm; such straddles are rare.
+                pn = np.sqrt(kr ** 2 + kr.reshape(*kr.shape[:-1], -1, 2)[..., ::-1].reshape(kr.shape) ** 2)
+                d = np.abs(gk - kr)
+                assert np.all(d <= 2.0 ** -8 * np.abs(kr) + np.sqrt(2.0) * 2.0 ** -7 * pn + 1e-3), (m, i)
+                assert np.mean(d > 2.0 ** -8 * np.abs(kr) + 1e-3) < 1e-2, (m, i)
+                # V: both sides round the projection to bf16; where the fp32
+                # and fp64 sums straddle a boundary they differ by one ulp
+                assert np.all(np.abs(gv - v) <= 2.0 ** -7 * np.abs(v) + 1e-3), (m, i)
+                assert np.mean(gv != v) < 1e-2, (m, i)
         run.cache.commit()
         if not run.host_inputs:
             run.drop(set(range(m - 70, m + 2)))
@@ -147,3 +161,48 @@ def test_qkv_prsink_512_full_shape_sampled():
     heads = [0, 39]
     run = QkvRun(cfg, host_inputs=False, heads=heads)
     _stream(cfg, run, check={0, 7}, heads=heads, rows=np.r_[0:64, 1500:1532, 3008:3072])
+
+
+# ---- the fused path with the FP8 key cache (K quantised in the epilogue)
+def test_qkv_fp8k_small_ragged():
+    """FP8 keys from the projection's epilogue: 3 heads, 180-token blocks (a
+    ragged last token tile, whose clamped rows must not enter the tile's
+    scale), model_dim 256, bias, 12 blocks: every output."""
+    cfg = synth.workload("prsink_512_qkv", dtype="bf16_fp8k", heads=3, grid_h=6, grid_w=10, bank=4, blocks=12,
+                         pose_dim=16, keyframes=5, model_dim=256)
+    _stream_fp8(cfg, QkvRun(cfg))
+
+
+def test_qkv_fp8k_convkv_small():
+    """ConvKV with FP8 keys through the fused path: raw K to the slot, E4M3
+    K~ into the context buffer; 8 blocks (memory from block 5)."""
+    cfg = synth.workload("convkv_512", dtype="bf16_fp8k", heads=2, grid_h=4, grid_w=6, blocks=8, model_dim=128)
+    _stream_fp8(cfg, QkvRun(cfg))
+
+
+def test_qkv_fp8k_prsink_512_full_shape_sampled():
+    cfg = synth.workload("prsink_512_qkv", dtype="bf16_fp8k", blocks=8)
+    heads = [0, 39]
+    _stream_fp8(cfg, QkvRun(cfg, host_inputs=False, heads=heads), check={0, 7}, heads=heads,
+                rows=np.r_[0:64, 1500:1532, 3008:3072])
+
+
+def _stream_fp8(cfg, run, check=None, heads=None, rows=None):
+    Ref = oracle.ConvKVReference if cfg["mode"] == "convkv" else oracle.PRSinkReference
+    ref = Ref(cfg, run)
+    for m in range(cfg["blocks"]):
+        run.open(m)
+        sel = None if cfg["mode"] == "convkv" else ref.selection(m)
+        if sel is not None:
+            assert run.cache.selection() == sel, m
+        out = run.attend(m, 0, 0)
+        if check is None or m in check:
+            want = (ref.attend(m, 0, 0, heads=heads, rows=rows) if sel is None
+                    else ref.attend(m, 0, 0, heads=heads, rows=rows, selection=sel))
+            err = max_err(out, want, heads, rows)
+            print(f"block {m}: max|err| {err:.3e}", flush=True)
+            assert err <= TOL["bf16_fp8k"], (m, err)
+        run.cache.commit()
+        if not run.host_inputs:
+            run.drop(set(range(m - 70, m + 2)))
+            run._host.clear()
