@@ -322,8 +322,7 @@ def test_fp8_key_cache_workspace_and_validation():
     kx = -(-(4 * H * Tp // 64) // 256) * 256          # exponents, 256-byte aligned
     slot8 = H * Tp * D + kx + H * Tp * D * 2
     slot16 = 2 * H * Tp * D * 2
-    qs = H * Tp * D * 2                                 # bf16 q scratch (fused projection path only)
-    assert n16 - n8 == 61 * (slot16 - slot8) + qs       # same 61 slots, tables and split slots
+    assert n16 - n8 == 61 * (slot16 - slot8)            # same 61 slots, tables, split slots, q scratch
     with pytest.raises(bkv.BkvError) as ei:
         bkv.workspace_size(bkv.config_from_workload(synth.workload("prsink_512_fp8k", head_dim=64)))
     assert ei.value.status == bkv.BKV_ERR_UNSUPPORTED
@@ -334,7 +333,7 @@ def test_fp8_key_cache_workspace_and_validation():
     xt = 1024 // 64 + 4 * (3072 // 64)                  # tiles: the memory frame, 3 windows + current
     ctx16 = al(H * rows * D * 2)
     ctx8 = al(al(H * rows * D) + 4 * H * xt)
-    assert c16 - c8 == (ctx16 - ctx8) + qs              # same bf16 slots and memory, no q scratch
+    assert c16 - c8 == ctx16 - ctx8                     # same bf16 slots, memory and q scratch
     c = bkv.config_from_workload(synth.workload("prsink_512"))
     c.dtype = 3
     with pytest.raises(bkv.BkvError) as ei:
@@ -396,7 +395,7 @@ def test_relative_positions_workspace_and_validation():
     assert n1 - n0 == ctx + tt
     r8 = bkv.workspace_size(bkv.config_from_workload(synth.workload("prsink_512_fp8k", positions="relative")))
     ctx8 = al(al((21504 + 64) * 40 * 128) + 4 * 40 * 7 * 48)
-    assert n1 - r8 == (ctx - ctx8) + 3072 * 40 * 128 * 2   # bf16 slots in both; no q scratch with FP8
+    assert n1 - r8 == ctx - ctx8                        # bf16 slots and a q scratch in both
     assert (bkv.workspace_size(bkv.config_from_workload(synth.workload("convkv_512_abs")))
             == bkv.workspace_size(bkv.config_from_workload(synth.workload("convkv_512"))))
     c = bkv.config_from_workload(synth.workload("convkv_512"))
