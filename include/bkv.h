@@ -128,10 +128,11 @@ typedef struct {
   int32_t head_dim;         /* 64 or 128 (bf16 and FP8-key paths: 128) */
   int32_t frames_per_block; /* latent frames per block, >= 1 */
   int32_t grid_h, grid_w;   /* latent grid; tokens per block T = frames*grid_h*grid_w */
-  int32_t window_blocks;    /* rolling window length, >= 1 (3 on the pages) */
+  int32_t window_blocks;    /* rolling window length, 1..8 (3 on the pages) */
   int32_t static_blocks;    /* PR-Sink: 0 or 1 (block 0 is the sink); ConvKV: 0 */
   int32_t dynamic_k;        /* PR-Sink: blocks retrieved per block, 0..8; ConvKV: 0 */
-  int32_t bank_blocks;      /* PR-Sink: FIFO bank of evicted blocks, 0..256; ConvKV: 0 */
+  int32_t bank_blocks;      /* PR-Sink: bank of evicted blocks, 0..256 (FIFO or pose-aware,
+                               bank_policy); ConvKV: 0 */
   int32_t pose_dim;         /* PR-Sink with dynamic_k > 0: 1..1024 fp32 values per pose */
   int32_t rope_t, rope_h, rope_w; /* RoPE channel split [t|h|w]; all 0 = none, else each
                                      even and summing to head_dim */
@@ -189,7 +190,7 @@ bkv_status bkv_create(const bkv_config* cfg, void* workspace, size_t bytes, hipS
 bkv_status bkv_destroy(bkv_cache h);
 
 /* Back to block 0, empty cache, error state cleared.  No (de)allocation; conv
-   weights already set are kept. */
+   weights and reference frames already set are kept. */
 bkv_status bkv_reset(bkv_cache h);
 
 /* ConvKV: set layer's depthwise conv weights from device buffers wk, wv, each
