@@ -75,10 +75,17 @@ def simulate_prsink_pose_bank(n_blocks: int, pose, window: int = 3, bank: int = 
     by pose similarity), so exact ties drop the lower stream id and a zero
     pose scores 0.  The entering block joins at the end (admission order).
     """
+    it = iter_prsink_pose_bank(pose, window, bank, static)
+    return [next(it) for _ in range(n_blocks)]
+
+
+def iter_prsink_pose_bank(pose, window: int = 3, bank: int = 8, static: int = 1):
+    """The records of :func:`simulate_prsink_pose_bank`, block by block, for
+    as long as asked: record m needs the poses of blocks < m only."""
     from .retrieval import retrieve
     statics, win, bnk = [], deque(), []
-    out = []
-    for m in range(n_blocks):
+    m = 0
+    while True:
         rec = {"static": list(statics), "bank": list(bnk), "window": list(win), "evicted": None}
         if len(statics) < static:
             statics.append(m)
@@ -92,8 +99,8 @@ def simulate_prsink_pose_bank(n_blocks: int, pose, window: int = 3, bank: int = 
                         victim = retrieve(pose(e), [(b, pose(b)) for b in bnk], 1)[0]
                         bnk.remove(victim)
                     bnk.append(e)
-        out.append(rec)
-    return out
+        yield rec
+        m += 1
 
 
 def convkv_schedule(m: int, frames: int, window: int = 3, kernel: int = 5,

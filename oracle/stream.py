@@ -36,7 +36,7 @@ Readings (beyond those stated in the modules used here):
     t = R + i * frames + f.  Keys are rotated per block at these positions,
     not once at append.
   * PR-Sink with bank_policy = "pose": the bank follows
-    ``simulate_prsink_pose_bank`` (pose-aware replacement) instead of FIFO.
+    ``iter_prsink_pose_bank`` (pose-aware replacement) instead of FIFO.
   * ConvKV with positions = "absolute" (the literal alternative of the same
     passage: only the memory's positions restart): memory frame j at t = j,
     window and current blocks at their absolute t = b * frames + f.
@@ -50,7 +50,7 @@ from .attention import attention
 from .convkv import conv_memory
 from .retrieval import retrieve
 from .rope import apply_rope
-from .schedule import convkv_schedule, prsink_schedule, simulate_prsink_pose_bank, token_positions
+from .schedule import convkv_schedule, iter_prsink_pose_bank, prsink_schedule, token_positions
 
 
 def _scale(cfg):
@@ -107,12 +107,12 @@ class PRSinkReference(_Base):
     def schedule(self, m: int) -> dict:
         c = self.cfg
         if c.get("bank_policy", "fifo") == "pose":
-            sim = getattr(self, "_pose_bank", [])
-            if m >= len(sim):
-                n = max(m + 1, 2 * len(sim), c["blocks"])
-                sim = simulate_prsink_pose_bank(n, self.p.pose, c["window"], c["bank"], c["static"])
-                self._pose_bank = sim
-            return sim[m]
+            if not hasattr(self, "_pose_bank"):
+                self._pose_bank = []
+                self._pose_iter = iter_prsink_pose_bank(self.p.pose, c["window"], c["bank"], c["static"])
+            while len(self._pose_bank) <= m:           # advances only as far as block m
+                self._pose_bank.append(next(self._pose_iter))
+            return self._pose_bank[m]
         return prsink_schedule(m, c["window"], c["bank"], c["static"])
 
     def selection(self, m: int) -> list:
