@@ -196,7 +196,8 @@ def main():
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
         print(f"bench.py runs on one GPU only (asked for --gpus {args.gpus}, WORLD_SIZE {world}): "
-              "the bounded-KV path shards by heads across GPUs, which this build does not run.",
+              "the bounded-KV path shards by heads across GPUs (one cache per GPU); this benchmark "
+              "measures the one-GPU share.",
               file=sys.stderr)
         sys.exit(2)
 

@@ -73,8 +73,7 @@ def lib() -> ctypes.CDLL:
     global _lib
     if _lib is None:
         if not os.path.exists(LIB_PATH):
-            raise RuntimeError(f"{LIB_PATH} is not built; run bounded_kv_block_amd/build.py "
-                               "(or __graft_entry__.build()) first")
+            raise RuntimeError(f"{LIB_PATH} is not built; run bounded_kv_block_amd/build.py first")
         L = ctypes.CDLL(LIB_PATH)
         vp, i32, sz = ctypes.c_void_p, ctypes.c_int32, ctypes.c_size_t
         sig = {

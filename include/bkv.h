@@ -59,7 +59,7 @@ typedef enum {
   BKV_ERR_STATE = 2,       /* call out of order (see each call), or handle in error state */
   BKV_ERR_WORKSPACE = 3,   /* workspace too small or misaligned (256-byte alignment needed) */
   BKV_ERR_DEVICE = 4,      /* HIP launch or runtime error */
-  BKV_ERR_UNSUPPORTED = 5  /* valid request this build does not implement */
+  BKV_ERR_UNSUPPORTED = 5  /* valid request the library does not implement */
 } bkv_status;
 
 typedef enum { BKV_PR_SINK = 0, BKV_CONVKV = 1 } bkv_mode;
