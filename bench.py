@@ -362,7 +362,11 @@ def main():
         "roofline": {"kernel": "attention", "bound": "mfma" if bf16 else "alu", "achieved": attn_tflops,
                      "peak": peak, "unit": "TFLOP/s", "frac": attn_tflops / peak, "traffic": measured_traffic(cfg["name"]),
                      "traffic_unit": "HBM bytes per launch", "algorithmic_bytes": attn_bytes,
-                     "flop_per_launch": flop_attend, "avg_launch_us": 1e3 * attn_avg_ms},
+                     "flop_per_launch": flop_attend, "avg_launch_us": 1e3 * attn_avg_ms,
+                     # an attention call whose last round of units is split runs
+                     # two launches (whole rounds, then the split remainder);
+                     # the times and flops above are per call, both launches
+                     "launches_per_call": 2 if cache.stats()["split_attends"] else 1},
         "workspace_bytes": int(cache.stats()["workspace_bytes"]),
     }
     # what the device sustains right after the timed region: the bf16 MFMA

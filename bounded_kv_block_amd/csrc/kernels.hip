@@ -659,10 +659,10 @@ void attn_bf16_kernel(AttnArgs a) {
   };
   int NT = 0;
   for (int g = 0; g < nseg; ++g) NT += (seg_n(g) + ABN - 1) / ABN;
-  // split launch: R full rounds, then Ur remainder units each cut into rP
-  // key-tile parts (part p = tiles [NT p / rP, NT (p+1) / rP))
-  const int rR = SPLIT ? a.H * nqt / kStreamWG : 0;
-  const int rU = SPLIT ? a.H * nqt - rR * kStreamWG : 0;
+  // split launch: the units from unit0 on (fewer than a round; the full
+  // rounds ran in a plain launch before it), each cut into rP key-tile parts
+  // (part p = tiles [NT p / rP, NT (p+1) / rP))
+  const int rU = SPLIT ? a.H * nqt - a.unit0 : 0;
   const int rP = SPLIT && rU > 0 ? min(NT, max(1, kStreamWG / max(rU, 1))) : 1;
 
   // ---- tile loads: chunk p = (4i + w)*64 + lane of a tile lands at LDS p*16
@@ -1201,18 +1201,16 @@ void attn_bf16_kernel(AttnArgs a) {
 
   if constexpr (!SPLIT) {
     // one unit per workgroup, XCD-contiguous (the query tiles of a head share an L2)
-    const int u = __builtin_amdgcn_readfirstlane(xcd_remap(blockIdx.x, gridDim.x));
+    const int u = __builtin_amdgcn_readfirstlane(a.unit0 + xcd_remap(blockIdx.x, gridDim.x));
     piece(u, 0, NT, -1, 0);
   } else {
-    // kStreamWG workgroups: rR full rounds of one unit each (XCD-contiguous,
-    // all workgroups of a round in step on the same key tiles), then part
-    // p of remainder unit v on workgroup p * rU + v: the query tiles of a head
-    // read the same key part at the same time.
+    // kStreamWG workgroups: part p of remainder unit v on workgroup
+    // p * rU + v, so the query tiles of a head read the same key part at the
+    // same time.
     const int jw = __builtin_amdgcn_readfirstlane(xcd_remap(blockIdx.x, kStreamWG));
-    for (int r = 0; r < rR; ++r) piece(r * kStreamWG + jw, 0, NT, -1, 0);
     if (jw < rU * rP) {
       const int v = jw % rU, p = jw / rU;
-      piece(rR * kStreamWG + v, NT * p / rP, NT * (p + 1) / rP, v, p);
+      piece(a.unit0 + v, NT * p / rP, NT * (p + 1) / rP, v, p);
     }
   }
 }
@@ -1893,14 +1891,22 @@ hipError_t launch_attention(const AttnArgs& a, bool bf16, hipStream_t s) {
     // One unit per workgroup unless whole-unit rounds would leave more than
     // 15% of kStreamWG workgroup slots idle; then the workgroups share the
     // key tiles (needs the split slots of the workspace).
+    // The split case runs its whole-unit rounds as a plain launch (the
+    // kernel without the split path holds fewer registers), then the
+    // remainder units, cut into key parts, as a second launch.
     const int units = ((a.T + ABM - 1) / ABM) * a.H;
     const bool split = attention_split(a.T, a.H, a.split != 0);
-    if (a.kf8) {
-      if (split) attn_bf16_kernel<true, true><<<kStreamWG, 64 * AWAVES, 0, s>>>(a);
-      else attn_bf16_kernel<false, true><<<units, 64 * AWAVES, 0, s>>>(a);
-    } else {
-      if (split) attn_bf16_kernel<true, false><<<kStreamWG, 64 * AWAVES, 0, s>>>(a);
-      else attn_bf16_kernel<false, false><<<units, 64 * AWAVES, 0, s>>>(a);
+    AttnArgs b = a;
+    b.unit0 = 0;
+    const int plain = split ? units / kStreamWG * kStreamWG : units;
+    if (plain > 0) {
+      if (a.kf8) attn_bf16_kernel<false, true><<<plain, 64 * AWAVES, 0, s>>>(b);
+      else attn_bf16_kernel<false, false><<<plain, 64 * AWAVES, 0, s>>>(b);
+    }
+    if (split) {
+      b.unit0 = plain;
+      if (a.kf8) attn_bf16_kernel<true, true><<<kStreamWG, 64 * AWAVES, 0, s>>>(b);
+      else attn_bf16_kernel<true, false><<<kStreamWG, 64 * AWAVES, 0, s>>>(b);
     }
   } else if (a.D == 64) {
     const int nwg = ((a.T + 127) / 128) * a.H;

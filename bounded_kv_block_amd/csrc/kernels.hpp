@@ -19,11 +19,12 @@ constexpr int kMaxK = 8;        // dynamic sinks per block
 constexpr int kMaxTaps = 32;    // ConvKV: conv_kernel * memory_frames source frames
 constexpr int kTokAlign = 64;   // token-stride alignment of every K / V^T buffer
 
-// bf16 attention work split.  A unit is (head, 256-query tile).  With more
-// units than kStreamWG, the kernel runs kStreamWG workgroups (8 XCDs x 32)
-// that each take an equal share of the (unit, 64-key tile) work of their
-// XCD; a unit cut by a share boundary is finished by two workgroups whose
-// fp32 partial results meet in a split slot (one per side of a boundary).
+// bf16 attention work split.  A unit is (head, 256-query tile).  When the
+// units leave the last round of kStreamWG workgroups (8 XCDs x 32) part
+// idle, the whole rounds run as a plain launch, one unit per workgroup, and
+// a second launch of kStreamWG workgroups cuts each remaining unit into up to
+// kStreamWG / remaining key-tile parts; the parts' fp32 partial results meet
+// in split slots, and the last part to arrive merges them.
 constexpr int kAttnBM = 256;
 constexpr int kStreamWG = 256;
 constexpr int kStreamPerXcd = kStreamWG / 8;
@@ -66,7 +67,8 @@ struct AttnArgs {
   long long slot_kx_off, slot_kx_hs;   // FP8 key cache: exponents inside a slot
   int slot_v_ld;
   int kf8;                  // 1: K is E4M3 with tile exponents (bf16 path only)
-  int split;                // 1: kStreamWG workgroups share the units' key tiles
+  int split;                // 1: split slots exist (remainder units may be cut into key parts)
+  int unit0;                // first (head, query tile) unit of this launch
   float* part;              // split slots: 2 per share boundary, kSplitSlotBytes each
   int* cnt;                 // arrival counter per share boundary (0 between launches)
   Seg seg[kMaxSeg];

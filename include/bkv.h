@@ -167,9 +167,9 @@ typedef struct {
   int32_t bank_count;      /* PR-Sink: blocks in the bank */
   int32_t memory_count;    /* ConvKV: memory frames present */
   size_t workspace_bytes;  /* bytes of workspace in use (constant for the handle's life) */
-  int64_t split_attends;   /* bf16 attention launches since create/reset that shared key tiles
-                              across workgroups (units, i.e. heads x 256-query tiles, that would
-                              leave > 15% of 256 workgroup slots idle) */
+  int64_t split_attends;   /* bf16 attends since create/reset whose attention cut its last,
+                              unfilled round of units (heads x 256-query tiles; > 15% of 256
+                              workgroup slots idle) into key parts: a second attention launch */
 } bkv_stats_t;
 
 /* Workspace bytes needed for cfg.  Pure host call.
