@@ -88,6 +88,15 @@ def measured_traffic(workload):
     return float(kv["traffic_bytes"])
 
 
+def attention_launches(T, H):
+    """Launches of one split attention call: whole rounds of 256 units, the
+    remainder units cut into 256 // remainder key parts, and the merge of the
+    parts when there is more than one."""
+    units = -(-T // 256) * H
+    rem = units % 256
+    return 2 + (1 if 256 // rem > 1 else 0)
+
+
 def steady_block(cfg):
     """First block whose context has its final size."""
     if cfg["mode"] == "convkv":
@@ -364,9 +373,10 @@ def main():
                      "traffic_unit": "HBM bytes per launch", "algorithmic_bytes": attn_bytes,
                      "flop_per_launch": flop_attend, "avg_launch_us": 1e3 * attn_avg_ms,
                      # an attention call whose last round of units is split runs
-                     # two launches (whole rounds, then the split remainder);
-                     # the times and flops above are per call, both launches
-                     "launches_per_call": 2 if cache.stats()["split_attends"] else 1},
+                     # the whole rounds, then the remainder units cut into key
+                     # parts, then (more than one part per unit) the merge of the
+                     # parts: the times and flops above are per call, all launches
+                     "launches_per_call": attention_launches(T, H) if cache.stats()["split_attends"] else 1},
         "workspace_bytes": int(cache.stats()["workspace_bytes"]),
     }
     # what the device sustains right after the timed region: the bf16 MFMA

@@ -43,7 +43,7 @@ struct Layout {
   size_t off_kv, off_ctx, ctx_layer_bytes, off_mem, mem_layer_bytes, mem_v_off;
   size_t off_pose, off_sel, off_victim, off_tt, off_th, off_tw, off_w, total;
   bool split;                        // bf16 attention shares key tiles across workgroups
-  size_t off_split, off_cnt;
+  size_t off_split;                  // split slots: kStreamWG fp32 part states
   bool kf8;                          // FP8 key cache: attention reads E4M3 K with tile exponents
   bool slot8;                        //   held in the slots (K rotated once, at append); else
                                      //   slots keep bf16 raw K and the context buffer is FP8
@@ -203,9 +203,7 @@ Layout layout_of(const bkv_config* c, const bkv::Schedule& sch) {
   const long long units = (long long)H * ((L.T + bkv::kAttnBM - 1) / bkv::kAttnBM);
   L.split = c->dtype != BKV_F32 && units > bkv::kStreamWG;
   L.off_split = off;
-  if (L.split) off = align_up(off + bkv::kSplitSlotBytes * 2 * (bkv::kStreamWG + 1), 256);
-  L.off_cnt = off;
-  if (L.split) off = align_up(off + sizeof(int) * (bkv::kStreamWG + 1), 256);
+  if (L.split) off = align_up(off + bkv::kSplitSlotBytes * bkv::kStreamWG, 256);
   L.off_q = off;
   if (c->dtype != BKV_F32) off = align_up(off + (size_t)L.T * H * D * 2, 256);
   L.total = off;
@@ -519,14 +517,6 @@ bkv_status bkv_reset(bkv_cache h) {
   h->error = false;
   h->ctx_ready.assign(h->cfg.layers, false);
   h->split_attends = 0;
-  if (h->L.split) {
-    // arrival counters return to 0 at the end of every launch; a launch cut
-    // short by a device error may leave them set
-    if (set_device(h) != BKV_OK) return fail(BKV_ERR_DEVICE, "reset: set device");
-    hipError_t e = hipMemset(h->ws + h->L.off_cnt, 0, sizeof(int) * (bkv::kStreamWG + 1));
-    if (e == hipSuccess) e = hipDeviceSynchronize();
-    if (e != hipSuccess) return fail(BKV_ERR_DEVICE, "reset: counter clear: %s", hipGetErrorString(e));
-  }
   return BKV_OK;
 }
 
@@ -730,7 +720,6 @@ bkv_status attend_context(bkv_cache h, int layer, const void* q, void* out, hipS
   a.slot_kx_hs = h->slot_kx_hs();
   a.split = h->L.split ? 1 : 0;
   a.part = reinterpret_cast<float*>(h->ws + h->L.off_split);
-  a.cnt = reinterpret_cast<int*>(h->ws + h->L.off_cnt);
   a.nseg = (int)segs.size();
   for (int i = 0; i < a.nseg; ++i) a.seg[i] = h->seg_arg(layer, segs[i]);
   hipError_t e = timed(h, K_ATTENTION, stream, [&] { return bkv::launch_attention(a, h->bf16(), stream); });

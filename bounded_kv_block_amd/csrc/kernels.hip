@@ -497,7 +497,6 @@ void attn_bf16_kernel(AttnArgs a) {
   __shared__ const int* s_x[kMaxSeg];       // FP8 K: tile exponents of the current head
   __shared__ const int* s_xb[kMaxSeg];
   __shared__ long long s_xhs[kMaxSeg];
-  __shared__ int s_arrived;
 
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);   // uniform by construction
@@ -662,8 +661,9 @@ void attn_bf16_kernel(AttnArgs a) {
   // split launch: the units from unit0 on (fewer than a round; the full
   // rounds ran in a plain launch before it), each cut into rP key-tile parts
   // (part p = tiles [NT p / rP, NT (p+1) / rP))
+  // (rP is set by the host, 1 <= rP <= NT, rP * rU <= kStreamWG)
   const int rU = SPLIT ? a.H * nqt - a.unit0 : 0;
-  const int rP = SPLIT && rU > 0 ? min(NT, max(1, kStreamWG / max(rU, 1))) : 1;
+  const int rP = SPLIT ? a.parts : 1;
 
   // ---- tile loads: chunk p = (4i + w)*64 + lane of a tile lands at LDS p*16
   // (w = wave within the loading group of four); the tile's first key enters
@@ -1166,36 +1166,14 @@ void attn_bf16_kernel(AttnArgs a) {
     (void)j;
     if constexpr (SPLIT) {
       // Part j of cut remainder unit v: its fp32 state (O, m, l in register
-      // order) goes to slot j * rU + v; the last of the unit's rP parts to
-      // arrive merges the others and writes the output.
+      // order) goes to slot j * rU + v; attn_merge_kernel, launched next on
+      // the same stream, combines a unit's parts and writes the output.
       constexpr int SLOT = (int)(kSplitSlotBytes / 4), ML = 8 * 64 * 64;
       float* mine = a.part + (size_t)(j * rU + v) * SLOT;
 #pragma unroll
       for (int r = 0; r < 64; ++r) mine[(wave * 64 + r) * 64 + lane] = o[r >> 4][r & 15];
       mine[ML + (wave * 2) * 64 + lane] = m_run;
       mine[ML + (wave * 2 + 1) * 64 + lane] = l_run;
-      __builtin_amdgcn_fence(__ATOMIC_RELEASE, "agent");
-      __syncthreads();
-      if (tid == 0) s_arrived = __hip_atomic_fetch_add(a.cnt + v, 1, __ATOMIC_ACQ_REL, __HIP_MEMORY_SCOPE_AGENT);
-      __syncthreads();
-      if (__builtin_amdgcn_readfirstlane(s_arrived) == rP - 1) {
-        __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
-        for (int q = 0; q < rP; ++q) {
-          if (q == j) continue;
-          const float* other = a.part + (size_t)(q * rU + v) * SLOT;
-          const float m2 = other[ML + (wave * 2) * 64 + lane];
-          const float l2 = other[ML + (wave * 2 + 1) * 64 + lane];
-          const float mm = fmaxf(m_run, m2);
-          const float al = __builtin_amdgcn_exp2f(m_run - mm), be = __builtin_amdgcn_exp2f(m2 - mm);
-#pragma unroll
-          for (int r = 0; r < 64; ++r)
-            o[r >> 4][r & 15] = al * o[r >> 4][r & 15] + be * other[(wave * 64 + r) * 64 + lane];
-          l_run = al * l_run + be * l2;
-          m_run = mm;
-        }
-        if (tid == 0) __hip_atomic_store(a.cnt + v, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-        write_out(head, qrow);
-      }
     }
   };
 
@@ -1213,6 +1191,56 @@ void attn_bf16_kernel(AttnArgs a) {
       piece(a.unit0 + v, NT * p / rP, NT * (p + 1) / rP, v, p);
     }
   }
+}
+
+// Split launch, second step: the rP part states of each cut remainder unit
+// (slot p * rU + v holds part p of unit unit0 + v, as the attention kernel's
+// lanes held it) are combined in part order, normalised and stored as bf16.
+// One wave per (unit, attention wave), i.e. per 32 query rows; the kernel
+// boundary after the split launch makes the slots visible.
+__global__ __launch_bounds__(64) void attn_merge_kernel(AttnArgs a) {
+  constexpr int SLOT = (int)(kSplitSlotBytes / 4), ML = 8 * 64 * 64;
+  const int nqt = (a.T + ABM - 1) / ABM;
+  const int rU = a.H * nqt - a.unit0, rP = a.parts;
+  const int v = blockIdx.x >> 3, wave = blockIdx.x & 7, lane = threadIdx.x;
+  const int u = a.unit0 + v;
+  const int head = u / nqt, qt = u - head * nqt;
+  const int qrow = qt * ABM + wave * 32 + (lane & 31), hh = lane >> 5;
+  const float* slot0 = a.part + (size_t)v * SLOT;
+  const size_t pstride = (size_t)rU * SLOT;
+  float mm = -INFINITY;
+  for (int p = 0; p < rP; ++p) mm = fmaxf(mm, slot0[p * pstride + ML + (wave * 2) * 64 + lane]);
+  float o[64];
+#pragma unroll
+  for (int r = 0; r < 64; ++r) o[r] = 0.f;
+  float l = 0.f;
+  for (int p = 0; p < rP; ++p) {
+    const float* sp = slot0 + p * pstride;
+    // all of the part's loads in flight before the first use
+    float t[64];
+#pragma unroll
+    for (int r = 0; r < 64; ++r) t[r] = sp[(wave * 64 + r) * 64 + lane];
+    const float mp = sp[ML + (wave * 2) * 64 + lane];
+    const float lp = sp[ML + (wave * 2 + 1) * 64 + lane];
+    const float be = mp > -INFINITY ? __builtin_amdgcn_exp2f(mp - mm) : 0.f;
+    l += be * lp;
+#pragma unroll
+    for (int r = 0; r < 64; ++r) o[r] += be * t[r];
+  }
+  // lanes l and l ^ 32 hold the two halves of a row's sum
+  const float lt = l + __shfl_xor(l, 32);
+  const float inv = lt > 0.f ? 1.f / lt : 0.f;
+  if (qrow >= a.T) return;
+  __bf16* op = static_cast<__bf16*>(a.out) + ((size_t)qrow * a.H + head) * AD;
+#pragma unroll
+  for (int db = 0; db < 4; ++db)
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      bf16x4 w;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) w[e] = (__bf16)(o[16 * db + 4 * j + e] * inv);
+      *reinterpret_cast<bf16x4*>(op + 32 * db + 8 * j + 4 * hh) = w;
+    }
 }
 
 // ------------------------------------------------------------------ attention, fp32
@@ -1889,11 +1917,10 @@ hipError_t launch_attention(const AttnArgs& a, bool bf16, hipStream_t s) {
   if (bf16) {
     if (a.D != AD) return hipErrorInvalidValue;
     // One unit per workgroup unless whole-unit rounds would leave more than
-    // 15% of kStreamWG workgroup slots idle; then the workgroups share the
-    // key tiles (needs the split slots of the workspace).
-    // The split case runs its whole-unit rounds as a plain launch (the
-    // kernel without the split path holds fewer registers), then the
-    // remainder units, cut into key parts, as a second launch.
+    // 15% of kStreamWG workgroup slots idle (and the workspace has split
+    // slots).  Then the whole rounds run as a plain launch, the remainder
+    // units, cut into key parts, as a second launch, and a third merges the
+    // parts.
     const int units = ((a.T + ABM - 1) / ABM) * a.H;
     const bool split = attention_split(a.T, a.H, a.split != 0);
     AttnArgs b = a;
@@ -1904,9 +1931,16 @@ hipError_t launch_attention(const AttnArgs& a, bool bf16, hipStream_t s) {
       else attn_bf16_kernel<false, false><<<plain, 64 * AWAVES, 0, s>>>(b);
     }
     if (split) {
+      // remainder units rU, each cut into rP key parts of at least one tile
+      int NT = 0;
+      for (int g = 0; g < a.nseg; ++g) NT += (a.seg[g].n + 63) / 64;
+      const int rU = units - plain;
+      if (NT < 1 || rU < 1 || rU >= kStreamWG) return hipErrorInvalidValue;
       b.unit0 = plain;
+      b.parts = NT < kStreamWG / rU ? NT : kStreamWG / rU;
       if (a.kf8) attn_bf16_kernel<true, true><<<kStreamWG, 64 * AWAVES, 0, s>>>(b);
       else attn_bf16_kernel<true, false><<<kStreamWG, 64 * AWAVES, 0, s>>>(b);
+      if (b.parts > 1) attn_merge_kernel<<<rU * AWAVES, 64, 0, s>>>(b);
     }
   } else if (a.D == 64) {
     const int nwg = ((a.T + 127) / 128) * a.H;

@@ -23,8 +23,8 @@ constexpr int kTokAlign = 64;   // token-stride alignment of every K / V^T buffe
 // units leave the last round of kStreamWG workgroups (8 XCDs x 32) part
 // idle, the whole rounds run as a plain launch, one unit per workgroup, and
 // a second launch of kStreamWG workgroups cuts each remaining unit into up to
-// kStreamWG / remaining key-tile parts; the parts' fp32 partial results meet
-// in split slots, and the last part to arrive merges them.
+// kStreamWG / remaining key-tile parts; the parts' fp32 partial results go
+// to split slots (at most kStreamWG), which a third launch merges.
 constexpr int kAttnBM = 256;
 constexpr int kStreamWG = 256;
 constexpr int kStreamPerXcd = kStreamWG / 8;
@@ -69,8 +69,8 @@ struct AttnArgs {
   int kf8;                  // 1: K is E4M3 with tile exponents (bf16 path only)
   int split;                // 1: split slots exist (remainder units may be cut into key parts)
   int unit0;                // first (head, query tile) unit of this launch
-  float* part;              // split slots: 2 per share boundary, kSplitSlotBytes each
-  int* cnt;                 // arrival counter per share boundary (0 between launches)
+  int parts;                // split launch: key parts per remainder unit
+  float* part;              // split slots, kSplitSlotBytes each: part p of remainder unit v at p * rU + v
   Seg seg[kMaxSeg];
 };
 

@@ -118,6 +118,24 @@ def test_split_launch_whole_remainder_units():
     assert run.cache.stats()["split_attends"] == cfg["blocks"]
 
 
+@pytest.mark.parametrize("name", ["prsink_512", "prsink_512_fp8k"])
+def test_split_launch_deterministic(name):
+    """The key parts of a cut remainder unit are merged in part order by a
+    launch of their own, so attending the same inputs twice in a block gives
+    bit-identical outputs (1800-query blocks: 64 remainder units in 4 parts)."""
+    import torch
+    cfg = synth.workload(name, frames=2, grid_h=30, grid_w=30, blocks=6, steps=2)
+    run = Run(cfg, host_inputs=False)
+    for m in range(cfg["blocks"]):
+        run.open(m)
+        q, k, v = run.qkv_dev(0, m, 0)
+        first = run.cache.attend(0, q, k, v).clone()
+        second = run.cache.attend(0, q, k, v)
+        assert torch.equal(first, second), m
+        run.cache.commit()
+    assert run.cache.stats()["split_attends"] == 2 * cfg["blocks"]
+
+
 def test_multistep_multilayer_commit_after_last_step():
     """3 layers x 3 steps per block; the cache keeps each layer's last-step K/V."""
     cfg = synth.workload("prsink_512", heads=2, grid_h=4, grid_w=10, bank=3, blocks=9, pose_dim=16,

@@ -278,9 +278,9 @@ def test_workspace_size_and_validation():
     c2 = bkv.config_from_workload(synth.workload("prsink_512"))
     n = bkv.workspace_size(c2)
     slot = 2 * 40 * 3072 * 128 * 2
-    # 480 (head, 256-query) units > 256 workgroups: the attention shares key
-    # tiles, with two fp32 split slots (O, m, l of 256 rows) per share boundary
-    split = 2 * 257 * (8 * 64 * 64 * 4 + 8 * 2 * 64 * 4)
+    # 480 (head, 256-query) units > 256 workgroups: the workspace holds 256
+    # fp32 split slots (O, m, l of 256 rows), one per key part of a cut unit
+    split = 256 * (8 * 64 * 64 * 4 + 8 * 2 * 64 * 4)
     qs = 3072 * 40 * 128 * 2                 # bf16 q scratch of the fused projection path
     assert 61 * slot + split + qs <= n < 61 * slot + split + qs + (1 << 20)   # 61 slots of 62.9 MB
     n8 = bkv.workspace_size(bkv.config_from_workload(synth.workload("prsink_512", heads=8)))
