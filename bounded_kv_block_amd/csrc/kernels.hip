@@ -1492,8 +1492,10 @@ __global__ __launch_bounds__(256) void gather_k8_kernel(GatherArgs a) {
 
 // ------------------------------------------------------------------ ConvKV conv
 // blockIdx.z = memory frame j, blockIdx.y = 0 (K rows) / 1 (V^T rows).
-// mem[j][h][s][c] = sum_i w[h][c][i] * frame[j*kernel + i][h][s][c], fp32 sums.
-template <typename T, bool VEC_V>
+// mem[j][h][s][c] = sum_i w[h][c][i] * frame[j*kernel + i][h][s][c], fp32 sums
+// in tap order.  KS = kernel (taps per memory frame): a thread issues the
+// loads of all its taps before the first multiply.
+template <typename T, bool VEC_V, int KS>
 __global__ __launch_bounds__(256) void conv_kernel(ConvArgs a) {
   constexpr int VEC = 16 / sizeof(T);
   const int j = blockIdx.z;
@@ -1507,16 +1509,27 @@ __global__ __launch_bounds__(256) void conv_kernel(ConvArgs a) {
     const int c = (int)(gid % cpr);
     const long long hs = gid / cpr;
     const int s = (int)(hs % Tf), h = (int)(hs / Tf);
+    uint4 raw[KS];
+#pragma unroll
+    for (int i = 0; i < KS; ++i)
+      raw[i] = *reinterpret_cast<const uint4*>(static_cast<const T*>(a.k_src[j * KS + i]) + h * a.k_hs +
+                                               (size_t)s * D + c * VEC);
+    // the thread's weights w[h][c*VEC + e][i] are VEC * KS consecutive floats
+    // (16-byte aligned: VEC * KS * 4 is a multiple of 16)
+    constexpr int NW = VEC * KS / 4;
+    float4 wq[NW];
+    const float4* wsrc = reinterpret_cast<const float4*>(a.wk + ((size_t)h * D + c * VEC) * KS);
+#pragma unroll
+    for (int q = 0; q < NW; ++q) wq[q] = wsrc[q];
+    const float* w = reinterpret_cast<const float*>(wq);
     float acc[VEC];
 #pragma unroll
     for (int e = 0; e < VEC; ++e) acc[e] = 0.f;
-    for (int i = 0; i < a.kernel; ++i) {
-      const T* src = static_cast<const T*>(a.k_src[j * a.kernel + i]) + h * a.k_hs + (size_t)s * D + c * VEC;
-      const uint4 raw = *reinterpret_cast<const uint4*>(src);
-      const T* v = reinterpret_cast<const T*>(&raw);
-      const float* w = a.wk + ((size_t)h * D + c * VEC) * a.kernel + i;
 #pragma unroll
-      for (int e = 0; e < VEC; ++e) acc[e] = fmaf(w[e * a.kernel], to_f(v[e]), acc[e]);
+    for (int i = 0; i < KS; ++i) {
+      const T* v = reinterpret_cast<const T*>(&raw[i]);
+#pragma unroll
+      for (int e = 0; e < VEC; ++e) acc[e] = fmaf(w[e * KS + i], to_f(v[e]), acc[e]);
     }
     uint4 out;
     T* ov = reinterpret_cast<T*>(&out);
@@ -1534,19 +1547,28 @@ __global__ __launch_bounds__(256) void conv_kernel(ConvArgs a) {
     const int d = (int)(hd % D), h = (int)(hd / D);
     const int s0 = g * VEC;
     const int nv = min(VEC, Tf - s0);
+    float w[KS];
+#pragma unroll
+    for (int i = 0; i < KS; ++i) w[i] = a.wv[((size_t)h * D + d) * KS + i];
     float acc[VEC];
 #pragma unroll
     for (int e = 0; e < VEC; ++e) acc[e] = 0.f;
-    for (int i = 0; i < a.kernel; ++i) {
-      const T* src = static_cast<const T*>(a.vt_src[j * a.kernel + i]) + h * a.vt_hs + (size_t)d * a.vt_ld + s0;
-      const float w = a.wv[((size_t)h * D + d) * a.kernel + i];
-      if (VEC_V && nv == VEC) {
-        const uint4 raw = *reinterpret_cast<const uint4*>(src);
-        const T* v = reinterpret_cast<const T*>(&raw);
+    if (VEC_V && nv == VEC) {
+      uint4 raw[KS];
 #pragma unroll
-        for (int e = 0; e < VEC; ++e) acc[e] = fmaf(w, to_f(v[e]), acc[e]);
-      } else {
-        for (int e = 0; e < nv; ++e) acc[e] = fmaf(w, to_f(src[e]), acc[e]);
+      for (int i = 0; i < KS; ++i)
+        raw[i] = *reinterpret_cast<const uint4*>(static_cast<const T*>(a.vt_src[j * KS + i]) + h * a.vt_hs +
+                                                 (size_t)d * a.vt_ld + s0);
+#pragma unroll
+      for (int i = 0; i < KS; ++i) {
+        const T* v = reinterpret_cast<const T*>(&raw[i]);
+#pragma unroll
+        for (int e = 0; e < VEC; ++e) acc[e] = fmaf(w[i], to_f(v[e]), acc[e]);
+      }
+    } else {
+      for (int i = 0; i < KS; ++i) {
+        const T* src = static_cast<const T*>(a.vt_src[j * KS + i]) + h * a.vt_hs + (size_t)d * a.vt_ld + s0;
+        for (int e = 0; e < nv; ++e) acc[e] = fmaf(w[i], to_f(src[e]), acc[e]);
       }
     }
     T* dst = static_cast<T*>(a.vt_mem) + h * a.vt_mem_hs + (size_t)d * a.vt_mem_ld + j * a.tf_pad + s0;
@@ -1973,6 +1995,17 @@ hipError_t launch_gather(const GatherArgs& a, bool bf16, hipStream_t s) {
   return hipGetLastError();
 }
 
+template <int KS>
+static void conv_launch(const ConvArgs& a, bool bf16, bool vec_v, dim3 grid, hipStream_t s) {
+  if (bf16) {
+    if (vec_v) conv_kernel<__bf16, true, KS><<<grid, 256, 0, s>>>(a);
+    else conv_kernel<__bf16, false, KS><<<grid, 256, 0, s>>>(a);
+  } else {
+    if (vec_v) conv_kernel<float, true, KS><<<grid, 256, 0, s>>>(a);
+    else conv_kernel<float, false, KS><<<grid, 256, 0, s>>>(a);
+  }
+}
+
 hipError_t launch_conv(const ConvArgs& a, bool bf16, hipStream_t s) {
   const int vec = bf16 ? 8 : 4;
   const long long nk = (long long)a.H * a.Tf * (a.D / vec);
@@ -1981,12 +2014,16 @@ hipError_t launch_conv(const ConvArgs& a, bool bf16, hipStream_t s) {
   dim3 grid((unsigned)((n + 255) / 256), 2, a.n_mem);
   const size_t esz = bf16 ? 2 : 4;
   const bool vec_v = ((size_t)a.Tf * esz) % 16 == 0;
-  if (bf16) {
-    if (vec_v) conv_kernel<__bf16, true><<<grid, 256, 0, s>>>(a);
-    else conv_kernel<__bf16, false><<<grid, 256, 0, s>>>(a);
-  } else {
-    if (vec_v) conv_kernel<float, true><<<grid, 256, 0, s>>>(a);
-    else conv_kernel<float, false><<<grid, 256, 0, s>>>(a);
+  switch (a.kernel) {
+    case 1: conv_launch<1>(a, bf16, vec_v, grid, s); break;
+    case 2: conv_launch<2>(a, bf16, vec_v, grid, s); break;
+    case 3: conv_launch<3>(a, bf16, vec_v, grid, s); break;
+    case 4: conv_launch<4>(a, bf16, vec_v, grid, s); break;
+    case 5: conv_launch<5>(a, bf16, vec_v, grid, s); break;
+    case 6: conv_launch<6>(a, bf16, vec_v, grid, s); break;
+    case 7: conv_launch<7>(a, bf16, vec_v, grid, s); break;
+    case 8: conv_launch<8>(a, bf16, vec_v, grid, s); break;
+    default: return hipErrorInvalidValue;
   }
   return hipGetLastError();
 }

@@ -59,6 +59,24 @@ def test_convkv_fp32_two_memory_frames():
     _run(cfg, export=True)
 
 
+@pytest.mark.parametrize("kernel", [1, 2, 3, 8])
+def test_convkv_conv_kernel_sizes(kernel):
+    """Temporal conv of 1, 2, 3 and 8 taps (stride = kernel), bf16, 2 heads:
+    outputs and every segment's K/V, the conv memory against the oracle's."""
+    cfg = synth.workload("convkv_512", heads=2, grid_h=4, grid_w=6, conv_kernel=kernel, conv_stride=kernel,
+                         blocks=8 + kernel)
+    run = _run(cfg, export=True)
+    assert run.cache.stats()["memory_count"] == 1
+
+
+def test_convkv_fp32_three_taps_two_memory_frames():
+    """fp32 conv (4-channel chunks) with 3 taps and two memory frames."""
+    cfg = synth.workload("convkv_512", dtype="f32", heads=2, head_dim=64, rope=(24, 20, 20), frames=2,
+                         grid_h=4, grid_w=4, conv_kernel=3, conv_stride=3, memory_frames=2, blocks=12)
+    run = _run(cfg, export=True)
+    assert run.cache.stats()["memory_count"] == 2
+
+
 def test_convkv_512_full_shape_sampled():
     """512x512 ConvKV at full size: 1024-token memory + 3 windows + current =
     13312 keys from block 5; outputs sampled on blocks 0, 4, 5, 7."""
