@@ -54,17 +54,38 @@ __device__ __forceinline__ void rope_pair(float& u0, float& u1, int ch, const Ro
   u1 = b;
 }
 
-// The same rotation with the table picked by selects rather than branches, so
-// that lanes whose channels fall on different axes issue one load each
-// instead of taking the three paths in turn.
-__device__ __forceinline__ void rope_pair_sel(float& u0, float& u1, int ch, const Rope& r, int trow,
-                                              int y, int x) {
+// The (cos, sin) of the channel pair (ch, ch+1) with the table picked by
+// selects rather than branches, so that lanes whose channels fall on
+// different axes issue one load each instead of taking the three paths in
+// turn; rope_rot applies it.
+__device__ __forceinline__ float2 rope_cs_sel(int ch, const Rope& r, int trow, int y, int x) {
   const bool in_t = ch < r.dt, in_h = ch < r.dt + r.dh;
   const float2* tab = in_t ? r.t : (in_h ? r.h : r.w);
   const int row = in_t ? trow : (in_h ? y : x);
   const int half = (in_t ? r.dt : (in_h ? r.dh : r.dw)) >> 1;
   const int col = (ch - (in_t ? 0 : (in_h ? r.dt : r.dt + r.dh))) >> 1;
-  const float2 cs = tab[row * half + col];
+  return tab[row * half + col];
+}
+// The same pick for kernels that load many pairs: the three tables are
+// addressed from the t table with uniform element offsets, so the selects
+// choose an index, never a kernel-argument field (which the compiler would
+// turn into a per-lane load of the argument ahead of the table load).
+struct RopeSel {
+  const float2* base;
+  long long oh, ow;
+  int dt, dth, ht, hh, hw;
+  __device__ explicit RopeSel(const Rope& r)
+      : base(r.t), oh(r.h - r.t), ow(r.w - r.t), dt(r.dt), dth(r.dt + r.dh), ht(r.dt >> 1),
+        hh(r.dh >> 1), hw(r.dw >> 1) {}
+  __device__ __forceinline__ float2 cs(int ch, int trow, int y, int x) const {
+    const bool in_t = ch < dt, in_h = ch < dth;
+    const float2* tab = base + (in_t ? 0 : (in_h ? oh : ow));
+    const int idx = in_t ? trow * ht + (ch >> 1) : (in_h ? y * hh + ((ch - dt) >> 1) : x * hw + ((ch - dth) >> 1));
+    return tab[idx];
+  }
+};
+
+__device__ __forceinline__ void rope_rot(float& u0, float& u1, float2 cs) {
   const float a = u0 * cs.x - u1 * cs.y;
   const float b = u0 * cs.y + u1 * cs.x;
   u0 = a;
@@ -1384,28 +1405,38 @@ __global__ __launch_bounds__(256) void gather_kernel(GatherArgs a) {
     t_row0 += rank * a.frames;
   }
   // every chunk's load first, then the rotations, then the stores: IT
-  // independent 16-byte loads in flight per thread
+  // independent 16-byte loads in flight per thread (rows past the tail load
+  // the tile's last row and are not stored, so no load sits in a branch)
   constexpr int IT = 64 * CPR / 256;
   static_assert(IT * 256 == 64 * CPR, "tile of 64 rows in whole passes of 256 threads");
   const T* sbase = static_cast<const T*>(src) + head * src_hs;
+  // the table loads first (cache hits), then the rows, all in flight together
+  float2 cs[IT][VEC / 2];
+  if (rope) {
+    const RopeSel rs(a.rope);
+#pragma unroll
+    for (int it = 0; it < IT; ++it) {
+      const int task = threadIdx.x + 256 * it, r = min(task / CPR, ntok - 1), c = task % CPR;
+      int f, y, x;
+      token_fyx(tile0 + r, a.rope.grid_h, a.rope.grid_w, f, y, x);
+#pragma unroll
+      for (int e = 0; e < VEC; e += 2) cs[it][e / 2] = rs.cs(c * VEC + e, t_row0 + f, y, x);
+    }
+  }
   uint4 raw[IT];
 #pragma unroll
   for (int it = 0; it < IT; ++it) {
-    const int task = threadIdx.x + 256 * it, r = task / CPR, c = task % CPR;
-    if (r < ntok) raw[it] = *reinterpret_cast<const uint4*>(sbase + (size_t)(tile0 + r) * D + c * VEC);
+    const int task = threadIdx.x + 256 * it, r = min(task / CPR, ntok - 1), c = task % CPR;
+    raw[it] = *reinterpret_cast<const uint4*>(sbase + (size_t)(tile0 + r) * D + c * VEC);
   }
   if (rope) {
 #pragma unroll
     for (int it = 0; it < IT; ++it) {
-      const int task = threadIdx.x + 256 * it, r = task / CPR, c = task % CPR;
-      if (r >= ntok) continue;
-      int f, y, x;
-      token_fyx(tile0 + r, a.rope.grid_h, a.rope.grid_w, f, y, x);
       T* kv = reinterpret_cast<T*>(&raw[it]);
 #pragma unroll
       for (int e = 0; e < VEC; e += 2) {
         float u0 = to_f(kv[e]), u1 = to_f(kv[e + 1]);
-        rope_pair_sel(u0, u1, c * VEC + e, a.rope, t_row0 + f, y, x);
+        rope_rot(u0, u1, cs[it][e / 2]);
         kv[e] = from_f<T>(u0);
         kv[e + 1] = from_f<T>(u1);
       }
@@ -1445,27 +1476,36 @@ __global__ __launch_bounds__(256) void gather_k8_kernel(GatherArgs a) {
     t_row0 += rank * a.frames;
   }
   const __bf16* sbase = static_cast<const __bf16*>(src) + head * src_hs;
+  // the table loads first (cache hits), then the rows, all in flight together
+  float2 cs[IT][VEC / 2];
+  if (rope) {
+    const RopeSel rs(a.rope);
+#pragma unroll
+    for (int it = 0; it < IT; ++it) {
+      const int task = tid + 256 * it, r = min(task / CPR, ntok - 1), c = task % CPR;
+      int f, y, x;
+      token_fyx(tile0 + r, a.rope.grid_h, a.rope.grid_w, f, y, x);
+#pragma unroll
+      for (int e = 0; e < VEC; e += 2) cs[it][e / 2] = rs.cs(c * VEC + e, t_row0 + f, y, x);
+    }
+  }
   float kr[IT][VEC];
   bf16x8 raw[IT];
 #pragma unroll
-  for (int it = 0; it < IT; ++it) {
-    const int task = tid + 256 * it, r = task / CPR, c = task % CPR;
-    if (r < ntok) raw[it] = *reinterpret_cast<const bf16x8*>(sbase + (size_t)(tile0 + r) * D + c * VEC);
+  for (int it = 0; it < IT; ++it) {   // rows past the tail load the last row (not used)
+    const int task = tid + 256 * it, r = min(task / CPR, ntok - 1), c = task % CPR;
+    raw[it] = *reinterpret_cast<const bf16x8*>(sbase + (size_t)(tile0 + r) * D + c * VEC);
   }
   float amax = 0.f;
 #pragma unroll
   for (int it = 0; it < IT; ++it) {
-    const int task = tid + 256 * it, r = task / CPR, c = task % CPR;
+    const int task = tid + 256 * it, r = task / CPR;
+    const bool live = r < ntok;           // rows past the tail count as 0
 #pragma unroll
-    for (int e = 0; e < VEC; ++e) kr[it][e] = 0.f;
-    if (r >= ntok) continue;
-#pragma unroll
-    for (int e = 0; e < VEC; ++e) kr[it][e] = (float)raw[it][e];
+    for (int e = 0; e < VEC; ++e) kr[it][e] = live ? (float)raw[it][e] : 0.f;
     if (rope) {
-      int f, y, x;
-      token_fyx(tile0 + r, a.rope.grid_h, a.rope.grid_w, f, y, x);
 #pragma unroll
-      for (int e = 0; e < VEC; e += 2) rope_pair_sel(kr[it][e], kr[it][e + 1], c * VEC + e, a.rope, t_row0 + f, y, x);
+      for (int e = 0; e < VEC; e += 2) rope_rot(kr[it][e], kr[it][e + 1], cs[it][e / 2]);
     }
 #pragma unroll
     for (int e = 0; e < VEC; ++e) amax = fmaxf(amax, fabsf(kr[it][e]));
