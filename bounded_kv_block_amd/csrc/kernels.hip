@@ -266,36 +266,71 @@ __global__ __launch_bounds__(256) void append_kernel(AppendArgs a) {
   const int head = blockIdx.y;
   const int tid = threadIdx.x;
   const int ntok = min(64, a.T - tile0);
-  const bool rope = has_rope(a.rope);
-  for (int task = tid; task < 64 * CPR; task += 256) {
-    const int r = task / CPR, c = task - r * CPR;
-    if (r >= ntok) continue;
-    const int tok = tile0 + r;
-    const size_t src = ((size_t)tok * a.H + head) * D + c * VEC;
-    const uint4 kraw = *reinterpret_cast<const uint4*>(static_cast<const T*>(a.k_in) + src);
-    const uint4 vraw = *reinterpret_cast<const uint4*>(static_cast<const T*>(a.v_in) + src);
-    *reinterpret_cast<uint4*>(s_v + r * RS + ((c ^ ((r >> 3) & 7)) << 4)) = vraw;
-    if (a.k_raw) {
-      T* dst = static_cast<T*>(a.k_raw) + head * a.k_raw_hs + (size_t)tok * D + c * VEC;
-      *reinterpret_cast<uint4*>(dst) = kraw;
-    }
-    if (a.k_rot) {
-      uint4 kout = kraw;
-      if (rope) {
-        int f, y, x;
-        token_fyx(tok, a.rope.grid_h, a.rope.grid_w, f, y, x);
-        const T* kin = reinterpret_cast<const T*>(&kraw);
-        T* ko = reinterpret_cast<T*>(&kout);
+  const bool rot = a.k_rot && has_rope(a.rope);
+  // every load first (RoPE table entries, then the K and V rows), then the
+  // rotations and stores; rows past the block's end load its last row and
+  // store nothing, so no load sits in a branch
+  constexpr int IT = 64 * CPR / 256;
+  static_assert(IT * 256 == 64 * CPR, "tile of 64 rows in whole passes of 256 threads");
+  float2 cs[IT][VEC / 2];
+  if (rot) {
+    const RopeSel rs(a.rope);
 #pragma unroll
-        for (int e = 0; e < VEC; e += 2) {
-          float u0 = to_f(kin[e]), u1 = to_f(kin[e + 1]);
-          rope_pair(u0, u1, c * VEC + e, a.rope, a.t_row0 + f, y, x);
-          ko[e] = from_f<T>(u0);
-          ko[e + 1] = from_f<T>(u1);
-        }
+    for (int it = 0; it < IT; ++it) {
+      const int task = tid + 256 * it, r = min(task / CPR, ntok - 1), c = task % CPR;
+      int f, y, x;
+      token_fyx(tile0 + r, a.rope.grid_h, a.rope.grid_w, f, y, x);
+#pragma unroll
+      for (int e = 0; e < VEC; e += 2) cs[it][e / 2] = rs.cs(c * VEC + e, a.t_row0 + f, y, x);
+    }
+  }
+  typedef T chunk __attribute__((ext_vector_type(VEC)));   // one 16-byte chunk
+  chunk kraw[IT], vraw[IT];
+#pragma unroll
+  for (int it = 0; it < IT; ++it) {
+    const int task = tid + 256 * it, r = min(task / CPR, ntok - 1), c = task % CPR;
+    const size_t src = ((size_t)(tile0 + r) * a.H + head) * D + c * VEC;
+    kraw[it] = *reinterpret_cast<const chunk*>(static_cast<const T*>(a.k_in) + src);
+    vraw[it] = *reinterpret_cast<const chunk*>(static_cast<const T*>(a.v_in) + src);
+  }
+  // raw K rows (a context rotated per block, and the conv) as soon as they
+  // arrive, V rows into LDS unguarded (rows past the end are never read
+  // back), K rotated in registers, then the guarded rotated-K stores
+  if (a.k_raw) {
+#pragma unroll
+    for (int it = 0; it < IT; ++it) {
+      const int task = tid + 256 * it, r = task / CPR, c = task % CPR;
+      if (r < ntok)
+        *reinterpret_cast<chunk*>(static_cast<T*>(a.k_raw) + head * a.k_raw_hs + (size_t)(tile0 + r) * D + c * VEC) =
+            kraw[it];
+    }
+  }
+#pragma unroll
+  for (int it = 0; it < IT; ++it) {
+    const int task = tid + 256 * it, r = task / CPR, c = task % CPR;
+    *reinterpret_cast<chunk*>(s_v + r * RS + ((c ^ ((r >> 3) & 7)) << 4)) = vraw[it];
+  }
+  chunk kout[IT];
+#pragma unroll
+  for (int it = 0; it < IT; ++it) {
+    kout[it] = kraw[it];
+    if (rot) {
+#pragma unroll
+      for (int e = 0; e < VEC; e += 2) {
+        float u0 = to_f(kraw[it][e]), u1 = to_f(kraw[it][e + 1]);
+        rope_rot(u0, u1, cs[it][e / 2]);
+        kout[it][e] = from_f<T>(u0);
+        kout[it][e + 1] = from_f<T>(u1);
       }
-      T* dst = static_cast<T*>(a.k_rot) + head * a.k_rot_hs + (size_t)(a.k_rot_off + tok) * D + c * VEC;
-      *reinterpret_cast<uint4*>(dst) = kout;
+    }
+  }
+  if (a.k_rot) {
+#pragma unroll
+    for (int it = 0; it < IT; ++it) {
+      const int task = tid + 256 * it, r = task / CPR, c = task % CPR;
+      if (r < ntok)
+        *reinterpret_cast<chunk*>(static_cast<T*>(a.k_rot) + head * a.k_rot_hs +
+                                  (size_t)(a.k_rot_off + tile0 + r) * D + c * VEC) = kout[it];
     }
   }
   __syncthreads();
@@ -333,28 +368,56 @@ __global__ __launch_bounds__(256) void append_k8_kernel(AppendArgs a) {
   const int tid = threadIdx.x;
   const int ntok = min(64, a.T - tile0);
   const bool rope = has_rope(a.rope);
+  // every load first (RoPE table entries, then the K and V rows); rows past
+  // the block's end load its last row, count as 0 and store nothing
+  float2 cs[IT][VEC / 2];
+  if (rope) {
+    const RopeSel rs(a.rope);
+#pragma unroll
+    for (int it = 0; it < IT; ++it) {
+      const int task = tid + 256 * it, r = min(task / CPR, ntok - 1), c = task % CPR;
+      int f, y, x;
+      token_fyx(tile0 + r, a.rope.grid_h, a.rope.grid_w, f, y, x);
+#pragma unroll
+      for (int e = 0; e < VEC; e += 2) cs[it][e / 2] = rs.cs(c * VEC + e, a.t_row0 + f, y, x);
+    }
+  }
+  bf16x8 kraw[IT];
+  uint4 vraw[IT];
+#pragma unroll
+  for (int it = 0; it < IT; ++it) {
+    const int task = tid + 256 * it, r = min(task / CPR, ntok - 1), c = task % CPR;
+    const size_t src = ((size_t)(tile0 + r) * a.H + head) * D + c * VEC;
+    kraw[it] = *reinterpret_cast<const bf16x8*>(static_cast<const __bf16*>(a.k_in) + src);
+    vraw[it] = *reinterpret_cast<const uint4*>(static_cast<const __bf16*>(a.v_in) + src);
+  }
+  // V rows into LDS unguarded (rows past the end are never read back), raw K
+  // (a context rotated per block, and the conv) stored for live rows
+#pragma unroll
+  for (int it = 0; it < IT; ++it) {
+    const int task = tid + 256 * it, r = task / CPR, c = task % CPR;
+    *reinterpret_cast<uint4*>(s_v + r * RS + ((c ^ ((r >> 3) & 7)) << 4)) = vraw[it];
+  }
+  if (a.k_raw) {
+#pragma unroll
+    for (int it = 0; it < IT; ++it) {
+      const int task = tid + 256 * it, r = task / CPR, c = task % CPR;
+      if (r < ntok)
+        *reinterpret_cast<bf16x8*>(static_cast<__bf16*>(a.k_raw) + head * a.k_raw_hs + (size_t)(tile0 + r) * D +
+                                   c * VEC) = kraw[it];
+    }
+  }
   float kr[IT][VEC];
   float amax = 0.f;
 #pragma unroll
   for (int it = 0; it < IT; ++it) {
-    const int task = tid + 256 * it, r = task / CPR, c = task % CPR;
+    const int task = tid + 256 * it, r = task / CPR;
+    const bool live = r < ntok;
 #pragma unroll
-    for (int e = 0; e < VEC; ++e) kr[it][e] = 0.f;
-    if (r >= ntok) continue;
-    const int tok = tile0 + r;
-    const size_t src = ((size_t)tok * a.H + head) * D + c * VEC;
-    const bf16x8 kraw = *reinterpret_cast<const bf16x8*>(static_cast<const __bf16*>(a.k_in) + src);
-    const uint4 vraw = *reinterpret_cast<const uint4*>(static_cast<const __bf16*>(a.v_in) + src);
-    *reinterpret_cast<uint4*>(s_v + r * RS + ((c ^ ((r >> 3) & 7)) << 4)) = vraw;
-    if (a.k_raw)                         // raw K for a context rotated per block (and the conv)
-      *reinterpret_cast<bf16x8*>(static_cast<__bf16*>(a.k_raw) + head * a.k_raw_hs + (size_t)tok * D + c * VEC) = kraw;
-#pragma unroll
-    for (int e = 0; e < VEC; ++e) kr[it][e] = (float)kraw[e];
+    for (int e = 0; e < VEC; ++e) kr[it][e] = live ? (float)kraw[it][e] : 0.f;
     if (rope) {
-      int f, y, x;
-      token_fyx(tok, a.rope.grid_h, a.rope.grid_w, f, y, x);
 #pragma unroll
-      for (int e = 0; e < VEC; e += 2) rope_pair(kr[it][e], kr[it][e + 1], c * VEC + e, a.rope, a.t_row0 + f, y, x);
+      for (int e = 0; e < VEC; e += 2) rope_rot(kr[it][e], kr[it][e + 1], cs[it][e / 2]);
     }
 #pragma unroll
     for (int e = 0; e < VEC; ++e) amax = fmaxf(amax, fabsf(kr[it][e]));
