@@ -122,14 +122,19 @@ __global__ void rope_table_kernel(float2* tab, int rows, int half, int dim, long
 // over the pose dimensions (staged through LDS 64 dimensions at a time, rows
 // padded so that the 256 lanes hit distinct banks); 0 when either norm is 0.
 // Rank: (score desc, stream id asc), k rounds of an arg-max by wave 0.
+// Staging: each thread issues kOpenBatch pose loads before it writes any of
+// them to LDS (indices past the end load the last element again).
 constexpr int kOpenThreads = 256;
 constexpr int kOpenChunk = 64;
+constexpr int kOpenBatch = 4;
 __global__ __launch_bounds__(kOpenThreads) void open_kernel(OpenArgs a) {
   __shared__ double s_score[kMaxBank];
   __shared__ int s_taken[kMaxBank];
+  __shared__ int s_slot[kMaxBank];
   __shared__ float s_q[kOpenChunk];
   __shared__ float s_b[kMaxBank][kOpenChunk + 1];
   const int tid = threadIdx.x, lane = tid & 63;
+  if (tid < a.nbank) s_slot[tid] = a.bank_slot[tid];
   if (a.pose_in) {
     for (int i = tid; i < a.P; i += kOpenThreads) a.pose_store[(size_t)a.cur_slot * a.P + i] = a.pose_in[i];
   }
@@ -151,9 +156,23 @@ __global__ __launch_bounds__(kOpenThreads) void open_kernel(OpenArgs a) {
     const int w = min(kOpenChunk, a.P - c0);
     __syncthreads();                       // the previous chunk has been consumed
     if (tid < w) s_q[tid] = qsrc[c0 + tid];
-    for (int idx = tid; idx < nb * w; idx += kOpenThreads) {
-      const int c = idx / w, i = idx - c * w;
-      s_b[c][i] = a.pose_store[(size_t)a.bank_slot[c] * a.P + c0 + i];
+    const int n = nb * w;
+    for (int base = 0; base < n; base += kOpenBatch * kOpenThreads) {
+      float v[kOpenBatch];
+#pragma unroll
+      for (int u = 0; u < kOpenBatch; ++u) {
+        const int idx = min(base + u * kOpenThreads + tid, n - 1);
+        const int c = idx / w, i = idx - c * w;
+        v[u] = a.pose_store[(size_t)s_slot[c] * a.P + c0 + i];
+      }
+#pragma unroll
+      for (int u = 0; u < kOpenBatch; ++u) {
+        const int idx = base + u * kOpenThreads + tid;
+        if (idx < n) {
+          const int c = idx / w, i = idx - c * w;
+          s_b[c][i] = v[u];
+        }
+      }
     }
     __syncthreads();
     if (tid < nb) {
