@@ -1107,26 +1107,41 @@ void attn_bf16_kernel(AttnArgs a) {
       s_v[tid] = s_vb[tid] + 2 * head * s_vhs[tid];
       if constexpr (KF8) s_x[tid] = s_xb[tid] + head * s_xhs[tid];
     }
+    // Q of the unit: the RoPE table entries and the 8 row chunks of a lane
+    // are loaded before the first use (rows past the block's end load its
+    // last row and are zeroed)
+    const bool valid = qrow < a.T;
+    const int qr = valid ? qrow : a.T - 1;
+    const bool rope = has_rope(a.rope);
+    const __bf16* qp = static_cast<const __bf16*>(a.q) + ((size_t)qr * a.H + head) * AD;
     if constexpr (KF8) {   // Q of the unit as E4M3, one scale per query
-      int f = 0, y = 0, x = 0;
-      const bool valid = qrow < a.T;
-      if (valid) token_fyx(qrow, a.rope.grid_h, a.rope.grid_w, f, y, x);
-      const bool rope = has_rope(a.rope);
-      const __bf16* qp = static_cast<const __bf16*>(a.q) + ((size_t)(valid ? qrow : 0) * a.H + head) * AD;
+      float2 cs[8][4];
+      if (rope) {
+        int f, y, x;
+        token_fyx(qr, a.rope.grid_h, a.rope.grid_w, f, y, x);
+        const RopeSel rsel(a.rope);
+#pragma unroll
+        for (int k = 0; k < 8; ++k)
+#pragma unroll
+          for (int e = 0; e < 8; e += 2)
+            cs[k][e / 2] = rsel.cs(64 * (k >> 2) + 32 * hh + 8 * (k & 3) + e, a.t_row0 + f, y, x);
+      }
+      bf16x8 raw[8];
+#pragma unroll
+      for (int k = 0; k < 8; ++k) raw[k] = *reinterpret_cast<const bf16x8*>(qp + 64 * (k >> 2) + 32 * hh + 8 * (k & 3));
       float u[2][32];
       float mx = 0.f;
 #pragma unroll
       for (int s2 = 0; s2 < 2; ++s2)
 #pragma unroll
         for (int c4 = 0; c4 < 4; ++c4) {
-          const int d0 = 64 * s2 + 32 * hh + 8 * c4;
-          const bf16x8 raw = valid ? *reinterpret_cast<const bf16x8*>(qp + d0) : bf16x8{};
+          const int k = 4 * s2 + c4;
           float* w = &u[s2][8 * c4];
 #pragma unroll
-          for (int e = 0; e < 8; ++e) w[e] = (float)raw[e];
-          if (rope && valid) {
+          for (int e = 0; e < 8; ++e) w[e] = valid ? (float)raw[k][e] : 0.f;
+          if (rope) {
 #pragma unroll
-            for (int e = 0; e < 8; e += 2) rope_pair(w[e], w[e + 1], d0 + e, a.rope, a.t_row0 + f, y, x);
+            for (int e = 0; e < 8; e += 2) rope_rot(w[e], w[e + 1], cs[k][e / 2]);
           }
 #pragma unroll
           for (int e = 0; e < 8; ++e) {
@@ -1146,22 +1161,28 @@ void attn_bf16_kernel(AttnArgs a) {
         for (int w = 0; w < 8; ++w)
           qreg8[s2][w] = e4m3_pack4(u[s2][4 * w] * inv, u[s2][4 * w + 1] * inv, u[s2][4 * w + 2] * inv,
                                     u[s2][4 * w + 3] * inv);
-    } else {   // Q of the unit
-      int f = 0, y = 0, x = 0;
-      const bool valid = qrow < a.T;
-      if (valid) token_fyx(qrow, a.rope.grid_h, a.rope.grid_w, f, y, x);
-      const bool rope = has_rope(a.rope);
-      const __bf16* qp = static_cast<const __bf16*>(a.q) + ((size_t)(valid ? qrow : 0) * a.H + head) * AD;
+    } else {
+      float2 cs[8][4];
+      if (rope) {
+        int f, y, x;
+        token_fyx(qr, a.rope.grid_h, a.rope.grid_w, f, y, x);
+        const RopeSel rsel(a.rope);
+#pragma unroll
+        for (int s = 0; s < 8; ++s)
+#pragma unroll
+          for (int e = 0; e < 8; e += 2) cs[s][e / 2] = rsel.cs(16 * s + 8 * hh + e, a.t_row0 + f, y, x);
+      }
+      bf16x8 raw[8];
+#pragma unroll
+      for (int s = 0; s < 8; ++s) raw[s] = *reinterpret_cast<const bf16x8*>(qp + 16 * s + 8 * hh);
 #pragma unroll
       for (int s = 0; s < 8; ++s) {
-        const int d0 = 16 * s + 8 * hh;
-        bf16x8 raw = valid ? *reinterpret_cast<const bf16x8*>(qp + d0) : bf16x8{};
         float u[8];
 #pragma unroll
-        for (int e = 0; e < 8; ++e) u[e] = (float)raw[e];
-        if (rope && valid) {
+        for (int e = 0; e < 8; ++e) u[e] = valid ? (float)raw[s][e] : 0.f;
+        if (rope) {
 #pragma unroll
-          for (int e = 0; e < 8; e += 2) rope_pair(u[e], u[e + 1], d0 + e, a.rope, a.t_row0 + f, y, x);
+          for (int e = 0; e < 8; e += 2) rope_rot(u[e], u[e + 1], cs[s][e / 2]);
         }
 #pragma unroll
         for (int e = 0; e < 8; ++e) qreg[s][e] = (__bf16)(u[e] * a.qscale);
