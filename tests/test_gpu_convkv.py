@@ -69,6 +69,14 @@ def test_convkv_conv_kernel_sizes(kernel):
     assert run.cache.stats()["memory_count"] == 1
 
 
+def test_convkv_odd_frame_size():
+    """15-token frames (3 x 5): a V^T row of a frame is 30 bytes, so the conv
+    reads and writes V^T element by element; 45-token blocks, ragged tiles."""
+    cfg = synth.workload("convkv_512", heads=2, grid_h=3, grid_w=5, blocks=10)
+    run = _run(cfg, export=True)
+    assert run.cache.stats()["memory_count"] == 1
+
+
 def test_convkv_fp32_three_taps_two_memory_frames():
     """fp32 conv (4-channel chunks) with 3 taps and two memory frames."""
     cfg = synth.workload("convkv_512", dtype="f32", heads=2, head_dim=64, rope=(24, 20, 20), frames=2,
