@@ -2,8 +2,8 @@
 //
 //   rope_table_kernel  (cos, sin) tables of the 3D RoPE, computed in fp64
 //   open_kernel        block open: store the pose, cosine top-k over the bank
-//                      (fp64, one wavefront, ties to the lower stream id), and
-//                      the current block's temporal RoPE rows
+//                      (fp64, one thread per candidate, ties to the lower
+//                      stream id), and the current block's temporal RoPE rows
 //   append_kernel      K with fused 3D RoPE -> cache rows; V -> cache V^T
 //   append_k8_kernel   the same with K stored as E4M3 + per-tile exponents
 //   qkv_gemm_kernel    fused QKV projection (bf16 MFMA) with the append's
@@ -11,9 +11,12 @@
 //   attn_bf16_kernel   flash attention on bf16 MFMA (32x32x16), K/V tiles
 //                      staged in LDS, online softmax in fp32; with an FP8
 //                      key cache Q K^T runs on scaled E4M3 MFMA (32x32x64)
+//   attn_merge_kernel  split launch: combines the key parts of the cut units
 //   attn_f32_kernel    the same contraction in fp32 on the vector ALUs
-//   gather_kernel      ConvKV: raw K of memory + window -> context-K rows,
-//                      rotated at context positions
+//   gather_kernel      ConvKV and context-relative positions: raw K of the
+//                      context's cached segments -> context-K rows, rotated
+//                      at context positions
+//   gather_k8_kernel   the same into E4M3 rows + per-tile exponents
 //   conv_kernel        ConvKV: depthwise temporal conv of evicted frames
 //   export_kernel      inspection copy of one context segment
 #include <math.h>
@@ -138,17 +141,22 @@ __global__ __launch_bounds__(kOpenThreads) void open_kernel(OpenArgs a) {
   if (a.pose_in) {
     for (int i = tid; i < a.P; i += kOpenThreads) a.pose_store[(size_t)a.cur_slot * a.P + i] = a.pose_in[i];
   }
-  if (a.ttab) {
+  // the block's temporal RoPE rows: (cos, sin) of (t_pos0 + r) * theta^(-2i/t_dim)
+  auto write_ttab = [&](int first, int stride) {
+    if (!a.ttab) return;
     const int half = a.t_dim >> 1;
-    for (int idx = tid; idx < a.t_rows * half; idx += kOpenThreads) {
+    for (int idx = first; idx < a.t_rows * half; idx += stride) {
       const int r = idx / half, i = idx - r * half;
       const double w = pow(a.theta, -2.0 * (double)i / (double)a.t_dim);
       double sn, cs;
       sincos((double)(a.t_pos0 + r) * w, &sn, &cs);
       a.ttab[idx] = make_float2((float)cs, (float)sn);
     }
+  };
+  if (a.k <= 0 || a.nbank <= 0) {
+    write_ttab(tid, kOpenThreads);
+    return;
   }
-  if (a.k <= 0 || a.nbank <= 0) return;
   const int nb = a.nbank;
   const float* qsrc = a.query ? a.query : a.pose_in;
   double qq = 0.0, dot = 0.0, bb = 0.0;
@@ -192,7 +200,10 @@ __global__ __launch_bounds__(kOpenThreads) void open_kernel(OpenArgs a) {
     s_taken[tid] = 0;
   }
   __syncthreads();
-  if (tid >= 64) return;
+  if (tid >= 64) {                       // waves 1-3 write the RoPE rows while wave 0 ranks
+    write_ttab(tid - 64, kOpenThreads - 64);
+    return;
+  }
   const int kk = a.k < nb ? a.k : nb;
   for (int r = 0; r < kk; ++r) {
     double best = -INFINITY;
