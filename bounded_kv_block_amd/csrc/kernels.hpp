@@ -30,6 +30,8 @@ constexpr int kStreamWG = 256;
 constexpr int kStreamPerXcd = kStreamWG / 8;
 constexpr size_t kSplitSlotBytes = 8 * 64 * 64 * 4 + 8 * 2 * 64 * 4;   // O registers + (m, l)
 
+// The three tables lie in one allocation (the handle's workspace): kernels
+// that pick a table per lane address h and w as element offsets from t.
 struct Rope {                   // 3D RoPE tables: (cos, sin) fp32 pairs, built in fp64
   const float2* t;              // [rows][dt/2]; row r <-> temporal position of row r
   const float2* h;              // [grid_h][dh/2]
