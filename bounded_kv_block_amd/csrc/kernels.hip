@@ -57,22 +57,14 @@ __device__ __forceinline__ void rope_pair(float& u0, float& u1, int ch, const Ro
   u1 = b;
 }
 
-// The (cos, sin) of the channel pair (ch, ch+1) with the table picked by
+// The (cos, sin) of the channel pair (ch, ch+1), with the table picked by
 // selects rather than branches, so that lanes whose channels fall on
 // different axes issue one load each instead of taking the three paths in
-// turn; rope_rot applies it.
-__device__ __forceinline__ float2 rope_cs_sel(int ch, const Rope& r, int trow, int y, int x) {
-  const bool in_t = ch < r.dt, in_h = ch < r.dt + r.dh;
-  const float2* tab = in_t ? r.t : (in_h ? r.h : r.w);
-  const int row = in_t ? trow : (in_h ? y : x);
-  const int half = (in_t ? r.dt : (in_h ? r.dh : r.dw)) >> 1;
-  const int col = (ch - (in_t ? 0 : (in_h ? r.dt : r.dt + r.dh))) >> 1;
-  return tab[row * half + col];
-}
-// The same pick for kernels that load many pairs: the three tables are
-// addressed from the t table with uniform element offsets, so the selects
-// choose an index, never a kernel-argument field (which the compiler would
-// turn into a per-lane load of the argument ahead of the table load).
+// turn, and no load sits in a branch.  The three tables are addressed from
+// the t table with uniform element offsets, so the selects choose an index,
+// never a kernel-argument field (which the compiler would turn into a
+// per-lane load of the argument ahead of the table load).  rope_rot applies
+// the pair.
 struct RopeSel {
   const float2* base;
   long long oh, ow;
