@@ -169,7 +169,8 @@ typedef struct {
   size_t workspace_bytes;  /* bytes of workspace in use (constant for the handle's life) */
   int64_t split_attends;   /* bf16 attends since create/reset whose attention cut its last,
                               unfilled round of units (heads x 256-query tiles; > 15% of 256
-                              workgroup slots idle) into key parts: a second attention launch */
+                              workgroup slots idle) into key parts: a second attention launch,
+                              and a third that merges the parts when a unit has more than one */
 } bkv_stats_t;
 
 /* Workspace bytes needed for cfg.  Pure host call.
