@@ -26,6 +26,9 @@ def command(out: str = LIB) -> list:
             # no packed-fp32 VALU forms in the device code
             "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
             "-Wall", "-Wno-unused-function",
+            # an inline-asm diagnostic (e.g. a reserved register in a clobber
+            # list) is an error, not a warning to scroll past
+            "-Werror=inline-asm",
             f"-I{os.path.join(ROOT, 'include')}", f"-I{CSRC}", *SOURCES, "-o", out]
 
 

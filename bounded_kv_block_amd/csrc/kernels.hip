@@ -564,16 +564,18 @@ __device__ __forceinline__ i32x4 buffer_rsrc(const char* base) {
 // (buffer_load_dwordx4 ... lds).  Written in asm so that the compiler does
 // not treat every later LDS read as waiting on it: the caller waits with
 // vmcnt(0) before the barrier that publishes the tile.  No register output.
+// The LDS address goes in as an operand bound to m0 ("{m0}"), so the compiler
+// writes m0 itself and knows it is live; the s_nop separates that write from
+// the load that reads it.
 __device__ __forceinline__ void dma16(i32x4 rsrc, unsigned voff, unsigned soff, unsigned lds_base) {
   // every scalar operand must sit in SGPRs, never a folded literal
   asm volatile("" : "+s"(soff), "+s"(rsrc), "+s"(lds_base));
   asm volatile(
-      "s_mov_b32 m0, %0\n\t"
       "s_nop 0\n\t"
-      "buffer_load_dwordx4 %1, %2, %3 offen lds"
+      "buffer_load_dwordx4 %0, %1, %2 offen lds"
       :
-      : "s"(lds_base), "v"(voff), "s"(rsrc), "s"(soff)
-      : "memory", "m0");
+      : "v"(voff), "s"(rsrc), "s"(soff), "{m0}"(lds_base)
+      : "memory");
 }
 
 // Tile cursor over the context segments: every full 64-key tile of every
