@@ -1,14 +1,23 @@
-"""FP8 (OCP E4M3) quantisation of attention keys and queries, fp64 (test infrastructure).
+"""FP8 (OCP E4M3) quantisation inside attention, fp64 (test infrastructure).
 
-The SoulX-LiveAct page (section 关键信息速览, and its 上手实践 deployment notes)
-runs attention in FP8 but fixes no scheme.  Reading taken here, for the PR-Sink
-cache mode with an FP8 key cache:
+The SoulX-LiveAct page (section 关键信息速览, and its 上手实践 deployment notes,
+which offer an FP8 KV cache) runs attention in FP8 but fixes no scheme.
+Reading taken here:
 
-  * K after RoPE is stored as E4M3 with one power-of-two scale per (head,
-    64-token tile of a block).
+  * FP8 key cache: K after RoPE is stored as E4M3 with one power-of-two scale
+    per (head, 64-token tile of a context segment, counted from the segment's
+    first token).
   * Q after RoPE, times softmax_scale * log2(e), is quantised the same way with
-    one scale per (query token, head).
-  * Q K^T uses the quantised values.  V, the softmax and P V are unchanged.
+    one scale per (query token, head).  The base-2 logits are the products of
+    these E4M3 values; P = 2^(logit - row max) is the softmax's numerator.
+  * Q K^T uses the quantised values.  With the key cache alone, V, the
+    softmax and P V are unchanged.
+  * FP8 KV cache (``attention_fp8_pv``): V is stored as E4M3 with the key
+    cache's tile rule (one power-of-two scale per head and 64-token tile of a
+    segment, over all channels), and P, taken against the exact row max so
+    that every P lies in (0, 1], is rounded to E4M3 at unit scale (P below
+    2^-10 becomes 0) before the P V product.  The denominator is the sum of
+    the unrounded P.
 
 E4M3 (OCP "fn" variant): 1 sign bit, 4 exponent bits with bias 7, 3 mantissa
 bits, no infinities; the largest finite magnitude is 448 and subnormals are
@@ -79,3 +88,29 @@ def quantize_queries(q_scaled) -> np.ndarray:
     q = np.asarray(q_scaled, np.float64)
     sc = np.ldexp(1.0, pow2_exponents(np.abs(q).max(axis=2)))[:, :, None]
     return e4m3_round(q / sc) * sc
+
+
+def quantize_values(v) -> np.ndarray:
+    """Dequantised E4M3 V [T, H, D] of one context segment: the key cache's
+    tile rule (one scale per 64-token tile and head, over all channels)."""
+    return quantize_keys(v)
+
+
+def attention_fp8_pv(q, k, v, rows=None) -> np.ndarray:
+    """o [Nq, H, D] for (already quantised) q and k and a quantised v, with
+    base-2 logits z = q . k: P = 2^(z - max_j z) rounded to E4M3 at unit
+    scale, o = sum_j P~_j v_j / sum_j P_j (the unrounded sum), fp64.
+    ``rows`` restricts the work to a subset of query rows (others zero)."""
+    q = np.asarray(q, np.float64)
+    k = np.asarray(k, np.float64)
+    v = np.asarray(v, np.float64)
+    Nq, H, D = q.shape
+    out = np.zeros((Nq, H, v.shape[-1]), np.float64)
+    rs = np.arange(Nq) if rows is None else np.asarray(rows)
+    for h in range(H):
+        for c0 in range(0, len(rs), 256):
+            r = rs[c0:c0 + 256]
+            z = q[r, h, :] @ k[:, h, :].T
+            p = np.exp2(z - z.max(axis=1, keepdims=True))
+            out[r, h, :] = (e4m3_round(p) @ v[:, h, :]) / p.sum(axis=1, keepdims=True)
+    return out

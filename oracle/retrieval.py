@@ -5,8 +5,9 @@ retrieval is by pose similarity): the dynamic sink holds historical blocks
 whose pose resembles the current one.  The page does not name the measure;
 the reading taken is cosine similarity between the current block's pose and
 each bank block's pose, top-k, ranked by (cosine descending, stream id
-ascending) so exact ties go to the lower id.  A zero-norm vector scores 0.
-Fewer candidates than k: return all of them.
+ascending) so exact ties go to the lower id.  A zero-norm vector scores 0,
+and so does a pose holding a non-finite value (Inf or NaN: its cosine has no
+value).  Fewer candidates than k: return all of them.
 
 Exactness: every fp32 value is an integer multiple of 2**-149, so scaling by
 2**149 turns the poses into Python integers and all dot products are exact.
@@ -23,19 +24,23 @@ import numpy as np
 _SCALE = 2.0 ** 149
 
 
-def _as_ints(v) -> list:
-    a = np.asarray(v, dtype=np.float32).astype(np.float64) * _SCALE   # exact: power-of-two scaling
-    return [int(x) for x in a]
+def _as_ints(v):
+    """The pose as exact integers, or None if it holds Inf or NaN."""
+    a = np.asarray(v, dtype=np.float32).astype(np.float64)
+    if not np.all(np.isfinite(a)):
+        return None
+    return [int(x) for x in a * _SCALE]                 # exact: power-of-two scaling
 
 
 def exact_keys(query, bank: list) -> list:
-    """Exact ranking key for each (id, pose) in ``bank``: Fraction d|d| / |b|^2, 0 for zero norms."""
+    """Exact ranking key for each (id, pose) in ``bank``: Fraction d|d| / |b|^2;
+    0 for zero norms and for non-finite poses."""
     q = _as_ints(query)
-    qq = sum(x * x for x in q)
+    qq = 0 if q is None else sum(x * x for x in q)
     keys = []
     for _, pose in bank:
         b = _as_ints(pose)
-        bb = sum(x * x for x in b)
+        bb = 0 if b is None else sum(x * x for x in b)
         if qq == 0 or bb == 0:
             keys.append(Fraction(0))
             continue

@@ -22,6 +22,10 @@ Readings (beyond those stated in the modules used here):
     and the softmax are unchanged.  For ConvKV the memory frames, window
     blocks and current block are the segments (the SoulX-LiveAct page runs
     its ConvKV attention in FP8, sections 关键信息速览 and 上手实践).
+  * An FP8 KV cache (dtype "bf16_fp8kv"): as the key cache, and V of each
+    segment quantised with the same tile rule, and P rounded to E4M3 against
+    the exact row max before P V (``fp8.attention_fp8_pv``; the same page's
+    上手实践 notes offer an FP8 KV cache).
   * PR-Sink with reference_frames = R > 0 (the LiveAnimate page, section 方法,
     conditions every block on the reference image; the Live Avatar page's
     abstract recalibrates appearance from a cached reference image): the R
@@ -80,7 +84,7 @@ class _Base:
         return apply_rope(xs, t, self.y_tok[tok], self.x_tok[tok], self.split, self.theta)
 
     def _attend(self, q_rot, ks, vs, heads, rows):
-        if self.cfg["dtype"] == "bf16_fp8k":
+        if self.cfg["dtype"] in ("bf16_fp8k", "bf16_fp8kv"):
             return self._attend_fp8(q_rot, ks, vs, rows)
         k = np.concatenate(ks, axis=0)
         v = np.concatenate([np.asarray(x, np.float64) for x in vs], axis=0)
@@ -88,17 +92,23 @@ class _Base:
         return o_sub
 
     def _attend_fp8(self, q_rot, ks, vs, rows):
-        """FP8 key cache: logits from E4M3 Q (in log2 units, one scale per row)
-        and E4M3 K (one scale per 64-token tile of each context segment);
-        quantising Q row by row lets the unrequested rows stay zero."""
+        """FP8 key (and value) cache: base-2 logits from E4M3 Q (one scale per
+        row) and E4M3 K (one scale per 64-token tile of each context segment);
+        quantising Q row by row lets the unrequested rows stay zero.  With the
+        FP8 KV cache, V is quantised per segment tile too and P rounded to
+        E4M3 against the exact row max."""
         log2e = 1.0 / np.log(2.0)
         s = _scale(self.cfg)
         rs = np.arange(self.T) if rows is None else np.asarray(rows)
-        qe = np.zeros_like(q_rot)
-        qe[rs] = fp8.quantize_queries(q_rot[rs] * (s * log2e)) / log2e
+        q2 = np.zeros_like(q_rot)
+        q2[rs] = fp8.quantize_queries(q_rot[rs] * (s * log2e))
         k = np.concatenate([fp8.quantize_keys(x) for x in ks], axis=0)
+        if self.cfg["dtype"] == "bf16_fp8kv":
+            v = np.concatenate([fp8.quantize_values(x) for x in vs], axis=0)
+            return fp8.attention_fp8_pv(q2, k, v, rows=rows)
         v = np.concatenate([np.asarray(x, np.float64) for x in vs], axis=0)
-        return attention(qe, k, v, 1.0, rows=rows)
+        # exp(q2 . k / log2 e) = 2^(q2 . k): the base-2 logits
+        return attention(q2 / log2e, k, v, 1.0, rows=rows)
 
 
 class PRSinkReference(_Base):

@@ -555,3 +555,64 @@ def check_fp8_pow2_invariance(Ref, cfgs, make_provider):
                 assert np.array_equal(x, y), (cfg["name"], a)
         plain = Ref(dict(cfg, dtype="bf16"), Scaled(0)).attend(cfg["blocks"] - 1, 0, 0)
         assert not np.array_equal(plain, outs[0][1])
+
+
+# ------------------------------------------------ FP8 attention, hand-worked
+def fp8_golden_cfg(dtype):
+    """The two-segment stream of golden/fp8_attend_two_segments.txt."""
+    from bounded_kv_block_amd import synth
+    return synth.workload("prsink_512", dtype=dtype, heads=1, head_dim=4, frames=1, grid_h=1, grid_w=1,
+                          window=1, static=1, dynamic_k=0, bank=0, pose_dim=0, rope=(0, 0, 0),
+                          softmax_scale=1.0, blocks=2, pose_kind="none")
+
+
+class Fp8GoldenProvider:
+    """Inputs of golden/fp8_attend_two_segments.txt, [1 token, 1 head, 4]."""
+    QKV = {0: ((0.0, 0.0, 0.0, 0.0), (0.0, 0.0, 40960.0, 0.0), (0.0, 1.09375, 0.0, 0.0)),
+           1: ((1.0, 0.0, 0.0, 0.0), (1.09375, 0.0, 0.0, 0.0), (1.0, 0.0, 0.0, 40960.0))}
+
+    def qkv(self, layer, block, step):
+        return tuple(np.array(x, np.float64).reshape(1, 1, 4) for x in self.QKV[block])
+
+    def pose(self, b):
+        return np.zeros(0, np.float32)
+
+
+def check_fp8_attend_golden(Ref):
+    """Block 1 of the hand-worked two-segment stream, for the plain bf16
+    reading, the FP8 key cache and the FP8 KV cache, equals the hand-derived
+    values to 1e-13 (relative)."""
+    rows = {r[0]: [float(x) for x in r[1:]] for r in read_table("fp8_attend_two_segments.txt")}
+    for dtype in ("bf16", "bf16_fp8k", "bf16_fp8kv"):
+        ref = Ref(fp8_golden_cfg(dtype), Fp8GoldenProvider())
+        got = ref.attend(1, 0, 0)[0, 0]
+        want = np.array(rows[dtype])
+        assert np.allclose(got, want, rtol=1e-13, atol=1e-13), (dtype, got, want)
+
+
+# ------------------------------------------------ token layout
+def check_token_positions(token_positions):
+    """(frame, y, x) of each token of a 2-frame 2x3 block against the hand table."""
+    rows = read_table("token_positions_f2_h2_w3.txt")
+    f, y, x = token_positions(2, 2, 3)
+    assert len(f) == len(rows)
+    for tok, ff, yy, xx in rows:
+        t = int(tok)
+        assert (int(f[t]), int(y[t]), int(x[t])) == (int(ff), int(yy), int(xx)), tok
+
+
+# ------------------------------------------------ bf16 rounding of the projection
+def check_bf16_round(bf16_round, rng):
+    """Nearest bf16, ties to even: hand values (ties at 1 + 2^-8 and 1 + 3*2^-8,
+    negative ties, a carry into the next binade, small and large magnitudes)
+    and torch's float32 -> bfloat16 conversion on random fp32 values (exact
+    in fp64, so no double rounding)."""
+    import torch
+    hand = [(1 + 2.0 ** -8, 1.0), (1 + 3 * 2.0 ** -8, 1 + 2.0 ** -6), (-(1 + 2.0 ** -8), -1.0),
+            (1 + 2.0 ** -8 + 2.0 ** -30, 1 + 2.0 ** -7), (2 - 2.0 ** -9, 2.0), (3.0 * 2.0 ** -100, 3.0 * 2.0 ** -100),
+            (1.0 + 2.0 ** -7, 1.0 + 2.0 ** -7), (0.0, 0.0), (255.5, 256.0), (-1000.1, -1000.0)]
+    for x, want in hand:
+        assert float(bf16_round(np.array([x]))[0]) == want, (x, want)
+    x = (rng.standard_normal(50000) * np.exp(rng.uniform(-20, 20, 50000))).astype(np.float32)
+    want = torch.from_numpy(x).to(torch.bfloat16).double().numpy()
+    assert np.array_equal(bf16_round(x.astype(np.float64)), want)

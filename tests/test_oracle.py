@@ -338,3 +338,50 @@ def test_projection_brute_force(rng):
 
 def test_projection_layout():
     pins.check_projection_layout(oracle.qkv_projection)
+
+
+def test_fp8_attend_hand_worked():
+    pins.check_fp8_attend_golden(oracle.PRSinkReference)
+
+
+def test_token_positions_hand_table():
+    pins.check_token_positions(oracle.token_positions)
+
+
+def test_projection_bf16_rounding(rng):
+    from oracle.projection import bf16_round
+    pins.check_bf16_round(bf16_round, rng)
+    # the projection's rounded form is the rounding of the fp64 projection
+    x, w, b = rng.standard_normal((5, 32)), rng.standard_normal((3 * 2 * 4, 32)), rng.standard_normal(24)
+    exact = oracle.qkv_projection(x, w, b, 2, 4)
+    rounded = oracle.qkv_projection(x, w, b, 2, 4, round_bf16=True)
+    for e, r in zip(exact, rounded):
+        assert np.array_equal(r, bf16_round(e)) and not np.array_equal(r, e)
+
+
+def test_fp8_readings_error_against_plain_attention():
+    """The accuracy cost of each FP8 reading itself (oracle against oracle, no
+    kernel involved): on a 512x512-shaped block (all 3072 queries, the full
+    21504-key context) of one head, the FP8 key cache and the FP8 KV cache
+    stay within the bf16 path's 2e-2 of the unquantised fp64 attention."""
+    cfg = synth.workload("prsink_512", heads=1, bank=4, pose_dim=16, keyframes=4, blocks=7)
+    prov = SynthProvider(cfg)
+    plain = oracle.PRSinkReference(cfg, prov).attend(6, 0, 0)
+    for dtype in ("bf16_fp8k", "bf16_fp8kv"):
+        got = oracle.PRSinkReference(dict(cfg, dtype=dtype), prov).attend(6, 0, 0)
+        err = float(np.max(np.abs(got - plain)))
+        print(f"{dtype}: max|fp8 reading - fp64 attention| = {err:.3e}")
+        assert 0 < err <= 2e-2, (dtype, err)
+
+
+def test_retrieval_non_finite_poses_score_zero():
+    # hand-derived: query e0; members 1: e0 (cos 1), 2: NaN pose (0), 3: -e0 (-1),
+    # 4: e1 (0), 5: Inf pose (0), 6: 0.5 e0 + 0.5 e1 (cos 1/sqrt 2)
+    e0, e1 = np.eye(4, dtype=np.float32)[:2]
+    nan = np.full(4, np.nan, np.float32)
+    inf = np.array([np.inf, 0, 0, 0], np.float32)
+    bank = [(1, e0), (2, nan), (3, -e0), (4, e1), (5, inf), (6, 0.5 * e0 + 0.5 * e1)]
+    assert oracle.retrieve(e0, bank, 6) == [1, 6, 2, 4, 5, 3]
+    # a non-finite query scores 0 against every member: ids ascending
+    assert oracle.retrieve(inf, bank, 4) == [1, 2, 3, 4]
+    assert oracle.retrieve(nan, bank, 2) == [1, 2]

@@ -450,3 +450,92 @@ def test_fp8_stream_mutant_fails():
     from conftest import SynthProvider
     cfg = synth.workload("convkv_512", dtype="bf16_fp8k", blocks=8, heads=2, frames=3, grid_h=2, grid_w=5)
     assert _fails(pins.check_fp8_pow2_invariance, _Fp8Unscaled, [cfg], SynthProvider)
+
+
+# -- FP8 attention mutants against the hand-worked two-segment stream -------------
+class _Fp8QNoLog2e(oracle.PRSinkReference):
+    """Q quantised without the log2 e factor (natural-unit logits)."""
+
+    def _attend_fp8(self, q_rot, ks, vs, rows):
+        s = self.cfg.get("softmax_scale", 0.0) or 1.0 / np.sqrt(self.cfg["head_dim"])
+        qe = oracle.fp8.quantize_queries(q_rot * s)
+        k = np.concatenate([oracle.fp8.quantize_keys(x) for x in ks], axis=0)
+        if self.cfg["dtype"] == "bf16_fp8kv":
+            v = np.concatenate([oracle.fp8.quantize_values(x) for x in vs], axis=0)
+            return oracle.fp8.attention_fp8_pv(qe * (1.0 / np.log(2.0)), k, v, rows=rows)
+        v = np.concatenate([np.asarray(x, np.float64) for x in vs], axis=0)
+        return oracle.attention(qe, k, v, 1.0, rows=rows)
+
+
+class _Fp8KTilesConcat(oracle.PRSinkReference):
+    """K tiles counted over the concatenated context, not per segment."""
+
+    def _attend_fp8(self, q_rot, ks, vs, rows):
+        return super()._attend_fp8(q_rot, [np.concatenate(ks, axis=0)], vs, rows)
+
+
+class _Fp8VTilesConcat(oracle.PRSinkReference):
+    """V tiles counted over the concatenated context, not per segment."""
+
+    def _attend_fp8(self, q_rot, ks, vs, rows):
+        return super()._attend_fp8(q_rot, ks, [np.concatenate(vs, axis=0)], rows)
+
+
+def _pv_p_unrounded(q, k, v, rows=None):
+    z = np.asarray(q, np.float64)[:, 0, :] @ np.asarray(k, np.float64)[:, 0, :].T
+    p = np.exp2(z - z.max(axis=1, keepdims=True))
+    return ((p @ np.asarray(v, np.float64)[:, 0, :]) / p.sum(axis=1, keepdims=True))[:, None, :]
+
+
+def _pv_rounded_denominator(q, k, v, rows=None):
+    z = np.asarray(q, np.float64)[:, 0, :] @ np.asarray(k, np.float64)[:, 0, :].T
+    p = oracle.fp8.e4m3_round(np.exp2(z - z.max(axis=1, keepdims=True)))
+    return ((p @ np.asarray(v, np.float64)[:, 0, :]) / p.sum(axis=1, keepdims=True))[:, None, :]
+
+
+@pytest.mark.parametrize("mutant", [_Fp8QNoLog2e, _Fp8KTilesConcat, _Fp8VTilesConcat])
+def test_fp8_attend_mutants_fail(mutant):
+    assert _fails(pins.check_fp8_attend_golden, mutant)
+
+
+@pytest.mark.parametrize("mutant", [_pv_p_unrounded, _pv_rounded_denominator])
+def test_fp8_pv_mutants_fail(mutant, monkeypatch):
+    monkeypatch.setattr(oracle.fp8, "attention_fp8_pv", mutant)
+    assert _fails(pins.check_fp8_attend_golden, oracle.PRSinkReference)
+
+
+# -- token layout mutants -----------------------------------------------------------
+def _tok_yx_swapped(frames, grid_h, grid_w):     # x taken as the slow axis
+    f, x, y = np.meshgrid(np.arange(frames), np.arange(grid_w), np.arange(grid_h), indexing="ij")
+    return f.reshape(-1), y.reshape(-1), x.reshape(-1)
+
+
+def _tok_frame_minor(frames, grid_h, grid_w):    # frames interleaved per position
+    y, x, f = np.meshgrid(np.arange(grid_h), np.arange(grid_w), np.arange(frames), indexing="ij")
+    return f.reshape(-1), y.reshape(-1), x.reshape(-1)
+
+
+@pytest.mark.parametrize("mutant", [_tok_yx_swapped, _tok_frame_minor])
+def test_token_position_mutants_fail(mutant):
+    assert _fails(pins.check_token_positions, mutant)
+
+
+# -- bf16 rounding mutants ------------------------------------------------------------
+def _bf16_half_away(x):
+    m, e = np.frexp(np.asarray(x, np.float64))
+    return np.ldexp(np.trunc(np.ldexp(m, 8) + np.copysign(0.5, m)), e - 8)
+
+
+def _bf16_truncate(x):
+    m, e = np.frexp(np.asarray(x, np.float64))
+    return np.ldexp(np.trunc(np.ldexp(m, 8)), e - 8)
+
+
+def _bf16_via_7_bits(x):                          # one significant bit short
+    m, e = np.frexp(np.asarray(x, np.float64))
+    return np.ldexp(np.round(np.ldexp(m, 7)), e - 7)
+
+
+@pytest.mark.parametrize("mutant", [_bf16_half_away, _bf16_truncate, _bf16_via_7_bits])
+def test_bf16_round_mutants_fail(mutant, rng):
+    assert _fails(pins.check_bf16_round, mutant, rng)
