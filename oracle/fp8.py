@@ -14,10 +14,12 @@ Reading taken here:
     softmax and P V are unchanged.
   * FP8 KV cache (``attention_fp8_pv``): V is stored as E4M3 with the key
     cache's tile rule (one power-of-two scale per head and 64-token tile of a
-    segment, over all channels), and P, taken against the exact row max so
-    that every P lies in (0, 1], is rounded to E4M3 at unit scale (P below
-    2^-10 becomes 0) before the P V product.  The denominator is the sum of
-    the unrounded P.
+    segment, over all channels), and the softmax numerator P is held as E4M3
+    with the same rule applied to each query row over its whole context: one
+    power-of-two scale per row, the smallest 2^e with max_j P_j * 2^-e <= 448.
+    Taking P = 2^(z - max z), the largest P is 1 and the scale is 2^-8, so
+    P~ = E4M3(256 P) / 256.  Any common factor of a row's P cancels in
+    o = sum_j P~_j v_j / sum_j P_j; the denominator sums the unrounded P.
 
 E4M3 (OCP "fn" variant): 1 sign bit, 4 exponent bits with bias 7, 3 mantissa
 bits, no infinities; the largest finite magnitude is 448 and subnormals are
@@ -96,11 +98,20 @@ def quantize_values(v) -> np.ndarray:
     return quantize_keys(v)
 
 
+def quantize_rows(p) -> np.ndarray:
+    """Dequantised E4M3 of p [N, Nk] with one power-of-two scale per row (the
+    tile rule of ``pow2_exponents`` over the row)."""
+    p = np.asarray(p, np.float64)
+    sc = np.ldexp(1.0, pow2_exponents(np.abs(p).max(axis=1)))[:, None]
+    return e4m3_round(p / sc) * sc
+
+
 def attention_fp8_pv(q, k, v, rows=None) -> np.ndarray:
     """o [Nq, H, D] for (already quantised) q and k and a quantised v, with
-    base-2 logits z = q . k: P = 2^(z - max_j z) rounded to E4M3 at unit
-    scale, o = sum_j P~_j v_j / sum_j P_j (the unrounded sum), fp64.
-    ``rows`` restricts the work to a subset of query rows (others zero)."""
+    base-2 logits z = q . k: P = 2^(z - max_j z) held as E4M3 with one
+    power-of-two scale per row, o = sum_j P~_j v_j / sum_j P_j (the unrounded
+    sum), fp64.  ``rows`` restricts the work to a subset of query rows
+    (others zero)."""
     q = np.asarray(q, np.float64)
     k = np.asarray(k, np.float64)
     v = np.asarray(v, np.float64)
@@ -112,5 +123,5 @@ def attention_fp8_pv(q, k, v, rows=None) -> np.ndarray:
             r = rs[c0:c0 + 256]
             z = q[r, h, :] @ k[:, h, :].T
             p = np.exp2(z - z.max(axis=1, keepdims=True))
-            out[r, h, :] = (e4m3_round(p) @ v[:, h, :]) / p.sum(axis=1, keepdims=True)
+            out[r, h, :] = (quantize_rows(p) @ v[:, h, :]) / p.sum(axis=1, keepdims=True)
     return out

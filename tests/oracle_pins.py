@@ -616,3 +616,20 @@ def check_bf16_round(bf16_round, rng):
     x = (rng.standard_normal(50000) * np.exp(rng.uniform(-20, 20, 50000))).astype(np.float32)
     want = torch.from_numpy(x).to(torch.bfloat16).double().numpy()
     assert np.array_equal(bf16_round(x.astype(np.float64)), want)
+
+
+def check_fp8_pv_row_scale(attention_fp8_pv):
+    """P of one query row with base-2 logits 0, -7.5, -12 against keys whose
+    values are the unit vectors: P = 1, 2^-7.5 = 0.0055243, 2^-12.  The row's
+    scale is 2^-8 (largest P = 1): 256 P = 256 (exact), 1.41421 (binade
+    [1, 2), quantum 1/8: 11.31 -> 11 -> 1.375), 2^-4 (exact, a normal
+    value).  So o = (1, 1.375/256, 0.0625/256) / (1 + 2^-7.5 + 2^-12).
+    (At unit scale 2^-7.5 would be a subnormal, 3 * 2^-9, and 2^-12 would
+    round to 0.)"""
+    q = np.ones((1, 1, 1))
+    k = np.array([0.0, -7.5, -12.0]).reshape(3, 1, 1)
+    v = np.eye(3).reshape(3, 1, 3)
+    l = 1.0 + 2.0 ** -7.5 + 2.0 ** -12
+    want = np.array([1.0, 1.375 / 256.0, 0.0625 / 256.0]) / l
+    got = attention_fp8_pv(q, k, v)[0, 0]
+    assert np.allclose(got, want, rtol=1e-14, atol=0), (got, want)

@@ -385,3 +385,7 @@ def test_retrieval_non_finite_poses_score_zero():
     # a non-finite query scores 0 against every member: ids ascending
     assert oracle.retrieve(inf, bank, 4) == [1, 2, 3, 4]
     assert oracle.retrieve(nan, bank, 2) == [1, 2]
+
+
+def test_fp8_pv_row_scale_hand_worked():
+    pins.check_fp8_pv_row_scale(oracle.fp8.attention_fp8_pv)

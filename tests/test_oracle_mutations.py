@@ -539,3 +539,21 @@ def _bf16_via_7_bits(x):                          # one significant bit short
 @pytest.mark.parametrize("mutant", [_bf16_half_away, _bf16_truncate, _bf16_via_7_bits])
 def test_bf16_round_mutants_fail(mutant, rng):
     assert _fails(pins.check_bf16_round, mutant, rng)
+
+
+def _pv_unit_scale(q, k, v, rows=None):
+    z = np.asarray(q, np.float64)[:, 0, :] @ np.asarray(k, np.float64)[:, 0, :].T
+    p = np.exp2(z - z.max(axis=1, keepdims=True))
+    return ((oracle.fp8.e4m3_round(p) @ np.asarray(v, np.float64)[:, 0, :]) / p.sum(axis=1, keepdims=True))[:, None, :]
+
+
+def _pv_scale_from_448(q, k, v, rows=None):      # the row max mapped onto 448 exactly (not a power of two)
+    z = np.asarray(q, np.float64)[:, 0, :] @ np.asarray(k, np.float64)[:, 0, :].T
+    p = np.exp2(z - z.max(axis=1, keepdims=True))
+    return ((oracle.fp8.e4m3_round(p * 448.0) / 448.0 @ np.asarray(v, np.float64)[:, 0, :])
+            / p.sum(axis=1, keepdims=True))[:, None, :]
+
+
+@pytest.mark.parametrize("mutant", [_pv_unit_scale, _pv_scale_from_448, _pv_p_unrounded, _pv_rounded_denominator])
+def test_fp8_pv_row_scale_mutants_fail(mutant):
+    assert _fails(pins.check_fp8_pv_row_scale, mutant)
