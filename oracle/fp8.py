@@ -14,12 +14,13 @@ Reading taken here:
     softmax and P V are unchanged.
   * FP8 KV cache (``attention_fp8_pv``): V is stored as E4M3 with the key
     cache's tile rule (one power-of-two scale per head and 64-token tile of a
-    segment, over all channels), and the softmax numerator P is held as E4M3
-    with the same rule applied to each query row over its whole context: one
-    power-of-two scale per row, the smallest 2^e with max_j P_j * 2^-e <= 448.
-    Taking P = 2^(z - max z), the largest P is 1 and the scale is 2^-8, so
-    P~ = E4M3(256 P) / 256.  Any common factor of a row's P cancels in
+    segment, over all channels), and the softmax numerator P_j = 2^(z_j) (z
+    the base-2 logit, so P_j = exp of the natural logit) is held as E4M3 with
+    the same rule applied to each query row over its whole context: one
+    power-of-two scale 2^e per row, the smallest with max_j P_j * 2^-e <= 448.
     o = sum_j P~_j v_j / sum_j P_j; the denominator sums the unrounded P.
+    (The codes are those of 2^(z_j - e): a whole-number shift of z, not a
+    shift by the row max itself, which would change every code.)
 
 E4M3 (OCP "fn" variant): 1 sign bit, 4 exponent bits with bias 7, 3 mantissa
 bits, no infinities; the largest finite magnitude is 448 and subnormals are
@@ -98,20 +99,24 @@ def quantize_values(v) -> np.ndarray:
     return quantize_keys(v)
 
 
-def quantize_rows(p) -> np.ndarray:
-    """Dequantised E4M3 of p [N, Nk] with one power-of-two scale per row (the
-    tile rule of ``pow2_exponents`` over the row)."""
-    p = np.asarray(p, np.float64)
-    sc = np.ldexp(1.0, pow2_exponents(np.abs(p).max(axis=1)))[:, None]
-    return e4m3_round(p / sc) * sc
+def numerators_e4m3(z):
+    """For base-2 logits z [N, Nk]: P = 2^z held as E4M3 with one
+    power-of-two scale 2^e per row (the tile rule of ``pow2_exponents`` on the
+    row's largest P = 2^max z).  Returns (P~ 2^-e, P 2^-e): the common factor
+    2^-e keeps both in range and cancels in a ratio."""
+    z = np.asarray(z, np.float64)
+    P = np.exp2(z)                                     # logits well inside fp64's exponent range
+    e = pow2_exponents(P.max(axis=1))[:, None]
+    p = np.ldexp(P, -e)                                # exact: a power-of-two scaling
+    return e4m3_round(p), p
 
 
 def attention_fp8_pv(q, k, v, rows=None) -> np.ndarray:
     """o [Nq, H, D] for (already quantised) q and k and a quantised v, with
-    base-2 logits z = q . k: P = 2^(z - max_j z) held as E4M3 with one
-    power-of-two scale per row, o = sum_j P~_j v_j / sum_j P_j (the unrounded
-    sum), fp64.  ``rows`` restricts the work to a subset of query rows
-    (others zero)."""
+    base-2 logits z = q . k: P = 2^z held as E4M3 with one power-of-two
+    scale per row (``numerators_e4m3``), o = sum_j P~_j v_j / sum_j P_j (the
+    unrounded sum), fp64.  ``rows`` restricts the work to a subset of query
+    rows (others zero)."""
     q = np.asarray(q, np.float64)
     k = np.asarray(k, np.float64)
     v = np.asarray(v, np.float64)
@@ -122,6 +127,6 @@ def attention_fp8_pv(q, k, v, rows=None) -> np.ndarray:
         for c0 in range(0, len(rs), 256):
             r = rs[c0:c0 + 256]
             z = q[r, h, :] @ k[:, h, :].T
-            p = np.exp2(z - z.max(axis=1, keepdims=True))
-            out[r, h, :] = (quantize_rows(p) @ v[:, h, :]) / p.sum(axis=1, keepdims=True)
+            pq, p = numerators_e4m3(z)
+            out[r, h, :] = (pq @ v[:, h, :]) / p.sum(axis=1, keepdims=True)
     return out

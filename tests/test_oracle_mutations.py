@@ -557,3 +557,17 @@ def _pv_scale_from_448(q, k, v, rows=None):      # the row max mapped onto 448 e
 @pytest.mark.parametrize("mutant", [_pv_unit_scale, _pv_scale_from_448, _pv_p_unrounded, _pv_rounded_denominator])
 def test_fp8_pv_row_scale_mutants_fail(mutant):
     assert _fails(pins.check_fp8_pv_row_scale, mutant)
+
+
+def _pv_max_normalised(q, k, v, rows=None):      # P taken against the row max, then the row scale
+    z = np.asarray(q, np.float64)[:, 0, :] @ np.asarray(k, np.float64)[:, 0, :].T
+    p = np.exp2(z - z.max(axis=1, keepdims=True))
+    sc = np.ldexp(1.0, oracle.fp8.pow2_exponents(p.max(axis=1)))[:, None]
+    pq = oracle.fp8.e4m3_round(p / sc) * sc
+    return ((pq @ np.asarray(v, np.float64)[:, 0, :]) / p.sum(axis=1, keepdims=True))[:, None, :]
+
+
+@pytest.mark.parametrize("mutant", [_pv_max_normalised, _pv_unit_scale, _pv_scale_from_448])
+def test_fp8_pv_reading_mutants_fail_the_golden(mutant, monkeypatch):
+    monkeypatch.setattr(oracle.fp8, "attention_fp8_pv", mutant)
+    assert _fails(pins.check_fp8_attend_golden, oracle.PRSinkReference)
