@@ -16,6 +16,10 @@ Readings (beyond those stated in the modules used here):
     three steps), a committed block contributes the K/V of its last step.
   * ConvKV context order is [memory frames, window blocks oldest first,
     current block]; temporal positions run 0, 1, 2, ... over those frames.
+  * The ConvKV memory frame is cached like every other K and V, in the
+    cache's element type: a bf16 cache (dtypes "bf16", "bf16_fp8k",
+    "bf16_fp8kv") holds the conv output rounded to bf16 (nearest, ties to
+    even); the FP8 caches quantise that held value.
   * An FP8 key cache (dtype "bf16_fp8k", either policy): the rotated K of
     each context segment and Q are quantised to E4M3 as ``fp8`` states (K in
     64-token tiles counted from the segment's first token) before Q K^T; V
@@ -52,6 +56,7 @@ import numpy as np
 from . import fp8
 from .attention import attention
 from .convkv import conv_memory
+from .projection import bf16_round
 from .retrieval import retrieve
 from .rope import apply_rope
 from .schedule import convkv_schedule, iter_prsink_pose_bank, prsink_schedule, token_positions
@@ -215,7 +220,7 @@ class ConvKVReference(_Base):
         return (np.asarray(k, np.float64)[sl][:, heads, :], np.asarray(v, np.float64)[sl][:, heads, :])
 
     def memory(self, m: int, layer: int, heads):
-        """Raw memory K and V, each [n_mem, Tf, len(heads), D] fp64."""
+        """Raw memory K and V as cached, each [n_mem, Tf, len(heads), D] fp64."""
         sch = self.schedule(m)
         if not sch["memory"]:
             return None, None
@@ -230,7 +235,10 @@ class ConvKVReference(_Base):
             fv = np.stack(fv).transpose(0, 2, 1, 3)
             mk.append(conv_memory(fk, wk)[0].transpose(1, 0, 2))
             mv.append(conv_memory(fv, wv)[0].transpose(1, 0, 2))
-        return np.stack(mk), np.stack(mv)
+        mk, mv = np.stack(mk), np.stack(mv)
+        if self.cfg["dtype"] != "f32":          # held in the cache's bf16
+            mk, mv = bf16_round(mk), bf16_round(mv)
+        return mk, mv
 
     def context_kv(self, m: int, layer: int, step: int, heads):
         """Rotated K and raw V of every context segment (memory frames: Tf tokens)."""

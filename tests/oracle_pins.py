@@ -633,3 +633,28 @@ def check_fp8_pv_row_scale(attention_fp8_pv):
     want = np.array([1.0, 1.375 / 256.0, 0.0625 / 256.0]) / l
     got = attention_fp8_pv(q, k, v)[0, 0]
     assert np.allclose(got, want, rtol=1e-14, atol=0), (got, want)
+
+
+def check_convkv_memory_cached_dtype(Ref, conv_memory, bf16_round, make_cfg, make_provider):
+    """The ConvKV memory frame as the cache holds it: for a bf16 cache, the
+    exact conv output (``conv_memory`` of the evicted raw frames, assembled
+    here by hand from the provider) rounded to bf16 -- values that bf16
+    represents and that differ from the exact output; for the fp32 cache, the
+    exact output itself."""
+    for dtype in ("bf16", "f32"):
+        cfg = make_cfg(dtype)
+        prov = make_provider(cfg)
+        ref = Ref(cfg, prov)
+        m = cfg["blocks"] - 1
+        mk, mv = ref.memory(m, 0, [0, 1])
+        F, Tf = cfg["frames"], cfg["grid_h"] * cfg["grid_w"]
+        frames = ref.schedule(m)["memory"][0]
+        wk, wv = (np.asarray(w, np.float64)[[0, 1]] for w in prov.conv_weights(0))
+        fk = np.stack([np.asarray(prov.qkv(0, e // F, cfg["steps"] - 1)[1], np.float64)[(e % F) * Tf:(e % F + 1) * Tf][:, [0, 1]]
+                       for e in frames]).transpose(0, 2, 1, 3)
+        exact = conv_memory(fk, wk)[0].transpose(1, 0, 2)
+        if dtype == "bf16":
+            assert np.array_equal(mk[0], bf16_round(exact)) and not np.array_equal(mk[0], exact)
+            assert np.array_equal(bf16_round(mv[0]), mv[0])
+        else:
+            assert np.array_equal(mk[0], exact)

@@ -214,21 +214,6 @@ def _check_stored_keys(run, kv, layer=0):
     return n_total, n_tie
 
 
-def _bf16_memory_kv(cfg, ref, m, heads):
-    """The oracle's context K/V with the memory frames' raw K rounded to bf16
-    before rotation, as the library stores the conv memory (fp32 sums, bf16
-    store)."""
-    import torch
-    kv = ref.context_kv(m, 0, 0, heads)
-    mk, _ = ref.memory(m, 0, heads)
-    f, y, x = oracle.token_positions(1, cfg["grid_h"], cfg["grid_w"])
-    for j in range(len(ref.schedule(m)["memory"])):
-        kb = torch.from_numpy(mk[j]).to(torch.bfloat16).double().numpy()
-        kr = oracle.apply_rope(kb, np.full(f.size, float(j)), y, x, cfg["rope"], cfg.get("theta", 10000.0))
-        kv[j] = (kv[j][0], kv[j][1], kr, kv[j][3])
-    return kv
-
-
 def _convkv_stream(cfg, check=None, heads=None, rows=None, host_inputs=True, keys=False):
     run = Run(cfg, host_inputs)
     ref = oracle.ConvKVReference(cfg, run)
@@ -242,7 +227,7 @@ def _convkv_stream(cfg, check=None, heads=None, rows=None, host_inputs=True, key
             print(f"block {m}: max|err| {err:.3e}", flush=True)
             assert err <= TOL["bf16_fp8k"], (m, err)
         if keys:
-            a, b = _check_stored_keys(run, _bf16_memory_kv(cfg, ref, m, list(range(cfg["heads"]))))
+            a, b = _check_stored_keys(run, ref.context_kv(m, 0, 0, list(range(cfg["heads"]))))
             n_total += a
             n_tie += b
         run.cache.commit()

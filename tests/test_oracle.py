@@ -389,3 +389,12 @@ def test_retrieval_non_finite_poses_score_zero():
 
 def test_fp8_pv_row_scale_hand_worked():
     pins.check_fp8_pv_row_scale(oracle.fp8.attention_fp8_pv)
+
+
+def test_convkv_memory_is_held_in_the_cache_dtype():
+    from oracle.projection import bf16_round
+    pins.check_convkv_memory_cached_dtype(
+        oracle.ConvKVReference, oracle.conv_memory, bf16_round,
+        lambda dt: synth.workload("convkv_512", dtype=dt, heads=2, grid_h=2, grid_w=3, blocks=7,
+                                  rope=(0, 0, 0) if dt == "f32" else (44, 42, 42)),
+        SynthProvider)

@@ -571,3 +571,25 @@ def _pv_max_normalised(q, k, v, rows=None):      # P taken against the row max, 
 def test_fp8_pv_reading_mutants_fail_the_golden(mutant, monkeypatch):
     monkeypatch.setattr(oracle.fp8, "attention_fp8_pv", mutant)
     assert _fails(pins.check_fp8_attend_golden, oracle.PRSinkReference)
+
+
+class _MemoryUnrounded(oracle.ConvKVReference):
+    """The conv memory kept exact (fp64) whatever the cache's element type."""
+
+    def memory(self, m, layer, heads):
+        cfg = self.cfg
+        self.cfg = dict(cfg, dtype="f32")
+        try:
+            return super().memory(m, layer, heads)
+        finally:
+            self.cfg = cfg
+
+
+def test_convkv_memory_dtype_mutant_fails():
+    from oracle.projection import bf16_round
+    from bounded_kv_block_amd import synth
+    from conftest import SynthProvider
+    assert _fails(pins.check_convkv_memory_cached_dtype, _MemoryUnrounded, oracle.conv_memory, bf16_round,
+                  lambda dt: synth.workload("convkv_512", dtype=dt, heads=2, grid_h=2, grid_w=3, blocks=7,
+                                            rope=(0, 0, 0) if dt == "f32" else (44, 42, 42)),
+                  SynthProvider)
