@@ -12,6 +12,13 @@ TFLOP/s and % of the bf16 MFMA peak, per-kernel event timings, the roofline
 of the dominant kernel, per-block latency percentiles and the CPU oracle
 timed on a bounded sample of the same workload.
 
+The default workload is the 720x416-shaped stream (3510 queries per block,
+24570 keys of context, 40 layers x 3 sampling steps per block): one step is
+one block of 120 attends.  `--workload prsink_long` runs its whole 1080-block
+stream (unless --steps is given) and reports the per-block latency
+distribution over it: p50, p99, the least-squares slope over block index and
+whether the workspace and torch's device allocation stayed constant.
+
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
 """
 import argparse
@@ -34,12 +41,14 @@ PEAK_HBM_GBS = 8000.0          # MI355X HBM3E
 def parse():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=40)
+    ap.add_argument("--steps", type=int, default=None,
+                    help="timed blocks (default 20; prsink_long: the rest of its 1080-block stream)")
     ap.add_argument("--warmup", type=int, default=5)
-    ap.add_argument("--workload", default="prsink_512",
-                    choices=["prsink_512", "prsink_512_fp8k", "prsink_512_qkv", "prsink_512_ref", "prsink_512_rel", "prsink_512_posebank", "prsink_512_qkv_fp8k",
-                             "prsink_720x416",
-                             "prsink_long", "convkv_512", "convkv_512_abs", "convkv_512_fp8k", "tiny_fp32"])
+    ap.add_argument("--workload", default="prsink_720x416",
+                    choices=["prsink_512", "prsink_512_fp8k", "prsink_512_fp8kv", "prsink_512_qkv", "prsink_512_ref",
+                             "prsink_512_rel", "prsink_512_posebank", "prsink_512_qkv_fp8k", "prsink_720x416",
+                             "prsink_720x416_fp8kv", "prsink_long", "convkv_512", "convkv_512_abs", "convkv_512_fp8k",
+                             "convkv_512_fp8kv", "tiny_fp32"])
     ap.add_argument("--pool", type=int, default=4, help="distinct resident input blocks cycled through")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=12.0, help="target CPU-oracle sample time")
@@ -133,7 +142,7 @@ def cpu_baseline(cfg, run_inputs, poses, m, target_s, weights=None):
                 h = self.head
                 x = self.hidden(layer, block, step)
                 rows = np.concatenate([np.arange(i * H * D + h * D, i * H * D + (h + 1) * D) for i in range(3)])
-                parts = oracle.qkv_projection(x, self.w[rows], self.b[rows], 1, D)
+                parts = oracle.qkv_projection(x, self.w[rows], self.b[rows], 1, D, round_bf16=True)
                 out = []
                 for part in parts:
                     a = np.zeros((x.shape[0], H, D))
@@ -187,17 +196,58 @@ def cpu_baseline(cfg, run_inputs, poses, m, target_s, weights=None):
             break
     dt = time.perf_counter() - t0
     T = cfg["frames"] * cfg["grid_h"] * cfg["grid_w"]
+    attends = cfg["layers"] * cfg["steps"]
     try:
         from threadpoolctl import threadpool_info
         blas = max([p.get("num_threads", 1) for p in threadpool_info()] or [1])
     except Exception:
         blas = 1
-    return {"value": T * done / H / dt, "unit": "query tokens/s", "cores": int(blas),
-            "host_cpus": len(os.sched_getaffinity(0)), "kind": "oracle",
-            "sample": f"block {m} of the {cfg['name']} stream: retrieval + "
-                      f"{'fp64 QKV projection + ' if weights is not None else ''}fp64 attention of {done}/{H} heads "
-                      f"x all {T} queries over the block's bounded context, "
-                      f"{dt:.1f} s; value scaled to the whole block (x{H}/{done})"}
+    res = {"value": T * done / H / dt / attends, "unit": "query tokens/s", "cores": int(blas),
+           "host_cpus": len(os.sched_getaffinity(0)), "kind": "oracle",
+           "sample": f"block {m} of the {cfg['name']} stream, layer 0, step 0: retrieval + "
+                     f"{'fp64 QKV projection + ' if weights is not None else ''}fp64 attention of {done}/{H} heads "
+                     f"x all {T} queries over the block's bounded context, "
+                     f"{dt:.1f} s; value scaled to the whole block (x{H}/{done} heads"
+                     f"{f', x{attends} attends per block' if attends > 1 else ''})"}
+    res["fp32_numpy"] = cpu_fp32(cfg, ref, m, sel, target_s / 2, attends)
+    return res
+
+
+def cpu_fp32(cfg, ref, m, sel, target_s, attends):
+    """CPU throughput line: the attention step (softmax(scale q k^T) v per
+    head over the block's bounded context, the O(T * N_k * D) part of the
+    path) as plain fp32 numpy matrix products, on the same block's rotated
+    q, k and v (rotation and retrieval done beforehand, untimed)."""
+    import numpy as np
+    H, D = cfg["heads"], cfg["head_dim"]
+    s = cfg.get("softmax_scale", 0.0) or 1.0 / np.sqrt(D)
+    done, dt = 0, 0.0
+    while done < H and dt < target_s:
+        heads = [done]
+        ref.p.head = done                  # the fused workload's provider projects this head
+        if cfg["mode"] == "convkv":
+            kv = ref.context_kv(m, 0, 0, heads)
+            t0 = ref.positions(m)[1]
+        else:
+            kv = ref.context_kv(m, 0, 0, heads, sel)
+            t0 = ref.context(m, sel)[-1][3]
+        q, _, _ = ref.p.qkv(0, m, 0)
+        q = ref._rot(q, lambda f: t0 + f, heads)[:, 0, :].astype(np.float32)
+        k = np.concatenate([x[2][:, 0, :] for x in kv]).astype(np.float32)
+        v = np.concatenate([x[3][:, 0, :] for x in kv]).astype(np.float32)
+        c0 = time.perf_counter()
+        for r in range(0, q.shape[0], 256):
+            z = (q[r:r + 256] @ k.T) * np.float32(s)
+            z -= z.max(axis=1, keepdims=True)
+            np.exp(z, out=z)
+            z /= z.sum(axis=1, keepdims=True)
+            _ = z @ v
+        dt += time.perf_counter() - c0
+        done += 1
+    T = q.shape[0]
+    return {"value": T * done / H / dt / attends, "unit": "query tokens/s",
+            "sample": f"{done}/{H} heads of the same block, fp32 numpy, {dt:.1f} s; "
+                      f"value scaled to the whole block"}
 
 
 def main():
@@ -219,6 +269,9 @@ def main():
     from bounded_kv_block_amd import bkv, synth
 
     cfg = synth.workload(args.workload)
+    long_stream = args.workload == "prsink_long"
+    if args.steps is None:
+        args.steps = cfg["blocks"] - steady_block(cfg) - args.warmup if long_stream else 20
     dev = torch.device("cuda", 0)
     torch.cuda.set_device(dev)
     T = synth.tokens_per_block(cfg)
@@ -274,6 +327,8 @@ def main():
         step(m)
         m += 1
     torch.cuda.synchronize()
+    alloc0 = torch.cuda.memory_allocated(dev)
+    ws_bytes = set()
     n_keys = []
     launches = args.steps * (3 + 2 * L * S + L) + 16
     cache.profile_start(launches)
@@ -283,7 +338,9 @@ def main():
     for i in range(args.steps):
         ev[i].record()
         cache.retrieve(poses[m] if poses is not None else None)
-        n_keys.append(cache.stats()["n_keys"])
+        st = cache.stats()
+        n_keys.append(st["n_keys"])
+        ws_bytes.add(int(st["workspace_bytes"]))
         for s in range(S):
             for l in range(L):
                 attend(l, m, s)
@@ -293,23 +350,31 @@ def main():
     torch.cuda.synchronize()
     t1 = time.perf_counter()
     kt = cache.profile_stop()
+    alloc1 = torch.cuda.memory_allocated(dev)
     wall = t1 - t0
     per_block = np.array([ev[i].elapsed_time(ev[i + 1]) for i in range(args.steps)])
+    # least-squares slope of the per-block latency over the block index
+    xb = np.arange(args.steps, dtype=np.float64)
+    slope = float(np.polyfit(xb, per_block, 1)[0]) if args.steps > 1 else 0.0
 
     bf16 = cfg["dtype"] != "f32"
-    fp8k = cfg["dtype"] == "bf16_fp8k"
+    fp8k = cfg["dtype"] in ("bf16_fp8k", "bf16_fp8kv")
+    fp8v = cfg["dtype"] == "bf16_fp8kv"
     Nk = int(np.median(n_keys))
     flop_attend = 4.0 * H * T * Nk * D
     attn_n, attn_ms, _ = kt["attention"]
     attn_avg_ms = attn_ms / attn_n
     attn_tflops = flop_attend / (attn_avg_ms * 1e-3) / 1e12
     peak = PEAK_BF16_TFLOPS if bf16 else PEAK_FP32_TFLOPS
-    if fp8k:
+    if fp8v:
+        peak = PEAK_FP8_TFLOPS                              # both products on fp8 MFMA
+    elif fp8k:
         # half the flops (Q K^T) on fp8 MFMA, half (P V) on bf16: the peak of
         # that mix is the harmonic mean of the two
         peak = 1.0 / (0.5 / PEAK_FP8_TFLOPS + 0.5 / PEAK_BF16_TFLOPS)
     esz = 2 if bf16 else 4
     kesz = 1 if fp8k else esz                               # bytes per cached K value
+    vesz = 1 if fp8v else esz                               # bytes per cached V value
     kernels = {}
     for name, (n, tot, mx) in kt.items():
         kernels[name] = {"launches": int(n), "avg_us": 1e3 * tot / n, "max_us": 1e3 * mx}
@@ -317,7 +382,8 @@ def main():
     # K, V read token-major; rotated K and V^T written (a context gathered per
     # block -- ConvKV, relative positions -- also keeps the raw K in the slot)
     ctx_mode = cfg["mode"] == "convkv" or cfg.get("positions") == "relative"
-    app_bytes = 2.0 * T * H * D * esz + T * H * D * (kesz + esz) + (T * H * D * esz if ctx_mode else 0)
+    app_bytes = (2.0 * T * H * D * esz + T * H * D * (kesz + vesz) + (T * H * D * esz if ctx_mode else 0)
+                 + (T * H * D * esz if fp8v and cfg["mode"] == "convkv" else 0))
     if "append" in kernels:
         kernels["append"]["gbs"] = app_bytes / (kernels["append"]["avg_us"] * 1e-6) / 1e9
     if "qkv" in kernels:
@@ -337,7 +403,7 @@ def main():
     attends_per_step = L * S
     # algorithmic bytes of one attention launch: Q and the output once, K and V
     # of the whole bounded context once
-    attn_bytes = 2.0 * T * H * D * esz + Nk * H * D * (kesz + esz)
+    attn_bytes = 2.0 * T * H * D * esz + Nk * H * D * (kesz + vesz)
     value = args.steps * T / wall
     res = {
         "metric": METRIC,
@@ -350,7 +416,8 @@ def main():
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": ("fp8_e4m3 QK^T + bf16 PV" if fp8k else "bf16") if bf16 else "f32",
+        "dtype": (("fp8_e4m3 QK^T + fp8_e4m3 PV" if fp8v else "fp8_e4m3 QK^T + bf16 PV") if fp8k else "bf16")
+                 if bf16 else "f32",
         "data": "synthetic",
         "config": {"workload": cfg["name"], "mode": cfg["mode"], "heads": H, "head_dim": D,
                    "queries_per_block": T, "keys_per_block": Nk, "layers": L, "steps_per_block": S,
@@ -366,7 +433,12 @@ def main():
         "attention_peak_tflops": peak,
         "step_tflops": flop_attend * attends_per_step * args.steps / wall / 1e12,
         "latency_ms": {"p50": float(np.percentile(per_block, 50)), "p99": float(np.percentile(per_block, 99)),
-                       "max": float(per_block.max())},
+                       "max": float(per_block.max()), "blocks": int(args.steps),
+                       "slope_ms_per_1000_blocks": 1000.0 * slope,
+                       "slope_pct_of_p50_per_1000_blocks": 100.0 * 1000.0 * slope / float(np.percentile(per_block, 50))},
+        "memory": {"workspace_bytes_constant": len(ws_bytes) == 1,
+                   "torch_allocated_constant": alloc0 == alloc1,
+                   "torch_allocated_bytes": int(alloc1)},
         "kernels": kernels,
         "roofline": {"kernel": "attention", "bound": "mfma" if bf16 else "alu", "achieved": attn_tflops,
                      "peak": peak, "unit": "TFLOP/s", "frac": attn_tflops / peak, "traffic": measured_traffic(cfg["name"]),

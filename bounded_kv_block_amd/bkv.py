@@ -15,8 +15,8 @@ LIB_PATH = os.path.join(HERE, "libbkv.so")
 
 BKV_OK, BKV_ERR_ARG, BKV_ERR_STATE, BKV_ERR_WORKSPACE, BKV_ERR_DEVICE, BKV_ERR_UNSUPPORTED = range(6)
 PR_SINK, CONVKV = 0, 1
-F32, BF16, BF16_FP8K = 0, 1, 2
-DTYPES = {"f32": F32, "bf16": BF16, "bf16_fp8k": BF16_FP8K}
+F32, BF16, BF16_FP8K, BF16_FP8KV = 0, 1, 2, 3
+DTYPES = {"f32": F32, "bf16": BF16, "bf16_fp8k": BF16_FP8K, "bf16_fp8kv": BF16_FP8KV}
 POSITIONS = {"default": 0, "relative": 1, "absolute": 2}     # bkv_positions
 BANK_POLICIES = {"fifo": 0, "pose": 1}                        # bkv_bank_policy
 SEG_KINDS = {0: "static", 1: "dynamic", 2: "window", 3: "current", 4: "memory", 5: "reference"}
@@ -25,7 +25,8 @@ SEG_KINDS = {0: "static", 1: "dynamic", 2: "window", 3: "current", 4: "memory", 
 EXPORTS = ("bkv_workspace_size", "bkv_create", "bkv_destroy", "bkv_reset", "bkv_set_conv_weights",
            "bkv_set_reference",
            "bkv_profile_start", "bkv_profile_stop",
-           "bkv_retrieve", "bkv_attend", "bkv_attend_qkv", "bkv_commit", "bkv_selection", "bkv_context", "bkv_stats",
+           "bkv_retrieve", "bkv_attend", "bkv_attend_qkv", "bkv_commit", "bkv_selection",
+           "bkv_context", "bkv_stats",
            "bkv_export_segment", "bkv_status_str", "bkv_last_error", "bkv_probe_mfma")
 
 

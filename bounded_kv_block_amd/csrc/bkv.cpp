@@ -35,6 +35,12 @@ bkv_status fail(bkv_status s, const char* fmt, ...) {
 
 size_t align_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
 
+// Pose-aware bank replacement (decided on the device): spare slots that let
+// blocks open while displaced members are still being read back, and the
+// ring of readbacks in flight.
+constexpr int kPoseSpare = 2;
+constexpr int kPoseRing = 4;
+
 struct Layout {
   int T, Tpad, Tf, tf_pad, esize;
   int n_slots, ctx_ld, mem_ld;
@@ -53,6 +59,11 @@ struct Layout {
   size_t off_q;                      // bf16: q scratch [T][H][D] of the fused projection path
   int ref_tok, ref_pad;              // reference frames: tokens, padded to whole key tiles
   size_t ref_bytes, ref_v_off, ref_kx_off, off_ref, off_tref;   // per layer, slot-shaped
+  bool vf8;                          // FP8 KV cache: attention reads E4M3 V^T with tile exponents
+  size_t slot_v8_off, slot_vx_off;   //   inside a slot: E4M3 V^T [H][D][Tpad], exponents [H][Tpad/64]
+                                     //   (ConvKV also keeps the raw bf16 V^T at slot_v_off for the conv)
+  size_t ref_vx_off;                 //   reference region: E4M3 V^T at ref_v_off, exponents here
+  size_t mem_v8_off, mem_vx_off;     //   ConvKV memory: E4M3 V^T [H][D][mem_ld], exponents [H][mem_ld/64]
 };
 
 bkv_status validate(const bkv_config* c) {
@@ -60,7 +71,7 @@ bkv_status validate(const bkv_config* c) {
   if (c->struct_size != sizeof(bkv_config))
     return fail(BKV_ERR_ARG, "config struct_size %u != %zu", c->struct_size, sizeof(bkv_config));
   if (c->mode != BKV_PR_SINK && c->mode != BKV_CONVKV) return fail(BKV_ERR_ARG, "bad mode %d", c->mode);
-  if (c->dtype != BKV_F32 && c->dtype != BKV_BF16 && c->dtype != BKV_BF16_FP8K)
+  if (c->dtype != BKV_F32 && c->dtype != BKV_BF16 && c->dtype != BKV_BF16_FP8K && c->dtype != BKV_BF16_FP8KV)
     return fail(BKV_ERR_ARG, "bad dtype %d", c->dtype);
   if (c->layers < 1 || c->heads < 1) return fail(BKV_ERR_ARG, "layers and heads must be >= 1");
   if (c->rope_positions != BKV_POS_DEFAULT && c->rope_positions != BKV_POS_CONTEXT &&
@@ -125,6 +136,7 @@ bkv::Schedule::Shape shape_of(const bkv_config* c) {
   s.memory_frames = s.convkv ? c->memory_frames : 0;
   s.ref_frames = s.convkv ? 0 : c->reference_frames;
   s.relative = !s.convkv && c->rope_positions == BKV_POS_CONTEXT;
+  s.spare = (!s.convkv && c->bank_policy == BKV_BANK_POSE) ? kPoseSpare : 0;
   return s;
 }
 
@@ -132,18 +144,32 @@ Layout layout_of(const bkv_config* c, const bkv::Schedule& sch) {
   Layout L{};
   const size_t H = c->heads, D = c->head_dim;
   L.esize = c->dtype == BKV_F32 ? 4 : 2;
-  L.kf8 = c->dtype == BKV_BF16_FP8K;
+  L.kf8 = c->dtype == BKV_BF16_FP8K || c->dtype == BKV_BF16_FP8KV;
+  L.vf8 = c->dtype == BKV_BF16_FP8KV;
   L.slot8 = L.kf8 && !sch.ctx_mode();
+  const size_t vx_bytes = sizeof(int) * H * (align_up(sch.tokens(), bkv::kTokAlign) / bkv::kTokAlign);
   L.T = sch.tokens();
   L.Tpad = (int)align_up(L.T, bkv::kTokAlign);
   L.Tf = c->grid_h * c->grid_w;
   L.tf_pad = (int)align_up(L.Tf, bkv::kTokAlign);
   L.n_slots = sch.n_slots();
-  if (L.slot8) {
+  if (L.slot8 && L.vf8) {
+    // [E4M3 K rows H x Tpad x D][K exponents H x Tpad/64][E4M3 V^T H x D x Tpad][V exponents]
+    L.slot_kx_off = H * L.Tpad * D;
+    L.slot_v_off = L.slot_v8_off = align_up(L.slot_kx_off + vx_bytes, 256);
+    L.slot_vx_off = L.slot_v8_off + H * L.Tpad * D;
+    L.slot_bytes = align_up(L.slot_vx_off + vx_bytes, 256);
+  } else if (L.slot8) {
     // [E4M3 K rows H x Tpad x D][int32 exponents H x Tpad/64][bf16 V^T H x D x Tpad]
     L.slot_kx_off = H * L.Tpad * D;
-    L.slot_v_off = align_up(L.slot_kx_off + sizeof(int) * H * (L.Tpad / bkv::kTokAlign), 256);
+    L.slot_v_off = align_up(L.slot_kx_off + vx_bytes, 256);
     L.slot_bytes = L.slot_v_off + H * L.Tpad * D * 2;
+  } else if (L.vf8) {
+    // context modes: [raw bf16 K][raw bf16 V^T, ConvKV only (the conv reads it)][E4M3 V^T][V exponents]
+    L.slot_v_off = H * L.Tpad * D * 2;
+    L.slot_v8_off = L.slot_v_off + (c->mode == BKV_CONVKV ? H * L.Tpad * D * 2 : 0);
+    L.slot_vx_off = L.slot_v8_off + H * L.Tpad * D;
+    L.slot_bytes = align_up(L.slot_vx_off + vx_bytes, 256);
   } else {
     L.slot_v_off = H * L.Tpad * D * L.esize;
     L.slot_bytes = 2 * L.slot_v_off;
@@ -155,7 +181,8 @@ Layout layout_of(const bkv_config* c, const bkv::Schedule& sch) {
   if (L.kf8) {
     L.ref_kx_off = H * L.ref_pad * D;
     L.ref_v_off = align_up(L.ref_kx_off + sizeof(int) * H * (L.ref_pad / bkv::kTokAlign), 256);
-    L.ref_bytes = align_up(L.ref_v_off + H * L.ref_pad * D * 2, 256);
+    L.ref_vx_off = L.ref_v_off + H * L.ref_pad * D * (L.vf8 ? 1 : 2);
+    L.ref_bytes = align_up(L.ref_vx_off + (L.vf8 ? sizeof(int) * H * (L.ref_pad / bkv::kTokAlign) : 0), 256);
   } else {
     L.ref_v_off = align_up(H * L.ref_pad * D * L.esize, 256);
     L.ref_bytes = align_up(L.ref_v_off + H * L.ref_pad * D * L.esize, 256);
@@ -179,7 +206,10 @@ Layout layout_of(const bkv_config* c, const bkv::Schedule& sch) {
   if (c->mode == BKV_CONVKV) {
     L.mem_ld = L.tf_pad * c->memory_frames;
     L.mem_v_off = H * L.mem_ld * D * L.esize;
-    L.mem_layer_bytes = align_up(2 * L.mem_v_off, 256);
+    L.mem_v8_off = align_up(2 * L.mem_v_off, 256);
+    L.mem_vx_off = L.mem_v8_off + H * L.mem_ld * D;
+    L.mem_layer_bytes = align_up(L.vf8 ? L.mem_vx_off + sizeof(int) * H * (L.mem_ld / bkv::kTokAlign)
+                                       : 2 * L.mem_v_off, 256);
     off = align_up(off + L.mem_layer_bytes * c->layers, 256);
   }
   L.off_pose = off;
@@ -187,8 +217,10 @@ Layout layout_of(const bkv_config* c, const bkv::Schedule& sch) {
   off = align_up(off + sizeof(float) * (size_t)L.n_slots * (P > 0 ? P : 1), 256);
   L.off_sel = off;
   off = align_up(off + 2 * sizeof(int) * bkv::kMaxK, 256);
-  L.off_victim = off;                // pose-aware replacement: displaced id and slot
-  if (c->mode == BKV_PR_SINK && c->bank_policy == BKV_BANK_POSE) off = align_up(off + 2 * sizeof(int), 256);
+  L.off_victim = off;                // pose-aware replacement: the bank table [ids | slots]
+                                     // (kMaxBank each), then kPoseRing (id, slot) readbacks
+  if (c->mode == BKV_PR_SINK && c->bank_policy == BKV_BANK_POSE)
+    off = align_up(off + sizeof(int) * (2 * bkv::kMaxBank + 2 * kPoseRing), 256);
   L.t_rows = sch.ctx_mode() ? sch.max_context_frames() : c->frames_per_block;
   L.off_tt = off;
   off = align_up(off + sizeof(float2) * (size_t)L.t_rows * (c->rope_t / 2 + 1), 256);
@@ -223,6 +255,13 @@ struct bkv_cache_s {
   std::vector<bool> weights_set;    // ConvKV: conv weights given per layer
   std::vector<bool> ref_set;        // PR-Sink: reference frames given per layer
   int64_t split_attends = 0;        // bf16 attention launches that used the split launch
+  // pose-aware bank: displaced (id, slot) pairs read back into pinned host
+  // memory, each with an event recorded after its copy; ring positions in
+  // flight, oldest first
+  int* victim_host = nullptr;
+  hipEvent_t victim_ev[kPoseRing] = {};
+  std::vector<int> victim_pending;
+  int victim_next = 0;
   struct Prof {                     // per-launch HIP event pairs (bkv_profile_start/stop)
     bool on = false;
     int cap = 0, used = 0;
@@ -251,6 +290,11 @@ struct bkv_cache_s {
   char* layer_kv(int l) const { return ws + L.off_kv + L.layer_kv_bytes * l; }
   char* slot_k(int l, int s) const { return layer_kv(l) + L.slot_bytes * s; }
   char* slot_vt(int l, int s) const { return slot_k(l, s) + L.slot_v_off; }
+  bool vf8() const { return L.vf8; }
+  char* slot_v8(int l, int s) const { return slot_k(l, s) + L.slot_v8_off; }
+  int* slot_vx(int l, int s) const { return reinterpret_cast<int*>(slot_k(l, s) + L.slot_vx_off); }
+  // the V^T that attention reads: E4M3 with the FP8 KV cache, else bf16
+  size_t slot_va_off() const { return L.vf8 ? L.slot_v8_off : L.slot_v_off; }
   int* slot_kx(int l, int s) const { return reinterpret_cast<int*>(slot_k(l, s) + L.slot_kx_off); }
   long long slot_kx_hs() const { return L.Tpad / bkv::kTokAlign; }
   char* ctx_k(int l) const { return ws + L.off_ctx + L.ctx_layer_bytes * l; }
@@ -267,6 +311,8 @@ struct bkv_cache_s {
   }
   char* mem_k(int l) const { return ws + L.off_mem + L.mem_layer_bytes * l; }
   char* mem_vt(int l) const { return mem_k(l) + L.mem_v_off; }
+  char* mem_v8(int l) const { return mem_k(l) + L.mem_v8_off; }
+  int* mem_vx(int l) const { return reinterpret_cast<int*>(mem_k(l) + L.mem_vx_off); }
   float* pose_store() const { return reinterpret_cast<float*>(ws + L.off_pose); }
   int* sel_ids() const { return reinterpret_cast<int*>(ws + L.off_sel); }
   int* sel_slots() const { return sel_ids() + bkv::kMaxK; }
@@ -277,8 +323,12 @@ struct bkv_cache_s {
     const size_t n = (size_t)cfg.heads * cfg.head_dim * cfg.conv_kernel;
     return reinterpret_cast<float*>(ws + L.off_w) + (2 * (size_t)l + which) * n;
   }
+  bool pose_bank() const { return cfg.mode == BKV_PR_SINK && cfg.bank_policy == BKV_BANK_POSE; }
+  int* bank_dev() const { return reinterpret_cast<int*>(ws + L.off_victim); }
+  int* victim_dev(int r) const { return bank_dev() + 2 * bkv::kMaxBank + 2 * r; }
   char* ref_k(int l) const { return ws + L.off_ref + L.ref_bytes * l; }
   char* ref_vt(int l) const { return ref_k(l) + L.ref_v_off; }
+  int* ref_vx(int l) const { return reinterpret_cast<int*>(ref_k(l) + L.ref_vx_off); }
   int* ref_kx(int l) const { return reinterpret_cast<int*>(ref_k(l) + L.ref_kx_off); }
   float2* tref() const { return reinterpret_cast<float2*>(ws + L.off_tref); }
   long long slot_k_hs() const { return (long long)L.Tpad * cfg.head_dim; }
@@ -315,9 +365,13 @@ struct bkv_cache_s {
         g.kx = ref_kx(l);
         g.kx_hs = L.ref_pad / bkv::kTokAlign;
       }
+      if (vf8()) {
+        g.vx = ref_vx(l);
+        g.vx_hs = L.ref_pad / bkv::kTokAlign;
+      }
     } else if (!ctx_mode()) {
       g.k = slot_k(l, p.slot);
-      g.v = slot_vt(l, p.slot);
+      g.v = slot_k(l, p.slot) + slot_va_off();
       g.k_hs = slot_k_hs();
       g.v_hs = slot_v_hs();
       g.v_ld = L.Tpad;
@@ -325,16 +379,29 @@ struct bkv_cache_s {
         g.kx = slot_kx(l, p.slot);
         g.kx_hs = slot_kx_hs();
       }
+      if (vf8()) {
+        g.vx = slot_vx(l, p.slot);
+        g.vx_hs = slot_kx_hs();
+      }
     } else {
       ctx_seg_k(l, p, g);
       if (p.kind == bkv::SEG_MEMORY) {
-        g.v = mem_vt(l) + (size_t)p.id * L.tf_pad * L.esize;
+        const size_t col = (size_t)p.id * L.tf_pad;       // the frame's first V^T column
+        g.v = vf8() ? mem_v8(l) + col : mem_vt(l) + col * L.esize;
         g.v_hs = (long long)L.mem_ld * cfg.head_dim;
         g.v_ld = L.mem_ld;
+        if (vf8()) {
+          g.vx = mem_vx(l) + col / bkv::kTokAlign;
+          g.vx_hs = L.mem_ld / bkv::kTokAlign;
+        }
       } else {
-        g.v = slot_vt(l, p.slot);
+        g.v = slot_k(l, p.slot) + slot_va_off();
         g.v_hs = slot_v_hs();
         g.v_ld = L.Tpad;
+        if (vf8()) {
+          g.vx = slot_vx(l, p.slot);
+          g.vx_hs = slot_kx_hs();
+        }
       }
     }
     return g;
@@ -347,6 +414,24 @@ void profile_release(bkv_cache h) {
   for (hipEvent_t e : h->prof.ev)
     if (e) (void)hipEventDestroy(e);
   h->prof = bkv_cache_s::Prof{};
+}
+
+// Pose-aware bank: wait for every displaced-member readback in flight and
+// forget them (reset, destroy).
+void victims_drain(bkv_cache h) {
+  for (int r : h->victim_pending) (void)hipEventSynchronize(h->victim_ev[r]);
+  h->victim_pending.clear();
+}
+
+void victims_release(bkv_cache h) {
+  victims_drain(h);
+  for (hipEvent_t& e : h->victim_ev)
+    if (e) {
+      (void)hipEventDestroy(e);
+      e = nullptr;
+    }
+  if (h->victim_host) (void)hipHostFree(h->victim_host);
+  h->victim_host = nullptr;
 }
 
 bkv_status check_handle(bkv_cache h, bool need_ok = true) {
@@ -500,6 +585,16 @@ bkv_status bkv_create(const bkv_config* cfg, void* workspace, size_t bytes, hipS
     delete h;
     return fail(BKV_ERR_DEVICE, "RoPE table launch: %s", hipGetErrorString(e));
   }
+  if (h->pose_bank()) {               // pinned host words for the displaced-member readbacks
+    e = hipHostMalloc(reinterpret_cast<void**>(&h->victim_host), sizeof(int) * 2 * kPoseRing);
+    for (int r = 0; r < kPoseRing && e == hipSuccess; ++r)
+      e = hipEventCreateWithFlags(&h->victim_ev[r], hipEventDisableTiming);
+    if (e != hipSuccess) {
+      victims_release(h);
+      delete h;
+      return fail(BKV_ERR_DEVICE, "pose bank readback set-up: %s", hipGetErrorString(e));
+    }
+  }
   *out = h;
   return BKV_OK;
 }
@@ -507,12 +602,14 @@ bkv_status bkv_create(const bkv_config* cfg, void* workspace, size_t bytes, hipS
 bkv_status bkv_destroy(bkv_cache h) {
   if (!h) return fail(BKV_ERR_ARG, "null handle");
   profile_release(h);
+  victims_release(h);
   delete h;
   return BKV_OK;
 }
 
 bkv_status bkv_reset(bkv_cache h) {
   if (!h) return fail(BKV_ERR_ARG, "null handle");
+  victims_drain(h);
   h->sched.reset();
   h->error = false;
   h->ctx_ready.assign(h->cfg.layers, false);
@@ -558,6 +655,14 @@ bkv_status bkv_set_reference(bkv_cache h, int32_t layer, const void* k, const vo
   ap.vt = h->ref_vt(layer);
   ap.vt_hs = (long long)h->L.ref_pad * h->cfg.head_dim;
   ap.vt_ld = h->L.ref_pad;
+  if (h->vf8()) {
+    ap.v8 = ap.vt;
+    ap.v8_hs = ap.vt_hs;
+    ap.v8_ld = ap.vt_ld;
+    ap.vt = nullptr;
+    ap.vx = h->ref_vx(layer);
+    ap.vx_hs = h->L.ref_pad / bkv::kTokAlign;
+  }
   if (h->kf8()) {
     ap.k8 = h->ref_k(layer);
     ap.k8_hs = ap.vt_hs;
@@ -589,6 +694,23 @@ bkv_status bkv_retrieve(bkv_cache h, const float* pose, hipStream_t stream) {
       if (!h->ref_set[l]) return fail(BKV_ERR_STATE, "reference frames of layer %d not set", l);
   }
   if ((st = set_device(h)) != BKV_OK) return st;
+  // pose-aware bank: take in the displaced members whose readback has
+  // landed; wait for the oldest only when no slot is free (the host is then
+  // kPoseSpare blocks ahead of the device)
+  while (!h->victim_pending.empty()) {
+    const int r = h->victim_pending.front();
+    hipError_t e = hipEventQuery(h->victim_ev[r]);
+    if (e == hipErrorNotReady) {
+      if (h->sched.free_slots() > 0) break;
+      e = hipEventSynchronize(h->victim_ev[r]);
+    }
+    if (e != hipSuccess) return device_fail(h, e, "bank replacement readback");
+    if (!h->sched.resolve_displaced(h->victim_host[2 * r])) {
+      h->error = true;
+      return fail(BKV_ERR_DEVICE, "bank replacement returned id %d, not a bank member", h->victim_host[2 * r]);
+    }
+    h->victim_pending.erase(h->victim_pending.begin());
+  }
   if (!h->sched.open()) return fail(BKV_ERR_STATE, "no free slot (internal)");
   h->ctx_ready.assign(h->cfg.layers, false);
   if (h->conv_abs() && h->cfg.rope_t) {
@@ -619,10 +741,15 @@ bkv_status bkv_retrieve(bkv_cache h, const float* pose, hipStream_t stream) {
     a.P = h->cfg.pose_dim;
     a.cur_slot = h->sched.cur_slot();
     a.k = h->sched.n_dynamic();
-    a.nbank = a.k > 0 ? (int)h->sched.bank().size() : 0;
-    for (int i = 0; i < a.nbank; ++i) {
-      a.bank_id[i] = (int)h->sched.bank()[i].first;
-      a.bank_slot[i] = h->sched.bank()[i].second;
+    a.nbank = a.k > 0 ? h->sched.bank_count() : 0;
+    a.upd_pos = -1;
+    if (h->pose_bank()) {
+      a.bank_dev = h->bank_dev();       // the device holds the pose-aware bank
+    } else {
+      for (int i = 0; i < a.nbank; ++i) {
+        a.bank_id[i] = (int)h->sched.bank()[i].first;
+        a.bank_slot[i] = h->sched.bank()[i].second;
+      }
     }
     a.sel_ids = h->sel_ids();
     a.sel_slots = h->sel_slots();
@@ -658,6 +785,14 @@ bkv::AppendArgs append_args(bkv_cache h, int layer) {
   ap.vt = h->slot_vt(layer, cur.slot);
   ap.vt_hs = h->slot_v_hs();
   ap.vt_ld = h->L.Tpad;
+  if (h->vf8()) {                     // E4M3 V^T; the raw bf16 V^T only where the conv reads it
+    ap.v8 = h->slot_v8(layer, cur.slot);
+    ap.v8_hs = h->slot_v_hs();
+    ap.v8_ld = h->L.Tpad;
+    ap.vx = h->slot_vx(layer, cur.slot);
+    ap.vx_hs = h->slot_kx_hs();
+    if (!h->convkv()) ap.vt = nullptr;
+  }
   if (h->slot8()) {
     ap.k8 = h->slot_k(layer, cur.slot);
     ap.k8_hs = h->slot_k_hs();
@@ -711,13 +846,16 @@ bkv_status attend_context(bkv_cache h, int layer, const void* q, void* out, hipS
   a.sel_slots = h->sel_slots();
   a.slot_base = h->layer_kv(layer);
   a.slot_bytes = (long long)h->L.slot_bytes;
-  a.slot_v_off = (long long)h->L.slot_v_off;
+  a.slot_v_off = (long long)h->slot_va_off();
   a.slot_k_hs = h->slot_k_hs();
   a.slot_v_hs = h->slot_v_hs();
   a.slot_v_ld = h->L.Tpad;
   a.kf8 = h->kf8() ? 1 : 0;
   a.slot_kx_off = (long long)h->L.slot_kx_off;
   a.slot_kx_hs = h->slot_kx_hs();
+  a.vf8 = h->vf8() ? 1 : 0;
+  a.slot_vx_off = (long long)h->L.slot_vx_off;
+  a.slot_vx_hs = h->slot_kx_hs();
   a.split = h->L.split ? 1 : 0;
   a.part = reinterpret_cast<float*>(h->ws + h->L.off_split);
   a.nseg = (int)segs.size();
@@ -789,34 +927,44 @@ bkv_status bkv_commit(bkv_cache h, hipStream_t stream) {
   if (!h->sched.all_attended()) return fail(BKV_ERR_STATE, "commit before every layer was attended");
   if ((st = set_device(h)) != BKV_OK) return st;
   int displace = -1;
-  if (h->cfg.mode == BKV_PR_SINK && h->cfg.bank_policy == BKV_BANK_POSE && h->sched.bank_full()) {
+  if (h->pose_bank()) {
     const auto ev = h->sched.pending_eviction();
     if (ev.first >= 0) {
-      // rank the bank against the leaving block's stored pose, top 1
+      // The leaving block joins the device's bank table: at the next free
+      // position while there is room; in a full bank it replaces the member
+      // ranked first against its stored pose (top 1), whose (id, slot) are
+      // copied back to pinned host memory and taken in by a later retrieve.
+      // Nothing here waits for the device.
+      const bool full = h->sched.bank_full();
+      if (full && (int)h->victim_pending.size() >= kPoseRing)
+        return fail(BKV_ERR_STATE, "too many bank replacements in flight (internal)");
       bkv::OpenArgs a{};
-      a.query = h->pose_store() + (size_t)ev.second * h->cfg.pose_dim;
       a.pose_store = h->pose_store();
       a.P = h->cfg.pose_dim;
       a.cur_slot = -1;
-      a.k = 1;
-      a.nbank = (int)h->sched.bank().size();
-      for (int i = 0; i < a.nbank; ++i) {
-        a.bank_id[i] = (int)h->sched.bank()[i].first;
-        a.bank_slot[i] = h->sched.bank()[i].second;
+      a.bank_dev = h->bank_dev();
+      a.upd_id = (int)ev.first;
+      a.upd_slot = ev.second;
+      a.upd_pos = full ? -1 : h->sched.bank_count();
+      const int r = h->victim_next;
+      if (full) {
+        a.query = h->pose_store() + (size_t)ev.second * h->cfg.pose_dim;
+        a.k = 1;
+        a.nbank = h->sched.bank_count();
+        a.victim_out = h->victim_dev(r);
+        a.sel_ids = h->victim_dev(r);  // the ranking's own outputs land in the same pair
+        a.sel_slots = h->victim_dev(r) + 1;
       }
-      int* vic = reinterpret_cast<int*>(h->ws + h->L.off_victim);
-      a.sel_ids = vic;
-      a.sel_slots = vic + 1;
-      int got = -1;
       hipError_t e = timed(h, K_REPLACE, stream, [&] { return bkv::launch_open(a, stream); });
-      if (e == hipSuccess) e = hipMemcpyAsync(&got, vic, sizeof(int), hipMemcpyDeviceToHost, stream);
-      if (e == hipSuccess) e = hipStreamSynchronize(stream);
+      if (e == hipSuccess && full)
+        e = hipMemcpyAsync(h->victim_host + 2 * r, h->victim_dev(r), 2 * sizeof(int), hipMemcpyDeviceToHost,
+                           stream);
+      if (e == hipSuccess && full) e = hipEventRecord(h->victim_ev[r], stream);
       if (e != hipSuccess) return device_fail(h, e, "bank replacement");
-      for (int i = 0; i < a.nbank; ++i)
-        if (a.bank_id[i] == got) displace = i;
-      if (displace < 0) {
-        h->error = true;
-        return fail(BKV_ERR_DEVICE, "bank replacement returned id %d, not a bank member", got);
+      if (full) {
+        h->victim_pending.push_back(r);
+        h->victim_next = (r + 1) % kPoseRing;
+        displace = bkv::Schedule::kDisplaceDeferred;
       }
     }
   }
@@ -852,6 +1000,21 @@ bkv_status bkv_commit(bkv_cache h, hipStream_t stream) {
       c.n_mem = n_mem;
       hipError_t e = timed(h, K_CONV, stream, [&] { return bkv::launch_conv(c, h->bf16(), stream); });
       if (e != hipSuccess) return device_fail(h, e, "conv launch");
+      if (h->vf8()) {                 // the memory's V^T as E4M3 for attention
+        bkv::VQuantArgs q{};
+        q.vt = h->mem_vt(l);
+        q.vt_hs = c.vt_mem_hs;
+        q.vt_ld = h->L.mem_ld;
+        q.v8 = h->mem_v8(l);
+        q.v8_hs = c.vt_mem_hs;
+        q.v8_ld = h->L.mem_ld;
+        q.vx = h->mem_vx(l);
+        q.vx_hs = h->L.mem_ld / bkv::kTokAlign;
+        q.H = h->cfg.heads;
+        q.n = h->L.mem_ld;            // every memory frame's padded columns (pad stays 0)
+        e = timed(h, K_CONV, stream, [&] { return bkv::launch_vquant(q, stream); });
+        if (e != hipSuccess) return device_fail(h, e, "memory V quantisation launch");
+      }
     }
   }
   return BKV_OK;
@@ -916,7 +1079,7 @@ bkv_status bkv_stats(bkv_cache h, bkv_stats_t* out) {
   out->n_segments = (int32_t)h->sched.segments().size();
   out->n_keys = h->sched.context_tokens();
   out->last_evicted = h->sched.last_evicted();
-  out->bank_count = (int32_t)h->sched.bank().size();
+  out->bank_count = (int32_t)h->sched.bank_count();
   out->memory_count = h->sched.memory_count();
   out->workspace_bytes = h->L.total;
   out->split_attends = h->split_attends;
@@ -944,13 +1107,16 @@ bkv_status bkv_export_segment(bkv_cache h, int32_t layer, int32_t seg, void* k_o
   a.sel_slots = h->sel_slots();
   a.slot_base = h->layer_kv(layer);
   a.slot_bytes = (long long)h->L.slot_bytes;
-  a.slot_v_off = (long long)h->L.slot_v_off;
+  a.slot_v_off = (long long)h->slot_va_off();
   a.slot_k_hs = h->slot_k_hs();
   a.slot_v_hs = h->slot_v_hs();
   a.slot_v_ld = h->L.Tpad;
   a.kf8 = h->kf8() ? 1 : 0;
   a.slot_kx_off = (long long)h->L.slot_kx_off;
   a.slot_kx_hs = h->slot_kx_hs();
+  a.vf8 = h->vf8() ? 1 : 0;
+  a.slot_vx_off = (long long)h->L.slot_vx_off;
+  a.slot_vx_hs = h->slot_kx_hs();
   a.k_out = k_out;
   a.v_out = v_out;
   a.H = h->cfg.heads;

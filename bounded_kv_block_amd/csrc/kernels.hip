@@ -6,6 +6,7 @@
 //                      stream id), and the current block's temporal RoPE rows
 //   append_kernel      K with fused 3D RoPE -> cache rows; V -> cache V^T
 //   append_k8_kernel   the same with K stored as E4M3 + per-tile exponents
+//                      (and, for the FP8 KV cache, V^T as E4M3 too)
 //   qkv_gemm_kernel    fused QKV projection (bf16 MFMA) with the append's
 //                      epilogue: q to scratch, K rotated into the cache, V^T
 //   attn_bf16_kernel   flash attention on bf16 MFMA (32x32x16), K/V tiles
@@ -18,6 +19,7 @@
 //                      at context positions
 //   gather_k8_kernel   the same into E4M3 rows + per-tile exponents
 //   conv_kernel        ConvKV: depthwise temporal conv of evicted frames
+//   vquant_kernel      FP8 KV cache, ConvKV memory: bf16 V^T -> E4M3 V^T
 //   export_kernel      inspection copy of one context segment
 #include <math.h>
 #include <stdint.h>
@@ -115,7 +117,9 @@ __global__ void rope_table_kernel(float2* tab, int rows, int half, int dim, long
 // 256 threads, one per bank candidate.  Scores: cos = dot / (sqrt(|q|^2)
 // sqrt(|b|^2)) in fp64, each candidate's sums in one fixed sequential order
 // over the pose dimensions (staged through LDS 64 dimensions at a time, rows
-// padded so that the 256 lanes hit distinct banks); 0 when either norm is 0.
+// padded so that the 256 lanes hit distinct banks); 0 when either norm is 0
+// or the score is not finite (a pose holding Inf or NaN), so every candidate
+// has a finite score and each rank round has a winner.
 // Rank: (score desc, stream id asc), k rounds of an arg-max by wave 0.
 // Staging: each thread issues kOpenBatch pose loads before it writes any of
 // them to LDS (indices past the end load the last element again).
@@ -126,10 +130,18 @@ __global__ __launch_bounds__(kOpenThreads) void open_kernel(OpenArgs a) {
   __shared__ double s_score[kMaxBank];
   __shared__ int s_taken[kMaxBank];
   __shared__ int s_slot[kMaxBank];
+  __shared__ int s_id[kMaxBank];
   __shared__ float s_q[kOpenChunk];
   __shared__ float s_b[kMaxBank][kOpenChunk + 1];
   const int tid = threadIdx.x, lane = tid & 63;
-  if (tid < a.nbank) s_slot[tid] = a.bank_slot[tid];
+  if (tid < a.nbank) {
+    s_slot[tid] = a.bank_dev ? a.bank_dev[kMaxBank + tid] : a.bank_slot[tid];
+    s_id[tid] = a.bank_dev ? a.bank_dev[tid] : a.bank_id[tid];
+  }
+  if (a.bank_dev && a.upd_pos >= 0 && tid == 0) {   // a block joins a bank with room
+    a.bank_dev[a.upd_pos] = a.upd_id;
+    a.bank_dev[kMaxBank + a.upd_pos] = a.upd_slot;
+  }
   if (a.pose_in) {
     for (int i = tid; i < a.P; i += kOpenThreads) a.pose_store[(size_t)a.cur_slot * a.P + i] = a.pose_in[i];
   }
@@ -188,6 +200,7 @@ __global__ __launch_bounds__(kOpenThreads) void open_kernel(OpenArgs a) {
   if (tid < nb) {
     double sc = 0.0;
     if (qq > 0.0 && bb > 0.0) sc = dot / (sqrt(qq) * sqrt(bb));
+    if (!isfinite(sc)) sc = 0.0;
     s_score[tid] = sc;
     s_taken[tid] = 0;
   }
@@ -203,7 +216,7 @@ __global__ __launch_bounds__(kOpenThreads) void open_kernel(OpenArgs a) {
     for (int c = lane; c < nb; c += 64) {
       if (s_taken[c]) continue;
       const double sc = s_score[c];
-      const int id = a.bank_id[c];
+      const int id = s_id[c];
       if (sc > best || (sc == best && id < bid)) {
         best = sc;
         bid = id;
@@ -222,8 +235,14 @@ __global__ __launch_bounds__(kOpenThreads) void open_kernel(OpenArgs a) {
     }
     if (lane == 0) {
       a.sel_ids[r] = bid;
-      a.sel_slots[r] = a.bank_slot[bc];
+      a.sel_slots[r] = s_slot[bc];
       s_taken[bc] = 1;
+      if (a.victim_out) {                  // replacement: the first-ranked member leaves the bank
+        a.victim_out[0] = bid;
+        a.victim_out[1] = s_slot[bc];
+        a.bank_dev[bc] = a.upd_id;
+        a.bank_dev[kMaxBank + bc] = a.upd_slot;
+      }
     }
     __builtin_amdgcn_wave_barrier();
     __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
@@ -377,14 +396,50 @@ __device__ __forceinline__ int e4m3_pack4(float x0, float x1, float x2, float x3
   return __builtin_amdgcn_cvt_pk_fp8_f32(x2, x3, w, true);
 }
 
+// E4M3 V^T rows of one (64-token tile, head) from the token-major bf16 V tile
+// in LDS (16-byte chunk c of row r at c ^ ((r >> 3) & 7)), each value times
+// inv (the tile's 2^-e): a task is 4 channels x 16 tokens, read as 8-byte
+// slices (4 channels of one token) and written as one 16-byte run per
+// channel.  Tokens past the block's end are written as 0, the value the pad
+// columns hold from the workspace clear.
+__device__ __forceinline__ void store_vt8(const AppendArgs& a, const char* s_v, int tile0, int head,
+                                          int ntok, float inv) {
+  constexpr int RS = 128 * 2;
+  const int task = threadIdx.x;
+  if (task >= 32 * 4) return;              // 32 channel groups x 4 token groups
+  const int cg = task >> 2, tg = task & 3;
+  const int t0 = tg * 16;
+  if (t0 >= ntok) return;
+  float col[4][16];
+#pragma unroll
+  for (int e = 0; e < 16; ++e) {
+    const int t = t0 + e;
+    const bf16x4 w = *reinterpret_cast<const bf16x4*>(s_v + t * RS + (((cg >> 1) ^ ((t >> 3) & 7)) << 4) + (cg & 1) * 8);
+#pragma unroll
+    for (int ch = 0; ch < 4; ++ch) col[ch][e] = t < ntok ? (float)w[ch] * inv : 0.f;
+  }
+#pragma unroll
+  for (int ch = 0; ch < 4; ++ch) {
+    uint4 o;
+    o.x = (unsigned)e4m3_pack4(col[ch][0], col[ch][1], col[ch][2], col[ch][3]);
+    o.y = (unsigned)e4m3_pack4(col[ch][4], col[ch][5], col[ch][6], col[ch][7]);
+    o.z = (unsigned)e4m3_pack4(col[ch][8], col[ch][9], col[ch][10], col[ch][11]);
+    o.w = (unsigned)e4m3_pack4(col[ch][12], col[ch][13], col[ch][14], col[ch][15]);
+    *reinterpret_cast<uint4*>(static_cast<char*>(a.v8) + head * a.v8_hs + (size_t)(4 * cg + ch) * a.v8_ld +
+                              tile0 + t0) = o;
+  }
+}
+
 // FP8 key cache append (bf16 inputs, D = 128): K rotated in fp32, then stored
 // as E4M3 with one power-of-two scale per (64-token tile, head) -- the
 // tile's largest |K~| reduced over the workgroup -- and the tile exponent
-// written beside the rows.  V goes to V^T as in append_kernel.
+// written beside the rows.  V goes to V^T as in append_kernel (bf16, when
+// vt is set) and, for the FP8 KV cache (v8 set), to E4M3 V^T with its own
+// tile scale, the same rule over the tile's largest |V|.
 __global__ __launch_bounds__(256) void append_k8_kernel(AppendArgs a) {
   constexpr int D = 128, VEC = 8, CPR = D / VEC, RS = D * 2, IT = 64 * CPR / 256;
   __shared__ __attribute__((aligned(16))) char s_v[64 * RS];
-  __shared__ float s_max[4];
+  __shared__ float s_max[4], s_vmax[4];
   const int tile0 = blockIdx.x * 64;
   const int head = blockIdx.y;
   const int tid = threadIdx.x;
@@ -430,7 +485,7 @@ __global__ __launch_bounds__(256) void append_k8_kernel(AppendArgs a) {
     }
   }
   float kr[IT][VEC];
-  float amax = 0.f;
+  float amax = 0.f, vmax = 0.f;
 #pragma unroll
   for (int it = 0; it < IT; ++it) {
     const int task = tid + 256 * it, r = task / CPR;
@@ -443,12 +498,24 @@ __global__ __launch_bounds__(256) void append_k8_kernel(AppendArgs a) {
     }
 #pragma unroll
     for (int e = 0; e < VEC; ++e) amax = fmaxf(amax, fabsf(kr[it][e]));
+    if (a.v8 && live) {
+      const bf16x8 vv = *reinterpret_cast<const bf16x8*>(&vraw[it]);
+#pragma unroll
+      for (int e = 0; e < VEC; ++e) vmax = fmaxf(vmax, fabsf((float)vv[e]));
+    }
   }
 #pragma unroll
-  for (int o = 32; o > 0; o >>= 1) amax = fmaxf(amax, __shfl_xor(amax, o));
-  if ((tid & 63) == 0) s_max[tid >> 6] = amax;
+  for (int o = 32; o > 0; o >>= 1) {
+    amax = fmaxf(amax, __shfl_xor(amax, o));
+    vmax = fmaxf(vmax, __shfl_xor(vmax, o));
+  }
+  if ((tid & 63) == 0) {
+    s_max[tid >> 6] = amax;
+    s_vmax[tid >> 6] = vmax;
+  }
   __syncthreads();
   amax = fmaxf(fmaxf(s_max[0], s_max[1]), fmaxf(s_max[2], s_max[3]));
+  vmax = fmaxf(fmaxf(s_vmax[0], s_vmax[1]), fmaxf(s_vmax[2], s_vmax[3]));
   const int ex = e4m3_exponent(amax);
   const float inv = __builtin_amdgcn_ldexpf(1.f, -ex);
 #pragma unroll
@@ -461,7 +528,12 @@ __global__ __launch_bounds__(256) void append_k8_kernel(AppendArgs a) {
     *reinterpret_cast<uint2*>(static_cast<char*>(a.k8) + head * a.k8_hs + (size_t)(tile0 + r) * D + c * VEC) = w;
   }
   if (tid == 0) a.kx[head * a.kx_hs + blockIdx.x] = ex;
-  store_vt<__bf16, D>(a, s_v, tile0, head, ntok);
+  if (a.v8) {
+    const int vex = e4m3_exponent(vmax);
+    if (tid == 0) a.vx[head * a.vx_hs + blockIdx.x] = vex;
+    store_vt8(a, s_v, tile0, head, ntok, __builtin_amdgcn_ldexpf(1.f, -vex));
+  }
+  if (a.vt) store_vt<__bf16, D>(a, s_v, tile0, head, ntok);
 }
 
 // ------------------------------------------------------------------ attention, bf16 MFMA
@@ -503,8 +575,13 @@ static_assert(ABM == kAttnBM, "unit rows");
 constexpr int KT_BYTES = ABN * AD * 2;
 constexpr int VT_BYTES = AD * ABN * 2;
 constexpr int KT8_BYTES = ABN * AD;      // FP8 K tile: 64 rows x 128 bytes
+constexpr int VT8_BYTES = AD * ABN;      // FP8 V^T tile: 128 channel rows x 64 bytes
 constexpr int NSTAGE = 3;
 constexpr float kSumLimit = 256.0f;     // lane partial row sum of P that forces a rescale
+// FP8 V: P is packed as E4M3 at unit scale, so P <= 448 (E4M3's largest
+// finite value) is the bound; log2(448) in the base-2 units of S.
+constexpr float kSumLimit8 = 448.0f;
+constexpr float kLog2E4M3Max = 8.8073549f;
 constexpr int kFragAhead = 3;            // LDS reads in flight ahead of the MFMA that uses them
 
 // K tile: 64 rows x 16 chunks of 16 B.  Rows read together by a 16-lane phase
@@ -518,6 +595,11 @@ __device__ __forceinline__ int kperm(int r) { return ((r >> 2) & 1) * 16 + (r >>
 // +32); (r & 1) picks the bank half and this swizzle the chunk position, so
 // the 16 reads cover the 64 banks once.
 __device__ __forceinline__ int k8swz(int r) { return ((r >> 1) & 3) | (((r >> 4) & 1) << 2); }
+// FP8 V^T tile: 128 channel rows x 4 chunks of 16 B (four rows per 256-B bank
+// line).  A 16-lane phase reads the same logical chunk of 16 consecutive
+// rows; rows r and r + 4 then sit at different chunk positions, so the 16
+// reads cover the 64 banks once.
+__device__ __forceinline__ int v8swz(int d) { return (d >> 2) & 3; }
 
 __device__ __forceinline__ int xcd_remap(int bid, int nwg) {
   // Consecutive workgroup ids are dispatched round-robin over the 8 XCDs; give
@@ -588,11 +670,13 @@ struct TileCursor {
                           // same segment when j0 + 128 <= lim (the common case)
 };
 
-template <bool SPLIT, bool KF8>
+template <bool SPLIT, bool KF8, bool VF8>
 __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2)))
 void attn_bf16_kernel(AttnArgs a) {
+  static_assert(KF8 || !VF8, "the FP8 V cache comes with the FP8 key cache");
   constexpr int KTB = KF8 ? KT8_BYTES : KT_BYTES;   // K tile bytes in LDS
-  constexpr int SB = KTB + VT_BYTES;                  // stage bytes
+  constexpr int VTB = VF8 ? VT8_BYTES : VT_BYTES;   // V^T tile bytes in LDS
+  constexpr int SB = KTB + VTB;                       // stage bytes
   __shared__ __attribute__((aligned(1024))) char lds[NSTAGE * SB];
   __shared__ const char* s_k[kMaxSeg];      // segment K / V^T of the current head
   __shared__ const char* s_v[kMaxSeg];
@@ -605,6 +689,9 @@ void attn_bf16_kernel(AttnArgs a) {
   __shared__ const int* s_x[kMaxSeg];       // FP8 K: tile exponents of the current head
   __shared__ const int* s_xb[kMaxSeg];
   __shared__ long long s_xhs[kMaxSeg];
+  __shared__ const int* s_vx[kMaxSeg];      // FP8 V: tile exponents of the current head
+  __shared__ const int* s_vxb[kMaxSeg];
+  __shared__ long long s_vxhs[kMaxSeg];
 
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);   // uniform by construction
@@ -638,6 +725,10 @@ void attn_bf16_kernel(AttnArgs a) {
           s_xb[gg] = reinterpret_cast<const int*>(kb + a.slot_kx_off);
           s_xhs[gg] = a.slot_kx_hs;
         }
+        if constexpr (VF8) {
+          s_vxb[gg] = reinterpret_cast<const int*>(kb + a.slot_vx_off);
+          s_vxhs[gg] = a.slot_vx_hs;
+        }
         if (sg.k) {                      // K rotated into the context-K buffer
           kb = static_cast<const char*>(sg.k);
           khs = sg.k_hs;
@@ -655,6 +746,10 @@ void attn_bf16_kernel(AttnArgs a) {
         if constexpr (KF8) {
           s_xb[gg] = sg.kx;
           s_xhs[gg] = sg.kx_hs;
+        }
+        if constexpr (VF8) {
+          s_vxb[gg] = sg.vx;
+          s_vxhs[gg] = sg.vx_hs;
         }
       }
       s_kb[gg] = kb;
@@ -798,6 +893,10 @@ void attn_bf16_kernel(AttnArgs a) {
   // does not depend on i, so one register serves both loads (+4096 i).
   const unsigned vk8 = (unsigned)(gw * 1024 + (lane >> 3) * 128 +
                                   (((lane & 7) ^ (((lane >> 4) & 3) | (((gw >> 1) & 1) << 2))) << 4));
+  // FP8 V^T (128 rows of 64 B): chunk p = (4i + w)*64 + lane of a tile holds
+  // row p >> 2 = 64i + 16w + (lane >> 2), chunk (p & 3) ^ v8swz(row); the
+  // swizzle is (lane >> 4) & 3 for every i, so one register serves both loads
+  // (+ 64 rows per i in the scalar offset).
   unsigned vv = 0;
   auto issue_setup = [&](const TileCursor& c, int stage) {
     if (c.sg != cur_sg) {
@@ -805,8 +904,12 @@ void attn_bf16_kernel(AttnArgs a) {
       krs = buffer_rsrc(uniform_ptr(s_k[c.sg]));
       vrs = buffer_rsrc(uniform_ptr(s_v[c.sg]));
       cur_ld = __builtin_amdgcn_readfirstlane(s_ld[c.sg]);
-      const int p = gw * 64 + lane;
-      vv = (unsigned)((p >> 3) * cur_ld * 2 + (((p & 7) ^ vswz(p >> 3)) << 4));
+      if constexpr (VF8) {
+        vv = (unsigned)((gw * 16 + (lane >> 2)) * cur_ld + (((lane & 3) ^ ((lane >> 4) & 3)) << 4));
+      } else {
+        const int p = gw * 64 + lane;
+        vv = (unsigned)((p >> 3) * cur_ld * 2 + (((p & 7) ^ vswz(p >> 3)) << 4));
+      }
     }
     ld_kt = __builtin_amdgcn_readfirstlane(lds0 + stage * SB + gw * 1024);
     ld_j0 = __builtin_amdgcn_readfirstlane((unsigned)c.j0);
@@ -817,13 +920,19 @@ void attn_bf16_kernel(AttnArgs a) {
     for (int e = 0; e < 4; ++e) u[e] = (int)__builtin_amdgcn_readfirstlane((unsigned)r[e]);
     return u;
   };
-  // bf16 K: k = 0..3 K chunks, 4..7 V chunks.  FP8 K: 0..1 K, 2..5 V, 6..7 none.
-  constexpr int NCHUNK = KF8 ? 6 : 8;
+  // bf16 K: k = 0..3 K chunks, 4..7 V chunks.  FP8 K: 0..1 K, 2..5 V, 6..7
+  // none.  FP8 K and V: 0..1 K, 2..3 V, 4..7 none.
+  constexpr int NCHUNK = VF8 ? 4 : (KF8 ? 6 : 8);
   auto issue_chunk = [&](int k) {
     const unsigned j0 = __builtin_amdgcn_readfirstlane(ld_j0);
     const unsigned kt = __builtin_amdgcn_readfirstlane(ld_kt);
     const unsigned ld = __builtin_amdgcn_readfirstlane((unsigned)cur_ld);
-    if constexpr (KF8) {
+    if constexpr (VF8) {
+      if (k < 2)
+        dma16(uni4(krs), vk8, j0 * 128u + (unsigned)k * 4096u, kt + k * 4096);
+      else if (k < 4)
+        dma16(uni4(vrs), vv, j0 + (unsigned)(k - 2) * 64u * ld, kt + KTB + (k - 2) * 4096);
+    } else if constexpr (KF8) {
       if (k < 2)
         dma16(uni4(krs), vk8, j0 * 128u + (unsigned)k * 4096u, kt + k * 4096);
       else if (k < 6)
@@ -852,6 +961,11 @@ void attn_bf16_kernel(AttnArgs a) {
   f32x16 negm = f32x16{};
   f32x16 sacc[2];
   bf16x8 pb[2][2];
+  // FP8 V: P^T as the B operand of the scaled 32x32x64 MFMA, E4M3 at unit
+  // scale.  Lane half h holds, as contraction indices 32h .. 32h+31, the
+  // keys 16h .. 16h+15 (sacc[0]) then 32+16h .. 32+16h+15 (sacc[1]): the
+  // lane's own scores in register order, so no exchange between lanes.
+  i32x8 pb8;
   i32x8 kf[4];                             // FP8 K fragments of the S product
 
   // MFMA block: PV of one tile (16 MFMA, V^T fragments) then, optionally, S of
@@ -990,6 +1104,64 @@ void attn_bf16_kernel(AttnArgs a) {
     __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
     __builtin_amdgcn_sched_group_barrier(0x008, 4, 0);
   };
+  // MFMA block of the FP8 K and V path: PV as 4 scaled MFMAs (32x32x64, A =
+  // the E4M3 V^T fragment of channel block db, B = pb8, A scale the V tile's
+  // exponent, B scale 2^0), then S as 4 scaled MFMAs.  The V^T fragment of
+  // channel row d = 32 db + col is its logical chunks h (keys 16h..16h+15)
+  // and 2+h (keys 32+16h..); those of db = 0 are read by m_prefetch88 before
+  // the barrier (the V tile was published a period earlier), the rest two
+  // MFMAs ahead inside the block, with the K tile's reads after the barrier.
+  i32x4 hv[8];
+  auto v8_half = [&](const char* vt, int c) -> i32x4 {   // c = 2 db + which
+    const int d = 32 * (c >> 1) + col;
+    const int lc = (c & 1) ? 2 + hh : hh;
+    return *reinterpret_cast<const i32x4*>(vt + d * 64 + ((lc ^ v8swz(d)) << 4));
+  };
+  auto m_prefetch88 = [&](const char* vt) {
+    hv[0] = v8_half(vt, 0);
+    hv[1] = v8_half(vt, 1);
+  };
+  auto m_block88 = [&](const char* vt, const char* kt, int sk, int sv, auto with_s_t) {
+    constexpr bool with_s = decltype(with_s_t)::value;
+    i32x4 hk[8];
+    auto k8_half = [&](int c) {
+      const int j = c >> 1, r = 32 * (j & 1) + kperm(col);
+      const int p = ((4 * (j >> 1) + 2 * hh) ^ k8swz(r)) ^ (c & 1);
+      return *reinterpret_cast<const i32x4*>(kt + r * 128 + (p << 4));
+    };
+#pragma unroll
+    for (int db = 0; db < 4; ++db) {
+      const i32x8 vf = __builtin_shufflevector(hv[2 * db], hv[2 * db + 1], 0, 1, 2, 3, 4, 5, 6, 7);
+      o[db] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(vf, pb8, o[db], 0, 0, 0, sv, 0, 127);
+      if (db < 3) {
+        hv[2 * db + 2] = v8_half(vt, 2 * db + 2);
+        hv[2 * db + 3] = v8_half(vt, 2 * db + 3);
+      }
+      if (with_s) {
+        hk[2 * db] = k8_half(2 * db);
+        hk[2 * db + 1] = k8_half(2 * db + 1);
+      }
+    }
+    if (with_s) {
+#pragma unroll
+      for (int j = 0; j < 4; ++j) kf[j] = __builtin_shufflevector(hk[2 * j], hk[2 * j + 1], 0, 1, 2, 3, 4, 5, 6, 7);
+#pragma unroll
+      for (int j = 0; j < 4; ++j) s8_step(j, sk, negm);
+    }
+    // instruction order: (MFMA, then the next fragments' reads) four times,
+    // then the S MFMAs
+    constexpr int NR = with_s ? 4 : 2;      // reads after each of the first three MFMAs
+#pragma unroll
+    for (int db = 0; db < 3; ++db) {
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+      __builtin_amdgcn_sched_group_barrier(0x100, NR, 0);
+    }
+    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+    if constexpr (with_s) {
+      __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
+      __builtin_amdgcn_sched_group_barrier(0x008, 4, 0);
+    }
+  };
   // E8M0 A scale (127 + exponent) of the FP8 K tile at cursor c, read through
   // the scalar cache: the exponents were written by an earlier launch.
   // The segment's exponent pointer is re-read from LDS only when the segment
@@ -1003,6 +1175,17 @@ void attn_bf16_kernel(AttnArgs a) {
       x_ptr = uniform_ptr(s_x[c.sg]);
     }
     return 127 + reinterpret_cast<const_int_ptr>(reinterpret_cast<uintptr_t>(x_ptr))[c.j0 >> 6];
+  };
+  // the same for the FP8 V tile at cursor c
+  int vx_sg = -1;
+  const char* vx_ptr = nullptr;
+  auto vtile_scale = [&](const TileCursor& c) -> int {
+    typedef const __attribute__((address_space(4))) int* const_int_ptr;
+    if (__builtin_expect(c.sg != vx_sg, 0)) {
+      vx_sg = c.sg;
+      vx_ptr = uniform_ptr(s_vx[c.sg]);
+    }
+    return 127 + reinterpret_cast<const_int_ptr>(reinterpret_cast<uintptr_t>(vx_ptr))[c.j0 >> 6];
   };
   auto mask_tail = [&](int nvalid) {
     if (nvalid < ABN) {
@@ -1034,17 +1217,26 @@ void attn_bf16_kernel(AttnArgs a) {
   // P = exp2(S - shift) packed to bf16; returns the lane's partial row sum of
   // P in fp32 (four chains of plain adds: the bf16 dot instructions would
   // share the matrix core with the other group's MFMAs)
+  // (FP8 V: P packed to E4M3 at unit scale, four values per word; P <= 2^8
+  // keeps every value within E4M3's range)
   auto exp_pack = [&](float shift, auto shifted, auto&& hook) {
     float ls[4] = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int mb = 0; mb < 2; ++mb)
 #pragma unroll
-      for (int i = 0; i < 16; ++i) {
-        const float x = decltype(shifted)::value ? sacc[mb][i] - shift : sacc[mb][i];
-        const float e = __builtin_amdgcn_exp2f(x);
-        pb[mb][i >> 3][i & 7] = (__bf16)e;
-        ls[2 * mb + (i >> 3)] += e;
-        if ((i & 3) == 3) hook(4 * mb + (i >> 2));
+      for (int g = 0; g < 4; ++g) {
+        float e4[4];
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+          const int i = 4 * g + u;
+          const float x = decltype(shifted)::value ? sacc[mb][i] - shift : sacc[mb][i];
+          const float e = __builtin_amdgcn_exp2f(x);
+          e4[u] = e;
+          if constexpr (!VF8) pb[mb][i >> 3][i & 7] = (__bf16)e;
+          ls[2 * mb + (g >> 1)] += e;
+        }
+        if constexpr (VF8) pb8[4 * mb + g] = e4m3_pack4(e4[0], e4[1], e4[2], e4[3]);
+        hook(4 * mb + g);
       }
     return (ls[0] + ls[1]) + (ls[2] + ls[3]);
   };
@@ -1054,18 +1246,38 @@ void attn_bf16_kernel(AttnArgs a) {
 #pragma unroll
     for (int i = 0; i < 16; ++i) negm[i] = -m;
   };
-  // first tile: S holds raw scores; m = the exact row max
+  // first tile: S holds raw scores; m = the exact row max.  FP8 V: m moves
+  // only by whole numbers, starting at ceil(row max) - 8, so P = 2^(s - m)
+  // is the row's P times a power of two, its largest value in (128, 256],
+  // and its E4M3 codes are those of P under the row's own power-of-two
+  // scale (up to values near E4M3's subnormal range); every rescale factor
+  // is then an exact power of two.
   auto softmax_first = [&](int nvalid, auto&& load_hook) {
     mask_tail(nvalid);
     const float mx = row_max();
-    set_m(mx);
-    l_run = exp_pack(mx, std::true_type{}, load_hook);
+    const float m0 = VF8 ? ceilf(mx) - 8.f : mx;
+    set_m(m0);
+    l_run = exp_pack(m0, std::true_type{}, load_hook);
   };
   // later tiles: S holds s - m
   auto softmax = [&](int nvalid, auto&& load_hook) {
     mask_tail(nvalid);
     float part = exp_pack(0.f, std::false_type{}, load_hook);
-    if (__any(!(part <= kSumLimit))) {
+    if constexpr (VF8) {
+      // a lane sum within the bound keeps each P within it; otherwise the
+      // row max decides: a row with a P above 448 moves m up by the whole
+      // number that brings its largest P back into (128, 256]
+      if (__any(!(part <= kSumLimit8))) {
+        const float rm = row_max();
+        const float d = rm > kLog2E4M3Max ? ceilf(rm - 8.f) : 0.f;   // 0: the row keeps m
+        const float alpha = __builtin_amdgcn_exp2f(-d);
+        set_m(m_run + d);
+        l_run *= alpha;
+#pragma unroll
+        for (int db = 0; db < 4; ++db) o[db] *= alpha;
+        part = exp_pack(d, std::true_type{}, no_hook);
+      }
+    } else if (__any(!(part <= kSumLimit))) {
       const float d = fmaxf(row_max(), 0.f);
       const float alpha = __builtin_amdgcn_exp2f(-d);
       set_m(m_run + d);
@@ -1109,8 +1321,9 @@ void attn_bf16_kernel(AttnArgs a) {
     __syncthreads();                       // the previous piece is done with LDS
     if (tid < nseg) {
       s_k[tid] = s_kb[tid] + (KF8 ? 1 : 2) * head * s_khs[tid];
-      s_v[tid] = s_vb[tid] + 2 * head * s_vhs[tid];
+      s_v[tid] = s_vb[tid] + (VF8 ? 1 : 2) * head * s_vhs[tid];
       if constexpr (KF8) s_x[tid] = s_xb[tid] + head * s_xhs[tid];
+      if constexpr (VF8) s_vx[tid] = s_vxb[tid] + head * s_vxhs[tid];
     }
     // Q of the unit: the RoPE table entries and the 8 row chunks of a lane
     // are loaded before the first use (rows past the block's end load its
@@ -1196,6 +1409,7 @@ void attn_bf16_kernel(AttnArgs a) {
     __syncthreads();
     cur_sg = -1;
     x_sg = -1;
+    vx_sg = -1;
 #pragma unroll
     for (int i = 0; i < 4; ++i) o[i] = f32x16{};
     m_run = 0.f;
@@ -1239,7 +1453,21 @@ void attn_bf16_kernel(AttnArgs a) {
               __builtin_amdgcn_sched_barrier(0);
             }
           };
-          if constexpr (KF8) {
+          if constexpr (VF8) {
+            // V scale of tile t (at the cursor, before it moves) and K scale
+            // of tile t+1, read before the softmax so that their scalar
+            // loads have returned by the MFMA block
+            const int nvalid = xc.n - xc.j0;
+            const int sv = vtile_scale(xc);
+            advance(xc);
+            const int sa = tile_scale(xc);
+            if constexpr (decltype(first)::value) softmax_first(nvalid, hook);
+            else softmax(nvalid, hook);
+            asm volatile("" ::"s"(sa), "s"(sv));
+            m_prefetch88(lds + stage_of(t) * SB + KTB);
+            wg_barrier();
+            m_block88(lds + stage_of(t) * SB + KTB, lds + stage_of(t + 1) * SB, sa, sv, std::true_type{});
+          } else if constexpr (KF8) {
             // the next tile's scale is read before the softmax, so its
             // scalar load has returned by the MFMA block
             const int nvalid = xc.n - xc.j0;
@@ -1279,9 +1507,16 @@ void attn_bf16_kernel(AttnArgs a) {
         } else {
           softmax_first(xc.n - xc.j0, no_hook);
         }
-        m_prefetch(lds + stage_of(NP - 1) * SB + KTB);
-        wg_barrier();
-        m_block(lds + stage_of(NP - 1) * SB + KTB, nullptr, std::false_type{});
+        if constexpr (VF8) {
+          const int sv = vtile_scale(xc);
+          m_prefetch88(lds + stage_of(NP - 1) * SB + KTB);
+          wg_barrier();
+          m_block88(lds + stage_of(NP - 1) * SB + KTB, nullptr, 0, sv, std::false_type{});
+        } else {
+          m_prefetch(lds + stage_of(NP - 1) * SB + KTB);
+          wg_barrier();
+          m_block(lds + stage_of(NP - 1) * SB + KTB, nullptr, std::false_type{});
+        }
         wg_barrier();
         if (group == 0) wg_barrier();          // match group B's extra leading barrier
       }
@@ -1867,74 +2102,104 @@ void qkv_gemm_kernel(QkvArgs a) {
   const AppendArgs& ap = a.ap;
   const bool rope = has_rope(ap.rope);
   const __bf16* bias = static_cast<const __bf16*>(a.b);
-  // FP8 key cache: a wave's 128 features x 64 tokens are one head's K over
-  // one 64-token tile of the block (both aligned), so the tile's scale is a
-  // reduction within the wave: rotate every K value in place, take the
-  // largest magnitude over the valid tokens, then store E4M3 and the tile
-  // exponent.
-  if (ap.k8) {
-    const int fw = f0 + 128 * wf, tw = t0 + 64 * wt;
-    if (fw < NF && fw / HD == 1 && tw < T) {
-      const int head = (fw - HD) / AD;
-      float amax = 0.f;
+  // FP8 caches: a wave's 128 features x 64 tokens are one head's K (or V)
+  // over one 64-token tile of the block (both aligned), so the tile's scale
+  // is a reduction within the wave.  Pass 1 forms every value (bias, bf16
+  // rounding as it leaves the projection, the raw copies, RoPE for K) and
+  // reduces the largest magnitude over the valid tokens; pass 2 forms the
+  // values again and stores E4M3 bytes and the tile exponent.  Forming them
+  // twice keeps the accumulators as they are, which keeps the epilogue free
+  // of register spills.
+  const int fw = f0 + 128 * wf, tw = t0 + 64 * wt;
+  const int which_w = fw < NF ? fw / HD : -1;
+  if ((ap.k8 && which_w == 1) || (ap.v8 && which_w == 2)) {
+    if (tw >= T) return;
+    const bool isk = which_w == 1;
+    const int head = (fw - which_w * HD) / AD;
+    // a token column's (frame, y, x), clamped to the block (rows past its end
+    // are never stored and never enter the scale)
+    int fy[2], yy[2], xx[2];
 #pragma unroll
-      for (int bn = 0; bn < 2; ++bn) {
-        const int t = tw + 32 * bn + col;
-        int fy = 0, yy = 0, xx = 0;
-        if (rope && t < T) token_fyx(t, ap.rope.grid_h, ap.rope.grid_w, fy, yy, xx);
+    for (int bn = 0; bn < 2; ++bn) token_fyx(min(tw + 32 * bn + col, T - 1), ap.rope.grid_h, ap.rope.grid_w,
+                                             fy[bn], yy[bn], xx[bn]);
+    const RopeSel rs(ap.rope);
+    const bool rot = isk && rope;
+    // value j of group (bm, g) for token column bn; raw: also store the raw
+    // copies.  Branch-free apart from the stores.
+    auto value4 = [&](int bm, int bn, int g, float (&v)[4], bool raw) {
+      const int t = tw + 32 * bn + col;
+      const int d0 = 32 * bm + 8 * g + 4 * hh;
 #pragma unroll
-        for (int bm = 0; bm < 4; ++bm)
+      for (int j = 0; j < 4; ++j) v[j] = acc[bm][bn][4 * g + j];
+      if (bias) {
+        const bf16x4 bb = *reinterpret_cast<const bf16x4*>(bias + fw + d0);
 #pragma unroll
-          for (int g = 0; g < 4; ++g) {
-            const int d0 = 32 * bm + 8 * g + 4 * hh;
-            float v[4];
-#pragma unroll
-            for (int j = 0; j < 4; ++j) v[j] = acc[bm][bn][4 * g + j];
-            if (bias) {
-              const bf16x4 bb = *reinterpret_cast<const bf16x4*>(bias + fw + d0);
-#pragma unroll
-              for (int j = 0; j < 4; ++j) v[j] += (float)bb[j];
-            }
-#pragma unroll
-            for (int j = 0; j < 4; ++j) v[j] = (float)(__bf16)v[j];   // k in bf16, as for the bf16 cache
-            if (t < T && ap.k_raw) {
-              bf16x4 o;
-#pragma unroll
-              for (int j = 0; j < 4; ++j) o[j] = (__bf16)v[j];
-              *reinterpret_cast<bf16x4*>(static_cast<__bf16*>(ap.k_raw) + head * ap.k_raw_hs + (size_t)t * AD + d0) = o;
-            }
-            if (rope && t < T) {
-              rope_pair(v[0], v[1], d0, ap.rope, ap.t_row0 + fy, yy, xx);
-              rope_pair(v[2], v[3], d0 + 2, ap.rope, ap.t_row0 + fy, yy, xx);
-            }
-#pragma unroll
-            for (int j = 0; j < 4; ++j) {
-              acc[bm][bn][4 * g + j] = v[j];
-              if (t < T) amax = fmaxf(amax, fabsf(v[j]));
-            }
-          }
+        for (int j = 0; j < 4; ++j) v[j] += (float)bb[j];
       }
 #pragma unroll
-      for (int o = 32; o > 0; o >>= 1) amax = fmaxf(amax, __shfl_xor(amax, o));
-      const int ex = e4m3_exponent(amax);
-      const float inv = __builtin_amdgcn_ldexpf(1.f, -ex);
+      for (int j = 0; j < 4; ++j) v[j] = (float)(__bf16)v[j];   // bf16, as the unfused path receives it
+      if (raw && t < T) {
+        if (isk && ap.k_raw) {
+          bf16x4 o;
 #pragma unroll
-      for (int bn = 0; bn < 2; ++bn) {
-        const int t = tw + 32 * bn + col;
-        if (t >= T) continue;
+          for (int j = 0; j < 4; ++j) o[j] = (__bf16)v[j];
+          *reinterpret_cast<bf16x4*>(static_cast<__bf16*>(ap.k_raw) + head * ap.k_raw_hs + (size_t)t * AD + d0) = o;
+        } else if (!isk && ap.vt) {
 #pragma unroll
-        for (int bm = 0; bm < 4; ++bm)
-#pragma unroll
-          for (int g = 0; g < 4; ++g) {
-            const int d0 = 32 * bm + 8 * g + 4 * hh;
-            const f32x16& c = acc[bm][bn];
-            *reinterpret_cast<int*>(static_cast<char*>(ap.k8) + head * ap.k8_hs + (size_t)t * AD + d0) =
-                e4m3_pack4(c[4 * g] * inv, c[4 * g + 1] * inv, c[4 * g + 2] * inv, c[4 * g + 3] * inv);
-          }
+          for (int j = 0; j < 4; ++j)
+            static_cast<__bf16*>(ap.vt)[head * ap.vt_hs + (size_t)(d0 + j) * ap.vt_ld + t] = (__bf16)v[j];
+        }
       }
-      if (lane == 0) ap.kx[head * ap.kx_hs + tw / 64] = ex;
-      return;                              // this wave held K only
+      if (rot) {
+        rope_rot(v[0], v[1], rs.cs(d0, ap.t_row0 + fy[bn], yy[bn], xx[bn]));
+        rope_rot(v[2], v[3], rs.cs(d0 + 2, ap.t_row0 + fy[bn], yy[bn], xx[bn]));
+      }
+    };
+    float amax = 0.f;
+#pragma unroll
+    for (int bn = 0; bn < 2; ++bn) {
+      const bool live = tw + 32 * bn + col < T;
+#pragma unroll
+      for (int bm = 0; bm < 4; ++bm)
+#pragma unroll
+        for (int g = 0; g < 4; ++g) {
+          float v[4];
+          value4(bm, bn, g, v, true);
+#pragma unroll
+          for (int j = 0; j < 4; ++j) amax = live ? fmaxf(amax, fabsf(v[j])) : amax;
+          asm volatile("" : "+v"(amax));   // reduce here: the group's values die now
+        }
     }
+#pragma unroll
+    for (int o = 32; o > 0; o >>= 1) amax = fmaxf(amax, __shfl_xor(amax, o));
+    const int ex = e4m3_exponent(amax);
+    const float inv = __builtin_amdgcn_ldexpf(1.f, -ex);
+#pragma unroll
+    for (int bn = 0; bn < 2; ++bn) {
+      const int t = tw + 32 * bn + col;
+      if (t >= T) continue;
+#pragma unroll
+      for (int bm = 0; bm < 4; ++bm)
+#pragma unroll
+        for (int g = 0; g < 4; ++g) {
+          float v[4];
+          value4(bm, bn, g, v, false);
+          const int d0 = 32 * bm + 8 * g + 4 * hh;
+          const int w = e4m3_pack4(v[0] * inv, v[1] * inv, v[2] * inv, v[3] * inv);
+          if (isk) {
+            *reinterpret_cast<int*>(static_cast<char*>(ap.k8) + head * ap.k8_hs + (size_t)t * AD + d0) = w;
+          } else {
+            unsigned char* vp = static_cast<unsigned char*>(ap.v8) + head * ap.v8_hs + t;
+#pragma unroll
+            for (int j = 0; j < 4; ++j) vp[(size_t)(d0 + j) * ap.v8_ld] = (unsigned char)(w >> (8 * j));
+          }
+        }
+    }
+    if (lane == 0) {
+      if (isk) ap.kx[head * ap.kx_hs + tw / 64] = ex;
+      else ap.vx[head * ap.vx_hs + tw / 64] = ex;
+    }
+    return;                                // this wave held K (or V) of the FP8 cache only
   }
 #pragma unroll
   for (int bn = 0; bn < 2; ++bn) {
@@ -1991,6 +2256,49 @@ void qkv_gemm_kernel(QkvArgs a) {
   }
 }
 
+// ------------------------------------------------------------------ FP8 V^T of a bf16 V^T
+// One workgroup per (64-token tile, head): the tile's 128 rows of 64 bf16
+// values (16 KiB) are loaded 16 bytes per chunk, the largest magnitude is
+// reduced over the workgroup, and each chunk is written back as 8 E4M3 bytes
+// with the tile's power-of-two scale (the append kernel's rule); the tile
+// exponent goes beside the rows.  Pad columns hold 0 in the source and stay
+// 0.
+__global__ __launch_bounds__(256) void vquant_kernel(VQuantArgs a) {
+  __shared__ float s_max[4];
+  const int tile0 = blockIdx.x * 64, head = blockIdx.y, tid = threadIdx.x;
+  const char* src = static_cast<const char*>(a.vt) + 2 * (head * a.vt_hs + tile0);
+  bf16x8 raw[4];
+#pragma unroll
+  for (int it = 0; it < 4; ++it) {          // chunk c = tid + 256 it: row c >> 3, 8 tokens (c & 7) * 8
+    const int c = tid + 256 * it;
+    raw[it] = *reinterpret_cast<const bf16x8*>(src + (size_t)(c >> 3) * a.vt_ld * 2 + (c & 7) * 16);
+  }
+  float amax = 0.f;
+#pragma unroll
+  for (int it = 0; it < 4; ++it)
+#pragma unroll
+    for (int e = 0; e < 8; ++e) amax = fmaxf(amax, fabsf((float)raw[it][e]));
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) amax = fmaxf(amax, __shfl_xor(amax, o));
+  if ((tid & 63) == 0) s_max[tid >> 6] = amax;
+  __syncthreads();
+  amax = fmaxf(fmaxf(s_max[0], s_max[1]), fmaxf(s_max[2], s_max[3]));
+  const int ex = e4m3_exponent(amax);
+  const float inv = __builtin_amdgcn_ldexpf(1.f, -ex);
+  char* dst = static_cast<char*>(a.v8) + head * a.v8_hs + tile0;
+#pragma unroll
+  for (int it = 0; it < 4; ++it) {
+    const int c = tid + 256 * it;
+    uint2 w;
+    w.x = (unsigned)e4m3_pack4((float)raw[it][0] * inv, (float)raw[it][1] * inv, (float)raw[it][2] * inv,
+                               (float)raw[it][3] * inv);
+    w.y = (unsigned)e4m3_pack4((float)raw[it][4] * inv, (float)raw[it][5] * inv, (float)raw[it][6] * inv,
+                               (float)raw[it][7] * inv);
+    *reinterpret_cast<uint2*>(dst + (size_t)(c >> 3) * a.v8_ld + (c & 7) * 8) = w;
+  }
+  if (tid == 0) a.vx[head * a.vx_hs + blockIdx.x] = ex;
+}
+
 // ------------------------------------------------------------------ export
 template <typename T>
 __global__ void export_kernel(ExportArgs a) {
@@ -2023,8 +2331,22 @@ __global__ void export_kernel(ExportArgs a) {
     vhs = a.seg.v_hs;
     ld = a.seg.v_ld;
   }
-  const T* v = reinterpret_cast<const T*>(vb) + h * vhs + (size_t)d * ld + tok;
-  static_cast<T*>(a.v_out)[gid] = *v;
+  if constexpr (std::is_same<T, __bf16>::value) {
+    if (a.vf8) {   // E4M3 byte times 2^(tile exponent): exact in bf16
+      const bool in_slot = a.seg.dyn >= 0;
+      const int* xb = in_slot ? reinterpret_cast<const int*>(a.slot_base + (long long)a.sel_slots[a.seg.dyn] *
+                                                              a.slot_bytes + a.slot_vx_off)
+                              : a.seg.vx;
+      const long long xhs = in_slot ? a.slot_vx_hs : a.seg.vx_hs;
+      const int byte = reinterpret_cast<const unsigned char*>(vb)[h * vhs + (size_t)d * ld + tok];
+      static_cast<T*>(a.v_out)[gid] =
+          (T)__builtin_amdgcn_ldexpf(__builtin_amdgcn_cvt_f32_fp8(byte, 0), xb[h * xhs + tok / 64]);
+    } else {
+      static_cast<T*>(a.v_out)[gid] = reinterpret_cast<const T*>(vb)[h * vhs + (size_t)d * ld + tok];
+    }
+  } else {
+    static_cast<T*>(a.v_out)[gid] = reinterpret_cast<const T*>(vb)[h * vhs + (size_t)d * ld + tok];
+  }
   if constexpr (std::is_same<T, __bf16>::value) {
     if (a.kf8) {   // E4M3 byte times 2^(tile exponent): exact in bf16
       const bool in_slot = a.seg.dyn >= 0 && !a.seg.k;
@@ -2060,7 +2382,7 @@ hipError_t launch_open(const OpenArgs& a, hipStream_t s) {
 hipError_t launch_append(const AppendArgs& a, bool bf16, hipStream_t s) {
   dim3 grid((a.T + 63) / 64, a.H);
   if (a.k8) {
-    if (!bf16 || a.D != 128) return hipErrorInvalidValue;
+    if (!bf16 || a.D != 128 || !(a.vt || (a.v8 && a.vx))) return hipErrorInvalidValue;
     append_k8_kernel<<<grid, 256, 0, s>>>(a);
   } else if (bf16) {
     if (a.D != 128) return hipErrorInvalidValue;
@@ -2076,7 +2398,8 @@ hipError_t launch_append(const AppendArgs& a, bool bf16, hipStream_t s) {
 }
 
 hipError_t launch_qkv(const QkvArgs& a, hipStream_t s) {
-  if (a.ap.D != AD || a.C <= 0 || a.C % GK != 0 || !(a.ap.k_rot || (a.ap.k8 && a.ap.kx)) || !a.ap.vt || !a.q)
+  if (a.ap.D != AD || a.C <= 0 || a.C % GK != 0 || !(a.ap.k_rot || (a.ap.k8 && a.ap.kx)) ||
+      !(a.ap.vt || (a.ap.v8 && a.ap.vx && a.ap.k8)) || !a.q)
     return hipErrorInvalidValue;
   const int nf = (3 * a.ap.H * AD + GF - 1) / GF, nt = (a.ap.T + GT - 1) / GT;
   qkv_gemm_kernel<<<nf * nt, 512, 0, s>>>(a);
@@ -2096,9 +2419,11 @@ hipError_t launch_attention(const AttnArgs& a, bool bf16, hipStream_t s) {
     AttnArgs b = a;
     b.unit0 = 0;
     const int plain = split ? units / kStreamWG * kStreamWG : units;
+    if (a.vf8 && !a.kf8) return hipErrorInvalidValue;
     if (plain > 0) {
-      if (a.kf8) attn_bf16_kernel<false, true><<<plain, 64 * AWAVES, 0, s>>>(b);
-      else attn_bf16_kernel<false, false><<<plain, 64 * AWAVES, 0, s>>>(b);
+      if (a.vf8) attn_bf16_kernel<false, true, true><<<plain, 64 * AWAVES, 0, s>>>(b);
+      else if (a.kf8) attn_bf16_kernel<false, true, false><<<plain, 64 * AWAVES, 0, s>>>(b);
+      else attn_bf16_kernel<false, false, false><<<plain, 64 * AWAVES, 0, s>>>(b);
     }
     if (split) {
       // remainder units rU, each cut into rP key parts of at least one tile
@@ -2108,8 +2433,9 @@ hipError_t launch_attention(const AttnArgs& a, bool bf16, hipStream_t s) {
       if (NT < 1 || rU < 1 || rU >= kStreamWG) return hipErrorInvalidValue;
       b.unit0 = plain;
       b.parts = NT < kStreamWG / rU ? NT : kStreamWG / rU;
-      if (a.kf8) attn_bf16_kernel<true, true><<<kStreamWG, 64 * AWAVES, 0, s>>>(b);
-      else attn_bf16_kernel<true, false><<<kStreamWG, 64 * AWAVES, 0, s>>>(b);
+      if (a.vf8) attn_bf16_kernel<true, true, true><<<kStreamWG, 64 * AWAVES, 0, s>>>(b);
+      else if (a.kf8) attn_bf16_kernel<true, true, false><<<kStreamWG, 64 * AWAVES, 0, s>>>(b);
+      else attn_bf16_kernel<true, false, false><<<kStreamWG, 64 * AWAVES, 0, s>>>(b);
       if (b.parts > 1) attn_merge_kernel<<<rU * AWAVES, 64, 0, s>>>(b);
     }
   } else if (a.D == 64) {
@@ -2209,6 +2535,12 @@ __global__ __launch_bounds__(512) void mfma_probe_kernel(float* sink, int iters)
 
 hipError_t launch_mfma_probe(int workgroups, int iters, float* sink, hipStream_t s) {
   mfma_probe_kernel<<<workgroups, 512, 0, s>>>(sink, iters);
+  return hipGetLastError();
+}
+
+hipError_t launch_vquant(const VQuantArgs& a, hipStream_t s) {
+  if (a.n <= 0) return hipSuccess;
+  vquant_kernel<<<dim3((a.n + 63) / 64, a.H), 256, 0, s>>>(a);
   return hipGetLastError();
 }
 

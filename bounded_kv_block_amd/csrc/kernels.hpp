@@ -7,6 +7,8 @@
 // ld (the token stride) is a multiple of 64, so tile loads never leave a row.
 // FP8 key cache: K rows hold E4M3 bytes, and an int32 power-of-two exponent
 // per (head, 64-token tile) sits at kx [H][ld/64]; V^T stays bf16.
+// FP8 KV cache: V^T rows hold E4M3 bytes too, with their own exponents per
+// (head, 64-token tile) at vx [H][ld/64].
 #pragma once
 #include <hip/hip_runtime.h>
 #include <stdint.h>
@@ -49,7 +51,8 @@ struct Seg {
   const void* k;
   const void* v;
   const int* kx;            // FP8 key cache: tile exponents, head h at kx + h*kx_hs
-  long long k_hs, v_hs, kx_hs;
+  const int* vx;            // FP8 KV cache: V tile exponents, head h at vx + h*vx_hs
+  long long k_hs, v_hs, kx_hs, vx_hs;
   int v_ld, n, dyn, pad_;
 };
 
@@ -67,8 +70,11 @@ struct AttnArgs {
   long long slot_v_off;     // byte offset of V^T inside a slot
   long long slot_k_hs, slot_v_hs;
   long long slot_kx_off, slot_kx_hs;   // FP8 key cache: exponents inside a slot
+  long long slot_vx_off, slot_vx_hs;   // FP8 KV cache: V exponents inside a slot
   int slot_v_ld;
   int kf8;                  // 1: K is E4M3 with tile exponents (bf16 path only)
+  int vf8;                  // 1: V^T is E4M3 with tile exponents too (needs kf8), P V on
+                            //    scaled FP8 MFMA with P rounded to E4M3
   int split;                // 1: split slots exist (remainder units may be cut into key parts)
   int unit0;                // first (head, query tile) unit of this launch
   int parts;                // split launch: key parts per remainder unit
@@ -85,6 +91,8 @@ struct AppendArgs {
   void* vt; long long vt_hs; int vt_ld;             // V^T destination
   void* k8; long long k8_hs;                        // FP8 key cache: E4M3 K rows (or null)
   int* kx; long long kx_hs;                         //   and their tile exponents
+  void* v8; long long v8_hs; int v8_ld;             // FP8 KV cache: E4M3 V^T (or null; vt, if
+  int* vx; long long vx_hs;                         //   also set, gets the bf16 V^T) + exponents
   int T, H, D;
   int t_row0;
   Rope rope;
@@ -116,6 +124,14 @@ struct OpenArgs {
   double theta;
   int bank_id[kMaxBank];
   int bank_slot[kMaxBank];
+  // Pose-aware bank kept on the device: ids at bank_dev[0..nbank), slots at
+  // bank_dev[kMaxBank..], read instead of bank_id / bank_slot when non-null.
+  // bank_upd (the same table): upd_pos >= 0 writes (upd_id, upd_slot) there
+  // (a block joining a bank with room); with k = 1, the member ranked first
+  // is replaced by (upd_id, upd_slot) and its (id, slot) go to victim_out.
+  int* bank_dev;
+  int upd_pos, upd_id, upd_slot;
+  int* victim_out;
 };
 
 // ConvKV and context-relative PR-Sink: rotate raw K rows of the context's
@@ -157,6 +173,7 @@ struct ExportArgs {
   const int* sel_slots;
   const char* slot_base; long long slot_bytes, slot_v_off, slot_k_hs, slot_v_hs; int slot_v_ld;
   long long slot_kx_off, slot_kx_hs; int kf8;   // FP8 key cache: K exported dequantised
+  long long slot_vx_off, slot_vx_hs; int vf8;   // FP8 KV cache: V exported dequantised
   void* k_out; void* v_out;
   int H, D;
 };
@@ -178,6 +195,15 @@ inline bool attention_split(int T, int H, bool slots) {
 }
 hipError_t launch_gather(const GatherArgs& a, bool bf16, hipStream_t s);
 hipError_t launch_conv(const ConvArgs& a, bool bf16, hipStream_t s);
+// FP8 KV cache, ConvKV memory: bf16 V^T [H][D][ld] of n tokens -> E4M3 V^T
+// with one exponent per (head, 64-token tile).
+struct VQuantArgs {
+  const void* vt; long long vt_hs; int vt_ld;
+  void* v8; long long v8_hs; int v8_ld;
+  int* vx; long long vx_hs;
+  int H, n;
+};
+hipError_t launch_vquant(const VQuantArgs& a, hipStream_t s);
 hipError_t launch_export(const ExportArgs& a, bool bf16, hipStream_t s);
 hipError_t launch_mfma_probe(int workgroups, int iters, float* sink, hipStream_t s);
 

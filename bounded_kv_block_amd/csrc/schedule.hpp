@@ -25,6 +25,13 @@
 // Slots: every block in the cache occupies one slot (K and V of every layer).
 // A block keeps its slot until it leaves the cache, so a commit moves ids
 // between lists and never copies tensor data.
+//
+// Pose-aware bank replacement decided on the device: a commit into a full
+// bank may leave the displaced member unknown to the host for a while
+// (kDisplaceDeferred).  The leaving block joins the host's bank list at once
+// and the list carries one unresolved member ("ghost") until
+// resolve_displaced(id) names it and frees its slot; spare slots (Shape.spare)
+// let blocks open meanwhile.
 #pragma once
 #include <algorithm>
 #include <cstdint>
@@ -60,7 +67,9 @@ class Schedule {
     int kernel, memory_frames;
     int ref_frames;                         // PR-Sink reference frames (0 = none)
     bool relative;                          // PR-Sink context-relative positions
+    int spare = 0;                          // extra slots (deferred bank displacements)
   };
+  static constexpr int kDisplaceDeferred = -2;
 
   explicit Schedule(const Shape& s) : s_(s) {
     T_ = s.frames * s.tokens_per_frame;
@@ -70,7 +79,7 @@ class Schedule {
       n_slots_ = s.window + 1 + staged_max_;
     } else {
       staged_max_ = 0;
-      n_slots_ = s.statics + s.window + 1 + s.bank;
+      n_slots_ = s.statics + s.window + 1 + s.bank + s.spare;
     }
     reset();
   }
@@ -117,6 +126,7 @@ class Schedule {
     for (int i = n_slots_ - 1; i >= 0; --i) free_.push_back(i);   // pop_back hands out 0, 1, ...
     evicted_frames_ = 0;
     last_evicted_ = -1;
+    ghosts_ = 0;
     attended_.assign(s_.layers, false);
     segs_.clear();
   }
@@ -127,8 +137,12 @@ class Schedule {
   int64_t last_evicted() const { return last_evicted_; }
   const std::vector<SegPlan>& segments() const { return segs_; }
   const std::deque<std::pair<int64_t, int>>& bank() const { return bank_; }
+  // members of the bank (the host's list less its unresolved displaced members)
+  int bank_count() const { return (int)bank_.size() - ghosts_; }
+  int unresolved() const { return ghosts_; }
+  int free_slots() const { return (int)free_.size(); }
   int n_dynamic() const {
-    return s_.convkv ? 0 : (int)std::min<size_t>((size_t)s_.k, bank_.size());
+    return s_.convkv ? 0 : std::min(s_.k, bank_count());
   }
   int memory_count() const {
     if (!s_.convkv) return 0;
@@ -166,7 +180,23 @@ class Schedule {
     if ((int)window_.size() + 1 <= s_.window) return {-1, -1};
     return window_.front();
   }
-  bool bank_full() const { return s_.bank > 0 && (int)bank_.size() == s_.bank; }
+  bool bank_full() const { return s_.bank > 0 && bank_count() == s_.bank; }
+
+  // A deferred displacement resolved: the displaced member `id` leaves the
+  // host's list and its slot is free.  false if `id` is not a member or no
+  // displacement is unresolved.
+  bool resolve_displaced(int64_t id) {
+    if (ghosts_ == 0) return false;
+    for (size_t i = 0; i < bank_.size(); ++i) {
+      if (bank_[i].first == id) {
+        free_.push_back(bank_[i].second);
+        bank_.erase(bank_.begin() + (long)i);
+        --ghosts_;
+        return true;
+      }
+    }
+    return false;
+  }
 
   bool all_attended() const {
     for (bool a : attended_)
@@ -177,7 +207,8 @@ class Schedule {
   // Close the open block.  On success fills `taps` (ConvKV: the frames the
   // memory is rebuilt from, tap order, n_mem*kernel entries; empty = none).
   // PR-Sink: `displace` >= 0 names the bank position the leaving block
-  // replaces when the bank is full (pose-aware replacement); -1 = FIFO.
+  // replaces when the bank is full (pose-aware replacement); -1 = FIFO;
+  // kDisplaceDeferred: it replaces a member the host learns of later.
   bool commit(std::vector<ConvTap>* taps, int displace = -1) {
     if (!open_ || !all_attended()) return false;
     taps->clear();
@@ -193,12 +224,15 @@ class Schedule {
           window_.pop_front();
           last_evicted_ = e.first;
           if (s_.bank > 0) {
-            if (displace >= 0 && displace < (int)bank_.size() && (int)bank_.size() == s_.bank) {
+            const bool full = bank_count() == s_.bank;
+            if (displace >= 0 && displace < (int)bank_.size() && full) {
               free_.push_back(bank_[displace].second);
               bank_.erase(bank_.begin() + displace);
+            } else if (displace == kDisplaceDeferred && full) {
+              ++ghosts_;
             }
             bank_.push_back(e);
-            if ((int)bank_.size() > s_.bank) {
+            if (bank_count() > s_.bank) {
               free_.push_back(bank_.front().second);
               bank_.pop_front();
             }
@@ -304,6 +338,7 @@ class Schedule {
   int cur_slot_ = -1;
   std::deque<std::pair<int64_t, int>> static_, window_, bank_, staged_;
   std::vector<int> free_;
+  int ghosts_ = 0;
   int64_t evicted_frames_ = 0;
   int64_t last_evicted_ = -1;
   std::vector<bool> attended_;

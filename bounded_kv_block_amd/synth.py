@@ -43,6 +43,8 @@ WORKLOADS = {
     "prsink_512": dict(_BASE),
     # the same with the FP8 key cache (K as E4M3 with per-tile scales)
     "prsink_512_fp8k": dict(_BASE, dtype="bf16_fp8k"),
+    # the same with the FP8 KV cache (K and V as E4M3, P V on FP8 MFMA)
+    "prsink_512_fp8kv": dict(_BASE, dtype="bf16_fp8kv"),
     # the same with one reference frame (1024 tokens) as a permanent sink
     "prsink_512_ref": dict(_BASE, reference_frames=1),
     # the same with context-relative RoPE positions (keys re-rotated per block)
@@ -68,6 +70,12 @@ WORKLOADS = {
     # the same with the FP8 key cache (the rotated context quantised as it is gathered)
     "convkv_512_fp8k": dict(_BASE, mode="convkv", dtype="bf16_fp8k", static=0, dynamic_k=0, bank=0, pose_dim=0,
                             blocks=200, seed=5, pose_kind="none"),
+    # the same with the FP8 KV cache
+    "convkv_512_fp8kv": dict(_BASE, mode="convkv", dtype="bf16_fp8kv", static=0, dynamic_k=0, bank=0, pose_dim=0,
+                             blocks=200, seed=5, pose_kind="none"),
+    # 720x416 with the FP8 KV cache
+    "prsink_720x416_fp8kv": dict(_BASE, grid_h=26, grid_w=45, layers=40, steps=3, bank=16, seed=3,
+                                 dtype="bf16_fp8kv"),
     # the same with only the memory's positions restarted (window and current absolute)
     "convkv_512_abs": dict(_BASE, mode="convkv", static=0, dynamic_k=0, bank=0, pose_dim=0,
                            blocks=200, seed=5, pose_kind="none", positions="absolute"),

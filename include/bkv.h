@@ -31,8 +31,11 @@
  * during the call's stream work.  The handle holds a little host state.
  *
  * Streams.  Every device operation is enqueued on the caller's stream; no
- * call synchronizes except those documented as synchronizing.  A handle is
- * not thread-safe; use one handle per host thread.
+ * call synchronizes except those documented as synchronizing.  The calls on
+ * one handle share its workspace (cache slots, the selection, split slots, q
+ * scratch): they must run on one stream, or the caller must order them
+ * across streams (events), as a later call reads what an earlier one wrote.
+ * A handle is not thread-safe; use one handle per host thread.
  *
  * Errors.  Every call returns bkv_status and never throws.  BKV_ERR_ARG and
  * BKV_ERR_STATE leave the handle unchanged.  BKV_ERR_DEVICE (a failed launch
@@ -78,8 +81,20 @@ typedef enum { BKV_PR_SINK = 0, BKV_CONVKV = 1 } bkv_mode;
    128 (K) + 256 (V) + 4/64).  ConvKV and context-relative PR-Sink keep raw
    bf16 K in the slots (the conv and the per-block rotation read it) and
    quantise the rotated context, segment by segment (memory frames, blocks),
-   as they gather it. */
-typedef enum { BKV_F32 = 0, BKV_BF16 = 1, BKV_BF16_FP8K = 2 } bkv_dtype;
+   as they gather it.
+   BKV_BF16_FP8KV: the FP8 KV cache (the same page's 上手实践 notes offer an
+   "FP8 KV cache"): K as for BKV_BF16_FP8K, and V held as E4M3 too, with the
+   same tile rule (one power-of-two scale per head and 64-token tile of a
+   segment, over all channels); the softmax numerator P is held as E4M3 with
+   that rule applied to each query row (one power-of-two scale per row, its
+   largest P mapped into (224, 448]) and P V runs on the scaled FP8 matrix
+   instruction; the softmax denominator sums the unrounded P.  The library
+   moves its running max by whole numbers only, so its P codes are the row's
+   own (its scale may sit one power of two higher, which changes only values
+   near E4M3's subnormal range).  Cache bytes per token and head: 128 (K) +
+   128 (V) + 8/64 (exponents); ConvKV slots also keep the raw bf16 V the conv
+   reads. */
+typedef enum { BKV_F32 = 0, BKV_BF16 = 1, BKV_BF16_FP8K = 2, BKV_BF16_FP8KV = 3 } bkv_dtype;
 
 /* Temporal RoPE positions (bkv_config.rope_positions).
    BKV_POS_DEFAULT: PR-Sink absolute (frame f of block b at
@@ -105,8 +120,12 @@ typedef enum { BKV_POS_DEFAULT = 0, BKV_POS_CONTEXT = 1, BKV_POS_ABSOLUTE = 2 } 
    the window.  BKV_BANK_POSE: a block leaving the window into a full bank
    displaces the member whose pose has the largest cosine with its own
    (fp64, ranked as retrieval ranks: exact ties displace the lower stream id;
-   a zero pose scores 0), and joins the bank; needs pose_dim >= 1 and
-   bank_blocks >= 1. */
+   a zero pose, and a pose holding Inf or NaN, scores 0), and joins the bank;
+   needs pose_dim >= 1 and bank_blocks >= 1.  The ranking runs on the device,
+   which holds the bank's membership; the displaced member's id comes back to
+   the host asynchronously (its slot is reused once it has), so no call
+   waits for the device except a bkv_retrieve that finds the host more than
+   two blocks ahead of it (the workspace holds two spare slots for this). */
 typedef enum { BKV_BANK_FIFO = 0, BKV_BANK_POSE = 1 } bkv_bank_policy;
 
 typedef enum {
@@ -219,12 +238,15 @@ bkv_status bkv_set_conv_weights(bkv_cache h, int32_t layer, const float* wk, con
 bkv_status bkv_set_reference(bkv_cache h, int32_t layer, const void* k, const void* v, hipStream_t stream);
 
 /* Open the next block m (pose retrieval; LiveAnimate page, section 方法, Dynamic
-   Sink bullet).  With reference_frames > 0, BKV_ERR_STATE until the reference
+   Sink bullet).  With BKV_BANK_POSE it first takes in the bank members that
+   earlier commits displaced, waiting on `stream` only if it needs a slot
+   whose displacement has not come back yet.  With reference_frames > 0, BKV_ERR_STATE until the reference
    of every layer is set.  pose: device fp32 [pose_dim], the block's pose embedding; it is
    stored with the block for later retrieval.  Selects the top-min(dynamic_k,
    bank_count) bank blocks by cosine similarity to `pose` (fp64 arithmetic;
-   exact ties to the lower stream id; a zero-norm pose scores 0) on the device:
-   the host is not synchronized.  ConvKV: pose may be NULL.
+   exact ties to the lower stream id; a zero-norm pose, and a pose holding a
+   non-finite value (Inf, NaN), scores 0) on the device: the host is not
+   synchronized.  ConvKV: pose may be NULL.
    Errors: BKV_ERR_STATE if a block is already open; BKV_ERR_ARG if pose is NULL
    where needed. */
 bkv_status bkv_retrieve(bkv_cache h, const float* pose, hipStream_t stream);
@@ -262,11 +284,11 @@ bkv_status bkv_attend_qkv(bkv_cache h, int32_t layer, const void* x, const void*
 
 /* Close the open block: it joins the window; the oldest window block leaves
    (PR-Sink: into the bank, the oldest bank block dropped when full -- or,
-   with BKV_BANK_POSE, the member most similar by pose, found on `stream`;
-   the call then synchronizes `stream` to read that member's id; ConvKV: its
-   raw frames feed the conv memory, rebuilt here on `stream` once
-   conv_kernel frames were evicted).  Errors: BKV_ERR_STATE if no block is open
-   or some layer was not attended in this block. */
+   with BKV_BANK_POSE, the member most similar by pose, found on `stream`
+   without waiting for it; ConvKV: its raw frames feed the conv memory,
+   rebuilt here on `stream` once conv_kernel frames were evicted).  Does not
+   synchronize.  Errors: BKV_ERR_STATE if no block is open or some layer was
+   not attended in this block. */
 bkv_status bkv_commit(bkv_cache h, hipStream_t stream);
 
 /* Stream ids retrieved for the open block, in rank order (cosine descending,
@@ -284,7 +306,7 @@ bkv_status bkv_stats(bkv_cache h, bkv_stats_t* out);
 
 /* Inspection: copy context segment `seg` of the open block at `layer` as
    attention reads it -- K rotated, V as stored -- into device k_out, v_out
-   [tokens][heads][head_dim] in the cache dtype (BKV_BF16_FP8K: bf16, K as
+   [tokens][heads][head_dim] in the cache dtype (BKV_BF16_FP8K(V): bf16, K (and V) as
    its dequantised E4M3 value code * 2^e, which bf16 holds exactly).  For the current segment this
    needs an earlier bkv_attend of `layer` in this block.
    Errors: BKV_ERR_STATE (no open block / current block not yet written). */

@@ -19,6 +19,15 @@ void* sched_new_ref(int layers, int frames, int tpf, int window, int statics, in
   Schedule::Shape s{false, layers, frames, tpf, window, statics, k, bank, 1, 0, ref_frames, relative != 0};
   return new Schedule(s);
 }
+// pose-aware bank decided on the device: `spare` extra slots
+void* sched_new_pose(int layers, int frames, int tpf, int window, int statics, int k, int bank, int spare) {
+  Schedule::Shape s{false, layers, frames, tpf, window, statics, k, bank, 1, 0, 0, false, spare};
+  return new Schedule(s);
+}
+int sched_resolve(void* p, int64_t id) { return static_cast<Schedule*>(p)->resolve_displaced(id) ? 1 : 0; }
+int sched_bank_count(void* p) { return static_cast<Schedule*>(p)->bank_count(); }
+int sched_free_slots(void* p) { return static_cast<Schedule*>(p)->free_slots(); }
+int sched_deferred_code() { return Schedule::kDisplaceDeferred; }
 // commit with the bank position the leaving block displaces (-1: FIFO)
 int sched_commit_displace(void* p, int displace) {
   std::vector<bkv::ConvTap> taps;

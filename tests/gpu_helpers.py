@@ -6,7 +6,7 @@ import numpy as np
 
 from bounded_kv_block_amd import bkv, synth
 
-TOL = {"f32": 1e-5, "bf16": 2e-2, "bf16_fp8k": 2e-2}
+TOL = {"f32": 1e-5, "bf16": 2e-2, "bf16_fp8k": 2e-2, "bf16_fp8kv": 2e-2}
 
 
 class Run:

@@ -24,3 +24,28 @@ def test_measured_traffic_reads_the_committed_counters():
     v = bench.measured_traffic("prsink_512")
     assert v is None or v > 503316480
     assert bench.measured_traffic("no_such_workload") is None
+
+
+def _cpu_legs(name, **over):
+    import torch
+    from bounded_kv_block_amd import synth
+    cfg = synth.workload(name, **over)
+    poses = synth.poses(cfg, cfg["blocks"])
+
+    def run_inputs(layer, block, step):
+        return tuple(torch.from_numpy(a) for a in synth.qkv(cfg, layer, block, step))
+    m = bench.steady_block(cfg) + 1
+    return cfg, bench.cpu_baseline(cfg, run_inputs, poses, m, 0.05)
+
+
+def test_cpu_baseline_legs_on_small_streams():
+    # the oracle leg and the fp32 numpy leg both report whole-block query
+    # tokens/s; a block of several attends (layers x steps) divides by them
+    for name, over in (("tiny_fp32", {}),
+                       ("prsink_720x416", dict(heads=2, grid_h=4, grid_w=5, layers=2, steps=3, pose_dim=8)),
+                       ("convkv_512", dict(heads=2, grid_h=4, grid_w=4, blocks=10))):
+        cfg, res = _cpu_legs(name, **over)
+        assert res["kind"] == "oracle" and res["value"] > 0 and res["cores"] >= 1
+        assert res["fp32_numpy"]["value"] > 0
+        if cfg["layers"] * cfg["steps"] > 1:
+            assert "attends per block" in res["sample"]

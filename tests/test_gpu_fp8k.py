@@ -183,7 +183,7 @@ def _check_stored_keys(run, kv, layer=0):
     """Every segment's stored K (E4M3 x 2^e, exact in bf16) against the
     oracle's quantisation of its rotated K, one E4M3 step apart at most and
     only at rounding ties within the fp32-vs-fp64 rotation error (for memory
-    frames, whose raw K the caller passes bf16-rounded as stored, within a
+    frames, whose raw K the oracle holds bf16-rounded as the cache does, within a
     bf16 step of the fp32-vs-fp64 conv sum: 2^-4 of an E4M3 step); V exact
     up to bf16 storage of the conv memory."""
     n_total = n_tie = 0

@@ -55,13 +55,13 @@ class QkvRun(Run):
             H, D = self.cfg["heads"], self.cfg["head_dim"]
             x = self.x_dev(layer, block, step).float().cpu().numpy()
             _, _, wsel, bsel = self._pw[layer]
-            parts = oracle.qkv_projection(x, wsel, bsel, len(self.heads), D)
+            # q, k and v leave the projection in bf16, where the unfused path
+            # receives its bf16 inputs
+            parts = oracle.qkv_projection(x, wsel, bsel, len(self.heads), D, round_bf16=True)
             full = []
             for i, p in enumerate(parts):
                 a = np.zeros((x.shape[0], H, D))
-                # q, k and v leave the projection in bf16, where the unfused
-                # path receives its bf16 inputs
-                a[:, self.heads, :] = self.torch.from_numpy(p).to(self.torch.bfloat16).double().numpy()
+                a[:, self.heads, :] = p
                 full.append(a)
             self._host[key] = tuple(full)
         return self._host[key]
@@ -206,3 +206,21 @@ def _stream_fp8(cfg, run, check=None, heads=None, rows=None):
         if not run.host_inputs:
             run.drop(set(range(m - 70, m + 2)))
             run._host.clear()
+
+
+# ---- the fused path with the FP8 KV cache (K and V quantised in the epilogue)
+def test_qkv_fp8kv_small_ragged():
+    """FP8 K and V from the projection's epilogue: 3 heads, 180-token blocks
+    (a ragged last token tile, whose clamped rows must not enter either tile
+    scale), model_dim 256, bias, 12 blocks: every output."""
+    cfg = synth.workload("prsink_512_qkv", dtype="bf16_fp8kv", heads=3, grid_h=6, grid_w=10, bank=4, blocks=12,
+                         pose_dim=16, keyframes=5, model_dim=256)
+    _stream_fp8(cfg, QkvRun(cfg))
+
+
+def test_qkv_fp8kv_convkv_small():
+    """ConvKV with the FP8 KV cache through the fused path: raw K and V^T to
+    the slot (the conv reads them), E4M3 V^T beside them, E4M3 K~ into the
+    context buffer; 8 blocks (memory from block 5)."""
+    cfg = synth.workload("convkv_512", dtype="bf16_fp8kv", heads=2, grid_h=4, grid_w=6, blocks=8, model_dim=128)
+    _stream_fp8(cfg, QkvRun(cfg))

@@ -43,6 +43,12 @@ def shim(tmp_path_factory):
     L.sched_pending.argtypes = [ctypes.c_void_p]
     L.sched_pending.restype = ctypes.c_int64
     L.sched_bank_full.argtypes = [ctypes.c_void_p]
+    L.sched_new_pose.restype = ctypes.c_void_p
+    L.sched_new_pose.argtypes = [ctypes.c_int] * 8
+    L.sched_resolve.argtypes = [ctypes.c_void_p, ctypes.c_int64]
+    for n in ("sched_bank_count", "sched_free_slots"):
+        getattr(L, n).argtypes = [ctypes.c_void_p]
+        getattr(L, n).restype = ctypes.c_int
     return L
 
 
@@ -182,6 +188,42 @@ def test_prsink_pose_bank_state_machine(shim, W, B, S):
             displace = bank_ids.index(victim)
         shim.sched_mark(s.p, 0)
         assert shim.sched_commit_displace(s.p, displace) == 1
+
+
+@pytest.mark.parametrize("W,B,lag", [(3, 4, 2), (1, 2, 1), (2, 3, 0)])
+def test_prsink_pose_bank_deferred_displacement(shim, W, B, lag):
+    """Pose-aware replacement decided on the device: a commit into a full
+    bank displaces a member the host learns of later (resolved `lag` blocks
+    late, as a readback would land), using the spare slots meanwhile.  After
+    each resolution the host's bank equals the oracle's; the bank count is
+    right at every block; slots stay distinct; a block can always open."""
+    rng = np.random.default_rng(3)
+    P = rng.standard_normal((50, 4)).astype(np.float32)
+    sim = oracle.simulate_prsink_pose_bank(50, lambda b: P[b], W, B, 1)
+    p = shim.sched_new_pose(1, 2, 4, W, 1, 1, B, 2)
+    deferred = shim.sched_deferred_code()
+    pending = []                                   # (resolve at block, victim id)
+    for m in range(49):
+        for due, vid in [x for x in pending if x[0] <= m or shim.sched_free_slots(p) == 0]:
+            assert shim.sched_resolve(p, vid) == 1
+            pending.remove((due, vid))
+        assert shim.sched_open(p) == 1, m
+        assert shim.sched_bank_count(p) == len(sim[m]["bank"]), m
+        if not pending:
+            ids = (ctypes.c_int64 * 512)()
+            slots = (ctypes.c_int * 512)()
+            n = shim.sched_bank(p, ids, slots, 512)
+            assert sorted(ids[:n]) == sorted(sim[m]["bank"]), m
+            assert len(set(slots[:n])) == n and shim.sched_cur_slot(p) not in slots[:n]
+        ev = shim.sched_pending(p)
+        displace = -1
+        if ev >= 0 and shim.sched_bank_full(p) == 1:
+            victim = oracle.retrieve(P[ev], [(b, P[b]) for b in sim[m]["bank"]], 1)[0]
+            pending.append((m + 1 + lag, victim))
+            displace = deferred
+        shim.sched_mark(p, 0)
+        assert shim.sched_commit_displace(p, displace) == 1
+    shim.sched_free(p)
 
 
 @pytest.mark.parametrize("R,k", [(0, 2), (2, 3), (1, 0)])
@@ -335,10 +377,37 @@ def test_fp8_key_cache_workspace_and_validation():
     ctx8 = al(al(H * rows * D) + 4 * H * xt)
     assert c16 - c8 == ctx16 - ctx8                     # same bf16 slots, memory and q scratch
     c = bkv.config_from_workload(synth.workload("prsink_512"))
-    c.dtype = 3
+    c.dtype = 4
     with pytest.raises(bkv.BkvError) as ei:
         bkv.workspace_size(c)
     assert ei.value.status == bkv.BKV_ERR_ARG
+
+
+def test_fp8_kv_cache_workspace():
+    """FP8 KV cache: a PR-Sink slot holds E4M3 K and E4M3 V^T (1 byte per
+    value each) with one int32 exponent per (head, 64-token tile) for each,
+    so K+V bytes per slot are half the bf16 slot's plus the exponents; a
+    ConvKV slot keeps its raw bf16 K and V^T (the conv and the rotation read
+    them) and adds the E4M3 V^T; its memory adds E4M3 V^T and exponents."""
+    from bounded_kv_block_amd import bkv, synth
+    al = lambda n: -(-n // 256) * 256
+    H, Tp, D = 40, 3072, 128
+    kx = 4 * H * Tp // 64
+    n16 = bkv.workspace_size(bkv.config_from_workload(synth.workload("prsink_512")))
+    n88 = bkv.workspace_size(bkv.config_from_workload(synth.workload("prsink_512_fp8kv")))
+    slot16 = 2 * H * Tp * D * 2
+    slot88 = al(al(H * Tp * D + kx) + H * Tp * D + kx)
+    assert 2 * (slot88 - 2 * kx) <= slot16 and n16 - n88 == 61 * (slot16 - slot88)
+    c16 = bkv.workspace_size(bkv.config_from_workload(synth.workload("convkv_512")))
+    c88 = bkv.workspace_size(bkv.config_from_workload(synth.workload("convkv_512_fp8kv")))
+    c8 = bkv.workspace_size(bkv.config_from_workload(synth.workload("convkv_512_fp8k")))
+    slot_c = 2 * H * Tp * D * 2
+    slot_c88 = al(2 * H * Tp * D * 2 + H * Tp * D + kx)
+    mem_extra = al(al(2 * H * 1024 * D * 2) + H * 1024 * D + 4 * H * 1024 // 64) - al(2 * H * 1024 * D * 2)
+    assert c88 - c8 == 6 * (slot_c88 - slot_c) + mem_extra and c8 < c16
+    with pytest.raises(bkv.BkvError) as ei:
+        bkv.workspace_size(bkv.config_from_workload(synth.workload("prsink_512_fp8kv", head_dim=64)))
+    assert ei.value.status == bkv.BKV_ERR_UNSUPPORTED
 
 
 def test_workspace_is_constant_in_stream_length():
@@ -407,11 +476,17 @@ def test_relative_positions_workspace_and_validation():
 
 def test_pose_bank_validation():
     """Pose-aware replacement needs poses and a bank; ConvKV has no bank; an
-    unknown policy is rejected.  It adds one 256-byte block to the workspace."""
+    unknown policy is rejected.  It adds two spare slots (blocks open while a
+    displaced member is being read back), their pose rows, and the device's
+    bank table (ids and slots of 256 members) with four readback pairs."""
     from bounded_kv_block_amd import bkv, synth
+    al = lambda n: -(-n // 256) * 256
     n0 = bkv.workspace_size(bkv.config_from_workload(synth.workload("prsink_512", bank=8)))
     n1 = bkv.workspace_size(bkv.config_from_workload(synth.workload("prsink_512_posebank")))
-    assert n1 - n0 == 256
+    slot = 2 * 40 * 3072 * 128 * 2
+    poses = al(4 * 15 * 128) - al(4 * 13 * 128)
+    table = al(4 * (2 * 256 + 2 * 4))
+    assert n1 - n0 == 2 * slot + poses + table
     for w in (synth.workload("prsink_512_posebank", bank=0), synth.workload("prsink_512_posebank", pose_dim=0,
                                                                           dynamic_k=0)):
         with pytest.raises(bkv.BkvError) as ei:
@@ -427,3 +502,19 @@ def test_pose_bank_validation():
     with pytest.raises(bkv.BkvError) as ei:
         bkv.workspace_size(c)
     assert ei.value.status == bkv.BKV_ERR_ARG
+
+
+def test_schedule_stress_under_address_and_ub_sanitizers(tmp_path):
+    """The host state machine under AddressSanitizer and
+    UndefinedBehaviorSanitizer (a g++ build of schedule.hpp with a stand-alone
+    driver): hundreds of random configurations of each mode, long streams,
+    late-resolved bank displacements, slot and count invariants after every
+    call; any sanitizer finding aborts the run."""
+    exe = str(tmp_path / "schedule_stress")
+    subprocess.run(["g++", "-std=c++17", "-O1", "-g", "-fsanitize=address,undefined",
+                    "-fno-sanitize-recover=all", "-fno-omit-frame-pointer", f"-I{CSRC}",
+                    os.path.join(ROOT, "tests", "csrc", "schedule_stress.cpp"), "-o", exe], check=True)
+    r = subprocess.run([exe, "300"], capture_output=True, text=True, timeout=240,
+                       env=dict(os.environ, ASAN_OPTIONS="detect_leaks=1", UBSAN_OPTIONS="print_stacktrace=1"))
+    assert r.returncode == 0, r.stdout[-2000:] + r.stderr[-4000:]
+    assert "no violation" in r.stdout
