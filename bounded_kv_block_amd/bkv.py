@@ -25,7 +25,7 @@ SEG_KINDS = {0: "static", 1: "dynamic", 2: "window", 3: "current", 4: "memory", 
 EXPORTS = ("bkv_workspace_size", "bkv_create", "bkv_destroy", "bkv_reset", "bkv_set_conv_weights",
            "bkv_set_reference",
            "bkv_profile_start", "bkv_profile_stop",
-           "bkv_retrieve", "bkv_attend", "bkv_attend_qkv", "bkv_commit", "bkv_selection",
+           "bkv_retrieve", "bkv_attend", "bkv_attend_static_scratch", "bkv_attend_qkv", "bkv_commit", "bkv_selection",
            "bkv_context", "bkv_stats",
            "bkv_export_segment", "bkv_status_str", "bkv_last_error", "bkv_probe_mfma")
 
@@ -86,6 +86,7 @@ def lib() -> ctypes.CDLL:
             "bkv_set_reference": [vp, i32, vp, vp, vp],
             "bkv_retrieve": [vp, vp, vp],
             "bkv_attend": [vp, i32, vp, vp, vp, vp, vp],
+            "bkv_attend_static_scratch": [vp, i32, vp, vp, vp, vp, vp],
             "bkv_attend_qkv": [vp, i32, vp, vp, vp, i32, vp, vp],
             "bkv_commit": [vp, vp],
             "bkv_selection": [vp, ctypes.POINTER(i32), i32, ctypes.POINTER(i32), vp],
@@ -229,6 +230,19 @@ class Cache:
         _check(lib().bkv_attend(self._h, layer, self._tensor(q, "q", shp, self.dtype),
                                 self._tensor(k, "k", shp, self.dtype), self._tensor(v, "v", shp, self.dtype),
                                 self._tensor(out, "out", shp, self.dtype), self._s()), "bkv_attend")
+        return out
+
+    def attend_static_scratch(self, layer: int, q, k, v, out=None):
+        """bkv_attend with the split launch's part states in the library's
+        static device array (the allocation-free entry point)."""
+        shp = self.qkv_shape
+        if out is None:
+            out = self._torch.empty(shp, dtype=self.dtype, device=self.device)
+        _check(lib().bkv_attend_static_scratch(self._h, layer, self._tensor(q, "q", shp, self.dtype),
+                                               self._tensor(k, "k", shp, self.dtype),
+                                               self._tensor(v, "v", shp, self.dtype),
+                                               self._tensor(out, "out", shp, self.dtype), self._s()),
+               "bkv_attend_static_scratch")
         return out
 
     def attend_qkv(self, layer: int, x, w, b=None, out=None):

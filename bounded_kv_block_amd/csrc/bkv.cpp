@@ -825,7 +825,10 @@ bkv::AppendArgs append_args(bkv_cache h, int layer) {
 
 // After the current block's K/V are in the cache: ConvKV context gather (once
 // per layer and block), then attention of q over the context into out.
-bkv_status attend_context(bkv_cache h, int layer, const void* q, void* out, hipStream_t stream) {
+// static_slots: the split launch's part states go to the static device array
+// (the allocation-free attend) instead of the workspace's split slots.
+bkv_status attend_context(bkv_cache h, int layer, const void* q, void* out, hipStream_t stream,
+                          float* static_slots = nullptr) {
   bkv_status st;
   if (h->ctx_mode() && !h->ctx_ready[layer]) {
     if ((st = gather_context(h, layer, stream)) != BKV_OK) return st;
@@ -857,7 +860,7 @@ bkv_status attend_context(bkv_cache h, int layer, const void* q, void* out, hipS
   a.slot_vx_off = (long long)h->L.slot_vx_off;
   a.slot_vx_hs = h->slot_kx_hs();
   a.split = h->L.split ? 1 : 0;
-  a.part = reinterpret_cast<float*>(h->ws + h->L.off_split);
+  a.part = static_slots ? static_slots : reinterpret_cast<float*>(h->ws + h->L.off_split);
   a.nseg = (int)segs.size();
   for (int i = 0; i < a.nseg; ++i) a.seg[i] = h->seg_arg(layer, segs[i]);
   hipError_t e = timed(h, K_ATTENTION, stream, [&] { return bkv::launch_attention(a, h->bf16(), stream); });
@@ -893,6 +896,24 @@ bkv_status bkv_attend(bkv_cache h, int32_t layer, const void* q, const void* k, 
   hipError_t e = timed(h, K_APPEND, stream, [&] { return bkv::launch_append(ap, h->bf16(), stream); });
   if (e != hipSuccess) return device_fail(h, e, "append launch");
   return attend_context(h, layer, q, out, stream);
+}
+
+bkv_status bkv_attend_static_scratch(bkv_cache h, int32_t layer, const void* q, const void* k, const void* v,
+                                     void* out, hipStream_t stream) {
+  bkv_status st = attend_checks(h, layer);
+  if (st != BKV_OK) return st;
+  if (!q || !k || !v || !out) return fail(BKV_ERR_ARG, "null q/k/v/out");
+  if (out == q || out == k || out == v) return fail(BKV_ERR_ARG, "out aliases an input");
+  if ((st = set_device(h)) != BKV_OK) return st;
+  float* slots = nullptr;
+  hipError_t e = bkv::static_split_slots(&slots);
+  if (e != hipSuccess) return device_fail(h, e, "static split slots");
+  bkv::AppendArgs ap = append_args(h, layer);
+  ap.k_in = k;
+  ap.v_in = v;
+  e = timed(h, K_APPEND, stream, [&] { return bkv::launch_append(ap, h->bf16(), stream); });
+  if (e != hipSuccess) return device_fail(h, e, "append launch");
+  return attend_context(h, layer, q, out, stream, slots);
 }
 
 bkv_status bkv_attend_qkv(bkv_cache h, int32_t layer, const void* x, const void* w, const void* b,

@@ -2406,6 +2406,30 @@ hipError_t launch_qkv(const QkvArgs& a, hipStream_t s) {
   return hipGetLastError();
 }
 
+// ------------------------------------------------------------------ static split slots
+// The split launch's part states (O, m, l of each key part) for the
+// allocation-free attend: a file-scope device array.  Host code uses only
+// the address hipGetSymbolAddress returns for the current device (the
+// array's name is a host-side stand-in there), kept per device.
+static __device__ __align__(256) float scratch[kStaticSplitBytes / sizeof(float)];
+
+hipError_t static_split_slots(float** slots) {
+  constexpr int kMaxDevices = 64;
+  static float* addr[kMaxDevices] = {};
+  int dev = -1;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+  if (!addr[dev]) {
+    void* p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return e;
+    addr[dev] = static_cast<float*>(p);
+  }
+  *slots = addr[dev];
+  return hipSuccess;
+}
+
 hipError_t launch_attention(const AttnArgs& a, bool bf16, hipStream_t s) {
   if (bf16) {
     if (a.D != AD) return hipErrorInvalidValue;

@@ -185,6 +185,14 @@ hipError_t launch_append(const AppendArgs& a, bool bf16, hipStream_t s);
 hipError_t launch_qkv(const QkvArgs& a, hipStream_t s);
 hipError_t launch_attention(const AttnArgs& a, bool bf16, hipStream_t s);
 
+// Split slots in a file-scope device array instead of the workspace, for
+// callers that cannot allocate: kStreamWG slots (the most a split launch
+// uses).  static_split_slots() returns the current device's copy (its
+// address is looked up once per device); the array keeps the last call's
+// contents, and calls that overlap on one device race for it.
+constexpr size_t kStaticSplitBytes = kSplitSlotBytes * kStreamWG;
+hipError_t static_split_slots(float** slots);
+
 // The bf16 attention shares key tiles across kStreamWG workgroups when its
 // (head, kAttnBM-query) units would leave more than 15% of whole-unit rounds
 // idle and the workspace holds split slots.

@@ -263,6 +263,23 @@ bkv_status bkv_retrieve(bkv_cache h, const float* pose, hipStream_t stream);
 bkv_status bkv_attend(bkv_cache h, int32_t layer, const void* q, const void* k, const void* v,
                       void* out, hipStream_t stream);
 
+/* For callers that cannot allocate device memory or must not touch more of it
+   than they pass (code under HIP graph capture, tight serving loops): the
+   same as bkv_attend, except that the split attention launch keeps its part
+   states (fp32 O, m, l of each key part of a cut unit; needed when heads x
+   256-query units leave the last round of 256 workgroups more than 15%
+   idle) in a file-scope device array of the library instead of the
+   workspace's split slots.  That array holds 256 slots of 132 KiB (33 MiB)
+   on each device the library runs on, until the process ends; its address
+   is looked up once per device, at the first call there.  It allocates
+   nothing and needs no clearing (a call reads only part states it wrote).
+   Every call of this entry point on one device shares the array: calls that
+   overlap on one device (other streams, other handles) race, so order them.
+   Errors: as bkv_attend; BKV_ERR_DEVICE if the array's address cannot be
+   found. */
+bkv_status bkv_attend_static_scratch(bkv_cache h, int32_t layer, const void* q, const void* k, const void* v,
+                                     void* out, hipStream_t stream);
+
 /* Fused QKV projection + attention of the open block at `layer` for one sampling
    step (the operator fusion of the LiveAnimate page, section 方法, and the
    fused-QKV build of the SoulX-LiveAct page, section 上手实践; neither writes the
