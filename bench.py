@@ -435,7 +435,10 @@ def main():
         "latency_ms": {"p50": float(np.percentile(per_block, 50)), "p99": float(np.percentile(per_block, 99)),
                        "max": float(per_block.max()), "blocks": int(args.steps),
                        "slope_ms_per_1000_blocks": 1000.0 * slope,
-                       "slope_pct_of_p50_per_1000_blocks": 100.0 * 1000.0 * slope / float(np.percentile(per_block, 50))},
+                       "slope_pct_of_p50_per_1000_blocks": 100.0 * 1000.0 * slope / float(np.percentile(per_block, 50)),
+                       # the fitted change from the first timed block to the last: the
+                       # per-1000-block figure extrapolates short runs far past their span
+                       "drift_pct_of_p50_over_run": 100.0 * slope * (args.steps - 1) / float(np.percentile(per_block, 50))},
         "memory": {"workspace_bytes_constant": len(ws_bytes) == 1,
                    "torch_allocated_constant": alloc0 == alloc1,
                    "torch_allocated_bytes": int(alloc1)},

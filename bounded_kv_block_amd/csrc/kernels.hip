@@ -580,7 +580,6 @@ constexpr int NSTAGE = 3;
 constexpr float kSumLimit = 256.0f;     // lane partial row sum of P that forces a rescale
 // FP8 V: P is packed as E4M3 at unit scale, so P <= 448 (E4M3's largest
 // finite value) is the bound; log2(448) in the base-2 units of S.
-constexpr float kSumLimit8 = 448.0f;
 constexpr float kLog2E4M3Max = 8.8073549f;
 constexpr int kFragAhead = 3;            // LDS reads in flight ahead of the MFMA that uses them
 
@@ -1199,7 +1198,7 @@ void attn_bf16_kernel(AttnArgs a) {
   };
   // row max of the tile's S: four max3 chains over the lane's 32 scores, then
   // lanes l and l^32 (same query) exchange
-  auto row_max = [&]() {
+  auto lane_max = [&]() {                 // over this lane's 32 keys of its row
     float c4[4];
 #pragma unroll
     for (int q = 0; q < 4; ++q) {
@@ -1210,7 +1209,10 @@ void attn_bf16_kernel(AttnArgs a) {
       x = __builtin_fmaxf(__builtin_fmaxf(x, v[b + 5]), v[b + 6]);
       c4[q] = __builtin_fmaxf(x, v[b + 7]);
     }
-    float mx = __builtin_fmaxf(__builtin_fmaxf(c4[0], c4[1]), __builtin_fmaxf(c4[2], c4[3]));
+    return __builtin_fmaxf(__builtin_fmaxf(c4[0], c4[1]), __builtin_fmaxf(c4[2], c4[3]));
+  };
+  auto row_max = [&]() {                  // lanes l and l ^ 32 hold a row's 64 keys
+    const float mx = lane_max();
     const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(mx), __float_as_uint(mx), false, false);
     return fmaxf(__uint_as_float(sw[0]), __uint_as_float(sw[1]));
   };
@@ -1264,10 +1266,11 @@ void attn_bf16_kernel(AttnArgs a) {
     mask_tail(nvalid);
     float part = exp_pack(0.f, std::false_type{}, load_hook);
     if constexpr (VF8) {
-      // a lane sum within the bound keeps each P within it; otherwise the
-      // row max decides: a row with a P above 448 moves m up by the whole
-      // number that brings its largest P back into (128, 256]
-      if (__any(!(part <= kSumLimit8))) {
+      // a row with a P above 448 moves m up by the whole number that brings
+      // its largest P back into (128, 256].  The test is on the lane's
+      // largest s - m: with the largest P near 256, a test on lane sums of
+      // P would fire on most tiles while every P stays below 448.
+      if (__any(lane_max() > kLog2E4M3Max)) {
         const float rm = row_max();
         const float d = rm > kLog2E4M3Max ? ceilf(rm - 8.f) : 0.f;   // 0: the row keeps m
         const float alpha = __builtin_amdgcn_exp2f(-d);
@@ -1608,13 +1611,16 @@ __global__ __launch_bounds__(64) void attn_merge_kernel(AttnArgs a) {
 }
 
 // ------------------------------------------------------------------ attention, fp32
-// One or two lanes per query (D = 64 or 128): each lane keeps 64 channels of
-// q~ and of the output accumulator in registers; key tiles of 32 in LDS.
+// A query's D channels are spread over G = D/8 lanes (8 channels each): a
+// score is 8 FMAs per lane and a butterfly sum over the G lanes, and the
+// lanes' 8 output channels accumulate P V directly.  Workgroup = 256 lanes =
+// 256/G queries of one head; key tiles of 64 in LDS (K rows and V^T rows,
+// padded by one float so the lanes of a query read distinct banks).
 template <int D>
-__global__ __launch_bounds__(128) void attn_f32_kernel(AttnArgs a) {
-  constexpr int LPQ = D / 64;
-  constexpr int QPB = 128 / LPQ;
-  constexpr int BNF = 32;
+__global__ __launch_bounds__(256) void attn_f32_kernel(AttnArgs a) {
+  constexpr int G = D / 8;                 // lanes per query
+  constexpr int QPB = 256 / G;             // queries per workgroup
+  constexpr int BNF = 64;
   __shared__ float s_kt[BNF][D + 1];
   __shared__ float s_vt[D][BNF + 1];
   __shared__ const float* s_k[kMaxSeg];
@@ -1653,22 +1659,22 @@ __global__ __launch_bounds__(128) void attn_f32_kernel(AttnArgs a) {
     s_n[tid] = sg.n;
     s_ld[tid] = ld;
   }
-  const int sub = tid % LPQ;
-  const int qrow = qt * QPB + tid / LPQ;
+  const int sub = tid % G, c0 = 8 * sub;   // this lane's channels c0 .. c0 + 7
+  const int qrow = qt * QPB + tid / G;
   const bool valid = qrow < a.T;
-  float q[64], o[64];
+  float q[8], o[8];
   {
     int f = 0, y = 0, x = 0;
     if (valid) token_fyx(qrow, a.rope.grid_h, a.rope.grid_w, f, y, x);
-    const float* qp = static_cast<const float*>(a.q) + ((size_t)(valid ? qrow : 0) * a.H + head) * D + sub * 64;
+    const float* qp = static_cast<const float*>(a.q) + ((size_t)(valid ? qrow : 0) * a.H + head) * D + c0;
 #pragma unroll
-    for (int c = 0; c < 64; ++c) q[c] = valid ? qp[c] : 0.f;
+    for (int c = 0; c < 8; ++c) q[c] = valid ? qp[c] : 0.f;
     if (valid && has_rope(a.rope)) {
 #pragma unroll
-      for (int c = 0; c < 64; c += 2) rope_pair(q[c], q[c + 1], sub * 64 + c, a.rope, a.t_row0 + f, y, x);
+      for (int c = 0; c < 8; c += 2) rope_pair(q[c], q[c + 1], c0 + c, a.rope, a.t_row0 + f, y, x);
     }
 #pragma unroll
-    for (int c = 0; c < 64; ++c) {
+    for (int c = 0; c < 8; ++c) {
       q[c] *= a.qscale;
       o[c] = 0.f;
     }
@@ -1681,47 +1687,48 @@ __global__ __launch_bounds__(128) void attn_f32_kernel(AttnArgs a) {
     const float* vb = s_v[sg];
     for (int j0 = 0; j0 < n; j0 += BNF) {
       const int nv = min(BNF, n - j0);
-      for (int i = tid; i < BNF * D; i += 128) {
+      for (int i = tid; i < BNF * D; i += 256) {
         const int r = i / D, c = i - r * D;
         s_kt[r][c] = (r < nv) ? kb[(size_t)(j0 + r) * D + c] : 0.f;
       }
-      for (int i = tid; i < D * BNF; i += 128) {
-        const int d = i / BNF, j = i - d * BNF;
-        s_vt[d][j] = (j < nv) ? vb[(size_t)d * ld + j0 + j] : 0.f;
+      for (int i = tid; i < D * BNF; i += 256) {
+        const int d = i / BNF, jj = i - d * BNF;
+        s_vt[d][jj] = (jj < nv) ? vb[(size_t)d * ld + j0 + jj] : 0.f;
       }
       __syncthreads();
       float s[BNF];
       float mx = -INFINITY;
 #pragma unroll
-      for (int j = 0; j < BNF; ++j) {
+      for (int jj = 0; jj < BNF; ++jj) {
         float acc = 0.f;
 #pragma unroll
-        for (int c = 0; c < 64; ++c) acc = fmaf(q[c], s_kt[j][sub * 64 + c], acc);
-        if (LPQ == 2) acc += __shfl_xor(acc, 1);
-        s[j] = (j < nv) ? acc : -INFINITY;
-        mx = fmaxf(mx, s[j]);
+        for (int c = 0; c < 8; ++c) acc = fmaf(q[c], s_kt[jj][c0 + c], acc);
+#pragma unroll
+        for (int w = 1; w < G; w <<= 1) acc += __shfl_xor(acc, w);
+        s[jj] = (jj < nv) ? acc : -INFINITY;
+        mx = fmaxf(mx, s[jj]);
       }
       const float m_new = fmaxf(m_run, mx);
       const float alpha = expf(m_run - m_new);
       m_run = m_new;
       l_run *= alpha;
 #pragma unroll
-      for (int c = 0; c < 64; ++c) o[c] *= alpha;
+      for (int c = 0; c < 8; ++c) o[c] *= alpha;
 #pragma unroll
-      for (int j = 0; j < BNF; ++j) {
-        const float p = expf(s[j] - m_new);
+      for (int jj = 0; jj < BNF; ++jj) {
+        const float p = expf(s[jj] - m_new);
         l_run += p;
 #pragma unroll
-        for (int c = 0; c < 64; ++c) o[c] = fmaf(p, s_vt[sub * 64 + c][j], o[c]);
+        for (int c = 0; c < 8; ++c) o[c] = fmaf(p, s_vt[c0 + c][jj], o[c]);
       }
       __syncthreads();
     }
   }
   if (valid) {
     const float inv = 1.f / l_run;
-    float* op = static_cast<float*>(a.out) + ((size_t)qrow * a.H + head) * D + sub * 64;
+    float* op = static_cast<float*>(a.out) + ((size_t)qrow * a.H + head) * D + c0;
 #pragma unroll
-    for (int c = 0; c < 64; ++c) op[c] = o[c] * inv;
+    for (int c = 0; c < 8; ++c) op[c] = o[c] * inv;
   }
 }
 
@@ -2401,6 +2408,9 @@ hipError_t launch_qkv(const QkvArgs& a, hipStream_t s) {
   if (a.ap.D != AD || a.C <= 0 || a.C % GK != 0 || !(a.ap.k_rot || (a.ap.k8 && a.ap.kx)) ||
       !(a.ap.vt || (a.ap.v8 && a.ap.vx && a.ap.k8)) || !a.q)
     return hipErrorInvalidValue;
+  // the tiles are addressed by 32-bit buffer offsets
+  if (3LL * a.ap.H * AD * a.C * 2 >= (1LL << 32) || (long long)a.ap.T * a.C * 2 >= (1LL << 32))
+    return hipErrorInvalidValue;
   const int nf = (3 * a.ap.H * AD + GF - 1) / GF, nt = (a.ap.T + GT - 1) / GT;
   qkv_gemm_kernel<<<nf * nt, 512, 0, s>>>(a);
   return hipGetLastError();
@@ -2463,11 +2473,11 @@ hipError_t launch_attention(const AttnArgs& a, bool bf16, hipStream_t s) {
       if (b.parts > 1) attn_merge_kernel<<<rU * AWAVES, 64, 0, s>>>(b);
     }
   } else if (a.D == 64) {
-    const int nwg = ((a.T + 127) / 128) * a.H;
-    attn_f32_kernel<64><<<nwg, 128, 0, s>>>(a);
+    const int nwg = ((a.T + 31) / 32) * a.H;
+    attn_f32_kernel<64><<<nwg, 256, 0, s>>>(a);
   } else if (a.D == 128) {
-    const int nwg = ((a.T + 63) / 64) * a.H;
-    attn_f32_kernel<128><<<nwg, 128, 0, s>>>(a);
+    const int nwg = ((a.T + 15) / 16) * a.H;
+    attn_f32_kernel<128><<<nwg, 256, 0, s>>>(a);
   } else {
     return hipErrorInvalidValue;
   }
