@@ -1612,10 +1612,28 @@ __global__ __launch_bounds__(64) void attn_merge_kernel(AttnArgs a) {
 
 // ------------------------------------------------------------------ attention, fp32
 // A query's D channels are spread over G = D/8 lanes (8 channels each): a
-// score is 8 FMAs per lane and a butterfly sum over the G lanes, and the
-// lanes' 8 output channels accumulate P V directly.  Workgroup = 256 lanes =
+// score is 8 FMAs per lane and a sum over the G lanes by DPP moves within
+// the lanes' row (every lane ends with the same value), and the lanes' 8
+// output channels accumulate P V directly.  Workgroup = 256 lanes =
 // 256/G queries of one head; key tiles of 64 in LDS (K rows and V^T rows,
 // padded by one float so the lanes of a query read distinct banks).
+// Sum over aligned groups of G = 8 or 16 lanes: swap neighbours, then pairs,
+// then the two quads of each 8 (row_half_mirror), then the two 8s of each
+// 16 (row_mirror).  Each step adds a value to its partner's, and fp32
+// addition is commutative, so all lanes of a group hold the same sum.
+template <int G>
+__device__ __forceinline__ float group_sum(float x) {
+  static_assert(G == 8 || G == 16, "groups of 8 or 16 lanes");
+  auto dpp = [](float v, auto ctrl_t) {
+    return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), decltype(ctrl_t)::value, 0xF, 0xF, false));
+  };
+  x += dpp(x, std::integral_constant<int, 0xB1>{});    // quad_perm [1,0,3,2]
+  x += dpp(x, std::integral_constant<int, 0x4E>{});    // quad_perm [2,3,0,1]
+  x += dpp(x, std::integral_constant<int, 0x141>{});   // row_half_mirror
+  if constexpr (G == 16) x += dpp(x, std::integral_constant<int, 0x140>{});   // row_mirror
+  return x;
+}
+
 template <int D>
 __global__ __launch_bounds__(256) void attn_f32_kernel(AttnArgs a) {
   constexpr int G = D / 8;                 // lanes per query
@@ -1687,13 +1705,40 @@ __global__ __launch_bounds__(256) void attn_f32_kernel(AttnArgs a) {
     const float* vb = s_v[sg];
     for (int j0 = 0; j0 < n; j0 += BNF) {
       const int nv = min(BNF, n - j0);
-      for (int i = tid; i < BNF * D; i += 256) {
-        const int r = i / D, c = i - r * D;
-        s_kt[r][c] = (r < nv) ? kb[(size_t)(j0 + r) * D + c] : 0.f;
+      // the tile's K rows and V^T columns as float4 loads, all issued before
+      // the first LDS store; keys past nv are not read and enter as 0
+      constexpr int NL = BNF * D / 4 / 256;   // float4 loads per lane per operand
+      float4 kl[NL], vl[NL];
+#pragma unroll
+      for (int it = 0; it < NL; ++it) {
+        const int idx = it * 256 + tid;
+        const int r = idx / (D / 4), c4 = idx - r * (D / 4);
+        kl[it] = r < nv ? *reinterpret_cast<const float4*>(kb + (size_t)(j0 + r) * D + 4 * c4)
+                        : make_float4(0.f, 0.f, 0.f, 0.f);
+        const int d = idx / (BNF / 4), jj = 4 * (idx - d * (BNF / 4));
+        const float* vp = vb + (size_t)d * ld + j0 + jj;
+        if (jj + 3 < nv) {
+          vl[it] = *reinterpret_cast<const float4*>(vp);
+        } else {
+          vl[it].x = jj < nv ? vp[0] : 0.f;
+          vl[it].y = jj + 1 < nv ? vp[1] : 0.f;
+          vl[it].z = jj + 2 < nv ? vp[2] : 0.f;
+          vl[it].w = 0.f;
+        }
       }
-      for (int i = tid; i < D * BNF; i += 256) {
-        const int d = i / BNF, jj = i - d * BNF;
-        s_vt[d][jj] = (jj < nv) ? vb[(size_t)d * ld + j0 + jj] : 0.f;
+#pragma unroll
+      for (int it = 0; it < NL; ++it) {
+        const int idx = it * 256 + tid;
+        const int r = idx / (D / 4), c4 = idx - r * (D / 4);
+        s_kt[r][4 * c4] = kl[it].x;
+        s_kt[r][4 * c4 + 1] = kl[it].y;
+        s_kt[r][4 * c4 + 2] = kl[it].z;
+        s_kt[r][4 * c4 + 3] = kl[it].w;
+        const int d = idx / (BNF / 4), jj = 4 * (idx - d * (BNF / 4));
+        s_vt[d][jj] = vl[it].x;
+        s_vt[d][jj + 1] = vl[it].y;
+        s_vt[d][jj + 2] = vl[it].z;
+        s_vt[d][jj + 3] = vl[it].w;
       }
       __syncthreads();
       float s[BNF];
@@ -1703,8 +1748,7 @@ __global__ __launch_bounds__(256) void attn_f32_kernel(AttnArgs a) {
         float acc = 0.f;
 #pragma unroll
         for (int c = 0; c < 8; ++c) acc = fmaf(q[c], s_kt[jj][c0 + c], acc);
-#pragma unroll
-        for (int w = 1; w < G; w <<= 1) acc += __shfl_xor(acc, w);
+        acc = group_sum<G>(acc);
         s[jj] = (jj < nv) ? acc : -INFINITY;
         mx = fmaxf(mx, s[jj]);
       }

@@ -170,3 +170,46 @@ def test_export_segments_match_oracle_context():
             assert np.max(np.abs(gk.float().cpu().numpy() - kr)) <= 2.0 ** -7 * np.max(np.abs(kr)) + 1e-6
             assert np.array_equal(gv.float().cpu().numpy(), v)
         run.cache.commit()
+
+
+class _GrowingKeys(Run):
+    """Block m's keys scaled by 1 + 0.75 m (rounded to bf16, the same values
+    for the device and the oracle).  Full tiles run in segment order, static
+    sink first, so a row's scores rise by several powers of two from tile to
+    tile and every row's running max must move within one attend.  Values
+    are scaled by 1/8 (exact): scores this large turn the bf16 rounding of
+    the rotated queries into errors of about 0.7% of the dominant P, which
+    on N(0,1) values would pass the bound, while a missed rescale of O or l
+    still moves an output by about |V|, some 0.5."""
+
+    def qkv(self, layer, block, step):
+        key = (layer, block, step)
+        if key not in self._host:
+            import torch
+            q, k, v = synth.qkv(self.cfg, layer, block, step)
+            k = torch.from_numpy(k * np.float32(1.0 + 0.75 * block)).to(torch.bfloat16).float().numpy()
+            self._host[key] = (q, k, v * np.float32(0.125))
+        return self._host[key]
+
+    def qkv_dev(self, layer, block, step):
+        key = (layer, block, step)
+        if key not in self._dev:
+            self._dev[key] = tuple(self.torch.from_numpy(a).to(self.device).to(self.dt)
+                                   for a in self.qkv(layer, block, step))
+        return self._dev[key]
+
+
+@pytest.mark.parametrize("name", ["prsink_512", "prsink_512_fp8k", "prsink_512_fp8kv"])
+def test_running_max_rescales_on_growing_scores(name):
+    """The lazy running max under scores that grow from tile to tile (bf16
+    and FP8 keys: the lane-sum test; FP8 KV: the lane-max test and whole
+    power-of-two moves of m): 2 heads, 3 frames of 4x8 tokens (one full tile
+    and a 32-key tail per segment), RoPE, top-2 of a bank of 3, 10 blocks,
+    every output of every block."""
+    cfg = synth.workload(name, heads=2, grid_h=4, grid_w=8, bank=3, blocks=10, pose_dim=16, keyframes=4)
+    run = _GrowingKeys(cfg)
+    ref = oracle.PRSinkReference(cfg, run)
+    for m in range(cfg["blocks"]):
+        run.open(m)
+        _check_block(run, ref, m)
+        run.cache.commit()
