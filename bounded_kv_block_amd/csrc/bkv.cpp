@@ -440,9 +440,9 @@ bkv_status check_handle(bkv_cache h, bool need_ok = true) {
   return BKV_OK;
 }
 
-enum { K_RETRIEVE = 0, K_APPEND, K_ATTENTION, K_GATHER, K_CONV, K_EXPORT, K_QKV, K_REPLACE, K_COUNT };
+enum { K_RETRIEVE = 0, K_APPEND, K_ATTENTION, K_GATHER, K_CONV, K_EXPORT, K_QKV, K_REPLACE, K_VQUANT, K_COUNT };
 const char* const kKernelNames[K_COUNT] = {"retrieve", "append", "attention", "gather", "conv", "export",
-                                           "qkv", "replace"};
+                                           "qkv", "replace", "vquant"};
 
 // Run `launch`, bracketed by event records on `s` while a profile is recording.
 template <class F>
@@ -1033,7 +1033,7 @@ bkv_status bkv_commit(bkv_cache h, hipStream_t stream) {
         q.vx_hs = h->L.mem_ld / bkv::kTokAlign;
         q.H = h->cfg.heads;
         q.n = h->L.mem_ld;            // every memory frame's padded columns (pad stays 0)
-        e = timed(h, K_CONV, stream, [&] { return bkv::launch_vquant(q, stream); });
+        e = timed(h, K_VQUANT, stream, [&] { return bkv::launch_vquant(q, stream); });
         if (e != hipSuccess) return device_fail(h, e, "memory V quantisation launch");
       }
     }

@@ -333,7 +333,8 @@ bkv_status bkv_export_segment(bkv_cache h, int32_t layer, int32_t seg, void* k_o
 /* Per-kernel device time, measured with HIP events recorded on the caller's
    stream immediately before and after each kernel the handle launches. */
 typedef struct {
-  char kernel[24];         /* "retrieve", "append", "attention", "gather", "conv", "export", "qkv" */
+  char kernel[24];         /* "retrieve", "append", "attention", "gather", "conv", "export", "qkv",
+                              "replace" (pose-bank ranking), "vquant" (FP8 V of the ConvKV memory) */
   int64_t launches;
   double total_ms;         /* sum of per-launch event intervals */
   double max_ms;
