@@ -581,6 +581,8 @@ constexpr float kSumLimit = 256.0f;     // lane partial row sum of P that forces
 // FP8 V: P is packed as E4M3 at unit scale, so P <= 448 (E4M3's largest
 // finite value) is the bound; log2(448) in the base-2 units of S.
 constexpr float kLog2E4M3Max = 8.8073549f;
+constexpr float kSumLimit8 = 448.0f;     // FP8 V: lane partial row sum of P that forces the row max test
+constexpr float kHead8 = 3.0f;           // FP8 V: m = ceil(row max) - kHead8, largest P in (4, 8]
 constexpr int kFragAhead = 3;            // LDS reads in flight ahead of the MFMA that uses them
 
 // K tile: 64 rows x 16 chunks of 16 B.  Rows read together by a 16-lane phase
@@ -1219,8 +1221,8 @@ void attn_bf16_kernel(AttnArgs a) {
   // P = exp2(S - shift) packed to bf16; returns the lane's partial row sum of
   // P in fp32 (four chains of plain adds: the bf16 dot instructions would
   // share the matrix core with the other group's MFMAs)
-  // (FP8 V: P packed to E4M3 at unit scale, four values per word; P <= 2^8
-  // keeps every value within E4M3's range)
+  // (FP8 V: P packed to E4M3 at unit scale, four values per word; the
+  // running max keeps every P within E4M3's largest finite value, 448)
   auto exp_pack = [&](float shift, auto shifted, auto&& hook) {
     float ls[4] = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
@@ -1249,15 +1251,16 @@ void attn_bf16_kernel(AttnArgs a) {
     for (int i = 0; i < 16; ++i) negm[i] = -m;
   };
   // first tile: S holds raw scores; m = the exact row max.  FP8 V: m moves
-  // only by whole numbers, starting at ceil(row max) - 8, so P = 2^(s - m)
-  // is the row's P times a power of two, its largest value in (128, 256],
-  // and its E4M3 codes are those of P under the row's own power-of-two
-  // scale (up to values near E4M3's subnormal range); every rescale factor
-  // is then an exact power of two.
+  // only by whole numbers, starting at ceil(row max) - 3, so P = 2^(s - m)
+  // is the row's P times a power of two, its largest value in (4, 8], and
+  // its E4M3 codes are those of P under the row's own power-of-two scale
+  // (E4M3's rounding is the same at every power of two, up to values in
+  // its subnormal range, 2^9 below the largest); every rescale factor is
+  // then an exact power of two.
   auto softmax_first = [&](int nvalid, auto&& load_hook) {
     mask_tail(nvalid);
     const float mx = row_max();
-    const float m0 = VF8 ? ceilf(mx) - 8.f : mx;
+    const float m0 = VF8 ? ceilf(mx) - kHead8 : mx;
     set_m(m0);
     l_run = exp_pack(m0, std::true_type{}, load_hook);
   };
@@ -1266,13 +1269,15 @@ void attn_bf16_kernel(AttnArgs a) {
     mask_tail(nvalid);
     float part = exp_pack(0.f, std::false_type{}, load_hook);
     if constexpr (VF8) {
-      // a row with a P above 448 moves m up by the whole number that brings
-      // its largest P back into (128, 256].  The test is on the lane's
-      // largest s - m: with the largest P near 256, a test on lane sums of
-      // P would fire on most tiles while every P stays below 448.
-      if (__any(lane_max() > kLog2E4M3Max)) {
+      // a lane sum within 448 keeps each P within it; otherwise the row max
+      // decides, and a row with a P above 448 moves m up by the whole number
+      // that brings its largest P back into (4, 8].  With every P at most 8
+      // until a row's max grows, a lane's 32 P sum to at most 256 (a flat
+      // row, as the zeroed rows past a block's end are, included), so the
+      // test fires only around a grown max.
+      if (__any(!(part <= kSumLimit8))) {
         const float rm = row_max();
-        const float d = rm > kLog2E4M3Max ? ceilf(rm - 8.f) : 0.f;   // 0: the row keeps m
+        const float d = rm > kLog2E4M3Max ? ceilf(rm - kHead8) : 0.f;   // 0: the row keeps m
         const float alpha = __builtin_amdgcn_exp2f(-d);
         set_m(m_run + d);
         l_run *= alpha;
