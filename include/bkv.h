@@ -89,9 +89,10 @@ typedef enum { BKV_PR_SINK = 0, BKV_CONVKV = 1 } bkv_mode;
    that rule applied to each query row (one power-of-two scale per row, its
    largest P mapped into (224, 448]) and P V runs on the scaled FP8 matrix
    instruction; the softmax denominator sums the unrounded P.  The library
-   moves its running max by whole numbers only, so its P codes are the row's
-   own (its scale may sit one power of two higher, which changes only values
-   near E4M3's subnormal range).  Cache bytes per token and head: 128 (K) +
+   moves its running max by whole numbers only, starting each row's largest
+   P in (4, 8], so its P codes are the row's own: E4M3 rounds alike at every
+   power of two, and the lower scale changes only values in its subnormal
+   range, 2^9 below the row's largest P.  Cache bytes per token and head: 128 (K) +
    128 (V) + 8/64 (exponents); ConvKV slots also keep the raw bf16 V the conv
    reads. */
 typedef enum { BKV_F32 = 0, BKV_BF16 = 1, BKV_BF16_FP8K = 2, BKV_BF16_FP8KV = 3 } bkv_dtype;
