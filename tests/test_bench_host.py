@@ -49,3 +49,13 @@ def test_cpu_baseline_legs_on_small_streams():
         assert res["fp32_numpy"]["value"] > 0
         if cfg["layers"] * cfg["steps"] > 1:
             assert "attends per block" in res["sample"]
+
+
+def test_more_than_one_gpu_exits_with_a_message():
+    # the benchmark measures one GPU's share; N > 1 is refused before any GPU work
+    import subprocess
+    r = subprocess.run([sys.executable, os.path.join(os.path.dirname(os.path.dirname(os.path.abspath(__file__))),
+                                                     "bench.py"), "--gpus", "2"],
+                       capture_output=True, text=True, timeout=120)
+    assert r.returncode == 2
+    assert "one GPU only" in r.stderr and r.stdout == ""
