@@ -4,8 +4,9 @@ every head and every query of the attention output against the CPU oracle
 benchmark times -- the 512x512 PR-Sink block (3072 queries over 21504 keys),
 one layer of the 720x416 block at its third sampling step (3510 queries over
 24570 keys, split launch), the ConvKV block (3072 queries over 13312 keys,
-the 1024-token memory frame present) and the 512x512 block with the FP8 key
-cache."""
+the 1024-token memory frame present), and the 512x512, 720x416 and ConvKV
+blocks with the FP8 key cache and with the FP8 KV cache (whose 720x416 split
+launch also carries the zeroed query rows past the block's end)."""
 import numpy as np
 import pytest
 
@@ -52,8 +53,18 @@ def test_prsink_512_fp8k_every_output_of_a_steady_block():
     _prsink(synth.workload("prsink_512_fp8k", blocks=7), 6)
 
 
-def test_convkv_512_every_output_of_a_steady_block():
-    cfg = synth.workload("convkv_512", blocks=7)
+def test_prsink_512_fp8kv_every_output_of_a_steady_block():
+    _prsink(synth.workload("prsink_512_fp8kv", blocks=7), 6)
+
+
+def test_prsink_720x416_fp8kv_every_output_of_one_layer():
+    run = _prsink(synth.workload("prsink_720x416_fp8kv", blocks=7), 6, layer=33, step=2)
+    assert run.cache.stats()["split_attends"] == 7 * 40 * 3
+
+
+@pytest.mark.parametrize("name", ["convkv_512", "convkv_512_fp8kv"])
+def test_convkv_512_every_output_of_a_steady_block(name):
+    cfg = synth.workload(name, blocks=7)
     run = Run(cfg, host_inputs=False)
     ref = oracle.ConvKVReference(cfg, run)
     for m in range(cfg["blocks"]):
@@ -63,8 +74,8 @@ def test_convkv_512_every_output_of_a_steady_block():
         if m == 6:
             assert run.cache.stats()["n_keys"] == 1024 + 4 * 3072
             err = max_err(out, ref.attend(m, 0, 0))
-            print(f"convkv_512 block {m}: all 40 heads x 3072 queries, max|err| {err:.3e}", flush=True)
-            assert err <= TOL["bf16"], err
+            print(f"{name} block {m}: all 40 heads x 3072 queries, max|err| {err:.3e}", flush=True)
+            assert err <= TOL[cfg["dtype"]], err
         run.cache.commit()
         run.drop(set(range(m - 8, m + 2)))
         run._host.clear()
