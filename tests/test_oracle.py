@@ -398,3 +398,25 @@ def test_convkv_memory_is_held_in_the_cache_dtype():
         lambda dt: synth.workload("convkv_512", dtype=dt, heads=2, grid_h=2, grid_w=3, blocks=7,
                                   rope=(0, 0, 0) if dt == "f32" else (44, 42, 42)),
         SynthProvider)
+
+
+def test_e4m3_rounds_alike_at_every_power_of_two_in_its_normal_range(rng):
+    """The FP8-KV library holds each row's P at its own power of two (largest P
+    in (4, 8]) rather than at the row scale of the reading (largest P in
+    (224, 448]); its codes are the same because E4M3 rounding commutes with
+    power-of-two scaling while both values stay in the normal range.  Checked
+    on fp32-exact values against torch's own float8_e4m3fn conversion; in the
+    subnormal range (below 2^-6, a fixed quantum of 2^-9) it does not
+    commute."""
+    import torch
+    x = rng.uniform(1.0, 2.0, 20000).astype(np.float32).astype(np.float64) * rng.choice([-1.0, 1.0], 20000)
+    base = oracle.fp8.e4m3_round(x)
+    for k in range(-6, 9):
+        y = x * 2.0 ** k
+        keep = np.abs(y) <= oracle.fp8.E4M3_MAX
+        got = oracle.fp8.e4m3_round(y[keep])
+        assert np.array_equal(got, base[keep] * 2.0 ** k), k
+        ref = torch.from_numpy(y[keep].astype(np.float32)).to(torch.float8_e4m3fn).double().numpy()
+        assert np.array_equal(got, ref), k
+    y = x * 2.0 ** -8
+    assert not np.array_equal(oracle.fp8.e4m3_round(y), base * 2.0 ** -8)
