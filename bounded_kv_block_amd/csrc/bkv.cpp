@@ -844,7 +844,7 @@ bkv_status attend_context(bkv_cache h, int layer, const void* q, void* out, hipS
   a.D = D;
   a.t_row0 = h->ctx_mode() ? (int)cur.t0 : 0;
   const float scale = h->cfg.softmax_scale > 0.f ? h->cfg.softmax_scale : 1.0f / std::sqrt((float)D);
-  a.qscale = h->bf16() ? scale * 1.4426950408889634f : scale;
+  a.qscale = scale * 1.4426950408889634f;   // base-2 logits on both paths
   a.rope = h->rope();
   a.sel_slots = h->sel_slots();
   a.slot_base = h->layer_kv(layer);

@@ -1620,8 +1620,17 @@ __global__ __launch_bounds__(64) void attn_merge_kernel(AttnArgs a) {
 // score is 8 FMAs per lane and a sum over the G lanes by DPP moves within
 // the lanes' row (every lane ends with the same value), and the lanes' 8
 // output channels accumulate P V directly.  Workgroup = 256 lanes =
-// 256/G queries of one head; key tiles of 64 in LDS (K rows and V^T rows,
-// padded by one float so the lanes of a query read distinct banks).
+// 256/G queries of one head, over key tiles of 64.
+//
+// Both tiles sit key-major in LDS, so a lane reads its 8 channels of a key
+// as two float4: K rows as they are, V transposed from V^T on the way in,
+// with the 16-byte chunk q of key row j at q ^ (j & (D/4 - 1)) so that the
+// transposing stores (four keys of one channel per lane) spread over the
+// banks.  A lane reads chunks c0/4 and c0/4 + 1 of one row, which the XOR
+// keeps distinct across the lanes of the row.  The next tile of a segment
+// is loaded into registers while the current one is computed.  Logits are
+// base 2 (q carries softmax_scale * log2 e).
+//
 // Sum over aligned groups of G = 8 or 16 lanes: swap neighbours, then pairs,
 // then the two quads of each 8 (row_half_mirror), then the two 8s of each
 // 16 (row_mirror).  Each step adds a value to its partner's, and fp32
@@ -1644,8 +1653,10 @@ __global__ __launch_bounds__(256) void attn_f32_kernel(AttnArgs a) {
   constexpr int G = D / 8;                 // lanes per query
   constexpr int QPB = 256 / G;             // queries per workgroup
   constexpr int BNF = 64;
-  __shared__ float s_kt[BNF][D + 1];
-  __shared__ float s_vt[D][BNF + 1];
+  constexpr int NC = D / 4;                // 16-byte chunks per key row
+  constexpr int NL = BNF * D / 4 / 256;    // float4 loads per lane per operand and tile
+  __shared__ __attribute__((aligned(16))) float s_k4[BNF][D];
+  __shared__ __attribute__((aligned(16))) float s_v4[BNF][D];
   __shared__ const float* s_k[kMaxSeg];
   __shared__ const float* s_v[kMaxSeg];
   __shared__ int s_n[kMaxSeg];
@@ -1703,72 +1714,95 @@ __global__ __launch_bounds__(256) void attn_f32_kernel(AttnArgs a) {
     }
   }
   __syncthreads();
+
+  // a tile's K rows and V^T columns as float4 loads into registers; keys
+  // past nv are not read and enter as 0
+  float4 kl[NL], vl[NL];
+  auto load_tile = [&](const float* kb, const float* vb, int ld, int j0, int nv) {
+#pragma unroll
+    for (int it = 0; it < NL; ++it) {
+      const int idx = it * 256 + tid;
+      const int r = idx / NC, c4 = idx - r * NC;
+      kl[it] = r < nv ? *reinterpret_cast<const float4*>(kb + (size_t)(j0 + r) * D + 4 * c4)
+                      : make_float4(0.f, 0.f, 0.f, 0.f);
+      const int d = idx / (BNF / 4), jj = 4 * (idx - d * (BNF / 4));
+      const float* vp = vb + (size_t)d * ld + j0 + jj;
+      if (jj + 3 < nv) {
+        vl[it] = *reinterpret_cast<const float4*>(vp);
+      } else {
+        vl[it].x = jj < nv ? vp[0] : 0.f;
+        vl[it].y = jj + 1 < nv ? vp[1] : 0.f;
+        vl[it].z = jj + 2 < nv ? vp[2] : 0.f;
+        vl[it].w = 0.f;
+      }
+    }
+  };
+  // chunk position of 16-byte chunk q of key row j
+  auto cpos = [](int j, int qc) { return (qc ^ (j & (NC - 1))) * 4; };
+  auto store_tile = [&]() {
+#pragma unroll
+    for (int it = 0; it < NL; ++it) {
+      const int idx = it * 256 + tid;
+      const int r = idx / NC, c4 = idx - r * NC;
+      *reinterpret_cast<float4*>(&s_k4[r][cpos(r, c4)]) = kl[it];
+      const int d = idx / (BNF / 4), jj = 4 * (idx - d * (BNF / 4));
+      const int qd = d >> 2, e = d & 3;
+      s_v4[jj][cpos(jj, qd) + e] = vl[it].x;
+      s_v4[jj + 1][cpos(jj + 1, qd) + e] = vl[it].y;
+      s_v4[jj + 2][cpos(jj + 2, qd) + e] = vl[it].z;
+      s_v4[jj + 3][cpos(jj + 3, qd) + e] = vl[it].w;
+    }
+  };
+
   float m_run = -INFINITY, l_run = 0.f;
   for (int sg = 0; sg < a.nseg; ++sg) {
     const int n = s_n[sg], ld = s_ld[sg];
     const float* kb = s_k[sg];
     const float* vb = s_v[sg];
+    if (n > 0) load_tile(kb, vb, ld, 0, min(BNF, n));
     for (int j0 = 0; j0 < n; j0 += BNF) {
       const int nv = min(BNF, n - j0);
-      // the tile's K rows and V^T columns as float4 loads, all issued before
-      // the first LDS store; keys past nv are not read and enter as 0
-      constexpr int NL = BNF * D / 4 / 256;   // float4 loads per lane per operand
-      float4 kl[NL], vl[NL];
-#pragma unroll
-      for (int it = 0; it < NL; ++it) {
-        const int idx = it * 256 + tid;
-        const int r = idx / (D / 4), c4 = idx - r * (D / 4);
-        kl[it] = r < nv ? *reinterpret_cast<const float4*>(kb + (size_t)(j0 + r) * D + 4 * c4)
-                        : make_float4(0.f, 0.f, 0.f, 0.f);
-        const int d = idx / (BNF / 4), jj = 4 * (idx - d * (BNF / 4));
-        const float* vp = vb + (size_t)d * ld + j0 + jj;
-        if (jj + 3 < nv) {
-          vl[it] = *reinterpret_cast<const float4*>(vp);
-        } else {
-          vl[it].x = jj < nv ? vp[0] : 0.f;
-          vl[it].y = jj + 1 < nv ? vp[1] : 0.f;
-          vl[it].z = jj + 2 < nv ? vp[2] : 0.f;
-          vl[it].w = 0.f;
-        }
-      }
-#pragma unroll
-      for (int it = 0; it < NL; ++it) {
-        const int idx = it * 256 + tid;
-        const int r = idx / (D / 4), c4 = idx - r * (D / 4);
-        s_kt[r][4 * c4] = kl[it].x;
-        s_kt[r][4 * c4 + 1] = kl[it].y;
-        s_kt[r][4 * c4 + 2] = kl[it].z;
-        s_kt[r][4 * c4 + 3] = kl[it].w;
-        const int d = idx / (BNF / 4), jj = 4 * (idx - d * (BNF / 4));
-        s_vt[d][jj] = vl[it].x;
-        s_vt[d][jj + 1] = vl[it].y;
-        s_vt[d][jj + 2] = vl[it].z;
-        s_vt[d][jj + 3] = vl[it].w;
-      }
+      store_tile();
       __syncthreads();
+      if (j0 + BNF < n) load_tile(kb, vb, ld, j0 + BNF, min(BNF, n - j0 - BNF));   // in flight meanwhile
       float s[BNF];
       float mx = -INFINITY;
 #pragma unroll
       for (int jj = 0; jj < BNF; ++jj) {
-        float acc = 0.f;
-#pragma unroll
-        for (int c = 0; c < 8; ++c) acc = fmaf(q[c], s_kt[jj][c0 + c], acc);
+        const float4 k0 = *reinterpret_cast<const float4*>(&s_k4[jj][cpos(jj, c0 / 4)]);
+        const float4 k1 = *reinterpret_cast<const float4*>(&s_k4[jj][cpos(jj, c0 / 4 + 1)]);
+        float acc = q[0] * k0.x;
+        acc = fmaf(q[1], k0.y, acc);
+        acc = fmaf(q[2], k0.z, acc);
+        acc = fmaf(q[3], k0.w, acc);
+        acc = fmaf(q[4], k1.x, acc);
+        acc = fmaf(q[5], k1.y, acc);
+        acc = fmaf(q[6], k1.z, acc);
+        acc = fmaf(q[7], k1.w, acc);
         acc = group_sum<G>(acc);
         s[jj] = (jj < nv) ? acc : -INFINITY;
         mx = fmaxf(mx, s[jj]);
       }
       const float m_new = fmaxf(m_run, mx);
-      const float alpha = expf(m_run - m_new);
+      const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);
       m_run = m_new;
       l_run *= alpha;
 #pragma unroll
       for (int c = 0; c < 8; ++c) o[c] *= alpha;
 #pragma unroll
       for (int jj = 0; jj < BNF; ++jj) {
-        const float p = expf(s[jj] - m_new);
+        const float p = __builtin_amdgcn_exp2f(s[jj] - m_new);
         l_run += p;
-#pragma unroll
-        for (int c = 0; c < 8; ++c) o[c] = fmaf(p, s_vt[c0 + c][jj], o[c]);
+        const float4 v0 = *reinterpret_cast<const float4*>(&s_v4[jj][cpos(jj, c0 / 4)]);
+        const float4 v1 = *reinterpret_cast<const float4*>(&s_v4[jj][cpos(jj, c0 / 4 + 1)]);
+        o[0] = fmaf(p, v0.x, o[0]);
+        o[1] = fmaf(p, v0.y, o[1]);
+        o[2] = fmaf(p, v0.z, o[2]);
+        o[3] = fmaf(p, v0.w, o[3]);
+        o[4] = fmaf(p, v1.x, o[4]);
+        o[5] = fmaf(p, v1.y, o[5]);
+        o[6] = fmaf(p, v1.z, o[6]);
+        o[7] = fmaf(p, v1.w, o[7]);
       }
       __syncthreads();
     }

@@ -61,7 +61,7 @@ struct AttnArgs {
   void* out;                // [T][H][D]
   int T, H, D;
   int t_row0;               // RoPE t-table row of the current block's frame 0
-  float qscale;             // softmax scale * log2(e) (bf16 path) or softmax scale (fp32 path)
+  float qscale;             // softmax scale * log2(e): the kernels' logits are base 2
   int nseg;
   Rope rope;
   const int* sel_slots;     // device, written by the retrieval kernel
