@@ -173,7 +173,7 @@ def test_export_segments_match_oracle_context():
 
 
 class _GrowingKeys(Run):
-    """Block m's keys scaled by 1 + 0.75 m (rounded to bf16, the same values
+    """Block m's keys scaled by 1 + g m (g = 0.75 unless set; rounded to bf16, the same values
     for the device and the oracle).  Full tiles run in segment order, static
     sink first, so a row's scores rise by several powers of two from tile to
     tile and every row's running max must move within one attend.  Values
@@ -182,12 +182,14 @@ class _GrowingKeys(Run):
     on N(0,1) values would pass the bound, while a missed rescale of O or l
     still moves an output by about |V|, some 0.5."""
 
+    growth = 0.75
+
     def qkv(self, layer, block, step):
         key = (layer, block, step)
         if key not in self._host:
             import torch
             q, k, v = synth.qkv(self.cfg, layer, block, step)
-            k = torch.from_numpy(k * np.float32(1.0 + 0.75 * block)).to(torch.bfloat16).float().numpy()
+            k = torch.from_numpy(k * np.float32(1.0 + self.growth * block)).to(torch.bfloat16).float().numpy()
             self._host[key] = (q, k, v * np.float32(0.125))
         return self._host[key]
 
@@ -212,4 +214,36 @@ def test_running_max_rescales_on_growing_scores(name):
     for m in range(cfg["blocks"]):
         run.open(m)
         _check_block(run, ref, m)
+        run.cache.commit()
+
+
+@pytest.mark.parametrize("name", ["prsink_512", "prsink_512_fp8k", "prsink_512_fp8kv"])
+def test_running_max_rescales_through_overflow(name):
+    """Keys scaled by 1 + 20 m: from block 3 on, the window's scores lie 150
+    to 750 powers of two above the static sink tile that opens each row, so
+    the first pass of exponentials over them overflows to infinity and the
+    rescale must recompute P from the new max.  Scores this large put the
+    softmax outside the range where the bf16 rounding of the rotated keys
+    leaves near-ties to the oracle, so this is a property test: retrieval
+    matches the oracle, every output is finite, and every output channel lies
+    within that channel's range over the context's values, widened by 10% of
+    its largest magnitude for the FP8 roundings of P and V (a missed rescale
+    of O or l leaves outputs at zero or scaled by 2^100 and more)."""
+    cfg = synth.workload(name, heads=2, grid_h=4, grid_w=8, bank=3, blocks=8, pose_dim=16, keyframes=4)
+    run = _GrowingKeys(cfg)
+    run.growth = 20.0
+    ref = oracle.PRSinkReference(cfg, run)
+    for m in range(cfg["blocks"]):
+        run.open(m)
+        sel = run.cache.selection()
+        assert sel == ref.selection(m), m
+        ctx = run.cache.context()                  # (kind, block, tokens, t0) per segment
+        out = run.attend(m, 0, 0).float().cpu().numpy()                  # [T, H, D]
+        assert np.isfinite(out).all(), m
+        vs = np.stack([run.qkv(0, blk, 0)[2] for _, blk, _, _ in ctx])  # [segments, T, H, D]
+        lo, hi = vs.min(axis=(0, 1)), vs.max(axis=(0, 1))                # [H, D]
+        slack = 0.1 * np.abs(vs).max(axis=(0, 1, 3))[:, None]            # [H, 1]
+        assert (out >= lo - slack).all() and (out <= hi + slack).all(), m
+        if m >= 3:                                 # the window dominates: outputs far from zero
+            assert np.abs(out).max() > 0.05 * np.abs(vs).max(), m
         run.cache.commit()
