@@ -22,6 +22,15 @@ Reading taken here:
     (The codes are those of 2^(z_j - e): a whole-number shift of z, not a
     shift by the row max itself, which would change every code.)
 
+  * Comparing a library's FP8-KV output with this reading: the library forms
+    the logits with the FP8 matrix product, whose sum of E4M3 products is not
+    exact, so a P whose exact value lies within that error of a rounding
+    boundary between two E4M3 codes has two valid codes, and no CPU reading
+    can know which one the matrix core's rounding picks.
+    ``attention_fp8_pv_slack`` bounds how far each output may move from such
+    codes; outputs are compared beyond that slack (zero for a row with no
+    such P).
+
 E4M3 (OCP "fn" variant): 1 sign bit, 4 exponent bits with bias 7, 3 mantissa
 bits, no infinities; the largest finite magnitude is 448 and subnormals are
 m * 2^-9 (m = 1..7).  Rounding is to nearest, ties to even.
@@ -109,6 +118,64 @@ def numerators_e4m3(z):
     e = pow2_exponents(P.max(axis=1))[:, None]
     p = np.ldexp(P, -e)                                # exact: a power-of-two scaling
     return e4m3_round(p), p
+
+
+# Bound on the FP8 matrix product's accumulation error in a logit, relative to
+# sum_i |q_i k_i|: the exact product of two E4M3 values fits fp32, but the
+# matrix core's sum of them is not exact.  Measured on MI355X (scaled E4M3
+# matrix product, 128-term dot products of random E4M3 operands): at most
+# 3.2e-5 of sum |q_i k_i|; the bound takes twice that, 2^-14.
+FP8_PRODUCT_REL_ERR = 2.0 ** -14
+
+
+def attention_fp8_pv_slack(q, k, v, rel=FP8_PRODUCT_REL_ERR, rows=None):
+    """``attention_fp8_pv`` together with how far each output may move where
+    the FP8 product's own rounding decides a P code.
+
+    The logit z_j = q . k_j that the product delivers lies within
+    b_j = rel * sum_i |q_i k_ij| of the exact one, so P_j (held as E4M3 under
+    the row's power-of-two scale, ``numerators_e4m3``) may be rounded from any
+    value in [p_j 2^-b_j, p_j 2^b_j].  Rounding is monotone, so the codes it
+    can take run from round(p_j 2^-b_j) to round(p_j 2^b_j); a P away from
+    every rounding boundary has one code, a P within b_j of a boundary two.
+    The output o = sum_j P~_j v_j / sum_j P_j then moves by at most
+    sum_j (round(p_j 2^b_j) - round(p_j 2^-b_j)) |v_j| / sum_j p_j per channel
+    (the denominator sums unrounded P, which moves continuously and is left
+    out).  Returns (o, slack), both [Nq, H, D] fp64."""
+    q = np.asarray(q, np.float64)
+    k = np.asarray(k, np.float64)
+    v = np.asarray(v, np.float64)
+    Nq, H, D = q.shape
+    out = np.zeros((Nq, H, v.shape[-1]), np.float64)
+    slack = np.zeros_like(out)
+    rs = np.arange(Nq) if rows is None else np.asarray(rows)
+    for h in range(H):
+        for c0 in range(0, len(rs), 256):
+            r = rs[c0:c0 + 256]
+            z = q[r, h, :] @ k[:, h, :].T
+            pq, p = numerators_e4m3(z)
+            b = rel * (np.abs(q[r, h, :]) @ np.abs(k[:, h, :]).T)
+            # Only a P whose interval reaches a rounding boundary beside its
+            # code needs rounding again.  Above a code c the next code is one
+            # quantum of c's binade up (none above 448); below, one quantum
+            # down, or half a quantum where c is a power of two (taken there
+            # also at 2^-6, where the true gap is wider); 2^-9 in the subnormal
+            # range.  The boundaries lie half a gap from c, and the tests are
+            # inclusive, so no P with two codes is missed.
+            hi_end, lo_end = p * np.exp2(b), p * np.exp2(-b)
+            frac, ex = np.frexp(np.where(pq > 0, pq, 1.0))
+            quantum = np.where(pq >= 2.0 ** -6, np.ldexp(1.0, ex - 4), 2.0 ** -9)
+            gap_up = np.where(pq >= E4M3_MAX, np.inf, quantum)
+            gap_dn = np.where(pq <= 0.0, np.inf, np.where((frac == 0.5) & (pq >= 2.0 ** -6), 0.5 * quantum, quantum))
+            near = (hi_end >= pq + 0.5 * gap_up) | (lo_end <= pq - 0.5 * gap_dn)
+            step = np.zeros_like(p)
+            if near.any():
+                step[near] = (e4m3_round(np.minimum(hi_end[near], E4M3_MAX)) -
+                              e4m3_round(lo_end[near]))
+            l = p.sum(axis=1, keepdims=True)
+            out[r, h, :] = (pq @ v[:, h, :]) / l
+            slack[r, h, :] = (step @ np.abs(v[:, h, :])) / l
+    return out, slack
 
 
 def attention_fp8_pv(q, k, v, rows=None) -> np.ndarray:

@@ -29,7 +29,9 @@ Readings (beyond those stated in the modules used here):
   * An FP8 KV cache (dtype "bf16_fp8kv"): as the key cache, and V of each
     segment quantised with the same tile rule, and P rounded to E4M3 against
     the exact row max before P V (``fp8.attention_fp8_pv``; the same page's
-    上手实践 notes offer an FP8 KV cache).
+    上手实践 notes offer an FP8 KV cache).  ``attend(..., with_slack=True)``
+    also returns how far each output may move where the FP8 product's own
+    rounding decides a P code (``fp8.attention_fp8_pv_slack``).
   * PR-Sink with reference_frames = R > 0 (the LiveAnimate page, section 方法,
     conditions every block on the reference image; the Live Avatar page's
     abstract recalibrates appearance from a cached reference image): the R
@@ -88,15 +90,15 @@ class _Base:
         t = np.array([t_of_frame(f) for f in self.f_tok[tok]], np.float64)
         return apply_rope(xs, t, self.y_tok[tok], self.x_tok[tok], self.split, self.theta)
 
-    def _attend(self, q_rot, ks, vs, heads, rows):
+    def _attend(self, q_rot, ks, vs, heads, rows, with_slack=False):
         if self.cfg["dtype"] in ("bf16_fp8k", "bf16_fp8kv"):
-            return self._attend_fp8(q_rot, ks, vs, rows)
+            return self._attend_fp8(q_rot, ks, vs, rows, with_slack)
         k = np.concatenate(ks, axis=0)
         v = np.concatenate([np.asarray(x, np.float64) for x in vs], axis=0)
         o_sub = attention(q_rot, k, v, _scale(self.cfg), rows=rows)
-        return o_sub
+        return (o_sub, np.zeros_like(o_sub)) if with_slack else o_sub
 
-    def _attend_fp8(self, q_rot, ks, vs, rows):
+    def _attend_fp8(self, q_rot, ks, vs, rows, with_slack=False):
         """FP8 key (and value) cache: base-2 logits from E4M3 Q (one scale per
         row) and E4M3 K (one scale per 64-token tile of each context segment);
         quantising Q row by row lets the unrequested rows stay zero.  With the
@@ -110,10 +112,13 @@ class _Base:
         k = np.concatenate([fp8.quantize_keys(x) for x in ks], axis=0)
         if self.cfg["dtype"] == "bf16_fp8kv":
             v = np.concatenate([fp8.quantize_values(x) for x in vs], axis=0)
+            if with_slack:
+                return fp8.attention_fp8_pv_slack(q2, k, v, rows=rows)
             return fp8.attention_fp8_pv(q2, k, v, rows=rows)
         v = np.concatenate([np.asarray(x, np.float64) for x in vs], axis=0)
         # exp(q2 . k / log2 e) = 2^(q2 . k): the base-2 logits
-        return attention(q2 / log2e, k, v, 1.0, rows=rows)
+        o = attention(q2 / log2e, k, v, 1.0, rows=rows)
+        return (o, np.zeros_like(o)) if with_slack else o
 
 
 class PRSinkReference(_Base):
@@ -175,8 +180,11 @@ class PRSinkReference(_Base):
             out.append((kind, b, kr, np.asarray(v, np.float64)[:, heads, :]))
         return out
 
-    def attend(self, m: int, layer: int, step: int, heads=None, rows=None, selection=None):
-        """Output [T, len(heads), D] fp64 of block m at (layer, step)."""
+    def attend(self, m: int, layer: int, step: int, heads=None, rows=None, selection=None, with_slack=False):
+        """Output [T, len(heads), D] fp64 of block m at (layer, step).  With
+        ``with_slack``, (output, slack): how far each output may move where the
+        FP8 product's rounding decides a P code (``fp8.attention_fp8_pv_slack``;
+        zeros for the dtypes without an FP8 P)."""
         H = self.cfg["heads"]
         heads = list(range(H)) if heads is None else list(heads)
         if selection is None:
@@ -185,7 +193,7 @@ class PRSinkReference(_Base):
         q, _, _ = self.p.qkv(layer, m, step)
         q_rot = self._rot(q, lambda f: t0 + f, heads)
         kv = self.context_kv(m, layer, step, heads, selection)
-        return self._attend(q_rot, [x[2] for x in kv], [x[3] for x in kv], heads, rows)
+        return self._attend(q_rot, [x[2] for x in kv], [x[3] for x in kv], heads, rows, with_slack)
 
 
 class ConvKVReference(_Base):
@@ -260,11 +268,13 @@ class ConvKVReference(_Base):
         out.append(("current", m, kr, np.asarray(v, np.float64)[:, heads, :]))
         return out
 
-    def attend(self, m: int, layer: int, step: int, heads=None, rows=None):
+    def attend(self, m: int, layer: int, step: int, heads=None, rows=None, with_slack=False):
+        """Output [T, len(heads), D] fp64 of block m at (layer, step); with
+        ``with_slack``, (output, slack) as for PR-Sink."""
         H = self.cfg["heads"]
         heads = list(range(H)) if heads is None else list(heads)
         t0 = self.positions(m)[1]
         q, _, _ = self.p.qkv(layer, m, step)
         q_rot = self._rot(q, lambda f: t0 + f, heads)
         kv = self.context_kv(m, layer, step, heads)
-        return self._attend(q_rot, [x[2] for x in kv], [x[3] for x in kv], heads, rows)
+        return self._attend(q_rot, [x[2] for x in kv], [x[3] for x in kv], heads, rows, with_slack)

@@ -98,10 +98,48 @@ class Run:
 
 
 def max_err(got, want, heads=None, rows=None):
+    """Largest |got - want|.  ``want`` may be the oracle's (output, slack)
+    pair (``attend(..., with_slack=True)``): then the largest amount by which
+    |got - want| exceeds the slack, i.e. the error left once every P code that
+    the FP8 product's rounding may decide either way has been allowed its other
+    value.  Where the slack is zero this is the plain error."""
+    slack = None
+    if isinstance(want, tuple):
+        want, slack = want
     g = got.float().cpu().numpy().astype(np.float64)
     if heads is not None:
         g = g[:, heads, :]
     if rows is not None:
         g = g[rows]
         want = want[rows]
-    return float(np.max(np.abs(g - want))) if g.size else 0.0
+        slack = None if slack is None else slack[rows]
+    if not g.size:
+        return 0.0
+    d = np.abs(g - want)
+    return float(np.max(d if slack is None else d - slack))
+
+
+def oracle_err(got, attend, heads=None, rows=None, tol=None):
+    """max_err of ``got`` against the oracle's ``attend(rows=...)`` (a callable
+    taking the reference's ``rows`` and ``with_slack`` keywords).  Rows whose
+    error exceeds ``tol`` are compared again beyond the oracle's slack
+    (``attend(rows=those, with_slack=True)``; zero slack, and so the same
+    error, for the dtypes without an FP8 P): the slack is computed only where
+    it is needed."""
+    want = attend(rows=rows)
+    g = got.float().cpu().numpy().astype(np.float64)
+    if heads is not None:
+        g = g[:, heads, :]
+    rs = np.arange(g.shape[0]) if rows is None else np.asarray(rows)
+    if not rs.size:
+        return 0.0
+    row_err = np.max(np.abs(g[rs] - want[rs]), axis=tuple(range(1, g.ndim)))
+    err = float(np.max(row_err))
+    if tol is None or err <= tol:
+        return err
+    bad = rs[row_err > tol]
+    want2, slack = attend(rows=bad, with_slack=True)
+    excess = float(np.max(np.abs(g[bad] - want2[bad]) - slack[bad]))
+    good = row_err[row_err <= tol]
+    return max(excess, float(np.max(good)) if good.size else 0.0)
+

@@ -658,3 +658,51 @@ def check_convkv_memory_cached_dtype(Ref, conv_memory, bf16_round, make_cfg, mak
             assert np.array_equal(bf16_round(mv[0]), mv[0])
         else:
             assert np.array_equal(mk[0], exact)
+
+
+def check_fp8_pv_slack(slack_fn, pv_fn):
+    """How far an FP8-KV output may move where the FP8 product's rounding
+    decides a P code (``slack_fn(q, k, v, rel) -> (o, slack)``), worked by
+    hand.
+
+    One query row, base-2 logits z = (8, log2 248, 4) through q = (1), value
+    rows the unit vectors.  The largest P is 256, so the row's scale is 2^0
+    and p = (256, 248, 16).  256 and 16 are codes, their neighbouring rounding
+    boundaries 248/272 and 15.5/17 at least 1.5% away; 248 is itself the
+    boundary between the codes 240 and 256 (fp64's 2^log2(248) may land a
+    hair either side).  With any rel > 0 the middle key's P has both codes,
+    one step of 16 apart, so slack = (0, 16, 0) / (256 + p1 + 16) and o is
+    (256, 240 or 256, 16) / l; with rel = 0 every slack is zero and o is
+    ``pv_fn``'s.
+
+    The bound grows with sum_i |q_i k_i|, not with |z|: q = (1, 1) and
+    k = (z + 10, -10) give the same z = log2(1.01 * 248) (P 1% above the
+    boundary, 250.48, which rounds to 256) but sum |q k| = |z| + 20.  The
+    other code needs a bound of log2(1.01) = 0.01436 in z: rel = 7e-4 gives
+    7e-4 (7.97 + 20) = 0.0196 (slack), while 7e-4 |z| = 0.0056 would not.
+
+    Channels weigh |v|: a value row (-1, 2) gives slack step * (1, 2) / l."""
+    q = np.ones((1, 1, 1))
+    z = np.array([8.0, np.log2(248.0), 4.0])
+    k = z.reshape(3, 1, 1)
+    v = np.eye(3).reshape(3, 1, 3)
+    p1 = float(np.exp2(z[1]))
+    assert abs(p1 - 248.0) < 1e-12
+    l = 256.0 + p1 + 16.0
+    o, s = slack_fn(q, k, v, 2.0 ** -14)
+    assert np.allclose(s[0, 0], [0.0, 16.0 / l, 0.0], rtol=1e-14, atol=0), s
+    assert np.isclose(o[0, 0, 0], 256.0 / l, rtol=1e-14) and np.isclose(o[0, 0, 2], 16.0 / l, rtol=1e-14), o
+    assert min(abs(o[0, 0, 1] - 240.0 / l), abs(o[0, 0, 1] - 256.0 / l)) < 1e-15, o
+    o0, s0 = slack_fn(q, k, v, 0.0)
+    assert np.all(s0 == 0.0) and np.allclose(o0, pv_fn(q, k, v), rtol=1e-15, atol=0)
+
+    zt = float(np.log2(1.01 * 248.0))
+    q2 = np.ones((1, 1, 2))
+    k2 = np.array([[zt + 10.0, -10.0], [0.0, 0.0]]).reshape(2, 1, 2)     # second key: z = 0, P = 1
+    v2 = np.array([[-1.0, 2.0], [0.0, 0.0]]).reshape(2, 1, 2)
+    P = np.array([2.0 ** zt, 1.0])
+    l2 = P.sum()                                                      # scale 2^0: p = P
+    _, s_small = slack_fn(q2, k2, v2, 1e-4)                           # 1e-4 * 27.97 = 0.0028 < 0.01436
+    assert np.all(s_small == 0.0), s_small
+    _, s_mid = slack_fn(q2, k2, v2, 7e-4)
+    assert np.allclose(s_mid[0, 0], np.array([1.0, 2.0]) * 16.0 / l2, rtol=1e-12, atol=0), s_mid

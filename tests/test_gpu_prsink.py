@@ -7,7 +7,7 @@ import pytest
 
 import oracle
 from bounded_kv_block_amd import synth
-from gpu_helpers import TOL, Run, max_err
+from gpu_helpers import TOL, Run, max_err, oracle_err
 
 pytestmark = pytest.mark.gpu
 
@@ -22,8 +22,8 @@ def _check_block(run, ref, m, layer=0, step=0, heads=None, rows=None, out=None):
     assert ctx == [(k, b, t, t0) for k, b, t, t0 in want_ctx], (m, ctx, want_ctx)
     if out is None:
         out = run.attend(m, layer, step)
-    want = ref.attend(m, layer, step, heads=heads, rows=rows, selection=want_sel)
-    err = max_err(out, want, heads, rows)
+    err = oracle_err(out, lambda **kw: ref.attend(m, layer, step, heads=heads, selection=want_sel, **kw),
+                     heads, rows, TOL[cfg["dtype"]])
     print(f"block {m} layer {layer} step {step}: keys {sum(c[2] for c in ctx)} max|err| {err:.3e}", flush=True)
     assert err <= TOL[cfg["dtype"]], (m, err)
     return out

@@ -391,6 +391,38 @@ def test_fp8_pv_row_scale_hand_worked():
     pins.check_fp8_pv_row_scale(oracle.fp8.attention_fp8_pv)
 
 
+def test_fp8_pv_slack_hand_worked():
+    pins.check_fp8_pv_slack(lambda q, k, v, rel: oracle.fp8.attention_fp8_pv_slack(q, k, v, rel),
+                            oracle.fp8.attention_fp8_pv)
+
+
+def test_fp8kv_stream_slack_beside_the_output():
+    """``attend(..., with_slack=True)`` returns the very output of ``attend``
+    and a slack that is zero for the dtypes without an FP8 P."""
+    from bounded_kv_block_amd import synth
+
+    class Prov:
+        def __init__(self, cfg):
+            self.cfg, self.p = cfg, synth.poses(cfg, cfg["blocks"])
+
+        def qkv(self, layer, block, step):
+            return synth.qkv(self.cfg, layer, block, step)
+
+        def pose(self, b):
+            return self.p[b]
+
+    for dtype in ("bf16", "bf16_fp8k", "bf16_fp8kv"):
+        cfg = synth.workload("prsink_512", dtype=dtype, heads=2, frames=1, grid_h=3, grid_w=5, bank=2, blocks=6,
+                             pose_dim=8, keyframes=3)
+        ref = oracle.PRSinkReference(cfg, Prov(cfg))
+        for m in (0, 5):
+            o = ref.attend(m, 0, 0)
+            o2, s = ref.attend(m, 0, 0, with_slack=True)
+            assert np.array_equal(o, o2) and s.shape == o.shape and np.all(s >= 0)
+            if dtype != "bf16_fp8kv":
+                assert np.all(s == 0)
+
+
 def test_convkv_memory_is_held_in_the_cache_dtype():
     from oracle.projection import bf16_round
     pins.check_convkv_memory_cached_dtype(

@@ -434,7 +434,7 @@ def test_pose_bank_mutants_fail(mutant):
 class _Fp8Unscaled(oracle.ConvKVReference):
     """Keys rounded to E4M3 as they are (no per-tile power-of-two scale)."""
 
-    def _attend_fp8(self, q_rot, ks, vs, rows):
+    def _attend_fp8(self, q_rot, ks, vs, rows, with_slack=False):
         log2e = 1.0 / np.log(2.0)
         s = 1.0 / np.sqrt(self.cfg["head_dim"])
         rs = np.arange(self.T) if rows is None else np.asarray(rows)
@@ -456,7 +456,7 @@ def test_fp8_stream_mutant_fails():
 class _Fp8QNoLog2e(oracle.PRSinkReference):
     """Q quantised without the log2 e factor (natural-unit logits)."""
 
-    def _attend_fp8(self, q_rot, ks, vs, rows):
+    def _attend_fp8(self, q_rot, ks, vs, rows, with_slack=False):
         s = self.cfg.get("softmax_scale", 0.0) or 1.0 / np.sqrt(self.cfg["head_dim"])
         qe = oracle.fp8.quantize_queries(q_rot * s)
         k = np.concatenate([oracle.fp8.quantize_keys(x) for x in ks], axis=0)
@@ -470,14 +470,14 @@ class _Fp8QNoLog2e(oracle.PRSinkReference):
 class _Fp8KTilesConcat(oracle.PRSinkReference):
     """K tiles counted over the concatenated context, not per segment."""
 
-    def _attend_fp8(self, q_rot, ks, vs, rows):
+    def _attend_fp8(self, q_rot, ks, vs, rows, with_slack=False):
         return super()._attend_fp8(q_rot, [np.concatenate(ks, axis=0)], vs, rows)
 
 
 class _Fp8VTilesConcat(oracle.PRSinkReference):
     """V tiles counted over the concatenated context, not per segment."""
 
-    def _attend_fp8(self, q_rot, ks, vs, rows):
+    def _attend_fp8(self, q_rot, ks, vs, rows, with_slack=False):
         return super()._attend_fp8(q_rot, ks, [np.concatenate(vs, axis=0)], rows)
 
 
@@ -593,3 +593,36 @@ def test_convkv_memory_dtype_mutant_fails():
                   lambda dt: synth.workload("convkv_512", dtype=dt, heads=2, grid_h=2, grid_w=3, blocks=7,
                                             rope=(0, 0, 0) if dt == "f32" else (44, 42, 42)),
                   SynthProvider)
+
+
+# -- FP8-KV slack mutants -------------------------------------------------------
+def _slack_copy(q, k, v, rel, bound="sum_abs", weigh="abs", step_scale=1.0):
+    """A copy of fp8.attention_fp8_pv_slack with one planted mistake."""
+    F = oracle.fp8
+    q = np.asarray(q, np.float64)
+    k = np.asarray(k, np.float64)
+    v = np.asarray(v, np.float64)
+    out = np.zeros((q.shape[0], q.shape[1], v.shape[-1]))
+    slack = np.zeros_like(out)
+    for h in range(q.shape[1]):
+        z = q[:, h, :] @ k[:, h, :].T
+        pq, p = F.numerators_e4m3(z)
+        b = rel * (np.abs(q[:, h, :]) @ np.abs(k[:, h, :]).T if bound == "sum_abs" else np.abs(z))
+        lo = F.e4m3_round(p * np.exp2(-b))
+        hi = F.e4m3_round(np.minimum(p * np.exp2(b), F.E4M3_MAX))
+        l = p.sum(axis=1, keepdims=True)
+        out[:, h, :] = (pq @ v[:, h, :]) / l
+        w = np.abs(v[:, h, :]) if weigh == "abs" else v[:, h, :]
+        slack[:, h, :] = step_scale * ((hi - lo) @ w) / l
+    return out, slack
+
+
+@pytest.mark.parametrize("mutant", [
+    lambda q, k, v, rel: _slack_copy(q, k, v, rel, bound="abs_z"),      # bound from |z| alone
+    lambda q, k, v, rel: _slack_copy(q, k, v, rel, weigh="signed"),     # signed values
+    lambda q, k, v, rel: _slack_copy(q, k, v, rel, step_scale=0.5),     # half a code step
+], ids=["bound-from-z", "signed-v", "half-step"])
+def test_fp8_pv_slack_mutants_fail(mutant):
+    # the faithful copy passes, so each failure below is its planted mistake
+    pins.check_fp8_pv_slack(lambda q, k, v, rel: _slack_copy(q, k, v, rel), oracle.fp8.attention_fp8_pv)
+    assert _fails(pins.check_fp8_pv_slack, mutant, oracle.fp8.attention_fp8_pv)
