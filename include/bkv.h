@@ -75,8 +75,9 @@ typedef enum { BKV_PR_SINK = 0, BKV_CONVKV = 1 } bkv_mode;
    smallest integer with max|K~| * 2^-e <= 448 (0 for an all-zero tile),
    clamped to [-120, 120]; Q after RoPE, times softmax_scale * log2(e), is
    quantised the same way with one scale per (token, head); the logits Q K^T
-   are formed from these E4M3 values (the products are exact, accumulated in
-   fp32); softmax and P V are as for BKV_BF16.  PR-Sink with absolute
+   are formed from these E4M3 values on the scaled FP8 matrix instruction
+   (each product is exact; the matrix core's sum of them is not, measured
+   within 3.2e-5 of sum |q_i k_i|); softmax and P V are as for BKV_BF16.  PR-Sink with absolute
    positions stores the E4M3 K in the slots (cache bytes per token and head:
    128 (K) + 256 (V) + 4/64).  ConvKV and context-relative PR-Sink keep raw
    bf16 K in the slots (the conv and the per-block rotation read it) and
@@ -92,7 +93,9 @@ typedef enum { BKV_PR_SINK = 0, BKV_CONVKV = 1 } bkv_mode;
    moves its running max by whole numbers only, starting each row's largest
    P in (4, 8], so its P codes are the row's own: E4M3 rounds alike at every
    power of two, and the lower scale changes only values in its subnormal
-   range, 2^9 below the row's largest P.  Cache bytes per token and head: 128 (K) +
+   range, 2^9 below the row's largest P.  A P whose exact value lies within
+   the logit's summation error of a rounding boundary between two codes may
+   take either code.  Cache bytes per token and head: 128 (K) +
    128 (V) + 8/64 (exponents); ConvKV slots also keep the raw bf16 V the conv
    reads. */
 typedef enum { BKV_F32 = 0, BKV_BF16 = 1, BKV_BF16_FP8K = 2, BKV_BF16_FP8KV = 3 } bkv_dtype;
