@@ -391,8 +391,11 @@ __device__ __forceinline__ int e4m3_exponent(float a) {
 
 // Four fp32 values (already divided by the scale) -> four E4M3 bytes, first
 // value in the low byte; v_cvt_pk_fp8_f32 rounds to nearest, ties to even.
+// The first convert writes the low half-word and keeps the high one from
+// its third operand, which the second convert then overwrites: x0's own bits
+// serve, so the result can take x0's register and none is cleared for it.
 __device__ __forceinline__ int e4m3_pack4(float x0, float x1, float x2, float x3) {
-  int w = __builtin_amdgcn_cvt_pk_fp8_f32(x0, x1, 0, false);
+  int w = __builtin_amdgcn_cvt_pk_fp8_f32(x0, x1, __float_as_int(x0), false);
   return __builtin_amdgcn_cvt_pk_fp8_f32(x2, x3, w, true);
 }
 
