@@ -17,7 +17,10 @@ The default workload is the 720x416-shaped stream (3510 queries per block,
 one block of 120 attends.  `--workload prsink_long` runs its whole 1080-block
 stream (unless --steps is given) and reports the per-block latency
 distribution over it: p50, p99, the least-squares slope over block index and
-whether the workspace and torch's device allocation stayed constant.
+whether the workspace and torch's device allocation stayed constant.  It runs
+the stream once untimed first and resets the cache: on a fresh GPU the clock
+settles over the first second or so of sustained load, which moves per-block
+latency by a percent or two with time, not with the stream's length.
 
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
 """
@@ -323,6 +326,11 @@ def main():
         cache.commit()
 
     m = 0
+    if long_stream:                                # settling pass, then back to block 0
+        for mm in range(n_blocks):
+            step(mm)
+        torch.cuda.synchronize()
+        cache.reset()
     for _ in range(prefix + args.warmup):          # fill the cache, then warm up
         step(m)
         m += 1
