@@ -4,7 +4,9 @@ point, gives bit-identical outputs on every block -- first a 1800-query,
 40-head stream (320 units: the split launch cuts the 64 remaining units
 into 4 key parts, 256 part states in the static array), then a smaller
 1600-query, 44-head one (308 units: 52 remaining, 4 parts, 208 states), so
-the second reads only what it wrote over the first's leftovers."""
+the second reads only what it wrote over the first's leftovers.  Then the
+FP8 KV cache and ConvKV on the first shape, whose split launches use the same
+array."""
 import numpy as np
 import pytest
 
@@ -32,3 +34,5 @@ def _pair(cfg):
 def test_static_scratch_attend_matches_attend_two_calls():
     _pair(synth.workload("prsink_512", frames=2, grid_h=30, grid_w=30, blocks=7))
     _pair(synth.workload("prsink_512", heads=44, frames=2, grid_h=20, grid_w=40, blocks=7))
+    _pair(synth.workload("prsink_512_fp8kv", frames=2, grid_h=30, grid_w=30, blocks=7))
+    _pair(synth.workload("convkv_512", frames=2, grid_h=30, grid_w=30, blocks=9))
