@@ -654,8 +654,10 @@ __device__ __forceinline__ i32x4 buffer_rsrc(const char* base) {
 // writes m0 itself and knows it is live; the s_nop separates that write from
 // the load that reads it.
 __device__ __forceinline__ void dma16(i32x4 rsrc, unsigned voff, unsigned soff, unsigned lds_base) {
-  // every scalar operand must sit in SGPRs, never a folded literal
-  asm volatile("" : "+s"(soff), "+s"(rsrc), "+s"(lds_base));
+  // the scalar offset must sit in an SGPR, never a folded literal (the
+  // descriptor and the LDS address come from registers anyway; marking them
+  // as rewritten here would make the compiler copy them for every load)
+  asm volatile("" : "+s"(soff));
   asm volatile(
       "s_nop 0\n\t"
       "buffer_load_dwordx4 %0, %1, %2 offen lds"
@@ -2113,11 +2115,10 @@ void qkv_gemm_kernel(QkvArgs a) {
   const unsigned lds0 = (unsigned)(uintptr_t)(lds_ptr_t)lds;
   const int S = C / GK;
   // load j (0..7) of step s: operand j >> 2 (W, x), i = (j >> 1) & 1, slot k = j & 1
-  auto issue_one = [&](int s, int j) {
+  auto issue_one = [&](int s, int j) {       // loading waves only
     const unsigned base = __builtin_amdgcn_readfirstlane(lds0 + (unsigned)(s & (GSTAGE - 1)) * 2 * G_OPB);
     const unsigned soff = __builtin_amdgcn_readfirstlane((unsigned)s * GK * 2u);
     const int i = (j >> 1) & 1, k = j & 1, w = (wave & 3) + 4 * k;
-    if (!loader) return;
     if (j < 4) dma16(rw, vw[i][k], soff, base + (8 * i + w) * 1024);
     else dma16(rx, vx[i][k], soff, base + G_OPB + (8 * i + w) * 1024);
   };
@@ -2150,34 +2151,41 @@ void qkv_gemm_kernel(QkvArgs a) {
 #pragma unroll
     for (int bn = 0; bn < 2; ++bn) bx[bn] = frag(B, 64 * wt + 32 * bn + col, 2 * ss + hh);
   };
-  // eight MFMAs; with load_step >= 0, loads load_j0 .. load_j0 + 3 of that
-  // step go in after MFMAs 1, 3, 5, 7 (loading waves only)
-  auto mfma_half = [&](const bf16x8 (&af)[4], const bf16x8 (&bx)[2], int load_step, int load_j0) {
+  // eight MFMAs; with loads (a compile-time choice: loading waves, steps
+  // with a step left to load), loads load_j0 .. load_j0 + 3 of load_step go
+  // in after MFMAs 1, 3, 5, 7
+  auto mfma_half = [&](const bf16x8 (&af)[4], const bf16x8 (&bx)[2], int load_step, int load_j0, auto loads) {
 #pragma unroll
     for (int bm = 0; bm < 4; ++bm)
 #pragma unroll
       for (int bn = 0; bn < 2; ++bn) {
         acc[bm][bn] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[bm], bx[bn], acc[bm][bn], 0, 0, 0);
-        if (load_step >= 0 && bn == 1) {
-          __builtin_amdgcn_sched_barrier(0);
-          issue_one(load_step, load_j0 + bm);
-          __builtin_amdgcn_sched_barrier(0);
+        if constexpr (decltype(loads)::value) {
+          if (bn == 1) {
+            __builtin_amdgcn_sched_barrier(0);
+            issue_one(load_step, load_j0 + bm);
+            __builtin_amdgcn_sched_barrier(0);
+          }
         }
       }
   };
   bf16x8 a0[4], b0[2], a1[4], b1[2];
-  issue(0);
-  if (S > 1) issue(1);
-  if (S > 2) issue(2);
+  if (loader) {
+    issue(0);
+    if (S > 1) issue(1);
+    if (S > 2) issue(2);
+  }
   // this wave's chunks of step 0 have landed
   if (S > 2) asm volatile("s_waitcnt vmcnt(16)" ::: "memory");
   else if (S > 1) asm volatile("s_waitcnt vmcnt(8)" ::: "memory");
   else asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
   wg_barrier();
   read_half(0, 0, a0, b0);
-  for (int s = 0; s < S; ++s) {
+  // step s; with_loads: step s+3 exists and this wave loads (the steady
+  // steps of a loading wave: no run-time test around any load)
+  auto step = [&](int s, auto with_loads) {
     read_half(s, 1, a1, b1);
-    mfma_half(a0, b0, s + 3 < S ? s + 3 : -1, 0);
+    mfma_half(a0, b0, s + 3, 0, with_loads);
     if (s + 1 < S) {
       // this wave's chunks of step s+1 have landed (step s+2 may be in flight)
       // loads after step s+1's: step s+2 (8) and the first 4 of step s+3
@@ -2187,8 +2195,12 @@ void qkv_gemm_kernel(QkvArgs a) {
       wg_barrier();
       read_half(s + 1, 0, a0, b0);
     }
-    mfma_half(a1, b1, s + 3 < S ? s + 3 : -1, 4);
-  }
+    mfma_half(a1, b1, s + 3, 4, with_loads);
+  };
+  int s = 0;
+  if (loader)
+    for (; s + 3 < S; ++s) step(s, std::true_type{});
+  for (; s < S; ++s) step(s, std::false_type{});
 
   // epilogue: + bias; q -> scratch [T][H][D]; k -> (raw copy,) RoPE -> cache
   // rows; v -> V^T.  A 32-feature block lies in one head of one of q, k, v.
