@@ -1653,20 +1653,34 @@ __device__ __forceinline__ float group_sum(float x) {
   return x;
 }
 
+// Key groups: with D = 64 a workgroup holds KG = 2 groups of 256 lanes over
+// the same queries, one wave of each on every SIMD.  The context's key tiles
+// are numbered in segment order and dealt round-robin, tile f to group
+// f mod KG, so each group runs half of the tiles with its own LDS tiles and
+// its own running (m, l, O); at the end group 1 hands its state to group 0
+// through LDS, which combines the two (m = the larger max, O and l summed
+// with weights 2^(m_g - m)) and writes the output.  Both groups pass every
+// barrier: a round in which a group has no tile left skips only its work.
+// D = 128 needs more than half of a SIMD's registers per wave, so it keeps
+// one group.
 template <int D>
-__global__ __launch_bounds__(256) void attn_f32_kernel(AttnArgs a) {
+__global__ __launch_bounds__(D == 64 ? 512 : 256) void attn_f32_kernel(AttnArgs a) {
   constexpr int G = D / 8;                 // lanes per query
   constexpr int QPB = 256 / G;             // queries per workgroup
+  constexpr int KG = D == 64 ? 2 : 1;      // key groups of 256 lanes
   constexpr int BNF = 64;
   constexpr int NC = D / 4;                // 16-byte chunks per key row
   constexpr int NL = BNF * D / 4 / 256;    // float4 loads per lane per operand and tile
-  __shared__ __attribute__((aligned(16))) float s_k4[BNF][D];
-  __shared__ __attribute__((aligned(16))) float s_v4[BNF][D];
+  static_assert(KG == 1 || 10 * 256 <= KG * BNF * D, "the merge state (m, l, 8 O per lane) fits the K tiles");
+  __shared__ __attribute__((aligned(16))) float s_k4[KG][BNF][D];
+  __shared__ __attribute__((aligned(16))) float s_v4[KG][BNF][D];
   __shared__ const float* s_k[kMaxSeg];
   __shared__ const float* s_v[kMaxSeg];
   __shared__ int s_n[kMaxSeg];
   __shared__ int s_ld[kMaxSeg];
   const int tid = threadIdx.x;
+  const int kg = __builtin_amdgcn_readfirstlane(tid >> 8);   // key group
+  const int gt = tid & 255;                // lane within the group
   const int nqt = (a.T + QPB - 1) / QPB;
   const int head = blockIdx.x / nqt, qt = blockIdx.x - head * nqt;
   if (tid < a.nseg) {
@@ -1698,8 +1712,8 @@ __global__ __launch_bounds__(256) void attn_f32_kernel(AttnArgs a) {
     s_n[tid] = sg.n;
     s_ld[tid] = ld;
   }
-  const int sub = tid % G, c0 = 8 * sub;   // this lane's channels c0 .. c0 + 7
-  const int qrow = qt * QPB + tid / G;
+  const int sub = gt % G, c0 = 8 * sub;    // this lane's channels c0 .. c0 + 7
+  const int qrow = qt * QPB + gt / G;
   const bool valid = qrow < a.T;
   float q[8], o[8];
   {
@@ -1720,13 +1734,15 @@ __global__ __launch_bounds__(256) void attn_f32_kernel(AttnArgs a) {
   }
   __syncthreads();
 
+  float (*const tk)[D] = s_k4[kg];
+  float (*const tv)[D] = s_v4[kg];
   // a tile's K rows and V^T columns as float4 loads into registers; keys
   // past nv are not read and enter as 0
   float4 kl[NL], vl[NL];
   auto load_tile = [&](const float* kb, const float* vb, int ld, int j0, int nv) {
 #pragma unroll
     for (int it = 0; it < NL; ++it) {
-      const int idx = it * 256 + tid;
+      const int idx = it * 256 + gt;
       const int r = idx / NC, c4 = idx - r * NC;
       kl[it] = r < nv ? *reinterpret_cast<const float4*>(kb + (size_t)(j0 + r) * D + 4 * c4)
                       : make_float4(0.f, 0.f, 0.f, 0.f);
@@ -1747,35 +1763,56 @@ __global__ __launch_bounds__(256) void attn_f32_kernel(AttnArgs a) {
   auto store_tile = [&]() {
 #pragma unroll
     for (int it = 0; it < NL; ++it) {
-      const int idx = it * 256 + tid;
+      const int idx = it * 256 + gt;
       const int r = idx / NC, c4 = idx - r * NC;
-      *reinterpret_cast<float4*>(&s_k4[r][cpos(r, c4)]) = kl[it];
+      *reinterpret_cast<float4*>(&tk[r][cpos(r, c4)]) = kl[it];
       const int d = idx / (BNF / 4), jj = 4 * (idx - d * (BNF / 4));
       const int qd = d >> 2, e = d & 3;
-      s_v4[jj][cpos(jj, qd) + e] = vl[it].x;
-      s_v4[jj + 1][cpos(jj + 1, qd) + e] = vl[it].y;
-      s_v4[jj + 2][cpos(jj + 2, qd) + e] = vl[it].z;
-      s_v4[jj + 3][cpos(jj + 3, qd) + e] = vl[it].w;
+      tv[jj][cpos(jj, qd) + e] = vl[it].x;
+      tv[jj + 1][cpos(jj + 1, qd) + e] = vl[it].y;
+      tv[jj + 2][cpos(jj + 2, qd) + e] = vl[it].z;
+      tv[jj + 3][cpos(jj + 3, qd) + e] = vl[it].w;
     }
   };
+  // tile cursor in segment order: (segment, first key); sg == nseg past the end
+  const int nseg = a.nseg;
+  auto skip_empty = [&](int& sg, int& j0) {
+    while (sg < nseg && j0 >= s_n[sg]) {
+      ++sg;
+      j0 = 0;
+    }
+  };
+  auto advance = [&](int& sg, int& j0, int k) {     // k tiles on
+    for (int i = 0; i < k && sg < nseg; ++i) {
+      j0 += BNF;
+      skip_empty(sg, j0);
+    }
+  };
+  int ntiles = 0;                          // context tiles, all segments
+  for (int g = 0; g < nseg; ++g) ntiles += (s_n[g] + BNF - 1) / BNF;
+  const int rounds = (ntiles + KG - 1) / KG;
+
+  int csg = 0, cj0 = 0;                    // this group's tile of the current round
+  skip_empty(csg, cj0);
+  advance(csg, cj0, kg);
+  if (csg < nseg) load_tile(s_k[csg], s_v[csg], s_ld[csg], cj0, min(BNF, s_n[csg] - cj0));
 
   float m_run = -INFINITY, l_run = 0.f;
-  for (int sg = 0; sg < a.nseg; ++sg) {
-    const int n = s_n[sg], ld = s_ld[sg];
-    const float* kb = s_k[sg];
-    const float* vb = s_v[sg];
-    if (n > 0) load_tile(kb, vb, ld, 0, min(BNF, n));
-    for (int j0 = 0; j0 < n; j0 += BNF) {
-      const int nv = min(BNF, n - j0);
-      store_tile();
-      __syncthreads();
-      if (j0 + BNF < n) load_tile(kb, vb, ld, j0 + BNF, min(BNF, n - j0 - BNF));   // in flight meanwhile
+  for (int r = 0; r < rounds; ++r) {
+    const bool have = csg < nseg;
+    const int nv = have ? min(BNF, s_n[csg] - cj0) : 0;
+    if (have) store_tile();
+    __syncthreads();
+    int nsg = csg, nj0 = cj0;              // the group's tile of the next round
+    advance(nsg, nj0, KG);
+    if (nsg < nseg) load_tile(s_k[nsg], s_v[nsg], s_ld[nsg], nj0, min(BNF, s_n[nsg] - nj0));   // in flight meanwhile
+    if (have) {
       float s[BNF];
       float mx = -INFINITY;
 #pragma unroll
       for (int jj = 0; jj < BNF; ++jj) {
-        const float4 k0 = *reinterpret_cast<const float4*>(&s_k4[jj][cpos(jj, c0 / 4)]);
-        const float4 k1 = *reinterpret_cast<const float4*>(&s_k4[jj][cpos(jj, c0 / 4 + 1)]);
+        const float4 k0 = *reinterpret_cast<const float4*>(&tk[jj][cpos(jj, c0 / 4)]);
+        const float4 k1 = *reinterpret_cast<const float4*>(&tk[jj][cpos(jj, c0 / 4 + 1)]);
         float acc = q[0] * k0.x;
         acc = fmaf(q[1], k0.y, acc);
         acc = fmaf(q[2], k0.z, acc);
@@ -1798,8 +1835,8 @@ __global__ __launch_bounds__(256) void attn_f32_kernel(AttnArgs a) {
       for (int jj = 0; jj < BNF; ++jj) {
         const float p = __builtin_amdgcn_exp2f(s[jj] - m_new);
         l_run += p;
-        const float4 v0 = *reinterpret_cast<const float4*>(&s_v4[jj][cpos(jj, c0 / 4)]);
-        const float4 v1 = *reinterpret_cast<const float4*>(&s_v4[jj][cpos(jj, c0 / 4 + 1)]);
+        const float4 v0 = *reinterpret_cast<const float4*>(&tv[jj][cpos(jj, c0 / 4)]);
+        const float4 v1 = *reinterpret_cast<const float4*>(&tv[jj][cpos(jj, c0 / 4 + 1)]);
         o[0] = fmaf(p, v0.x, o[0]);
         o[1] = fmaf(p, v0.y, o[1]);
         o[2] = fmaf(p, v0.z, o[2]);
@@ -1809,8 +1846,29 @@ __global__ __launch_bounds__(256) void attn_f32_kernel(AttnArgs a) {
         o[6] = fmaf(p, v1.z, o[6]);
         o[7] = fmaf(p, v1.w, o[7]);
       }
-      __syncthreads();
     }
+    __syncthreads();
+    csg = nsg;
+    cj0 = nj0;
+  }
+  if constexpr (KG > 1) {
+    // group 1's (m, l, O) per lane, in the tile memory the last barrier freed
+    float* st = &s_k4[0][0][0];
+    if (kg == 1) {
+      st[gt] = m_run;
+      st[256 + gt] = l_run;
+#pragma unroll
+      for (int c = 0; c < 8; ++c) st[512 + c * 256 + gt] = o[c];
+    }
+    __syncthreads();
+    if (kg != 0) return;
+    const float m1 = st[gt], l1 = st[256 + gt];
+    const float m = fmaxf(m_run, m1);
+    const float a0 = m_run > -INFINITY ? __builtin_amdgcn_exp2f(m_run - m) : 0.f;
+    const float a1 = m1 > -INFINITY ? __builtin_amdgcn_exp2f(m1 - m) : 0.f;
+    l_run = l_run * a0 + l1 * a1;
+#pragma unroll
+    for (int c = 0; c < 8; ++c) o[c] = o[c] * a0 + st[512 + c * 256 + gt] * a1;
   }
   if (valid) {
     const float inv = 1.f / l_run;
@@ -2572,7 +2630,7 @@ hipError_t launch_attention(const AttnArgs& a, bool bf16, hipStream_t s) {
     }
   } else if (a.D == 64) {
     const int nwg = ((a.T + 31) / 32) * a.H;
-    attn_f32_kernel<64><<<nwg, 256, 0, s>>>(a);
+    attn_f32_kernel<64><<<nwg, 512, 0, s>>>(a);        // two key groups
   } else if (a.D == 128) {
     const int nwg = ((a.T + 15) / 16) * a.H;
     attn_f32_kernel<128><<<nwg, 256, 0, s>>>(a);
