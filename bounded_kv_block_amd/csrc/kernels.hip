@@ -1653,25 +1653,26 @@ __device__ __forceinline__ float group_sum(float x) {
   return x;
 }
 
-// Key groups: with D = 64 a workgroup holds KG = 2 groups of 256 lanes over
-// the same queries, one wave of each on every SIMD.  The context's key tiles
-// are numbered in segment order and dealt round-robin, tile f to group
-// f mod KG, so each group runs half of the tiles with its own LDS tiles and
-// its own running (m, l, O); at the end group 1 hands its state to group 0
-// through LDS, which combines the two (m = the larger max, O and l summed
-// with weights 2^(m_g - m)) and writes the output.  Both groups pass every
-// barrier: a round in which a group has no tile left skips only its work.
-// D = 128 needs more than half of a SIMD's registers per wave, so it keeps
-// one group.
+// Key groups: with D = 64 a workgroup holds KG = 4 groups of 256 lanes over
+// the same queries, one wave of each on every SIMD, with key tiles of 32.
+// The context's key tiles are numbered in segment order and dealt
+// round-robin, tile f to group f mod KG, so each group runs a quarter of the
+// tiles with its own LDS tiles and its own running (m, l, O); at the end
+// groups 1..KG-1 hand their states to group 0 through LDS, which combines
+// them in group order (m = the largest max, O and l summed with weights
+// 2^(m_g - m)) and writes the output.  Every group passes every barrier: a
+// round in which a group has no tile left skips only its work.  D = 128
+// needs more than half of a SIMD's registers per wave, so it keeps one
+// group and tiles of 64.
 template <int D>
-__global__ __launch_bounds__(D == 64 ? 512 : 256) void attn_f32_kernel(AttnArgs a) {
+__global__ __launch_bounds__(D == 64 ? 1024 : 256) void attn_f32_kernel(AttnArgs a) {
   constexpr int G = D / 8;                 // lanes per query
   constexpr int QPB = 256 / G;             // queries per workgroup
-  constexpr int KG = D == 64 ? 2 : 1;      // key groups of 256 lanes
-  constexpr int BNF = 64;
+  constexpr int KG = D == 64 ? 4 : 1;      // key groups of 256 lanes
+  constexpr int BNF = D == 64 ? 32 : 64;   // keys per tile
   constexpr int NC = D / 4;                // 16-byte chunks per key row
   constexpr int NL = BNF * D / 4 / 256;    // float4 loads per lane per operand and tile
-  static_assert(KG == 1 || 10 * 256 <= KG * BNF * D, "the merge state (m, l, 8 O per lane) fits the K tiles");
+  static_assert(KG == 1 || (KG - 1) * 10 * 256 <= KG * BNF * D, "the merge states (m, l, 8 O per lane) fit the K tiles");
   __shared__ __attribute__((aligned(16))) float s_k4[KG][BNF][D];
   __shared__ __attribute__((aligned(16))) float s_v4[KG][BNF][D];
   __shared__ const float* s_k[kMaxSeg];
@@ -1852,23 +1853,34 @@ __global__ __launch_bounds__(D == 64 ? 512 : 256) void attn_f32_kernel(AttnArgs 
     cj0 = nj0;
   }
   if constexpr (KG > 1) {
-    // group 1's (m, l, O) per lane, in the tile memory the last barrier freed
+    // groups 1..KG-1 store (m, l, O) per lane in the tile memory the last
+    // barrier freed; group 0 combines all KG states in group order
     float* st = &s_k4[0][0][0];
-    if (kg == 1) {
-      st[gt] = m_run;
-      st[256 + gt] = l_run;
+    if (kg > 0) {
+      float* sg = st + (kg - 1) * 10 * 256;
+      sg[gt] = m_run;
+      sg[256 + gt] = l_run;
 #pragma unroll
-      for (int c = 0; c < 8; ++c) st[512 + c * 256 + gt] = o[c];
+      for (int c = 0; c < 8; ++c) sg[512 + c * 256 + gt] = o[c];
     }
     __syncthreads();
     if (kg != 0) return;
-    const float m1 = st[gt], l1 = st[256 + gt];
-    const float m = fmaxf(m_run, m1);
-    const float a0 = m_run > -INFINITY ? __builtin_amdgcn_exp2f(m_run - m) : 0.f;
-    const float a1 = m1 > -INFINITY ? __builtin_amdgcn_exp2f(m1 - m) : 0.f;
-    l_run = l_run * a0 + l1 * a1;
+    float m = m_run;
 #pragma unroll
-    for (int c = 0; c < 8; ++c) o[c] = o[c] * a0 + st[512 + c * 256 + gt] * a1;
+    for (int g = 1; g < KG; ++g) m = fmaxf(m, st[(g - 1) * 2560 + gt]);
+    const float a0 = m_run > -INFINITY ? __builtin_amdgcn_exp2f(m_run - m) : 0.f;
+    l_run *= a0;
+#pragma unroll
+    for (int c = 0; c < 8; ++c) o[c] *= a0;
+#pragma unroll
+    for (int g = 1; g < KG; ++g) {
+      const float* sg = st + (g - 1) * 2560;
+      const float mg = sg[gt];
+      const float ag = mg > -INFINITY ? __builtin_amdgcn_exp2f(mg - m) : 0.f;
+      l_run += sg[256 + gt] * ag;
+#pragma unroll
+      for (int c = 0; c < 8; ++c) o[c] += sg[512 + c * 256 + gt] * ag;
+    }
   }
   if (valid) {
     const float inv = 1.f / l_run;
@@ -2630,7 +2642,7 @@ hipError_t launch_attention(const AttnArgs& a, bool bf16, hipStream_t s) {
     }
   } else if (a.D == 64) {
     const int nwg = ((a.T + 31) / 32) * a.H;
-    attn_f32_kernel<64><<<nwg, 512, 0, s>>>(a);        // two key groups
+    attn_f32_kernel<64><<<nwg, 1024, 0, s>>>(a);       // four key groups
   } else if (a.D == 128) {
     const int nwg = ((a.T + 15) / 16) * a.H;
     attn_f32_kernel<128><<<nwg, 256, 0, s>>>(a);
