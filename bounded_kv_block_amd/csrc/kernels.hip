@@ -1624,8 +1624,8 @@ __global__ __launch_bounds__(64) void attn_merge_kernel(AttnArgs a) {
 // A query's D channels are spread over G = D/8 lanes (8 channels each): a
 // score is 8 FMAs per lane and a sum over the G lanes by DPP moves within
 // the lanes' row (every lane ends with the same value), and the lanes' 8
-// output channels accumulate P V directly.  Workgroup = 256 lanes =
-// 256/G queries of one head, over key tiles of 64.
+// output channels accumulate P V directly.  A workgroup holds the queries
+// of one head (key groups below).
 //
 // Both tiles sit key-major in LDS, so a lane reads its 8 channels of a key
 // as two float4: K rows as they are, V transposed from V^T on the way in,
@@ -1653,26 +1653,28 @@ __device__ __forceinline__ float group_sum(float x) {
   return x;
 }
 
-// Key groups: with D = 64 a workgroup holds KG = 4 groups of 256 lanes over
-// the same queries, one wave of each on every SIMD, with key tiles of 32.
-// The context's key tiles are numbered in segment order and dealt
-// round-robin, tile f to group f mod KG, so each group runs a quarter of the
+// Key groups: a workgroup holds KG groups of LG lanes over the same
+// queries.  The context's key tiles are numbered in segment order and dealt
+// round-robin, tile f to group f mod KG, so each group runs 1/KG of the
 // tiles with its own LDS tiles and its own running (m, l, O); at the end
 // groups 1..KG-1 hand their states to group 0 through LDS, which combines
 // them in group order (m = the largest max, O and l summed with weights
 // 2^(m_g - m)) and writes the output.  Every group passes every barrier: a
-// round in which a group has no tile left skips only its work.  D = 128
-// needs more than half of a SIMD's registers per wave, so it keeps one
-// group and tiles of 64.
+// round in which a group has no tile left skips only its work.  With D = 64
+// a group is one wave of 8 queries and a workgroup 8 groups (two waves per
+// SIMD) over key tiles of 32, so that small blocks spread over many CUs;
+// D = 128 needs more than half of a SIMD's registers per wave, so it keeps
+// one group of 256 lanes (16 queries) and tiles of 64.
 template <int D>
-__global__ __launch_bounds__(D == 64 ? 1024 : 256) void attn_f32_kernel(AttnArgs a) {
+__global__ __launch_bounds__(D == 64 ? 512 : 256) void attn_f32_kernel(AttnArgs a) {
   constexpr int G = D / 8;                 // lanes per query
-  constexpr int QPB = 256 / G;             // queries per workgroup
-  constexpr int KG = D == 64 ? 4 : 1;      // key groups of 256 lanes
+  constexpr int LG = D == 64 ? 64 : 256;   // lanes per key group
+  constexpr int QPB = LG / G;              // queries per workgroup
+  constexpr int KG = D == 64 ? 8 : 1;      // key groups
   constexpr int BNF = D == 64 ? 32 : 64;   // keys per tile
   constexpr int NC = D / 4;                // 16-byte chunks per key row
-  constexpr int NL = BNF * D / 4 / 256;    // float4 loads per lane per operand and tile
-  static_assert(KG == 1 || (KG - 1) * 10 * 256 <= KG * BNF * D, "the merge states (m, l, 8 O per lane) fit the K tiles");
+  constexpr int NL = BNF * D / 4 / LG;     // float4 loads per lane per operand and tile
+  static_assert(KG == 1 || (KG - 1) * 10 * LG <= KG * BNF * D, "the merge states (m, l, 8 O per lane) fit the K tiles");
   __shared__ __attribute__((aligned(16))) float s_k4[KG][BNF][D];
   __shared__ __attribute__((aligned(16))) float s_v4[KG][BNF][D];
   __shared__ const float* s_k[kMaxSeg];
@@ -1680,8 +1682,8 @@ __global__ __launch_bounds__(D == 64 ? 1024 : 256) void attn_f32_kernel(AttnArgs
   __shared__ int s_n[kMaxSeg];
   __shared__ int s_ld[kMaxSeg];
   const int tid = threadIdx.x;
-  const int kg = __builtin_amdgcn_readfirstlane(tid >> 8);   // key group
-  const int gt = tid & 255;                // lane within the group
+  const int kg = __builtin_amdgcn_readfirstlane(tid / LG);   // key group
+  const int gt = tid % LG;                 // lane within the group
   const int nqt = (a.T + QPB - 1) / QPB;
   const int head = blockIdx.x / nqt, qt = blockIdx.x - head * nqt;
   if (tid < a.nseg) {
@@ -1743,7 +1745,7 @@ __global__ __launch_bounds__(D == 64 ? 1024 : 256) void attn_f32_kernel(AttnArgs
   auto load_tile = [&](const float* kb, const float* vb, int ld, int j0, int nv) {
 #pragma unroll
     for (int it = 0; it < NL; ++it) {
-      const int idx = it * 256 + gt;
+      const int idx = it * LG + gt;
       const int r = idx / NC, c4 = idx - r * NC;
       kl[it] = r < nv ? *reinterpret_cast<const float4*>(kb + (size_t)(j0 + r) * D + 4 * c4)
                       : make_float4(0.f, 0.f, 0.f, 0.f);
@@ -1764,7 +1766,7 @@ __global__ __launch_bounds__(D == 64 ? 1024 : 256) void attn_f32_kernel(AttnArgs
   auto store_tile = [&]() {
 #pragma unroll
     for (int it = 0; it < NL; ++it) {
-      const int idx = it * 256 + gt;
+      const int idx = it * LG + gt;
       const int r = idx / NC, c4 = idx - r * NC;
       *reinterpret_cast<float4*>(&tk[r][cpos(r, c4)]) = kl[it];
       const int d = idx / (BNF / 4), jj = 4 * (idx - d * (BNF / 4));
@@ -1856,30 +1858,31 @@ __global__ __launch_bounds__(D == 64 ? 1024 : 256) void attn_f32_kernel(AttnArgs
     // groups 1..KG-1 store (m, l, O) per lane in the tile memory the last
     // barrier freed; group 0 combines all KG states in group order
     float* st = &s_k4[0][0][0];
+    constexpr int SW = 10 * LG;            // floats per group state
     if (kg > 0) {
-      float* sg = st + (kg - 1) * 10 * 256;
+      float* sg = st + (kg - 1) * SW;
       sg[gt] = m_run;
-      sg[256 + gt] = l_run;
+      sg[LG + gt] = l_run;
 #pragma unroll
-      for (int c = 0; c < 8; ++c) sg[512 + c * 256 + gt] = o[c];
+      for (int c = 0; c < 8; ++c) sg[(2 + c) * LG + gt] = o[c];
     }
     __syncthreads();
     if (kg != 0) return;
     float m = m_run;
 #pragma unroll
-    for (int g = 1; g < KG; ++g) m = fmaxf(m, st[(g - 1) * 2560 + gt]);
+    for (int g = 1; g < KG; ++g) m = fmaxf(m, st[(g - 1) * SW + gt]);
     const float a0 = m_run > -INFINITY ? __builtin_amdgcn_exp2f(m_run - m) : 0.f;
     l_run *= a0;
 #pragma unroll
     for (int c = 0; c < 8; ++c) o[c] *= a0;
 #pragma unroll
     for (int g = 1; g < KG; ++g) {
-      const float* sg = st + (g - 1) * 2560;
+      const float* sg = st + (g - 1) * SW;
       const float mg = sg[gt];
       const float ag = mg > -INFINITY ? __builtin_amdgcn_exp2f(mg - m) : 0.f;
-      l_run += sg[256 + gt] * ag;
+      l_run += sg[LG + gt] * ag;
 #pragma unroll
-      for (int c = 0; c < 8; ++c) o[c] += sg[512 + c * 256 + gt] * ag;
+      for (int c = 0; c < 8; ++c) o[c] += sg[(2 + c) * LG + gt] * ag;
     }
   }
   if (valid) {
@@ -2641,8 +2644,8 @@ hipError_t launch_attention(const AttnArgs& a, bool bf16, hipStream_t s) {
       if (b.parts > 1) attn_merge_kernel<<<rU * AWAVES, 64, 0, s>>>(b);
     }
   } else if (a.D == 64) {
-    const int nwg = ((a.T + 31) / 32) * a.H;
-    attn_f32_kernel<64><<<nwg, 1024, 0, s>>>(a);       // four key groups
+    const int nwg = ((a.T + 7) / 8) * a.H;             // 8 queries per workgroup
+    attn_f32_kernel<64><<<nwg, 512, 0, s>>>(a);        // 8 key groups of one wave
   } else if (a.D == 128) {
     const int nwg = ((a.T + 15) / 16) * a.H;
     attn_f32_kernel<128><<<nwg, 256, 0, s>>>(a);
