@@ -2276,102 +2276,131 @@ void qkv_gemm_kernel(QkvArgs a) {
   for (; s < S; ++s) step(s, std::false_type{});
 
   // epilogue: + bias; q -> scratch [T][H][D]; k -> (raw copy,) RoPE -> cache
-  // rows; v -> V^T.  A 32-feature block lies in one head of one of q, k, v.
+  // rows; v -> V^T.  A wave's 128 features are one head of one of q, k, v
+  // (f0 is a multiple of 256 and a head is 128 features), so which and head
+  // are wave-uniform.
+  // Loads come before stores: the compiler cannot move a load above a store
+  // that may alias it, so a bias or RoPE table load placed between stores
+  // waits out its whole latency, once per load.  For each token column and
+  // 32-feature block (bn, bm), the bias (4 values per group g) and the RoPE
+  // (cos, sin) of the block's 8 channel pairs are loaded together, then the
+  // block's 4 groups are formed and stored.
   const AppendArgs& ap = a.ap;
   const bool rope = has_rope(ap.rope);
   const __bf16* bias = static_cast<const __bf16*>(a.b);
+  const int fw = f0 + 128 * wf, tw = t0 + 64 * wt;
+  if (fw >= NF || tw >= T) return;         // rows past the last feature or token: never stored
+  const int which = fw / HD, head = (fw - which * HD) / AD;
+  const RopeSel rs(ap.rope);
+  const bool rot = which == 1 && rope;
+  int fyx[2][3];                           // (frame, y, x) of the token columns, clamped into the block
+#pragma unroll
+  for (int bn = 0; bn < 2; ++bn)
+    token_fyx(min(tw + 32 * bn + col, T - 1), ap.rope.grid_h, ap.rope.grid_w, fyx[bn][0], fyx[bn][1], fyx[bn][2]);
+  bf16x4 bb[4];                            // bias of the block's groups
+  float2 cs[4][2];                         // (cos, sin) of channel pairs d0, d0 + 2 of each group
+  auto load_block = [&](int bn, int bm) {
+    if (bias) {
+#pragma unroll
+      for (int g = 0; g < 4; ++g) bb[g] = *reinterpret_cast<const bf16x4*>(bias + fw + 32 * bm + 8 * g + 4 * hh);
+    }
+    if (rot) {
+#pragma unroll
+      for (int g = 0; g < 4; ++g)
+#pragma unroll
+        for (int p2 = 0; p2 < 2; ++p2)
+          cs[g][p2] = rs.cs(32 * bm + 8 * g + 4 * hh + 2 * p2, ap.t_row0 + fyx[bn][0], fyx[bn][1], fyx[bn][2]);
+    }
+  };
+  // value j of group (bm, g) for token column bn: + bias, rounded to bf16 as
+  // it leaves the projection (as the unfused path receives it)
+  auto value4 = [&](int bm, int bn, int g, float (&v)[4]) {
+#pragma unroll
+    for (int j = 0; j < 4; ++j) v[j] = acc[bm][bn][4 * g + j];
+    if (bias) {
+#pragma unroll
+      for (int j = 0; j < 4; ++j) v[j] += (float)bb[g][j];
+    }
+#pragma unroll
+    for (int j = 0; j < 4; ++j) v[j] = (float)(__bf16)v[j];
+  };
   // FP8 caches: a wave's 128 features x 64 tokens are one head's K (or V)
   // over one 64-token tile of the block (both aligned), so the tile's scale
   // is a reduction within the wave.  Pass 1 forms every value (bias, bf16
-  // rounding as it leaves the projection, the raw copies, RoPE for K) and
-  // reduces the largest magnitude over the valid tokens; pass 2 forms the
-  // values again and stores E4M3 bytes and the tile exponent.  Forming them
-  // twice keeps the accumulators as they are, which keeps the epilogue free
-  // of register spills.
-  const int fw = f0 + 128 * wf, tw = t0 + 64 * wt;
-  const int which_w = fw < NF ? fw / HD : -1;
-  if ((ap.k8 && which_w == 1) || (ap.v8 && which_w == 2)) {
-    if (tw >= T) return;
-    const bool isk = which_w == 1;
-    const int head = (fw - which_w * HD) / AD;
-    // a token column's (frame, y, x), clamped to the block (rows past its end
-    // are never stored and never enter the scale)
-    int fy[2], yy[2], xx[2];
-#pragma unroll
-    for (int bn = 0; bn < 2; ++bn) token_fyx(min(tw + 32 * bn + col, T - 1), ap.rope.grid_h, ap.rope.grid_w,
-                                             fy[bn], yy[bn], xx[bn]);
-    const RopeSel rs(ap.rope);
-    const bool rot = isk && rope;
-    // value j of group (bm, g) for token column bn; raw: also store the raw
-    // copies.  Branch-free apart from the stores.
-    auto value4 = [&](int bm, int bn, int g, float (&v)[4], bool raw) {
-      const int t = tw + 32 * bn + col;
-      const int d0 = 32 * bm + 8 * g + 4 * hh;
-#pragma unroll
-      for (int j = 0; j < 4; ++j) v[j] = acc[bm][bn][4 * g + j];
-      if (bias) {
-        const bf16x4 bb = *reinterpret_cast<const bf16x4*>(bias + fw + d0);
-#pragma unroll
-        for (int j = 0; j < 4; ++j) v[j] += (float)bb[j];
-      }
-#pragma unroll
-      for (int j = 0; j < 4; ++j) v[j] = (float)(__bf16)v[j];   // bf16, as the unfused path receives it
-      if (raw && t < T) {
-        if (isk && ap.k_raw) {
-          bf16x4 o;
-#pragma unroll
-          for (int j = 0; j < 4; ++j) o[j] = (__bf16)v[j];
-          *reinterpret_cast<bf16x4*>(static_cast<__bf16*>(ap.k_raw) + head * ap.k_raw_hs + (size_t)t * AD + d0) = o;
-        } else if (!isk && ap.vt) {
-#pragma unroll
-          for (int j = 0; j < 4; ++j)
-            static_cast<__bf16*>(ap.vt)[head * ap.vt_hs + (size_t)(d0 + j) * ap.vt_ld + t] = (__bf16)v[j];
-        }
-      }
-      if (rot) {
-        rope_rot(v[0], v[1], rs.cs(d0, ap.t_row0 + fy[bn], yy[bn], xx[bn]));
-        rope_rot(v[2], v[3], rs.cs(d0 + 2, ap.t_row0 + fy[bn], yy[bn], xx[bn]));
-      }
-    };
+  // rounding, the raw copies, RoPE for K) and reduces the largest magnitude
+  // over the valid tokens; pass 2 forms the values again and stores E4M3
+  // bytes and the tile exponent.  Forming them twice keeps the accumulators
+  // as they are, which keeps the epilogue free of register spills.
+  if ((ap.k8 && which == 1) || (ap.v8 && which == 2)) {
+    const bool isk = which == 1;
     float amax = 0.f;
 #pragma unroll
     for (int bn = 0; bn < 2; ++bn) {
-      const bool live = tw + 32 * bn + col < T;
+      const int t = tw + 32 * bn + col;
+      const bool live = t < T;
 #pragma unroll
-      for (int bm = 0; bm < 4; ++bm)
+      for (int bm = 0; bm < 4; ++bm) {
+        load_block(bn, bm);
 #pragma unroll
         for (int g = 0; g < 4; ++g) {
+          const int d0 = 32 * bm + 8 * g + 4 * hh;
           float v[4];
-          value4(bm, bn, g, v, true);
+          value4(bm, bn, g, v);
+          if (live) {
+            if (isk && ap.k_raw) {
+              bf16x4 o;
+#pragma unroll
+              for (int j = 0; j < 4; ++j) o[j] = (__bf16)v[j];
+              *reinterpret_cast<bf16x4*>(static_cast<__bf16*>(ap.k_raw) + head * ap.k_raw_hs + (size_t)t * AD + d0) = o;
+            } else if (!isk && ap.vt) {
+#pragma unroll
+              for (int j = 0; j < 4; ++j)
+                static_cast<__bf16*>(ap.vt)[head * ap.vt_hs + (size_t)(d0 + j) * ap.vt_ld + t] = (__bf16)v[j];
+            }
+          }
+          if (rot) {
+            rope_rot(v[0], v[1], cs[g][0]);
+            rope_rot(v[2], v[3], cs[g][1]);
+          }
 #pragma unroll
           for (int j = 0; j < 4; ++j) amax = live ? fmaxf(amax, fabsf(v[j])) : amax;
           asm volatile("" : "+v"(amax));   // reduce here: the group's values die now
         }
+      }
     }
 #pragma unroll
     for (int o = 32; o > 0; o >>= 1) amax = fmaxf(amax, __shfl_xor(amax, o));
     const int ex = e4m3_exponent(amax);
     const float inv = __builtin_amdgcn_ldexpf(1.f, -ex);
+    // pass 2: the values again, stored as E4M3 with the tile's scale
 #pragma unroll
     for (int bn = 0; bn < 2; ++bn) {
       const int t = tw + 32 * bn + col;
-      if (t >= T) continue;
+      const bool live = t < T;
 #pragma unroll
-      for (int bm = 0; bm < 4; ++bm)
+      for (int bm = 0; bm < 4; ++bm) {
+        load_block(bn, bm);
 #pragma unroll
         for (int g = 0; g < 4; ++g) {
-          float v[4];
-          value4(bm, bn, g, v, false);
           const int d0 = 32 * bm + 8 * g + 4 * hh;
+          float v[4];
+          value4(bm, bn, g, v);
+          if (rot) {
+            rope_rot(v[0], v[1], cs[g][0]);
+            rope_rot(v[2], v[3], cs[g][1]);
+          }
           const int w = e4m3_pack4(v[0] * inv, v[1] * inv, v[2] * inv, v[3] * inv);
-          if (isk) {
-            *reinterpret_cast<int*>(static_cast<char*>(ap.k8) + head * ap.k8_hs + (size_t)t * AD + d0) = w;
-          } else {
-            unsigned char* vp = static_cast<unsigned char*>(ap.v8) + head * ap.v8_hs + t;
+          if (live) {
+            if (isk) {
+              *reinterpret_cast<int*>(static_cast<char*>(ap.k8) + head * ap.k8_hs + (size_t)t * AD + d0) = w;
+            } else {
+              unsigned char* vp = static_cast<unsigned char*>(ap.v8) + head * ap.v8_hs + t;
 #pragma unroll
-            for (int j = 0; j < 4; ++j) vp[(size_t)(d0 + j) * ap.v8_ld] = (unsigned char)(w >> (8 * j));
+              for (int j = 0; j < 4; ++j) vp[(size_t)(d0 + j) * ap.v8_ld] = (unsigned char)(w >> (8 * j));
+            }
           }
         }
+      }
     }
     if (lane == 0) {
       if (isk) ap.kx[head * ap.kx_hs + tw / 64] = ex;
@@ -2381,44 +2410,32 @@ void qkv_gemm_kernel(QkvArgs a) {
   }
 #pragma unroll
   for (int bn = 0; bn < 2; ++bn) {
-    const int t = t0 + 64 * wt + 32 * bn + col;
-    if (t >= T) continue;
-    int fy = 0, yy = 0, xx = 0;
-    if (rope) token_fyx(t, ap.rope.grid_h, ap.rope.grid_w, fy, yy, xx);
+    const int t = tw + 32 * bn + col;
+    const bool live = t < T;
 #pragma unroll
     for (int bm = 0; bm < 4; ++bm) {
-      const int fbase = f0 + 128 * wf + 32 * bm;
-      if (fbase >= NF) continue;
-      const int which = fbase / HD, head = (fbase - which * HD) / AD, db = fbase % AD;
+      load_block(bn, bm);
 #pragma unroll
       for (int g = 0; g < 4; ++g) {
-        const int d0 = db + 8 * g + 4 * hh;
+        const int d0 = 32 * bm + 8 * g + 4 * hh;
         float v[4];
-#pragma unroll
-        for (int j = 0; j < 4; ++j) v[j] = acc[bm][bn][4 * g + j];
-        if (bias) {
-          const bf16x4 bb = *reinterpret_cast<const bf16x4*>(bias + fbase + 8 * g + 4 * hh);
-#pragma unroll
-          for (int j = 0; j < 4; ++j) v[j] += (float)bb[j];
-        }
+        value4(bm, bn, g, v);
+        if (!live) continue;
         bf16x4 o;
         if (which == 0) {
 #pragma unroll
           for (int j = 0; j < 4; ++j) o[j] = (__bf16)v[j];
           *reinterpret_cast<bf16x4*>(static_cast<__bf16*>(a.q) + ((size_t)t * H + head) * AD + d0) = o;
         } else if (which == 1) {
-          // k leaves the projection in bf16, as the unfused path receives it;
-          // the rotation then starts from that value
+          // the rotation starts from the bf16 value k leaves the projection with
+          if (ap.k_raw) {
 #pragma unroll
-          for (int j = 0; j < 4; ++j) {
-            o[j] = (__bf16)v[j];
-            v[j] = (float)o[j];
-          }
-          if (ap.k_raw)
+            for (int j = 0; j < 4; ++j) o[j] = (__bf16)v[j];
             *reinterpret_cast<bf16x4*>(static_cast<__bf16*>(ap.k_raw) + head * ap.k_raw_hs + (size_t)t * AD + d0) = o;
-          if (rope) {
-            rope_pair(v[0], v[1], d0, ap.rope, ap.t_row0 + fy, yy, xx);
-            rope_pair(v[2], v[3], d0 + 2, ap.rope, ap.t_row0 + fy, yy, xx);
+          }
+          if (rot) {
+            rope_rot(v[0], v[1], cs[g][0]);
+            rope_rot(v[2], v[3], cs[g][1]);
           }
 #pragma unroll
           for (int j = 0; j < 4; ++j) o[j] = (__bf16)v[j];
