@@ -651,15 +651,22 @@ __device__ __forceinline__ i32x4 buffer_rsrc(const char* base) {
 // not treat every later LDS read as waiting on it: the caller waits with
 // vmcnt(0) before the barrier that publishes the tile.  No register output.
 // The LDS address goes in as an operand bound to m0 ("{m0}"), so the compiler
-// writes m0 itself and knows it is live; the s_nop separates that write from
-// the load that reads it.
+// writes m0 itself and knows it is live.
+// The compiler's hazard checks do not look inside asm, so the asm provides
+// the wait states a memory instruction needs itself: an SGPR written by a
+// VALU instruction (v_readlane reloading a spilled SGPR, v_readfirstlane)
+// may be read by a VMEM instruction only 5 wait states later, and the load
+// reads the descriptor and the scalar offset from SGPRs (and m0, written by
+// a scalar move, 1 wait state later).  s_nop 4 gives all 5 whatever
+// precedes the asm.  With fewer, a build whose descriptor was reloaded from
+// spill lanes just before a load read a stale descriptor and faulted.
 __device__ __forceinline__ void dma16(i32x4 rsrc, unsigned voff, unsigned soff, unsigned lds_base) {
   // the scalar offset must sit in an SGPR, never a folded literal (the
   // descriptor and the LDS address come from registers anyway; marking them
   // as rewritten here would make the compiler copy them for every load)
   asm volatile("" : "+s"(soff));
   asm volatile(
-      "s_nop 0\n\t"
+      "s_nop 4\n\t"
       "buffer_load_dwordx4 %0, %1, %2 offen lds"
       :
       : "v"(voff), "s"(rsrc), "s"(soff), "{m0}"(lds_base)
@@ -1242,7 +1249,10 @@ void attn_bf16_kernel(AttnArgs a) {
           const float e = __builtin_amdgcn_exp2f(x);
           e4[u] = e;
           if constexpr (!VF8) pb[mb][i >> 3][i & 7] = (__bf16)e;
-          ls[2 * mb + (g >> 1)] += e;
+          // a chain's first term is stored, not added to 0 (the same value:
+          // exp2 is never -0), which saves four adds per tile
+          if ((g & 1) == 0 && u == 0) ls[2 * mb + (g >> 1)] = e;
+          else ls[2 * mb + (g >> 1)] += e;
         }
         if constexpr (VF8) pb8[4 * mb + g] = e4m3_pack4(e4[0], e4[1], e4[2], e4[3]);
         hook(4 * mb + g);

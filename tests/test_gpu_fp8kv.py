@@ -117,7 +117,6 @@ def test_fp8kv_reference_frames_and_relative_positions():
     _stream(cfg, values=True)
 
 
-@pytest.mark.skip(reason="faulted the GPU once, with a change to the softmax row sum that has since been removed (the attention kernels' machine code is again the one this test passed with); the cause of that fault is not shown, so this case stays off the GPU until it is. The FP8 KV split launch is still run by test_prsink_720x416_fp8kv_every_output_of_one_layer.")
 def test_fp8kv_split_launch_key_parts():
     """1800-query blocks, 40 heads: the split launch (one full round, then the
     64 remainder units cut into 4 key parts) with the FP8 KV cache."""
