@@ -63,7 +63,11 @@ def scan(asm):
                 break
             if op.startswith("s_endpgm") or op.startswith("s_branch") or op.startswith("s_cbranch"):
                 break
-            dst = _sgprs(tj.split(None, 1)[1].split(",")[0]) if " " in tj else set()
+            ops_j = [x.strip() for x in tj.split(None, 1)[1].split(",")] if " " in tj else []
+            dst = _sgprs(ops_j[0]) if ops_j else set()
+            # VOP3 forms that also write an SGPR pair (carry out, or the scale flag)
+            if len(ops_j) > 1 and re.match(r"v_(add|sub|subrev|addc|subb|subbrev)_co|v_mad_[iu]64_[iu]32|v_div_scale", op):
+                dst |= _sgprs(ops_j[1])
             hit = dst & reads
             if hit:
                 if op.startswith("v_") and not op.startswith("v_mfma") and ws < VMEM_SGPR_WAITS:
@@ -96,6 +100,8 @@ def test_scan_finds_the_hazard_it_looks_for():
             "\tbuffer_load_dwordx4 v172, s[4:7], s2 offen lds\n")
     assert len(scan(bad)) == 1 and scan(good) == []
     assert len(scan("\ts_mov_b32 m0, s2\n\tbuffer_load_dwordx4 v1, s[4:7], s3 offen lds\n")) == 1
+    carry = "\tv_add_co_u32_e64 v1, s[6:7], v2, v3\n\ts_nop 1\n\tbuffer_load_dwordx4 v1, s[4:7], s3 offen lds\n"
+    assert len(scan(carry)) == 1
 
 
 def test_lds_dma_loads_have_their_wait_states(device_asm):
